@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs for the deformable-convolution forward.
+
+This module only draws random tensors.  It holds none of the method's arithmetic
+(no sampling positions, no interpolation, no output-size formula: the output
+size of each named workload is stated in the table as data, and callers pass it
+in for other shapes).  Both the HIP path's tests and bench and the oracle's
+tests take their inputs from here.
+
+The named workloads stand in for ResNet-50 / Faster R-CNN backbone activations
+on COCO-sized images (deformable 3x3 layers in stages c3-c5, res5 with
+dilation 2) and for the single 224x224 RGB example of the torchvision
+deform_conv2d tutorial (agent.csdn.net/6a744b3d10ee7a33f2973402.html, section
+2.2).  No dataset is read: only shapes and value distributions are reproduced.
+
+Draw order per workload, all in float32 on the CPU from
+``torch.Generator().manual_seed(seed)``: x, weight, offset, mask, bias.  For
+bf16 workloads every tensor is then rounded to bfloat16 (round to nearest
+even), and the oracle reads back exactly those rounded values.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "f32" or "bf16": element type of every tensor
+    B: int
+    Cin: int
+    H: int
+    W: int
+    Cout: int
+    K: int
+    stride: int
+    pad: int
+    dilation: int
+    Ho: int               # stated output size (data, not computed here)
+    Wo: int
+    offset: str           # "uniform:a" U(-a,a) | "normal:s" s*N(0,1) | "tanh:s" s*tanh(N(0,1))
+    mask: str | None      # "sigmoid" = sigmoid(N(0,1)) | "ones" | None (DCNv1)
+    bias: str | None      # "zeros" | "normal:s" s*N(0,1) | None
+    seed: int = 0
+    x: str = "normal"     # "normal" = N(0,1)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def flops(self) -> int:
+        """2*B*Cout*Ho*Wo*Cin*K^2: the multiply-adds of the contraction."""
+        return 2 * self.B * self.Cout * self.Ho * self.Wo * self.Cin * self.K * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Each tensor crossing the boundary counted once, at its element size."""
+        es = 4 if self.dtype == "f32" else 2
+        KK = self.K * self.K
+        n = (self.B * self.Cin * self.H * self.W
+             + self.B * 2 * KK * self.Ho * self.Wo
+             + (self.B * KK * self.Ho * self.Wo if self.mask is not None else 0)
+             + self.Cout * self.Cin * KK
+             + (self.Cout if self.bias is not None else 0)
+             + self.B * self.Cout * self.Ho * self.Wo)
+        return n * es
+
+
+# The five workloads: tiny smoke case, the 224x224 single image, and the
+# ResNet-50 c3 / c4 (stride-2 downsampling) / c5 (DCNv1, dilation 2) layers.
+WORKLOADS = {
+    "tiny": Workload("tiny", "f32", 1, 3, 32, 32, 8, 3, 1, 1, 1, 32, 32,
+                     offset="uniform:2", mask="sigmoid", bias="zeros", seed=1000),
+    "single224": Workload("single224", "f32", 1, 3, 224, 224, 64, 3, 1, 1, 1, 224, 224,
+                          offset="tanh:0.5", mask="sigmoid", bias=None, seed=1001),
+    "c3": Workload("c3", "bf16", 2, 128, 100, 168, 128, 3, 1, 1, 1, 100, 168,
+                   offset="normal:2", mask="sigmoid", bias=None, seed=1002),
+    "c4": Workload("c4", "bf16", 2, 256, 100, 168, 256, 3, 2, 1, 1, 50, 84,
+                   offset="normal:1", mask="sigmoid", bias=None, seed=1003),
+    "c5": Workload("c5", "bf16", 8, 512, 25, 42, 512, 3, 1, 2, 2, 25, 42,
+                   offset="uniform:8", mask=None, bias="normal:0.01", seed=1004),
+}
+ORDER = ["tiny", "single224", "c3", "c4", "c5"]
+
+
+def _draw(kind: str, shape, g: torch.Generator) -> torch.Tensor:
+    name, _, arg = kind.partition(":")
+    if name == "normal":
+        s = float(arg) if arg else 1.0
+        return torch.randn(shape, generator=g) * s
+    if name == "uniform":
+        a = float(arg)
+        return (torch.rand(shape, generator=g) * 2.0 - 1.0) * a
+    if name == "tanh":
+        return torch.tanh(torch.randn(shape, generator=g)) * float(arg)
+    if name == "sigmoid":
+        return torch.sigmoid(torch.randn(shape, generator=g))
+    if name == "ones":
+        return torch.ones(shape)
+    if name == "zeros":
+        return torch.zeros(shape)
+    raise ValueError(f"unknown distribution {kind!r}")
+
+
+def generate(w: Workload, seed: int | None = None) -> dict[str, torch.Tensor | None]:
+    """Seeded CPU tensors for one workload, in the workload's element type.
+
+    Weight: Kaiming-normal, fan-in mode with gain sqrt(2): std = sqrt(2 / (Cin*K*K)).
+    """
+    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+    KK = w.K * w.K
+    x = _draw(w.x, (w.B, w.Cin, w.H, w.W), g)
+    weight = torch.randn((w.Cout, w.Cin, w.K, w.K), generator=g) * math.sqrt(2.0 / (w.Cin * KK))
+    offset = _draw(w.offset, (w.B, 2 * KK, w.Ho, w.Wo), g)
+    mask = _draw(w.mask, (w.B, KK, w.Ho, w.Wo), g) if w.mask is not None else None
+    bias = _draw(w.bias, (w.Cout,), g) if w.bias is not None else None
+    dt = w.torch_dtype
+    cast = (lambda t: None if t is None else t.to(dt).contiguous())
+    return {"x": cast(x), "offset": cast(offset), "mask": cast(mask), "weight": cast(weight),
+            "bias": cast(bias)}
+
+
+def custom(name: str, dtype: str, B: int, Cin: int, H: int, W: int, Cout: int, K: int,
+           stride: int, pad: int, dilation: int, Ho: int, Wo: int, offset: str = "normal:1",
+           mask: str | None = "sigmoid", bias: str | None = "normal:0.1", seed: int = 0,
+           x: str = "normal") -> Workload:
+    """A workload of any shape (used for edge cases); the caller supplies Ho, Wo."""
+    return Workload(name, dtype, B, Cin, H, W, Cout, K, stride, pad, dilation, Ho, Wo,
+                    offset=offset, mask=mask, bias=bias, seed=seed, x=x)

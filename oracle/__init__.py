@@ -1,0 +1,151 @@
+"""CPU oracle for the modulated deformable convolution forward (DCNv2; DCNv1 when
+the mask is absent).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+package ``deformable_convolution_vision_amd`` never imports it, and the two
+share no code: this package wraps ``libdcn_oracle.so``, built by ``g++`` from
+``dcn_oracle.cpp`` alone (see that file and ``dcn_oracle.h`` for the definition
+and its sources on the pages).
+
+Every function here takes host arrays that are already rounded to the element
+type under test (fp32 values, or bf16 values widened to fp32) and returns
+float64 results.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "dcn_oracle.cpp")
+LIB = os.path.join(HERE, "libdcn_oracle.so")
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in
+                ("B", "Cin", "H", "W", "Cout", "K", "stride", "pad", "dilation")]
+
+
+def build(out_path: str = LIB, extra_flags: tuple[str, ...] = (), src: str = SRC) -> str:
+    """Compile the oracle with g++ (OpenMP, IEEE arithmetic: no fast-math)."""
+    tmp = out_path + ".tmp"
+    cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           f"-I{HERE}", *extra_flags, src, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+_lib_cache: dict[str, ctypes.CDLL] = {}
+
+
+def load(path: str = LIB) -> ctypes.CDLL:
+    """Load the oracle library, building it only if it is not there yet."""
+    if path in _lib_cache:
+        return _lib_cache[path]
+    if not os.path.exists(path):
+        build(path)
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.oracle_output_hw.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(ctypes.c_int64),
+                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.oracle_output_hw.restype = ctypes.c_int
+    lib.oracle_forward.argtypes = [ctypes.POINTER(_Desc), P, P, P, P, P, ctypes.c_int64,
+                                   ctypes.c_int64, P, P, ctypes.c_int]
+    lib.oracle_forward.restype = ctypes.c_int
+    lib.oracle_points.argtypes = [ctypes.POINTER(_Desc), P, P, P, P, P, P, ctypes.c_int64, P, P,
+                                  ctypes.c_int]
+    lib.oracle_points.restype = ctypes.c_int
+    lib.oracle_threads.argtypes = [ctypes.c_int]
+    lib.oracle_threads.restype = ctypes.c_int
+    _lib_cache[path] = lib
+    return lib
+
+
+def _f32(a):
+    """Host float32 C-contiguous copy of an array-like (numpy or torch CPU)."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor: widen (bf16 -> fp32 is exact) on the host
+        a = a.detach().to("cpu").float().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _desc(x, weight, stride, pad, dilation):
+    B, Cin, H, W = x.shape
+    Cout, Cin_w, K, K2 = weight.shape
+    if Cin_w != Cin or K != K2:
+        raise ValueError("weight must be [Cout, Cin, K, K] with Cin matching x")
+    return _Desc(B, Cin, H, W, Cout, K, stride, pad, dilation)
+
+
+def output_hw(B, Cin, H, W, Cout, K, stride=1, pad=0, dilation=1, lib_path: str = LIB):
+    lib = load(lib_path)
+    ho, wo = ctypes.c_int64(), ctypes.c_int64()
+    rc = lib.oracle_output_hw(ctypes.byref(_Desc(B, Cin, H, W, Cout, K, stride, pad, dilation)),
+                              ctypes.byref(ho), ctypes.byref(wo))
+    if rc != 0:
+        raise ValueError("invalid geometry")
+    return ho.value, wo.value
+
+
+def _check(x, offset, mask, weight, bias, d, Ho, Wo):
+    KK = d.K * d.K
+    if offset.shape != (d.B, 2 * KK, Ho, Wo):
+        raise ValueError(f"offset must be {(d.B, 2 * KK, Ho, Wo)}, got {offset.shape}")
+    if mask is not None and mask.shape != (d.B, KK, Ho, Wo):
+        raise ValueError(f"mask must be {(d.B, KK, Ho, Wo)}, got {mask.shape}")
+    if bias is not None and bias.shape != (d.Cout,):
+        raise ValueError("bias must be [Cout]")
+
+
+def forward(x, offset, weight, bias=None, stride=1, padding=0, dilation=1, mask=None,
+            cout_range=None, threads=0, with_abs=True, lib_path: str = LIB):
+    """y (and sum of |terms|) for the full output grid, float64 [B, Cout', Ho, Wo].
+
+    ``cout_range=(o0, o1)`` restricts the output channels computed.
+    """
+    lib = load(lib_path)
+    x, offset, weight, bias, mask = map(_f32, (x, offset, weight, bias, mask))
+    d = _desc(x, weight, stride, padding, dilation)
+    Ho, Wo = output_hw(d.B, d.Cin, d.H, d.W, d.Cout, d.K, stride, padding, dilation, lib_path)
+    _check(x, offset, mask, weight, bias, d, Ho, Wo)
+    o0, o1 = (0, d.Cout) if cout_range is None else cout_range
+    out = np.empty((d.B, o1 - o0, Ho, Wo), dtype=np.float64)
+    ab = np.empty_like(out) if with_abs else None
+    rc = lib.oracle_forward(ctypes.byref(d), _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight),
+                            _ptr(bias), o0, o1, _ptr(out), _ptr(ab), threads)
+    if rc != 0:
+        raise ValueError("oracle_forward rejected its arguments")
+    return (out, ab) if with_abs else out
+
+
+def points(x, offset, weight, pts, bias=None, stride=1, padding=0, dilation=1, mask=None,
+           threads=0, lib_path: str = LIB):
+    """y and sum of |terms| at individual outputs; pts is an int array [n, 4] of (b, o, oy, ox)."""
+    lib = load(lib_path)
+    x, offset, weight, bias, mask = map(_f32, (x, offset, weight, bias, mask))
+    d = _desc(x, weight, stride, padding, dilation)
+    Ho, Wo = output_hw(d.B, d.Cin, d.H, d.W, d.Cout, d.K, stride, padding, dilation, lib_path)
+    _check(x, offset, mask, weight, bias, d, Ho, Wo)
+    pts = np.ascontiguousarray(np.asarray(pts, dtype=np.int64).reshape(-1, 4))
+    out = np.empty(len(pts), dtype=np.float64)
+    ab = np.empty(len(pts), dtype=np.float64)
+    rc = lib.oracle_points(ctypes.byref(d), _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight),
+                           _ptr(bias), _ptr(pts), len(pts), _ptr(out), _ptr(ab), threads)
+    if rc != 0:
+        raise ValueError("oracle_points rejected its arguments")
+    return out, ab
+
+
+def threads_used(threads: int = 0, lib_path: str = LIB) -> int:
+    return load(lib_path).oracle_threads(threads)

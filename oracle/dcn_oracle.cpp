@@ -1,0 +1,165 @@
+// dcn_oracle.cpp -- plain CPU oracle for the modulated deformable convolution
+// forward.  TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and
+// the bench's CPU-baseline leg, never by the product path.
+//
+// The definition is stated in dcn_oracle.h.  This file writes it out as a
+// plain loop over (b, cout, oy, ox, cin, k) with the bilinear sample spelled
+// out in the innermost step, in double precision, with no blocking, caching
+// or reordering.  OpenMP splits the outermost (b, cout) pairs across threads;
+// each output element is produced by exactly one thread, so the result does
+// not depend on the thread count.
+
+#include "dcn_oracle.h"
+
+#include <cmath>
+#include <cstddef>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+bool valid_desc(const oracle_desc* d) {
+  if (d == nullptr) return false;
+  if (d->B < 0 || d->Cout < 0) return false;
+  if (d->Cin < 1 || d->H < 1 || d->W < 1 || d->K < 1) return false;
+  if (d->stride < 1 || d->dilation < 1 || d->pad < 0) return false;
+  return true;
+}
+
+// Output size of a strided, padded, dilated window (torchvision's
+// deform_conv2d parameter table: stride, padding and dilation act as in a
+// regular convolution).
+int64_t out_size(int64_t in, int64_t K, int64_t stride, int64_t pad, int64_t dil) {
+  const int64_t span = in + 2 * pad - dil * (K - 1) - 1;
+  if (span < 0) return 0;
+  return span / stride + 1;
+}
+
+// Value of one input plane at the fractional position (py, px): the four
+// integer neighbours, each weighted by (1-|py-yy|)*(1-|px-xx|) (the areas of
+// the bilinear-interpolation equation), a neighbour outside the plane
+// counting as zero.  Returns the sample; inside tests use floating compares
+// before any integer conversion, so NaN and infinite positions give zero.
+double bilinear_zero_outside(const float* plane, int64_t H, int64_t W, double py, double px) {
+  const double y0 = std::floor(py);
+  const double x0 = std::floor(px);
+  double acc = 0.0;
+  for (int dy = 0; dy < 2; ++dy) {
+    const double yy = y0 + dy;
+    if (!(yy >= 0.0 && yy <= static_cast<double>(H - 1))) continue;
+    for (int dx = 0; dx < 2; ++dx) {
+      const double xx = x0 + dx;
+      if (!(xx >= 0.0 && xx <= static_cast<double>(W - 1))) continue;
+      const double g = (1.0 - std::fabs(py - yy)) * (1.0 - std::fabs(px - xx));
+      const int64_t iy = static_cast<int64_t>(yy);
+      const int64_t ix = static_cast<int64_t>(xx);
+      acc += g * static_cast<double>(plane[iy * W + ix]);
+    }
+  }
+  return acc;
+}
+
+// One output element y[b,o,oy,ox] and its sum of |terms|.
+void one_output(const oracle_desc* d, int64_t Ho, int64_t Wo, const float* x,
+                const float* offset, const float* mask, const float* weight,
+                const float* bias, int64_t b, int64_t o, int64_t oy, int64_t ox,
+                double* y_out, double* abs_out) {
+  const int64_t K = d->K, KK = K * K;
+  double y = 0.0, a = 0.0;
+  if (bias != nullptr) {
+    y = static_cast<double>(bias[o]);
+    a = std::fabs(y);
+  }
+  for (int64_t c = 0; c < d->Cin; ++c) {
+    const float* plane = x + ((b * d->Cin + c) * d->H) * d->W;
+    for (int64_t k = 0; k < KK; ++k) {
+      const int64_t i = k / K, j = k % K;
+      const double dy = offset[((b * 2 * KK + 2 * k) * Ho + oy) * Wo + ox];
+      const double dx = offset[((b * 2 * KK + 2 * k + 1) * Ho + oy) * Wo + ox];
+      const double py = static_cast<double>(oy * d->stride - d->pad + i * d->dilation) + dy;
+      const double px = static_cast<double>(ox * d->stride - d->pad + j * d->dilation) + dx;
+      const double m = (mask != nullptr) ? static_cast<double>(mask[((b * KK + k) * Ho + oy) * Wo + ox]) : 1.0;
+      const double w = weight[((o * d->Cin + c) * K + i) * K + j];
+      const double term = w * m * bilinear_zero_outside(plane, d->H, d->W, py, px);
+      y += term;
+      a += std::fabs(term);
+    }
+  }
+  *y_out = y;
+  if (abs_out != nullptr) *abs_out = a;
+}
+
+}  // namespace
+
+extern "C" int oracle_output_hw(const oracle_desc* d, int64_t* Ho, int64_t* Wo) {
+  if (!valid_desc(d) || Ho == nullptr || Wo == nullptr) return -1;
+  const int64_t ho = out_size(d->H, d->K, d->stride, d->pad, d->dilation);
+  const int64_t wo = out_size(d->W, d->K, d->stride, d->pad, d->dilation);
+  if (ho < 1 || wo < 1) return -1;
+  *Ho = ho;
+  *Wo = wo;
+  return 0;
+}
+
+extern "C" int oracle_threads(int threads) {
+#ifdef _OPENMP
+  return threads > 0 ? threads : omp_get_max_threads();
+#else
+  (void)threads;
+  return 1;
+#endif
+}
+
+extern "C" int oracle_forward(const oracle_desc* d, const float* x, const float* offset,
+                              const float* mask, const float* weight, const float* bias,
+                              int64_t cout_begin, int64_t cout_end,
+                              double* out, double* abs_terms, int threads) {
+  int64_t Ho = 0, Wo = 0;
+  if (oracle_output_hw(d, &Ho, &Wo) != 0) return -1;
+  if (x == nullptr || offset == nullptr || weight == nullptr || out == nullptr) return -1;
+  if (cout_begin < 0 || cout_end > d->Cout || cout_begin > cout_end) return -1;
+  const int64_t B = d->B, nO = cout_end - cout_begin;
+  const int nthreads = oracle_threads(threads);
+  (void)nthreads;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t oo = 0; oo < nO; ++oo) {
+      const int64_t o = cout_begin + oo;
+      for (int64_t oy = 0; oy < Ho; ++oy) {
+        for (int64_t ox = 0; ox < Wo; ++ox) {
+          const int64_t idx = ((b * nO + oo) * Ho + oy) * Wo + ox;
+          one_output(d, Ho, Wo, x, offset, mask, weight, bias, b, o, oy, ox,
+                     &out[idx], abs_terms != nullptr ? &abs_terms[idx] : nullptr);
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+extern "C" int oracle_points(const oracle_desc* d, const float* x, const float* offset,
+                             const float* mask, const float* weight, const float* bias,
+                             const int64_t* points, int64_t npts,
+                             double* out, double* abs_terms, int threads) {
+  int64_t Ho = 0, Wo = 0;
+  if (oracle_output_hw(d, &Ho, &Wo) != 0) return -1;
+  if (x == nullptr || offset == nullptr || weight == nullptr || out == nullptr) return -1;
+  if (npts < 0 || (npts > 0 && points == nullptr)) return -1;
+  for (int64_t p = 0; p < npts; ++p) {
+    const int64_t* q = points + 4 * p;
+    if (q[0] < 0 || q[0] >= d->B || q[1] < 0 || q[1] >= d->Cout || q[2] < 0 || q[2] >= Ho ||
+        q[3] < 0 || q[3] >= Wo)
+      return -1;
+  }
+  const int nthreads = oracle_threads(threads);
+  (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+  for (int64_t p = 0; p < npts; ++p) {
+    const int64_t* q = points + 4 * p;
+    one_output(d, Ho, Wo, x, offset, mask, weight, bias, q[0], q[1], q[2], q[3], &out[p],
+               abs_terms != nullptr ? &abs_terms[p] : nullptr);
+  }
+  return 0;
+}

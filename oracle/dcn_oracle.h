@@ -1,0 +1,86 @@
+/*
+ * dcn_oracle.h -- CPU oracle for the modulated deformable convolution forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  The product path never calls it and
+ * shares no code, header, table or helper with it.
+ *
+ * What it computes (written out from the pages' definitions):
+ *
+ *   y[b,o,oy,ox] = bias[o] + sum_{c<Cin} sum_{k<K*K} W[o,c,i,j] * m_k * S(X[b,c], py_k, px_k)
+ *      i = k / K, j = k % K            (kernel point k in row-major order)
+ *      py_k = oy*stride - pad + i*dilation + offset[b, 2k,   oy, ox]
+ *      px_k = ox*stride - pad + j*dilation + offset[b, 2k+1, oy, ox]
+ *      m_k  = mask[b, k, oy, ox]       (1 when mask is NULL: DCNv1)
+ *      S(X, py, px) = sum over the four integer neighbours (yy, xx) of (py, px),
+ *                     yy in {floor(py), floor(py)+1}, xx in {floor(px), floor(px)+1},
+ *                     of (1-|py-yy|)*(1-|px-xx|) * X[yy, xx], where a neighbour
+ *                     outside [0,H) x [0,W) contributes zero.
+ *
+ *   abs_terms[b,o,oy,ox] = |bias[o]| + sum_{c,k} |W[o,c,i,j] * m_k * S(...)|
+ *
+ * Sources:
+ *  - regular grid R and the deformable-convolution equation: csdn.net tags page
+ *    "可变形卷积：Deformable ConvNets", part "Deformable Convolutional Networks",
+ *    section 可变形卷积 (grid R, regular-conv and deformable-conv equations);
+ *  - the modulation scalar per sampling point: same page, DCNv2 section 3.2,
+ *    and the DCNv2 formula on un.csdn.net/5xxxf43i9i (section 自行实现方法);
+ *  - bilinear interpolation from the four neighbours: same csdn tags page,
+ *    section 可变形卷积Pytorch实现, bilinear-interpolation equation (areas S1..S4);
+ *  - stride / padding / dilation as in torchvision's deform_conv2d parameter
+ *    table on agent.csdn.net/6a744b3d10ee7a33f2973402.html, section 2.1.
+ * Readings taken where the pages are silent or disagree: offset channel 2k is
+ * the row displacement dy and 2k+1 the column displacement dx; a neighbour
+ * outside the image counts as zero (no clamping); the upper neighbour is
+ * floor+1 (not ceil, which would lose the sample at integer positions);
+ * offsets are in input pixels, never scaled by stride or dilation; one offset
+ * group shared by all input channels.
+ *
+ * Arithmetic: inputs arrive as float (already rounded to the element type the
+ * caller uses); every position, weight, product and sum is formed in double.
+ * Positions are tested against the image with floating compares before any
+ * conversion to an integer, so NaN, +-Inf and huge offsets contribute zero.
+ *
+ * All pointers are host pointers to contiguous row-major arrays:
+ *   x[B,Cin,H,W], offset[B,2K^2,Ho,Wo], mask[B,K^2,Ho,Wo] or NULL,
+ *   weight[Cout,Cin,K,K], bias[Cout] or NULL.
+ * Return value: 0 on success, -1 on an invalid argument.
+ */
+#ifndef DCN_ORACLE_H
+#define DCN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct oracle_desc {
+  int64_t B, Cin, H, W, Cout, K, stride, pad, dilation;
+} oracle_desc;
+
+/* Ho = floor((H + 2*pad - dilation*(K-1) - 1) / stride) + 1, likewise Wo. */
+int oracle_output_hw(const oracle_desc* d, int64_t* Ho, int64_t* Wo);
+
+/* Full output grid for output channels [cout_begin, cout_end).
+ * out and abs_terms are [B, cout_end-cout_begin, Ho, Wo] doubles.
+ * abs_terms may be NULL.  threads <= 0 means the OpenMP default. */
+int oracle_forward(const oracle_desc* d, const float* x, const float* offset,
+                   const float* mask, const float* weight, const float* bias,
+                   int64_t cout_begin, int64_t cout_end,
+                   double* out, double* abs_terms, int threads);
+
+/* Individual outputs: points is npts rows of (b, o, oy, ox). */
+int oracle_points(const oracle_desc* d, const float* x, const float* offset,
+                  const float* mask, const float* weight, const float* bias,
+                  const int64_t* points, int64_t npts,
+                  double* out, double* abs_terms, int threads);
+
+/* Number of threads an oracle_forward call with this request would use. */
+int oracle_threads(int threads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,321 @@
+"""Checks that pin the CPU oracle to facts fixed outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle library at
+``lib`` disagrees with what the pages and the mathematics fix.  The tests run
+them against the real oracle (all must pass) and against copies of the oracle
+with a mistake planted on purpose (at least one must fail for each).
+
+What each pin reduces to (no pin restates the oracle's own formula):
+  p1  zero offsets, mask 1   -> a separate direct-convolution loop and torch conv2d
+  p2  integer offsets        -> shifted convolution by integer indexing
+  p3  bilinear input field   -> closed form alpha+beta*y+gamma*x+delta*x*y at the position
+  p4  every sample outside   -> bias exactly
+  p5  linear in the mask     -> homogeneity and additivity
+  p6  mask absent            -> identical to mask of ones
+  p7  offsets (+.5, +.5)     -> mean of the four neighbours
+  p8  constant input         -> C * sum of W*m, plus bias
+  p9  general offsets        -> torch grid_sample (bilinear, zero padding, align_corners)
+                                per kernel point, then a contraction with W
+  p10 NaN / Inf / 1e30 offsets -> that sample contributes zero
+  golden                      -> hand-worked examples in tests/golden/
+"""
+
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def out_hw(H, W, K, s, p, d):
+    """Output size of a regular strided convolution (textbook formula)."""
+    return (H + 2 * p - d * (K - 1) - 1) // s + 1, (W + 2 * p - d * (K - 1) - 1) // s + 1
+
+
+def rand_case(rng, B, Cin, H, W, Cout, K, s, p, d, offset_scale=1.5, mask=True, bias=True):
+    Ho, Wo = out_hw(H, W, K, s, p, d)
+    x = rng.standard_normal((B, Cin, H, W)).astype(np.float32)
+    w = rng.standard_normal((Cout, Cin, K, K)).astype(np.float32)
+    off = (rng.standard_normal((B, 2 * K * K, Ho, Wo)) * offset_scale).astype(np.float32)
+    m = rng.uniform(0.0, 1.0, (B, K * K, Ho, Wo)).astype(np.float32) if mask else None
+    b = rng.standard_normal(Cout).astype(np.float32) if bias else None
+    return x, off, m, w, b, Ho, Wo
+
+
+def direct_conv(x, w, b, s, p, d):
+    """Regular convolution, written as the textbook loop on a zero-padded input."""
+    B, Cin, H, W = x.shape
+    Cout, _, K, _ = w.shape
+    Ho, Wo = out_hw(H, W, K, s, p, d)
+    xp = np.zeros((B, Cin, H + 2 * p, W + 2 * p))
+    xp[:, :, p:p + H, p:p + W] = x
+    y = np.zeros((B, Cout, Ho, Wo))
+    for oy in range(Ho):
+        for ox in range(Wo):
+            patch = xp[:, :, oy * s:oy * s + d * (K - 1) + 1:d, ox * s:ox * s + d * (K - 1) + 1:d]
+            y[:, :, oy, ox] = np.einsum("bcij,ocij->bo", patch, w.astype(np.float64))
+    if b is not None:
+        y += b[None, :, None, None]
+    return y
+
+
+def _close(a, b, tol, what):
+    err = np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max error {err:.3e} > {tol:.1e}"
+
+
+def pin_p1_zero_offsets(lib):
+    rng = np.random.default_rng(11)
+    for K in (1, 3, 5):
+        for s in (1, 2, 3):
+            for p in (0, 1, 2):
+                for d in (1, 2):
+                    H, W = 9, 8
+                    if out_hw(H, W, K, s, p, d)[0] < 1 or out_hw(H, W, K, s, p, d)[1] < 1:
+                        continue
+                    x, off, _, w, b, Ho, Wo = rand_case(rng, 2, 3, H, W, 4, K, s, p, d)
+                    off[:] = 0.0
+                    y = oracle.forward(x, off, w, b, s, p, d, mask=None, with_abs=False, lib_path=lib)
+                    _close(y, direct_conv(x, w, b, s, p, d), 1e-12, f"p1 loop K{K} s{s} p{p} d{d}")
+                    ref = F.conv2d(torch.from_numpy(x).double(), torch.from_numpy(w).double(),
+                                   torch.from_numpy(b).double(), stride=s, padding=p, dilation=d)
+                    _close(y, ref.numpy(), 1e-12, f"p1 conv2d K{K} s{s} p{p} d{d}")
+
+
+def pin_p2_integer_offsets(lib):
+    rng = np.random.default_rng(12)
+    for (K, s, p, d) in [(3, 1, 1, 1), (3, 2, 1, 1), (2, 1, 0, 2), (3, 1, 2, 2)]:
+        B, Cin, H, W, Cout = 2, 3, 7, 9, 3
+        x, _, m, w, b, Ho, Wo = rand_case(rng, B, Cin, H, W, Cout, K, s, p, d)
+        off = rng.integers(-3, 4, (B, 2 * K * K, Ho, Wo)).astype(np.float32)
+        y, a = oracle.forward(x, off, w, b, s, p, d, mask=m, lib_path=lib)
+        # shifted convolution: read the integer position from a zero-padded copy
+        M = 3 + p + d * K + 1
+        xp = np.zeros((B, Cin, H + 2 * M, W + 2 * M))
+        xp[:, :, M:M + H, M:M + W] = x
+        ref = np.zeros((B, Cout, Ho, Wo))
+        ref_abs = np.zeros((B, Cout, Ho, Wo))
+        oy, ox = np.meshgrid(np.arange(Ho), np.arange(Wo), indexing="ij")
+        for bb in range(B):
+            for k in range(K * K):
+                i, j = divmod(k, K)
+                yy = oy * s - p + i * d + off[bb, 2 * k].astype(np.int64)
+                xx = ox * s - p + j * d + off[bb, 2 * k + 1].astype(np.int64)
+                vals = xp[bb][:, yy + M, xx + M]                        # [Cin, Ho, Wo]
+                wk, mk = w[:, :, i, j].astype(np.float64), m[bb, k].astype(np.float64)
+                ref[bb] += np.einsum("chw,oc,hw->ohw", vals, wk, mk)
+                ref_abs[bb] += np.einsum("chw,oc,hw->ohw", np.abs(vals), np.abs(wk), np.abs(mk))
+        ref += b[None, :, None, None]
+        ref_abs += np.abs(b)[None, :, None, None]
+        _close(y, ref, 1e-12, f"p2 K{K} s{s} p{p} d{d}")
+        _close(a, ref_abs, 1e-12, f"p2 sum of |terms| K{K} s{s} p{p} d{d}")
+
+
+def pin_p3_bilinear_field(lib):
+    """X = a + b*y + c*x + e*x*y is reproduced exactly by bilinear interpolation."""
+    rng = np.random.default_rng(13)
+    B, Cin, H, W, Cout, K, s, p, d = 1, 2, 12, 13, 3, 3, 1, 0, 2
+    Ho, Wo = out_hw(H, W, K, s, p, d)
+    coef = rng.integers(-2, 3, (Cin, 4)).astype(np.float64)
+    yy, xx = np.meshgrid(np.arange(H, dtype=np.float64), np.arange(W, dtype=np.float64), indexing="ij")
+    x = np.stack([c[0] + c[1] * yy + c[2] * xx + c[3] * xx * yy for c in coef])[None].astype(np.float32)
+    w = rng.integers(-3, 4, (Cout, Cin, K, K)).astype(np.float32)
+    m = (rng.integers(0, 5, (B, K * K, Ho, Wo)) / 4.0).astype(np.float32)
+    ref = np.zeros((B, Cout, Ho, Wo))
+    oy, ox = np.meshgrid(np.arange(Ho), np.arange(Wo), indexing="ij")
+    off = np.zeros((B, 2 * K * K, Ho, Wo), dtype=np.float32)
+    for k in range(K * K):
+        i, j = divmod(k, K)
+        by, bx = oy * s - p + i * d, ox * s - p + j * d
+        # dyadic offsets keeping the position inside [0,H-1] x [0,W-1]
+        py = np.clip(by + rng.integers(-96, 97, by.shape) / 64.0, 0, H - 1)
+        px = np.clip(bx + rng.integers(-96, 97, bx.shape) / 64.0, 0, W - 1)
+        off[0, 2 * k], off[0, 2 * k + 1] = py - by, px - bx
+        field = np.stack([c[0] + c[1] * py + c[2] * px + c[3] * px * py for c in coef])   # [Cin,Ho,Wo]
+        ref[0] += np.einsum("chw,oc,hw->ohw", field, w[:, :, i, j].astype(np.float64), m[0, k])
+    y = oracle.forward(x, off, w, None, s, p, d, mask=m, with_abs=False, lib_path=lib)
+    _close(y, ref, 1e-12, "p3 bilinear field")
+
+
+def pin_p4_all_outside(lib):
+    rng = np.random.default_rng(14)
+    H, W = 6, 7
+    x, off, m, w, b, Ho, Wo = rand_case(rng, 2, 3, H, W, 4, 3, 1, 1, 1)
+    bias = np.broadcast_to(b.astype(np.float64)[None, :, None, None], (2, 4, Ho, Wo))
+    for dy, dx in ((100.25, None), (None, -100.25), (-11.0, None), (None, 3e4)):
+        o = off.copy()
+        if dy is not None:
+            o[:, 0::2] = dy
+        if dx is not None:
+            o[:, 1::2] = dx
+        y, a = oracle.forward(x, o, w, b, 1, 1, 1, mask=m, lib_path=lib)
+        assert np.array_equal(y, bias), f"p4 dy={dy} dx={dx}: output is not the bias"
+        assert np.array_equal(a, np.abs(bias)), f"p4 dy={dy} dx={dx}: abs terms are not |bias|"
+    # every row position exactly H (one past the last row) or exactly -1: the sample is zero
+    for target in (float(H), -1.0):
+        o = off.copy()
+        oy = np.arange(Ho)[None, :, None]
+        for k in range(9):
+            i = k // 3
+            o[:, 2 * k] = (target - (oy - 1 + i)).astype(np.float32)
+        y = oracle.forward(x, o, w, b, 1, 1, 1, mask=m, with_abs=False, lib_path=lib)
+        assert np.array_equal(y, bias), f"p4 row position exactly {target}: must contribute zero"
+
+
+def pin_p5_linear_in_mask(lib):
+    rng = np.random.default_rng(15)
+    x, off, m, w, b, Ho, Wo = rand_case(rng, 1, 4, 8, 9, 3, 3, 2, 1, 1)
+    m2 = rng.uniform(0, 1, m.shape).astype(np.float32)
+    f = lambda mm: oracle.forward(x, off, w, b, 2, 1, 1, mask=mm, with_abs=False, lib_path=lib)
+    bb = b.astype(np.float64)[None, :, None, None]
+    y1, y2, y12 = f(m), f(m2), f((m.astype(np.float64) + m2).astype(np.float32))
+    msum_exact = np.array_equal((m.astype(np.float64) + m2).astype(np.float32).astype(np.float64),
+                                m.astype(np.float64) + m2)
+    y2m = f(2.0 * m)
+    _close(y2m - bb, 2.0 * (y1 - bb), 1e-12, "p5 homogeneity")
+    if msum_exact:
+        _close(y12 - bb, (y1 - bb) + (y2 - bb), 1e-12, "p5 additivity")
+    else:
+        _close(y12 - bb, (y1 - bb) + (y2 - bb), 1e-6, "p5 additivity (rounded mask sum)")
+    y0 = f(np.zeros_like(m))
+    assert np.array_equal(y0, np.broadcast_to(bb, y0.shape)), "p5 mask 0 must give the bias"
+
+
+def pin_p6_mask_absent(lib):
+    rng = np.random.default_rng(16)
+    x, off, m, w, b, Ho, Wo = rand_case(rng, 2, 3, 7, 8, 3, 3, 1, 1, 1)
+    y_none, a_none = oracle.forward(x, off, w, b, 1, 1, 1, mask=None, lib_path=lib)
+    y_one, a_one = oracle.forward(x, off, w, b, 1, 1, 1, mask=np.ones_like(m), lib_path=lib)
+    assert np.array_equal(y_none, y_one) and np.array_equal(a_none, a_one), "p6 mask None != ones"
+
+
+def pin_p7_half_offsets(lib):
+    rng = np.random.default_rng(17)
+    B, Cin, H, W, Cout, K, s, p, d = 1, 3, 8, 9, 2, 3, 1, 0, 1
+    x, off, m, w, b, Ho, Wo = rand_case(rng, B, Cin, H, W, Cout, K, s, p, d)
+    off[:] = 0.5
+    # choose an output region whose every neighbour is inside (pad 0 and one-pixel margin)
+    y = oracle.forward(x, off, w, b, s, p, d, mask=m, with_abs=False, lib_path=lib)
+    xd = x.astype(np.float64)
+    mean4 = (xd[:, :, :-1, :-1] + xd[:, :, 1:, :-1] + xd[:, :, :-1, 1:] + xd[:, :, 1:, 1:]) / 4.0
+    ref = np.zeros_like(y)
+    for k in range(K * K):
+        i, j = divmod(k, K)
+        hh, ww = min(Ho, mean4.shape[2] - i), min(Wo, mean4.shape[3] - j)
+        ref[:, :, :hh, :ww] += np.einsum("bchw,oc,bhw->bohw", mean4[:, :, i:i + hh, j:j + ww],
+                                         w[:, :, i, j].astype(np.float64), m[:, k, :hh, :ww])
+    ref += b[None, :, None, None]
+    hh, ww = H - 1 - (K - 1), W - 1 - (K - 1)
+    _close(y[:, :, :hh, :ww], ref[:, :, :hh, :ww], 1e-12, "p7 half-pixel mean")
+
+
+def pin_p8_constant_input(lib):
+    rng = np.random.default_rng(18)
+    B, Cin, H, W, Cout, K, s, p, d = 2, 3, 10, 11, 4, 3, 1, 0, 1
+    x, off, m, w, b, Ho, Wo = rand_case(rng, B, Cin, H, W, Cout, K, s, p, d)
+    C = 1.75
+    x[:] = C
+    oy, ox = np.meshgrid(np.arange(Ho), np.arange(Wo), indexing="ij")
+    for k in range(K * K):   # keep every position inside
+        i, j = divmod(k, K)
+        by, bx = oy * s - p + i * d, ox * s - p + j * d
+        off[:, 2 * k] = np.clip(by + off[:, 2 * k], 0, H - 1) - by
+        off[:, 2 * k + 1] = np.clip(bx + off[:, 2 * k + 1], 0, W - 1) - bx
+    y = oracle.forward(x, off, w, b, s, p, d, mask=m, with_abs=False, lib_path=lib)
+    wk = w.reshape(Cout, Cin, K * K).astype(np.float64).sum(1)          # [Cout, K^2]
+    ref = C * np.einsum("ok,bkhw->bohw", wk, m.astype(np.float64)) + b[None, :, None, None]
+    _close(y, ref, 1e-12, "p8 constant input")
+
+
+def grid_sample_formulation(x, off, m, w, b, s, p, d):
+    """The whole operation via torch grid_sample (bilinear, zeros, align_corners=True)."""
+    B, Cin, H, W = x.shape
+    Cout, _, K, _ = w.shape
+    Ho, Wo = off.shape[2:]
+    xt = torch.from_numpy(x).double()
+    y = torch.zeros((B, Cout, Ho, Wo), dtype=torch.float64)
+    oy, ox = torch.meshgrid(torch.arange(Ho, dtype=torch.float64),
+                            torch.arange(Wo, dtype=torch.float64), indexing="ij")
+    for k in range(K * K):
+        i, j = divmod(k, K)
+        py = oy * s - p + i * d + torch.from_numpy(off[:, 2 * k]).double()
+        px = ox * s - p + j * d + torch.from_numpy(off[:, 2 * k + 1]).double()
+        grid = torch.stack([2.0 * px / (W - 1) - 1.0, 2.0 * py / (H - 1) - 1.0], dim=-1)
+        smp = F.grid_sample(xt, grid, mode="bilinear", padding_mode="zeros", align_corners=True)
+        if m is not None:
+            smp = smp * torch.from_numpy(m[:, k]).double()[:, None]
+        y += torch.einsum("bchw,oc->bohw", smp, torch.from_numpy(w[:, :, i, j]).double())
+    if b is not None:
+        y += torch.from_numpy(b).double()[None, :, None, None]
+    return y.numpy()
+
+
+def pin_p9_grid_sample(lib, cases=None):
+    rng = np.random.default_rng(19)
+    if cases is None:
+        cases = [(1, 3, 5, 6, 2, 3, 1, 1, 1), (2, 4, 9, 7, 3, 3, 2, 1, 1), (1, 2, 8, 8, 3, 5, 1, 2, 1),
+                 (2, 3, 11, 10, 4, 3, 1, 2, 2), (1, 5, 6, 9, 2, 2, 3, 0, 1), (1, 3, 2, 2, 2, 1, 1, 0, 1)]
+    for (B, Cin, H, W, Cout, K, s, p, d) in cases:
+        for mask in (True, False):
+            x, off, m, w, b, Ho, Wo = rand_case(rng, B, Cin, H, W, Cout, K, s, p, d,
+                                                 offset_scale=2.5, mask=mask, bias=mask)
+            y = oracle.forward(x, off, w, b, s, p, d, mask=m, with_abs=False, lib_path=lib)
+            ref = grid_sample_formulation(x, off, m, w, b, s, p, d)
+            _close(y, ref, 1e-10, f"p9 {(B, Cin, H, W, Cout, K, s, p, d)} mask={mask}")
+
+
+def pin_p10_nonfinite_offsets(lib):
+    rng = np.random.default_rng(20)
+    x, off, m, w, b, Ho, Wo = rand_case(rng, 2, 3, 7, 8, 3, 3, 1, 1, 1)
+    bad = rng.uniform(size=(2, 9, Ho, Wo)) < 0.3
+    specials = np.array([np.nan, np.inf, -np.inf, 1e30, -1e30, 3e38], dtype=np.float32)
+    o = off.copy()
+    pick = rng.integers(0, len(specials), bad.shape)
+    which = rng.integers(0, 3, bad.shape)    # 0: dy bad, 1: dx bad, 2: both
+    for k in range(9):
+        sel = bad[:, k]
+        val = specials[pick[:, k]]
+        o[:, 2 * k][sel & (which[:, k] != 1)] = val[sel & (which[:, k] != 1)]
+        o[:, 2 * k + 1][sel & (which[:, k] != 0)] = val[sel & (which[:, k] != 0)]
+    m0 = m.copy()
+    m0[bad] = 0.0
+    y_bad, a_bad = oracle.forward(x, o, w, b, 1, 1, 1, mask=m, lib_path=lib)
+    y_ref, a_ref = oracle.forward(x, off, w, b, 1, 1, 1, mask=m0, lib_path=lib)
+    assert np.all(np.isfinite(y_bad)), "p10: non-finite offsets leaked into the output"
+    _close(y_bad, y_ref, 1e-12, "p10 non-finite offsets contribute zero")
+    _close(a_bad, a_ref, 1e-12, "p10 abs terms")
+
+
+def pin_golden(lib):
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        g = json.load(f)
+    x = np.array(g["x"], dtype=np.float32)[None, None]
+    for ex in g["examples"]:
+        K = ex["K"]
+        Ho, Wo = out_hw(3, 3, K, ex["stride"], ex["pad"], ex["dilation"])
+        w = np.array(ex["weight"], dtype=np.float32)
+        b = None if ex["bias"] is None else np.array(ex["bias"], dtype=np.float32)
+        off = np.zeros((1, 2 * K * K, Ho, Wo), dtype=np.float32)
+        if "offset_dy" in ex:
+            off[0, 0] = ex["offset_dy"]
+            off[0, 1] = ex["offset_dx"]
+        else:
+            for k in range(K * K):
+                off[0, 2 * k, 0, 0] = ex["offset_at_00"][f"k{k}_dy"]
+                off[0, 2 * k + 1, 0, 0] = ex["offset_at_00"][f"k{k}_dx"]
+        m = None if ex["mask"] is None else np.array(ex["mask"], dtype=np.float32)[None, None]
+        y, a = oracle.forward(x, off, w, b, ex["stride"], ex["pad"], ex["dilation"], mask=m, lib_path=lib)
+        assert np.array_equal(y[0, 0], np.array(ex["expected_y"])), f"golden {ex['name']}: {y[0, 0]}"
+        assert np.array_equal(a[0, 0], np.array(ex["expected_abs"])), f"golden {ex['name']} abs"
+
+
+ALL_PINS = [pin_p1_zero_offsets, pin_p2_integer_offsets, pin_p3_bilinear_field, pin_p4_all_outside,
+            pin_p5_linear_in_mask, pin_p6_mask_absent, pin_p7_half_offsets, pin_p8_constant_input,
+            pin_p9_grid_sample, pin_p10_nonfinite_offsets, pin_golden]

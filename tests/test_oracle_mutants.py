@@ -1,0 +1,94 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins catch each.
+
+Every mutant is a textual edit of ``oracle/dcn_oracle.cpp`` compiled to a
+temporary library (CPU only).  Its pins run in a child process, so a mutant
+that reads out of bounds and crashes also counts as caught.  The real oracle
+is never modified.
+"""
+
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, [(old, new), ...]) -- each old string must occur in the source.
+MUTANTS = [
+    ("swap_dy_dx", [("const double dy = offset[((b * 2 * KK + 2 * k) *",
+                     "const double dy = offset[((b * 2 * KK + 2 * k + 1) *"),
+                    ("const double dx = offset[((b * 2 * KK + 2 * k + 1) *",
+                     "const double dx = offset[((b * 2 * KK + 2 * k) *")]),
+    ("ceil_upper_corner", [("const double yy = y0 + dy;",
+                            "const double yy = (dy == 0) ? y0 : std::ceil(py);")]),
+    ("truncate_not_floor", [("const double y0 = std::floor(py);", "const double y0 = std::trunc(py);")]),
+    ("drop_mask", [("(mask != nullptr) ? static_cast<double>", "(false) ? static_cast<double>")]),
+    ("pad_sign", [("oy * d->stride - d->pad", "oy * d->stride + d->pad")]),
+    ("ignore_dilation", [("i * d->dilation", "i")]),
+    ("ignore_stride_x", [("ox * d->stride - d->pad", "ox - d->pad")]),
+    ("weight_ij_transposed", [("((o * d->Cin + c) * K + i) * K + j", "((o * d->Cin + c) * K + j) * K + i")]),
+    ("kernel_points_column_major", [("const int64_t i = k / K, j = k % K;",
+                                     "const int64_t i = k % K, j = k / K;")]),
+    ("drop_one_corner", [("for (int dx = 0; dx < 2; ++dx)", "for (int dx = 0; dx < 1; ++dx)")]),
+    ("complement_weight", [("(1.0 - std::fabs(py - yy))", "std::fabs(py - yy)")]),
+    ("clamp_not_zero", [("if (!(yy >= 0.0 && yy <= static_cast<double>(H - 1))) continue;",
+                         "const double yyc = std::fmin(std::fmax(yy, 0.0), static_cast<double>(H - 1));"),
+                        ("const int64_t iy = static_cast<int64_t>(yy);",
+                         "const int64_t iy = static_cast<int64_t>(yyc);")]),
+    ("inside_bound_off_by_one", [("xx <= static_cast<double>(W - 1)", "xx < static_cast<double>(W - 1)")]),
+    ("drop_bias", [("y = static_cast<double>(bias[o]);", "y = 0.0;")]),
+    ("abs_terms_signed", [("a += std::fabs(term);", "a += term;")]),
+    ("mask_kernel_point_reversed", [("mask[((b * KK + k) * Ho + oy) * Wo + ox]",
+                                     "mask[((b * KK + (KK - 1 - k)) * Ho + oy) * Wo + ox]")]),
+    ("offset_batch_stride", [("offset[((b * 2 * KK + 2 * k) *", "offset[((b * KK + 2 * k) *"),
+                             ("offset[((b * 2 * KK + 2 * k + 1) *", "offset[((b * KK + 2 * k + 1) *")]),
+    ("x_channel_stride", [("x + ((b * d->Cin + c) * d->H) * d->W", "x + ((b * d->Cin + c) * d->W) * d->W")]),
+]
+
+RUNNER = """
+import sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import warnings; warnings.filterwarnings("ignore")
+import pins
+failed = []
+for pin in pins.ALL_PINS:
+    try:
+        pin({lib!r})
+    except AssertionError as e:
+        failed.append(pin.__name__)
+        break
+print("CAUGHT" if failed else "SURVIVED", failed)
+sys.exit(0)
+"""
+
+
+def _run_mutant(name, edits, workdir):
+    with open(oracle.SRC) as f:
+        src = f.read()
+    for old, new in edits:
+        assert old in src, f"mutant {name}: pattern not found: {old}"
+        src = src.replace(old, new)
+    path = os.path.join(workdir, f"{name}.cpp")
+    with open(path, "w") as f:
+        f.write(src)
+    lib = os.path.join(workdir, f"lib_{name}.so")
+    oracle.build(lib, src=path)
+    code = RUNNER.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=lib)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "OMP_NUM_THREADS": "1"})
+    if r.returncode != 0:       # crashed (e.g. an out-of-bounds read): caught
+        return name, "CAUGHT(crash)"
+    return name, r.stdout.strip()
+
+
+def test_every_planted_mistake_is_caught():
+    with tempfile.TemporaryDirectory() as wd:
+        with ThreadPoolExecutor(max_workers=6) as ex:
+            results = list(ex.map(lambda m: _run_mutant(m[0], m[1], wd), MUTANTS))
+    survivors = [(n, r) for n, r in results if not r.startswith("CAUGHT")]
+    assert not survivors, f"mutants not caught by any pin: {survivors}"
