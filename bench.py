@@ -1,0 +1,229 @@
+"""Benchmark of the deformable convolution forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--all] [--no-cpu]
+
+One step = one full dcn_forward (staging launch + fused launch) over the
+workload's synthetic inputs, which are resident in HBM before timing starts.
+The default workload is the ResNet-50 c4 downsampling layer (bf16, B=2,
+Cin=Cout=256, 100x168 input, 3x3, stride 2, pad 1 -> 50x84).  Prints one JSON
+line; with --all, one line per named workload (the first line is still the
+headline workload).
+
+value       = effective TFLOP/s of the whole step, 2*B*Cout*Ho*Wo*Cin*K^2 / step time
+roofline    = the fused kernel alone: algorithmic flops per launch / its mean duration
+              (HIP events on the stream it is launched on), against the dense MFMA
+              peak of the element type (HBM peak for the fp32 single-image workload)
+cpu_baseline = the CPU oracle on a bounded slice of the same workload (a range of
+              output channels), scaled to TFLOP/s, with the threads it used
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16_mfma": 2516.6, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, TFLOP/s, GB/s
+KERNEL_SRC = os.path.join(ROOT, "deformable_convolution_vision_amd", "csrc", "dcn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per fused launch from the committed counter runs, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(workload)
+    if not entry or entry.get("kernel_sha") != kernel_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: float):
+    import numpy as np
+    import torch
+
+    import deformable_convolution_vision_amd as dcn
+    from deformable_convolution_vision_amd.workloads import WORKLOADS, generate
+
+    w = WORKLOADS[name]
+    host = generate(w)
+    g = {k: (None if v is None else v.cuda()) for k, v in host.items()}
+    desc = dcn.describe(g["x"], g["weight"], w.stride, w.pad, w.dilation)
+    Ho, Wo = dcn.check_tensors(desc, g["x"], g["offset"], g["weight"], g["bias"], g["mask"])
+    assert (Ho, Wo) == (w.Ho, w.Wo)
+    nb = dcn.dcn_workspace_bytes(desc)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.B, w.Cout, Ho, Wo), dtype=g["x"].dtype, device="cuda")
+    variant = dcn.dcn_variant_name(desc)
+    stream = torch.cuda.current_stream()
+    wsp = ws if nb else None
+
+    def step():
+        dcn.dcn_forward(desc, g["x"], g["offset"], g["mask"], g["weight"], g["bias"], out, wsp, nb, stream)
+
+    # parity on sampled outputs before timing (same launch configuration)
+    step()
+    torch.cuda.synchronize()
+    import oracle
+    rng = np.random.default_rng(0)
+    npts = 512
+    pts = np.stack([rng.integers(0, w.B, npts), rng.integers(0, w.Cout, npts), rng.integers(0, Ho, npts),
+                    rng.integers(0, Wo, npts)], 1).astype(np.int64)
+    y, a = oracle.points(host["x"], host["offset"], host["weight"], pts, host["bias"], w.stride, w.pad,
+                         w.dilation, mask=host["mask"])
+    got = out.float().cpu().numpy()[pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
+    tol = 1e-4 if w.dtype == "f32" else 1e-2
+    rel = np.where(a > 0, np.abs(got - y) / np.where(a > 0, a, 1), np.abs(got - y))
+    max_rel = float(rel.max())
+    if not max_rel <= tol:
+        raise SystemExit(f"bench parity failure on {name}: max relative error {max_rel:.3e} > {tol}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step throughput: K back-to-back steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    ms_per_step = total_ms / steps
+
+    # per-kernel durations: events around the staging and the fused launch of each step
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        dcn.dcn_stage(desc, g["x"], g["weight"], wsp, nb, stream)
+        ev[i][1].record(stream)
+        dcn.dcn_forward_staged(desc, g["x"], g["offset"], g["mask"], g["weight"], g["bias"], out, wsp, nb,
+                               stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(steps))
+    fused_ms = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(steps))
+    fused_mean = sum(fused_ms) / steps
+    stage_mean = sum(stage_ms) / steps
+
+    flops = w.flops
+    abytes = w.algorithmic_bytes
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    gbps = abytes / (ms_per_step * 1e-3) / 1e9
+    if w.name == "single224":
+        bound, peak, unit = "hbm", PEAK["hbm"], "GB/s"
+        achieved = abytes / (fused_mean * 1e-3) / 1e9
+    else:
+        bound, unit = "mfma", "TFLOP/s"
+        peak = PEAK["bf16_mfma"] if w.dtype == "bf16" else PEAK["f32_mfma"]
+        achieved = flops / (fused_mean * 1e-3) / 1e12
+    traffic = traffic_for(name)
+
+    rec = {
+        "metric": "deform_conv2d fwd effective TFLOP/s + GB/s (c4 stride-2 bf16), % of roofline",
+        "value": round(tflops, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; shapes and value distributions of the workload)",
+        "config": {"workload": f"{w.name}: B={w.B} Cin={w.Cin} {w.H}x{w.W} -> Cout={w.Cout} {Ho}x{Wo}, "
+                               f"K={w.K} stride={w.stride} pad={w.pad} dilation={w.dilation}, "
+                               f"mask={'yes' if w.mask else 'no'}, bias={'yes' if w.bias else 'no'}",
+                   "variant": variant},
+        "effective_gbps": round(gbps, 2),
+        "frac_mfma_peak": round(tflops / (PEAK["bf16_mfma"] if w.dtype == "bf16" else PEAK["f32_mfma"]), 5),
+        "frac_hbm_peak": round(gbps / PEAK["hbm"], 5),
+        "roofline": {"bound": bound, "achieved": round(achieved, 4), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 5), "traffic": traffic,
+                     "kernel": f"dcn_fused_kernel ({variant})",
+                     "per_launch": {"flops": flops, "algorithmic_bytes": abytes}},
+        "kernels_us": {"stage_mean": round(stage_mean * 1e3, 3), "fused_mean": round(fused_mean * 1e3, 3),
+                       "fused_median": round(fused_ms[steps // 2] * 1e3, 3),
+                       "fused_min": round(fused_ms[0] * 1e3, 3)},
+        "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
+        "parity_max_rel_err_sampled": max_rel,
+        "cpu_baseline": None,
+    }
+    if cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, host, cpu_seconds)
+    return rec
+
+
+def cpu_baseline(w, host, target_s: float):
+    """The oracle as it stands on a bounded slice (a range of output channels)."""
+    import oracle
+    kw = dict(mask=host["mask"], with_abs=False)
+    args = (host["x"], host["offset"], host["weight"], host["bias"], w.stride, w.pad, w.dilation)
+    n1 = max(1, min(w.Cout, 2))
+    t = time.perf_counter()
+    oracle.forward(*args, cout_range=(0, n1), **kw)
+    t1 = time.perf_counter() - t
+    n = int(min(w.Cout, max(n1, round(target_s / max(t1, 1e-6) * n1))))
+    t = time.perf_counter()
+    oracle.forward(*args, cout_range=(0, n), **kw)
+    dt = time.perf_counter() - t
+    flops = 2 * w.B * n * w.Ho * w.Wo * w.Cin * w.K * w.K
+    return {"value": round(flops / dt / 1e12, 8), "unit": "TFLOP/s", "cores": oracle.threads_used(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"output channels [0,{n}) of {w.Cout} ({n / w.Cout:.1%} of the workload), all pixels, "
+                      f"all batches; fp64 accumulate",
+            "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--all", action="store_true", help="also print one line per other named workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
+              f"multi-GPU path: the forward shards by batch or output channel with no exchange).",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    names = [args.workload]
+    if args.all:
+        from deformable_convolution_vision_amd.workloads import ORDER
+        names += [n for n in ORDER if n != args.workload]
+    for i, n in enumerate(names):
+        rec = bench_workload(n, args.steps, args.warmup, cpu=(not args.no_cpu) and i == 0,
+                             cpu_seconds=args.cpu_seconds)
+        print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

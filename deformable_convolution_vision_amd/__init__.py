@@ -1,0 +1,203 @@
+"""MI355X (gfx950) modulated deformable convolution forward (DCNv2; DCNv1 without mask).
+
+A thin ctypes binding over ``libdcn_hip.so`` (C ABI in ``include/dcn.h``).  The
+functions named like the C entry points marshal torch tensors into device
+pointers and the current HIP stream; every step of the computation runs in the
+library's kernels.  ``deform_conv2d`` mirrors torchvision's keyword order
+(input, offset, weight, bias, stride, padding, dilation, mask) and allocates the
+output and the workspace with torch.
+
+There is no fallback: if the library is missing or no GPU is present the
+calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["Desc", "dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_stage",
+           "dcn_forward_staged", "dcn_variant_name", "dcn_status_str", "deform_conv2d",
+           "DcnError", "library_path", "load_library", "F32", "BF16"]
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdcn_hip.so")
+
+F32, BF16 = 0, 1
+OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+_EXPORTS = ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_stage", "dcn_forward_staged",
+            "dcn_variant_name", "dcn_status_str")
+
+
+class DcnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {dcn_status_str(status)} (status {status})")
+
+
+class Desc(ctypes.Structure):
+    """Mirror of ``dcn_desc``."""
+    _fields_ = [("batch", ctypes.c_int64), ("in_channels", ctypes.c_int64), ("height", ctypes.c_int64),
+                ("width", ctypes.c_int64), ("out_channels", ctypes.c_int64),
+                ("kernel_size", ctypes.c_int64), ("stride", ctypes.c_int64), ("pad", ctypes.c_int64),
+                ("dilation", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def __repr__(self):
+        return "Desc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("DCN_HIP_LIB", LIB_PATH)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with "
+                           "`python -m deformable_convolution_vision_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, S, D = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Desc)
+    lib.dcn_output_hw.argtypes = [D, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.dcn_workspace_bytes.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.dcn_forward.argtypes = [D, P, P, P, P, P, P, P, S, P]
+    lib.dcn_forward_staged.argtypes = [D, P, P, P, P, P, P, P, S, P]
+    lib.dcn_stage.argtypes = [D, P, P, P, S, P]
+    lib.dcn_variant_name.argtypes = [D]
+    lib.dcn_variant_name.restype = ctypes.c_char_p
+    lib.dcn_status_str.argtypes = [ctypes.c_int]
+    lib.dcn_status_str.restype = ctypes.c_char_p
+    for name in ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_forward_staged", "dcn_stage"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def dcn_status_str(status: int) -> str:
+    return load_library().dcn_status_str(int(status)).decode()
+
+
+def make_desc(B, Cin, H, W, Cout, K, stride=1, pad=0, dilation=1, dtype=F32) -> Desc:
+    return Desc(B, Cin, H, W, Cout, K, stride, pad, dilation, dtype, 0)
+
+
+def dcn_output_hw(desc: Desc) -> tuple[int, int]:
+    ho, wo = ctypes.c_int64(), ctypes.c_int64()
+    rc = load_library().dcn_output_hw(ctypes.byref(desc), ctypes.byref(ho), ctypes.byref(wo))
+    if rc != OK:
+        raise DcnError(rc, "dcn_output_hw")
+    return ho.value, wo.value
+
+
+def dcn_workspace_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    rc = load_library().dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    if rc != OK:
+        raise DcnError(rc, "dcn_workspace_bytes")
+    return n.value
+
+
+def dcn_variant_name(desc: Desc) -> str:
+    return load_library().dcn_variant_name(ctypes.byref(desc)).decode()
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def dcn_forward(desc: Desc, x, offset, mask, weight, bias, out, workspace, workspace_bytes: int,
+                stream=None) -> None:
+    """Raw call: tensors (or integer device addresses) already laid out as dcn.h states."""
+    rc = load_library().dcn_forward(ctypes.byref(desc), _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight),
+                                    _ptr(bias), _ptr(out), _ptr(workspace), workspace_bytes,
+                                    _stream(stream))
+    if rc != OK:
+        raise DcnError(rc, "dcn_forward")
+
+
+def dcn_stage(desc: Desc, x, weight, workspace, workspace_bytes: int, stream=None) -> None:
+    rc = load_library().dcn_stage(ctypes.byref(desc), _ptr(x), _ptr(weight), _ptr(workspace),
+                                  workspace_bytes, _stream(stream))
+    if rc != OK:
+        raise DcnError(rc, "dcn_stage")
+
+
+def dcn_forward_staged(desc: Desc, x, offset, mask, weight, bias, out, workspace, workspace_bytes: int,
+                       stream=None) -> None:
+    rc = load_library().dcn_forward_staged(ctypes.byref(desc), _ptr(x), _ptr(offset), _ptr(mask),
+                                           _ptr(weight), _ptr(bias), _ptr(out), _ptr(workspace),
+                                           workspace_bytes, _stream(stream))
+    if rc != OK:
+        raise DcnError(rc, "dcn_forward_staged")
+
+
+def describe(input, weight, stride=1, padding=0, dilation=1) -> Desc:
+    if input.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {input.dtype}; use float32 or bfloat16")
+    if input.dim() != 4 or weight.dim() != 4:
+        raise ValueError("input must be [B,Cin,H,W] and weight [Cout,Cin,K,K]")
+    B, Cin, H, W = input.shape
+    Cout, Cin_w, K, K2 = weight.shape
+    if Cin_w != Cin or K != K2:
+        raise ValueError(f"weight {tuple(weight.shape)} does not match input {tuple(input.shape)}")
+    return make_desc(B, Cin, H, W, Cout, K, int(stride), int(padding), int(dilation), _DTYPES[input.dtype])
+
+
+def check_tensors(desc: Desc, input, offset, weight, bias, mask) -> tuple[int, int]:
+    """Shape, dtype, device and contiguity checks; returns (Ho, Wo)."""
+    Ho, Wo = dcn_output_hw(desc)
+    KK = desc.kernel_size ** 2
+    expect = {"offset": (offset, (desc.batch, 2 * KK, Ho, Wo)),
+              "mask": (mask, (desc.batch, KK, Ho, Wo)),
+              "bias": (bias, (desc.out_channels,))}
+    for name, t in (("input", input), ("offset", offset), ("weight", weight), ("bias", bias), ("mask", mask)):
+        if t is None:
+            continue
+        if t.dtype != input.dtype:
+            raise TypeError(f"{name} is {t.dtype}, input is {input.dtype}: all tensors share one dtype")
+        if not t.is_cuda or t.device != input.device:
+            raise ValueError(f"{name} must be on the input's GPU device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if name in expect and tuple(t.shape) != expect[name][1]:
+            raise ValueError(f"{name} must have shape {expect[name][1]}, got {tuple(t.shape)}")
+    return Ho, Wo
+
+
+def deform_conv2d(input, offset, weight, bias=None, stride=1, padding=0, dilation=1, mask=None,
+                  out=None, workspace=None):
+    """Deformable convolution forward on the GPU (torchvision's argument order).
+
+    input [B,Cin,H,W], offset [B,2K^2,Ho,Wo] (channel 2k = dy, 2k+1 = dx of kernel
+    point k = i*K + j), weight [Cout,Cin,K,K], bias [Cout] or None, mask
+    [B,K^2,Ho,Wo] or None.  float32 or bfloat16, contiguous, on one GPU.
+    """
+    desc = describe(input, weight, stride, padding, dilation)
+    Ho, Wo = check_tensors(desc, input, offset, weight, bias, mask)
+    if out is None:
+        out = torch.empty((desc.batch, desc.out_channels, Ho, Wo), dtype=input.dtype, device=input.device)
+    nbytes = dcn_workspace_bytes(desc)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=input.device)
+    with torch.cuda.device(input.device):
+        dcn_forward(desc, input, offset, mask, weight, bias, out, workspace if nbytes else None, nbytes)
+    return out

@@ -1,0 +1,269 @@
+// dcn_api.hip -- host side of the C ABI declared in include/dcn.h: argument
+// validation, output geometry, workspace layout, variant choice and launches.
+// Every check happens before the first HIP call; nothing here allocates or
+// synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+
+#include "dcn.h"
+#include "dcn_internal.h"
+
+namespace {
+
+using dcn::FusedArgs;
+using dcn::StageArgs;
+
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;   // int32 element indexing
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Output size of the strided, padded, dilated window, as for a regular
+// convolution (torchvision deform_conv2d parameter table: stride, padding,
+// dilation).  Returns 0 when the window does not fit.
+int64_t out_extent(int64_t in, int64_t K, int64_t stride, int64_t pad, int64_t dil) {
+  const int64_t span = in + 2 * pad - dil * (K - 1) - 1;
+  return span < 0 ? 0 : span / stride + 1;
+}
+
+struct Plan {
+  int64_t Ho = 0, Wo = 0;
+  int variant = -1;
+  int64_t Cp = 0, Mp = 0;       // channel and output-channel padding of the staged buffers
+  size_t ws_x = 0, ws_w = 0;    // workspace byte offsets
+  size_t ws_bytes = 0;
+  bool empty = false;           // B == 0 or Cout == 0: nothing to launch
+};
+
+bool geometry_ok(const dcn_desc* d) {
+  if (d == nullptr || d->reserved != 0) return false;
+  if (d->batch < 0 || d->out_channels < 0) return false;
+  if (d->in_channels < 1 || d->height < 1 || d->width < 1 || d->kernel_size < 1) return false;
+  if (d->stride < 1 || d->dilation < 1 || d->pad < 0) return false;
+  // keep intermediate products far from int64 overflow
+  const int64_t big = int64_t(1) << 30;
+  if (d->height > big || d->width > big || d->kernel_size > 4096 || d->stride > big ||
+      d->pad > big || d->dilation > big || d->batch > big || d->in_channels > big ||
+      d->out_channels > big)
+    return false;
+  return true;
+}
+
+// Pick the kernel variant for a valid descriptor.
+int choose_variant(const dcn_desc* d, int64_t N) {
+  const int64_t M = d->out_channels;
+  if (d->dtype == DCN_F32) return M <= 64 ? dcn::V_TILE_F32_M64_N64 : dcn::V_TILE_F32_M128_N64;
+  if (M <= 64) return dcn::V_TILE_BF16_M64_N64;
+  // enough workgroups to cover 256 CUs with the wider tile?
+  if (M >= 256 && (N + 63) / 64 * ((M + 255) / 256) >= 512) return dcn::V_TILE_BF16_M256_N64;
+  if ((N + 63) / 64 * ((M + 127) / 128) >= 512) return dcn::V_TILE_BF16_M128_N64;
+  return dcn::V_TILE_BF16_M128_N32;
+}
+
+int make_plan(const dcn_desc* d, Plan* p) {
+  if (!geometry_ok(d)) return DCN_E_ARG;
+  if (d->dtype != DCN_F32 && d->dtype != DCN_BF16) return DCN_E_UNSUPPORTED;
+  p->Ho = out_extent(d->height, d->kernel_size, d->stride, d->pad, d->dilation);
+  p->Wo = out_extent(d->width, d->kernel_size, d->stride, d->pad, d->dilation);
+  if (p->Ho < 1 || p->Wo < 1) return DCN_E_ARG;
+  const int64_t B = d->batch, Cin = d->in_channels, H = d->height, W = d->width;
+  const int64_t Cout = d->out_channels, K = d->kernel_size, KK = K * K;
+  const int64_t HoWo = p->Ho * p->Wo;
+  const int64_t N = B * HoWo;
+  p->variant = choose_variant(d, N);
+  // DCN_VARIANT=<name> pins the kernel variant (tile sweeps and tests); an
+  // unknown name or one built for the other dtype is rejected.
+  if (const char* force = std::getenv("DCN_VARIANT")) {
+    if (force[0] != '\0') {
+      int found = -1;
+      for (int v = 0; v < dcn::V_COUNT; ++v)
+        if (std::strcmp(force, dcn::variant_info(v).name) == 0) found = v;
+      if (found < 0 || dcn::variant_info(found).is_bf16 != (d->dtype == DCN_BF16)) return DCN_E_UNSUPPORTED;
+      p->variant = found;
+    }
+  }
+  const dcn::VariantInfo& vi = dcn::variant_info(p->variant);
+  p->Cp = round_up(Cin, vi.ck);
+  p->Mp = round_up(Cout > 0 ? Cout : 1, vi.mt);
+  // element-count limits (int32 indexing inside the kernels)
+  const double lim = static_cast<double>(kMaxElems);
+  if (static_cast<double>(B) * Cin * H * W > lim || static_cast<double>(B) * 2 * KK * HoWo > lim ||
+      static_cast<double>(Cout) * Cin * KK > lim || static_cast<double>(B) * Cout * HoWo > lim ||
+      static_cast<double>(B) * H * W * p->Cp > lim || static_cast<double>(p->Mp) * KK * p->Cp > lim ||
+      static_cast<double>(N) + vi.nt > lim)
+    return DCN_E_UNSUPPORTED;
+  const size_t es = d->dtype == DCN_BF16 ? 2 : 4;
+  p->empty = (B == 0 || Cout == 0);
+  if (vi.staged && !p->empty) {
+    p->ws_x = 0;
+    p->ws_w = align_up(static_cast<size_t>(B * H * W * p->Cp) * es, kAlign);
+    p->ws_bytes = p->ws_w + align_up(static_cast<size_t>(p->Mp * KK * p->Cp) * es, kAlign);
+  }
+  return DCN_OK;
+}
+
+int check_workspace(const Plan& p, const void* ws, size_t ws_bytes) {
+  if (p.ws_bytes == 0) return DCN_OK;
+  if (ws == nullptr || ws_bytes < p.ws_bytes) return DCN_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return DCN_E_WORKSPACE;
+  return DCN_OK;
+}
+
+StageArgs stage_args(const dcn_desc* d, const Plan& p, const void* x, const void* w, void* ws) {
+  StageArgs a{};
+  a.x = x;
+  a.w = w;
+  a.xs = static_cast<unsigned char*>(ws) + p.ws_x;
+  a.wp = static_cast<unsigned char*>(ws) + p.ws_w;
+  a.B = static_cast<int>(d->batch);
+  a.Cin = static_cast<int>(d->in_channels);
+  a.HW = static_cast<int>(d->height * d->width);
+  a.Cp = static_cast<int>(p.Cp);
+  a.Cout = static_cast<int>(d->out_channels);
+  a.Mp = static_cast<int>(p.Mp);
+  a.KK = static_cast<int>(d->kernel_size * d->kernel_size);
+  return a;
+}
+
+FusedArgs fused_args(const dcn_desc* d, const Plan& p, const void* x, const void* offset, const void* mask,
+                     const void* w, const void* bias, void* out, const void* ws) {
+  const dcn::VariantInfo& vi = dcn::variant_info(p.variant);
+  FusedArgs a{};
+  a.xs = ws ? static_cast<const unsigned char*>(ws) + p.ws_x : nullptr;
+  a.wp = ws ? static_cast<const unsigned char*>(ws) + p.ws_w : nullptr;
+  a.x = x;
+  a.w = w;
+  a.offset = offset;
+  a.mask = mask;
+  a.bias = bias;
+  a.out = out;
+  a.B = static_cast<int>(d->batch);
+  a.Cin = static_cast<int>(d->in_channels);
+  a.H = static_cast<int>(d->height);
+  a.W = static_cast<int>(d->width);
+  a.Cp = static_cast<int>(p.Cp);
+  a.Cout = static_cast<int>(d->out_channels);
+  a.K = static_cast<int>(d->kernel_size);
+  a.KK = a.K * a.K;
+  a.stride = static_cast<int>(d->stride);
+  a.pad = static_cast<int>(d->pad);
+  a.dil = static_cast<int>(d->dilation);
+  a.Ho = static_cast<int>(p.Ho);
+  a.Wo = static_cast<int>(p.Wo);
+  a.HoWo = a.Ho * a.Wo;
+  a.N = a.B * a.HoWo;
+  a.m_tiles = static_cast<int>(p.Mp / vi.mt);
+  a.n_tiles = (a.N + vi.nt - 1) / vi.nt;
+  return a;
+}
+
+int check_positions(const dcn_desc* d, int64_t K, int64_t stride, int64_t pad, int64_t dil, int64_t Ho,
+                    int64_t Wo) {
+  // Base sampling positions oy*stride - pad + i*dilation must be exact in fp32
+  // (the fractional offset is added separately): keep them below 2^24.
+  const double ymax = static_cast<double>(Ho) * stride + pad + static_cast<double>(K) * dil;
+  const double xmax = static_cast<double>(Wo) * stride + pad + static_cast<double>(K) * dil;
+  const double hmax = static_cast<double>(d->height) + 2, wmax = static_cast<double>(d->width) + 2;
+  const double lim = 16777216.0;
+  return (ymax < lim && xmax < lim && hmax < lim && wmax < lim) ? DCN_OK : DCN_E_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" int dcn_output_hw(const dcn_desc* desc, int64_t* out_h, int64_t* out_w) {
+  if (out_h == nullptr || out_w == nullptr || !geometry_ok(desc)) return DCN_E_ARG;
+  const int64_t ho = out_extent(desc->height, desc->kernel_size, desc->stride, desc->pad, desc->dilation);
+  const int64_t wo = out_extent(desc->width, desc->kernel_size, desc->stride, desc->pad, desc->dilation);
+  if (ho < 1 || wo < 1) return DCN_E_ARG;
+  *out_h = ho;
+  *out_w = wo;
+  return DCN_OK;
+}
+
+extern "C" int dcn_workspace_bytes(const dcn_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return DCN_E_ARG;
+  Plan p;
+  const int rc = make_plan(desc, &p);
+  if (rc != DCN_OK) return rc;
+  *bytes = p.ws_bytes;
+  return DCN_OK;
+}
+
+extern "C" const char* dcn_variant_name(const dcn_desc* desc) {
+  Plan p;
+  if (make_plan(desc, &p) != DCN_OK) return "invalid";
+  return dcn::variant_info(p.variant).name;
+}
+
+extern "C" const char* dcn_status_str(int status) {
+  switch (status) {
+    case DCN_OK: return "ok";
+    case DCN_E_ARG: return "invalid argument";
+    case DCN_E_UNSUPPORTED: return "unsupported (dtype or size limit)";
+    case DCN_E_WORKSPACE: return "workspace missing, too small or misaligned";
+    case DCN_E_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+namespace {
+
+int validate_call(const dcn_desc* desc, Plan* p, const void* offset, const void* weight, const void* out,
+                  const void* x) {
+  const int rc = make_plan(desc, p);
+  if (rc != DCN_OK) return rc;
+  if (p->empty) return DCN_OK;
+  if (x == nullptr || offset == nullptr || weight == nullptr || out == nullptr) return DCN_E_ARG;
+  return check_positions(desc, desc->kernel_size, desc->stride, desc->pad, desc->dilation, p->Ho, p->Wo);
+}
+
+}  // namespace
+
+extern "C" int dcn_stage(const dcn_desc* desc, const void* x, const void* weight, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  int rc = make_plan(desc, &p);
+  if (rc != DCN_OK) return rc;
+  if (p.empty || !dcn::variant_info(p.variant).staged) return DCN_OK;
+  if (x == nullptr || weight == nullptr) return DCN_E_ARG;
+  rc = check_workspace(p, workspace, workspace_bytes);
+  if (rc != DCN_OK) return rc;
+  const StageArgs a = stage_args(desc, p, x, weight, workspace);
+  return dcn::launch_stage(p.variant, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
+}
+
+extern "C" int dcn_forward_staged(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                                  const void* weight, const void* bias, void* out, const void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  int rc = validate_call(desc, &p, offset, weight, out, x);
+  if (rc != DCN_OK) return rc;
+  if (p.empty) return DCN_OK;
+  rc = check_workspace(p, workspace, workspace_bytes);
+  if (rc != DCN_OK) return rc;
+  const FusedArgs a = fused_args(desc, p, x, offset, mask, weight, bias, out, workspace);
+  return dcn::launch_fused(p.variant, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
+}
+
+extern "C" int dcn_forward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                           const void* weight, const void* bias, void* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  int rc = validate_call(desc, &p, offset, weight, out, x);
+  if (rc != DCN_OK) return rc;
+  if (p.empty) return DCN_OK;
+  rc = check_workspace(p, workspace, workspace_bytes);
+  if (rc != DCN_OK) return rc;
+  if (dcn::variant_info(p.variant).staged) {
+    const StageArgs s = stage_args(desc, p, x, weight, workspace);
+    if (dcn::launch_stage(p.variant, s, stream) != hipSuccess) return DCN_E_HIP;
+  }
+  const FusedArgs a = fused_args(desc, p, x, offset, mask, weight, bias, out, workspace);
+  return dcn::launch_fused(p.variant, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
+}

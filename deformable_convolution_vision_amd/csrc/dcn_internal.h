@@ -1,0 +1,56 @@
+// dcn_internal.h -- launch interface between the host API (dcn_api.hip) and the
+// gfx950 kernels (dcn_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dcn {
+
+// Everything the fused kernel needs; all sizes fit int32 (checked on the host).
+struct FusedArgs {
+  const void* xs;      // staged x, channels last: [B][H][W][Cp]
+  const void* wp;      // repacked weight: [Mp][K*K][Cp], zero rows/channels beyond Cout/Cin
+  const void* x;       // x as given, [B][Cin][H][W] (direct variants only)
+  const void* w;       // weight as given, [Cout][Cin][K][K] (direct variants only)
+  const void* offset;  // [B][2K^2][Ho][Wo]
+  const void* mask;    // [B][K^2][Ho][Wo] or null
+  const void* bias;    // [Cout] or null
+  void* out;           // [B][Cout][Ho][Wo]
+  int B, Cin, H, W, Cp, Cout, K, KK, stride, pad, dil, Ho, Wo, HoWo, N;
+  int m_tiles, n_tiles;
+};
+
+struct StageArgs {
+  const void* x;   // [B][Cin][H][W]
+  const void* w;   // [Cout][Cin][K][K]
+  void* xs;        // [B][H*W][Cp]
+  void* wp;        // [Mp][KK][Cp]
+  int B, Cin, HW, Cp, Cout, Mp, KK;
+};
+
+enum Variant : int {
+  V_TILE_F32_M64_N64 = 0,
+  V_TILE_F32_M128_N64,
+  V_TILE_BF16_M64_N64,
+  V_TILE_BF16_M128_N64,
+  V_TILE_BF16_M128_N32,
+  V_TILE_BF16_M256_N64,
+  V_COUNT
+};
+
+struct VariantInfo {
+  const char* name;
+  int is_bf16;
+  int mt, nt;      // tile of the fused kernel: MT output channels x NT output pixels
+  int ck;          // channels per reduction chunk (Cp is a multiple of it)
+  int staged;      // 1: needs dcn_stage's workspace
+};
+
+const VariantInfo& variant_info(int v);
+
+hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream);
+hipError_t launch_fused(int variant, const FusedArgs& a, hipStream_t stream);
+
+}  // namespace dcn

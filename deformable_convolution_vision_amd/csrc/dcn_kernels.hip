@@ -1,0 +1,452 @@
+// dcn_kernels.hip -- gfx950 kernels of the deformable convolution forward.
+//
+// Two launches per call:
+//   stage_x / pack_w : x from [B][Cin][H][W] to channels-last [B][H][W][Cp] and the
+//                      weight from [Cout][Cin][K][K] to [Mp][K^2][Cp] (zero padding up
+//                      to Cp channels and Mp rows), so that the samples of one kernel
+//                      point form a contiguous reduction run of Cp channels;
+//   dcn_fused        : one workgroup per (MT output channels) x (NT output pixels)
+//                      tile.  For each reduction chunk (kernel point k, CK channels):
+//                      the sampling positions and bilinear corner weights of
+//                      (pixel, k) times the mask (computed once per k, kept in
+//                      registers), coalesced 16-byte gathers of the four corner
+//                      channel vectors from the channels-last copy, fp32
+//                      interpolation, rounding to the element type, a column tile
+//                      in LDS; MFMA against the weight tile; fp32 accumulators; bias
+//                      added in the epilogue and the result stored as [B][Cout][Ho][Wo].
+//
+// The computation follows the deformable-convolution equation (csdn.net tags page
+// "可变形卷积：Deformable ConvNets", part "Deformable Convolutional Networks",
+// section on deformable convolution), with the modulation scalar of DCNv2 (same
+// page, section 3.2) and bilinear interpolation from the four integer neighbours
+// (same page, bilinear-interpolation equation).  The im2col -> GEMM -> reduce
+// split of a convolution (same page, supplement on im2col) is realised with the
+// column matrix kept in LDS only: it never goes to HBM.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dcn_internal.h"
+
+namespace dcn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;  // four wave64 per workgroup
+
+// ---------------------------------------------------------------------------
+// element helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_scalar(const void* p, int idx) {
+  if constexpr (BF16) {
+    const uint16_t v = reinterpret_cast<const uint16_t*>(p)[idx];
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+  } else {
+    return reinterpret_cast<const float*>(p)[idx];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_scalar(void* p, int idx, float v) {
+  if constexpr (BF16) {
+    reinterpret_cast<uint16_t*>(p)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  } else {
+    reinterpret_cast<float*>(p)[idx] = v;
+  }
+}
+
+// Workgroup id -> tile id, so that consecutive tiles run on the same XCD.
+// Workgroups are dealt to the 8 XCDs round-robin in id order; this gives XCD x
+// the contiguous tile range [x*q + min(x,r), ... + q + (x<r)) of T = 8q + r
+// tiles.  It is a bijection on [0, T) for any T.
+__device__ __forceinline__ int xcd_tile(int g, int T) {
+  const int xcd = g & 7, idx = g >> 3;
+  const int q = T >> 3, r = T & 7;
+  return xcd * q + min(xcd, r) + idx;
+}
+
+// ---------------------------------------------------------------------------
+// staging
+// ---------------------------------------------------------------------------
+
+// x[b][c][s] -> xs[b][s][c] for s in [0, H*W), c in [0, Cp); channels >= Cin get 0.
+// One workgroup moves a 64-channel x 64-pixel tile through LDS so both the read
+// (along s) and the write (along c) are contiguous.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void stage_x_kernel(StageArgs a) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  __shared__ T tile[64][65];
+  const int s_tiles = (a.HW + 63) / 64;
+  const int b = blockIdx.x / s_tiles;
+  const int s0 = (blockIdx.x - b * s_tiles) * 64, c0 = blockIdx.y * 64;
+  const T* x = reinterpret_cast<const T*>(a.x) + static_cast<size_t>(b) * a.Cin * a.HW;
+  T* xs = reinterpret_cast<T*>(a.xs) + static_cast<size_t>(b) * a.HW * a.Cp;
+  for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
+    const int cl = e >> 6, sl = e & 63;
+    const int c = c0 + cl, s = s0 + sl;
+    T v = T(0);
+    if (c < a.Cin && s < a.HW) v = x[static_cast<size_t>(c) * a.HW + s];
+    tile[cl][sl] = v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
+    const int sl = e >> 6, cl = e & 63;
+    const int c = c0 + cl, s = s0 + sl;
+    if (c < a.Cp && s < a.HW) xs[static_cast<size_t>(s) * a.Cp + c] = tile[cl][sl];
+  }
+}
+
+// w[o][c][k] -> wp[o][k][c] for o < Mp, k < KK, c < Cp; zero outside Cout x Cin.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void pack_w_kernel(StageArgs a) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  const T* w = reinterpret_cast<const T*>(a.w);
+  T* wp = reinterpret_cast<T*>(a.wp);
+  const int total = a.Mp * a.KK * a.Cp;
+  for (int e = blockIdx.x * kThreads + threadIdx.x; e < total; e += gridDim.x * kThreads) {
+    const int c = e % a.Cp;
+    const int k = (e / a.Cp) % a.KK;
+    const int o = e / (a.Cp * a.KK);
+    T v = T(0);
+    if (o < a.Cout && c < a.Cin) v = w[(o * a.Cin + c) * a.KK + k];
+    wp[e] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fused deformable im2col + MFMA + bias
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int MT, int NT>
+struct TileCfg {
+  static constexpr int ES = BF16 ? 2 : 4;          // element bytes
+  static constexpr int CK = 32;                     // channels per reduction chunk
+  static constexpr int VEC = 16 / ES;               // elements per 16-byte unit
+  static constexpr int UPR = CK / VEC;              // 16-byte units per tile row
+  static constexpr int ROWB = CK * ES + 16;         // LDS row stride in bytes (padded)
+  static constexpr int G_UNITS = NT * UPR;          // column-tile units per chunk
+  static constexpr int GU = (G_UNITS + kThreads - 1) / kThreads;
+  static constexpr int A_UNITS = MT * UPR;          // weight-tile units per chunk
+  static constexpr int AU = (A_UNITS + kThreads - 1) / kThreads;
+  static constexpr int WAVES_M = 2, WAVES_N = 2;
+  static constexpr int WM = MT / WAVES_M, WN = NT / WAVES_N;
+  static constexpr int FM = WM / 16, FN = WN / 16;  // 16x16 MFMA fragments per wave
+  static constexpr int BUF_BYTES = (MT + NT) * ROWB;
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+};
+
+template <bool BF16, int MT, int NT>
+__global__ __launch_bounds__(kThreads) void dcn_fused_kernel(FusedArgs a) {
+  using C = TileCfg<BF16, MT, NT>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][C::BUF_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.m_tiles * a.n_tiles;
+  const int t = xcd_tile(blockIdx.x, T);
+  const int m0 = (t % a.m_tiles) * MT;
+  const int n0 = (t / a.m_tiles) * NT;
+  const int KK = a.KK, Cp = a.Cp;
+  const int cch = Cp / C::CK;          // channel chunks per kernel point
+  const int nq = KK * cch;             // reduction chunks
+
+  const unsigned char* xs = reinterpret_cast<const unsigned char*>(a.xs);
+  const unsigned char* wp = reinterpret_cast<const unsigned char*>(a.wp);
+
+  // --- gather units owned by this thread: (pixel of the tile, 16-byte sub-block)
+  int g_pl[C::GU], g_sub[C::GU], g_b[C::GU], g_oy[C::GU], g_ox[C::GU], g_rem[C::GU];
+  bool g_on[C::GU];
+#pragma unroll
+  for (int u = 0; u < C::GU; ++u) {
+    const int unit = tid + u * kThreads;
+    g_pl[u] = unit / C::UPR;
+    g_sub[u] = unit % C::UPR;
+    const int n = n0 + g_pl[u];
+    g_on[u] = unit < C::G_UNITS && n < a.N;
+    const int nn = g_on[u] ? n : 0;
+    g_b[u] = nn / a.HoWo;
+    g_rem[u] = nn - g_b[u] * a.HoWo;
+    g_oy[u] = g_rem[u] / a.Wo;
+    g_ox[u] = g_rem[u] - g_oy[u] * a.Wo;
+  }
+
+  // corner table of the current kernel point: element offsets into xs (or -1)
+  // and bilinear weights times the mask (0 for a corner outside the image)
+  int c_off[C::GU][4];
+  float c_w[C::GU][4];
+
+  auto corners = [&](int k) {
+    const int i = k / a.K, j = k - (k / a.K) * a.K;
+#pragma unroll
+    for (int u = 0; u < C::GU; ++u) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { c_off[u][q] = -1; c_w[u][q] = 0.f; }
+      if (!g_on[u]) continue;
+      const int ob = (g_b[u] * 2 * KK + 2 * k) * a.HoWo + g_rem[u];
+      const float dy = load_scalar<BF16>(a.offset, ob);
+      const float dx = load_scalar<BF16>(a.offset, ob + a.HoWo);
+      const float m = a.mask ? load_scalar<BF16>(a.mask, (g_b[u] * KK + k) * a.HoWo + g_rem[u]) : 1.f;
+      // integer and fractional parts of the offset are exact in fp32, so the
+      // neighbour rows/columns and the interpolation fractions are exact too.
+      const float fy = floorf(dy), fx = floorf(dx);
+      const float ly = dy - fy, lx = dx - fx;
+      const float y0 = static_cast<float>(g_oy[u] * a.stride - a.pad + i * a.dil) + fy;
+      const float x0 = static_cast<float>(g_ox[u] * a.stride - a.pad + j * a.dil) + fx;
+      // inside tests on floats first: NaN and huge values fail every test
+      const bool vy0 = (y0 >= 0.f) && (y0 <= static_cast<float>(a.H - 1));
+      const bool vy1 = (y0 >= -1.f) && (y0 <= static_cast<float>(a.H - 2));
+      const bool vx0 = (x0 >= 0.f) && (x0 <= static_cast<float>(a.W - 1));
+      const bool vx1 = (x0 >= -1.f) && (x0 <= static_cast<float>(a.W - 2));
+      if (!((vy0 || vy1) && (vx0 || vx1))) continue;
+      const int iy = static_cast<int>(y0), ix = static_cast<int>(x0);
+      const int base = ((g_b[u] * a.H + iy) * a.W + ix) * Cp;
+      const float hy = 1.f - ly, hx = 1.f - lx;
+      if (vy0 && vx0) { c_off[u][0] = base;                  c_w[u][0] = hy * hx * m; }
+      if (vy0 && vx1) { c_off[u][1] = base + Cp;             c_w[u][1] = hy * lx * m; }
+      if (vy1 && vx0) { c_off[u][2] = base + a.W * Cp;       c_w[u][2] = ly * hx * m; }
+      if (vy1 && vx1) { c_off[u][3] = base + a.W * Cp + Cp;  c_w[u][3] = ly * lx * m; }
+    }
+  };
+
+  uint4 graw[C::GU][4];
+  uint4 araw[C::AU];
+
+  // global loads for chunk q into registers
+  auto issue = [&](int q) {
+    const int k = q / cch, cc = q - (q / cch) * cch;
+    if (cc == 0) corners(k);
+#pragma unroll
+    for (int u = 0; u < C::GU; ++u) {
+      const int ch = cc * C::CK + g_sub[u] * C::VEC;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        graw[u][q4] = make_uint4(0u, 0u, 0u, 0u);
+        if (c_off[u][q4] >= 0)
+          graw[u][q4] = *reinterpret_cast<const uint4*>(xs + static_cast<size_t>(c_off[u][q4] + ch) * C::ES);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < C::AU; ++u) {
+      const int unit = tid + u * kThreads;
+      if (unit < C::A_UNITS) {
+        const int row = unit / C::UPR, sub = unit % C::UPR;
+        const size_t e = (static_cast<size_t>(m0 + row) * KK + k) * Cp + cc * C::CK + sub * C::VEC;
+        araw[u] = *reinterpret_cast<const uint4*>(wp + e * C::ES);
+      }
+    }
+  };
+
+  // interpolate the gathered corners and write both tiles to LDS buffer `buf`
+  auto commit = [&](int buf) {
+    unsigned char* As = lds[buf];
+    unsigned char* Bs = lds[buf] + MT * C::ROWB;
+#pragma unroll
+    for (int u = 0; u < C::GU; ++u) {
+      const int unit = tid + u * kThreads;
+      if (unit >= C::G_UNITS) continue;
+      uint4 res;
+      const float w0 = c_w[u][0], w1 = c_w[u][1], w2 = c_w[u][2], w3 = c_w[u][3];
+      if constexpr (BF16) {
+        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&graw[u][0]);
+        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&graw[u][1]);
+        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&graw[u][2]);
+        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&graw[u][3]);
+        uint32_t* o = reinterpret_cast<uint32_t*>(&res);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float lo = w0 * bf16_lo(r0[e]);
+          lo = fmaf(w1, bf16_lo(r1[e]), lo);
+          lo = fmaf(w2, bf16_lo(r2[e]), lo);
+          lo = fmaf(w3, bf16_lo(r3[e]), lo);
+          float hi = w0 * bf16_hi(r0[e]);
+          hi = fmaf(w1, bf16_hi(r1[e]), hi);
+          hi = fmaf(w2, bf16_hi(r2[e]), hi);
+          hi = fmaf(w3, bf16_hi(r3[e]), hi);
+          o[e] = pack_bf16x2(lo, hi);
+        }
+      } else {
+        const float* r0 = reinterpret_cast<const float*>(&graw[u][0]);
+        const float* r1 = reinterpret_cast<const float*>(&graw[u][1]);
+        const float* r2 = reinterpret_cast<const float*>(&graw[u][2]);
+        const float* r3 = reinterpret_cast<const float*>(&graw[u][3]);
+        float* o = reinterpret_cast<float*>(&res);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = w0 * r0[e];
+          v = fmaf(w1, r1[e], v);
+          v = fmaf(w2, r2[e], v);
+          v = fmaf(w3, r3[e], v);
+          o[e] = v;
+        }
+      }
+      *reinterpret_cast<uint4*>(Bs + g_pl[u] * C::ROWB + g_sub[u] * 16) = res;
+    }
+#pragma unroll
+    for (int u = 0; u < C::AU; ++u) {
+      const int unit = tid + u * kThreads;
+      if (unit < C::A_UNITS) {
+        const int row = unit / C::UPR, sub = unit % C::UPR;
+        *reinterpret_cast<uint4*>(As + row * C::ROWB + sub * 16) = araw[u];
+      }
+    }
+  };
+
+  floatx4 acc[C::FM][C::FN];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int wave_m = wave % C::WAVES_M, wave_n = wave / C::WAVES_M;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+
+  auto mma = [&](int buf) {
+    const unsigned char* As = lds[buf];
+    const unsigned char* Bs = lds[buf] + MT * C::ROWB;
+    if constexpr (BF16) {
+      // 16x16x32: lane supplies 8 consecutive reduction values of row/column lane%16
+      bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+        af[fm] = *reinterpret_cast<const bf16x8*>(As + (wave_m * C::WM + fm * 16 + lrow) * C::ROWB + lgrp * 16);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        bfr[fn] = *reinterpret_cast<const bf16x8*>(Bs + (wave_n * C::WN + fn * 16 + lrow) * C::ROWB + lgrp * 16);
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+    } else {
+      // 16x16x4 fp32, eight steps per 32-channel chunk: at step s lane l supplies
+      // reduction index (l/16)*8 + s of its row (A) and column (B)
+      floatx4 a8[C::FM][2], b8[C::FN][2];
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const unsigned char* p = As + (wave_m * C::WM + fm * 16 + lrow) * C::ROWB + lgrp * 32;
+        a8[fm][0] = *reinterpret_cast<const floatx4*>(p);
+        a8[fm][1] = *reinterpret_cast<const floatx4*>(p + 16);
+      }
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const unsigned char* p = Bs + (wave_n * C::WN + fn * 16 + lrow) * C::ROWB + lgrp * 32;
+        b8[fn][0] = *reinterpret_cast<const floatx4*>(p);
+        b8[fn][1] = *reinterpret_cast<const floatx4*>(p + 16);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(a8[fm][s >> 2][s & 3], b8[fn][s >> 2][s & 3],
+                                                               acc[fm][fn], 0, 0, 0);
+    }
+  };
+
+  // --- main loop: loads for chunk q+1 are in flight while chunk q multiplies
+  issue(0);
+  commit(0);
+  __syncthreads();
+  for (int q = 0; q < nq; ++q) {
+    const bool more = q + 1 < nq;
+    if (more) issue(q + 1);
+    mma(q & 1);
+    if (more) commit((q + 1) & 1);
+    __syncthreads();
+  }
+
+  // --- epilogue: bias, rounding, NCHW store.  D fragment: lane l holds rows
+  // 4*(l/16)+i, column l%16.
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int n = n0 + wave_n * C::WN + fn * 16 + lrow;
+      if (n >= a.N) continue;
+      const int b = n / a.HoWo, rem = n - (n / a.HoWo) * a.HoWo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = m0 + wave_m * C::WM + fm * 16 + lgrp * 4 + i;
+        if (o >= a.Cout) continue;
+        float v = acc[fm][fn][i];
+        if (a.bias) v += load_scalar<BF16>(a.bias, o);
+        store_scalar<BF16>(a.out, (b * a.Cout + o) * a.HoWo + rem, v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// variant table and launchers
+// ---------------------------------------------------------------------------
+
+static const VariantInfo kVariants[V_COUNT] = {
+    {"tile_f32_m64_n64", 0, 64, 64, 32, 1},
+    {"tile_f32_m128_n64", 0, 128, 64, 32, 1},
+    {"tile_bf16_m64_n64", 1, 64, 64, 32, 1},
+    {"tile_bf16_m128_n64", 1, 128, 64, 32, 1},
+    {"tile_bf16_m128_n32", 1, 128, 32, 32, 1},
+    {"tile_bf16_m256_n64", 1, 256, 64, 32, 1},
+};
+
+const VariantInfo& variant_info(int v) { return kVariants[v]; }
+
+hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream) {
+  const VariantInfo& vi = kVariants[variant];
+  if (!vi.staged) return hipSuccess;
+  const dim3 gx(((a.HW + 63) / 64) * a.B, (a.Cp + 63) / 64);
+  const int wtotal = a.Mp * a.KK * a.Cp;
+  const dim3 gw(min((wtotal + kThreads - 1) / kThreads, 4096));
+  void* args[] = {const_cast<StageArgs*>(&a)};
+  hipError_t e;
+  if (vi.is_bf16) {
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&stage_x_kernel<true>), gx, dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&pack_w_kernel<true>), gw, dim3(kThreads), args, 0, stream);
+  } else {
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&stage_x_kernel<false>), gx, dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&pack_w_kernel<false>), gw, dim3(kThreads), args, 0, stream);
+  }
+  return e;
+}
+
+template <bool BF16, int MT, int NT>
+static hipError_t launch_tile(const FusedArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<FusedArgs*>(&a)};
+  const dim3 grid(a.m_tiles * a.n_tiles);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dcn_fused_kernel<BF16, MT, NT>), grid, dim3(kThreads),
+                         args, 0, stream);
+}
+
+hipError_t launch_fused(int variant, const FusedArgs& a, hipStream_t stream) {
+  switch (variant) {
+    case V_TILE_F32_M64_N64: return launch_tile<false, 64, 64>(a, stream);
+    case V_TILE_F32_M128_N64: return launch_tile<false, 128, 64>(a, stream);
+    case V_TILE_BF16_M64_N64: return launch_tile<true, 64, 64>(a, stream);
+    case V_TILE_BF16_M128_N64: return launch_tile<true, 128, 64>(a, stream);
+    case V_TILE_BF16_M128_N32: return launch_tile<true, 128, 32>(a, stream);
+    case V_TILE_BF16_M256_N64: return launch_tile<true, 256, 64>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dcn

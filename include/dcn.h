@@ -1,0 +1,128 @@
+/*
+ * dcn.h -- C ABI of the MI355X (gfx950) modulated deformable convolution forward.
+ *
+ * The operation (DCNv2 deform_conv2d; DCNv1 when the mask is absent): for every
+ * batch b, output channel o and output pixel (oy, ox)
+ *
+ *   out[b,o,oy,ox] = bias[o] + sum_{c<Cin} sum_{k<K*K} weight[o,c,i,j] * m_k * S(x[b,c], py_k, px_k)
+ *     i = k / K, j = k % K                       kernel point k in row-major order
+ *     py_k = oy*stride - pad + i*dilation + offset[b, 2k,   oy, ox]
+ *     px_k = ox*stride - pad + j*dilation + offset[b, 2k+1, oy, ox]
+ *     m_k  = mask[b, k, oy, ox], or 1 when mask is NULL
+ *     S    = bilinear interpolation from the four integer neighbours of (py, px);
+ *            a neighbour outside [0,H) x [0,W) contributes zero
+ *
+ * Sources: the deformable-convolution equation over the regular grid R and the
+ * bilinear-interpolation equation (csdn.net tags page "可变形卷积：Deformable
+ * ConvNets", part "Deformable Convolutional Networks", sections on deformable
+ * convolution and on the PyTorch implementation); the modulation scalar per
+ * sampling point (same page, DCNv2 section 3.2; un.csdn.net/5xxxf43i9i, DCNv2
+ * formula); the call and its parameters as torchvision's deform_conv2d takes
+ * them (agent.csdn.net/6a744b3d10ee7a33f2973402.html, sections 2.1 and 2.2).
+ * Offset channel 2k is the row displacement and 2k+1 the column displacement;
+ * displacements are in input pixels.  A NaN or infinite displacement makes its
+ * sample zero.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense, contiguous, row-major, in device memory of the current
+ *    device, all of the element type desc->dtype:
+ *      x[B,Cin,H,W], offset[B,2K^2,Ho,Wo], mask[B,K^2,Ho,Wo] or NULL,
+ *      weight[Cout,Cin,K,K], bias[Cout] or NULL, out[B,Cout,Ho,Wo].
+ *  - The caller owns every buffer, including the workspace.  The library keeps
+ *    no per-call state and allocates nothing.  Work is queued on `stream`
+ *    (asynchronous: no synchronisation, no host<->device copies); buffers must
+ *    stay alive until that work completes.  Two calls that share a workspace
+ *    must be ordered on one stream.
+ *  - Return value: DCN_OK (0) or a negative status.  Every argument is checked
+ *    on the host before any HIP call; on an error nothing is launched and out
+ *    is not written.  DCN_E_HIP reports a failed kernel launch (the launch's own
+ *    return code).  No C++ exception crosses this interface.
+ *  - Arithmetic: positions and bilinear weights in fp32; bf16 samples are
+ *    interpolated in fp32 and rounded to bf16 (nearest even) before the matrix
+ *    product; products accumulate in fp32; out is rounded to dtype.
+ *  - Limits: every tensor (and the staged copy of x) has fewer than 2^31
+ *    elements; otherwise DCN_E_UNSUPPORTED.
+ *  - Variant choice: a kernel variant is picked from the descriptor.  The
+ *    environment variable DCN_VARIANT=<name> (a name dcn_variant_name can
+ *    return) pins it, for tile sweeps and tests; a name that does not exist or
+ *    was built for the other dtype makes every call return DCN_E_UNSUPPORTED.
+ */
+#ifndef DCN_H
+#define DCN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dcn_dtype { DCN_F32 = 0, DCN_BF16 = 1 };
+
+enum dcn_status {
+  DCN_OK = 0,
+  DCN_E_ARG = -1,          /* NULL required pointer, a dimension out of range, Ho or Wo < 1 */
+  DCN_E_UNSUPPORTED = -2,  /* dtype not built, or a tensor at or beyond 2^31 elements */
+  DCN_E_WORKSPACE = -3,    /* workspace NULL or smaller than dcn_workspace_bytes() */
+  DCN_E_HIP = -4           /* a kernel launch failed */
+};
+
+/* Problem descriptor.  B >= 0 and Cout >= 0 (0 means an empty output: the
+ * call succeeds and launches nothing); Cin, H, W, K, stride, dilation >= 1;
+ * pad >= 0.  One square kernel, one stride, one pad and one dilation for both
+ * axes, as in torchvision's deform_conv2d call; one offset group. */
+typedef struct dcn_desc {
+  int64_t batch, in_channels, height, width, out_channels;
+  int64_t kernel_size, stride, pad, dilation;
+  int32_t dtype;     /* enum dcn_dtype */
+  int32_t reserved;  /* must be 0 */
+} dcn_desc;
+
+/* Output size of the strided, padded, dilated window (as for a regular
+ * convolution; the offset and mask are given at this resolution):
+ *   Ho = floor((H + 2*pad - dilation*(K-1) - 1) / stride) + 1, likewise Wo.
+ * Host only.  DCN_E_ARG if desc is invalid or Ho or Wo would be < 1. */
+int dcn_output_hw(const dcn_desc* desc, int64_t* out_h, int64_t* out_w);
+
+/* Bytes of device workspace dcn_forward needs for this descriptor (a staged
+ * channels-last copy of x and the weight repacked to [Cout][K^2][Cin]; 0 for
+ * variants that read x and weight directly).  Host only; deterministic in the
+ * descriptor.  The workspace must be 256-byte aligned. */
+int dcn_workspace_bytes(const dcn_desc* desc, size_t* bytes);
+
+/* The forward pass: out = deform_conv2d(x, offset, weight, bias, stride, pad,
+ * dilation, mask).  Equivalent to dcn_stage() followed by dcn_forward_staged()
+ * on the same stream with the same arguments. */
+int dcn_forward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                const void* weight, const void* bias, void* out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* First half of dcn_forward: writes the staged copy of x and the repacked
+ * weight into the workspace (the deformable im2col reads channel vectors of x
+ * contiguously from it).  Launches nothing for variants with no workspace. */
+int dcn_stage(const dcn_desc* desc, const void* x, const void* weight,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Second half of dcn_forward: sampling, interpolation, modulation, the matrix
+ * product and the bias epilogue in one kernel, reading the workspace that
+ * dcn_stage filled for the same descriptor, x and weight.  Takes the same
+ * arguments as dcn_forward (x and weight are read directly by variants with
+ * no workspace). */
+int dcn_forward_staged(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                       const void* weight, const void* bias, void* out,
+                       const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Name of the kernel variant dcn_forward runs for this descriptor (static
+ * string; "invalid" if the descriptor is rejected). */
+const char* dcn_variant_name(const dcn_desc* desc);
+
+/* Static text for a status code. */
+const char* dcn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCN_H */

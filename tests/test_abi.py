@@ -1,0 +1,190 @@
+"""C ABI of libdcn_hip.so on the host: exports, geometry, workspace sizing and
+error paths.  No GPU: every call here returns before its first HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import deformable_convolution_vision_amd as dcn
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dcn.LIB_PATH):
+        from deformable_convolution_vision_amd import build
+        build.build()
+    return dcn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dcn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(dcn._EXPORTS) <= set(names), names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", dcn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in dcn.h but not exported"
+        assert getattr(lib, name) is not None
+
+
+def test_exports_are_plain_c(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", dcn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = re.findall(r"\bT (\w+)$", out, flags=re.M)
+    assert not [s for s in exported if s.startswith("dcn") and s.startswith("_Z")]
+
+
+GEOMS = [(1, 3, 32, 32, 8, 3, 1, 1, 1), (1, 3, 224, 224, 64, 3, 1, 1, 1), (2, 128, 100, 168, 128, 3, 1, 1, 1),
+         (2, 256, 100, 168, 256, 3, 2, 1, 1), (8, 512, 25, 42, 512, 3, 1, 2, 2), (1, 1, 1, 1, 1, 1, 1, 0, 1),
+         (3, 5, 7, 9, 2, 5, 3, 2, 2), (1, 4, 6, 5, 3, 2, 2, 0, 3), (2, 2, 13, 1, 3, 1, 4, 0, 1)]
+
+
+@pytest.mark.parametrize("g", GEOMS)
+def test_output_hw_matches_oracle(lib, g):
+    B, Cin, H, W, Cout, K, s, p, d = g
+    desc = dcn.make_desc(B, Cin, H, W, Cout, K, s, p, d, dcn.BF16)
+    assert dcn.dcn_output_hw(desc) == oracle.output_hw(B, Cin, H, W, Cout, K, s, p, d)
+
+
+def test_named_workload_sizes(lib):
+    from deformable_convolution_vision_amd.workloads import WORKLOADS
+    for w in WORKLOADS.values():
+        desc = dcn.make_desc(w.B, w.Cin, w.H, w.W, w.Cout, w.K, w.stride, w.pad, w.dilation,
+                             dcn.F32 if w.dtype == "f32" else dcn.BF16)
+        assert dcn.dcn_output_hw(desc) == (w.Ho, w.Wo), w.name
+
+
+def test_workspace_is_deterministic_and_covers_staged_copy(lib):
+    for g in GEOMS:
+        for dt, es in ((dcn.F32, 4), (dcn.BF16, 2)):
+            desc = dcn.make_desc(*g, dt)
+            a, b = dcn.dcn_workspace_bytes(desc), dcn.dcn_workspace_bytes(desc)
+            assert a == b
+            if "tile" in dcn.dcn_variant_name(desc):
+                B, Cin, H, W, Cout, K = g[:6]
+                assert a >= B * H * W * Cin * es + Cout * Cin * K * K * es
+                assert a % 256 == 0
+
+
+BAD = [
+    dict(batch=-1), dict(in_channels=0), dict(height=0), dict(width=0), dict(kernel_size=0),
+    dict(stride=0), dict(dilation=0), dict(pad=-1), dict(out_channels=-2), dict(reserved=7),
+    dict(kernel_size=9, height=4, width=4, pad=0),            # window larger than the padded input
+]
+
+
+@pytest.mark.parametrize("bad", BAD, ids=lambda b: ",".join(f"{k}={v}" for k, v in b.items()))
+def test_invalid_descriptor_is_rejected(lib, bad):
+    desc = dcn.make_desc(2, 8, 10, 12, 4, 3, 1, 1, 1, dcn.BF16)
+    for k, v in bad.items():
+        setattr(desc, k, v)
+    ho, wo = ctypes.c_int64(-7), ctypes.c_int64(-7)
+    assert lib.dcn_output_hw(ctypes.byref(desc), ctypes.byref(ho), ctypes.byref(wo)) == dcn.E_ARG
+    assert (ho.value, wo.value) == (-7, -7)
+    n = ctypes.c_size_t(12345)
+    assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_ARG
+    assert n.value == 12345
+    fake = 0x10000
+    assert lib.dcn_forward(ctypes.byref(desc), fake, fake, None, fake, None, fake, fake, 1 << 30,
+                           None) == dcn.E_ARG
+    assert dcn.dcn_variant_name(desc) == "invalid"
+
+
+def test_bad_dtype_is_unsupported(lib):
+    desc = dcn.make_desc(1, 3, 8, 8, 4, 3, 1, 1, 1, 7)
+    n = ctypes.c_size_t()
+    assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+
+
+def test_null_pointers_are_rejected_before_launch(lib):
+    desc = dcn.make_desc(1, 8, 9, 9, 4, 3, 1, 1, 1, dcn.BF16)
+    fake, ws = 0x10000, 0x20000
+    nb = dcn.dcn_workspace_bytes(desc)
+    fwd = lib.dcn_forward
+    for args in [(None, fake, fake, fake), (fake, None, fake, fake), (fake, fake, None, fake),
+                 (fake, fake, fake, None)]:
+        x, off, w, out = args
+        assert fwd(ctypes.byref(desc), x, off, None, w, None, out, ws, nb, None) == dcn.E_ARG
+    assert lib.dcn_forward(None, fake, fake, None, fake, None, fake, ws, nb, None) == dcn.E_ARG
+    assert lib.dcn_stage(ctypes.byref(desc), None, fake, ws, nb, None) == dcn.E_ARG
+
+
+def test_workspace_errors(lib):
+    desc = dcn.make_desc(2, 64, 20, 20, 32, 3, 1, 1, 1, dcn.BF16)
+    fake = 0x10000
+    nb = dcn.dcn_workspace_bytes(desc)
+    assert nb > 0
+    f = lib.dcn_forward
+    assert f(ctypes.byref(desc), fake, fake, None, fake, None, fake, None, nb, None) == dcn.E_WORKSPACE
+    assert f(ctypes.byref(desc), fake, fake, None, fake, None, fake, 0x20000, nb - 1, None) == dcn.E_WORKSPACE
+    assert f(ctypes.byref(desc), fake, fake, None, fake, None, fake, 0x20010, nb, None) == dcn.E_WORKSPACE
+    assert lib.dcn_stage(ctypes.byref(desc), fake, fake, 0x20000, nb - 256, None) == dcn.E_WORKSPACE
+    assert lib.dcn_forward_staged(ctypes.byref(desc), fake, fake, None, fake, None, fake, None, nb,
+                                  None) == dcn.E_WORKSPACE
+
+
+def test_empty_batch_or_channels_is_a_no_op(lib):
+    for desc in (dcn.make_desc(0, 8, 9, 9, 4, 3, 1, 1, 1, dcn.BF16),
+                 dcn.make_desc(2, 8, 9, 9, 0, 3, 1, 1, 1, dcn.F32)):
+        assert dcn.dcn_workspace_bytes(desc) == 0
+        # nothing is launched, so null data pointers are fine
+        assert lib.dcn_forward(ctypes.byref(desc), None, None, None, None, None, None, None, 0, None) == dcn.OK
+        assert lib.dcn_stage(ctypes.byref(desc), None, None, None, 0, None) == dcn.OK
+
+
+def test_size_limits(lib):
+    # a staged copy at or beyond 2^31 elements is refused rather than mis-indexed
+    desc = dcn.make_desc(64, 1024, 256, 256, 64, 3, 1, 1, 1, dcn.BF16)
+    n = ctypes.c_size_t()
+    assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+    desc = dcn.make_desc(1, 3, 1 << 25, 2, 4, 1, 1, 0, 1, dcn.F32)   # positions beyond exact fp32 integers
+    fake = 0x10000
+    assert lib.dcn_forward(ctypes.byref(desc), fake, fake, None, fake, None, fake, 0x20000, 1 << 40,
+                           None) == dcn.E_UNSUPPORTED
+
+
+def test_forced_variant(lib, monkeypatch):
+    desc = dcn.make_desc(2, 64, 20, 20, 32, 3, 1, 1, 1, dcn.BF16)
+    monkeypatch.setenv("DCN_VARIANT", "tile_bf16_m128_n64")
+    assert dcn.dcn_variant_name(desc) == "tile_bf16_m128_n64"
+    monkeypatch.setenv("DCN_VARIANT", "tile_f32_m64_n64")          # other dtype
+    n = ctypes.c_size_t()
+    assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+    monkeypatch.setenv("DCN_VARIANT", "no_such_variant")
+    assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+
+
+def test_status_strings(lib):
+    for s in (dcn.OK, dcn.E_ARG, dcn.E_UNSUPPORTED, dcn.E_WORKSPACE, dcn.E_HIP):
+        assert dcn.dcn_status_str(s) != "unknown status"
+    assert dcn.dcn_status_str(-99) == "unknown status"
+
+
+def test_python_binding_rejects_bad_tensors(lib):
+    import torch
+    x = torch.zeros(1, 3, 8, 8)
+    w = torch.zeros(4, 3, 3, 3)
+    off = torch.zeros(1, 18, 8, 8)
+    with pytest.raises(ValueError):          # not on a GPU
+        dcn.deform_conv2d(x, off, w, padding=1)
+    with pytest.raises(TypeError):
+        dcn.deform_conv2d(x.double(), off.double(), w.double(), padding=1)
+    with pytest.raises(ValueError):
+        dcn.deform_conv2d(x, off, torch.zeros(4, 2, 3, 3), padding=1)

@@ -1,0 +1,174 @@
+"""The HIP path against the CPU oracle, through the C ABI, on an MI355X.
+
+Tolerance: per output, |y_gpu - y_oracle| / sum|terms| <= 1e-4 (fp32) or 1e-2
+(bf16), exact where the sum of |terms| is 0."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import deformable_convolution_vision_amd as dcn
+import oracle
+from deformable_convolution_vision_amd.workloads import WORKLOADS, custom, generate
+from gpu_common import TOL, check, full_parity, run_hip, sampled_parity, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def make(name, dtype, B, Cin, H, W, Cout, K, s, p, d, **kw):
+    Ho, Wo = oracle.output_hw(B, Cin, H, W, Cout, K, s, p, d)
+    return custom(name, dtype, B, Cin, H, W, Cout, K, s, p, d, Ho, Wo, **kw)
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.name}", flush=True)
+    yield
+
+
+@pytest.mark.parametrize("name", ["tiny", "single224"])
+def test_named_workload_full(name):
+    print(f"[gpu-test] variant {variant_of(WORKLOADS[name])}", flush=True)
+    full_parity(WORKLOADS[name])
+
+
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_named_workload_sampled(name):
+    print(f"[gpu-test] variant {variant_of(WORKLOADS[name])}", flush=True)
+    sampled_parity(WORKLOADS[name])
+
+
+def variant_of(w):
+    return dcn.dcn_variant_name(dcn.make_desc(w.B, w.Cin, w.H, w.W, w.Cout, w.K, w.stride, w.pad, w.dilation,
+                                              dcn.F32 if w.dtype == "f32" else dcn.BF16))
+
+
+EDGE = [
+    ("ragged", dict(B=3, Cin=37, H=11, W=13, Cout=70, K=3, s=1, p=1, d=1, offset="normal:2")),
+    ("k1", dict(B=2, Cin=16, H=9, W=7, Cout=24, K=1, s=1, p=0, d=1)),
+    ("k5_s3_d2", dict(B=1, Cin=12, H=23, W=19, Cout=40, K=5, s=3, p=2, d=2, offset="normal:3")),
+    ("hw1", dict(B=2, Cin=8, H=1, W=1, Cout=5, K=3, s=1, p=1, d=1)),
+    ("no_mask_no_bias", dict(B=2, Cin=33, H=10, W=12, Cout=17, K=3, s=1, p=1, d=1, mask=None, bias=None)),
+    ("odd_stride2", dict(B=1, Cin=40, H=15, W=17, Cout=66, K=3, s=2, p=1, d=1)),
+    ("cin3", dict(B=2, Cin=3, H=20, W=21, Cout=9, K=3, s=1, p=1, d=1, offset="uniform:2")),
+    ("cout300", dict(B=1, Cin=64, H=12, W=14, Cout=300, K=3, s=1, p=1, d=1)),
+    ("far_offsets_d2", dict(B=2, Cin=24, H=13, W=11, Cout=20, K=3, s=1, p=2, d=2, offset="uniform:8",
+                            mask=None)),
+    ("many_pixels", dict(B=1, Cin=32, H=64, W=96, Cout=64, K=3, s=1, p=1, d=1)),
+    ("pad0_k2", dict(B=2, Cin=8, H=6, W=9, Cout=3, K=2, s=1, p=0, d=1, offset="normal:1.5")),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shape(name, kw, dtype):
+    kw = dict(kw)
+    g = {k: kw.pop(k) for k in ("B", "Cin", "H", "W", "Cout", "K", "s", "p", "d")}
+    w = make(name, dtype, g["B"], g["Cin"], g["H"], g["W"], g["Cout"], g["K"], g["s"], g["p"], g["d"],
+             seed=zlib.crc32(name.encode()) % 1000, **kw)
+    print(f"[gpu-test] {w} variant {variant_of(w)}", flush=True)
+    full_parity(w)
+
+
+def _variants(dtype):
+    names = []
+    for v in ("tile_f32_m64_n64", "tile_f32_m128_n64", "tile_bf16_m64_n64", "tile_bf16_m128_n64",
+              "tile_bf16_m128_n32", "tile_bf16_m256_n64"):
+        if ("bf16" in v) == (dtype == "bf16"):
+            names.append(v)
+    return names
+
+
+@pytest.mark.parametrize("variant", _variants("f32") + _variants("bf16"))
+def test_every_variant(variant, monkeypatch):
+    dtype = "bf16" if "bf16" in variant else "f32"
+    monkeypatch.setenv("DCN_VARIANT", variant)
+    for seed, shape in enumerate([(3, 37, 11, 13, 70, 3, 1, 1, 1), (2, 64, 9, 10, 260, 3, 2, 1, 1)]):
+        w = make(f"sweep_{variant}", dtype, *shape, offset="normal:2", seed=seed)
+        assert variant_of(w) == variant
+        full_parity(w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_samples_outside_gives_bias(dtype):
+    w = make("outside", dtype, 2, 20, 9, 10, 12, 3, 1, 1, 1)
+    inp = generate(w)
+    inp["offset"] = torch.full_like(inp["offset"], 100.5)
+    out = run_hip(w, to_gpu(inp)).cpu()
+    assert torch.equal(out, inp["bias"][None, :, None, None].expand_as(out))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nonfinite_offsets_contribute_zero(dtype):
+    w = make("nonfinite", dtype, 2, 24, 9, 10, 12, 3, 1, 1, 1, offset="normal:2")
+    inp = generate(w)
+    off = inp["offset"].float().clone()
+    g = torch.Generator().manual_seed(3)
+    sel = torch.rand(off.shape, generator=g) < 0.2
+    specials = torch.tensor([float("nan"), float("inf"), -float("inf"), 1e30, -1e30])
+    pick = torch.randint(0, len(specials), off.shape, generator=g)
+    off[sel] = specials[pick[sel]]
+    inp["offset"] = off.to(inp["x"].dtype)
+    out = run_hip(w, to_gpu(inp)).cpu()
+    assert torch.isfinite(out).all()
+    y, a = oracle.forward(inp["x"], inp["offset"], inp["weight"], inp["bias"], 1, 1, 1, mask=inp["mask"])
+    check(out.float().numpy(), y, a, TOL[dtype], "nonfinite offsets")
+
+
+def test_deterministic_and_stage_split_matches():
+    w = WORKLOADS["c4"]
+    g = to_gpu(generate(w))
+    outs = [run_hip(w, g) for _ in range(3)]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    desc = dcn.describe(g["x"], g["weight"], w.stride, w.pad, w.dilation)
+    nb = dcn.dcn_workspace_bytes(desc)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(outs[0])
+    dcn.dcn_stage(desc, g["x"], g["weight"], ws, nb)
+    dcn.dcn_forward_staged(desc, g["x"], g["offset"], g["mask"], g["weight"], g["bias"], out, ws, nb)
+    torch.cuda.synchronize()
+    assert torch.equal(out, outs[0])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_guard_bands_untouched(dtype):
+    w = make("guard", dtype, 2, 40, 11, 12, 70, 3, 1, 1, 1)
+    g = to_gpu(generate(w))
+    desc = dcn.describe(g["x"], g["weight"], w.stride, w.pad, w.dilation)
+    nb = dcn.dcn_workspace_bytes(desc)
+    G = 4096
+    n_out = w.B * w.Cout * w.Ho * w.Wo
+    tdt = g["x"].dtype
+    out_buf = torch.full((n_out + 2 * G,), 1234.5, dtype=tdt, device="cuda")
+    ws_buf = torch.full((nb + 2 * G * 4,), 77, dtype=torch.uint8, device="cuda")
+    out_view = out_buf[G:G + n_out]
+    ws_view = ws_buf[4 * G:4 * G + nb]
+    assert ws_view.data_ptr() % 256 == 0
+    dcn.dcn_forward(desc, g["x"], g["offset"], g["mask"], g["weight"], g["bias"], out_view, ws_view, nb)
+    torch.cuda.synchronize()
+    assert torch.all(out_buf[:G] == 1234.5) and torch.all(out_buf[G + n_out:] == 1234.5)
+    assert torch.all(ws_buf[:4 * G] == 77) and torch.all(ws_buf[4 * G + nb:] == 77)
+    ref = run_hip(w, g)
+    assert torch.equal(out_view.view_as(ref), ref)
+
+
+def test_error_leaves_output_untouched():
+    w = make("err", "bf16", 1, 8, 9, 9, 4, 3, 1, 1, 1)
+    g = to_gpu(generate(w))
+    desc = dcn.describe(g["x"], g["weight"], 1, 1, 1)
+    nb = dcn.dcn_workspace_bytes(desc)
+    out = torch.full((1, 4, 9, 9), 5.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dcn.DcnError) as e:
+        dcn.dcn_forward(desc, g["x"], g["offset"], g["mask"], g["weight"], None, out, None, nb)
+    assert e.value.status == dcn.E_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(out == 5.0)
+
+
+def test_empty_batch():
+    x = torch.zeros(0, 8, 9, 9, device="cuda")
+    out = dcn.deform_conv2d(x, torch.zeros(0, 18, 9, 9, device="cuda"), torch.zeros(4, 8, 3, 3, device="cuda"),
+                            padding=1)
+    assert out.shape == (0, 4, 9, 9)
