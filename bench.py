@@ -179,7 +179,8 @@ def cpu_baseline(w, host, target_s: float):
     import oracle
     kw = dict(mask=host["mask"], with_abs=False)
     args = (host["x"], host["offset"], host["weight"], host["bias"], w.stride, w.pad, w.dilation)
-    n1 = max(1, min(w.Cout, 2))
+    n1 = max(1, min(w.Cout, 4))
+    oracle.forward(*args, cout_range=(0, 1), **kw)          # first-touch warm-up
     t = time.perf_counter()
     oracle.forward(*args, cout_range=(0, n1), **kw)
     t1 = time.perf_counter() - t
@@ -195,6 +196,24 @@ def cpu_baseline(w, host, target_s: float):
             "affinity_cores": len(os.sched_getaffinity(0))}
 
 
+def copy_calibration(nbytes: int, reps: int) -> int:
+    """A plain copy of known size, so HBM counters can be scaled to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps, "ms_per_copy": round(ms, 5),
+                      "gbps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +223,8 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="also print one line per other named workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
@@ -214,6 +235,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_bytes:
+        return copy_calibration(args.copy_bytes, max(args.steps, 1))
     names = [args.workload]
     if args.all:
         from deformable_convolution_vision_amd.workloads import ORDER

@@ -19,7 +19,7 @@ import os
 import torch
 
 __all__ = ["Desc", "dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_stage",
-           "dcn_forward_staged", "dcn_variant_name", "dcn_status_str", "deform_conv2d",
+           "dcn_forward_staged", "dcn_variant_name", "dcn_plan_describe", "dcn_status_str", "deform_conv2d",
            "DcnError", "library_path", "load_library", "F32", "BF16"]
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,7 @@ F32, BF16 = 0, 1
 OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 _EXPORTS = ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_stage", "dcn_forward_staged",
-            "dcn_variant_name", "dcn_status_str")
+            "dcn_variant_name", "dcn_plan_describe", "dcn_status_str")
 
 
 class DcnError(RuntimeError):
@@ -74,6 +74,8 @@ def load_library() -> ctypes.CDLL:
     lib.dcn_stage.argtypes = [D, P, P, P, S, P]
     lib.dcn_variant_name.argtypes = [D]
     lib.dcn_variant_name.restype = ctypes.c_char_p
+    lib.dcn_plan_describe.argtypes = [D, ctypes.c_char_p, ctypes.c_size_t]
+    lib.dcn_plan_describe.restype = ctypes.c_int
     lib.dcn_status_str.argtypes = [ctypes.c_int]
     lib.dcn_status_str.restype = ctypes.c_char_p
     for name in ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_forward_staged", "dcn_stage"):
@@ -108,6 +110,14 @@ def dcn_workspace_bytes(desc: Desc) -> int:
 
 def dcn_variant_name(desc: Desc) -> str:
     return load_library().dcn_variant_name(ctypes.byref(desc)).decode()
+
+
+def dcn_plan_describe(desc: Desc) -> str:
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().dcn_plan_describe(ctypes.byref(desc), buf, len(buf))
+    if rc != OK:
+        raise DcnError(rc, "dcn_plan_describe")
+    return buf.value.decode()
 
 
 def _ptr(t) -> int | None:

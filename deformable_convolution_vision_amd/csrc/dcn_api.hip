@@ -5,7 +5,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <limits>
@@ -32,6 +35,13 @@ int64_t out_extent(int64_t in, int64_t K, int64_t stride, int64_t pad, int64_t d
   return span < 0 ? 0 : span / stride + 1;
 }
 
+struct BoxPlan {
+  int fm = 0, fn = 0;           // MT = 64*fm output channels, 16*fn pixel slots
+  int TH = 0, TW = 0, tiles_x = 0, tiles_per_img = 0;
+  int box_px = 0, lds = 0;
+  double cost = 1e300;
+};
+
 struct Plan {
   int64_t Ho = 0, Wo = 0;
   int variant = -1;
@@ -39,6 +49,7 @@ struct Plan {
   size_t ws_x = 0, ws_w = 0;    // workspace byte offsets
   size_t ws_bytes = 0;
   bool empty = false;           // B == 0 or Cout == 0: nothing to launch
+  BoxPlan box;
 };
 
 bool geometry_ok(const dcn_desc* d) {
@@ -55,10 +66,76 @@ bool geometry_ok(const dcn_desc* d) {
   return true;
 }
 
+// Tile plan of the box kernel: the output tile (TH x TW pixels of one image by
+// 64*fm output channels) minimising an estimate of the time of the busiest CU,
+// assuming one workgroup per CU on 256 CUs.  Per reduction step (32 channels of one
+// kernel point) a SIMD runs one consumer wave (fm*fn MFMA 16x16x32, 16 cycles each)
+// next to one producer wave (about 50 VALU instructions of 4 cycles per 64 column
+// units); per workgroup the vector-memory pipe moves the weight rows and the input
+// box at about 50 bytes per cycle.  The workgroup time is the larger of the two,
+// times the number of rounds of workgroups.
+bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* out) {
+  if (d->dtype != DCN_BF16) return false;
+  if (d->height > 32000 || d->width > 32000) return false;
+  const int64_t K = d->kernel_size, KK = K * K;
+  if (KK > dcn::kBoxMaxKK) return false;
+  const int64_t M = d->out_channels, Cp = round_up(d->in_channels, 32), Kr = Cp * KK;
+  const int64_t s = d->stride, dil = d->dilation;
+  const int64_t steps = (Cp / 32) * KK;
+  BoxPlan best;
+  for (int fm = 2; fm <= 4; fm += 2) {
+    if (fm_only && fm != fm_only) continue;
+    const int64_t MT = 64 * fm, m_tiles = (M + MT - 1) / MT;
+    for (int fn : {4, 5, 6, 8, 9}) {
+      if (fm == 4 && fn > 5) continue;
+      const int NT = 16 * fn;
+      const int box_px = dcn::box_capacity_px(fn);
+      if (box_px < 64) continue;
+      for (int TH = 1; TH <= 16; ++TH) {
+        for (int dw = 0; dw < 2; ++dw) {
+          const int TW = NT / TH - dw;
+          if (TW < 1 || (TH * TW + 15) / 16 != fn) continue;
+          const int64_t bh0 = (TH - 1) * s + (K - 1) * dil + 2, bw0 = (TW - 1) * s + (K - 1) * dil + 2;
+          if (bh0 * bw0 > box_px) continue;
+          const int64_t ty = (Ho + TH - 1) / TH, tx = (Wo + TW - 1) / TW;
+          const int64_t tiles = d->batch * ty * tx * m_tiles;
+          if (tiles > (int64_t(1) << 30)) continue;
+          const double est_box = std::min<double>(std::min<double>((bh0 + 6) * (bw0 + 6), box_px),
+                                                  (d->height + 2.0) * (d->width + 2.0));
+          const double mfma_step = double(fm) * fn * 16;
+          const double valu_step = std::ceil(NT * 4 / 256.0) * 50 * 4 + 40;
+          const double compute = steps * std::max(mfma_step, valu_step);
+          const double mem = (double(MT) * Kr * 2 + est_box * Cp * 2) / 50;
+          const double wg = std::max(compute, mem) + 4000;
+          const double rounds = std::ceil(double(tiles) / 256);
+          const double cost = rounds * wg;
+          if (cost < best.cost) {
+            best.fm = fm;
+            best.fn = fn;
+            best.TH = TH;
+            best.TW = TW;
+            best.tiles_x = static_cast<int>(tx);
+            best.tiles_per_img = static_cast<int>(ty * tx);
+            best.box_px = box_px;
+            best.lds = dcn::kLdsBudget;
+            best.cost = cost;
+          }
+        }
+      }
+    }
+  }
+  if (best.fm == 0) return false;
+  *out = best;
+  return true;
+}
+
 // Pick the kernel variant for a valid descriptor.
-int choose_variant(const dcn_desc* d, int64_t N) {
+int choose_variant(const dcn_desc* d, int64_t N, int64_t Ho, int64_t Wo, BoxPlan* bp) {
   const int64_t M = d->out_channels;
   if (d->dtype == DCN_F32) return M <= 64 ? dcn::V_TILE_F32_M64_N64 : dcn::V_TILE_F32_M128_N64;
+  // the box kernel for channel counts where a 32-channel chunk is mostly real data
+  if (d->in_channels >= 24 && M >= 64 && plan_box(d, Ho, Wo, 0, bp))
+    return bp->fm == 2 ? dcn::V_BOX_BF16_M128 : dcn::V_BOX_BF16_M256;
   if (M <= 64) return dcn::V_TILE_BF16_M64_N64;
   // enough workgroups to cover 256 CUs with the wider tile?
   if (M >= 256 && (N + 63) / 64 * ((M + 255) / 256) >= 512) return dcn::V_TILE_BF16_M256_N64;
@@ -76,7 +153,7 @@ int make_plan(const dcn_desc* d, Plan* p) {
   const int64_t Cout = d->out_channels, K = d->kernel_size, KK = K * K;
   const int64_t HoWo = p->Ho * p->Wo;
   const int64_t N = B * HoWo;
-  p->variant = choose_variant(d, N);
+  p->variant = choose_variant(d, N, p->Ho, p->Wo, &p->box);
   // DCN_VARIANT=<name> pins the kernel variant (tile sweeps and tests); an
   // unknown name or one built for the other dtype is rejected.
   if (const char* force = std::getenv("DCN_VARIANT")) {
@@ -85,6 +162,9 @@ int make_plan(const dcn_desc* d, Plan* p) {
       for (int v = 0; v < dcn::V_COUNT; ++v)
         if (std::strcmp(force, dcn::variant_info(v).name) == 0) found = v;
       if (found < 0 || dcn::variant_info(found).is_bf16 != (d->dtype == DCN_BF16)) return DCN_E_UNSUPPORTED;
+      if (found == dcn::V_BOX_BF16_M128 || found == dcn::V_BOX_BF16_M256) {
+        if (!plan_box(d, p->Ho, p->Wo, found == dcn::V_BOX_BF16_M128 ? 2 : 4, &p->box)) return DCN_E_UNSUPPORTED;
+      }
       p->variant = found;
     }
   }
@@ -134,6 +214,7 @@ StageArgs stage_args(const dcn_desc* d, const Plan& p, const void* x, const void
 FusedArgs fused_args(const dcn_desc* d, const Plan& p, const void* x, const void* offset, const void* mask,
                      const void* w, const void* bias, void* out, const void* ws) {
   const dcn::VariantInfo& vi = dcn::variant_info(p.variant);
+  const int nt = vi.nt > 0 ? vi.nt : 16 * p.box.fn;
   FusedArgs a{};
   a.xs = ws ? static_cast<const unsigned char*>(ws) + p.ws_x : nullptr;
   a.wp = ws ? static_cast<const unsigned char*>(ws) + p.ws_w : nullptr;
@@ -159,8 +240,24 @@ FusedArgs fused_args(const dcn_desc* d, const Plan& p, const void* x, const void
   a.HoWo = a.Ho * a.Wo;
   a.N = a.B * a.HoWo;
   a.m_tiles = static_cast<int>(p.Mp / vi.mt);
-  a.n_tiles = (a.N + vi.nt - 1) / vi.nt;
+  a.n_tiles = (a.N + nt - 1) / nt;
   return a;
+}
+
+bool is_box(int variant) { return variant == dcn::V_BOX_BF16_M128 || variant == dcn::V_BOX_BF16_M256; }
+
+hipError_t launch_fused_plan(const Plan& p, const FusedArgs& a, hipStream_t stream) {
+  if (!is_box(p.variant)) return dcn::launch_fused(p.variant, a, stream);
+  dcn::BoxArgs ba{};
+  ba.f = a;
+  ba.TH = p.box.TH;
+  ba.TW = p.box.TW;
+  ba.tiles_x = p.box.tiles_x;
+  ba.tiles_per_img = p.box.tiles_per_img;
+  ba.box_px = p.box.box_px;
+  ba.KK_NT = a.KK * 16 * p.box.fn;
+  ba.lds_bytes = 0;
+  return dcn::launch_box(p.box.fm, p.box.fn, ba, stream);
 }
 
 int check_positions(const dcn_desc* d, int64_t K, int64_t stride, int64_t pad, int64_t dil, int64_t Ho,
@@ -199,6 +296,27 @@ extern "C" const char* dcn_variant_name(const dcn_desc* desc) {
   Plan p;
   if (make_plan(desc, &p) != DCN_OK) return "invalid";
   return dcn::variant_info(p.variant).name;
+}
+
+extern "C" int dcn_plan_describe(const dcn_desc* desc, char* buf, size_t len) {
+  if (buf == nullptr || len == 0) return DCN_E_ARG;
+  Plan p;
+  const int rc = make_plan(desc, &p);
+  if (rc != DCN_OK) {
+    buf[0] = '\0';
+    return rc;
+  }
+  const dcn::VariantInfo& vi = dcn::variant_info(p.variant);
+  if (is_box(p.variant)) {
+    std::snprintf(buf, len,
+                  "%s tile=%dx%d px (%d slots) x %d ch, tiles=%lld, box_px=%d, ws=%zu B",
+                  vi.name, p.box.TH, p.box.TW, 16 * p.box.fn, 64 * p.box.fm,
+                  static_cast<long long>(desc->batch) * p.box.tiles_per_img * (p.Mp / (64 * p.box.fm)),
+                  p.box.box_px, p.ws_bytes);
+  } else {
+    std::snprintf(buf, len, "%s tile=%d px x %d ch, ws=%zu B", vi.name, vi.nt, vi.mt, p.ws_bytes);
+  }
+  return DCN_OK;
 }
 
 extern "C" const char* dcn_status_str(int status) {
@@ -248,7 +366,7 @@ extern "C" int dcn_forward_staged(const dcn_desc* desc, const void* x, const voi
   rc = check_workspace(p, workspace, workspace_bytes);
   if (rc != DCN_OK) return rc;
   const FusedArgs a = fused_args(desc, p, x, offset, mask, weight, bias, out, workspace);
-  return dcn::launch_fused(p.variant, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
+  return launch_fused_plan(p, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
 }
 
 extern "C" int dcn_forward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
@@ -265,5 +383,5 @@ extern "C" int dcn_forward(const dcn_desc* desc, const void* x, const void* offs
     if (dcn::launch_stage(p.variant, s, stream) != hipSuccess) return DCN_E_HIP;
   }
   const FusedArgs a = fused_args(desc, p, x, offset, mask, weight, bias, out, workspace);
-  return dcn::launch_fused(p.variant, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
+  return launch_fused_plan(p, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
 }

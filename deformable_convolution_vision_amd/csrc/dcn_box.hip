@@ -1,0 +1,467 @@
+// dcn_box.hip -- gfx950 fused deformable-convolution kernel for bf16 with an LDS input box.
+//
+// One workgroup computes an MT x (TH x TW) tile: MT output channels by a rectangular
+// TH x TW block of output pixels of one image.  It runs eight wave64, two per SIMD:
+//
+//  * four producer waves build the column matrix of the deformable im2col, one
+//    (32-channel chunk, kernel point) step at a time, into a double-buffered LDS
+//    tile.  The sampling positions, bilinear corner weights times the mask and the
+//    corner offsets are computed once per (pixel, kernel point) in the prologue and
+//    kept in an LDS table.  For each 32-channel chunk the producers copy the
+//    rectangle of the channels-last input that the tile's samples touch (the "box":
+//    its extent comes from the tile's own offsets, clipped to one pixel around the
+//    image) into LDS with direct global->LDS loads, one chunk ahead, so each input
+//    vector crosses the vector-memory pipe once per chunk instead of once per
+//    (sample, corner).  A sample is interpolated from the box with two bf16 dot
+//    products per channel (corner pairs built with byte permutes); samples whose
+//    corners lie outside the box are read from the channels-last copy in global
+//    memory instead;
+//  * four consumer waves multiply the previous step's column tile with MFMA
+//    16x16x32 bf16 against their rows of the repacked weight, which they stream
+//    from L2 straight into registers through a four-deep prefetch ring, and
+//    accumulate in fp32.
+//
+// On each SIMD the producer's VALU work overlaps the consumer's matrix work.  The
+// two box buffers are separate LDS arrays (and the producer loop is instantiated
+// once per buffer parity) so the compiler can tell the copy into one from the reads
+// of the other and does not make reads wait for the copy.
+//
+// The computation follows the deformable-convolution equation (csdn.net tags page
+// "可变形卷积：Deformable ConvNets", part "Deformable Convolutional Networks",
+// section on deformable convolution), with the DCNv2 modulation scalar (same page,
+// section 3.2) and bilinear interpolation from the four integer neighbours (same
+// page, bilinear-interpolation equation); neighbours outside the image contribute 0.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "dcn_internal.h"
+
+namespace dcn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kThreads = 512;    // 4 consumer + 4 producer waves
+constexpr int kCK = 32;          // channels per reduction chunk (one MFMA k-step)
+constexpr int kPXB = 64;         // bytes per box pixel (32 bf16 channels)
+constexpr int kCOLB = 80;        // bytes per column-tile row (64 + 16 pad)
+constexpr int kRing = 4;         // weight-fragment prefetch ring depth
+
+// corner-table entry of one (kernel point, pixel)
+struct CEnt {
+  int off;      // >= 0: byte offset of corner (y0, x0) in a box buffer; -1: read from global; -2: zero
+  int yx;       // (y0 + 1) << 16 | (x0 + 1), for the global path
+  uint32_t w01, w23;
+};
+
+template <int FN>
+struct BoxCfg {
+  static constexpr int NT = 16 * FN;
+  static constexpr int COL_BYTES = 2 * NT * kCOLB;
+  static constexpr int CTAB_BYTES = kBoxMaxKK * NT * 16;
+  // what is left of the LDS, split into two box buffers, in 16-pixel blocks
+  static constexpr int BOX_PX = ((kLdsBudget - COL_BYTES - CTAB_BYTES - 64) / (2 * kPXB)) / 16 * 16;
+};
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// 8 channels of one sample from the four corner vectors (row 0: q00, q01; row 1:
+// q10, q11) and the packed bf16 weight pairs w01 = (w00, w01), w23 = (w10, w11).
+__device__ __forceinline__ uint4 interp8(uint4 q00, uint4 q01, uint4 q10, uint4 q11, uint32_t w01, uint32_t w23) {
+  const uint32_t a0[4] = {q00.x, q00.y, q00.z, q00.w};
+  const uint32_t a1[4] = {q01.x, q01.y, q01.z, q01.w};
+  const uint32_t b0[4] = {q10.x, q10.y, q10.z, q10.w};
+  const uint32_t b1[4] = {q11.x, q11.y, q11.z, q11.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // (x00.c, x01.c) and (x10.c, x11.c) for the low channel, then the high one
+    const uint32_t p0lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
+    const uint32_t p0hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
+    const uint32_t p1lo = __builtin_amdgcn_perm(b1[e], b0[e], 0x05040100u);
+    const uint32_t p1hi = __builtin_amdgcn_perm(b1[e], b0[e], 0x07060302u);
+    const float lo = dot2(p1lo, w23, dot2(p0lo, w01, 0.f));
+    const float hi = dot2(p1hi, w23, dot2(p0hi, w01, 0.f));
+    r[e] = pk_bf16(lo, hi);
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+__device__ __forceinline__ int xcd_tile(int g, int T) {
+  const int xcd = g & 7, idx = g >> 3;
+  const int q = T >> 3, r = T & 7;
+  return xcd * q + min(xcd, r) + idx;
+}
+
+__device__ __forceinline__ float ld_bf16(const void* p, int idx) {
+  const uint16_t v = reinterpret_cast<const uint16_t*>(p)[idx];
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are complete
+// and visible, outstanding global loads stay in flight.  The "memory" clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+}  // namespace
+
+template <int FM, int FN>
+__global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
+  using Cfg = BoxCfg<FN>;
+  const FusedArgs& a = ba.f;
+  constexpr int WM = 16 * FM;         // rows per consumer wave
+  constexpr int MT = 4 * WM;          // rows per workgroup
+  constexpr int NT = Cfg::NT;         // pixel slots per workgroup
+  constexpr int GUNITS = NT * 4;      // 16-byte column units per chunk
+  constexpr int GU = (GUNITS + 255) / 256;
+  constexpr int BOXB = Cfg::BOX_PX * kPXB;
+
+  __shared__ __attribute__((aligned(16))) unsigned char col[Cfg::COL_BYTES];
+  __shared__ __attribute__((aligned(16))) CEnt ctab[kBoxMaxKK * NT];
+  __shared__ __attribute__((aligned(16))) unsigned char box0[BOXB];
+  __shared__ __attribute__((aligned(16))) unsigned char box1[BOXB];
+  __shared__ int red[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool consumer = wv < 4;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int KK = a.KK, Cp = a.Cp, K = a.K;
+  const int T = a.m_tiles * ba.tiles_per_img * a.B;
+  const int t = xcd_tile(blockIdx.x, T);
+  const int mt = t % a.m_tiles;
+  const int pt = t / a.m_tiles;
+  const int b = pt / ba.tiles_per_img;
+  const int rt = pt - b * ba.tiles_per_img;
+  const int ty = rt / ba.tiles_x, tx = rt - (rt / ba.tiles_x) * ba.tiles_x;
+  const int oy0 = ty * ba.TH, ox0 = tx * ba.TW;
+  const int m0 = mt * MT;
+  const int nCC = Cp / kCK;
+  const int S = nCC * KK;
+
+  const unsigned char* xs = reinterpret_cast<const unsigned char*>(a.xs);
+  const unsigned char* wp = reinterpret_cast<const unsigned char*>(a.wp);
+
+  // ---- consumer state: weight-fragment ring (four named slots, never addressed)
+  struct AFrag { uint4 v[FM]; };
+  auto load_a = [&](int s) -> AFrag {
+    AFrag r;
+    const int cc = s / KK, k = s - (s / KK) * KK;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const size_t row = static_cast<size_t>(m0 + wv * WM + fm * 16 + lrow);
+      const size_t e = (row * KK + k) * Cp + cc * kCK + lgrp * 8;
+      r.v[fm] = *reinterpret_cast<const uint4*>(wp + e * 2);
+    }
+    return r;
+  };
+  AFrag a0{}, a1{}, a2{}, a3{};
+  if (consumer) {
+    a0 = load_a(0);
+    a1 = load_a(min(1, S - 1));
+    a2 = load_a(min(2, S - 1));
+  }
+
+  // ---- prologue pass 1 (all waves): sampling positions and weights; extent of the upper corners
+  if (tid < 4) red[tid] = (tid & 1) ? -0x40000000 : 0x40000000;   // min y, max y, min x, max x
+  __syncthreads();
+  int lminy = 0x40000000, lmaxy = -0x40000000, lminx = 0x40000000, lmaxx = -0x40000000;
+  const int ntile = ba.TH * ba.TW;
+  for (int e = tid; e < KK * NT; e += kThreads) {
+    const int k = e / NT, p = e - (e / NT) * NT;
+    CEnt ce;
+    ce.off = -2;
+    ce.yx = 0;
+    ce.w01 = 0u;
+    ce.w23 = 0u;
+    const int py = p / ba.TW, px = p - (p / ba.TW) * ba.TW;
+    const int oy = oy0 + py, ox = ox0 + px;
+    if (p < ntile && oy < a.Ho && ox < a.Wo) {
+      const int i = k / K, j = k - (k / K) * K;
+      const int rem = oy * a.Wo + ox;
+      const int ob = (b * 2 * KK + 2 * k) * a.HoWo + rem;
+      const float dy = ld_bf16(a.offset, ob);
+      const float dx = ld_bf16(a.offset, ob + a.HoWo);
+      const float m = a.mask ? ld_bf16(a.mask, (b * KK + k) * a.HoWo + rem) : 1.f;
+      // integer and fractional parts of the offset are exact in fp32
+      const float fy = floorf(dy), fx = floorf(dx);
+      const float ly = dy - fy, lx = dx - fx;
+      const float y0 = static_cast<float>(oy * a.stride - a.pad + i * a.dil) + fy;
+      const float x0 = static_cast<float>(ox * a.stride - a.pad + j * a.dil) + fx;
+      // at least one corner inside the image (float tests first: NaN fails them all)
+      if (y0 >= -1.f && y0 <= static_cast<float>(a.H - 1) && x0 >= -1.f && x0 <= static_cast<float>(a.W - 1)) {
+        const int iy = static_cast<int>(y0), ix = static_cast<int>(x0);
+        const float hy = 1.f - ly, hx = 1.f - lx;
+        ce.off = -1;
+        ce.yx = ((iy + 1) << 16) | (ix + 1);
+        ce.w01 = pk_bf16(hy * hx * m, hy * lx * m);
+        ce.w23 = pk_bf16(ly * hx * m, ly * lx * m);
+        lminy = min(lminy, iy);
+        lmaxy = max(lmaxy, iy);
+        lminx = min(lminx, ix);
+        lmaxx = max(lmaxx, ix);
+      }
+    }
+    ctab[e] = ce;
+  }
+  if (lminy <= lmaxy) {
+    atomicMin(&red[0], lminy);
+    atomicMax(&red[1], lmaxy);
+    atomicMin(&red[2], lminx);
+    atomicMax(&red[3], lmaxx);
+  }
+  __syncthreads();
+
+  // ---- box geometry (uniform): rows [by0, by0+BH), cols [bx0, bx0+BW) within [-1, H] x [-1, W]
+  int by0, bx0, BH, BW;
+  {
+    int y_lo = red[0], y_hi = red[1] + 1, x_lo = red[2], x_hi = red[3] + 1;  // corner rows/cols
+    if (y_lo > y_hi) { y_lo = 0; y_hi = 0; x_lo = 0; x_hi = 0; }           // tile has no samples
+    y_lo = max(y_lo, -1);
+    y_hi = min(y_hi, a.H);
+    x_lo = max(x_lo, -1);
+    x_hi = min(x_hi, a.W);
+    BH = y_hi - y_lo + 1;
+    BW = x_hi - x_lo + 1;
+    by0 = y_lo;
+    bx0 = x_lo;
+    if (BH * BW > Cfg::BOX_PX) {
+      // too wide for LDS: keep the window the tile's samples would use without
+      // offsets, widened evenly as far as the budget allows; the rest goes global
+      const int bh0 = (ba.TH - 1) * a.stride + (K - 1) * a.dil + 2;
+      const int bw0 = (ba.TW - 1) * a.stride + (K - 1) * a.dil + 2;
+      int mg = 0;
+      while ((bh0 + 2 * (mg + 1)) * (bw0 + 2 * (mg + 1)) <= Cfg::BOX_PX) ++mg;
+      by0 = max(oy0 * a.stride - a.pad - mg, -1);
+      bx0 = max(ox0 * a.stride - a.pad - mg, -1);
+      BH = min(bh0 + 2 * mg, a.H + 1 - by0);
+      BW = min(bw0 + 2 * mg, a.W + 1 - bx0);
+      if (BH * BW > Cfg::BOX_PX) { BH = 1; BW = 1; }   // not reached: the host checks the base window fits
+    }
+  }
+  const int npx = BH * BW;
+
+  // ---- prologue pass 2: corner offsets inside the box; zero the box pixels outside the image;
+  // chunk 0 of the box (all waves)
+  for (int e = tid; e < KK * NT; e += kThreads) {
+    const CEnt ce = ctab[e];
+    if (ce.off == -1) {
+      const int ry = (ce.yx >> 16) - 1 - by0, rx = (ce.yx & 0xffff) - 1 - bx0;
+      if (ry >= 0 && ry + 1 < BH && rx >= 0 && rx + 1 < BW) ctab[e].off = (ry * BW + rx) * kPXB;
+    }
+  }
+  for (int u = tid; u < npx * 4; u += kThreads) {
+    const int px = u >> 2;
+    const int gy = by0 + px / BW, gx = bx0 + px - (px / BW) * BW;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (gy >= 0 && gy < a.H && gx >= 0 && gx < a.W) {
+      const size_t e = (static_cast<size_t>(b * a.H + gy) * a.W + gx) * Cp + (u & 3) * 8;
+      v = *reinterpret_cast<const uint4*>(xs + e * 2);
+    } else {
+      *reinterpret_cast<uint4*>(box1 + px * kPXB + (u & 3) * 16) = v;
+    }
+    *reinterpret_cast<uint4*>(box0 + px * kPXB + (u & 3) * 16) = v;
+  }
+  __syncthreads();
+
+  if (consumer) {
+    // ================= consumers: MFMA on the previous step's column tile =================
+    floatx4 acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto mma = [&](int s, const AFrag& af) {
+      const unsigned char* csrc = col + (s & 1) * NT * kCOLB;
+      bf16x8 bfr[FN];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        bfr[fn] = *reinterpret_cast<const bf16x8*>(csrc + (fn * 16 + lrow) * kCOLB + lgrp * 16);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, af.v[fm]);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bfr[fn], acc[fm][fn], 0, 0, 0);
+      }
+    };
+    // step s: multiply chunk s-1, refill its ring slot with chunk s+3 (a valid
+    // chunk is re-read past the end, so every step issues the same loads)
+    auto cstep = [&](int s, AFrag& af_prev) {
+      mma(s - 1, af_prev);
+      af_prev = load_a(min(s + kRing - 1, S - 1));
+      lds_barrier();
+    };
+    a3 = load_a(min(kRing - 1, S - 1));   // step 0: nothing to multiply yet
+    lds_barrier();
+    int s = 1;
+    for (; s + 3 < S; s += kRing) {
+      cstep(s, a0);
+      cstep(s + 1, a1);
+      cstep(s + 2, a2);
+      cstep(s + 3, a3);
+    }
+    if (s < S) cstep(s, a0);
+    if (s + 1 < S) cstep(s + 1, a1);
+    if (s + 2 < S) cstep(s + 2, a2);
+    switch ((S - 1) % kRing) {   // the last chunk, produced before the last barrier
+      case 0: mma(S - 1, a0); break;
+      case 1: mma(S - 1, a1); break;
+      case 2: mma(S - 1, a2); break;
+      default: mma(S - 1, a3); break;
+    }
+
+    // ---- epilogue: bias, bf16 rounding, NCHW store
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int p = fn * 16 + lrow;
+      const int py = p / ba.TW, px = p - (p / ba.TW) * ba.TW;
+      const int oy = oy0 + py, ox = ox0 + px;
+      if (p >= ntile || oy >= a.Ho || ox >= a.Wo) continue;
+      const int rem = oy * a.Wo + ox;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int o = m0 + wv * WM + fm * 16 + lgrp * 4 + i;
+          if (o >= a.Cout) continue;
+          float v = acc[fm][fn][i];
+          if (a.bias) v += ld_bf16(a.bias, o);
+          reinterpret_cast<uint16_t*>(a.out)[(b * a.Cout + o) * a.HoWo + rem] =
+              static_cast<uint16_t>(pk_bf16(v, 0.f) & 0xffffu);
+        }
+      }
+    }
+  } else {
+    // ================= producers: box copies and column tiles =================
+    const int pw = wv - 4;                  // producer wave 0..3
+    const int ptid = tid - 256;             // producer thread 0..255
+    // Box copy, one wave instruction per 16 pixels: lane -> pixel blk*16 + lane/4,
+    // 16-byte quarter lane%4.  Pixels advance by 64 between a wave's blocks; the
+    // row/column step is precomputed so no division is needed per block.
+    const int nblk = (npx + 15) >> 4;
+    const int step_r = 64 / BW, step_c = 64 - (64 / BW) * BW;
+    const int px_first = pw * 16 + (lane >> 2);
+    const int ry_first = px_first / BW, rx_first = px_first - (px_first / BW) * BW;
+    auto copy_box = [&](int cc, unsigned char* dst) {
+      int px = px_first, ry = ry_first, rx = rx_first;
+      for (int blk = pw; blk < nblk; blk += 4) {
+        const int gy = by0 + ry, gx = bx0 + rx;
+        if (px < npx && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W) {
+          const size_t e = (static_cast<size_t>(b * a.H + gy) * a.W + gx) * Cp + cc * kCK + (lane & 3) * 8;
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xs + e * 2),
+                                           (lds_void*)(dst + blk * 1024), 16, 0, 0);
+        }
+        px += 64;
+        ry += step_r;
+        rx += step_c;
+        if (rx >= BW) { rx -= BW; ++ry; }
+      }
+    };
+
+    // interpolate step s = (cc, k) from `src` into column buffer s & 1
+    auto gather = [&](int s, int k, int cc, const unsigned char* src) {
+      unsigned char* cdst = col + (s & 1) * NT * kCOLB;
+#pragma unroll
+      for (int g = 0; g < GU; ++g) {
+        // GUNITS is a multiple of 64, so whole waves are in or out (a uniform branch)
+        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
+          const int u = ptid + g * 256;
+          const int p = u >> 2, sub = u & 3;
+          const CEnt ce = ctab[k * NT + p];
+          const unsigned char* q = src + (ce.off >= 0 ? ce.off : 0) + sub * 16;
+          const uint4 q00 = *reinterpret_cast<const uint4*>(q);
+          const uint4 q01 = *reinterpret_cast<const uint4*>(q + kPXB);
+          const uint4 q10 = *reinterpret_cast<const uint4*>(q + BW * kPXB);
+          const uint4 q11 = *reinterpret_cast<const uint4*>(q + BW * kPXB + kPXB);
+          uint4 r = interp8(q00, q01, q10, q11, ce.w01, ce.w23);
+          if (ce.off < 0) r = make_uint4(0u, 0u, 0u, 0u);
+          // samples outside the box: read the channels-last copy (a uniform branch, rarely taken)
+          if (__ballot(ce.off == -1) != 0) {
+            const int y0 = (ce.yx >> 16) - 1, x0 = (ce.yx & 0xffff) - 1;
+            const size_t rowb = static_cast<size_t>(b * a.H) * a.W;
+            const int ch = cc * kCK + sub * 8;
+            uint4 c4[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int yy = y0 + (qq >> 1), xx = x0 + (qq & 1);
+              const bool ok = (ce.off == -1) & (yy >= 0) & (yy < a.H) & (xx >= 0) & (xx < a.W);
+              c4[qq] = make_uint4(0u, 0u, 0u, 0u);
+              if (ok)
+                c4[qq] = *reinterpret_cast<const uint4*>(xs + ((rowb + static_cast<size_t>(yy) * a.W + xx) * Cp + ch) * 2);
+            }
+            const uint4 rg = interp8(c4[0], c4[1], c4[2], c4[3], ce.w01, ce.w23);
+            if (ce.off == -1) r = rg;
+          }
+          *reinterpret_cast<uint4*>(cdst + p * kCOLB + sub * 16) = r;
+        }
+      }
+    };
+
+    // one chunk: start copying the next chunk's box into the other buffer, then
+    // interpolate every kernel point; wait for the copy before the last barrier.
+    // The buffer parity is a compile-time constant and the two parities are laid
+    // out one after the other (never behind a runtime pointer select), so every
+    // LDS access names its array and only waits for copies into that array.
+    auto chunk = [&](int cc, auto parity) {
+      constexpr bool odd = decltype(parity)::value;
+      const unsigned char* src = odd ? box1 : box0;
+      unsigned char* dst = odd ? box0 : box1;
+      if (cc + 1 < nCC) copy_box(cc + 1, dst);
+      for (int k = 0; k < KK; ++k) {
+        gather(cc * KK + k, k, cc, src);
+        if (k == KK - 1 && cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+      }
+    };
+    for (int cc = 0; cc < nCC; cc += 2) {
+      chunk(cc, std::false_type());
+      if (cc + 1 < nCC) chunk(cc + 1, std::true_type());
+    }
+    // S barriers here match the consumers' S barriers
+  }
+}
+
+template <int FM, int FN>
+static hipError_t launch_box_t(const BoxArgs& ba, hipStream_t stream) {
+  void* args[] = {const_cast<BoxArgs*>(&ba)};
+  const dim3 grid(ba.f.m_tiles * ba.tiles_per_img * ba.f.B);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN>), grid, dim3(kThreads), args, 0,
+                         stream);
+}
+
+hipError_t launch_box(int fm, int fn, const BoxArgs& ba, hipStream_t stream) {
+#define DCN_BOX_CASE(FMv, FNv) \
+  if (fm == FMv && fn == FNv) return launch_box_t<FMv, FNv>(ba, stream);
+  DCN_BOX_CASE(2, 4) DCN_BOX_CASE(2, 5) DCN_BOX_CASE(2, 6) DCN_BOX_CASE(2, 8) DCN_BOX_CASE(2, 9)
+  DCN_BOX_CASE(4, 4) DCN_BOX_CASE(4, 5)
+#undef DCN_BOX_CASE
+  return hipErrorInvalidValue;
+}
+
+int box_capacity_px(int fn) {
+  switch (fn) {
+    case 4: return BoxCfg<4>::BOX_PX;
+    case 5: return BoxCfg<5>::BOX_PX;
+    case 6: return BoxCfg<6>::BOX_PX;
+    case 8: return BoxCfg<8>::BOX_PX;
+    case 9: return BoxCfg<9>::BOX_PX;
+    default: return 0;
+  }
+}
+
+}  // namespace dcn

@@ -30,6 +30,17 @@ struct StageArgs {
   int B, Cin, HW, Cp, Cout, Mp, KK;
 };
 
+// Box kernel (bf16): FusedArgs plus the output-tile geometry and the LDS budget.
+struct BoxArgs {
+  FusedArgs f;
+  int TH, TW;            // output tile: TH rows x TW columns of one image
+  int tiles_x;           // tiles per output row of tiles
+  int tiles_per_img;
+  int box_px;            // capacity of one LDS box buffer, in pixels
+  int KK_NT;             // corner-table entries: K*K * 16*FN
+  int lds_bytes;         // dynamic LDS per workgroup
+};
+
 enum Variant : int {
   V_TILE_F32_M64_N64 = 0,
   V_TILE_F32_M128_N64,
@@ -37,6 +48,8 @@ enum Variant : int {
   V_TILE_BF16_M128_N64,
   V_TILE_BF16_M128_N32,
   V_TILE_BF16_M256_N64,
+  V_BOX_BF16_M128,
+  V_BOX_BF16_M256,
   V_COUNT
 };
 
@@ -52,5 +65,12 @@ const VariantInfo& variant_info(int v);
 
 hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream);
 hipError_t launch_fused(int variant, const FusedArgs& a, hipStream_t stream);
+
+// box kernel: fm = MT/64 (2: fn 4, 5, 6, 8, 9; 4: fn 4, 5), fn = NT/16.
+// box_capacity_px: pixels one LDS box buffer holds for a given fn (0 if not built).
+hipError_t launch_box(int fm, int fn, const BoxArgs& a, hipStream_t stream);
+int box_capacity_px(int fn);
+constexpr int kLdsBudget = 160 * 1024;   // LDS per workgroup on gfx950
+constexpr int kBoxMaxKK = 9;             // the box kernel handles K*K <= 9
 
 }  // namespace dcn

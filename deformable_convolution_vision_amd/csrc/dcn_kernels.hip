@@ -405,6 +405,8 @@ static const VariantInfo kVariants[V_COUNT] = {
     {"tile_bf16_m128_n64", 1, 128, 64, 32, 1},
     {"tile_bf16_m128_n32", 1, 128, 32, 32, 1},
     {"tile_bf16_m256_n64", 1, 256, 64, 32, 1},
+    {"box_bf16_m128", 1, 128, 0, 32, 1},
+    {"box_bf16_m256", 1, 256, 0, 32, 1},
 };
 
 const VariantInfo& variant_info(int v) { return kVariants[v]; }

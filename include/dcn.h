@@ -118,6 +118,12 @@ int dcn_forward_staged(const dcn_desc* desc, const void* x, const void* offset, 
  * string; "invalid" if the descriptor is rejected). */
 const char* dcn_variant_name(const dcn_desc* desc);
 
+/* Human-readable description of the plan dcn_forward uses for this descriptor
+ * (variant, tile shape, LDS and workspace sizes), written NUL-terminated into
+ * buf (at most len bytes).  Host only.  Status as for dcn_workspace_bytes;
+ * DCN_E_ARG if buf is NULL or len is 0. */
+int dcn_plan_describe(const dcn_desc* desc, char* buf, size_t len);
+
 /* Static text for a status code. */
 const char* dcn_status_str(int status);
 

@@ -58,6 +58,10 @@ EDGE = [
                             mask=None)),
     ("many_pixels", dict(B=1, Cin=32, H=64, W=96, Cout=64, K=3, s=1, p=1, d=1)),
     ("pad0_k2", dict(B=2, Cin=8, H=6, W=9, Cout=3, K=2, s=1, p=0, d=1, offset="normal:1.5")),
+    # offsets far beyond any LDS box: exercises the global-memory path of the box kernel
+    ("huge_offsets", dict(B=1, Cin=64, H=48, W=64, Cout=128, K=3, s=1, p=1, d=1, offset="uniform:30")),
+    ("k5_box", dict(B=1, Cin=48, H=30, W=26, Cout=96, K=5, s=2, p=2, d=1, offset="normal:2")),
+    ("k1_box", dict(B=2, Cin=64, H=17, W=19, Cout=130, K=1, s=1, p=0, d=1)),
 ]
 
 
@@ -75,7 +79,7 @@ def test_edge_shape(name, kw, dtype):
 def _variants(dtype):
     names = []
     for v in ("tile_f32_m64_n64", "tile_f32_m128_n64", "tile_bf16_m64_n64", "tile_bf16_m128_n64",
-              "tile_bf16_m128_n32", "tile_bf16_m256_n64"):
+              "tile_bf16_m128_n32", "tile_bf16_m256_n64", "box_bf16_m128", "box_bf16_m256"):
         if ("bf16" in v) == (dtype == "bf16"):
             names.append(v)
     return names
