@@ -82,6 +82,9 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
   const int64_t M = d->out_channels, Cp = round_up(d->in_channels, 32), Kr = Cp * KK;
   const int64_t s = d->stride, dil = d->dilation;
   const int64_t steps = (Cp / 32) * KK;
+  // 32-bit byte offsets inside the kernel: staged x and repacked weight under 4 GiB
+  if (static_cast<double>(d->batch) * d->height * d->width * Cp * 2 >= 4294967296.0) return false;
+  if (static_cast<double>(round_up(M, 256)) * Kr * 2 >= 4294967296.0) return false;
   BoxPlan best;
   for (int fm = 2; fm <= 4; fm += 2) {
     if (fm_only && fm != fm_only) continue;

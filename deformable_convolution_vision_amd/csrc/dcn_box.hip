@@ -60,13 +60,18 @@ struct CEnt {
   uint32_t w01, w23;
 };
 
+constexpr int kColBufs = 3;      // column-tile ring: produced at step s, read at s+1, multiplied at s+2
+constexpr int kZeroB = 128;      // zero bytes after each box buffer: the source of samples that read nothing
+constexpr int kFbB = 4 * 4 * 1024;  // global-path staging: 4 producer waves x 4 corners x 64 lanes x 16 B
+
 template <int FN>
 struct BoxCfg {
   static constexpr int NT = 16 * FN;
-  static constexpr int COL_BYTES = 2 * NT * kCOLB;
+  static constexpr int COL_BYTES = kColBufs * NT * kCOLB;
   static constexpr int CTAB_BYTES = kBoxMaxKK * NT * 16;
   // what is left of the LDS, split into two box buffers, in 16-pixel blocks
-  static constexpr int BOX_PX = ((kLdsBudget - COL_BYTES - CTAB_BYTES - 64) / (2 * kPXB)) / 16 * 16;
+  static constexpr int BOX_PX =
+      ((kLdsBudget - COL_BYTES - CTAB_BYTES - kFbB - 2 * kZeroB - 64) / (2 * kPXB)) / 16 * 16;
 };
 
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
@@ -76,6 +81,14 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// a.lo*b.lo + a.hi*b.hi in fp32, as the three-operand form with a zero addend (the
+// two-operand accumulate form the compiler picks would need a register set to 0 first)
+__device__ __forceinline__ float dot2_0(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // 8 channels of one sample from the four corner vectors (row 0: q00, q01; row 1:
@@ -93,8 +106,8 @@ __device__ __forceinline__ uint4 interp8(uint4 q00, uint4 q01, uint4 q10, uint4 
     const uint32_t p0hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
     const uint32_t p1lo = __builtin_amdgcn_perm(b1[e], b0[e], 0x05040100u);
     const uint32_t p1hi = __builtin_amdgcn_perm(b1[e], b0[e], 0x07060302u);
-    const float lo = dot2(p1lo, w23, dot2(p0lo, w01, 0.f));
-    const float hi = dot2(p1hi, w23, dot2(p0hi, w01, 0.f));
+    const float lo = dot2(p1lo, w23, dot2_0(p0lo, w01));
+    const float hi = dot2(p1hi, w23, dot2_0(p0hi, w01));
     r[e] = pk_bf16(lo, hi);
   }
   return make_uint4(r[0], r[1], r[2], r[3]);
@@ -111,10 +124,24 @@ __device__ __forceinline__ float ld_bf16(const void* p, int idx) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// Workgroup barrier for LDS traffic only: this wave's LDS operations are complete
-// and visible, outstanding global loads stay in flight.  The "memory" clobber keeps
-// the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Workgroup barriers that order LDS traffic only; outstanding global loads stay in
+// flight across them.
+//  * lds_barrier: release/acquire fences limited to the local address space around
+//    the barrier.  The compiler knows what they order, so its wait counts for the
+//    global loads before and after stay exact.  Used by waves that have no direct
+//    global->LDS loads in flight (the fence would have to wait for those: they write LDS).
+//  * lds_barrier_dma: the same barrier as an opaque instruction sequence, for the
+//    waves whose box copies must stay in flight across it.  The "memory" clobber keeps
+//    the compiler from moving memory accesses across it; its wait counts around it
+//    are conservative.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);   // keep the instruction scheduler from moving work across
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void lds_barrier_dma() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 }  // namespace
 
@@ -131,8 +158,9 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 
   __shared__ __attribute__((aligned(16))) unsigned char col[Cfg::COL_BYTES];
   __shared__ __attribute__((aligned(16))) CEnt ctab[kBoxMaxKK * NT];
-  __shared__ __attribute__((aligned(16))) unsigned char box0[BOXB];
-  __shared__ __attribute__((aligned(16))) unsigned char box1[BOXB];
+  __shared__ __attribute__((aligned(16))) unsigned char box0[BOXB + kZeroB];
+  __shared__ __attribute__((aligned(16))) unsigned char box1[BOXB + kZeroB];
+  __shared__ __attribute__((aligned(16))) unsigned char fbuf[kFbB];
   __shared__ int red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -156,31 +184,66 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   const unsigned char* wp = reinterpret_cast<const unsigned char*>(a.wp);
 
   // ---- consumer state: weight-fragment ring (four named slots, never addressed)
+  // Per-lane byte offsets of this wave's weight rows (the host keeps the repacked
+  // weight under 4 GiB) and a wave-uniform base per step: each fragment load is one
+  // scalar-base + vector-offset instruction, with no per-step address arithmetic.
   struct AFrag { uint4 v[FM]; };
+  uint32_t aoff[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+    aoff[fm] = (static_cast<uint32_t>(m0 + wv * WM + fm * 16 + lrow) * static_cast<uint32_t>(KK * Cp) +
+                static_cast<uint32_t>(lgrp * 8)) * 2u;
   auto load_a = [&](int s) -> AFrag {
     AFrag r;
     const int cc = s / KK, k = s - (s / KK) * KK;
+    const unsigned char* base = wp + static_cast<size_t>(k * Cp + cc * kCK) * 2;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const size_t row = static_cast<size_t>(m0 + wv * WM + fm * 16 + lrow);
-      const size_t e = (row * KK + k) * Cp + cc * kCK + lgrp * 8;
-      r.v[fm] = *reinterpret_cast<const uint4*>(wp + e * 2);
-    }
+    for (int fm = 0; fm < FM; ++fm) r.v[fm] = *reinterpret_cast<const uint4*>(base + aoff[fm]);
     return r;
   };
-  AFrag a0{}, a1{}, a2{}, a3{};
-  if (consumer) {
-    a0 = load_a(0);
-    a1 = load_a(min(1, S - 1));
-    a2 = load_a(min(2, S - 1));
-  }
+  // Weight fragments in two sets of G named slots: chunks G*g .. G*g+G-1 live in set
+  // p for even g and in set q for odd g (G = 4 for the smaller tiles; G = 2 where
+  // 2*G*FM fragments would not fit next to the accumulators and column fragments).
+  constexpr int G = (FM == 2 && FN <= 8) ? 4 : 2;
+  AFrag p0{}, p1{}, p2{}, p3{}, q0{}, q1{}, q2{}, q3{};
+  // weights for chunks c0 .. c0+G-1 (past the end a valid chunk is re-read, so every
+  // group issues the same loads)
+  auto load_group = [&](int c0, AFrag& x0, AFrag& x1, AFrag& x2, AFrag& x3) {
+    x0 = load_a(min(c0, S - 1));
+    x1 = load_a(min(c0 + 1, S - 1));
+    if constexpr (G == 4) {
+      x2 = load_a(min(c0 + 2, S - 1));
+      x3 = load_a(min(c0 + 3, S - 1));
+    }
+  };
+  if (consumer) load_group(0, p0, p1, p2, p3);
 
   // ---- prologue pass 1 (all waves): sampling positions and weights; extent of the upper corners
   if (tid < 4) red[tid] = (tid & 1) ? -0x40000000 : 0x40000000;   // min y, max y, min x, max x
   __syncthreads();
   int lminy = 0x40000000, lmaxy = -0x40000000, lminx = 0x40000000, lmaxx = -0x40000000;
   const int ntile = ba.TH * ba.TW;
-  for (int e = tid; e < KK * NT; e += kThreads) {
+  // all offset and mask loads of this thread first (independent, so they overlap), then the math
+  constexpr int kPE = (kBoxMaxKK * NT + kThreads - 1) / kThreads;
+  float ldy[kPE], ldx[kPE], lm[kPE];
+#pragma unroll
+  for (int j = 0; j < kPE; ++j) {
+    const int e = tid + j * kThreads;
+    const int k = e / NT, p = e - (e / NT) * NT;
+    const int py = p / ba.TW, px = p - (p / ba.TW) * ba.TW;
+    const int oy = oy0 + py, ox = ox0 + px;
+    const bool ok = e < KK * NT && p < ntile && oy < a.Ho && ox < a.Wo;
+    const int rem = ok ? oy * a.Wo + ox : 0;
+    const int kk = ok ? k : 0;
+    const int ob = (b * 2 * KK + 2 * kk) * a.HoWo + rem;
+    ldy[j] = ld_bf16(a.offset, ob);
+    ldx[j] = ld_bf16(a.offset, ob + a.HoWo);
+    lm[j] = a.mask ? ld_bf16(a.mask, (b * KK + kk) * a.HoWo + rem) : 1.f;
+  }
+#pragma unroll
+  for (int jj = 0; jj < kPE; ++jj) {
+    const int e = tid + jj * kThreads;
+    if (e >= KK * NT) continue;
     const int k = e / NT, p = e - (e / NT) * NT;
     CEnt ce;
     ce.off = -2;
@@ -191,11 +254,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const int oy = oy0 + py, ox = ox0 + px;
     if (p < ntile && oy < a.Ho && ox < a.Wo) {
       const int i = k / K, j = k - (k / K) * K;
-      const int rem = oy * a.Wo + ox;
-      const int ob = (b * 2 * KK + 2 * k) * a.HoWo + rem;
-      const float dy = ld_bf16(a.offset, ob);
-      const float dx = ld_bf16(a.offset, ob + a.HoWo);
-      const float m = a.mask ? ld_bf16(a.mask, (b * KK + k) * a.HoWo + rem) : 1.f;
+      const float dy = ldy[jj], dx = ldx[jj], m = lm[jj];
       // integer and fractional parts of the offset are exact in fp32
       const float fy = floorf(dy), fx = floorf(dx);
       const float ly = dy - fy, lx = dx - fx;
@@ -263,17 +322,30 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       if (ry >= 0 && ry + 1 < BH && rx >= 0 && rx + 1 < BW) ctab[e].off = (ry * BW + rx) * kPXB;
     }
   }
-  for (int u = tid; u < npx * 4; u += kThreads) {
-    const int px = u >> 2;
-    const int gy = by0 + px / BW, gx = bx0 + px - (px / BW) * BW;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (gy >= 0 && gy < a.H && gx >= 0 && gx < a.W) {
-      const size_t e = (static_cast<size_t>(b * a.H + gy) * a.W + gx) * Cp + (u & 3) * 8;
-      v = *reinterpret_cast<const uint4*>(xs + e * 2);
-    } else {
-      *reinterpret_cast<uint4*>(box1 + px * kPXB + (u & 3) * 16) = v;
+  if (tid < kZeroB / 16) {
+    *reinterpret_cast<uint4*>(box0 + BOXB + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(box1 + BOXB + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  // chunk 0 of the box: direct global->LDS loads by all eight waves (16 pixels per
+  // wave instruction), zeros for pixels outside the image in both buffers
+  {
+    const int nblk0 = (npx + 15) >> 4;
+    for (int blk = wv; blk < nblk0; blk += 8) {
+      const int px = blk * 16 + (lane >> 2);
+      const int ry = px / BW;
+      const int gy = by0 + ry, gx = bx0 + px - ry * BW;
+      if (px < npx) {
+        if (gy >= 0 && gy < a.H && gx >= 0 && gx < a.W) {
+          const size_t e = (static_cast<size_t>(b * a.H + gy) * a.W + gx) * Cp + (lane & 3) * 8;
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xs + e * 2),
+                                           (lds_void*)(box0 + blk * 1024), 16, 0, 0);
+        } else {
+          *reinterpret_cast<uint4*>(box0 + px * kPXB + (lane & 3) * 16) = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(box1 + px * kPXB + (lane & 3) * 16) = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
     }
-    *reinterpret_cast<uint4*>(box0 + px * kPXB + (u & 3) * 16) = v;
+    __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
 
@@ -285,47 +357,94 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto mma = [&](int s, const AFrag& af) {
-      const unsigned char* csrc = col + (s & 1) * NT * kCOLB;
-      bf16x8 bfr[FN];
+    // B fragments of one column tile (read one step before they are multiplied)
+    struct BFrag { bf16x8 v[FN]; };
+    auto read_b = [&](int c) -> BFrag {
+      BFrag r;
+      const unsigned char* csrc = col + (c % kColBufs) * NT * kCOLB;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        bfr[fn] = *reinterpret_cast<const bf16x8*>(csrc + (fn * 16 + lrow) * kCOLB + lgrp * 16);
+        r.v[fn] = *reinterpret_cast<const bf16x8*>(csrc + (fn * 16 + lrow) * kCOLB + lgrp * 16);
+      return r;
+    };
+    auto mma = [&](const AFrag& af, const BFrag& bf) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const bf16x8 av = __builtin_bit_cast(bf16x8, af.v[fm]);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bfr[fn], acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bf.v[fn], acc[fm][fn], 0, 0, 0);
       }
     };
-    // step s: multiply chunk s-1, refill its ring slot with chunk s+3 (a valid
-    // chunk is re-read past the end, so every step issues the same loads)
-    auto cstep = [&](int s, AFrag& af_prev) {
-      mma(s - 1, af_prev);
-      af_prev = load_a(min(s + kRing - 1, S - 1));
+    // Chunk c is multiplied during step c+2, between barriers c+1 and c+2: read
+    // chunk c+1's columns (produced in step c+1), multiply chunk c (columns read
+    // during step c+1), then barrier c+2.  Steps 0 and 1 have no multiply and the
+    // last two chunks no barrier after them, so the consumers pass exactly S barriers,
+    // like the producers.  `step` is the steady state (all three parts present);
+    // `step_tail` tests each part.
+    auto step = [&](int c, const AFrag& af, const BFrag& bc, BFrag& bn) {
+      bn = read_b(c + 1);
+      mma(af, bc);
       lds_barrier();
     };
-    a3 = load_a(min(kRing - 1, S - 1));   // step 0: nothing to multiply yet
-    lds_barrier();
-    int s = 1;
-    for (; s + 3 < S; s += kRing) {
-      cstep(s, a0);
-      cstep(s + 1, a1);
-      cstep(s + 2, a2);
-      cstep(s + 3, a3);
+    auto step_tail = [&](int c, const AFrag& af, const BFrag& bc, BFrag& bn) {
+      if (c >= S) return;
+      if (c + 1 < S) bn = read_b(c + 1);
+      mma(af, bc);
+      if (c + 2 < S) lds_barrier();
+    };
+    BFrag b0{}, b1{};
+    lds_barrier();                 // barrier 0: chunk 0 is produced
+    b0 = read_b(0);
+    if (S > 1) lds_barrier();      // barrier 1: chunk 1 is produced
+    // 2G chunks per iteration; each group of G starts by loading the weights of the
+    // next group, which then have G steps to arrive.  The loop runs while every step
+    // of the iteration has all three parts, so its body has no branches.
+    int c = 0;
+    for (; c + 2 * G + 2 <= S; c += 2 * G) {
+      load_group(c + G, q0, q1, q2, q3);
+      step(c, p0, b0, b1);
+      step(c + 1, p1, b1, b0);
+      if constexpr (G == 4) {
+        step(c + 2, p2, b0, b1);
+        step(c + 3, p3, b1, b0);
+      }
+      load_group(c + 2 * G, p0, p1, p2, p3);
+      step(c + G, q0, b0, b1);
+      step(c + G + 1, q1, b1, b0);
+      if constexpr (G == 4) {
+        step(c + 6, q2, b0, b1);
+        step(c + 7, q3, b1, b0);
+      }
     }
-    if (s < S) cstep(s, a0);
-    if (s + 1 < S) cstep(s + 1, a1);
-    if (s + 2 < S) cstep(s + 2, a2);
-    switch ((S - 1) % kRing) {   // the last chunk, produced before the last barrier
-      case 0: mma(S - 1, a0); break;
-      case 1: mma(S - 1, a1); break;
-      case 2: mma(S - 1, a2); break;
-      default: mma(S - 1, a3); break;
+    // at most 2G+1 chunks remain
+    load_group(c + G, q0, q1, q2, q3);
+    step_tail(c, p0, b0, b1);
+    step_tail(c + 1, p1, b1, b0);
+    if constexpr (G == 4) {
+      step_tail(c + 2, p2, b0, b1);
+      step_tail(c + 3, p3, b1, b0);
     }
+    if (c + 2 * G < S) load_group(c + 2 * G, p0, p1, p2, p3);
+    step_tail(c + G, q0, b0, b1);
+    step_tail(c + G + 1, q1, b1, b0);
+    if constexpr (G == 4) {
+      step_tail(c + 6, q2, b0, b1);
+      step_tail(c + 7, q3, b1, b0);
+    }
+    step_tail(c + 2 * G, p0, b0, b1);
 
-    // ---- epilogue: bias, bf16 rounding, NCHW store
+    // ---- epilogue: bias, bf16 rounding, NCHW store.  The bias values are loaded
+    // before the first store so no load waits behind the stores.
+    // (Rows past Cout read the last bias value; they are not stored.)
+    float bv[FM][4] = {};
+    if (a.bias) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bv[fm][i] = ld_bf16(a.bias, min(m0 + wv * WM + fm * 16 + lgrp * 4 + i, a.Cout - 1));
+    }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int p = fn * 16 + lrow;
@@ -339,8 +458,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         for (int i = 0; i < 4; ++i) {
           const int o = m0 + wv * WM + fm * 16 + lgrp * 4 + i;
           if (o >= a.Cout) continue;
-          float v = acc[fm][fn][i];
-          if (a.bias) v += ld_bf16(a.bias, o);
+          const float v = acc[fm][fn][i] + bv[fm][i];
           reinterpret_cast<uint16_t*>(a.out)[(b * a.Cout + o) * a.HoWo + rem] =
               static_cast<uint16_t>(pk_bf16(v, 0.f) & 0xffffu);
         }
@@ -357,13 +475,19 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const int step_r = 64 / BW, step_c = 64 - (64 / BW) * BW;
     const int px_first = pw * 16 + (lane >> 2);
     const int ry_first = px_first / BW, rx_first = px_first - (px_first / BW) * BW;
+    // per-lane byte offsets (32-bit: the host keeps the staged copy under 4 GiB)
+    // relative to a wave-uniform base for the chunk
+    const uint32_t img_off = static_cast<uint32_t>(b * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u +
+                             static_cast<uint32_t>((lane & 3) * 16);
+    const uint32_t row_bytes = static_cast<uint32_t>(a.W * Cp) * 2u, px_bytes = static_cast<uint32_t>(Cp) * 2u;
     auto copy_box = [&](int cc, unsigned char* dst) {
+      const unsigned char* base = xs + static_cast<size_t>(cc * kCK) * 2;
       int px = px_first, ry = ry_first, rx = rx_first;
       for (int blk = pw; blk < nblk; blk += 4) {
         const int gy = by0 + ry, gx = bx0 + rx;
         if (px < npx && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W) {
-          const size_t e = (static_cast<size_t>(b * a.H + gy) * a.W + gx) * Cp + cc * kCK + (lane & 3) * 8;
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xs + e * 2),
+          const uint32_t off = img_off + static_cast<uint32_t>(gy) * row_bytes + static_cast<uint32_t>(gx) * px_bytes;
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off),
                                            (lds_void*)(dst + blk * 1024), 16, 0, 0);
         }
         px += 64;
@@ -373,36 +497,63 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       }
     };
 
-    // interpolate step s = (cc, k) from `src` into column buffer s & 1
-    auto gather = [&](int s, int k, int cc, const unsigned char* src) {
-      unsigned char* cdst = col + (s & 1) * NT * kCOLB;
+    // Step s = (cc, k) in two halves: fetch (corner-table entries and the four corner
+    // vectors from the box, issued a step ahead) and finish (interpolate, global path,
+    // store into column buffer s % 3).  A sample with nothing in the box reads the
+    // zero bytes after the buffer with a row stride of 0.
+    struct Fetch { CEnt ce[GU]; uint4 q[GU][4]; };
+    auto fetch = [&](int k, const unsigned char* src) -> Fetch {
+      Fetch f;
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
-        // GUNITS is a multiple of 64, so whole waves are in or out (a uniform branch)
         if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
           const int u = ptid + g * 256;
           const int p = u >> 2, sub = u & 3;
-          const CEnt ce = ctab[k * NT + p];
-          const unsigned char* q = src + (ce.off >= 0 ? ce.off : 0) + sub * 16;
-          const uint4 q00 = *reinterpret_cast<const uint4*>(q);
-          const uint4 q01 = *reinterpret_cast<const uint4*>(q + kPXB);
-          const uint4 q10 = *reinterpret_cast<const uint4*>(q + BW * kPXB);
-          const uint4 q11 = *reinterpret_cast<const uint4*>(q + BW * kPXB + kPXB);
-          uint4 r = interp8(q00, q01, q10, q11, ce.w01, ce.w23);
-          if (ce.off < 0) r = make_uint4(0u, 0u, 0u, 0u);
-          // samples outside the box: read the channels-last copy (a uniform branch, rarely taken)
+          f.ce[g] = ctab[k * NT + p];
+          const bool in_box = f.ce[g].off >= 0;
+          const unsigned char* q = src + (in_box ? f.ce[g].off : BOXB) + sub * 16;
+          const int rs = in_box ? BW * kPXB : 0;
+          f.q[g][0] = *reinterpret_cast<const uint4*>(q);
+          f.q[g][1] = *reinterpret_cast<const uint4*>(q + kPXB);
+          f.q[g][2] = *reinterpret_cast<const uint4*>(q + rs);
+          f.q[g][3] = *reinterpret_cast<const uint4*>(q + rs + kPXB);
+        }
+      }
+      return f;
+    };
+    unsigned char* fb = fbuf + pw * 4096;
+    auto finish = [&](int s, int cc, const Fetch& f) {
+      unsigned char* cdst = col + (s % kColBufs) * NT * kCOLB;
+#pragma unroll
+      for (int g = 0; g < GU; ++g) {
+        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
+          const int u = ptid + g * 256;
+          const int p = u >> 2, sub = u & 3;
+          const CEnt& ce = f.ce[g];
+          uint4 r = interp8(f.q[g][0], f.q[g][1], f.q[g][2], f.q[g][3], ce.w01, ce.w23);
+          // Samples outside the box (a uniform branch, rarely taken): the corners are
+          // copied from the channels-last input into this wave's staging slots with
+          // direct global->LDS loads (every lane loads; lanes without such a sample
+          // read a valid dummy vector), then read back like box data.
           if (__ballot(ce.off == -1) != 0) {
             const int y0 = (ce.yx >> 16) - 1, x0 = (ce.yx & 0xffff) - 1;
             const size_t rowb = static_cast<size_t>(b * a.H) * a.W;
             const int ch = cc * kCK + sub * 8;
-            uint4 c4[4];
+            bool ok[4];
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
               const int yy = y0 + (qq >> 1), xx = x0 + (qq & 1);
-              const bool ok = (ce.off == -1) & (yy >= 0) & (yy < a.H) & (xx >= 0) & (xx < a.W);
-              c4[qq] = make_uint4(0u, 0u, 0u, 0u);
-              if (ok)
-                c4[qq] = *reinterpret_cast<const uint4*>(xs + ((rowb + static_cast<size_t>(yy) * a.W + xx) * Cp + ch) * 2);
+              ok[qq] = (ce.off == -1) & (yy >= 0) & (yy < a.H) & (xx >= 0) & (xx < a.W);
+              const size_t e = ok[qq] ? ((rowb + static_cast<size_t>(yy) * a.W + xx) * Cp + ch) * 2 : 0;
+              __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xs + e), (lds_void*)(fb + qq * 1024),
+                                               16, 0, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            uint4 c4[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              c4[qq] = *reinterpret_cast<const uint4*>(fb + qq * 1024 + lane * 16);
+              if (!ok[qq]) c4[qq] = make_uint4(0u, 0u, 0u, 0u);
             }
             const uint4 rg = interp8(c4[0], c4[1], c4[2], c4[3], ce.w01, ce.w23);
             if (ce.off == -1) r = rg;
@@ -412,20 +563,25 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       }
     };
 
-    // one chunk: start copying the next chunk's box into the other buffer, then
-    // interpolate every kernel point; wait for the copy before the last barrier.
-    // The buffer parity is a compile-time constant and the two parities are laid
-    // out one after the other (never behind a runtime pointer select), so every
-    // LDS access names its array and only waits for copies into that array.
+    // One chunk: start copying the next chunk's box into the other buffer; for each
+    // kernel point fetch the next step's inputs before finishing the current one;
+    // wait for the copy before the chunk's last barrier.  The buffer parity is a
+    // compile-time constant and the two parities are laid out one after the other
+    // (never behind a runtime pointer select), so every LDS access names its array
+    // and only waits for copies into that array.
     auto chunk = [&](int cc, auto parity) {
       constexpr bool odd = decltype(parity)::value;
       const unsigned char* src = odd ? box1 : box0;
       unsigned char* dst = odd ? box0 : box1;
       if (cc + 1 < nCC) copy_box(cc + 1, dst);
+      Fetch cur = fetch(0, src);
       for (int k = 0; k < KK; ++k) {
-        gather(cc * KK + k, k, cc, src);
+        Fetch nxt;
+        if (k + 1 < KK) nxt = fetch(k + 1, src);
+        finish(cc * KK + k, cc, cur);
         if (k == KK - 1 && cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
-        lds_barrier();
+        lds_barrier_dma();
+        cur = nxt;
       }
     };
     for (int cc = 0; cc < nCC; cc += 2) {

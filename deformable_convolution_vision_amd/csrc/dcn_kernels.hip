@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dcn_internal.h"
 
 namespace dcn {
@@ -87,47 +89,88 @@ __device__ __forceinline__ int xcd_tile(int g, int T) {
 // staging
 // ---------------------------------------------------------------------------
 
-// x[b][c][s] -> xs[b][s][c] for s in [0, H*W), c in [0, Cp); channels >= Cin get 0.
-// One workgroup moves a 64-channel x 64-pixel tile through LDS so both the read
-// (along s) and the write (along c) are contiguous.
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void stage_x_kernel(StageArgs a) {
+// One launch stages both operands of the fused kernel.
+//   Workgroups [0, nx):  x[b][c][s] -> xs[b][s][c] for s in [0, H*W), c in [0, Cp),
+//                        channels >= Cin written as 0.  Each moves a 64-channel x
+//                        64-pixel tile through LDS: global reads are VEC pixels of
+//                        one channel (VEC = 16 bytes' worth when H*W allows the
+//                        alignment, fewer otherwise), global writes are 16-byte
+//                        channel vectors of one pixel.
+//   Workgroups [nx, ..): w[o][c][k] -> wp[o][k][c] for o < Mp, k < KK, c < Cp,
+//                        zero outside Cout x Cin.
+template <bool BF16, int VEC>
+__global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a, int nx, int s_tiles, int c_tiles) {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
-  __shared__ T tile[64][65];
-  const int s_tiles = (a.HW + 63) / 64;
-  const int b = blockIdx.x / s_tiles;
-  const int s0 = (blockIdx.x - b * s_tiles) * 64, c0 = blockIdx.y * 64;
+  constexpr int ES = sizeof(T);
+  constexpr int OUTV = 16 / ES;                  // elements per 16-byte channel vector
+  __shared__ T tile[64][64 + 2];                 // [channel][pixel]
+  const int tid = threadIdx.x;
+  if (static_cast<int>(blockIdx.x) >= nx) {
+    const T* w = reinterpret_cast<const T*>(a.w);
+    T* wp = reinterpret_cast<T*>(a.wp);
+    const int total = a.Mp * a.KK * a.Cp;
+    const int nw = gridDim.x - nx;
+    for (int e = (blockIdx.x - nx) * kThreads + tid; e < total; e += nw * kThreads) {
+      const int c = e % a.Cp;
+      const int k = (e / a.Cp) % a.KK;
+      const int o = e / (a.Cp * a.KK);
+      T v = T(0);
+      if (o < a.Cout && c < a.Cin) v = w[(o * a.Cin + c) * a.KK + k];
+      wp[e] = v;
+    }
+    return;
+  }
+  const int per_img = s_tiles * c_tiles;
+  const int b = blockIdx.x / per_img;
+  const int r = blockIdx.x - b * per_img;
+  const int ct = r / s_tiles, st = r - (r / s_tiles) * s_tiles;
+  const int s0 = st * 64, c0 = ct * 64;
   const T* x = reinterpret_cast<const T*>(a.x) + static_cast<size_t>(b) * a.Cin * a.HW;
   T* xs = reinterpret_cast<T*>(a.xs) + static_cast<size_t>(b) * a.HW * a.Cp;
-  for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
-    const int cl = e >> 6, sl = e & 63;
-    const int c = c0 + cl, s = s0 + sl;
-    T v = T(0);
-    if (c < a.Cin && s < a.HW) v = x[static_cast<size_t>(c) * a.HW + s];
-    tile[cl][sl] = v;
+  // read: 64 channels x (64 / VEC) vectors of VEC pixels
+  for (int e = tid; e < 64 * (64 / VEC); e += kThreads) {
+    const int cl = e / (64 / VEC), sv = e - (e / (64 / VEC)) * (64 / VEC);
+    const int c = c0 + cl, sp = s0 + sv * VEC;
+    T v[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = T(0);
+    if (c < a.Cin) {
+      const T* src = x + static_cast<size_t>(c) * a.HW + sp;
+      if (sp + VEC <= a.HW) {
+        if constexpr (VEC * ES == 16) {
+          const uint4 q = *reinterpret_cast<const uint4*>(src);
+          __builtin_memcpy(v, &q, 16);
+        } else if constexpr (VEC * ES == 8) {
+          const uint2 q = *reinterpret_cast<const uint2*>(src);
+          __builtin_memcpy(v, &q, 8);
+        } else if constexpr (VEC * ES == 4) {
+          const uint32_t q = *reinterpret_cast<const uint32_t*>(src);
+          __builtin_memcpy(v, &q, 4);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) v[i] = src[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+          if (sp + i < a.HW) v[i] = src[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) tile[cl][sv * VEC + i] = v[i];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
-    const int sl = e >> 6, cl = e & 63;
-    const int c = c0 + cl, s = s0 + sl;
-    if (c < a.Cp && s < a.HW) xs[static_cast<size_t>(s) * a.Cp + c] = tile[cl][sl];
-  }
-}
-
-// w[o][c][k] -> wp[o][k][c] for o < Mp, k < KK, c < Cp; zero outside Cout x Cin.
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void pack_w_kernel(StageArgs a) {
-  using T = typename std::conditional<BF16, uint16_t, float>::type;
-  const T* w = reinterpret_cast<const T*>(a.w);
-  T* wp = reinterpret_cast<T*>(a.wp);
-  const int total = a.Mp * a.KK * a.Cp;
-  for (int e = blockIdx.x * kThreads + threadIdx.x; e < total; e += gridDim.x * kThreads) {
-    const int c = e % a.Cp;
-    const int k = (e / a.Cp) % a.KK;
-    const int o = e / (a.Cp * a.KK);
-    T v = T(0);
-    if (o < a.Cout && c < a.Cin) v = w[(o * a.Cin + c) * a.KK + k];
-    wp[e] = v;
+  // write: 64 pixels x (64 / OUTV) vectors of OUTV channels
+  for (int e = tid; e < 64 * (64 / OUTV); e += kThreads) {
+    const int sl = e / (64 / OUTV), cv = e - (e / (64 / OUTV)) * (64 / OUTV);
+    const int sp = s0 + sl, c = c0 + cv * OUTV;
+    if (sp >= a.HW || c >= a.Cp) continue;
+    T v[OUTV];
+#pragma unroll
+    for (int i = 0; i < OUTV; ++i) v[i] = tile[cv * OUTV + i][sl];
+    uint4 q;
+    __builtin_memcpy(&q, v, 16);
+    *reinterpret_cast<uint4*>(xs + static_cast<size_t>(sp) * a.Cp + c) = q;
   }
 }
 
@@ -414,21 +457,28 @@ const VariantInfo& variant_info(int v) { return kVariants[v]; }
 hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream) {
   const VariantInfo& vi = kVariants[variant];
   if (!vi.staged) return hipSuccess;
-  const dim3 gx(((a.HW + 63) / 64) * a.B, (a.Cp + 63) / 64);
+  const int s_tiles = (a.HW + 63) / 64, c_tiles = (a.Cp + 63) / 64;
+  const int nx = s_tiles * c_tiles * a.B;
   const int wtotal = a.Mp * a.KK * a.Cp;
-  const dim3 gw(min((wtotal + kThreads - 1) / kThreads, 4096));
-  void* args[] = {const_cast<StageArgs*>(&a)};
-  hipError_t e;
-  if (vi.is_bf16) {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&stage_x_kernel<true>), gx, dim3(kThreads), args, 0, stream);
-    if (e != hipSuccess) return e;
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&pack_w_kernel<true>), gw, dim3(kThreads), args, 0, stream);
-  } else {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&stage_x_kernel<false>), gx, dim3(kThreads), args, 0, stream);
-    if (e != hipSuccess) return e;
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&pack_w_kernel<false>), gw, dim3(kThreads), args, 0, stream);
-  }
-  return e;
+  const int nw = min((wtotal + kThreads - 1) / kThreads, 1024);
+  const dim3 grid(nx + nw);
+  StageArgs sa = a;
+  void* args[] = {&sa, const_cast<int*>(&nx), const_cast<int*>(&s_tiles), const_cast<int*>(&c_tiles)};
+  const void* fn;
+  // widest global read that every channel plane (starting at x + c*H*W elements)
+  // keeps aligned, given the caller's x pointer
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(a.x);
+  auto fits = [&](int vec, int es) { return a.HW % vec == 0 && xa % static_cast<uintptr_t>(vec * es) == 0; };
+  if (vi.is_bf16)
+    fn = fits(8, 2)   ? reinterpret_cast<const void*>(&stage_kernel<true, 8>)
+       : fits(4, 2)   ? reinterpret_cast<const void*>(&stage_kernel<true, 4>)
+       : fits(2, 2)   ? reinterpret_cast<const void*>(&stage_kernel<true, 2>)
+                      : reinterpret_cast<const void*>(&stage_kernel<true, 1>);
+  else
+    fn = fits(4, 4)   ? reinterpret_cast<const void*>(&stage_kernel<false, 4>)
+       : fits(2, 4)   ? reinterpret_cast<const void*>(&stage_kernel<false, 2>)
+                      : reinterpret_cast<const void*>(&stage_kernel<false, 1>);
+  return hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, stream);
 }
 
 template <bool BF16, int MT, int NT>
