@@ -2,17 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--all] [--no-cpu]
 
-One step = one full dcn_forward (staging launch + fused launch) over the
-workload's synthetic inputs, which are resident in HBM before timing starts.
+One step = one full forward (the staging launch, then the fused launch, exactly
+what dcn_forward issues) over the workload's synthetic inputs, which are resident
+in HBM before timing starts.
 The default workload is the ResNet-50 c4 downsampling layer (bf16, B=2,
 Cin=Cout=256, 100x168 input, 3x3, stride 2, pad 1 -> 50x84).  Prints one JSON
 line; with --all, one line per named workload (the first line is still the
 headline workload).
 
 value       = effective TFLOP/s of the whole step, 2*B*Cout*Ho*Wo*Cin*K^2 / step time
-roofline    = the fused kernel alone: algorithmic flops per launch / its mean duration
-              (HIP events on the stream it is launched on), against the dense MFMA
-              peak of the element type (HBM peak for the fp32 single-image workload)
+roofline    = the fused kernel alone: algorithmic flops per launch / its mean duration,
+              from HIP events recorded around each launch inside the timed region on
+              the stream the kernels run on, against the dense MFMA peak of the element
+              type (HBM peak for the fp32 single-image workload); traffic = HBM bytes
+              per launch from the committed counter runs, if the kernels are unchanged
 cpu_baseline = the CPU oracle on a bounded slice of the same workload (a range of
               output channels), scaled to TFLOP/s, with the threads it used
 """
@@ -30,13 +33,76 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK = {"bf16_mfma": 2516.6, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, TFLOP/s, GB/s
-KERNEL_SRC = os.path.join(ROOT, "deformable_convolution_vision_amd", "csrc", "dcn_kernels.hip")
+CSRC = os.path.join(ROOT, "deformable_convolution_vision_amd", "csrc")
+KERNEL_SRCS = ("dcn_internal.h", "dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel sources (the counter figures are valid only for these)."""
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_symbol(variant: str, plan: str) -> str:
+    """Device symbol of the fused launch, as rocprofv3 names it."""
+    import re
+    if variant.startswith("box"):
+        m = re.search(r"\((\d+) slots\) x (\d+) ch", plan)
+        return f"dcn_box_kernel<{int(m.group(2)) // 64}, {int(m.group(1)) // 16}>"
+    return f"dcn_fused_kernel ({variant})"
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class HipEvents:
+    """HIP events from the runtime torch has loaded, created without the system-scope
+    release fence (a timing marker then adds no cache write-back between launches)."""
+
+    def __init__(self, n: int):
+        import ctypes
+        path = "libamdhip64.so"
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        self.ct = ctypes
+        self.hip = hip = ctypes.CDLL(path)
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def record(self, i: int, stream: int):
+        if self.hip.hipEventRecord(self.ev[i], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def sync(self, i: int):
+        if self.hip.hipEventSynchronize(self.ev[i]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+
+    def ms(self, i: int, j: int) -> float:
+        f = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(f), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
 def traffic_for(workload: str):
@@ -69,6 +135,7 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.B, w.Cout, Ho, Wo), dtype=g["x"].dtype, device="cuda")
     variant = dcn.dcn_variant_name(desc)
+    plan = dcn.dcn_plan_describe(desc)
     stream = torch.cuda.current_stream()
     wsp = ws if nb else None
 
@@ -96,32 +163,28 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
         step()
     torch.cuda.synchronize()
 
-    # whole-step throughput: K back-to-back steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region: K steps back to back.  Each step issues the staging launch and
+    # the fused launch (the two launches dcn_forward makes); events recorded between
+    # them on the same stream give each kernel's duration inside the region.
+    ev = HipEvents(2 * steps + 1)
+    sp = stream.cuda_stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = e0.elapsed_time(e1)
-    ms_per_step = total_ms / steps
-
-    # per-kernel durations: events around the staging and the fused launch of each step
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
+    ev.record(0, sp)
     for i in range(steps):
-        ev[i][0].record(stream)
         dcn.dcn_stage(desc, g["x"], g["weight"], wsp, nb, stream)
-        ev[i][1].record(stream)
+        ev.record(2 * i + 1, sp)
         dcn.dcn_forward_staged(desc, g["x"], g["offset"], g["mask"], g["weight"], g["bias"], out, wsp, nb,
                                stream)
-        ev[i][2].record(stream)
+        ev.record(2 * i + 2, sp)
+    ev.sync(2 * steps)
     torch.cuda.synchronize()
-    stage_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(steps))
-    fused_ms = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(steps))
+    wall = time.perf_counter() - t0
+    total_ms = ev.ms(0, 2 * steps)
+    ms_per_step = total_ms / steps
+    stage_ms = sorted(ev.ms(2 * i, 2 * i + 1) for i in range(steps))
+    fused_ms = sorted(ev.ms(2 * i + 1, 2 * i + 2) for i in range(steps))
+    ev.close()
     fused_mean = sum(fused_ms) / steps
     stage_mean = sum(stage_ms) / steps
 
@@ -154,13 +217,13 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
         "config": {"workload": f"{w.name}: B={w.B} Cin={w.Cin} {w.H}x{w.W} -> Cout={w.Cout} {Ho}x{Wo}, "
                                f"K={w.K} stride={w.stride} pad={w.pad} dilation={w.dilation}, "
                                f"mask={'yes' if w.mask else 'no'}, bias={'yes' if w.bias else 'no'}",
-                   "variant": variant},
+                   "variant": variant, "plan": plan},
         "effective_gbps": round(gbps, 2),
         "frac_mfma_peak": round(tflops / (PEAK["bf16_mfma"] if w.dtype == "bf16" else PEAK["f32_mfma"]), 5),
         "frac_hbm_peak": round(gbps / PEAK["hbm"], 5),
         "roofline": {"bound": bound, "achieved": round(achieved, 4), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 5), "traffic": traffic,
-                     "kernel": f"dcn_fused_kernel ({variant})",
+                     "kernel": kernel_symbol(variant, plan), "kernel_sha": kernel_hash(),
                      "per_launch": {"flops": flops, "algorithmic_bytes": abytes}},
         "kernels_us": {"stage_mean": round(stage_mean * 1e3, 3), "fused_mean": round(fused_mean * 1e3, 3),
                        "fused_median": round(fused_ms[steps // 2] * 1e3, 3),
