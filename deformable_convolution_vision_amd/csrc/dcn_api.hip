@@ -12,6 +12,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <limits>
+#include <mutex>
 
 #include "dcn.h"
 #include "dcn_internal.h"
@@ -85,6 +86,11 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
   // 32-bit byte offsets inside the kernel: staged x and repacked weight under 4 GiB
   if (static_cast<double>(d->batch) * d->height * d->width * Cp * 2 >= 4294967296.0) return false;
   if (static_cast<double>(round_up(M, 256)) * Kr * 2 >= 4294967296.0) return false;
+  // DCN_BOX_TILE="fn,TH,TW" restricts the search to one tile shape (tile sweeps)
+  int want_fn = 0, want_th = 0, want_tw = 0;
+  if (const char* t = std::getenv("DCN_BOX_TILE")) {
+    if (std::sscanf(t, "%d,%d,%d", &want_fn, &want_th, &want_tw) != 3) want_fn = want_th = want_tw = 0;
+  }
   BoxPlan best;
   for (int fm = 2; fm <= 4; fm += 2) {
     if (fm_only && fm != fm_only) continue;
@@ -95,9 +101,10 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
       const int box_px = dcn::box_capacity_px(fn);
       if (box_px < 64) continue;
       for (int TH = 1; TH <= 16; ++TH) {
-        for (int dw = 0; dw < 2; ++dw) {
+        for (int dw = 0; dw < (want_fn ? NT : 2); ++dw) {
           const int TW = NT / TH - dw;
           if (TW < 1 || (TH * TW + 15) / 16 != fn) continue;
+          if (want_fn && (fn != want_fn || TH != want_th || TW != want_tw)) continue;
           const int64_t bh0 = (TH - 1) * s + (K - 1) * dil + 2, bw0 = (TW - 1) * s + (K - 1) * dil + 2;
           if (bh0 * bw0 > box_px) continue;
           const int64_t ty = (Ho + TH - 1) / TH, tx = (Wo + TW - 1) / TW;
@@ -146,7 +153,7 @@ int choose_variant(const dcn_desc* d, int64_t N, int64_t Ho, int64_t Wo, BoxPlan
   return dcn::V_TILE_BF16_M128_N32;
 }
 
-int make_plan(const dcn_desc* d, Plan* p) {
+int compute_plan(const dcn_desc* d, Plan* p) {
   if (!geometry_ok(d)) return DCN_E_ARG;
   if (d->dtype != DCN_F32 && d->dtype != DCN_BF16) return DCN_E_UNSUPPORTED;
   p->Ho = out_extent(d->height, d->kernel_size, d->stride, d->pad, d->dilation);
@@ -191,12 +198,63 @@ int make_plan(const dcn_desc* d, Plan* p) {
   return DCN_OK;
 }
 
+// Plans are cached per descriptor (and the two tuning variables), so repeated calls
+// with one shape skip the tile search.  Thread-safe; a small round-robin table.
+struct PlanKey {
+  dcn_desc d;
+  char variant[48], tile[48];
+};
+struct PlanSlot {
+  bool used = false;
+  PlanKey key;
+  Plan plan;
+};
+
+void fill_key(const dcn_desc* d, PlanKey* k) {
+  std::memset(k, 0, sizeof(*k));
+  std::memcpy(&k->d, d, sizeof(dcn_desc));
+  if (const char* v = std::getenv("DCN_VARIANT")) std::strncpy(k->variant, v, sizeof(k->variant) - 1);
+  if (const char* t = std::getenv("DCN_BOX_TILE")) std::strncpy(k->tile, t, sizeof(k->tile) - 1);
+}
+
+int make_plan(const dcn_desc* d, Plan* p) {
+  if (d == nullptr) return DCN_E_ARG;
+  static std::mutex mu;
+  static PlanSlot slots[32];
+  static int next = 0;
+  PlanKey key;
+  fill_key(d, &key);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const PlanSlot& sl : slots)
+      if (sl.used && std::memcmp(&sl.key, &key, sizeof(key)) == 0) {
+        *p = sl.plan;
+        return DCN_OK;
+      }
+  }
+  Plan fresh;
+  const int rc = compute_plan(d, &fresh);
+  if (rc != DCN_OK) return rc;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    PlanSlot& sl = slots[next];
+    next = (next + 1) % 32;
+    sl.used = true;
+    sl.key = key;
+    sl.plan = fresh;
+  }
+  *p = fresh;
+  return DCN_OK;
+}
+
 int check_workspace(const Plan& p, const void* ws, size_t ws_bytes) {
   if (p.ws_bytes == 0) return DCN_OK;
   if (ws == nullptr || ws_bytes < p.ws_bytes) return DCN_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return DCN_E_WORKSPACE;
   return DCN_OK;
 }
+
+bool is_box(int variant) { return variant == dcn::V_BOX_BF16_M128 || variant == dcn::V_BOX_BF16_M256; }
 
 StageArgs stage_args(const dcn_desc* d, const Plan& p, const void* x, const void* w, void* ws) {
   StageArgs a{};
@@ -211,6 +269,7 @@ StageArgs stage_args(const dcn_desc* d, const Plan& p, const void* x, const void
   a.Cout = static_cast<int>(d->out_channels);
   a.Mp = static_cast<int>(p.Mp);
   a.KK = static_cast<int>(d->kernel_size * d->kernel_size);
+  a.wlayout = is_box(p.variant) ? 1 : 0;
   return a;
 }
 
@@ -246,8 +305,6 @@ FusedArgs fused_args(const dcn_desc* d, const Plan& p, const void* x, const void
   a.n_tiles = (a.N + nt - 1) / nt;
   return a;
 }
-
-bool is_box(int variant) { return variant == dcn::V_BOX_BF16_M128 || variant == dcn::V_BOX_BF16_M256; }
 
 hipError_t launch_fused_plan(const Plan& p, const FusedArgs& a, hipStream_t stream) {
   if (!is_box(p.variant)) return dcn::launch_fused(p.variant, a, stream);

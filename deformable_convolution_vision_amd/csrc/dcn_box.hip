@@ -113,6 +113,15 @@ __device__ __forceinline__ uint4 interp8(uint4 q00, uint4 q01, uint4 q10, uint4 
   return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, each call inlined with I known at compile time
+template <int I, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>());
+    static_for<I + 1, E>(f);
+  }
+}
+
 __device__ __forceinline__ int xcd_tile(int g, int T) {
   const int xcd = g & 7, idx = g >> 3;
   const int q = T >> 3, r = T & 7;
@@ -145,7 +154,7 @@ __device__ __forceinline__ void lds_barrier_dma() { asm volatile("s_waitcnt lgkm
 
 }  // namespace
 
-template <int FM, int FN>
+template <int FM, int FN, int KKT>
 __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   using Cfg = BoxCfg<FN>;
   const FusedArgs& a = ba.f;
@@ -183,20 +192,20 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   const unsigned char* xs = reinterpret_cast<const unsigned char*>(a.xs);
   const unsigned char* wp = reinterpret_cast<const unsigned char*>(a.wp);
 
-  // ---- consumer state: weight-fragment ring (four named slots, never addressed)
-  // Per-lane byte offsets of this wave's weight rows (the host keeps the repacked
-  // weight under 4 GiB) and a wave-uniform base per step: each fragment load is one
-  // scalar-base + vector-offset instruction, with no per-step address arithmetic.
+  // ---- consumer state: weight fragments
+  // The repacked weight is step-major, [step][Mp][32 channels], so the 16 rows x 64
+  // bytes one fragment load reads are one contiguous kilobyte.  Per-lane byte offsets
+  // of this wave's rows (the host keeps the repacked weight under 4 GiB) plus a
+  // wave-uniform base per step: one scalar-base + vector-offset load per fragment.
   struct AFrag { uint4 v[FM]; };
+  const uint32_t step_bytes = static_cast<uint32_t>(a.m_tiles * MT) * 64u;
   uint32_t aoff[FM];
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
-    aoff[fm] = (static_cast<uint32_t>(m0 + wv * WM + fm * 16 + lrow) * static_cast<uint32_t>(KK * Cp) +
-                static_cast<uint32_t>(lgrp * 8)) * 2u;
-  auto load_a = [&](int s) -> AFrag {
+    aoff[fm] = static_cast<uint32_t>(m0 + wv * WM + fm * 16 + lrow) * 64u + static_cast<uint32_t>(lgrp * 16);
+  auto load_a = [&](int s) __attribute__((always_inline)) -> AFrag {
     AFrag r;
-    const int cc = s / KK, k = s - (s / KK) * KK;
-    const unsigned char* base = wp + static_cast<size_t>(k * Cp + cc * kCK) * 2;
+    const unsigned char* base = wp + static_cast<size_t>(static_cast<uint32_t>(s) * step_bytes);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) r.v[fm] = *reinterpret_cast<const uint4*>(base + aoff[fm]);
     return r;
@@ -204,11 +213,11 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   // Weight fragments in two sets of G named slots: chunks G*g .. G*g+G-1 live in set
   // p for even g and in set q for odd g (G = 4 for the smaller tiles; G = 2 where
   // 2*G*FM fragments would not fit next to the accumulators and column fragments).
-  constexpr int G = (FM == 2 && FN <= 8) ? 4 : 2;
+  constexpr int G = (FM * FN <= 16) ? 4 : 2;
   AFrag p0{}, p1{}, p2{}, p3{}, q0{}, q1{}, q2{}, q3{};
   // weights for chunks c0 .. c0+G-1 (past the end a valid chunk is re-read, so every
   // group issues the same loads)
-  auto load_group = [&](int c0, AFrag& x0, AFrag& x1, AFrag& x2, AFrag& x3) {
+  auto load_group = [&](int c0, AFrag& x0, AFrag& x1, AFrag& x2, AFrag& x3) __attribute__((always_inline)) {
     x0 = load_a(min(c0, S - 1));
     x1 = load_a(min(c0 + 1, S - 1));
     if constexpr (G == 4) {
@@ -276,7 +285,16 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     }
     ctab[e] = ce;
   }
-  if (lminy <= lmaxy) {
+  // reduce within the wave first (lanes without samples hold the neutral values),
+  // then one LDS atomic per wave and value: 512 atomics on four words would serialise
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    lminy = min(lminy, __shfl_xor(lminy, sh));
+    lmaxy = max(lmaxy, __shfl_xor(lmaxy, sh));
+    lminx = min(lminx, __shfl_xor(lminx, sh));
+    lmaxx = max(lmaxx, __shfl_xor(lmaxx, sh));
+  }
+  if (lane == 0 && lminy <= lmaxy) {
     atomicMin(&red[0], lminy);
     atomicMax(&red[1], lmaxy);
     atomicMin(&red[2], lminx);
@@ -359,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 
     // B fragments of one column tile (read one step before they are multiplied)
     struct BFrag { bf16x8 v[FN]; };
-    auto read_b = [&](int c) -> BFrag {
+    auto read_b = [&](int c) __attribute__((always_inline)) -> BFrag {
       BFrag r;
       const unsigned char* csrc = col + (c % kColBufs) * NT * kCOLB;
 #pragma unroll
@@ -367,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         r.v[fn] = *reinterpret_cast<const bf16x8*>(csrc + (fn * 16 + lrow) * kCOLB + lgrp * 16);
       return r;
     };
-    auto mma = [&](const AFrag& af, const BFrag& bf) {
+    auto mma = [&](const AFrag& af, const BFrag& bf) __attribute__((always_inline)) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const bf16x8 av = __builtin_bit_cast(bf16x8, af.v[fm]);
@@ -382,12 +400,12 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // last two chunks no barrier after them, so the consumers pass exactly S barriers,
     // like the producers.  `step` is the steady state (all three parts present);
     // `step_tail` tests each part.
-    auto step = [&](int c, const AFrag& af, const BFrag& bc, BFrag& bn) {
+    auto step = [&](int c, const AFrag& af, const BFrag& bc, BFrag& bn) __attribute__((always_inline)) {
       bn = read_b(c + 1);
       mma(af, bc);
       lds_barrier();
     };
-    auto step_tail = [&](int c, const AFrag& af, const BFrag& bc, BFrag& bn) {
+    auto step_tail = [&](int c, const AFrag& af, const BFrag& bc, BFrag& bn) __attribute__((always_inline)) {
       if (c >= S) return;
       if (c + 1 < S) bn = read_b(c + 1);
       mma(af, bc);
@@ -434,9 +452,11 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     }
     step_tail(c + 2 * G, p0, b0, b1);
 
-    // ---- epilogue: bias, bf16 rounding, NCHW store.  The bias values are loaded
-    // before the first store so no load waits behind the stores.
-    // (Rows past Cout read the last bias value; they are not stored.)
+    // ---- epilogue, part 1: bias and bf16 rounding into an LDS copy of the output
+    // tile, [row][pixel] with a row stride of NT+2 elements, in the first box
+    // buffer.  The producers read no box after barrier S-1, and the consumers pass
+    // that barrier only after every producer's reads are complete.  The bias values
+    // are loaded first; rows past Cout read the last bias value and are not stored.
     float bv[FM][4] = {};
     if (a.bias) {
 #pragma unroll
@@ -445,25 +465,15 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         for (int i = 0; i < 4; ++i)
           bv[fm][i] = ld_bf16(a.bias, min(m0 + wv * WM + fm * 16 + lgrp * 4 + i, a.Cout - 1));
     }
+    uint16_t* stage = reinterpret_cast<uint16_t*>(box0);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int p = fn * 16 + lrow;
-      const int py = p / ba.TW, px = p - (p / ba.TW) * ba.TW;
-      const int oy = oy0 + py, ox = ox0 + px;
-      if (p >= ntile || oy >= a.Ho || ox >= a.Wo) continue;
-      const int rem = oy * a.Wo + ox;
+    for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
+      for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int o = m0 + wv * WM + fm * 16 + lgrp * 4 + i;
-          if (o >= a.Cout) continue;
-          const float v = acc[fm][fn][i] + bv[fm][i];
-          reinterpret_cast<uint16_t*>(a.out)[(b * a.Cout + o) * a.HoWo + rem] =
-              static_cast<uint16_t>(pk_bf16(v, 0.f) & 0xffffu);
-        }
-      }
-    }
+        for (int i = 0; i < 4; ++i)
+          stage[(wv * WM + fm * 16 + lgrp * 4 + i) * (NT + 2) + fn * 16 + lrow] =
+              static_cast<uint16_t>(pk_bf16(acc[fm][fn][i] + bv[fm][i], 0.f) & 0xffffu);
   } else {
     // ================= producers: box copies and column tiles =================
     const int pw = wv - 4;                  // producer wave 0..3
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const uint32_t img_off = static_cast<uint32_t>(b * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u +
                              static_cast<uint32_t>((lane & 3) * 16);
     const uint32_t row_bytes = static_cast<uint32_t>(a.W * Cp) * 2u, px_bytes = static_cast<uint32_t>(Cp) * 2u;
-    auto copy_box = [&](int cc, unsigned char* dst) {
+    auto copy_box = [&](int cc, unsigned char* dst) __attribute__((always_inline)) {
       const unsigned char* base = xs + static_cast<size_t>(cc * kCK) * 2;
       int px = px_first, ry = ry_first, rx = rx_first;
       for (int blk = pw; blk < nblk; blk += 4) {
@@ -497,21 +507,21 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       }
     };
 
-    // Step s = (cc, k) in two halves: fetch (corner-table entries and the four corner
-    // vectors from the box, issued a step ahead) and finish (interpolate, global path,
-    // store into column buffer s % 3).  A sample with nothing in the box reads the
-    // zero bytes after the buffer with a row stride of 0.
-    struct Fetch { CEnt ce[GU]; uint4 q[GU][4]; };
-    auto fetch = [&](int k, const unsigned char* src) -> Fetch {
-      Fetch f;
+    // Producer state of one step: the corner-table entries and the four corner vectors
+    // of this thread's samples.  A sample with nothing in the box reads the zero bytes
+    // after the buffer with a row stride of 0.
+    struct PSet { CEnt ce[GU]; uint4 q[GU][4]; };
+    auto read_ce = [&](int k, PSet& f) __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < GU; ++g)
+        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) f.ce[g] = ctab[k * NT + ((ptid + g * 256) >> 2)];
+    };
+    auto read_q = [&](const unsigned char* src, PSet& f) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
         if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
-          const int u = ptid + g * 256;
-          const int p = u >> 2, sub = u & 3;
-          f.ce[g] = ctab[k * NT + p];
           const bool in_box = f.ce[g].off >= 0;
-          const unsigned char* q = src + (in_box ? f.ce[g].off : BOXB) + sub * 16;
+          const unsigned char* q = src + (in_box ? f.ce[g].off : BOXB) + (ptid & 3) * 16;
           const int rs = in_box ? BW * kPXB : 0;
           f.q[g][0] = *reinterpret_cast<const uint4*>(q);
           f.q[g][1] = *reinterpret_cast<const uint4*>(q + kPXB);
@@ -519,10 +529,10 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
           f.q[g][3] = *reinterpret_cast<const uint4*>(q + rs + kPXB);
         }
       }
-      return f;
     };
+    // interpolate (global path for samples outside the box) and store into column buffer s % 3
     unsigned char* fb = fbuf + pw * 4096;
-    auto finish = [&](int s, int cc, const Fetch& f) {
+    auto finish = [&](int s, int cc, const PSet& f) __attribute__((always_inline)) {
       unsigned char* cdst = col + (s % kColBufs) * NT * kCOLB;
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
@@ -563,32 +573,114 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       }
     };
 
-    // One chunk: start copying the next chunk's box into the other buffer; for each
-    // kernel point fetch the next step's inputs before finishing the current one;
-    // wait for the copy before the chunk's last barrier.  The buffer parity is a
-    // compile-time constant and the two parities are laid out one after the other
-    // (never behind a runtime pointer select), so every LDS access names its array
-    // and only waits for copies into that array.
-    auto chunk = [&](int cc, auto parity) {
-      constexpr bool odd = decltype(parity)::value;
-      const unsigned char* src = odd ? box1 : box0;
-      unsigned char* dst = odd ? box0 : box1;
-      if (cc + 1 < nCC) copy_box(cc + 1, dst);
-      Fetch cur = fetch(0, src);
-      for (int k = 0; k < KK; ++k) {
-        Fetch nxt;
-        if (k + 1 < KK) nxt = fetch(k + 1, src);
-        finish(cc * KK + k, cc, cur);
-        if (k == KK - 1 && cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
-        lds_barrier_dma();
-        cur = nxt;
+    // Chunks alternate between the two box buffers.  The buffer of each chunk is a
+    // compile-time choice (the two parities are laid out one after the other, never
+    // behind a runtime pointer select), so every LDS access names its array and only
+    // waits for copies into that array.  Each chunk starts copying the next chunk's
+    // box into the other buffer and waits for that copy before its last barrier.
+    PSet X, Y;
+    if constexpr (KKT == 9) {
+      // Three kernel points: the nine steps of a chunk are unrolled and software
+      // pipelined over the register sets X and Y, which alternate from step to step
+      // (no copies between steps).  During step s the producer reads the corner
+      // vectors of step s+1 (from entries read during step s-1), interpolates step s
+      // from vectors read during step s-1, and reads the entries of step s+2, so no
+      // LDS round trip waits on another inside a step.  The entries depend only on
+      // the kernel point, so the ones of the next chunk's first steps are read at the
+      // end of a chunk; its first corner vectors follow the chunk's last barrier, when
+      // the copy of its box is complete.
+      auto chunk9 = [&](int cc, auto parity) __attribute__((always_inline)) {
+        constexpr bool odd = decltype(parity)::value;
+        const unsigned char* src = odd ? box1 : box0;
+        unsigned char* dst = odd ? box0 : box1;
+        if (cc + 1 < nCC) copy_box(cc + 1, dst);
+        static_for<0, 9>([&](auto kc) __attribute__((always_inline)) {
+          constexpr int k = decltype(kc)::value;
+          // an odd chunk starts with Y (nine steps per chunk)
+          PSet& cur = ((k + (odd ? 1 : 0)) & 1) == 0 ? X : Y;
+          PSet& oth = ((k + (odd ? 1 : 0)) & 1) == 0 ? Y : X;
+          if constexpr (k + 1 < 9) read_q(src, oth);
+          finish(cc * 9 + k, cc, cur);
+          read_ce((k + 2) % 9, cur);
+          if constexpr (k == 8) {
+            if (cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
+          }
+          lds_barrier_dma();
+          if constexpr (k == 8) {
+            if (cc + 1 < nCC) read_q(dst, oth);
+          }
+        });
+      };
+      read_ce(0, X);
+      read_ce(1, Y);
+      read_q(box0, X);
+      for (int cc = 0; cc < nCC; cc += 2) {
+        chunk9(cc, std::false_type());
+        if (cc + 1 < nCC) chunk9(cc + 1, std::true_type());
       }
-    };
-    for (int cc = 0; cc < nCC; cc += 2) {
-      chunk(cc, std::false_type());
-      if (cc + 1 < nCC) chunk(cc + 1, std::true_type());
+    } else {
+      // any other kernel size: one step at a time, the entries and corners of each
+      // step read at its start
+      auto chunk = [&](int cc, auto parity) __attribute__((always_inline)) {
+        constexpr bool odd = decltype(parity)::value;
+        const unsigned char* src = odd ? box1 : box0;
+        unsigned char* dst = odd ? box0 : box1;
+        if (cc + 1 < nCC) copy_box(cc + 1, dst);
+        for (int k = 0; k < KK; ++k) {
+          read_ce(k, X);
+          read_q(src, X);
+          finish(cc * KK + k, cc, X);
+          if (k == KK - 1 && cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
+          lds_barrier_dma();
+        }
+      };
+      for (int cc = 0; cc < nCC; cc += 2) {
+        chunk(cc, std::false_type());
+        if (cc + 1 < nCC) chunk(cc + 1, std::true_type());
+      }
     }
     // S barriers here match the consumers' S barriers
+  }
+
+  // ---- epilogue, part 2 (all waves): NCHW stores of the tile, along its rows, two
+  // pixels per 4-byte store where the element index is even
+  static_assert(MT * (NT + 2) * 2 <= BOXB, "output tile must fit in a box buffer");
+  __syncthreads();
+  {
+    // thread -> (pixel pair of a tile row, first row); rows advance by a fixed stride
+    // with the (row, channel) split kept incrementally, so the loop has no divisions
+    const uint16_t* stage = reinterpret_cast<const uint16_t*>(box0);
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    const int TH = ba.TH, TW = ba.TW, TWp = (TW + 1) >> 1;
+    const int rows = MT * TH, rstep = kThreads / TWp;
+    const int pxp = tid % TWp, r0 = tid / TWp;
+    const int px = pxp * 2, ox = ox0 + px;
+    const bool two = px + 1 < TW && ox + 1 < a.Wo;
+    if (r0 < rstep && ox < a.Wo) {
+      const int dol = rstep / TH, dpy = rstep - (rstep / TH) * TH;
+      int ol = r0 / TH, py = r0 - (r0 / TH) * TH;
+#pragma unroll 4
+      for (int r = r0; r < rows; r += rstep) {
+        const int o = m0 + ol, oy = oy0 + py;
+        if (o < a.Cout && oy < a.Ho) {
+          const uint16_t* src = stage + ol * (NT + 2) + py * TW + px;
+          const int e = (b * a.Cout + o) * a.HoWo + oy * a.Wo + ox;
+          if (two && (e & 1) == 0) {
+            *reinterpret_cast<uint32_t*>(out + e) =
+                static_cast<uint32_t>(src[0]) | (static_cast<uint32_t>(src[1]) << 16);
+          } else {
+            out[e] = src[0];
+            if (two) out[e + 1] = src[1];
+          }
+        }
+        ol += dol;
+        py += dpy;
+        if (py >= TH) {
+          py -= TH;
+          ++ol;
+        }
+      }
+    }
   }
 }
 
@@ -596,8 +688,9 @@ template <int FM, int FN>
 static hipError_t launch_box_t(const BoxArgs& ba, hipStream_t stream) {
   void* args[] = {const_cast<BoxArgs*>(&ba)};
   const dim3 grid(ba.f.m_tiles * ba.tiles_per_img * ba.f.B);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN>), grid, dim3(kThreads), args, 0,
-                         stream);
+  const void* fn = ba.f.KK == 9 ? reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN, 9>)
+                                : reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN, 0>);
+  return hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, stream);
 }
 
 hipError_t launch_box(int fm, int fn, const BoxArgs& ba, hipStream_t stream) {

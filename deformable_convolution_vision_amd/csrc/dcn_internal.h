@@ -26,8 +26,9 @@ struct StageArgs {
   const void* x;   // [B][Cin][H][W]
   const void* w;   // [Cout][Cin][K][K]
   void* xs;        // [B][H*W][Cp]
-  void* wp;        // [Mp][KK][Cp]
+  void* wp;        // wlayout 0: [Mp][KK][Cp]; wlayout 1: [Cp/32 * KK][Mp][32] (step-major)
   int B, Cin, HW, Cp, Cout, Mp, KK;
+  int wlayout;
 };
 
 // Box kernel (bf16): FusedArgs plus the output-tile geometry and the LDS budget.

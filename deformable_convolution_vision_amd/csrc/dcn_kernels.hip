@@ -96,7 +96,8 @@ __device__ __forceinline__ int xcd_tile(int g, int T) {
 //                        one channel (VEC = 16 bytes' worth when H*W allows the
 //                        alignment, fewer otherwise), global writes are 16-byte
 //                        channel vectors of one pixel.
-//   Workgroups [nx, ..): w[o][c][k] -> wp[o][k][c] for o < Mp, k < KK, c < Cp,
+//   Workgroups [nx, ..): w[o][c][k] -> wp[o][k][c] (or the step-major layout of the
+//   box kernel) for o < Mp, k < KK, c < Cp,
 //                        zero outside Cout x Cin.
 template <bool BF16, int VEC>
 __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a, int nx, int s_tiles, int c_tiles) {
@@ -111,9 +112,18 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a, int nx, in
     const int total = a.Mp * a.KK * a.Cp;
     const int nw = gridDim.x - nx;
     for (int e = (blockIdx.x - nx) * kThreads + tid; e < total; e += nw * kThreads) {
-      const int c = e % a.Cp;
-      const int k = (e / a.Cp) % a.KK;
-      const int o = e / (a.Cp * a.KK);
+      int c, k, o;
+      if (a.wlayout == 0) {
+        c = e % a.Cp;
+        k = (e / a.Cp) % a.KK;
+        o = e / (a.Cp * a.KK);
+      } else {
+        // step s = chunk * KK + k, then row, then the 32 channels of the chunk
+        const int s = e / (32 * a.Mp);
+        o = (e / 32) % a.Mp;
+        k = s % a.KK;
+        c = (s / a.KK) * 32 + (e % 32);
+      }
       T v = T(0);
       if (o < a.Cout && c < a.Cin) v = w[(o * a.Cin + c) * a.KK + k];
       wp[e] = v;
