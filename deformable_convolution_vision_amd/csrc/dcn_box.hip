@@ -151,6 +151,13 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 __device__ __forceinline__ void lds_barrier_dma() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The same with the last N LDS operations of this wave still in flight: reads whose
+// data nobody changes across the barrier.  LDS operations complete in order, so the
+// operations before them (the column stores the barrier publishes) are complete.
+template <int N>
+__device__ __forceinline__ void lds_barrier_keep() {
+  asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 }  // namespace
 
@@ -225,7 +232,10 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       x3 = load_a(min(c0 + 3, S - 1));
     }
   };
-  if (consumer) load_group(0, p0, p1, p2, p3);
+  if (consumer) {
+    load_group(0, p0, p1, p2, p3);
+    load_group(G, q0, q1, q2, q3);
+  }
 
   // ---- prologue pass 1 (all waves): sampling positions and weights; extent of the upper corners
   if (tid < 4) red[tid] = (tid & 1) ? -0x40000000 : 0x40000000;   // min y, max y, min x, max x
@@ -400,34 +410,35 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // last two chunks no barrier after them, so the consumers pass exactly S barriers,
     // like the producers.  `step` is the steady state (all three parts present);
     // `step_tail` tests each part.
-    auto step = [&](int c, const AFrag& af, const BFrag& bc, BFrag& bn) __attribute__((always_inline)) {
+    // Each step reloads the weight slot it has just multiplied with the chunk 2G
+    // steps later, so the weight loads are spread evenly and arrive 2G-1 steps early.
+    auto step = [&](int c, AFrag& af, const BFrag& bc, BFrag& bn) __attribute__((always_inline)) {
       bn = read_b(c + 1);
       mma(af, bc);
+      af = load_a(min(c + 2 * G, S - 1));
       lds_barrier();
     };
-    auto step_tail = [&](int c, const AFrag& af, const BFrag& bc, BFrag& bn) __attribute__((always_inline)) {
+    auto step_tail = [&](int c, AFrag& af, const BFrag& bc, BFrag& bn) __attribute__((always_inline)) {
       if (c >= S) return;
       if (c + 1 < S) bn = read_b(c + 1);
       mma(af, bc);
+      if (c + 2 * G < S) af = load_a(c + 2 * G);
       if (c + 2 < S) lds_barrier();
     };
     BFrag b0{}, b1{};
     lds_barrier();                 // barrier 0: chunk 0 is produced
     b0 = read_b(0);
     if (S > 1) lds_barrier();      // barrier 1: chunk 1 is produced
-    // 2G chunks per iteration; each group of G starts by loading the weights of the
-    // next group, which then have G steps to arrive.  The loop runs while every step
+    // 2G chunks per iteration (slots p0.. then q0..).  The loop runs while every step
     // of the iteration has all three parts, so its body has no branches.
     int c = 0;
     for (; c + 2 * G + 2 <= S; c += 2 * G) {
-      load_group(c + G, q0, q1, q2, q3);
       step(c, p0, b0, b1);
       step(c + 1, p1, b1, b0);
       if constexpr (G == 4) {
         step(c + 2, p2, b0, b1);
         step(c + 3, p3, b1, b0);
       }
-      load_group(c + 2 * G, p0, p1, p2, p3);
       step(c + G, q0, b0, b1);
       step(c + G + 1, q1, b1, b0);
       if constexpr (G == 4) {
@@ -435,15 +446,14 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         step(c + 7, q3, b1, b0);
       }
     }
-    // at most 2G+1 chunks remain
-    load_group(c + G, q0, q1, q2, q3);
+    // at most 2G+1 chunks remain; the slots hold chunks c .. c+2G-1 and step c
+    // reloads p0 with chunk c+2G
     step_tail(c, p0, b0, b1);
     step_tail(c + 1, p1, b1, b0);
     if constexpr (G == 4) {
       step_tail(c + 2, p2, b0, b1);
       step_tail(c + 3, p3, b1, b0);
     }
-    if (c + 2 * G < S) load_group(c + 2 * G, p0, p1, p2, p3);
     step_tail(c + G, q0, b0, b1);
     step_tail(c + G + 1, q1, b1, b0);
     if constexpr (G == 4) {
@@ -490,22 +500,38 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const uint32_t img_off = static_cast<uint32_t>(b * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u +
                              static_cast<uint32_t>((lane & 3) * 16);
     const uint32_t row_bytes = static_cast<uint32_t>(a.W * Cp) * 2u, px_bytes = static_cast<uint32_t>(Cp) * 2u;
-    auto copy_box = [&](int cc, unsigned char* dst) __attribute__((always_inline)) {
+    // The copy can be issued in parts: `cp` holds the position of the wave's next block.
+    struct Copier { int blk, px, ry, rx; };
+    auto copy_begin = [&](Copier& cp) __attribute__((always_inline)) {
+      cp.blk = pw;
+      cp.px = px_first;
+      cp.ry = ry_first;
+      cp.rx = rx_first;
+    };
+    auto copy_part = [&](int cc, unsigned char* dst, Copier& cp, int nmax) __attribute__((always_inline)) {
       const unsigned char* base = xs + static_cast<size_t>(cc * kCK) * 2;
-      int px = px_first, ry = ry_first, rx = rx_first;
-      for (int blk = pw; blk < nblk; blk += 4) {
-        const int gy = by0 + ry, gx = bx0 + rx;
-        if (px < npx && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W) {
+      for (int n = 0; n < nmax && cp.blk < nblk; ++n) {
+        const int gy = by0 + cp.ry, gx = bx0 + cp.rx;
+        if (cp.px < npx && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W) {
           const uint32_t off = img_off + static_cast<uint32_t>(gy) * row_bytes + static_cast<uint32_t>(gx) * px_bytes;
           __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off),
-                                           (lds_void*)(dst + blk * 1024), 16, 0, 0);
+                                           (lds_void*)(dst + cp.blk * 1024), 16, 0, 0);
         }
-        px += 64;
-        ry += step_r;
-        rx += step_c;
-        if (rx >= BW) { rx -= BW; ++ry; }
+        cp.blk += 4;
+        cp.px += 64;
+        cp.ry += step_r;
+        cp.rx += step_c;
+        if (cp.rx >= BW) { cp.rx -= BW; ++cp.ry; }
       }
     };
+    auto copy_box = [&](int cc, unsigned char* dst) __attribute__((always_inline)) {
+      Copier cp;
+      copy_begin(cp);
+      copy_part(cc, dst, cp, nblk);
+    };
+    // this wave's blocks, and the share issued in each of the first four steps of a chunk
+    const int wave_blocks = nblk > pw ? (nblk - pw + 3) / 4 : 0;
+    const int part_blocks = (wave_blocks + 3) / 4;
 
     // Producer state of one step: the corner-table entries and the four corner vectors
     // of this thread's samples.  A sample with nothing in the box reads the zero bytes
@@ -514,7 +540,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     auto read_ce = [&](int k, PSet& f) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < GU; ++g)
-        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) f.ce[g] = ctab[k * NT + ((ptid + g * 256) >> 2)];
+        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS)
+          f.ce[g] = __builtin_bit_cast(CEnt, reinterpret_cast<const uint4*>(ctab)[k * NT + ((ptid + g * 256) >> 2)]);
     };
     auto read_q = [&](const unsigned char* src, PSet& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -578,45 +605,94 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // behind a runtime pointer select), so every LDS access names its array and only
     // waits for copies into that array.  Each chunk starts copying the next chunk's
     // box into the other buffer and waits for that copy before its last barrier.
-    PSet X, Y;
+    PSet X, Y, Z;
     if constexpr (KKT == 9) {
       // Three kernel points: the nine steps of a chunk are unrolled and software
-      // pipelined over the register sets X and Y, which alternate from step to step
-      // (no copies between steps).  During step s the producer reads the corner
-      // vectors of step s+1 (from entries read during step s-1), interpolates step s
-      // from vectors read during step s-1, and reads the entries of step s+2, so no
-      // LDS round trip waits on another inside a step.  The entries depend only on
-      // the kernel point, so the ones of the next chunk's first steps are read at the
-      // end of a chunk; its first corner vectors follow the chunk's last barrier, when
-      // the copy of its box is complete.
+      // pipelined over three register sets, step k using set k % 3 (nine steps per
+      // chunk keep the assignment the same in every chunk).  Step k interpolates from
+      // corner vectors read during step k-2, stores its column tile, and then reads
+      // the corner vectors of step k+2 and the corner-table entries of step k+3; those
+      // reads stay in flight across the barrier (the box being read and the table do
+      // not change), so no LDS round trip is on a step's critical path.  The next
+      // chunk's box is copied during steps 0-3; each wave waits for its part before
+      // barrier 6, after which the whole box is in LDS and steps 7 and 8 read the
+      // corners of the next chunk's steps 0 and 1 from it.
+      constexpr int kKeep = GU * 5 < 15 ? GU * 5 : 15;   // LDS reads issued after the column stores
       auto chunk9 = [&](int cc, auto parity) __attribute__((always_inline)) {
         constexpr bool odd = decltype(parity)::value;
         const unsigned char* src = odd ? box1 : box0;
         unsigned char* dst = odd ? box0 : box1;
-        if (cc + 1 < nCC) copy_box(cc + 1, dst);
+        Copier cp;
+        copy_begin(cp);
         static_for<0, 9>([&](auto kc) __attribute__((always_inline)) {
           constexpr int k = decltype(kc)::value;
-          // an odd chunk starts with Y (nine steps per chunk)
+          PSet& cur = k % 3 == 0 ? X : (k % 3 == 1 ? Y : Z);
+          PSet& ahead = (k + 2) % 3 == 0 ? X : ((k + 2) % 3 == 1 ? Y : Z);
+          if constexpr (k < 4) {
+            if (cc + 1 < nCC) copy_part(cc + 1, dst, cp, part_blocks);
+          }
+          finish(cc * 9 + k, cc, cur);
+          asm volatile("" ::: "memory");   // the column stores stay ahead of the reads below
+          read_ce((k + 3) % 9, cur);
+          if constexpr (k + 2 < 9) {
+            read_q(src, ahead);
+          } else {
+            // the next chunk's steps 0 and 1 (a dummy re-read of this box after the last chunk)
+            if (cc + 1 < nCC) read_q(dst, ahead);
+            else read_q(src, ahead);
+          }
+          if constexpr (k == 6) {
+            if (cc + 1 < nCC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          }
+          lds_barrier_keep<kKeep>();
+        });
+      };
+      // With more than one sample per thread three sets would not fit in registers:
+      // two sets, step k using set (k + chunk parity) % 2, corners read one step ahead.
+      auto chunk9_two = [&](int cc, auto parity) __attribute__((always_inline)) {
+        constexpr bool odd = decltype(parity)::value;
+        const unsigned char* src = odd ? box1 : box0;
+        unsigned char* dst = odd ? box0 : box1;
+        Copier cp;
+        copy_begin(cp);
+        static_for<0, 9>([&](auto kc) __attribute__((always_inline)) {
+          constexpr int k = decltype(kc)::value;
           PSet& cur = ((k + (odd ? 1 : 0)) & 1) == 0 ? X : Y;
           PSet& oth = ((k + (odd ? 1 : 0)) & 1) == 0 ? Y : X;
-          if constexpr (k + 1 < 9) read_q(src, oth);
+          if constexpr (k < 4) {
+            if (cc + 1 < nCC) copy_part(cc + 1, dst, cp, part_blocks);
+          }
           finish(cc * 9 + k, cc, cur);
+          asm volatile("" ::: "memory");
+          if constexpr (k + 1 < 9) read_q(src, oth);
           read_ce((k + 2) % 9, cur);
           if constexpr (k == 8) {
             if (cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
-          }
-          lds_barrier_dma();
-          if constexpr (k == 8) {
+            lds_barrier_dma();
             if (cc + 1 < nCC) read_q(dst, oth);
+          } else {
+            lds_barrier_keep<kKeep>();
           }
         });
       };
-      read_ce(0, X);
-      read_ce(1, Y);
-      read_q(box0, X);
-      for (int cc = 0; cc < nCC; cc += 2) {
-        chunk9(cc, std::false_type());
-        if (cc + 1 < nCC) chunk9(cc + 1, std::true_type());
+      if constexpr (GU == 1) {
+        read_ce(0, X);
+        read_ce(1, Y);
+        read_ce(2, Z);
+        read_q(box0, X);
+        read_q(box0, Y);
+        for (int cc = 0; cc < nCC; cc += 2) {
+          chunk9(cc, std::false_type());
+          if (cc + 1 < nCC) chunk9(cc + 1, std::true_type());
+        }
+      } else {
+        read_ce(0, X);
+        read_ce(1, Y);
+        read_q(box0, X);
+        for (int cc = 0; cc < nCC; cc += 2) {
+          chunk9_two(cc, std::false_type());
+          if (cc + 1 < nCC) chunk9_two(cc + 1, std::true_type());
+        }
       }
     } else {
       // any other kernel size: one step at a time, the entries and corners of each
@@ -647,30 +723,37 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   static_assert(MT * (NT + 2) * 2 <= BOXB, "output tile must fit in a box buffer");
   __syncthreads();
   {
-    // thread -> (pixel pair of a tile row, first row); rows advance by a fixed stride
-    // with the (row, channel) split kept incrementally, so the loop has no divisions
+    // Thread -> (column pair of a tile row, first row).  Pairs are aligned to even
+    // output columns, so with even Wo and Ho*Wo a pair with both columns in the tile
+    // is one aligned 4-byte store.  Rows advance by a fixed stride with the (row,
+    // channel) split kept incrementally; LDS reads are unconditional (clamped index)
+    // so the loop has no divisions and no branch around a read.
     const uint16_t* stage = reinterpret_cast<const uint16_t*>(box0);
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-    const int TH = ba.TH, TW = ba.TW, TWp = (TW + 1) >> 1;
-    const int rows = MT * TH, rstep = kThreads / TWp;
-    const int pxp = tid % TWp, r0 = tid / TWp;
-    const int px = pxp * 2, ox = ox0 + px;
-    const bool two = px + 1 < TW && ox + 1 < a.Wo;
-    if (r0 < rstep && ox < a.Wo) {
+    const int TH = ba.TH, TW = ba.TW;
+    const int xs0 = ox0 & ~1;
+    const int slots = (ox0 - xs0 + TW + 1) >> 1;
+    const int rows = MT * TH, rstep = kThreads / slots;
+    const int slot = tid % slots, r0 = tid / slots;
+    const int c0 = xs0 + slot * 2, xend = min(ox0 + TW, a.Wo);
+    const bool in0 = c0 >= ox0 && c0 < xend, in1 = c0 + 1 >= ox0 && c0 + 1 < xend;
+    const int q0 = max(c0 - ox0, 0), q1 = min(c0 + 1 - ox0, TW - 1);
+    const bool pair = in0 && in1 && (a.Wo & 1) == 0 && (a.HoWo & 1) == 0;
+    if (r0 < rstep && (in0 || in1)) {
       const int dol = rstep / TH, dpy = rstep - (rstep / TH) * TH;
       int ol = r0 / TH, py = r0 - (r0 / TH) * TH;
 #pragma unroll 4
       for (int r = r0; r < rows; r += rstep) {
         const int o = m0 + ol, oy = oy0 + py;
+        const uint16_t* src = stage + ol * (NT + 2) + py * TW;
+        const uint32_t v0 = src[q0], v1 = src[q1];
         if (o < a.Cout && oy < a.Ho) {
-          const uint16_t* src = stage + ol * (NT + 2) + py * TW + px;
-          const int e = (b * a.Cout + o) * a.HoWo + oy * a.Wo + ox;
-          if (two && (e & 1) == 0) {
-            *reinterpret_cast<uint32_t*>(out + e) =
-                static_cast<uint32_t>(src[0]) | (static_cast<uint32_t>(src[1]) << 16);
+          const int e = (b * a.Cout + o) * a.HoWo + oy * a.Wo + c0;
+          if (pair) {
+            *reinterpret_cast<uint32_t*>(out + e) = v0 | (v1 << 16);
           } else {
-            out[e] = src[0];
-            if (two) out[e + 1] = src[1];
+            if (in0) out[e] = static_cast<uint16_t>(v0);
+            if (in1) out[e + 1] = static_cast<uint16_t>(v1);
           }
         }
         ol += dol;
