@@ -89,6 +89,29 @@ __device__ __forceinline__ int xcd_tile(int g, int T) {
 // staging
 // ---------------------------------------------------------------------------
 
+// Weight repack, one thread per (row o, channel c): the K*K values of (o, c) are
+// contiguous in w, and for each kernel point neighbouring threads write neighbouring
+// channels.  Layout 0: wp[o][k][c]; layout 1 (box kernel): wp[c/32 * KK + k][o][c%32].
+// Rows >= Cout and channels >= Cin are written as 0.
+template <typename T>
+__device__ __forceinline__ void pack_weight(const StageArgs& a, int wg, int nwg) {
+  const T* w = reinterpret_cast<const T*>(a.w);
+  T* wp = reinterpret_cast<T*>(a.wp);
+  const int total = a.Mp * a.Cp;
+  for (int e = wg * kThreads + static_cast<int>(threadIdx.x); e < total; e += nwg * kThreads) {
+    const int o = e / a.Cp, c = e - (e / a.Cp) * a.Cp;
+    const bool live = o < a.Cout && c < a.Cin;
+    const T* src = w + (static_cast<size_t>(o) * a.Cin + c) * a.KK;
+    for (int k = 0; k < a.KK; ++k) {
+      const T v = live ? src[k] : T(0);
+      const size_t dst = a.wlayout == 0
+                             ? (static_cast<size_t>(o) * a.KK + k) * a.Cp + c
+                             : ((static_cast<size_t>(c >> 5) * a.KK + k) * a.Mp + o) * 32 + (c & 31);
+      wp[dst] = v;
+    }
+  }
+}
+
 // One launch stages both operands of the fused kernel.
 //   Workgroups [0, nx):  x[b][c][s] -> xs[b][s][c] for s in [0, H*W), c in [0, Cp),
 //                        channels >= Cin written as 0.  Each moves a 64-channel x
@@ -107,27 +130,7 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a, int nx, in
   __shared__ T tile[64][64 + 2];                 // [channel][pixel]
   const int tid = threadIdx.x;
   if (static_cast<int>(blockIdx.x) >= nx) {
-    const T* w = reinterpret_cast<const T*>(a.w);
-    T* wp = reinterpret_cast<T*>(a.wp);
-    const int total = a.Mp * a.KK * a.Cp;
-    const int nw = gridDim.x - nx;
-    for (int e = (blockIdx.x - nx) * kThreads + tid; e < total; e += nw * kThreads) {
-      int c, k, o;
-      if (a.wlayout == 0) {
-        c = e % a.Cp;
-        k = (e / a.Cp) % a.KK;
-        o = e / (a.Cp * a.KK);
-      } else {
-        // step s = chunk * KK + k, then row, then the 32 channels of the chunk
-        const int s = e / (32 * a.Mp);
-        o = (e / 32) % a.Mp;
-        k = s % a.KK;
-        c = (s / a.KK) * 32 + (e % 32);
-      }
-      T v = T(0);
-      if (o < a.Cout && c < a.Cin) v = w[(o * a.Cin + c) * a.KK + k];
-      wp[e] = v;
-    }
+    pack_weight<T>(a, static_cast<int>(blockIdx.x) - nx, static_cast<int>(gridDim.x) - nx);
     return;
   }
   const int per_img = s_tiles * c_tiles;
@@ -467,17 +470,16 @@ const VariantInfo& variant_info(int v) { return kVariants[v]; }
 hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream) {
   const VariantInfo& vi = kVariants[variant];
   if (!vi.staged) return hipSuccess;
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(a.x);
   const int s_tiles = (a.HW + 63) / 64, c_tiles = (a.Cp + 63) / 64;
   const int nx = s_tiles * c_tiles * a.B;
-  const int wtotal = a.Mp * a.KK * a.Cp;
-  const int nw = min((wtotal + kThreads - 1) / kThreads, 1024);
+  const int nw = min((a.Mp * a.Cp + kThreads - 1) / kThreads, 1024);
   const dim3 grid(nx + nw);
   StageArgs sa = a;
   void* args[] = {&sa, const_cast<int*>(&nx), const_cast<int*>(&s_tiles), const_cast<int*>(&c_tiles)};
   const void* fn;
   // widest global read that every channel plane (starting at x + c*H*W elements)
   // keeps aligned, given the caller's x pointer
-  const uintptr_t xa = reinterpret_cast<uintptr_t>(a.x);
   auto fits = [&](int vec, int es) { return a.HW % vec == 0 && xa % static_cast<uintptr_t>(vec * es) == 0; };
   if (vi.is_bf16)
     fn = fits(8, 2)   ? reinterpret_cast<const void*>(&stage_kernel<true, 8>)
