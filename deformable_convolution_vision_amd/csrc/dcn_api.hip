@@ -142,6 +142,9 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
 // Pick the kernel variant for a valid descriptor.
 int choose_variant(const dcn_desc* d, int64_t N, int64_t Ho, int64_t Wo, BoxPlan* bp) {
   const int64_t M = d->out_channels;
+  // tiny reductions (an RGB first layer): the column fits in registers
+  if (dcn::direct_supported(static_cast<int>(d->in_channels), static_cast<int>(d->kernel_size * d->kernel_size)))
+    return d->dtype == DCN_F32 ? dcn::V_DIRECT_F32 : dcn::V_DIRECT_BF16;
   if (d->dtype == DCN_F32) return M <= 64 ? dcn::V_TILE_F32_M64_N64 : dcn::V_TILE_F32_M128_N64;
   // the box kernel for channel counts where a 32-channel chunk is mostly real data
   if (d->in_channels >= 24 && M >= 64 && plan_box(d, Ho, Wo, 0, bp))
@@ -172,6 +175,9 @@ int compute_plan(const dcn_desc* d, Plan* p) {
       for (int v = 0; v < dcn::V_COUNT; ++v)
         if (std::strcmp(force, dcn::variant_info(v).name) == 0) found = v;
       if (found < 0 || dcn::variant_info(found).is_bf16 != (d->dtype == DCN_BF16)) return DCN_E_UNSUPPORTED;
+      if ((found == dcn::V_DIRECT_F32 || found == dcn::V_DIRECT_BF16) &&
+          !dcn::direct_supported(static_cast<int>(Cin), static_cast<int>(KK)))
+        return DCN_E_UNSUPPORTED;
       if (found == dcn::V_BOX_BF16_M128 || found == dcn::V_BOX_BF16_M256) {
         if (!plan_box(d, p->Ho, p->Wo, found == dcn::V_BOX_BF16_M128 ? 2 : 4, &p->box)) return DCN_E_UNSUPPORTED;
       }
@@ -255,6 +261,7 @@ int check_workspace(const Plan& p, const void* ws, size_t ws_bytes) {
 }
 
 bool is_box(int variant) { return variant == dcn::V_BOX_BF16_M128 || variant == dcn::V_BOX_BF16_M256; }
+bool is_direct(int variant) { return variant == dcn::V_DIRECT_F32 || variant == dcn::V_DIRECT_BF16; }
 
 StageArgs stage_args(const dcn_desc* d, const Plan& p, const void* x, const void* w, void* ws) {
   StageArgs a{};
@@ -307,6 +314,7 @@ FusedArgs fused_args(const dcn_desc* d, const Plan& p, const void* x, const void
 }
 
 hipError_t launch_fused_plan(const Plan& p, const FusedArgs& a, hipStream_t stream) {
+  if (is_direct(p.variant)) return dcn::launch_direct(p.variant == dcn::V_DIRECT_BF16, a, stream);
   if (!is_box(p.variant)) return dcn::launch_fused(p.variant, a, stream);
   dcn::BoxArgs ba{};
   ba.f = a;

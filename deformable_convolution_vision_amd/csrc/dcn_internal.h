@@ -51,6 +51,8 @@ enum Variant : int {
   V_TILE_BF16_M256_N64,
   V_BOX_BF16_M128,
   V_BOX_BF16_M256,
+  V_DIRECT_F32,
+  V_DIRECT_BF16,
   V_COUNT
 };
 
@@ -71,6 +73,10 @@ hipError_t launch_fused(int variant, const FusedArgs& a, hipStream_t stream);
 // box_capacity_px: pixels one LDS box buffer holds for a given fn (0 if not built).
 hipError_t launch_box(int fm, int fn, const BoxArgs& a, hipStream_t stream);
 int box_capacity_px(int fn);
+
+// direct kernel (no staging): Cin <= 4 and K*K in {1, 4, 9}
+bool direct_supported(int cin, int kk);
+hipError_t launch_direct(bool bf16, const FusedArgs& a, hipStream_t stream);
 constexpr int kLdsBudget = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kBoxMaxKK = 9;             // the box kernel handles K*K <= 9
 

@@ -463,6 +463,8 @@ static const VariantInfo kVariants[V_COUNT] = {
     {"tile_bf16_m256_n64", 1, 256, 64, 32, 1},
     {"box_bf16_m128", 1, 128, 0, 32, 1},
     {"box_bf16_m256", 1, 256, 0, 32, 1},
+    {"direct_f32", 0, 64, 64, 1, 0},
+    {"direct_bf16", 1, 64, 64, 1, 0},
 };
 
 const VariantInfo& variant_info(int v) { return kVariants[v]; }

@@ -169,6 +169,18 @@ def test_forced_variant(lib, monkeypatch):
     assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
     monkeypatch.setenv("DCN_VARIANT", "no_such_variant")
     assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+    monkeypatch.setenv("DCN_VARIANT", "direct_bf16")                # 64 input channels: too many
+    assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+
+
+def test_small_reductions_take_the_direct_kernel_without_workspace(lib):
+    for dt, name in ((dcn.F32, "direct_f32"), (dcn.BF16, "direct_bf16")):
+        for cin, k in ((3, 3), (1, 1), (4, 2)):
+            desc = dcn.make_desc(1, cin, 40, 40, 64, k, 1, k // 2, 1, dt)
+            assert dcn.dcn_variant_name(desc) == name
+            assert dcn.dcn_workspace_bytes(desc) == 0
+        desc = dcn.make_desc(1, 3, 40, 40, 64, 5, 1, 2, 1, dt)      # K*K = 25: staged kernels
+        assert not dcn.dcn_variant_name(desc).startswith("direct")
 
 
 def test_status_strings(lib):

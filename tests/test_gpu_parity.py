@@ -79,7 +79,8 @@ def test_edge_shape(name, kw, dtype):
 def _variants(dtype):
     names = []
     for v in ("tile_f32_m64_n64", "tile_f32_m128_n64", "tile_bf16_m64_n64", "tile_bf16_m128_n64",
-              "tile_bf16_m128_n32", "tile_bf16_m256_n64", "box_bf16_m128", "box_bf16_m256"):
+              "tile_bf16_m128_n32", "tile_bf16_m256_n64", "box_bf16_m128", "box_bf16_m256",
+              "direct_f32", "direct_bf16"):
         if ("bf16" in v) == (dtype == "bf16"):
             names.append(v)
     return names
@@ -89,7 +90,10 @@ def _variants(dtype):
 def test_every_variant(variant, monkeypatch):
     dtype = "bf16" if "bf16" in variant else "f32"
     monkeypatch.setenv("DCN_VARIANT", variant)
-    for seed, shape in enumerate([(3, 37, 11, 13, 70, 3, 1, 1, 1), (2, 64, 9, 10, 260, 3, 2, 1, 1)]):
+    shapes = [(3, 37, 11, 13, 70, 3, 1, 1, 1), (2, 64, 9, 10, 260, 3, 2, 1, 1)]
+    if variant.startswith("direct"):   # at most 4 input channels, K*K in {1, 4, 9}
+        shapes = [(3, 3, 11, 13, 70, 3, 1, 1, 1), (2, 4, 9, 10, 37, 2, 2, 0, 1), (1, 1, 6, 7, 5, 1, 1, 0, 1)]
+    for seed, shape in enumerate(shapes):
         w = make(f"sweep_{variant}", dtype, *shape, offset="normal:2", seed=seed)
         assert variant_of(w) == variant
         full_parity(w)
