@@ -139,11 +139,22 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
   return true;
 }
 
+// The direct kernel: at most 4 input channels, K*K in {1, 4, 9}, and every tensor it
+// reads under 2 GiB (it addresses them with 32-bit byte offsets).
+bool direct_fits(const dcn_desc* d, int64_t HoWo) {
+  const int64_t KK = d->kernel_size * d->kernel_size;
+  if (!dcn::direct_supported(static_cast<int>(d->in_channels), static_cast<int>(KK))) return false;
+  const double es = d->dtype == DCN_BF16 ? 2.0 : 4.0, lim = 2147483647.0;
+  return static_cast<double>(d->batch) * d->in_channels * d->height * d->width * es < lim &&
+         static_cast<double>(d->batch) * 2 * KK * HoWo * es < lim &&
+         static_cast<double>(d->out_channels) * d->in_channels * KK * es < lim;
+}
+
 // Pick the kernel variant for a valid descriptor.
 int choose_variant(const dcn_desc* d, int64_t N, int64_t Ho, int64_t Wo, BoxPlan* bp) {
   const int64_t M = d->out_channels;
   // tiny reductions (an RGB first layer): the column fits in registers
-  if (dcn::direct_supported(static_cast<int>(d->in_channels), static_cast<int>(d->kernel_size * d->kernel_size)))
+  if (direct_fits(d, Ho * Wo))
     return d->dtype == DCN_F32 ? dcn::V_DIRECT_F32 : dcn::V_DIRECT_BF16;
   if (d->dtype == DCN_F32) return M <= 64 ? dcn::V_TILE_F32_M64_N64 : dcn::V_TILE_F32_M128_N64;
   // the box kernel for channel counts where a 32-channel chunk is mostly real data
@@ -175,8 +186,7 @@ int compute_plan(const dcn_desc* d, Plan* p) {
       for (int v = 0; v < dcn::V_COUNT; ++v)
         if (std::strcmp(force, dcn::variant_info(v).name) == 0) found = v;
       if (found < 0 || dcn::variant_info(found).is_bf16 != (d->dtype == DCN_BF16)) return DCN_E_UNSUPPORTED;
-      if ((found == dcn::V_DIRECT_F32 || found == dcn::V_DIRECT_BF16) &&
-          !dcn::direct_supported(static_cast<int>(Cin), static_cast<int>(KK)))
+      if ((found == dcn::V_DIRECT_F32 || found == dcn::V_DIRECT_BF16) && !direct_fits(d, HoWo))
         return DCN_E_UNSUPPORTED;
       if (found == dcn::V_BOX_BF16_M128 || found == dcn::V_BOX_BF16_M256) {
         if (!plan_box(d, p->Ho, p->Wo, found == dcn::V_BOX_BF16_M128 ? 2 : 4, &p->box)) return DCN_E_UNSUPPORTED;
