@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16_mfma": 2516.6, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, TFLOP/s, GB/s
 CSRC = os.path.join(ROOT, "deformable_convolution_vision_amd", "csrc")
-KERNEL_SRCS = ("dcn_internal.h", "dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip")
+KERNEL_SRCS = ("dcn_internal.h", "dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip", "dcn_direct.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -47,13 +47,18 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_symbol(variant: str, plan: str) -> str:
+def kernel_symbol(variant: str, plan: str, w) -> str:
     """Device symbol of the fused launch, as rocprofv3 names it."""
     import re
+    kk = w.K * w.K
     if variant.startswith("box"):
         m = re.search(r"\((\d+) slots\) x (\d+) ch", plan)
-        return f"dcn_box_kernel<{int(m.group(2)) // 64}, {int(m.group(1)) // 16}>"
-    return f"dcn_fused_kernel ({variant})"
+        return f"dcn_box_kernel<{int(m.group(2)) // 64}, {int(m.group(1)) // 16}, {9 if kk == 9 else 0}>"
+    if variant.startswith("direct"):
+        bf16 = "true" if variant.endswith("bf16") else "false"
+        return f"dcn_direct_kernel<{bf16}, {kk}, {3 if (w.Cin == 3 and kk == 9) else 0}>"
+    m = re.match(r"tile_(\w+)_m(\d+)_n(\d+)", variant)
+    return f"dcn_fused_kernel<{'true' if m.group(1) == 'bf16' else 'false'}, {m.group(2)}, {m.group(3)}>"
 
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
@@ -223,7 +228,7 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
         "frac_hbm_peak": round(gbps / PEAK["hbm"], 5),
         "roofline": {"bound": bound, "achieved": round(achieved, 4), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 5), "traffic": traffic,
-                     "kernel": kernel_symbol(variant, plan), "kernel_sha": kernel_hash(),
+                     "kernel": kernel_symbol(variant, plan, w), "kernel_sha": kernel_hash(),
                      "per_launch": {"flops": flops, "algorithmic_bytes": abytes}},
         "kernels_us": {"stage_mean": round(stage_mean * 1e3, 3), "fused_mean": round(fused_mean * 1e3, 3),
                        "fused_median": round(fused_ms[steps // 2] * 1e3, 3),
