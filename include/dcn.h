@@ -38,14 +38,20 @@
  *    is not written.  DCN_E_HIP reports a failed kernel launch (the launch's own
  *    return code).  No C++ exception crosses this interface.
  *  - Arithmetic: positions and bilinear weights in fp32; bf16 samples are
- *    interpolated in fp32 and rounded to bf16 (nearest even) before the matrix
- *    product; products accumulate in fp32; out is rounded to dtype.
+ *    interpolated in fp32 (the box kernel rounds the bilinear weights times the
+ *    mask to bf16 first) and rounded to bf16 (nearest even) before the matrix
+ *    product; products accumulate in fp32; out is rounded to dtype.  With at
+ *    most 4 input channels and K*K in {1, 4, 9} the column stays in fp32 and no
+ *    workspace is needed (dcn_workspace_bytes returns 0).
  *  - Limits: every tensor (and the staged copy of x) has fewer than 2^31
  *    elements; otherwise DCN_E_UNSUPPORTED.
  *  - Variant choice: a kernel variant is picked from the descriptor.  The
  *    environment variable DCN_VARIANT=<name> (a name dcn_variant_name can
- *    return) pins it, for tile sweeps and tests; a name that does not exist or
- *    was built for the other dtype makes every call return DCN_E_UNSUPPORTED.
+ *    return) pins it, for tile sweeps and tests; a name that does not exist, was
+ *    built for the other dtype or cannot run the shape makes every call return
+ *    DCN_E_UNSUPPORTED.  DCN_BOX_TILE="fn,TH,TW" restricts the box kernel's tile
+ *    to 16*fn pixel slots holding TH x TW output pixels (sweeps only).  Plans are
+ *    cached per descriptor and the two variables' values.
  */
 #ifndef DCN_H
 #define DCN_H
