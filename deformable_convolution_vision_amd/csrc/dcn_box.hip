@@ -133,6 +133,16 @@ __device__ __forceinline__ float ld_bf16(const void* p, int idx) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
+// Raw buffer resource over `p` with the largest range (4 GiB - 1 bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const unsigned char* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(p), 0, -1, 0x00020000);
+}
+// Direct buffer->LDS load: 16 bytes per lane from byte offset `voff`, lane l's bytes
+// at dst + 16*l.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+
 // Workgroup barriers that order LDS traffic only; outstanding global loads stay in
 // flight across them.
 //  * lds_barrier: release/acquire fences limited to the local address space around
@@ -500,38 +510,46 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const uint32_t img_off = static_cast<uint32_t>(b * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u +
                              static_cast<uint32_t>((lane & 3) * 16);
     const uint32_t row_bytes = static_cast<uint32_t>(a.W * Cp) * 2u, px_bytes = static_cast<uint32_t>(Cp) * 2u;
-    // The copy can be issued in parts: `cp` holds the position of the wave's next block.
-    struct Copier { int blk, px, ry, rx; };
-    auto copy_begin = [&](Copier& cp) __attribute__((always_inline)) {
-      cp.blk = pw;
-      cp.px = px_first;
-      cp.ry = ry_first;
-      cp.rx = rx_first;
-    };
-    auto copy_part = [&](int cc, unsigned char* dst, Copier& cp, int nmax) __attribute__((always_inline)) {
-      const unsigned char* base = xs + static_cast<size_t>(cc * kCK) * 2;
-      for (int n = 0; n < nmax && cp.blk < nblk; ++n) {
-        const int gy = by0 + cp.ry, gx = bx0 + cp.rx;
-        if (cp.px < npx && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W) {
-          const uint32_t off = img_off + static_cast<uint32_t>(gy) * row_bytes + static_cast<uint32_t>(gx) * px_bytes;
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off),
-                                           (lds_void*)(dst + cp.blk * 1024), 16, 0, 0);
-        }
-        cp.blk += 4;
-        cp.px += 64;
-        cp.ry += step_r;
-        cp.rx += step_c;
-        if (cp.rx >= BW) { cp.rx -= BW; ++cp.ry; }
-      }
+    // The per-lane byte offsets of the wave's blocks are the same for every chunk (only
+    // the chunk's channel base moves), so they are computed once; each copy is then
+    // one direct global->LDS load per block.  kNoCopy marks a lane with no pixel to
+    // copy (past the box, or outside the image: those box pixels stay zero).
+    constexpr int MAXB = (Cfg::BOX_PX / 16 + 3) / 4;   // blocks per wave at most
+    constexpr uint32_t kNoCopy = 0xffffffffu;
+    uint32_t boff[MAXB];
+    {
+      int px = px_first, ry = ry_first, rx = rx_first;
+      static_for<0, MAXB>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        const int gy = by0 + ry, gx = bx0 + rx;
+        const bool ok = pw + 4 * j < nblk && px < npx && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W;
+        boff[j] = ok ? img_off + static_cast<uint32_t>(gy) * row_bytes + static_cast<uint32_t>(gx) * px_bytes
+                     : kNoCopy;
+        px += 64;
+        ry += step_r;
+        rx += step_c;
+        if (rx >= BW) { rx -= BW; ++ry; }
+      });
+    }
+    // blocks J0 .. J1-1 of the wave for chunk cc into `dst`
+    // (raw buffer loads into LDS: a scalar resource per chunk plus a 32-bit vector
+    // offset, so no per-block 64-bit address arithmetic)
+    auto copy_blocks = [&](int cc, unsigned char* dst, auto j0c, auto j1c) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(xs + cc * kCK * 2);
+      static_for<decltype(j0c)::value, decltype(j1c)::value>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        if (boff[j] != kNoCopy) buffer_to_lds16(rsrc, dst + (pw + 4 * j) * 1024, boff[j]);
+      });
     };
     auto copy_box = [&](int cc, unsigned char* dst) __attribute__((always_inline)) {
-      Copier cp;
-      copy_begin(cp);
-      copy_part(cc, dst, cp, nblk);
+      copy_blocks(cc, dst, std::integral_constant<int, 0>(), std::integral_constant<int, MAXB>());
     };
-    // this wave's blocks, and the share issued in each of the first four steps of a chunk
-    const int wave_blocks = nblk > pw ? (nblk - pw + 3) / 4 : 0;
-    const int part_blocks = (wave_blocks + 3) / 4;
+    // the share of the copy issued in step k < 4 of a chunk
+    auto copy_part4 = [&](int cc, unsigned char* dst, auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      copy_blocks(cc, dst, std::integral_constant<int, k * MAXB / 4>(),
+                  std::integral_constant<int, (k + 1) * MAXB / 4>());
+    };
 
     // Producer state of one step: the corner-table entries and the four corner vectors
     // of this thread's samples.  A sample with nothing in the box reads the zero bytes
@@ -622,14 +640,12 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         constexpr bool odd = decltype(parity)::value;
         const unsigned char* src = odd ? box1 : box0;
         unsigned char* dst = odd ? box0 : box1;
-        Copier cp;
-        copy_begin(cp);
         static_for<0, 9>([&](auto kc) __attribute__((always_inline)) {
           constexpr int k = decltype(kc)::value;
           PSet& cur = k % 3 == 0 ? X : (k % 3 == 1 ? Y : Z);
           PSet& ahead = (k + 2) % 3 == 0 ? X : ((k + 2) % 3 == 1 ? Y : Z);
           if constexpr (k < 4) {
-            if (cc + 1 < nCC) copy_part(cc + 1, dst, cp, part_blocks);
+            if (cc + 1 < nCC) copy_part4(cc + 1, dst, kc);
           }
           finish(cc * 9 + k, cc, cur);
           asm volatile("" ::: "memory");   // the column stores stay ahead of the reads below
@@ -653,14 +669,12 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         constexpr bool odd = decltype(parity)::value;
         const unsigned char* src = odd ? box1 : box0;
         unsigned char* dst = odd ? box0 : box1;
-        Copier cp;
-        copy_begin(cp);
         static_for<0, 9>([&](auto kc) __attribute__((always_inline)) {
           constexpr int k = decltype(kc)::value;
           PSet& cur = ((k + (odd ? 1 : 0)) & 1) == 0 ? X : Y;
           PSet& oth = ((k + (odd ? 1 : 0)) & 1) == 0 ? Y : X;
           if constexpr (k < 4) {
-            if (cc + 1 < nCC) copy_part(cc + 1, dst, cp, part_blocks);
+            if (cc + 1 < nCC) copy_part4(cc + 1, dst, kc);
           }
           finish(cc * 9 + k, cc, cur);
           asm volatile("" ::: "memory");

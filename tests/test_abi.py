@@ -44,6 +44,14 @@ def test_every_declared_symbol_is_exported(lib):
         assert getattr(lib, name) is not None
 
 
+def test_library_has_no_undefined_own_symbols():
+    # a kernel whose host stub was not emitted shows up as an undefined dcn:: symbol
+    out = subprocess.run(["nm", "-D", "--undefined-only", dcn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    own = [l for l in out.splitlines() if "_ZN3dcn" in l or " dcn_" in l]
+    assert not own, own
+
+
 def test_exports_are_plain_c(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", dcn.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
