@@ -95,8 +95,8 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
   for (int fm = 2; fm <= 4; fm += 2) {
     if (fm_only && fm != fm_only) continue;
     const int64_t MT = 64 * fm, m_tiles = (M + MT - 1) / MT;
-    for (int fn : {4, 5, 6, 8, 9}) {
-      if (fm == 4 && fn > 5) continue;
+    for (int fn : {4, 6, 8, 10}) {
+      if (fm == 4 && fn > 6) continue;
       const int NT = 16 * fn;
       const int box_px = dcn::box_capacity_px(fn);
       if (box_px < 64) continue;
@@ -118,7 +118,11 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
           const double mem = (double(MT) * Kr * 2 + est_box * Cp * 2) / 50;
           const double wg = std::max(compute, mem) + 4000;
           const double rounds = std::ceil(double(tiles) / 256);
-          const double cost = rounds * wg;
+          // margin of the capped box around the offset-free window: samples pushed
+          // past it take the slower global path, so thin margins are penalised
+          int64_t mg = 0;
+          while ((bh0 + 2 * (mg + 1)) * (bw0 + 2 * (mg + 1)) <= box_px) ++mg;
+          const double cost = rounds * wg * (1.0 + 4.0 / (1.0 + static_cast<double>(mg)));
           if (cost < best.cost) {
             best.fm = fm;
             best.fn = fn;

@@ -17,9 +17,11 @@
 //    corners lie outside the box are read from the channels-last copy in global
 //    memory instead;
 //  * four consumer waves multiply the previous step's column tile with MFMA
-//    16x16x32 bf16 against their rows of the repacked weight, which they stream
-//    from L2 straight into registers through a four-deep prefetch ring, and
-//    accumulate in fp32.
+//    32x32x16 bf16 (two per 32-channel step and 32x32 output block) against their
+//    rows of the repacked weight, which they stream from L2 straight into registers
+//    through a prefetch ring, and accumulate in fp32.  The 32x32 shape keeps the
+//    matrix core at full rate next to the producers' VALU work and takes fewer VALU
+//    issue cycles away from them than the 16x16 shape does.
 //
 // On each SIMD the producer's VALU work overlaps the consumer's matrix work.  The
 // two box buffers are separate LDS arrays (and the producer loop is instantiated
@@ -44,7 +46,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kThreads = 512;    // 4 consumer + 4 producer waves
@@ -175,6 +177,8 @@ template <int FM, int FN, int KKT>
 __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   using Cfg = BoxCfg<FN>;
   const FusedArgs& a = ba.f;
+  static_assert(FM % 2 == 0 && FN % 2 == 0, "whole 32x32 MFMA blocks per wave");
+  constexpr int TM = FM / 2, TN = FN / 2;   // 32x32 output blocks per consumer wave
   constexpr int WM = 16 * FM;         // rows per consumer wave
   constexpr int MT = 4 * WM;          // rows per workgroup
   constexpr int NT = Cfg::NT;         // pixel slots per workgroup
@@ -192,7 +196,10 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const bool consumer = wv < 4;
-  const int lrow = lane & 15, lgrp = lane >> 4;
+  // MFMA 32x32x16 operand lanes: row (A) or column (B) lane & 31, and a 16-byte
+  // channel group: lane half lh holds channels 16*lh + 8*h .. +7 of k-half h, so a
+  // lane's two halves are one contiguous 32-byte run
+  const int l32 = lane & 31, lh = lane >> 5;
   const int KK = a.KK, Cp = a.Cp, K = a.K;
   const int T = a.m_tiles * ba.tiles_per_img * a.B;
   const int t = xcd_tile(blockIdx.x, T);
@@ -210,21 +217,24 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   const unsigned char* wp = reinterpret_cast<const unsigned char*>(a.wp);
 
   // ---- consumer state: weight fragments
-  // The repacked weight is step-major, [step][Mp][32 channels], so the 16 rows x 64
-  // bytes one fragment load reads are one contiguous kilobyte.  Per-lane byte offsets
-  // of this wave's rows (the host keeps the repacked weight under 4 GiB) plus a
-  // wave-uniform base per step: one scalar-base + vector-offset load per fragment.
-  struct AFrag { uint4 v[FM]; };
+  // The repacked weight is step-major, [step][Mp][32 channels], so the 32 rows x 64
+  // bytes of one 32-row block are one contiguous 2 KB.  Per-lane byte offsets of this
+  // wave's rows (the host keeps the repacked weight under 4 GiB) plus a wave-uniform
+  // base per step: scalar-base + vector-offset loads, the second half at +16 bytes.
+  struct AFrag { uint4 v[TM][2]; };
   const uint32_t step_bytes = static_cast<uint32_t>(a.m_tiles * MT) * 64u;
-  uint32_t aoff[FM];
+  uint32_t aoff[TM];
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-    aoff[fm] = static_cast<uint32_t>(m0 + wv * WM + fm * 16 + lrow) * 64u + static_cast<uint32_t>(lgrp * 16);
+  for (int tm = 0; tm < TM; ++tm)
+    aoff[tm] = static_cast<uint32_t>(m0 + wv * WM + tm * 32 + l32) * 64u + static_cast<uint32_t>(lh * 32);
   auto load_a = [&](int s) __attribute__((always_inline)) -> AFrag {
     AFrag r;
     const unsigned char* base = wp + static_cast<size_t>(static_cast<uint32_t>(s) * step_bytes);
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) r.v[fm] = *reinterpret_cast<const uint4*>(base + aoff[fm]);
+    for (int tm = 0; tm < TM; ++tm) {
+      r.v[tm][0] = *reinterpret_cast<const uint4*>(base + aoff[tm]);
+      r.v[tm][1] = *reinterpret_cast<const uint4*>(base + aoff[tm] + 16);
+    }
     return r;
   };
   // Weight fragments in two sets of G named slots: chunks G*g .. G*g+G-1 live in set
@@ -389,30 +399,37 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 
   if (consumer) {
     // ================= consumers: MFMA on the previous step's column tile =================
-    floatx4 acc[FM][FN];
+    floatx16 acc[TM][TN];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
 
     // B fragments of one column tile (read one step before they are multiplied)
-    struct BFrag { bf16x8 v[FN]; };
+    struct BFrag { bf16x8 v[TN][2]; };
     auto read_b = [&](int c) __attribute__((always_inline)) -> BFrag {
       BFrag r;
-      const unsigned char* csrc = col + (c % kColBufs) * NT * kCOLB;
+      const unsigned char* csrc = col + (c % kColBufs) * NT * kCOLB + l32 * kCOLB + lh * 32;
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        r.v[fn] = *reinterpret_cast<const bf16x8*>(csrc + (fn * 16 + lrow) * kCOLB + lgrp * 16);
+      for (int tn = 0; tn < TN; ++tn) {
+        r.v[tn][0] = *reinterpret_cast<const bf16x8*>(csrc + tn * 32 * kCOLB);
+        r.v[tn][1] = *reinterpret_cast<const bf16x8*>(csrc + tn * 32 * kCOLB + 16);
+      }
       return r;
     };
+    // k-half outer, so two MFMAs into one accumulator are TM*TN instructions apart
     auto mma = [&](const AFrag& af, const BFrag& bf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, af.v[fm]);
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bf.v[fn], acc[fm][fn], 0, 0, 0);
-      }
+        for (int tm = 0; tm < TM; ++tm) {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, af.v[tm][h]);
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bf.v[tn][h], acc[tm][tn], 0, 0, 0);
+        }
     };
     // Chunk c is multiplied during step c+2, between barriers c+1 and c+2: read
     // chunk c+1's columns (produced in step c+1), multiply chunk c (columns read
@@ -477,23 +494,24 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // buffer.  The producers read no box after barrier S-1, and the consumers pass
     // that barrier only after every producer's reads are complete.  The bias values
     // are loaded first; rows past Cout read the last bias value and are not stored.
-    float bv[FM][4] = {};
+    // Accumulator element r of a 32x32 block: row 8*(r/4) + 4*lh + r%4, column l32.
+    float bv[TM][16] = {};
     if (a.bias) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          bv[fm][i] = ld_bf16(a.bias, min(m0 + wv * WM + fm * 16 + lgrp * 4 + i, a.Cout - 1));
+        for (int r = 0; r < 16; ++r)
+          bv[tm][r] = ld_bf16(a.bias, min(m0 + wv * WM + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3), a.Cout - 1));
     }
     uint16_t* stage = reinterpret_cast<uint16_t*>(box0);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
+    for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          stage[(wv * WM + fm * 16 + lgrp * 4 + i) * (NT + 2) + fn * 16 + lrow] =
-              static_cast<uint16_t>(pk_bf16(acc[fm][fn][i] + bv[fm][i], 0.f) & 0xffffu);
+        for (int r = 0; r < 16; ++r)
+          stage[(wv * WM + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)) * (NT + 2) + tn * 32 + l32] =
+              static_cast<uint16_t>(pk_bf16(acc[tm][tn][r] + bv[tm][r], 0.f) & 0xffffu);
   } else {
     // ================= producers: box copies and column tiles =================
     const int pw = wv - 4;                  // producer wave 0..3
@@ -793,8 +811,8 @@ static hipError_t launch_box_t(const BoxArgs& ba, hipStream_t stream) {
 hipError_t launch_box(int fm, int fn, const BoxArgs& ba, hipStream_t stream) {
 #define DCN_BOX_CASE(FMv, FNv) \
   if (fm == FMv && fn == FNv) return launch_box_t<FMv, FNv>(ba, stream);
-  DCN_BOX_CASE(2, 4) DCN_BOX_CASE(2, 5) DCN_BOX_CASE(2, 6) DCN_BOX_CASE(2, 8) DCN_BOX_CASE(2, 9)
-  DCN_BOX_CASE(4, 4) DCN_BOX_CASE(4, 5)
+  DCN_BOX_CASE(2, 4) DCN_BOX_CASE(2, 6) DCN_BOX_CASE(2, 8) DCN_BOX_CASE(2, 10)
+  DCN_BOX_CASE(4, 4) DCN_BOX_CASE(4, 6)
 #undef DCN_BOX_CASE
   return hipErrorInvalidValue;
 }
@@ -802,10 +820,9 @@ hipError_t launch_box(int fm, int fn, const BoxArgs& ba, hipStream_t stream) {
 int box_capacity_px(int fn) {
   switch (fn) {
     case 4: return BoxCfg<4>::BOX_PX;
-    case 5: return BoxCfg<5>::BOX_PX;
     case 6: return BoxCfg<6>::BOX_PX;
     case 8: return BoxCfg<8>::BOX_PX;
-    case 9: return BoxCfg<9>::BOX_PX;
+    case 10: return BoxCfg<10>::BOX_PX;
     default: return 0;
   }
 }

@@ -69,7 +69,7 @@ const VariantInfo& variant_info(int v);
 hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream);
 hipError_t launch_fused(int variant, const FusedArgs& a, hipStream_t stream);
 
-// box kernel: fm = MT/64 (2: fn 4, 5, 6, 8, 9; 4: fn 4, 5), fn = NT/16.
+// box kernel: fm = MT/64 (2: fn 4, 6, 8, 10; 4: fn 4, 6), fn = NT/16.
 // box_capacity_px: pixels one LDS box buffer holds for a given fn (0 if not built).
 hipError_t launch_box(int fm, int fn, const BoxArgs& a, hipStream_t stream);
 int box_capacity_px(int fn);
