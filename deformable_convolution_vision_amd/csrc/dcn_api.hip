@@ -101,7 +101,7 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
       const int box_px = dcn::box_capacity_px(fn);
       if (box_px < 64) continue;
       for (int TH = 1; TH <= 16; ++TH) {
-        for (int dw = 0; dw < (want_fn ? NT : 2); ++dw) {
+        for (int dw = 0; dw < (want_fn ? NT : 3); ++dw) {
           const int TW = NT / TH - dw;
           if (TW < 1 || (TH * TW + 15) / 16 != fn) continue;
           if (want_fn && (fn != want_fn || TH != want_th || TW != want_tw)) continue;
@@ -122,7 +122,10 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
           // past it take the slower global path, so thin margins are penalised
           int64_t mg = 0;
           while ((bh0 + 2 * (mg + 1)) * (bw0 + 2 * (mg + 1)) <= box_px) ++mg;
-          const double cost = rounds * wg * (1.0 + 4.0 / (1.0 + static_cast<double>(mg)));
+          // tiles about twice as wide as tall measured fastest (rows of the box and of
+          // the NCHW output are longer; the margin still grows in both directions)
+          const double aspect = std::fabs(std::log2(double(TW) / (2.0 * TH)));
+          const double cost = rounds * wg * (1.0 + 4.0 / (1.0 + static_cast<double>(mg))) * (1.0 + 0.3 * aspect);
           if (cost < best.cost) {
             best.fm = fm;
             best.fn = fn;

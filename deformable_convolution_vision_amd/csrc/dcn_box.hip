@@ -64,16 +64,15 @@ struct CEnt {
 
 constexpr int kColBufs = 3;      // column-tile ring: produced at step s, read at s+1, multiplied at s+2
 constexpr int kZeroB = 128;      // zero bytes after each box buffer: the source of samples that read nothing
-constexpr int kFbB = 4 * 4 * 1024;  // global-path staging: 4 producer waves x 4 corners x 64 lanes x 16 B
 
 template <int FN>
 struct BoxCfg {
   static constexpr int NT = 16 * FN;
   static constexpr int COL_BYTES = kColBufs * NT * kCOLB;
   static constexpr int CTAB_BYTES = kBoxMaxKK * NT * 16;
-  // what is left of the LDS, split into two box buffers, in 16-pixel blocks
-  static constexpr int BOX_PX =
-      ((kLdsBudget - COL_BYTES - CTAB_BYTES - kFbB - 2 * kZeroB - 64) / (2 * kPXB)) / 16 * 16;
+  // what is left of the LDS, split into two box buffers, in whole 64-pixel groups
+  // (each of the four producer waves copies 16-pixel blocks, every block of a group)
+  static constexpr int BOX_PX = ((kLdsBudget - COL_BYTES - CTAB_BYTES - 2 * kZeroB - 64) / (2 * kPXB)) / 64 * 64;
 };
 
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
@@ -115,6 +114,12 @@ __device__ __forceinline__ uint4 interp8(uint4 q00, uint4 q01, uint4 q10, uint4 
   return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
+// component-wise select (a select of whole structs can become a select of their
+// addresses, which keeps them out of registers)
+__device__ __forceinline__ uint4 sel4(bool c, uint4 a, uint4 b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 // f(integral_constant<int, I>) for I = B .. E-1, each call inlined with I known at compile time
 template <int I, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -135,9 +140,17 @@ __device__ __forceinline__ float ld_bf16(const void* p, int idx) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// Raw buffer resource over `p` with the largest range (4 GiB - 1 bytes).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const unsigned char* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(p), 0, -1, 0x00020000);
+// Raw buffer resource over the `bytes` bytes at `p`: loads at offsets past the end
+// return zeros (and move no data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const unsigned char* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+// a byte offset past the end of every buffer here (the host keeps them under 4 GiB - 64)
+constexpr uint32_t kOOB = 0xfffffff0u;
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 // Direct buffer->LDS load: 16 bytes per lane from byte offset `voff`, lane l's bytes
 // at dst + 16*l.
@@ -190,7 +203,6 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   __shared__ __attribute__((aligned(16))) CEnt ctab[kBoxMaxKK * NT];
   __shared__ __attribute__((aligned(16))) unsigned char box0[BOXB + kZeroB];
   __shared__ __attribute__((aligned(16))) unsigned char box1[BOXB + kZeroB];
-  __shared__ __attribute__((aligned(16))) unsigned char fbuf[kFbB];
   __shared__ int red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -530,10 +542,13 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const uint32_t row_bytes = static_cast<uint32_t>(a.W * Cp) * 2u, px_bytes = static_cast<uint32_t>(Cp) * 2u;
     // The per-lane byte offsets of the wave's blocks are the same for every chunk (only
     // the chunk's channel base moves), so they are computed once; each copy is then
-    // one direct global->LDS load per block.  kNoCopy marks a lane with no pixel to
-    // copy (past the box, or outside the image: those box pixels stay zero).
-    constexpr int MAXB = (Cfg::BOX_PX / 16 + 3) / 4;   // blocks per wave at most
-    constexpr uint32_t kNoCopy = 0xffffffffu;
+    // one direct global->LDS load per block.  A lane with no pixel to copy (past the
+    // box, or outside the image: those box pixels are zero) loads from past the end
+    // of the buffer, which moves no data, so every block is issued unconditionally
+    // and the number of vector-memory operations of each step is a compile-time
+    // constant (exact wait counts for the prefetched global-path corners below).
+    constexpr int MAXB = Cfg::BOX_PX / 64;   // blocks per wave; 4 * MAXB blocks fill the buffer
+    const uint32_t xs_bytes = static_cast<uint32_t>(a.B * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u;
     uint32_t boff[MAXB];
     {
       int px = px_first, ry = ry_first, rx = rx_first;
@@ -542,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         const int gy = by0 + ry, gx = bx0 + rx;
         const bool ok = pw + 4 * j < nblk && px < npx && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W;
         boff[j] = ok ? img_off + static_cast<uint32_t>(gy) * row_bytes + static_cast<uint32_t>(gx) * px_bytes
-                     : kNoCopy;
+                     : kOOB;
         px += 64;
         ry += step_r;
         rx += step_c;
@@ -552,11 +567,16 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // blocks J0 .. J1-1 of the wave for chunk cc into `dst`
     // (raw buffer loads into LDS: a scalar resource per chunk plus a 32-bit vector
     // offset, so no per-block 64-bit address arithmetic)
+    // chunk cc's view of the staged copy; past the last chunk an empty range, so the
+    // steady-state schedule can issue its copies and loads there too (they move no data)
+    auto chunk_rsrc = [&](int cc) __attribute__((always_inline)) {
+      return make_rsrc(xs + cc * kCK * 2, cc < nCC ? xs_bytes - static_cast<uint32_t>(cc * kCK * 2) : 0u);
+    };
     auto copy_blocks = [&](int cc, unsigned char* dst, auto j0c, auto j1c) __attribute__((always_inline)) {
-      const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(xs + cc * kCK * 2);
+      const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(cc);
       static_for<decltype(j0c)::value, decltype(j1c)::value>([&](auto jc) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
-        if (boff[j] != kNoCopy) buffer_to_lds16(rsrc, dst + (pw + 4 * j) * 1024, boff[j]);
+        buffer_to_lds16(rsrc, dst + (pw + 4 * j) * 1024, boff[j]);
       });
     };
     auto copy_box = [&](int cc, unsigned char* dst) __attribute__((always_inline)) {
@@ -573,6 +593,14 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // of this thread's samples.  A sample with nothing in the box reads the zero bytes
     // after the buffer with a row stride of 0.
     struct PSet { CEnt ce[GU]; uint4 q[GU][4]; };
+    // Samples whose corners lie outside the box (ce.off == -1) take their corners from
+    // the channels-last copy in global memory.  When a wave has any such sample in a
+    // step (gfl, wave-uniform), its lanes load the four corner vectors straight into
+    // registers (gq) one step ahead, right after the previous step's interpolation,
+    // so the loads are in flight across a barrier; lanes without such a sample, and
+    // corners outside the image, load zeros.  One step's vectors are live at a time.
+    uint4 gq[GU][4];
+    bool gfl[GU];
     auto read_ce = [&](int k, PSet& f) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < GU; ++g)
@@ -583,8 +611,9 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
         if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
-          const bool in_box = f.ce[g].off >= 0;
-          const unsigned char* q = src + (in_box ? f.ce[g].off : BOXB) + (ptid & 3) * 16;
+          const CEnt& ce = f.ce[g];
+          const bool in_box = ce.off >= 0;
+          const unsigned char* q = src + (in_box ? ce.off : BOXB) + (ptid & 3) * 16;
           const int rs = in_box ? BW * kPXB : 0;
           f.q[g][0] = *reinterpret_cast<const uint4*>(q);
           f.q[g][1] = *reinterpret_cast<const uint4*>(q + kPXB);
@@ -593,9 +622,30 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         }
       }
     };
-    // interpolate (global path for samples outside the box) and store into column buffer s % 3
-    unsigned char* fb = fbuf + pw * 4096;
-    auto finish = [&](int s, int cc, const PSet& f) __attribute__((always_inline)) {
+    // the global-path corner vectors of the step whose table entries are in f (chunk cc)
+    auto load_g = [&](int cc, const PSet& f) __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < GU; ++g) {
+        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
+          const CEnt& ce = f.ce[g];
+          gfl[g] = __ballot(ce.off == -1) != 0;
+          if (gfl[g]) {
+            const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(cc);
+            const int y0 = (ce.yx >> 16) - 1, x0 = (ce.yx & 0xffff) - 1;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int yy = y0 + (qq >> 1), xx = x0 + (qq & 1);
+              const bool ok = (ce.off == -1) & (yy >= 0) & (yy < a.H) & (xx >= 0) & (xx < a.W);
+              const uint32_t voff =
+                  ok ? img_off + static_cast<uint32_t>(yy) * row_bytes + static_cast<uint32_t>(xx) * px_bytes : kOOB;
+              gq[g][qq] = buffer_load16(rsrc, voff);
+            }
+          }
+        }
+      }
+    };
+    // interpolate and store into column buffer s % 3
+    auto finish = [&](int s, const PSet& f) __attribute__((always_inline)) {
       unsigned char* cdst = col + (s % kColBufs) * NT * kCOLB;
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
@@ -603,34 +653,15 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
           const int u = ptid + g * 256;
           const int p = u >> 2, sub = u & 3;
           const CEnt& ce = f.ce[g];
-          uint4 r = interp8(f.q[g][0], f.q[g][1], f.q[g][2], f.q[g][3], ce.w01, ce.w23);
-          // Samples outside the box (a uniform branch, rarely taken): the corners are
-          // copied from the channels-last input into this wave's staging slots with
-          // direct global->LDS loads (every lane loads; lanes without such a sample
-          // read a valid dummy vector), then read back like box data.
-          if (__ballot(ce.off == -1) != 0) {
-            const int y0 = (ce.yx >> 16) - 1, x0 = (ce.yx & 0xffff) - 1;
-            const size_t rowb = static_cast<size_t>(b * a.H) * a.W;
-            const int ch = cc * kCK + sub * 8;
-            bool ok[4];
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              const int yy = y0 + (qq >> 1), xx = x0 + (qq & 1);
-              ok[qq] = (ce.off == -1) & (yy >= 0) & (yy < a.H) & (xx >= 0) & (xx < a.W);
-              const size_t e = ok[qq] ? ((rowb + static_cast<size_t>(yy) * a.W + xx) * Cp + ch) * 2 : 0;
-              __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xs + e), (lds_void*)(fb + qq * 1024),
-                                               16, 0, 0);
-            }
-            __builtin_amdgcn_s_waitcnt(0);
-            uint4 c4[4];
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              c4[qq] = *reinterpret_cast<const uint4*>(fb + qq * 1024 + lane * 16);
-              if (!ok[qq]) c4[qq] = make_uint4(0u, 0u, 0u, 0u);
-            }
-            const uint4 rg = interp8(c4[0], c4[1], c4[2], c4[3], ce.w01, ce.w23);
-            if (ce.off == -1) r = rg;
+          uint4 c0 = f.q[g][0], c1 = f.q[g][1], c2 = f.q[g][2], c3 = f.q[g][3];
+          if (gfl[g]) {   // wave-uniform: some lane's sample takes the global-path corners
+            const bool o = ce.off == -1;
+            c0 = sel4(o, gq[g][0], c0);
+            c1 = sel4(o, gq[g][1], c1);
+            c2 = sel4(o, gq[g][2], c2);
+            c3 = sel4(o, gq[g][3], c3);
           }
+          const uint4 r = interp8(c0, c1, c2, c3, ce.w01, ce.w23);
           *reinterpret_cast<uint4*>(cdst + p * kCOLB + sub * 16) = r;
         }
       }
@@ -662,10 +693,10 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
           constexpr int k = decltype(kc)::value;
           PSet& cur = k % 3 == 0 ? X : (k % 3 == 1 ? Y : Z);
           PSet& ahead = (k + 2) % 3 == 0 ? X : ((k + 2) % 3 == 1 ? Y : Z);
-          if constexpr (k < 4) {
-            if (cc + 1 < nCC) copy_part4(cc + 1, dst, kc);
-          }
-          finish(cc * 9 + k, cc, cur);
+          if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
+          PSet& next = (k + 1) % 3 == 0 ? X : ((k + 1) % 3 == 1 ? Y : Z);
+          finish(cc * 9 + k, cur);
+          load_g(k < 8 ? cc : cc + 1, next);
           asm volatile("" ::: "memory");   // the column stores stay ahead of the reads below
           read_ce((k + 3) % 9, cur);
           if constexpr (k + 2 < 9) {
@@ -675,9 +706,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
             if (cc + 1 < nCC) read_q(dst, ahead);
             else read_q(src, ahead);
           }
-          if constexpr (k == 6) {
-            if (cc + 1 < nCC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          }
+          if constexpr (k == 6) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           lds_barrier_keep<kKeep>();
         });
       };
@@ -691,17 +720,19 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
           constexpr int k = decltype(kc)::value;
           PSet& cur = ((k + (odd ? 1 : 0)) & 1) == 0 ? X : Y;
           PSet& oth = ((k + (odd ? 1 : 0)) & 1) == 0 ? Y : X;
-          if constexpr (k < 4) {
-            if (cc + 1 < nCC) copy_part4(cc + 1, dst, kc);
-          }
-          finish(cc * 9 + k, cc, cur);
+          if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
+          finish(cc * 9 + k, cur);
+          if constexpr (k < 8) load_g(cc, oth);
           asm volatile("" ::: "memory");
           if constexpr (k + 1 < 9) read_q(src, oth);
           read_ce((k + 2) % 9, cur);
           if constexpr (k == 8) {
-            if (cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_waitcnt(0);
             lds_barrier_dma();
-            if (cc + 1 < nCC) read_q(dst, oth);
+            if (cc + 1 < nCC) {
+              read_q(dst, oth);
+              load_g(cc + 1, oth);
+            }
           } else {
             lds_barrier_keep<kKeep>();
           }
@@ -713,6 +744,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         read_ce(2, Z);
         read_q(box0, X);
         read_q(box0, Y);
+        load_g(0, X);
         for (int cc = 0; cc < nCC; cc += 2) {
           chunk9(cc, std::false_type());
           if (cc + 1 < nCC) chunk9(cc + 1, std::true_type());
@@ -721,6 +753,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         read_ce(0, X);
         read_ce(1, Y);
         read_q(box0, X);
+        load_g(0, X);
         for (int cc = 0; cc < nCC; cc += 2) {
           chunk9_two(cc, std::false_type());
           if (cc + 1 < nCC) chunk9_two(cc + 1, std::true_type());
@@ -737,7 +770,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         for (int k = 0; k < KK; ++k) {
           read_ce(k, X);
           read_q(src, X);
-          finish(cc * KK + k, cc, X);
+          load_g(cc, X);
+          finish(cc * KK + k, X);
           if (k == KK - 1 && cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
           lds_barrier_dma();
         }
