@@ -95,19 +95,29 @@ __device__ __forceinline__ int xcd_tile(int g, int T) {
 // Rows >= Cout and channels >= Cin are written as 0.
 template <typename T>
 __device__ __forceinline__ void pack_weight(const StageArgs& a, int wg, int nwg) {
-  const T* w = reinterpret_cast<const T*>(a.w);
-  T* wp = reinterpret_cast<T*>(a.wp);
+  // the two do not overlap (the workspace is the caller's scratch), so every load of
+  // a row can be issued before its stores
+  const T* __restrict__ w = reinterpret_cast<const T*>(a.w);
+  T* __restrict__ wp = reinterpret_cast<T*>(a.wp);
   const int total = a.Mp * a.Cp;
   for (int e = wg * kThreads + static_cast<int>(threadIdx.x); e < total; e += nwg * kThreads) {
     const int o = e / a.Cp, c = e - (e / a.Cp) * a.Cp;
     const bool live = o < a.Cout && c < a.Cin;
     const T* src = w + (static_cast<size_t>(o) * a.Cin + c) * a.KK;
-    for (int k = 0; k < a.KK; ++k) {
-      const T v = live ? src[k] : T(0);
-      const size_t dst = a.wlayout == 0
-                             ? (static_cast<size_t>(o) * a.KK + k) * a.Cp + c
-                             : ((static_cast<size_t>(c >> 5) * a.KK + k) * a.Mp + o) * 32 + (c & 31);
-      wp[dst] = v;
+    // nine kernel points at a time: all loads in flight before the stores
+    for (int k0 = 0; k0 < a.KK; k0 += 9) {
+      T v[9];
+#pragma unroll
+      for (int j = 0; j < 9; ++j) v[j] = (live && k0 + j < a.KK) ? src[k0 + j] : T(0);
+#pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        const int k = k0 + j;
+        if (k >= a.KK) break;
+        const size_t dst = a.wlayout == 0
+                               ? (static_cast<size_t>(o) * a.KK + k) * a.Cp + c
+                               : ((static_cast<size_t>(c >> 5) * a.KK + k) * a.Mp + o) * 32 + (c & 31);
+        wp[dst] = v[j];
+      }
     }
   }
 }

@@ -62,6 +62,9 @@ EDGE = [
     ("huge_offsets", dict(B=1, Cin=64, H=48, W=64, Cout=128, K=3, s=1, p=1, d=1, offset="uniform:30")),
     ("k5_box", dict(B=1, Cin=48, H=30, W=26, Cout=96, K=5, s=2, p=2, d=1, offset="normal:2")),
     ("k1_box", dict(B=2, Cin=64, H=17, W=19, Cout=130, K=1, s=1, p=0, d=1)),
+    # H*W a multiple of 8: the register-transpose staging; 70 channels pad to 96, so
+    # the second 64-channel block is half padding
+    ("stage_cp96", dict(B=3, Cin=70, H=8, W=12, Cout=40, K=3, s=1, p=1, d=1, offset="normal:1.5")),
 ]
 
 
