@@ -203,7 +203,6 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   __shared__ __attribute__((aligned(16))) CEnt ctab[kBoxMaxKK * NT];
   __shared__ __attribute__((aligned(16))) unsigned char box0[BOXB + kZeroB];
   __shared__ __attribute__((aligned(16))) unsigned char box1[BOXB + kZeroB];
-  __shared__ int red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -264,36 +263,147 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       x3 = load_a(min(c0 + 3, S - 1));
     }
   };
+
+  // The prologue has one barrier, and it orders LDS traffic only (lds_barrier): it
+  // does not wait for the consumers' weight prefetch.
+
+  // ---- box geometry (uniform, from the tile alone): the window the tile's samples
+  // use with zero offsets, widened evenly by the largest margin the LDS budget allows,
+  // within [-1, H] x [-1, W] (the host checks the offset-free window fits).  Samples
+  // whose corners leave it take the global path.  Known before any offset arrives, so
+  // the first chunk's copy overlaps the offset loads.
+  int by0, bx0, BH, BW;
+  {
+    const int bh0 = (ba.TH - 1) * a.stride + (K - 1) * a.dil + 2;
+    const int bw0 = (ba.TW - 1) * a.stride + (K - 1) * a.dil + 2;
+    int mg = 0;
+    while ((bh0 + 2 * (mg + 1)) * (bw0 + 2 * (mg + 1)) <= Cfg::BOX_PX) ++mg;
+    by0 = max(oy0 * a.stride - a.pad - mg, -1);
+    bx0 = max(ox0 * a.stride - a.pad - mg, -1);
+    BH = max(min(bh0 + 2 * mg, a.H + 1 - by0), 1);
+    BW = max(min(bw0 + 2 * mg, a.W + 1 - bx0), 1);
+  }
+  const int npx = BH * BW;
+  if (tid < kZeroB / 16) {
+    *reinterpret_cast<uint4*>(box0 + BOXB + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(box1 + BOXB + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // ---- the consumer waves build the corner table while the producer waves copy the
+  // first box chunk (a wave waiting for its offsets would otherwise also wait for its
+  // older box loads).  The consumers issue the offset and mask loads of every (tap,
+  // pixel) entry, then the first 2G weight steps; the table math waits only for the
+  // offsets, the weights stay in flight.
+  const int ntile = ba.TH * ba.TW;
+  constexpr int kPE = (kBoxMaxKK * NT + 255) / 256;
+  // raw bf16 bits; every address first, then every load
+  uint32_t ldy[kPE], ldx[kPE], lm[kPE];
   if (consumer) {
+    int ob[kPE], mb[kPE];
+#pragma unroll
+    for (int j = 0; j < kPE; ++j) {
+      const int e = tid + j * 256;
+      const int k = e / NT, p = e - (e / NT) * NT;
+      const int py = p / ba.TW, px = p - (p / ba.TW) * ba.TW;
+      const int oy = oy0 + py, ox = ox0 + px;
+      const bool ok = e < KK * NT && p < ntile && oy < a.Ho && ox < a.Wo;
+      const int rem = ok ? oy * a.Wo + ox : 0;
+      const int kk = ok ? k : 0;
+      ob[j] = (b * 2 * KK + 2 * kk) * a.HoWo + rem;
+      // always a load (from the offsets when there is no mask, ignored below), so no
+      // branch joins on a value still in flight
+      mb[j] = a.mask ? (b * KK + kk) * a.HoWo + rem : ob[j];
+    }
+    const uint16_t* offs = reinterpret_cast<const uint16_t*>(a.offset);
+    const uint16_t* msk = reinterpret_cast<const uint16_t*>(a.mask ? a.mask : a.offset);
+#pragma unroll
+    for (int j = 0; j < kPE; ++j) {
+      ldy[j] = offs[ob[j]];
+      ldx[j] = offs[ob[j] + a.HoWo];
+      lm[j] = msk[mb[j]];
+    }
     load_group(0, p0, p1, p2, p3);
     load_group(G, q0, q1, q2, q3);
   }
 
-  // ---- prologue pass 1 (all waves): sampling positions and weights; extent of the upper corners
-  if (tid < 4) red[tid] = (tid & 1) ? -0x40000000 : 0x40000000;   // min y, max y, min x, max x
-  __syncthreads();
-  int lminy = 0x40000000, lmaxy = -0x40000000, lminx = 0x40000000, lmaxx = -0x40000000;
-  const int ntile = ba.TH * ba.TW;
-  // all offset and mask loads of this thread first (independent, so they overlap), then the math
-  constexpr int kPE = (kBoxMaxKK * NT + kThreads - 1) / kThreads;
-  float ldy[kPE], ldx[kPE], lm[kPE];
-#pragma unroll
-  for (int j = 0; j < kPE; ++j) {
-    const int e = tid + j * kThreads;
-    const int k = e / NT, p = e - (e / NT) * NT;
-    const int py = p / ba.TW, px = p - (p / ba.TW) * ba.TW;
-    const int oy = oy0 + py, ox = ox0 + px;
-    const bool ok = e < KK * NT && p < ntile && oy < a.Ho && ox < a.Wo;
-    const int rem = ok ? oy * a.Wo + ox : 0;
-    const int kk = ok ? k : 0;
-    const int ob = (b * 2 * KK + 2 * kk) * a.HoWo + rem;
-    ldy[j] = ld_bf16(a.offset, ob);
-    ldx[j] = ld_bf16(a.offset, ob + a.HoWo);
-    lm[j] = a.mask ? ld_bf16(a.mask, (b * KK + kk) * a.HoWo + rem) : 1.f;
+  // ---- the producers' box-copy plan (with the box pixels outside the image zeroed),
+  // then chunk 0 of the box
+  const int pw = wv - 4;                    // producer wave 0..3 (unused by consumers)
+  // Box copy, one wave instruction per 16 pixels: lane -> pixel blk*16 + lane/4,
+  // 16-byte quarter lane%4.  Pixels advance by 64 between a wave's blocks; the
+  // row/column step is precomputed so no division is needed per block.
+  const int nblk = (npx + 15) >> 4;
+  const int step_r = 64 / BW, step_c = 64 - (64 / BW) * BW;
+  const int px_first = pw * 16 + (lane >> 2);
+  const int ry_first = px_first / BW, rx_first = px_first - (px_first / BW) * BW;
+  // per-lane byte offsets (32-bit: the host keeps the staged copy under 4 GiB)
+  // relative to a wave-uniform base for the chunk
+  const uint32_t img_off = static_cast<uint32_t>(b * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u +
+                           static_cast<uint32_t>((lane & 3) * 16);
+  const uint32_t row_bytes = static_cast<uint32_t>(a.W * Cp) * 2u, px_bytes = static_cast<uint32_t>(Cp) * 2u;
+  // The per-lane byte offsets of the wave's blocks are the same for every chunk (only
+  // the chunk's channel base moves), so they are computed once; each copy is then
+  // one direct global->LDS load per block.  A lane with no pixel to copy (past the
+  // box, or outside the image: those box pixels are zero) loads from past the end
+  // of the buffer, which moves no data, so every block is issued unconditionally
+  // and the number of vector-memory operations of each step is a compile-time
+  // constant (exact wait counts for the prefetched global-path corners below).
+  constexpr int MAXB = Cfg::BOX_PX / 64;   // blocks per wave; 4 * MAXB blocks fill the buffer
+  const uint32_t xs_bytes = static_cast<uint32_t>(a.B * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u;
+  uint32_t boff[MAXB];
+  if (!consumer) {
+    int px = px_first, ry = ry_first, rx = rx_first;
+    static_for<0, MAXB>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      const int gy = by0 + ry, gx = bx0 + rx;
+      const bool inside = gy >= 0 && gy < a.H && gx >= 0 && gx < a.W;
+      const bool ok = pw + 4 * j < nblk && px < npx && inside;
+      boff[j] = ok ? img_off + static_cast<uint32_t>(gy) * row_bytes + static_cast<uint32_t>(gx) * px_bytes
+                   : kOOB;
+      // box pixels outside the image stay zero in both buffers
+      if (pw + 4 * j < nblk && px < npx && !inside) {
+        *reinterpret_cast<uint4*>(box0 + px * kPXB + (lane & 3) * 16) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(box1 + px * kPXB + (lane & 3) * 16) = make_uint4(0u, 0u, 0u, 0u);
+      }
+      px += 64;
+      ry += step_r;
+      rx += step_c;
+      if (rx >= BW) { rx -= BW; ++ry; }
+    });
   }
+  // chunk cc's view of the staged copy; past the last chunk an empty range, so the
+  // steady-state schedule can issue its copies and loads there too (they move no data)
+  auto chunk_rsrc = [&](int cc) __attribute__((always_inline)) {
+    return make_rsrc(xs + cc * kCK * 2, cc < nCC ? xs_bytes - static_cast<uint32_t>(cc * kCK * 2) : 0u);
+  };
+  // blocks J0 .. J1-1 of the wave for chunk cc into `dst` (raw buffer loads into LDS:
+  // a scalar resource per chunk plus a 32-bit vector offset, so no per-block 64-bit
+  // address arithmetic)
+  auto copy_blocks = [&](int cc, unsigned char* dst, auto j0c, auto j1c) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(cc);
+    static_for<decltype(j0c)::value, decltype(j1c)::value>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      buffer_to_lds16(rsrc, dst + (pw + 4 * j) * 1024, boff[j]);
+    });
+  };
+  auto copy_box = [&](int cc, unsigned char* dst) __attribute__((always_inline)) {
+    copy_blocks(cc, dst, std::integral_constant<int, 0>(), std::integral_constant<int, MAXB>());
+  };
+  // the share of the copy issued in step k < 4 of a chunk
+  auto copy_part4 = [&](int cc, unsigned char* dst, auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    copy_blocks(cc, dst, std::integral_constant<int, k * MAXB / 4>(),
+                std::integral_constant<int, (k + 1) * MAXB / 4>());
+  };
+  // chunk 0: direct buffer->LDS loads by the four producer waves
+  if (!consumer) copy_box(0, box0);
+
+  // ---- corner table (consumer waves): sampling positions, bilinear weights times
+  // the mask, and the byte offset of corner (y0, x0) in a box buffer
+  if (consumer) {
 #pragma unroll
   for (int jj = 0; jj < kPE; ++jj) {
-    const int e = tid + jj * kThreads;
+    const int e = tid + jj * 256;
     if (e >= KK * NT) continue;
     const int k = e / NT, p = e - (e / NT) * NT;
     CEnt ce;
@@ -305,7 +415,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const int oy = oy0 + py, ox = ox0 + px;
     if (p < ntile && oy < a.Ho && ox < a.Wo) {
       const int i = k / K, j = k - (k / K) * K;
-      const float dy = ldy[jj], dx = ldx[jj], m = lm[jj];
+      const float dy = __uint_as_float(ldy[jj] << 16), dx = __uint_as_float(ldx[jj] << 16);
+      const float m = a.mask ? __uint_as_float(lm[jj] << 16) : 1.f;
       // integer and fractional parts of the offset are exact in fp32
       const float fy = floorf(dy), fx = floorf(dx);
       const float ly = dy - fy, lx = dx - fx;
@@ -315,99 +426,21 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       if (y0 >= -1.f && y0 <= static_cast<float>(a.H - 1) && x0 >= -1.f && x0 <= static_cast<float>(a.W - 1)) {
         const int iy = static_cast<int>(y0), ix = static_cast<int>(x0);
         const float hy = 1.f - ly, hx = 1.f - lx;
-        ce.off = -1;
+        const int ry = iy - by0, rx = ix - bx0;
+        ce.off = (ry >= 0 && ry + 1 < BH && rx >= 0 && rx + 1 < BW) ? (ry * BW + rx) * kPXB : -1;
         ce.yx = ((iy + 1) << 16) | (ix + 1);
         ce.w01 = pk_bf16(hy * hx * m, hy * lx * m);
         ce.w23 = pk_bf16(ly * hx * m, ly * lx * m);
-        lminy = min(lminy, iy);
-        lmaxy = max(lmaxy, iy);
-        lminx = min(lminx, ix);
-        lmaxx = max(lmaxx, ix);
       }
     }
     ctab[e] = ce;
   }
-  // reduce within the wave first (lanes without samples hold the neutral values),
-  // then one LDS atomic per wave and value: 512 atomics on four words would serialise
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) {
-    lminy = min(lminy, __shfl_xor(lminy, sh));
-    lmaxy = max(lmaxy, __shfl_xor(lmaxy, sh));
-    lminx = min(lminx, __shfl_xor(lminx, sh));
-    lmaxx = max(lmaxx, __shfl_xor(lmaxx, sh));
   }
-  if (lane == 0 && lminy <= lmaxy) {
-    atomicMin(&red[0], lminy);
-    atomicMax(&red[1], lmaxy);
-    atomicMin(&red[2], lminx);
-    atomicMax(&red[3], lmaxx);
-  }
-  __syncthreads();
-
-  // ---- box geometry (uniform): rows [by0, by0+BH), cols [bx0, bx0+BW) within [-1, H] x [-1, W]
-  int by0, bx0, BH, BW;
-  {
-    int y_lo = red[0], y_hi = red[1] + 1, x_lo = red[2], x_hi = red[3] + 1;  // corner rows/cols
-    if (y_lo > y_hi) { y_lo = 0; y_hi = 0; x_lo = 0; x_hi = 0; }           // tile has no samples
-    y_lo = max(y_lo, -1);
-    y_hi = min(y_hi, a.H);
-    x_lo = max(x_lo, -1);
-    x_hi = min(x_hi, a.W);
-    BH = y_hi - y_lo + 1;
-    BW = x_hi - x_lo + 1;
-    by0 = y_lo;
-    bx0 = x_lo;
-    if (BH * BW > Cfg::BOX_PX) {
-      // too wide for LDS: keep the window the tile's samples would use without
-      // offsets, widened evenly as far as the budget allows; the rest goes global
-      const int bh0 = (ba.TH - 1) * a.stride + (K - 1) * a.dil + 2;
-      const int bw0 = (ba.TW - 1) * a.stride + (K - 1) * a.dil + 2;
-      int mg = 0;
-      while ((bh0 + 2 * (mg + 1)) * (bw0 + 2 * (mg + 1)) <= Cfg::BOX_PX) ++mg;
-      by0 = max(oy0 * a.stride - a.pad - mg, -1);
-      bx0 = max(ox0 * a.stride - a.pad - mg, -1);
-      BH = min(bh0 + 2 * mg, a.H + 1 - by0);
-      BW = min(bw0 + 2 * mg, a.W + 1 - bx0);
-      if (BH * BW > Cfg::BOX_PX) { BH = 1; BW = 1; }   // not reached: the host checks the base window fits
-    }
-  }
-  const int npx = BH * BW;
-
-  // ---- prologue pass 2: corner offsets inside the box; zero the box pixels outside the image;
-  // chunk 0 of the box (all waves)
-  for (int e = tid; e < KK * NT; e += kThreads) {
-    const CEnt ce = ctab[e];
-    if (ce.off == -1) {
-      const int ry = (ce.yx >> 16) - 1 - by0, rx = (ce.yx & 0xffff) - 1 - bx0;
-      if (ry >= 0 && ry + 1 < BH && rx >= 0 && rx + 1 < BW) ctab[e].off = (ry * BW + rx) * kPXB;
-    }
-  }
-  if (tid < kZeroB / 16) {
-    *reinterpret_cast<uint4*>(box0 + BOXB + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(box1 + BOXB + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
-  }
-  // chunk 0 of the box: direct global->LDS loads by all eight waves (16 pixels per
-  // wave instruction), zeros for pixels outside the image in both buffers
-  {
-    const int nblk0 = (npx + 15) >> 4;
-    for (int blk = wv; blk < nblk0; blk += 8) {
-      const int px = blk * 16 + (lane >> 2);
-      const int ry = px / BW;
-      const int gy = by0 + ry, gx = bx0 + px - ry * BW;
-      if (px < npx) {
-        if (gy >= 0 && gy < a.H && gx >= 0 && gx < a.W) {
-          const size_t e = (static_cast<size_t>(b * a.H + gy) * a.W + gx) * Cp + (lane & 3) * 8;
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xs + e * 2),
-                                           (lds_void*)(box0 + blk * 1024), 16, 0, 0);
-        } else {
-          *reinterpret_cast<uint4*>(box0 + px * kPXB + (lane & 3) * 16) = make_uint4(0u, 0u, 0u, 0u);
-          *reinterpret_cast<uint4*>(box1 + px * kPXB + (lane & 3) * 16) = make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  __syncthreads();
+  // Drain: the producers' chunk-0 copy, and the consumers' weight and offset loads
+  // (the padded entries' loads are never read, and a register they left pending would
+  // later make a wait cover other loads too).
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0) only
+  lds_barrier();
 
   if (consumer) {
     // ================= consumers: MFMA on the previous step's column tile =================
@@ -500,6 +533,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       step_tail(c + 7, q3, b1, b0);
     }
     step_tail(c + 2 * G, p0, b0, b1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0) only; see the end of the producer branch
 
     // ---- epilogue, part 1: bias and bf16 rounding into an LDS copy of the output
     // tile, [row][pixel] with a row stride of NT+2 elements, in the first box
@@ -526,68 +560,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
               static_cast<uint16_t>(pk_bf16(acc[tm][tn][r] + bv[tm][r], 0.f) & 0xffffu);
   } else {
     // ================= producers: box copies and column tiles =================
-    const int pw = wv - 4;                  // producer wave 0..3
     const int ptid = tid - 256;             // producer thread 0..255
-    // Box copy, one wave instruction per 16 pixels: lane -> pixel blk*16 + lane/4,
-    // 16-byte quarter lane%4.  Pixels advance by 64 between a wave's blocks; the
-    // row/column step is precomputed so no division is needed per block.
-    const int nblk = (npx + 15) >> 4;
-    const int step_r = 64 / BW, step_c = 64 - (64 / BW) * BW;
-    const int px_first = pw * 16 + (lane >> 2);
-    const int ry_first = px_first / BW, rx_first = px_first - (px_first / BW) * BW;
-    // per-lane byte offsets (32-bit: the host keeps the staged copy under 4 GiB)
-    // relative to a wave-uniform base for the chunk
-    const uint32_t img_off = static_cast<uint32_t>(b * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u +
-                             static_cast<uint32_t>((lane & 3) * 16);
-    const uint32_t row_bytes = static_cast<uint32_t>(a.W * Cp) * 2u, px_bytes = static_cast<uint32_t>(Cp) * 2u;
-    // The per-lane byte offsets of the wave's blocks are the same for every chunk (only
-    // the chunk's channel base moves), so they are computed once; each copy is then
-    // one direct global->LDS load per block.  A lane with no pixel to copy (past the
-    // box, or outside the image: those box pixels are zero) loads from past the end
-    // of the buffer, which moves no data, so every block is issued unconditionally
-    // and the number of vector-memory operations of each step is a compile-time
-    // constant (exact wait counts for the prefetched global-path corners below).
-    constexpr int MAXB = Cfg::BOX_PX / 64;   // blocks per wave; 4 * MAXB blocks fill the buffer
-    const uint32_t xs_bytes = static_cast<uint32_t>(a.B * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u;
-    uint32_t boff[MAXB];
-    {
-      int px = px_first, ry = ry_first, rx = rx_first;
-      static_for<0, MAXB>([&](auto jc) __attribute__((always_inline)) {
-        constexpr int j = decltype(jc)::value;
-        const int gy = by0 + ry, gx = bx0 + rx;
-        const bool ok = pw + 4 * j < nblk && px < npx && gy >= 0 && gy < a.H && gx >= 0 && gx < a.W;
-        boff[j] = ok ? img_off + static_cast<uint32_t>(gy) * row_bytes + static_cast<uint32_t>(gx) * px_bytes
-                     : kOOB;
-        px += 64;
-        ry += step_r;
-        rx += step_c;
-        if (rx >= BW) { rx -= BW; ++ry; }
-      });
-    }
-    // blocks J0 .. J1-1 of the wave for chunk cc into `dst`
-    // (raw buffer loads into LDS: a scalar resource per chunk plus a 32-bit vector
-    // offset, so no per-block 64-bit address arithmetic)
-    // chunk cc's view of the staged copy; past the last chunk an empty range, so the
-    // steady-state schedule can issue its copies and loads there too (they move no data)
-    auto chunk_rsrc = [&](int cc) __attribute__((always_inline)) {
-      return make_rsrc(xs + cc * kCK * 2, cc < nCC ? xs_bytes - static_cast<uint32_t>(cc * kCK * 2) : 0u);
-    };
-    auto copy_blocks = [&](int cc, unsigned char* dst, auto j0c, auto j1c) __attribute__((always_inline)) {
-      const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(cc);
-      static_for<decltype(j0c)::value, decltype(j1c)::value>([&](auto jc) __attribute__((always_inline)) {
-        constexpr int j = decltype(jc)::value;
-        buffer_to_lds16(rsrc, dst + (pw + 4 * j) * 1024, boff[j]);
-      });
-    };
-    auto copy_box = [&](int cc, unsigned char* dst) __attribute__((always_inline)) {
-      copy_blocks(cc, dst, std::integral_constant<int, 0>(), std::integral_constant<int, MAXB>());
-    };
-    // the share of the copy issued in step k < 4 of a chunk
-    auto copy_part4 = [&](int cc, unsigned char* dst, auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value;
-      copy_blocks(cc, dst, std::integral_constant<int, k * MAXB / 4>(),
-                  std::integral_constant<int, (k + 1) * MAXB / 4>());
-    };
 
     // Producer state of one step: the corner-table entries and the four corner vectors
     // of this thread's samples.  A sample with nothing in the box reads the zero bytes
@@ -781,7 +754,10 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         if (cc + 1 < nCC) chunk(cc + 1, std::true_type());
       }
     }
-    // S barriers here match the consumers' S barriers
+    // S barriers here match the consumers' S barriers.  The role branches are laid out
+    // one after the other in the compiled code, so loads still counted at the end of
+    // one look pending to the other; drain them here (nothing useful is in flight).
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0) only
   }
 
   // ---- epilogue, part 2 (all waves): NCHW stores of the tile, along its rows, two
