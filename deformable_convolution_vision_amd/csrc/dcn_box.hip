@@ -536,8 +536,9 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0) only; see the end of the producer branch
 
     // ---- epilogue, part 1: bias and bf16 rounding into an LDS copy of the output
-    // tile, [row][pixel] with a row stride of NT+2 elements, in the first box
-    // buffer.  The producers read no box after barrier S-1, and the consumers pass
+    // tile, [pixel][row] with a pixel stride of MT+2 elements (an odd number of
+    // dwords, so neighbouring pixels start in neighbouring banks), in the first box
+    // buffer.  A lane's four consecutive rows of a pixel are one 8-byte write.  The producers read no box after barrier S-1, and the consumers pass
     // that barrier only after every producer's reads are complete.  The bias values
     // are loaded first; rows past Cout read the last bias value and are not stored.
     // Accumulator element r of a 32x32 block: row 8*(r/4) + 4*lh + r%4, column l32.
@@ -549,15 +550,18 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         for (int r = 0; r < 16; ++r)
           bv[tm][r] = ld_bf16(a.bias, min(m0 + wv * WM + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3), a.Cout - 1));
     }
-    uint16_t* stage = reinterpret_cast<uint16_t*>(box0);
+    uint32_t* stage = reinterpret_cast<uint32_t*>(box0);
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          stage[(wv * WM + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)) * (NT + 2) + tn * 32 + l32] =
-              static_cast<uint16_t>(pk_bf16(acc[tm][tn][r] + bv[tm][r], 0.f) & 0xffffu);
+        for (int g = 0; g < 4; ++g) {
+          const int row = wv * WM + tm * 32 + 8 * g + 4 * lh;   // even
+          uint32_t* d = stage + ((tn * 32 + l32) * (MT + 2) + row) / 2;
+          d[0] = pk_bf16(acc[tm][tn][4 * g] + bv[tm][4 * g], acc[tm][tn][4 * g + 1] + bv[tm][4 * g + 1]);
+          d[1] = pk_bf16(acc[tm][tn][4 * g + 2] + bv[tm][4 * g + 2], acc[tm][tn][4 * g + 3] + bv[tm][4 * g + 3]);
+        }
   } else {
     // ================= producers: box copies and column tiles =================
     const int ptid = tid - 256;             // producer thread 0..255
@@ -762,7 +766,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 
   // ---- epilogue, part 2 (all waves): NCHW stores of the tile, along its rows, two
   // pixels per 4-byte store where the element index is even
-  static_assert(MT * (NT + 2) * 2 <= BOXB, "output tile must fit in a box buffer");
+  static_assert(NT * (MT + 2) * 2 <= BOXB, "output tile must fit in a box buffer");
   __syncthreads();
   {
     // Thread -> (column pair of a tile row, first row).  Pairs are aligned to even
@@ -787,8 +791,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 #pragma unroll 4
       for (int r = r0; r < rows; r += rstep) {
         const int o = m0 + ol, oy = oy0 + py;
-        const uint16_t* src = stage + ol * (NT + 2) + py * TW;
-        const uint32_t v0 = src[q0], v1 = src[q1];
+        const uint16_t* src = stage + (py * TW) * (MT + 2) + ol;
+        const uint32_t v0 = src[q0 * (MT + 2)], v1 = src[q1 * (MT + 2)];
         if (o < a.Cout && oy < a.Ho) {
           const int e = (b * a.Cout + o) * a.HoWo + oy * a.Wo + c0;
           if (pair) {
