@@ -292,8 +292,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   // ---- the consumer waves build the corner table while the producer waves copy the
   // first box chunk (a wave waiting for its offsets would otherwise also wait for its
   // older box loads).  The consumers issue the offset and mask loads of every (tap,
-  // pixel) entry, then the first 2G weight steps; the table math waits only for the
-  // offsets, the weights stay in flight.
+  // pixel) entry, all independent, then do the table math.
   const int ntile = ba.TH * ba.TW;
   constexpr int kPE = (kBoxMaxKK * NT + 255) / 256;
   // raw bf16 bits; every address first, then every load
@@ -322,8 +321,6 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       ldx[j] = offs[ob[j] + a.HoWo];
       lm[j] = msk[mb[j]];
     }
-    load_group(0, p0, p1, p2, p3);
-    load_group(G, q0, q1, q2, q3);
   }
 
   // ---- the producers' box-copy plan (with the box pixels outside the image zeroed),
@@ -436,14 +433,20 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     ctab[e] = ce;
   }
   }
-  // Drain: the producers' chunk-0 copy, and the consumers' weight and offset loads
-  // (the padded entries' loads are never read, and a register they left pending would
-  // later make a wait cover other loads too).
+  // Drain: the producers' chunk-0 copy and the consumers' offset loads (the padded
+  // entries' loads are never read, and a register they left pending would later make
+  // a wait cover the weight loads too).
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0) only
   lds_barrier();
 
   if (consumer) {
     // ================= consumers: MFMA on the previous step's column tile =================
+    // The first 2G weight steps are loaded here rather than in the shared prologue:
+    // the two role branches are laid out one after the other in the compiled code, so
+    // registers the consumers load before the branch would stay allocated through the
+    // producers' code.  Steps 0 and 1 have no multiply, which hides most of the latency.
+    load_group(0, p0, p1, p2, p3);
+    load_group(G, q0, q1, q2, q3);
     floatx16 acc[TM][TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -578,11 +581,35 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // corners outside the image, load zeros.  One step's vectors are live at a time.
     uint4 gq[GU][4];
     bool gfl[GU];
-    auto read_ce = [&](int k, PSet& f) __attribute__((always_inline)) {
+    // With one sample per thread and 3x3 taps the offsets and weights of the thread's
+    // nine table entries stay in registers for the whole tile (the steps index them
+    // with compile-time taps), which takes the table reads off every step; the global
+    // path reads its pixel coordinates from the table when it needs them.
+    constexpr bool kCeRegs = GU == 1 && KKT == 9;
+    constexpr int kCeN = kCeRegs ? 9 : 1;
+    int ce_off[kCeN];
+    uint32_t ce_w01[kCeN], ce_w23[kCeN];
+    if constexpr (kCeRegs) {
 #pragma unroll
-      for (int g = 0; g < GU; ++g)
-        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS)
-          f.ce[g] = __builtin_bit_cast(CEnt, reinterpret_cast<const uint4*>(ctab)[k * NT + ((ptid + g * 256) >> 2)]);
+      for (int k = 0; k < 9; ++k) {
+        const CEnt e = ctab[k * NT + (ptid >> 2)];
+        ce_off[k] = e.off;
+        ce_w01[k] = e.w01;
+        ce_w23[k] = e.w23;
+      }
+    }
+    auto read_ce = [&](int k, PSet& f) __attribute__((always_inline)) {
+      if constexpr (kCeRegs) {
+        f.ce[0].off = ce_off[k];
+        f.ce[0].yx = 0;
+        f.ce[0].w01 = ce_w01[k];
+        f.ce[0].w23 = ce_w23[k];
+      } else {
+#pragma unroll
+        for (int g = 0; g < GU; ++g)
+          if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS)
+            f.ce[g] = __builtin_bit_cast(CEnt, reinterpret_cast<const uint4*>(ctab)[k * NT + ((ptid + g * 256) >> 2)]);
+      }
     };
     auto read_q = [&](const unsigned char* src, PSet& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -599,8 +626,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         }
       }
     };
-    // the global-path corner vectors of the step whose table entries are in f (chunk cc)
-    auto load_g = [&](int cc, const PSet& f) __attribute__((always_inline)) {
+    // the global-path corner vectors of the step (chunk cc, tap k) whose table entries are in f
+    auto load_g = [&](int cc, int k, const PSet& f) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
         if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
@@ -608,7 +635,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
           gfl[g] = __ballot(ce.off == -1) != 0;
           if (gfl[g]) {
             const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(cc);
-            const int y0 = (ce.yx >> 16) - 1, x0 = (ce.yx & 0xffff) - 1;
+            const int yx = kCeRegs ? ctab[k * NT + ((ptid + g * 256) >> 2)].yx : ce.yx;
+            const int y0 = (yx >> 16) - 1, x0 = (yx & 0xffff) - 1;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
               const int yy = y0 + (qq >> 1), xx = x0 + (qq & 1);
@@ -673,7 +701,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
           if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
           PSet& next = (k + 1) % 3 == 0 ? X : ((k + 1) % 3 == 1 ? Y : Z);
           finish(cc * 9 + k, cur);
-          load_g(k < 8 ? cc : cc + 1, next);
+          load_g(k < 8 ? cc : cc + 1, (k + 1) % 9, next);
           asm volatile("" ::: "memory");   // the column stores stay ahead of the reads below
           read_ce((k + 3) % 9, cur);
           if constexpr (k + 2 < 9) {
@@ -699,7 +727,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
           PSet& oth = ((k + (odd ? 1 : 0)) & 1) == 0 ? Y : X;
           if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
           finish(cc * 9 + k, cur);
-          if constexpr (k < 8) load_g(cc, oth);
+          if constexpr (k < 8) load_g(cc, k + 1, oth);
           asm volatile("" ::: "memory");
           if constexpr (k + 1 < 9) read_q(src, oth);
           read_ce((k + 2) % 9, cur);
@@ -708,7 +736,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
             lds_barrier_dma();
             if (cc + 1 < nCC) {
               read_q(dst, oth);
-              load_g(cc + 1, oth);
+              load_g(cc + 1, 0, oth);
             }
           } else {
             lds_barrier_keep<kKeep>();
@@ -721,7 +749,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         read_ce(2, Z);
         read_q(box0, X);
         read_q(box0, Y);
-        load_g(0, X);
+        load_g(0, 0, X);
         for (int cc = 0; cc < nCC; cc += 2) {
           chunk9(cc, std::false_type());
           if (cc + 1 < nCC) chunk9(cc + 1, std::true_type());
@@ -730,7 +758,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         read_ce(0, X);
         read_ce(1, Y);
         read_q(box0, X);
-        load_g(0, X);
+        load_g(0, 0, X);
         for (int cc = 0; cc < nCC; cc += 2) {
           chunk9_two(cc, std::false_type());
           if (cc + 1 < nCC) chunk9_two(cc + 1, std::true_type());
@@ -747,7 +775,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         for (int k = 0; k < KK; ++k) {
           read_ce(k, X);
           read_q(src, X);
-          load_g(cc, X);
+          load_g(cc, k, X);
           finish(cc * KK + k, X);
           if (k == KK - 1 && cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
           lds_barrier_dma();
