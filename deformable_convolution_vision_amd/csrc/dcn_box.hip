@@ -677,42 +677,50 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // behind a runtime pointer select), so every LDS access names its array and only
     // waits for copies into that array.  Each chunk starts copying the next chunk's
     // box into the other buffer and waits for that copy before its last barrier.
-    PSet X, Y, Z;
+    PSet X, Y;
     if constexpr (KKT == 9) {
       // Three kernel points: the nine steps of a chunk are unrolled and software
-      // pipelined over three register sets, step k using set k % 3 (nine steps per
-      // chunk keep the assignment the same in every chunk).  Step k interpolates from
-      // corner vectors read during step k-2, stores its column tile, and then reads
-      // the corner vectors of step k+2 and the corner-table entries of step k+3; those
-      // reads stay in flight across the barrier (the box being read and the table do
-      // not change), so no LDS round trip is on a step's critical path.  The next
-      // chunk's box is copied during steps 0-3; each wave waits for its part before
-      // barrier 6, after which the whole box is in LDS and steps 7 and 8 read the
-      // corners of the next chunk's steps 0 and 1 from it.
+      // pipelined over register sets.  The next chunk's box is copied during steps 0-3;
+      // each wave waits for its part before barrier 6, after which the whole box is in
+      // LDS and steps 7 and 8 read the corners of the next chunk's steps 0 and 1 from it.
       constexpr int kKeep = GU * 5 < 15 ? GU * 5 : 15;   // LDS reads issued after the column stores
-      auto chunk9 = [&](int cc, auto parity) __attribute__((always_inline)) {
+      // One sample per thread: each step interpolates the NEXT step's column, so its
+      // column store stays in flight across the barrier (the consumers read it only
+      // after the next one) and no store latency is on a step's critical path.  Two
+      // register sets, step j's data in set j % 2 (the parity flips with each
+      // nine-step chunk).  Step k of chunk cc (global step s):
+      //   1. reads the corners of step s+2 into set s % 2, whose step s was
+      //      interpolated during step k-1 (box of the next chunk from step 7 on,
+      //      after barrier 6);
+      //   2. issues its share of the next chunk's box copy (k < 4);
+      //   3. interpolates step s+1 from corners read a step earlier and stores it;
+      //   4. loads the global-path corners of step s+2.
+      // The corner-table entries of all nine taps are in registers.
+      auto chunk9w = [&](int cc, auto parity) __attribute__((always_inline)) {
         constexpr bool odd = decltype(parity)::value;
         const unsigned char* src = odd ? box1 : box0;
         unsigned char* dst = odd ? box0 : box1;
         static_for<0, 9>([&](auto kc) __attribute__((always_inline)) {
           constexpr int k = decltype(kc)::value;
-          PSet& cur = k % 3 == 0 ? X : (k % 3 == 1 ? Y : Z);
-          PSet& ahead = (k + 2) % 3 == 0 ? X : ((k + 2) % 3 == 1 ? Y : Z);
-          if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
-          PSet& next = (k + 1) % 3 == 0 ? X : ((k + 1) % 3 == 1 ? Y : Z);
-          finish(cc * 9 + k, cur);
-          load_g(k < 8 ? cc : cc + 1, (k + 1) % 9, next);
-          asm volatile("" ::: "memory");   // the column stores stay ahead of the reads below
-          read_ce((k + 3) % 9, cur);
+          PSet& s0 = ((k + (odd ? 1 : 0)) & 1) == 0 ? X : Y;   // set of steps s and s+2
+          PSet& s1 = ((k + (odd ? 1 : 0)) & 1) == 0 ? Y : X;   // set of step s+1
+          read_ce((k + 2) % 9, s0);
           if constexpr (k + 2 < 9) {
-            read_q(src, ahead);
+            read_q(src, s0);
           } else {
             // the next chunk's steps 0 and 1 (a dummy re-read of this box after the last chunk)
-            if (cc + 1 < nCC) read_q(dst, ahead);
-            else read_q(src, ahead);
+            if (cc + 1 < nCC) read_q(dst, s0);
+            else read_q(src, s0);
           }
+          if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
+          const bool last = k == 8 && cc + 1 == nCC;   // no step s+1
+          if (!last) finish(cc * 9 + k + 1, s1);
+          load_g(k < 7 ? cc : cc + 1, (k + 2) % 9, s0);
           if constexpr (k == 6) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          lds_barrier_keep<kKeep>();
+          // keep the corner reads and the column store in flight; the previous step's
+          // store (older) is complete
+          if (!last) lds_barrier_keep<5>();
+          else lds_barrier_keep<4>();
         });
       };
       // With more than one sample per thread three sets would not fit in registers:
@@ -745,14 +753,15 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       };
       if constexpr (GU == 1) {
         read_ce(0, X);
-        read_ce(1, Y);
-        read_ce(2, Z);
         read_q(box0, X);
+        read_ce(1, Y);
         read_q(box0, Y);
         load_g(0, 0, X);
+        finish(0, X);          // column 0, before the loop
+        load_g(0, 1, Y);
         for (int cc = 0; cc < nCC; cc += 2) {
-          chunk9(cc, std::false_type());
-          if (cc + 1 < nCC) chunk9(cc + 1, std::true_type());
+          chunk9w(cc, std::false_type());
+          if (cc + 1 < nCC) chunk9w(cc + 1, std::true_type());
         }
       } else {
         read_ce(0, X);
