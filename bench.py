@@ -18,6 +18,9 @@ roofline    = the fused kernel alone: algorithmic flops per launch / its mean du
               per launch from the committed counter runs, if the kernels are unchanged
 cpu_baseline = the CPU oracle on a bounded slice of the same workload (a range of
               output channels), scaled to TFLOP/s, with the threads it used
+cold        = separate from value: steps each preceded by a 512 MiB device write that
+              evicts the inputs from L2 and the 256 MB last-level cache (MALL), timed
+              with events around the step alone
 """
 
 from __future__ import annotations
@@ -123,7 +126,7 @@ def traffic_for(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: float):
+def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: float, cold_steps: int = 0):
     import numpy as np
     import torch
 
@@ -193,6 +196,33 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
     fused_mean = sum(fused_ms) / steps
     stage_mean = sum(stage_ms) / steps
 
+    cold = None
+    if cold_steps > 0:
+        # Cold caches: before each step, write 512 MiB (twice the MALL) so that no input
+        # byte is left in L2 or the MALL; only the step itself is between the events.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cev = HipEvents(3 * cold_steps)
+        for i in range(cold_steps):
+            flush.fill_(i & 0xff)
+            cev.record(3 * i, sp)
+            dcn.dcn_stage(desc, g["x"], g["weight"], wsp, nb, stream)
+            cev.record(3 * i + 1, sp)
+            dcn.dcn_forward_staged(desc, g["x"], g["offset"], g["mask"], g["weight"], g["bias"], out, wsp, nb,
+                                   stream)
+            cev.record(3 * i + 2, sp)
+        cev.sync(3 * cold_steps - 1)
+        torch.cuda.synchronize()
+        c_step = [cev.ms(3 * i, 3 * i + 2) for i in range(cold_steps)]
+        c_stage = [cev.ms(3 * i, 3 * i + 1) for i in range(cold_steps)]
+        c_fused = [cev.ms(3 * i + 1, 3 * i + 2) for i in range(cold_steps)]
+        cev.close()
+        del flush
+        c_ms = sum(c_step) / cold_steps
+        cold = {"steps": cold_steps, "ms_per_step": round(c_ms, 6),
+                "tflops": round(w.flops / (c_ms * 1e-3) / 1e12, 4),
+                "stage_mean_us": round(sum(c_stage) / cold_steps * 1e3, 3),
+                "fused_mean_us": round(sum(c_fused) / cold_steps * 1e3, 3)}
+
     flops = w.flops
     abytes = w.algorithmic_bytes
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -235,6 +265,7 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
                        "fused_min": round(fused_ms[0] * 1e3, 3)},
         "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
         "parity_max_rel_err_sampled": max_rel,
+        "cold": cold,
         "cpu_baseline": None,
     }
     if cpu:
@@ -291,6 +322,8 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="also print one line per other named workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed after evicting the caches (reported under 'cold'; 0 skips them)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -311,7 +344,7 @@ def main(argv=None):
         names += [n for n in ORDER if n != args.workload]
     for i, n in enumerate(names):
         rec = bench_workload(n, args.steps, args.warmup, cpu=(not args.no_cpu) and i == 0,
-                             cpu_seconds=args.cpu_seconds)
+                             cpu_seconds=args.cpu_seconds, cold_steps=args.cold_steps)
         print(json.dumps(rec), flush=True)
     return 0
 
