@@ -122,32 +122,131 @@ __device__ __forceinline__ void pack_weight(const StageArgs& a, int wg, int nwg)
   }
 }
 
+// The step-major weight layout from bf16 with Cin a multiple of 8 and a 16-byte aligned
+// w: one thread per (row o, 8 channels), whose 8*K*K values are contiguous in w
+// (nine 16-byte loads for 3x3); for each kernel point the 8 channels' values are
+// gathered into one 16-byte store.
+__device__ __forceinline__ bool pack_weight_v8_ok(const StageArgs& a) {
+  return a.wlayout == 1 && a.KK == 9 && a.Cin % 8 == 0 && reinterpret_cast<uintptr_t>(a.w) % 16 == 0;
+}
+__device__ __forceinline__ void pack_weight_v8(const StageArgs& a, int wg, int nwg) {
+  const uint4* w = reinterpret_cast<const uint4*>(a.w);
+  uint4* wp = reinterpret_cast<uint4*>(a.wp);
+  const int groups = a.Cp / 8, total = a.Mp * groups;
+  for (int e = wg * kThreads + static_cast<int>(threadIdx.x); e < total; e += nwg * kThreads) {
+    const int o = e / groups, c = (e - (e / groups) * groups) * 8;
+    uint32_t d[36];   // 72 bf16: channel i, kernel point k at element 9i + k
+    if (o < a.Cout && c < a.Cin) {
+      const uint4* src = w + (static_cast<size_t>(o) * a.Cin + c) * 9 / 8;
+#pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        const uint4 q = src[j];
+        d[4 * j] = q.x; d[4 * j + 1] = q.y; d[4 * j + 2] = q.z; d[4 * j + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 36; ++j) d[j] = 0;
+    }
+    uint4* dst = wp + ((static_cast<size_t>(c >> 5) * 9) * a.Mp + o) * 4 + ((c & 31) >> 3);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      uint32_t r[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int e0 = 18 * m + k, e1 = e0 + 9;   // channels 2m and 2m+1
+        // byte selectors of v_perm: 0-3 pick from the second operand, 4-7 from the first
+        const uint32_t s0 = (e0 & 1) ? 0x0302u : 0x0100u, s1 = (e1 & 1) ? 0x0706u : 0x0504u;
+        r[m] = __builtin_amdgcn_perm(d[e1 >> 1], d[e0 >> 1], (s1 << 16) | s0);
+      }
+      dst[static_cast<size_t>(k) * a.Mp * 4] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+  }
+}
+
 // One launch stages both operands of the fused kernel.
-//   Workgroups [0, nx):  x[b][c][s] -> xs[b][s][c] for s in [0, H*W), c in [0, Cp),
+//   Workgroups [0, nw):  w[o][c][k] -> wp[o][k][c] (or the step-major layout of the
+//                        box kernel) for o < Mp, k < KK, c < Cp, zero outside
+//                        Cout x Cin.
+//   Workgroups [nw, ..): x[b][c][s] -> xs[b][s][c] for s in [0, H*W), c in [0, Cp),
 //                        channels >= Cin written as 0.  Each moves a 64-channel x
-//                        64-pixel tile through LDS: global reads are VEC pixels of
-//                        one channel (VEC = 16 bytes' worth when H*W allows the
-//                        alignment, fewer otherwise), global writes are 16-byte
-//                        channel vectors of one pixel.
-//   Workgroups [nx, ..): w[o][c][k] -> wp[o][k][c] (or the step-major layout of the
-//   box kernel) for o < Mp, k < KK, c < Cp,
-//                        zero outside Cout x Cin.
+//                        64-pixel tile (128 pixels for bf16 with 16-byte reads)
+//                        through LDS: global reads are VEC pixels of one channel
+//                        (VEC = 16 bytes' worth when H*W allows the alignment, fewer
+//                        otherwise), global writes are 16-byte channel vectors of one
+//                        pixel.
+// bf16 with 16-byte reads (H*W a multiple of 8): the transpose goes through LDS as
+// channel pairs.  Thread (channel pair cp, pixel group pg) reads 8 pixels of channels
+// 2cp and 2cp+1 (eight lanes cover 128 contiguous bytes of one channel), packs each
+// pixel's two channels into one dword and writes the eight dwords to tile[p][cp].
+// The 16-byte group of 4 channel pairs is XOR-swizzled with the pixel group, so the
+// dword writes of a wave and the 16-byte reads of one pixel's 8 channels both hit
+// distinct banks; a thread then writes 8 channels of one pixel as one 16-byte store
+// (eight lanes cover the 128 bytes of the tile's 64 channels of that pixel).
+constexpr int kPairPx = 128;   // pixels per tile of the channel-pair transpose
+__device__ __forceinline__ void stage_x_bf16_v8(const StageArgs& a, uint32_t* tile, int b, int s0, int c0) {
+  const int tid = threadIdx.x;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(a.x) + static_cast<size_t>(b) * a.Cin * a.HW;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(a.xs) + static_cast<size_t>(b) * a.HW * a.Cp;
+#pragma unroll
+  for (int u = 0; u < kPairPx / 64; ++u) {
+    const int pg = (tid & 7) + 8 * u, cp = tid >> 3;
+    const int c = c0 + 2 * cp, sp = s0 + 8 * pg;
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    if (sp < a.HW) {   // H*W is a multiple of 8: the vector is all in or all out
+      const uint16_t* src = x + static_cast<size_t>(c) * a.HW + sp;
+      if (c < a.Cin) lo = *reinterpret_cast<const uint4*>(src);
+      if (c + 1 < a.Cin) hi = *reinterpret_cast<const uint4*>(src + a.HW);
+    }
+    const uint32_t l[4] = {lo.x, lo.y, lo.z, lo.w}, h[4] = {hi.x, hi.y, hi.z, hi.w};
+    uint32_t* t = tile + (8 * pg) * 32 + (((cp >> 2) ^ (pg & 7)) << 2) + (cp & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t[(2 * i) * 32] = __builtin_amdgcn_perm(h[i], l[i], 0x05040100u);      // pixel 2i
+      t[(2 * i + 1) * 32] = __builtin_amdgcn_perm(h[i], l[i], 0x07060302u);  // pixel 2i+1
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPairPx / 32; ++j) {
+    const int g = tid & 7, p = (tid >> 3) + 32 * j;
+    const int sp = s0 + p, c = c0 + 8 * g;
+    if (sp >= a.HW || c >= a.Cp) continue;
+    const uint4 q = *reinterpret_cast<const uint4*>(tile + p * 32 + ((g ^ ((p >> 3) & 7)) << 2));
+    *reinterpret_cast<uint4*>(xs + static_cast<size_t>(sp) * a.Cp + c) = q;
+  }
+}
+
 template <bool BF16, int VEC>
 __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a, int nx, int s_tiles, int c_tiles) {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int ES = sizeof(T);
   constexpr int OUTV = 16 / ES;                  // elements per 16-byte channel vector
-  __shared__ T tile[64][64 + 2];                 // [channel][pixel]
+  constexpr bool kPairs = BF16 && VEC == 8;
+  __shared__ __attribute__((aligned(16))) T tile[64][kPairs ? kPairPx : 64 + 2];   // [channel][pixel]
   const int tid = threadIdx.x;
-  if (static_cast<int>(blockIdx.x) >= nx) {
-    pack_weight<T>(a, static_cast<int>(blockIdx.x) - nx, static_cast<int>(gridDim.x) - nx);
+  // the weight workgroups come first, so that they run beside the first x tiles
+  // rather than after the last
+  const int nw = static_cast<int>(gridDim.x) - nx;
+  if (static_cast<int>(blockIdx.x) < nw) {
+    if constexpr (BF16) {
+      if (pack_weight_v8_ok(a)) {
+        pack_weight_v8(a, static_cast<int>(blockIdx.x), nw);
+        return;
+      }
+    }
+    pack_weight<T>(a, static_cast<int>(blockIdx.x), nw);
     return;
   }
+  const int bx = static_cast<int>(blockIdx.x) - nw;
   const int per_img = s_tiles * c_tiles;
-  const int b = blockIdx.x / per_img;
-  const int r = blockIdx.x - b * per_img;
+  const int b = bx / per_img;
+  const int r = bx - b * per_img;
   const int ct = r / s_tiles, st = r - (r / s_tiles) * s_tiles;
-  const int s0 = st * 64, c0 = ct * 64;
+  const int s0 = st * (kPairs ? kPairPx : 64), c0 = ct * 64;
+  if constexpr (kPairs) {
+    stage_x_bf16_v8(a, reinterpret_cast<uint32_t*>(&tile[0][0]), b, s0, c0);
+    return;
+  }
   const T* x = reinterpret_cast<const T*>(a.x) + static_cast<size_t>(b) * a.Cin * a.HW;
   T* xs = reinterpret_cast<T*>(a.xs) + static_cast<size_t>(b) * a.HW * a.Cp;
   // read: 64 channels x (64 / VEC) vectors of VEC pixels
@@ -483,16 +582,20 @@ hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream) {
   const VariantInfo& vi = kVariants[variant];
   if (!vi.staged) return hipSuccess;
   const uintptr_t xa = reinterpret_cast<uintptr_t>(a.x);
-  const int s_tiles = (a.HW + 63) / 64, c_tiles = (a.Cp + 63) / 64;
+  // widest global read that every channel plane (starting at x + c*H*W elements)
+  // keeps aligned, given the caller's x pointer
+  auto fits = [&](int vec, int es) { return a.HW % vec == 0 && xa % static_cast<uintptr_t>(vec * es) == 0; };
+  const int spx = vi.is_bf16 && fits(8, 2) ? kPairPx : 64;   // pixels per x tile
+  const int s_tiles = (a.HW + spx - 1) / spx, c_tiles = (a.Cp + 63) / 64;
   const int nx = s_tiles * c_tiles * a.B;
-  const int nw = min((a.Mp * a.Cp + kThreads - 1) / kThreads, 1024);
+  const bool wv8 = vi.is_bf16 && a.wlayout == 1 && a.KK == 9 && a.Cin % 8 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.w) % 16 == 0;   // pack_weight_v8_ok
+  const int wunits = wv8 ? a.Mp * (a.Cp / 8) : a.Mp * a.Cp;
+  const int nw = min((wunits + kThreads - 1) / kThreads, 1024);
   const dim3 grid(nx + nw);
   StageArgs sa = a;
   void* args[] = {&sa, const_cast<int*>(&nx), const_cast<int*>(&s_tiles), const_cast<int*>(&c_tiles)};
   const void* fn;
-  // widest global read that every channel plane (starting at x + c*H*W elements)
-  // keeps aligned, given the caller's x pointer
-  auto fits = [&](int vec, int es) { return a.HW % vec == 0 && xa % static_cast<uintptr_t>(vec * es) == 0; };
   if (vi.is_bf16)
     fn = fits(8, 2)   ? reinterpret_cast<const void*>(&stage_kernel<true, 8>)
        : fits(4, 2)   ? reinterpret_cast<const void*>(&stage_kernel<true, 4>)
