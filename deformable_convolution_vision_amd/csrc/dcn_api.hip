@@ -40,6 +40,7 @@ struct BoxPlan {
   int fm = 0, fn = 0;           // MT = 64*fm output channels, 16*fn pixel slots
   int TH = 0, TW = 0, tiles_x = 0, tiles_per_img = 0;
   int box_px = 0, lds = 0;
+  int split = 0;                // BoxArgs::split_roles
   double cost = 1e300;
 };
 
@@ -142,6 +143,15 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
     }
   }
   if (best.fm == 0) return false;
+  // Role placement: with 256 output channels and 96 pixel slots (12 matrix
+  // instructions per consumer wave and step, two samples per producer thread) the
+  // step is shorter when the consumers and producers do not share SIMDs (measured on
+  // the c5 layer: 108 -> 100 us); with 64 slots, halving the SIMDs that run matrix
+  // instructions costs more than it saves (c4: 36 -> 38 us).
+  best.split = best.fm == 4 && best.fn == 6;
+  if (const char* r = std::getenv("DCN_BOX_ROLES")) {
+    if (r[0] == '0' || r[0] == '1') best.split = r[0] - '0';
+  }
   *out = best;
   return true;
 }
@@ -225,7 +235,7 @@ int compute_plan(const dcn_desc* d, Plan* p) {
 // with one shape skip the tile search.  Thread-safe; a small round-robin table.
 struct PlanKey {
   dcn_desc d;
-  char variant[48], tile[48];
+  char variant[48], tile[48], roles[8];
 };
 struct PlanSlot {
   bool used = false;
@@ -238,6 +248,7 @@ void fill_key(const dcn_desc* d, PlanKey* k) {
   std::memcpy(&k->d, d, sizeof(dcn_desc));
   if (const char* v = std::getenv("DCN_VARIANT")) std::strncpy(k->variant, v, sizeof(k->variant) - 1);
   if (const char* t = std::getenv("DCN_BOX_TILE")) std::strncpy(k->tile, t, sizeof(k->tile) - 1);
+  if (const char* r = std::getenv("DCN_BOX_ROLES")) std::strncpy(k->roles, r, sizeof(k->roles) - 1);
 }
 
 int make_plan(const dcn_desc* d, Plan* p) {
@@ -342,6 +353,7 @@ hipError_t launch_fused_plan(const Plan& p, const FusedArgs& a, hipStream_t stre
   ba.box_px = p.box.box_px;
   ba.KK_NT = a.KK * 16 * p.box.fn;
   ba.lds_bytes = 0;
+  ba.split_roles = p.box.split;
   return dcn::launch_box(p.box.fm, p.box.fn, ba, stream);
 }
 
@@ -394,10 +406,10 @@ extern "C" int dcn_plan_describe(const dcn_desc* desc, char* buf, size_t len) {
   const dcn::VariantInfo& vi = dcn::variant_info(p.variant);
   if (is_box(p.variant)) {
     std::snprintf(buf, len,
-                  "%s tile=%dx%d px (%d slots) x %d ch, tiles=%lld, box_px=%d, ws=%zu B",
+                  "%s tile=%dx%d px (%d slots) x %d ch, tiles=%lld, box_px=%d, roles=%s, ws=%zu B",
                   vi.name, p.box.TH, p.box.TW, 16 * p.box.fn, 64 * p.box.fm,
                   static_cast<long long>(desc->batch) * p.box.tiles_per_img * (p.Mp / (64 * p.box.fm)),
-                  p.box.box_px, p.ws_bytes);
+                  p.box.box_px, p.box.split ? "split" : "paired", p.ws_bytes);
   } else {
     std::snprintf(buf, len, "%s tile=%d px x %d ch, ws=%zu B", vi.name, vi.nt, vi.mt, p.ws_bytes);
   }

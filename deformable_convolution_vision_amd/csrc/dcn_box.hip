@@ -205,8 +205,14 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   __shared__ __attribute__((aligned(16))) unsigned char box1[BOXB + kZeroB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const bool consumer = wv < 4;
+  // Waves w and w+4 of a workgroup run on the same SIMD.  Roles: by default waves
+  // 0-3 consume and 4-7 produce, so every SIMD runs one of each; with split_roles
+  // waves 0, 1, 4, 5 consume (two SIMDs) and 2, 3, 6, 7 produce (the other two).
+  // wv is the wave's index within its role, rtid the thread's.
+  const int wraw = __builtin_amdgcn_readfirstlane(wave);
+  const bool consumer = ba.split_roles ? (wraw & 2) == 0 : wraw < 4;
+  const int wv = ba.split_roles ? (wraw & 1) | ((wraw >> 2) << 1) : (wraw & 3);
+  const int rtid = wv * 64 + lane;
   // MFMA 32x32x16 operand lanes: row (A) or column (B) lane & 31, and a 16-byte
   // channel group: lane half lh holds channels 16*lh + 8*h .. +7 of k-half h, so a
   // lane's two halves are one contiguous 32-byte run
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     int ob[kPE], mb[kPE];
 #pragma unroll
     for (int j = 0; j < kPE; ++j) {
-      const int e = tid + j * 256;
+      const int e = rtid + j * 256;
       const int k = e / NT, p = e - (e / NT) * NT;
       const int py = p / ba.TW, px = p - (p / ba.TW) * ba.TW;
       const int oy = oy0 + py, ox = ox0 + px;
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 
   // ---- the producers' box-copy plan (with the box pixels outside the image zeroed),
   // then chunk 0 of the box
-  const int pw = wv - 4;                    // producer wave 0..3 (unused by consumers)
+  const int pw = wv;                        // producer wave 0..3 (unused by consumers)
   // Box copy, one wave instruction per 16 pixels: lane -> pixel blk*16 + lane/4,
   // 16-byte quarter lane%4.  Pixels advance by 64 between a wave's blocks; the
   // row/column step is precomputed so no division is needed per block.
@@ -400,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   if (consumer) {
 #pragma unroll
   for (int jj = 0; jj < kPE; ++jj) {
-    const int e = tid + jj * 256;
+    const int e = rtid + jj * 256;
     if (e >= KK * NT) continue;
     const int k = e / NT, p = e - (e / NT) * NT;
     CEnt ce;
@@ -567,7 +573,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         }
   } else {
     // ================= producers: box copies and column tiles =================
-    const int ptid = tid - 256;             // producer thread 0..255
+    const int ptid = rtid;                  // producer thread 0..255
 
     // Producer state of one step: the corner-table entries and the four corner vectors
     // of this thread's samples.  A sample with nothing in the box reads the zero bytes

@@ -40,6 +40,8 @@ struct BoxArgs {
   int box_px;            // capacity of one LDS box buffer, in pixels
   int KK_NT;             // corner-table entries: K*K * 16*FN
   int lds_bytes;         // dynamic LDS per workgroup
+  int split_roles;       // 0: each SIMD runs one consumer and one producer wave;
+                         // 1: the consumers share two SIMDs, the producers the other two
 };
 
 enum Variant : int {

@@ -50,8 +50,10 @@
  *    return) pins it, for tile sweeps and tests; a name that does not exist, was
  *    built for the other dtype or cannot run the shape makes every call return
  *    DCN_E_UNSUPPORTED.  DCN_BOX_TILE="fn,TH,TW" restricts the box kernel's tile
- *    to 16*fn pixel slots holding TH x TW output pixels (sweeps only).  Plans are
- *    cached per descriptor and the two variables' values.
+ *    to 16*fn pixel slots holding TH x TW output pixels (sweeps only), and
+ *    DCN_BOX_ROLES=0|1 pins its placement of consumer and producer waves on the
+ *    SIMDs (tests and sweeps).  Plans are cached per descriptor and the three
+ *    variables' values.
  */
 #ifndef DCN_H
 #define DCN_H

@@ -183,3 +183,22 @@ def test_empty_batch():
     out = dcn.deform_conv2d(x, torch.zeros(0, 18, 9, 9, device="cuda"), torch.zeros(4, 8, 3, 3, device="cuda"),
                             padding=1)
     assert out.shape == (0, 4, 9, 9)
+
+
+@pytest.mark.parametrize("roles", ["0", "1"])
+@pytest.mark.parametrize("variant,tile", [("box_bf16_m256", "4,5,10"), ("box_bf16_m256", "6,7,13"),
+                                          ("box_bf16_m128", "8,8,16"), ("box_bf16_m128", "10,9,17")])
+def test_box_role_placement(variant, tile, roles, monkeypatch):
+    """Both placements of the box kernel's consumer and producer waves on the SIMDs,
+    with one, two and three samples per producer thread and step."""
+    monkeypatch.setenv("DCN_VARIANT", variant)
+    monkeypatch.setenv("DCN_BOX_TILE", tile)
+    monkeypatch.setenv("DCN_BOX_ROLES", roles)
+    shapes = [(2, 64, 9, 10, 260, 3, 2, 1, 1), (2, 64, 17, 19, 130, 1, 1, 0, 1), (2, 40, 12, 14, 300, 3, 1, 2, 2)]
+    for seed, shape in enumerate(shapes):
+        w = make(f"roles_{variant}_{roles}", "bf16", *shape, offset="uniform:8", seed=seed)
+        desc = dcn.make_desc(w.B, w.Cin, w.H, w.W, w.Cout, w.K, w.stride, w.pad, w.dilation, dcn.BF16)
+        plan = dcn.dcn_plan_describe(desc)
+        print(f"[gpu-test] {shape} {plan}", flush=True)
+        assert ("roles=split" if roles == "1" else "roles=paired") in plan
+        full_parity(w)
