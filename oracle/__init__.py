@@ -28,7 +28,7 @@ LIB = os.path.join(HERE, "libdcn_oracle.so")
 
 class _Desc(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in
-                ("B", "Cin", "H", "W", "Cout", "K", "stride", "pad", "dilation")]
+                ("B", "Cin", "H", "W", "Cout", "K", "stride", "pad", "dilation", "groups")]
 
 
 def build(out_path: str = LIB, extra_flags: tuple[str, ...] = (), src: str = SRC) -> str:
@@ -80,18 +80,25 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _desc(x, weight, stride, pad, dilation):
+def _desc(x, weight, stride, pad, dilation, offset=None):
     B, Cin, H, W = x.shape
     Cout, Cin_w, K, K2 = weight.shape
     if Cin_w != Cin or K != K2:
         raise ValueError("weight must be [Cout, Cin, K, K] with Cin matching x")
-    return _Desc(B, Cin, H, W, Cout, K, stride, pad, dilation)
+    G = 1
+    if offset is not None:   # offset groups from the offset's channel count, as torchvision does
+        if offset.ndim != 4 or offset.shape[1] % (2 * K * K) != 0:
+            raise ValueError("offset must have 2*G*K*K channels")
+        G = offset.shape[1] // (2 * K * K)
+        if G < 1 or Cin % G != 0:
+            raise ValueError("Cin must be a multiple of the offset groups")
+    return _Desc(B, Cin, H, W, Cout, K, stride, pad, dilation, G)
 
 
 def output_hw(B, Cin, H, W, Cout, K, stride=1, pad=0, dilation=1, lib_path: str = LIB):
     lib = load(lib_path)
     ho, wo = ctypes.c_int64(), ctypes.c_int64()
-    rc = lib.oracle_output_hw(ctypes.byref(_Desc(B, Cin, H, W, Cout, K, stride, pad, dilation)),
+    rc = lib.oracle_output_hw(ctypes.byref(_Desc(B, Cin, H, W, Cout, K, stride, pad, dilation, 1)),
                               ctypes.byref(ho), ctypes.byref(wo))
     if rc != 0:
         raise ValueError("invalid geometry")
@@ -99,7 +106,7 @@ def output_hw(B, Cin, H, W, Cout, K, stride=1, pad=0, dilation=1, lib_path: str 
 
 
 def _check(x, offset, mask, weight, bias, d, Ho, Wo):
-    KK = d.K * d.K
+    KK = d.K * d.K * d.groups
     if offset.shape != (d.B, 2 * KK, Ho, Wo):
         raise ValueError(f"offset must be {(d.B, 2 * KK, Ho, Wo)}, got {offset.shape}")
     if mask is not None and mask.shape != (d.B, KK, Ho, Wo):
@@ -116,7 +123,7 @@ def forward(x, offset, weight, bias=None, stride=1, padding=0, dilation=1, mask=
     """
     lib = load(lib_path)
     x, offset, weight, bias, mask = map(_f32, (x, offset, weight, bias, mask))
-    d = _desc(x, weight, stride, padding, dilation)
+    d = _desc(x, weight, stride, padding, dilation, offset)
     Ho, Wo = output_hw(d.B, d.Cin, d.H, d.W, d.Cout, d.K, stride, padding, dilation, lib_path)
     _check(x, offset, mask, weight, bias, d, Ho, Wo)
     o0, o1 = (0, d.Cout) if cout_range is None else cout_range
@@ -134,7 +141,7 @@ def points(x, offset, weight, pts, bias=None, stride=1, padding=0, dilation=1, m
     """y and sum of |terms| at individual outputs; pts is an int array [n, 4] of (b, o, oy, ox)."""
     lib = load(lib_path)
     x, offset, weight, bias, mask = map(_f32, (x, offset, weight, bias, mask))
-    d = _desc(x, weight, stride, padding, dilation)
+    d = _desc(x, weight, stride, padding, dilation, offset)
     Ho, Wo = output_hw(d.B, d.Cin, d.H, d.W, d.Cout, d.K, stride, padding, dilation, lib_path)
     _check(x, offset, mask, weight, bias, d, Ho, Wo)
     pts = np.ascontiguousarray(np.asarray(pts, dtype=np.int64).reshape(-1, 4))

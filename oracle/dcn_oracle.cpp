@@ -25,6 +25,7 @@ bool valid_desc(const oracle_desc* d) {
   if (d->B < 0 || d->Cout < 0) return false;
   if (d->Cin < 1 || d->H < 1 || d->W < 1 || d->K < 1) return false;
   if (d->stride < 1 || d->dilation < 1 || d->pad < 0) return false;
+  if (d->groups < 0 || (d->groups > 1 && d->Cin % d->groups != 0)) return false;
   return true;
 }
 
@@ -67,6 +68,7 @@ void one_output(const oracle_desc* d, int64_t Ho, int64_t Wo, const float* x,
                 const float* bias, int64_t b, int64_t o, int64_t oy, int64_t ox,
                 double* y_out, double* abs_out) {
   const int64_t K = d->K, KK = K * K;
+  const int64_t G = d->groups > 1 ? d->groups : 1, Cg = d->Cin / G;
   double y = 0.0, a = 0.0;
   if (bias != nullptr) {
     y = static_cast<double>(bias[o]);
@@ -74,13 +76,15 @@ void one_output(const oracle_desc* d, int64_t Ho, int64_t Wo, const float* x,
   }
   for (int64_t c = 0; c < d->Cin; ++c) {
     const float* plane = x + ((b * d->Cin + c) * d->H) * d->W;
+    const int64_t g = c / Cg;   // offset group of this channel
     for (int64_t k = 0; k < KK; ++k) {
       const int64_t i = k / K, j = k % K;
-      const double dy = offset[((b * 2 * KK + 2 * k) * Ho + oy) * Wo + ox];
-      const double dx = offset[((b * 2 * KK + 2 * k + 1) * Ho + oy) * Wo + ox];
+      const int64_t gk = g * KK + k;   // (group, kernel point) index of the offset and mask fields
+      const double dy = offset[((b * 2 * KK * G + 2 * gk) * Ho + oy) * Wo + ox];
+      const double dx = offset[((b * 2 * KK * G + 2 * gk + 1) * Ho + oy) * Wo + ox];
       const double py = static_cast<double>(oy * d->stride - d->pad + i * d->dilation) + dy;
       const double px = static_cast<double>(ox * d->stride - d->pad + j * d->dilation) + dx;
-      const double m = (mask != nullptr) ? static_cast<double>(mask[((b * KK + k) * Ho + oy) * Wo + ox]) : 1.0;
+      const double m = (mask != nullptr) ? static_cast<double>(mask[((b * KK * G + gk) * Ho + oy) * Wo + ox]) : 1.0;
       const double w = weight[((o * d->Cin + c) * K + i) * K + j];
       const double term = w * m * bilinear_zero_outside(plane, d->H, d->W, py, px);
       y += term;

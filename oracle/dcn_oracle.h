@@ -9,9 +9,10 @@
  *
  *   y[b,o,oy,ox] = bias[o] + sum_{c<Cin} sum_{k<K*K} W[o,c,i,j] * m_k * S(X[b,c], py_k, px_k)
  *      i = k / K, j = k % K            (kernel point k in row-major order)
- *      py_k = oy*stride - pad + i*dilation + offset[b, 2k,   oy, ox]
- *      px_k = ox*stride - pad + j*dilation + offset[b, 2k+1, oy, ox]
- *      m_k  = mask[b, k, oy, ox]       (1 when mask is NULL: DCNv1)
+ *      g = c / (Cin/G)                 (offset group of channel c; G = 1 by default)
+ *      py_k = oy*stride - pad + i*dilation + offset[b, 2(g*K*K + k),   oy, ox]
+ *      px_k = ox*stride - pad + j*dilation + offset[b, 2(g*K*K + k)+1, oy, ox]
+ *      m_k  = mask[b, g*K*K + k, oy, ox]   (1 when mask is NULL: DCNv1)
  *      S(X, py, px) = sum over the four integer neighbours (yy, xx) of (py, px),
  *                     yy in {floor(py), floor(py)+1}, xx in {floor(px), floor(px)+1},
  *                     of (1-|py-yy|)*(1-|px-xx|) * X[yy, xx], where a neighbour
@@ -28,13 +29,18 @@
  *  - bilinear interpolation from the four neighbours: same csdn tags page,
  *    section 可变形卷积Pytorch实现, bilinear-interpolation equation (areas S1..S4);
  *  - stride / padding / dilation as in torchvision's deform_conv2d parameter
- *    table on agent.csdn.net/6a744b3d10ee7a33f2973402.html, section 2.1.
+ *    table on agent.csdn.net/6a744b3d10ee7a33f2973402.html, section 2.1;
+ *  - offset groups (channels split along the channel axis into G consecutive
+ *    groups, each with its own offset field; 2K^2 * G offset channels): the csdn
+ *    tags page, section Deformable Group; the deform_groups argument of the DCN
+ *    config on 51itzy.com/kjqy/64159.html (mmdetection section).
  * Readings taken where the pages are silent or disagree: offset channel 2k is
  * the row displacement dy and 2k+1 the column displacement dx; a neighbour
  * outside the image counts as zero (no clamping); the upper neighbour is
  * floor+1 (not ceil, which would lose the sample at integer positions);
- * offsets are in input pixels, never scaled by stride or dilation; one offset
- * group shared by all input channels.
+ * offsets are in input pixels, never scaled by stride or dilation; group g's
+ * offsets are the 2K^2 consecutive channels starting at 2gK^2 (and its mask
+ * the K^2 channels from gK^2), in the per-group order of the one-group layout.
  *
  * Arithmetic: inputs arrive as float (already rounded to the element type the
  * caller uses); every position, weight, product and sum is formed in double.
@@ -42,7 +48,7 @@
  * conversion to an integer, so NaN, +-Inf and huge offsets contribute zero.
  *
  * All pointers are host pointers to contiguous row-major arrays:
- *   x[B,Cin,H,W], offset[B,2K^2,Ho,Wo], mask[B,K^2,Ho,Wo] or NULL,
+ *   x[B,Cin,H,W], offset[B,2GK^2,Ho,Wo], mask[B,GK^2,Ho,Wo] or NULL,
  *   weight[Cout,Cin,K,K], bias[Cout] or NULL.
  * Return value: 0 on success, -1 on an invalid argument.
  */
@@ -57,6 +63,7 @@ extern "C" {
 
 typedef struct oracle_desc {
   int64_t B, Cin, H, W, Cout, K, stride, pad, dilation;
+  int64_t groups;   /* offset groups G (0 means 1); Cin must be a multiple of G */
 } oracle_desc;
 
 /* Ho = floor((H + 2*pad - dilation*(K-1) - 1) / stride) + 1, likewise Wo. */

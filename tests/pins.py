@@ -17,6 +17,9 @@ What each pin reduces to (no pin restates the oracle's own formula):
   p9  general offsets        -> torch grid_sample (bilinear, zero padding, align_corners)
                                 per kernel point, then a contraction with W
   p10 NaN / Inf / 1e30 offsets -> that sample contributes zero
+  p11 offset groups           -> the sum over groups of one-group problems (each channel slice
+                                with its own offset and mask slice) via the grid_sample
+                                formulation; G copies of one offset field -> one group
   golden                      -> hand-worked examples in tests/golden/
 """
 
@@ -293,6 +296,32 @@ def pin_p10_nonfinite_offsets(lib):
     _close(a_bad, a_ref, 1e-12, "p10 abs terms")
 
 
+def pin_p11_offset_groups(lib):
+    rng = np.random.default_rng(21)
+    cases = [(2, 6, 3, 7, 8, 4, 3, 1, 1, 1), (1, 4, 2, 9, 6, 3, 2, 2, 0, 1), (2, 4, 4, 6, 7, 2, 3, 1, 2, 2)]
+    for (B, Cin, G, H, W, Cout, K, s, p, d) in cases:
+        KK = K * K
+        Cg = Cin // G
+        for mask in (True, False):
+            x, _, _, w, b, Ho, Wo = rand_case(rng, B, Cin, H, W, Cout, K, s, p, d, mask=mask, bias=mask)
+            off = (rng.standard_normal((B, 2 * KK * G, Ho, Wo)) * 2.0).astype(np.float32)
+            m = rng.uniform(0.0, 1.0, (B, KK * G, Ho, Wo)).astype(np.float32) if mask else None
+            y = oracle.forward(x, off, w, b, s, p, d, mask=m, with_abs=False, lib_path=lib)
+            # channels [g*Cg, (g+1)*Cg) use offset channels [2*KK*g, 2*KK*(g+1)) and mask [KK*g, KK*(g+1))
+            ref = b[None, :, None, None].astype(np.float64) if b is not None else 0.0
+            for g in range(G):
+                ref = ref + grid_sample_formulation(
+                    x[:, g * Cg:(g + 1) * Cg], off[:, 2 * KK * g:2 * KK * (g + 1)],
+                    None if m is None else m[:, KK * g:KK * (g + 1)], w[:, g * Cg:(g + 1) * Cg], None, s, p, d)
+            _close(y, ref, 1e-10, f"p11 groups {(B, Cin, G, H, W, Cout, K, s, p, d)} mask={mask}")
+            # every group given the same field: the one-group result, exactly
+            off1, m1 = off[:, :2 * KK], None if m is None else m[:, :KK]
+            yg = oracle.forward(x, np.tile(off1, (1, G, 1, 1)), w, b, s, p, d,
+                                mask=None if m1 is None else np.tile(m1, (1, G, 1, 1)), with_abs=False, lib_path=lib)
+            y1 = oracle.forward(x, off1, w, b, s, p, d, mask=m1, with_abs=False, lib_path=lib)
+            assert np.array_equal(yg, y1), "p11 replicated groups differ from one group"
+
+
 def pin_golden(lib):
     with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
         g = json.load(f)
@@ -318,4 +347,4 @@ def pin_golden(lib):
 
 ALL_PINS = [pin_p1_zero_offsets, pin_p2_integer_offsets, pin_p3_bilinear_field, pin_p4_all_outside,
             pin_p5_linear_in_mask, pin_p6_mask_absent, pin_p7_half_offsets, pin_p8_constant_input,
-            pin_p9_grid_sample, pin_p10_nonfinite_offsets, pin_golden]
+            pin_p9_grid_sample, pin_p10_nonfinite_offsets, pin_p11_offset_groups, pin_golden]

@@ -20,10 +20,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # (name, [(old, new), ...]) -- each old string must occur in the source.
 MUTANTS = [
-    ("swap_dy_dx", [("const double dy = offset[((b * 2 * KK + 2 * k) *",
-                     "const double dy = offset[((b * 2 * KK + 2 * k + 1) *"),
-                    ("const double dx = offset[((b * 2 * KK + 2 * k + 1) *",
-                     "const double dx = offset[((b * 2 * KK + 2 * k) *")]),
+    ("swap_dy_dx", [("const double dy = offset[((b * 2 * KK * G + 2 * gk) *",
+                     "const double dy = offset[((b * 2 * KK * G + 2 * gk + 1) *"),
+                    ("const double dx = offset[((b * 2 * KK * G + 2 * gk + 1) *",
+                     "const double dx = offset[((b * 2 * KK * G + 2 * gk) *")]),
     ("ceil_upper_corner", [("const double yy = y0 + dy;",
                             "const double yy = (dy == 0) ? y0 : std::ceil(py);")]),
     ("truncate_not_floor", [("const double y0 = std::floor(py);", "const double y0 = std::trunc(py);")]),
@@ -43,10 +43,15 @@ MUTANTS = [
     ("inside_bound_off_by_one", [("xx <= static_cast<double>(W - 1)", "xx < static_cast<double>(W - 1)")]),
     ("drop_bias", [("y = static_cast<double>(bias[o]);", "y = 0.0;")]),
     ("abs_terms_signed", [("a += std::fabs(term);", "a += term;")]),
-    ("mask_kernel_point_reversed", [("mask[((b * KK + k) * Ho + oy) * Wo + ox]",
-                                     "mask[((b * KK + (KK - 1 - k)) * Ho + oy) * Wo + ox]")]),
-    ("offset_batch_stride", [("offset[((b * 2 * KK + 2 * k) *", "offset[((b * KK + 2 * k) *"),
-                             ("offset[((b * 2 * KK + 2 * k + 1) *", "offset[((b * KK + 2 * k + 1) *")]),
+    ("mask_kernel_point_reversed", [("mask[((b * KK * G + gk) * Ho + oy) * Wo + ox]",
+                                     "mask[((b * KK * G + g * KK + (KK - 1 - k)) * Ho + oy) * Wo + ox]")]),
+    ("offset_batch_stride", [("offset[((b * 2 * KK * G + 2 * gk) *", "offset[((b * KK * G + 2 * gk) *"),
+                             ("offset[((b * 2 * KK * G + 2 * gk + 1) *", "offset[((b * KK * G + 2 * gk + 1) *")]),
+    ("group_of_channel_modulo", [("const int64_t g = c / Cg;", "const int64_t g = c % G;")]),
+    ("groups_interleaved_by_kernel_point", [("const int64_t gk = g * KK + k;", "const int64_t gk = k * G + g;")]),
+    ("group_batch_stride_dropped", [("offset[((b * 2 * KK * G + 2 * gk) *", "offset[((b * 2 * KK + 2 * gk) *"),
+                                    ("offset[((b * 2 * KK * G + 2 * gk + 1) *", "offset[((b * 2 * KK + 2 * gk + 1) *")]),
+    ("mask_ignores_group", [("mask[((b * KK * G + gk) * Ho + oy) * Wo + ox]", "mask[((b * KK * G + k) * Ho + oy) * Wo + ox]")]),
     ("x_channel_stride", [("x + ((b * d->Cin + c) * d->H) * d->W", "x + ((b * d->Cin + c) * d->W) * d->W")]),
 ]
 
