@@ -136,7 +136,7 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
     w = WORKLOADS[name]
     host = generate(w)
     g = {k: (None if v is None else v.cuda()) for k, v in host.items()}
-    desc = dcn.describe(g["x"], g["weight"], w.stride, w.pad, w.dilation)
+    desc = dcn.describe(g["x"], g["weight"], w.stride, w.pad, w.dilation, g["offset"])
     Ho, Wo = dcn.check_tensors(desc, g["x"], g["offset"], g["weight"], g["bias"], g["mask"])
     assert (Ho, Wo) == (w.Ho, w.Wo)
     nb = dcn.dcn_workspace_bytes(desc)
@@ -251,7 +251,8 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": f"{w.name}: B={w.B} Cin={w.Cin} {w.H}x{w.W} -> Cout={w.Cout} {Ho}x{Wo}, "
                                f"K={w.K} stride={w.stride} pad={w.pad} dilation={w.dilation}, "
-                               f"mask={'yes' if w.mask else 'no'}, bias={'yes' if w.bias else 'no'}",
+                               f"mask={'yes' if w.mask else 'no'}, bias={'yes' if w.bias else 'no'}"
+                               + (f", offset groups={w.groups}" if w.groups > 1 else ""),
                    "variant": variant, "plan": plan},
         "effective_gbps": round(gbps, 2),
         "frac_mfma_peak": round(tflops / (PEAK["bf16_mfma"] if w.dtype == "bf16" else PEAK["f32_mfma"]), 5),

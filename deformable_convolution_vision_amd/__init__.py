@@ -43,7 +43,7 @@ class Desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("in_channels", ctypes.c_int64), ("height", ctypes.c_int64),
                 ("width", ctypes.c_int64), ("out_channels", ctypes.c_int64),
                 ("kernel_size", ctypes.c_int64), ("stride", ctypes.c_int64), ("pad", ctypes.c_int64),
-                ("dilation", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("dilation", ctypes.c_int64), ("dtype", ctypes.c_int32), ("offset_groups", ctypes.c_int32)]
 
     def __repr__(self):
         return "Desc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -88,8 +88,8 @@ def dcn_status_str(status: int) -> str:
     return load_library().dcn_status_str(int(status)).decode()
 
 
-def make_desc(B, Cin, H, W, Cout, K, stride=1, pad=0, dilation=1, dtype=F32) -> Desc:
-    return Desc(B, Cin, H, W, Cout, K, stride, pad, dilation, dtype, 0)
+def make_desc(B, Cin, H, W, Cout, K, stride=1, pad=0, dilation=1, dtype=F32, offset_groups=1) -> Desc:
+    return Desc(B, Cin, H, W, Cout, K, stride, pad, dilation, dtype, offset_groups)
 
 
 def dcn_output_hw(desc: Desc) -> tuple[int, int]:
@@ -160,7 +160,9 @@ def dcn_forward_staged(desc: Desc, x, offset, mask, weight, bias, out, workspace
         raise DcnError(rc, "dcn_forward_staged")
 
 
-def describe(input, weight, stride=1, padding=0, dilation=1) -> Desc:
+def describe(input, weight, stride=1, padding=0, dilation=1, offset=None) -> Desc:
+    """Descriptor of a call; the offset groups follow from the offset's channel count
+    (2*G*K*K), as in torchvision, when offset is given."""
     if input.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {input.dtype}; use float32 or bfloat16")
     if input.dim() != 4 or weight.dim() != 4:
@@ -169,13 +171,20 @@ def describe(input, weight, stride=1, padding=0, dilation=1) -> Desc:
     Cout, Cin_w, K, K2 = weight.shape
     if Cin_w != Cin or K != K2:
         raise ValueError(f"weight {tuple(weight.shape)} does not match input {tuple(input.shape)}")
-    return make_desc(B, Cin, H, W, Cout, K, int(stride), int(padding), int(dilation), _DTYPES[input.dtype])
+    G = 1
+    if offset is not None:
+        if offset.dim() != 4 or offset.shape[1] % (2 * K * K) != 0 or offset.shape[1] == 0:
+            raise ValueError(f"offset must have 2*G*K*K channels, got {tuple(offset.shape)}")
+        G = offset.shape[1] // (2 * K * K)
+        if Cin % G != 0:
+            raise ValueError(f"{Cin} input channels do not split into {G} offset groups")
+    return make_desc(B, Cin, H, W, Cout, K, int(stride), int(padding), int(dilation), _DTYPES[input.dtype], G)
 
 
 def check_tensors(desc: Desc, input, offset, weight, bias, mask) -> tuple[int, int]:
     """Shape, dtype, device and contiguity checks; returns (Ho, Wo)."""
     Ho, Wo = dcn_output_hw(desc)
-    KK = desc.kernel_size ** 2
+    KK = desc.kernel_size ** 2 * max(desc.offset_groups, 1)
     expect = {"offset": (offset, (desc.batch, 2 * KK, Ho, Wo)),
               "mask": (mask, (desc.batch, KK, Ho, Wo)),
               "bias": (bias, (desc.out_channels,))}
@@ -197,11 +206,12 @@ def deform_conv2d(input, offset, weight, bias=None, stride=1, padding=0, dilatio
                   out=None, workspace=None):
     """Deformable convolution forward on the GPU (torchvision's argument order).
 
-    input [B,Cin,H,W], offset [B,2K^2,Ho,Wo] (channel 2k = dy, 2k+1 = dx of kernel
-    point k = i*K + j), weight [Cout,Cin,K,K], bias [Cout] or None, mask
-    [B,K^2,Ho,Wo] or None.  float32 or bfloat16, contiguous, on one GPU.
+    input [B,Cin,H,W], offset [B,2GK^2,Ho,Wo] (channel 2(gK^2+k) = dy, 2(gK^2+k)+1 =
+    dx of kernel point k = i*K + j for offset group g; G = 1 by default), weight
+    [Cout,Cin,K,K], bias [Cout] or None, mask [B,GK^2,Ho,Wo] or None.  float32 or
+    bfloat16, contiguous, on one GPU.
     """
-    desc = describe(input, weight, stride, padding, dilation)
+    desc = describe(input, weight, stride, padding, dilation, offset)
     Ho, Wo = check_tensors(desc, input, offset, weight, bias, mask)
     if out is None:
         out = torch.empty((desc.batch, desc.out_channels, Ho, Wo), dtype=input.dtype, device=input.device)

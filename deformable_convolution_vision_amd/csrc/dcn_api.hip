@@ -55,7 +55,7 @@ struct Plan {
 };
 
 bool geometry_ok(const dcn_desc* d) {
-  if (d == nullptr || d->reserved != 0) return false;
+  if (d == nullptr || d->offset_groups < 0) return false;
   if (d->batch < 0 || d->out_channels < 0) return false;
   if (d->in_channels < 1 || d->height < 1 || d->width < 1 || d->kernel_size < 1) return false;
   if (d->stride < 1 || d->dilation < 1 || d->pad < 0) return false;
@@ -65,7 +65,19 @@ bool geometry_ok(const dcn_desc* d) {
       d->pad > big || d->dilation > big || d->batch > big || d->in_channels > big ||
       d->out_channels > big)
     return false;
+  if (d->offset_groups > 1 && d->in_channels % d->offset_groups != 0) return false;
   return true;
+}
+
+int64_t offset_groups(const dcn_desc* d) { return d->offset_groups > 1 ? d->offset_groups : 1; }
+
+// Variants that take offset groups: the tile kernels, when every 16-byte channel
+// vector of the staged copy lies in one group.
+bool groups_fit(const dcn_desc* d, int variant) {
+  if (offset_groups(d) == 1) return true;
+  const dcn::VariantInfo& vi = dcn::variant_info(variant);
+  if (!vi.staged || variant == dcn::V_BOX_BF16_M128 || variant == dcn::V_BOX_BF16_M256) return false;
+  return (d->in_channels / offset_groups(d)) % (vi.is_bf16 ? 8 : 4) == 0;
 }
 
 // Tile plan of the box kernel: the output tile (TH x TW pixels of one image by
@@ -170,12 +182,13 @@ bool direct_fits(const dcn_desc* d, int64_t HoWo) {
 // Pick the kernel variant for a valid descriptor.
 int choose_variant(const dcn_desc* d, int64_t N, int64_t Ho, int64_t Wo, BoxPlan* bp) {
   const int64_t M = d->out_channels;
+  const bool grouped = offset_groups(d) > 1;   // tile kernels only
   // tiny reductions (an RGB first layer): the column fits in registers
-  if (direct_fits(d, Ho * Wo))
+  if (!grouped && direct_fits(d, Ho * Wo))
     return d->dtype == DCN_F32 ? dcn::V_DIRECT_F32 : dcn::V_DIRECT_BF16;
   if (d->dtype == DCN_F32) return M <= 64 ? dcn::V_TILE_F32_M64_N64 : dcn::V_TILE_F32_M128_N64;
   // the box kernel for channel counts where a 32-channel chunk is mostly real data
-  if (d->in_channels >= 24 && M >= 64 && plan_box(d, Ho, Wo, 0, bp))
+  if (!grouped && d->in_channels >= 24 && M >= 64 && plan_box(d, Ho, Wo, 0, bp))
     return bp->fm == 2 ? dcn::V_BOX_BF16_M128 : dcn::V_BOX_BF16_M256;
   if (M <= 64) return dcn::V_TILE_BF16_M64_N64;
   // enough workgroups to cover 256 CUs with the wider tile?
@@ -194,6 +207,7 @@ int compute_plan(const dcn_desc* d, Plan* p) {
   const int64_t Cout = d->out_channels, K = d->kernel_size, KK = K * K;
   const int64_t HoWo = p->Ho * p->Wo;
   const int64_t N = B * HoWo;
+  const int64_t G = offset_groups(d);
   p->variant = choose_variant(d, N, p->Ho, p->Wo, &p->box);
   // DCN_VARIANT=<name> pins the kernel variant (tile sweeps and tests); an
   // unknown name or one built for the other dtype is rejected.
@@ -211,12 +225,13 @@ int compute_plan(const dcn_desc* d, Plan* p) {
       p->variant = found;
     }
   }
+  if (!groups_fit(d, p->variant)) return DCN_E_UNSUPPORTED;
   const dcn::VariantInfo& vi = dcn::variant_info(p->variant);
   p->Cp = round_up(Cin, vi.ck);
   p->Mp = round_up(Cout > 0 ? Cout : 1, vi.mt);
   // element-count limits (int32 indexing inside the kernels)
   const double lim = static_cast<double>(kMaxElems);
-  if (static_cast<double>(B) * Cin * H * W > lim || static_cast<double>(B) * 2 * KK * HoWo > lim ||
+  if (static_cast<double>(B) * Cin * H * W > lim || static_cast<double>(B) * 2 * KK * G * HoWo > lim ||
       static_cast<double>(Cout) * Cin * KK > lim || static_cast<double>(B) * Cout * HoWo > lim ||
       static_cast<double>(B) * H * W * p->Cp > lim || static_cast<double>(p->Mp) * KK * p->Cp > lim ||
       static_cast<double>(N) + vi.nt > lim)
@@ -332,6 +347,8 @@ FusedArgs fused_args(const dcn_desc* d, const Plan& p, const void* x, const void
   a.stride = static_cast<int>(d->stride);
   a.pad = static_cast<int>(d->pad);
   a.dil = static_cast<int>(d->dilation);
+  a.G = static_cast<int>(offset_groups(d));
+  a.Cg = static_cast<int>(d->in_channels / a.G);
   a.Ho = static_cast<int>(p.Ho);
   a.Wo = static_cast<int>(p.Wo);
   a.HoWo = a.Ho * a.Wo;
@@ -411,7 +428,8 @@ extern "C" int dcn_plan_describe(const dcn_desc* desc, char* buf, size_t len) {
                   static_cast<long long>(desc->batch) * p.box.tiles_per_img * (p.Mp / (64 * p.box.fm)),
                   p.box.box_px, p.box.split ? "split" : "paired", p.ws_bytes);
   } else {
-    std::snprintf(buf, len, "%s tile=%d px x %d ch, ws=%zu B", vi.name, vi.nt, vi.mt, p.ws_bytes);
+    std::snprintf(buf, len, "%s tile=%d px x %d ch, offset groups=%lld, ws=%zu B", vi.name, vi.nt, vi.mt,
+                  static_cast<long long>(offset_groups(desc)), p.ws_bytes);
   }
   return DCN_OK;
 }

@@ -14,12 +14,13 @@ struct FusedArgs {
   const void* wp;      // repacked weight: [Mp][K*K][Cp], zero rows/channels beyond Cout/Cin
   const void* x;       // x as given, [B][Cin][H][W] (direct variants only)
   const void* w;       // weight as given, [Cout][Cin][K][K] (direct variants only)
-  const void* offset;  // [B][2K^2][Ho][Wo]
-  const void* mask;    // [B][K^2][Ho][Wo] or null
+  const void* offset;  // [B][2G K^2][Ho][Wo]
+  const void* mask;    // [B][G K^2][Ho][Wo] or null
   const void* bias;    // [Cout] or null
   void* out;           // [B][Cout][Ho][Wo]
   int B, Cin, H, W, Cp, Cout, K, KK, stride, pad, dil, Ho, Wo, HoWo, N;
   int m_tiles, n_tiles;
+  int G, Cg;           // offset groups and channels per group (1 and Cin for one group)
 };
 
 struct StageArgs {

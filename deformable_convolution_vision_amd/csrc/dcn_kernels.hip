@@ -357,17 +357,21 @@ __global__ __launch_bounds__(kThreads) void dcn_fused_kernel(FusedArgs a) {
   int c_off[C::GU][4];
   float c_w[C::GU][4];
 
-  auto corners = [&](int k) {
+  // Offset group of a unit in channel chunk cc: every 16-byte unit lies in one group
+  // (Cg is a multiple of VEC); channels past Cin (zero weights) use the last group.
+  auto corners = [&](int k, int cc) {
     const int i = k / a.K, j = k - (k / a.K) * a.K;
 #pragma unroll
     for (int u = 0; u < C::GU; ++u) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) { c_off[u][q] = -1; c_w[u][q] = 0.f; }
       if (!g_on[u]) continue;
-      const int ob = (g_b[u] * 2 * KK + 2 * k) * a.HoWo + g_rem[u];
+      const int grp = a.G == 1 ? 0 : min((cc * C::CK + g_sub[u] * C::VEC) / a.Cg, a.G - 1);
+      const int gk = grp * KK + k;
+      const int ob = (g_b[u] * 2 * KK * a.G + 2 * gk) * a.HoWo + g_rem[u];
       const float dy = load_scalar<BF16>(a.offset, ob);
       const float dx = load_scalar<BF16>(a.offset, ob + a.HoWo);
-      const float m = a.mask ? load_scalar<BF16>(a.mask, (g_b[u] * KK + k) * a.HoWo + g_rem[u]) : 1.f;
+      const float m = a.mask ? load_scalar<BF16>(a.mask, (g_b[u] * KK * a.G + gk) * a.HoWo + g_rem[u]) : 1.f;
       // integer and fractional parts of the offset are exact in fp32, so the
       // neighbour rows/columns and the interpolation fractions are exact too.
       const float fy = floorf(dy), fx = floorf(dx);
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void dcn_fused_kernel(FusedArgs a) {
   // global loads for chunk q into registers
   auto issue = [&](int q) {
     const int k = q / cch, cc = q - (q / cch) * cch;
-    if (cc == 0) corners(k);
+    if (cc == 0 || a.G > 1) corners(k, cc);
 #pragma unroll
     for (int u = 0; u < C::GU; ++u) {
       const int ch = cc * C::CK + g_sub[u] * C::VEC;

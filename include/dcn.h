@@ -80,12 +80,20 @@ enum dcn_status {
 /* Problem descriptor.  B >= 0 and Cout >= 0 (0 means an empty output: the
  * call succeeds and launches nothing); Cin, H, W, K, stride, dilation >= 1;
  * pad >= 0.  One square kernel, one stride, one pad and one dilation for both
- * axes, as in torchvision's deform_conv2d call; one offset group. */
+ * axes, as in torchvision's deform_conv2d call.
+ *
+ * Offset groups (the csdn.net tags page "可变形卷积：Deformable ConvNets",
+ * section Deformable Group): the input channels are split into G consecutive
+ * groups of Cin/G channels, and group g samples at its own offsets
+ * offset[b, 2(g*K*K + k) + {0: dy, 1: dx}] and mask[b, g*K*K + k], so offset has
+ * 2*G*K*K channels and mask G*K*K.  offset_groups 0 or 1 means one group (the
+ * layout below).  G > 1 needs Cin % G == 0 (else DCN_E_ARG) and Cin/G a multiple
+ * of 8 (bf16) or 4 (fp32) (else DCN_E_UNSUPPORTED). */
 typedef struct dcn_desc {
   int64_t batch, in_channels, height, width, out_channels;
   int64_t kernel_size, stride, pad, dilation;
-  int32_t dtype;     /* enum dcn_dtype */
-  int32_t reserved;  /* must be 0 */
+  int32_t dtype;          /* enum dcn_dtype */
+  int32_t offset_groups;  /* G; 0 or 1 for one group */
 } dcn_desc;
 
 /* Output size of the strided, padded, dilated window (as for a regular

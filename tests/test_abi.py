@@ -93,7 +93,8 @@ def test_workspace_is_deterministic_and_covers_staged_copy(lib):
 
 BAD = [
     dict(batch=-1), dict(in_channels=0), dict(height=0), dict(width=0), dict(kernel_size=0),
-    dict(stride=0), dict(dilation=0), dict(pad=-1), dict(out_channels=-2), dict(reserved=7),
+    dict(stride=0), dict(dilation=0), dict(pad=-1), dict(out_channels=-2), dict(offset_groups=-1),
+    dict(offset_groups=3),                                    # 8 input channels do not split in 3
     dict(kernel_size=9, height=4, width=4, pad=0),            # window larger than the padded input
 ]
 
@@ -179,6 +180,33 @@ def test_forced_variant(lib, monkeypatch):
     assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
     monkeypatch.setenv("DCN_VARIANT", "direct_bf16")                # 64 input channels: too many
     assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+
+
+def test_offset_groups_planning(lib, monkeypatch):
+    """G > 1: tile kernels only, Cin % G == 0 (else an argument error) and Cin/G a
+    multiple of the 16-byte channel vector (8 bf16, 4 fp32; else unsupported)."""
+    n = ctypes.c_size_t()
+    for dt, vec in ((dcn.BF16, 8), (dcn.F32, 4)):
+        for Cin, G in ((256, 4), (64, 2), (48, 3), (64, 16), (16, 4), (12, 3), (3, 3)):
+            desc = dcn.make_desc(2, Cin, 20, 24, 70, 3, 1, 1, 1, dt, G)
+            rc = lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+            if (Cin // G) % vec == 0:
+                assert rc == dcn.OK, (dt, Cin, G)
+                assert dcn.dcn_variant_name(desc).startswith("tile_"), (dt, Cin, G)
+                assert f"offset groups={G}" in dcn.dcn_plan_describe(desc)
+            else:
+                assert rc == dcn.E_UNSUPPORTED, (dt, Cin, G)
+    desc = dcn.make_desc(2, 64, 20, 24, 70, 3, 1, 1, 1, dcn.BF16, 3)        # 64 channels in 3 groups
+    assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_ARG
+    for G in (0, 1):                                                         # one group either way
+        desc = dcn.make_desc(2, 256, 40, 40, 256, 3, 1, 1, 1, dcn.BF16, G)
+        assert dcn.dcn_variant_name(desc).startswith("box_")
+    desc = dcn.make_desc(2, 256, 40, 40, 256, 3, 1, 1, 1, dcn.BF16, 4)
+    for v in ("box_bf16_m256", "direct_bf16"):
+        monkeypatch.setenv("DCN_VARIANT", v)
+        assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+    monkeypatch.setenv("DCN_VARIANT", "tile_bf16_m128_n32")
+    assert dcn.dcn_variant_name(desc) == "tile_bf16_m128_n32"
 
 
 def test_small_reductions_take_the_direct_kernel_without_workspace(lib):

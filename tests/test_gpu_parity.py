@@ -42,7 +42,7 @@ def test_named_workload_sampled(name):
 
 def variant_of(w):
     return dcn.dcn_variant_name(dcn.make_desc(w.B, w.Cin, w.H, w.W, w.Cout, w.K, w.stride, w.pad, w.dilation,
-                                              dcn.F32 if w.dtype == "f32" else dcn.BF16))
+                                              dcn.F32 if w.dtype == "f32" else dcn.BF16, w.groups))
 
 
 EDGE = [
@@ -202,3 +202,42 @@ def test_box_role_placement(variant, tile, roles, monkeypatch):
         print(f"[gpu-test] {shape} {plan}", flush=True)
         assert ("roles=split" if roles == "1" else "roles=paired") in plan
         full_parity(w)
+
+
+GROUPED = [
+    ("g2_k3", dict(B=2, Cin=64, H=11, W=13, Cout=70, K=3, s=1, p=1, d=1, G=2, offset="normal:2")),
+    ("g4_s2", dict(B=1, Cin=32, H=15, W=17, Cout=40, K=3, s=2, p=1, d=1, G=4, offset="normal:1.5")),
+    ("g3_nomask", dict(B=2, Cin=48, H=9, W=10, Cout=33, K=3, s=1, p=2, d=2, G=3, offset="uniform:4",
+                       mask=None)),
+    ("g2_k1", dict(B=2, Cin=16, H=9, W=7, Cout=24, K=1, s=1, p=0, d=1, G=2)),
+    ("g8_k5", dict(B=1, Cin=64, H=12, W=14, Cout=130, K=5, s=1, p=2, d=1, G=8, offset="normal:2")),
+    ("g4_cout300", dict(B=3, Cin=96, H=8, W=12, Cout=300, K=3, s=1, p=1, d=1, G=4, offset="normal:1.5")),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name,kw", GROUPED, ids=[e[0] for e in GROUPED])
+def test_offset_groups(name, kw, dtype):
+    kw = dict(kw)
+    g = {k: kw.pop(k) for k in ("B", "Cin", "H", "W", "Cout", "K", "s", "p", "d", "G")}
+    w = make(name, dtype, g["B"], g["Cin"], g["H"], g["W"], g["Cout"], g["K"], g["s"], g["p"], g["d"],
+             seed=zlib.crc32(name.encode()) % 1000, groups=g["G"], **kw)
+    inp = generate(w)
+    desc = dcn.describe(inp["x"], inp["weight"], w.stride, w.pad, w.dilation, inp["offset"])
+    assert desc.offset_groups == g["G"]
+    print(f"[gpu-test] {w} plan {dcn.dcn_plan_describe(desc)}", flush=True)
+    full_parity(w, inp)
+
+
+@pytest.mark.parametrize("variant", ["tile_f32_m64_n64", "tile_f32_m128_n64", "tile_bf16_m64_n64",
+                                     "tile_bf16_m128_n64", "tile_bf16_m128_n32", "tile_bf16_m256_n64"])
+def test_offset_groups_every_tile_variant(variant, monkeypatch):
+    dtype = "bf16" if "bf16" in variant else "f32"
+    monkeypatch.setenv("DCN_VARIANT", variant)
+    w = make(f"groups_{variant}", dtype, 2, 64, 9, 10, 260, 3, 2, 1, 1, offset="normal:2", seed=7, groups=4)
+    full_parity(w)
+
+
+def test_offset_groups_sampled_c4_layer():
+    print(f"[gpu-test] variant {variant_of(WORKLOADS['c4_g4'])}", flush=True)
+    sampled_parity(WORKLOADS["c4_g4"])
