@@ -72,12 +72,16 @@ bool geometry_ok(const dcn_desc* d) {
 int64_t offset_groups(const dcn_desc* d) { return d->offset_groups > 1 ? d->offset_groups : 1; }
 
 // Variants that take offset groups: the tile kernels, when every 16-byte channel
-// vector of the staged copy lies in one group.
+// vector of the staged copy lies in one group; the box kernel for 3x3 when every
+// 32-channel chunk does.
 bool groups_fit(const dcn_desc* d, int variant) {
   if (offset_groups(d) == 1) return true;
   const dcn::VariantInfo& vi = dcn::variant_info(variant);
-  if (!vi.staged || variant == dcn::V_BOX_BF16_M128 || variant == dcn::V_BOX_BF16_M256) return false;
-  return (d->in_channels / offset_groups(d)) % (vi.is_bf16 ? 8 : 4) == 0;
+  const int64_t Cg = d->in_channels / offset_groups(d);
+  if (variant == dcn::V_BOX_BF16_M128 || variant == dcn::V_BOX_BF16_M256)
+    return d->kernel_size == 3 && Cg % 32 == 0;
+  if (!vi.staged) return false;
+  return Cg % (vi.is_bf16 ? 8 : 4) == 0;
 }
 
 // Tile plan of the box kernel: the output tile (TH x TW pixels of one image by
@@ -111,7 +115,9 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
     for (int fn : {4, 6, 8, 10}) {
       if (fm == 4 && fn > 6) continue;
       const int NT = 16 * fn;
-      const int box_px = dcn::box_capacity_px(fn);
+      const bool grouped = offset_groups(d) > 1;
+      if (grouped && !dcn::box_groups_supported(fm, fn)) continue;
+      const int box_px = dcn::box_capacity_px(fn, grouped);
       if (box_px < 64) continue;
       for (int TH = 1; TH <= 16; ++TH) {
         for (int dw = 0; dw < (want_fn ? NT : 3); ++dw) {
@@ -182,13 +188,15 @@ bool direct_fits(const dcn_desc* d, int64_t HoWo) {
 // Pick the kernel variant for a valid descriptor.
 int choose_variant(const dcn_desc* d, int64_t N, int64_t Ho, int64_t Wo, BoxPlan* bp) {
   const int64_t M = d->out_channels;
-  const bool grouped = offset_groups(d) > 1;   // tile kernels only
+  const bool grouped = offset_groups(d) > 1;
   // tiny reductions (an RGB first layer): the column fits in registers
   if (!grouped && direct_fits(d, Ho * Wo))
     return d->dtype == DCN_F32 ? dcn::V_DIRECT_F32 : dcn::V_DIRECT_BF16;
   if (d->dtype == DCN_F32) return M <= 64 ? dcn::V_TILE_F32_M64_N64 : dcn::V_TILE_F32_M128_N64;
   // the box kernel for channel counts where a 32-channel chunk is mostly real data
-  if (!grouped && d->in_channels >= 24 && M >= 64 && plan_box(d, Ho, Wo, 0, bp))
+  // (offset groups: 3x3 with whole 32-channel chunks per group)
+  const bool box_groups_ok = !grouped || (d->kernel_size == 3 && (d->in_channels / offset_groups(d)) % 32 == 0);
+  if (box_groups_ok && d->in_channels >= 24 && M >= 64 && plan_box(d, Ho, Wo, 0, bp))
     return bp->fm == 2 ? dcn::V_BOX_BF16_M128 : dcn::V_BOX_BF16_M256;
   if (M <= 64) return dcn::V_TILE_BF16_M64_N64;
   // enough workgroups to cover 256 CUs with the wider tile?
@@ -423,10 +431,12 @@ extern "C" int dcn_plan_describe(const dcn_desc* desc, char* buf, size_t len) {
   const dcn::VariantInfo& vi = dcn::variant_info(p.variant);
   if (is_box(p.variant)) {
     std::snprintf(buf, len,
-                  "%s tile=%dx%d px (%d slots) x %d ch, tiles=%lld, box_px=%d, roles=%s, ws=%zu B",
+                  "%s tile=%dx%d px (%d slots) x %d ch, tiles=%lld, box_px=%d, roles=%s, offset groups=%lld, "
+                  "ws=%zu B",
                   vi.name, p.box.TH, p.box.TW, 16 * p.box.fn, 64 * p.box.fm,
                   static_cast<long long>(desc->batch) * p.box.tiles_per_img * (p.Mp / (64 * p.box.fm)),
-                  p.box.box_px, p.box.split ? "split" : "paired", p.ws_bytes);
+                  p.box.box_px, p.box.split ? "split" : "paired", static_cast<long long>(offset_groups(desc)),
+                  p.ws_bytes);
   } else {
     std::snprintf(buf, len, "%s tile=%d px x %d ch, offset groups=%lld, ws=%zu B", vi.name, vi.nt, vi.mt,
                   static_cast<long long>(offset_groups(desc)), p.ws_bytes);

@@ -65,11 +65,13 @@ struct CEnt {
 constexpr int kColBufs = 3;      // column-tile ring: produced at step s, read at s+1, multiplied at s+2
 constexpr int kZeroB = 128;      // zero bytes after each box buffer: the source of samples that read nothing
 
-template <int FN>
+// GRP: offset groups (one corner table per group, two tables in LDS: the consumers
+// fill the next group's table while the current group's chunks run)
+template <int FN, bool GRP = false>
 struct BoxCfg {
   static constexpr int NT = 16 * FN;
   static constexpr int COL_BYTES = kColBufs * NT * kCOLB;
-  static constexpr int CTAB_BYTES = kBoxMaxKK * NT * 16;
+  static constexpr int CTAB_BYTES = (GRP ? 2 : 1) * kBoxMaxKK * NT * 16;
   // what is left of the LDS, split into two box buffers, in whole 64-pixel groups
   // (each of the four producer waves copies 16-pixel blocks, every block of a group)
   static constexpr int BOX_PX = ((kLdsBudget - COL_BYTES - CTAB_BYTES - 2 * kZeroB - 64) / (2 * kPXB)) / 64 * 64;
@@ -186,10 +188,11 @@ __device__ __forceinline__ void lds_barrier_keep() {
 
 }  // namespace
 
-template <int FM, int FN, int KKT>
+template <int FM, int FN, int KKT, bool GRP>
 __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
-  using Cfg = BoxCfg<FN>;
+  using Cfg = BoxCfg<FN, GRP>;
   const FusedArgs& a = ba.f;
+  static_assert(!GRP || KKT == 9, "offset groups: 3x3 only");
   static_assert(FM % 2 == 0 && FN % 2 == 0, "whole 32x32 MFMA blocks per wave");
   constexpr int TM = FM / 2, TN = FN / 2;   // 32x32 output blocks per consumer wave
   constexpr int WM = 16 * FM;         // rows per consumer wave
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   constexpr int BOXB = Cfg::BOX_PX * kPXB;
 
   __shared__ __attribute__((aligned(16))) unsigned char col[Cfg::COL_BYTES];
-  __shared__ __attribute__((aligned(16))) CEnt ctab[kBoxMaxKK * NT];
+  __shared__ __attribute__((aligned(16))) CEnt ctab[(GRP ? 2 : 1) * kBoxMaxKK * NT];
   __shared__ __attribute__((aligned(16))) unsigned char box0[BOXB + kZeroB];
   __shared__ __attribute__((aligned(16))) unsigned char box1[BOXB + kZeroB];
 
@@ -229,6 +232,14 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   const int m0 = mt * MT;
   const int nCC = Cp / kCK;
   const int S = nCC * KK;
+  // offset groups (GRP): NG groups of cpg chunks each; group g's corner table is
+  // table g % 2
+  const int NG = GRP ? a.G : 1;
+  const int cpg = GRP ? a.Cg / kCK : nCC;
+  auto table_of_chunk = [&](int cc) __attribute__((always_inline)) -> CEnt* {
+    if constexpr (GRP) return ctab + ((cc / cpg) & 1) * (kBoxMaxKK * NT);
+    else return ctab;
+  };
 
   const unsigned char* xs = reinterpret_cast<const unsigned char*>(a.xs);
   const unsigned char* wp = reinterpret_cast<const unsigned char*>(a.wp);
@@ -256,8 +267,9 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   };
   // Weight fragments in two sets of G named slots: chunks G*g .. G*g+G-1 live in set
   // p for even g and in set q for odd g (G = 4 for the smaller tiles; G = 2 where
-  // 2*G*FM fragments would not fit next to the accumulators and column fragments).
-  constexpr int G = (FM * FN <= 16) ? 4 : 2;
+  // 2*G*FM fragments would not fit next to the accumulators and column fragments, and
+  // with offset groups, whose table work adds to the consumers' registers).
+  constexpr int G = (FM * FN <= 16 && !GRP) ? 4 : 2;
   AFrag p0{}, p1{}, p2{}, p3{}, q0{}, q1{}, q2{}, q3{};
   // weights for chunks c0 .. c0+G-1 (past the end a valid chunk is re-read, so every
   // group issues the same loads)
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const int bh0 = (ba.TH - 1) * a.stride + (K - 1) * a.dil + 2;
     const int bw0 = (ba.TW - 1) * a.stride + (K - 1) * a.dil + 2;
     int mg = 0;
-    while ((bh0 + 2 * (mg + 1)) * (bw0 + 2 * (mg + 1)) <= Cfg::BOX_PX) ++mg;
+    while ((bh0 + 2 * (mg + 1)) * (bw0 + 2 * (mg + 1)) <= min(ba.box_px, Cfg::BOX_PX)) ++mg;
     by0 = max(oy0 * a.stride - a.pad - mg, -1);
     bx0 = max(ox0 * a.stride - a.pad - mg, -1);
     BH = max(min(bh0 + 2 * mg, a.H + 1 - by0), 1);
@@ -303,7 +315,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   constexpr int kPE = (kBoxMaxKK * NT + 255) / 256;
   // raw bf16 bits; every address first, then every load
   uint32_t ldy[kPE], ldx[kPE], lm[kPE];
-  if (consumer) {
+  // offsets and mask of group g (field g*KK + k of each kernel point k)
+  auto load_offsets = [&](int g) __attribute__((always_inline)) {
     int ob[kPE], mb[kPE];
 #pragma unroll
     for (int j = 0; j < kPE; ++j) {
@@ -313,11 +326,11 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       const int oy = oy0 + py, ox = ox0 + px;
       const bool ok = e < KK * NT && p < ntile && oy < a.Ho && ox < a.Wo;
       const int rem = ok ? oy * a.Wo + ox : 0;
-      const int kk = ok ? k : 0;
-      ob[j] = (b * 2 * KK + 2 * kk) * a.HoWo + rem;
+      const int gk = g * KK + (ok ? k : 0);
+      ob[j] = (b * 2 * KK * NG + 2 * gk) * a.HoWo + rem;
       // always a load (from the offsets when there is no mask, ignored below), so no
       // branch joins on a value still in flight
-      mb[j] = a.mask ? (b * KK + kk) * a.HoWo + rem : ob[j];
+      mb[j] = a.mask ? (b * KK * NG + gk) * a.HoWo + rem : ob[j];
     }
     const uint16_t* offs = reinterpret_cast<const uint16_t*>(a.offset);
     const uint16_t* msk = reinterpret_cast<const uint16_t*>(a.mask ? a.mask : a.offset);
@@ -327,7 +340,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       ldx[j] = offs[ob[j] + a.HoWo];
       lm[j] = msk[mb[j]];
     }
-  }
+  };
+  if (consumer) load_offsets(0);
 
   // ---- the producers' box-copy plan (with the box pixels outside the image zeroed),
   // then chunk 0 of the box
@@ -402,8 +416,9 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   if (!consumer) copy_box(0, box0);
 
   // ---- corner table (consumer waves): sampling positions, bilinear weights times
-  // the mask, and the byte offset of corner (y0, x0) in a box buffer
-  if (consumer) {
+  // the mask, and the byte offset of corner (y0, x0) in a box buffer, from the
+  // offsets load_offsets left in ldy/ldx/lm
+  auto build_table = [&](CEnt* tbl) __attribute__((always_inline)) {
 #pragma unroll
   for (int jj = 0; jj < kPE; ++jj) {
     const int e = rtid + jj * 256;
@@ -436,9 +451,10 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         ce.w23 = pk_bf16(ly * hx * m, ly * lx * m);
       }
     }
-    ctab[e] = ce;
+    tbl[e] = ce;
   }
-  }
+  };
+  if (consumer) build_table(ctab);
   // Drain: the producers' chunk-0 copy and the consumers' offset loads (the padded
   // entries' loads are never read, and a register they left pending would later make
   // a wait cover the weight loads too).
@@ -493,17 +509,37 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // `step_tail` tests each part.
     // Each step reloads the weight slot it has just multiplied with the chunk 2G
     // steps later, so the weight loads are spread evenly and arrive 2G-1 steps early.
+    // Offset groups: during the first chunk cc0 of group g the consumers fill group
+    // g+1's table (the other table, last read by group g-1's steps): its offset loads
+    // in step 9*cc0 (between barriers 9*cc0+1 and +2), its entries in step 9*cc0+2
+    // (barriers +3 to +4).  The producers first read it at step 7 of group g's last
+    // chunk, three barriers or more later.
+    auto table_work = [&](int c, auto phase) __attribute__((always_inline)) {
+      if constexpr (GRP) {
+        constexpr int ph = decltype(phase)::value;
+        const int cc = c / 9, kk = c - cc * 9;
+        if (kk != (ph == 0 ? 0 : 2)) return;
+        const int g = cc / cpg;
+        if (g * cpg != cc || g + 1 >= NG) return;
+        if constexpr (ph == 0) load_offsets(g + 1);
+        else build_table(ctab + ((g + 1) & 1) * (kBoxMaxKK * NT));
+      }
+    };
     auto step = [&](int c, AFrag& af, const BFrag& bc, BFrag& bn) __attribute__((always_inline)) {
+      table_work(c, std::integral_constant<int, 0>());
       bn = read_b(c + 1);
       mma(af, bc);
       af = load_a(min(c + 2 * G, S - 1));
+      table_work(c, std::integral_constant<int, 1>());
       lds_barrier();
     };
     auto step_tail = [&](int c, AFrag& af, const BFrag& bc, BFrag& bn) __attribute__((always_inline)) {
       if (c >= S) return;
+      table_work(c, std::integral_constant<int, 0>());
       if (c + 1 < S) bn = read_b(c + 1);
       mma(af, bc);
       if (c + 2 * G < S) af = load_a(c + 2 * G);
+      table_work(c, std::integral_constant<int, 1>());
       if (c + 2 < S) lds_barrier();
     };
     BFrag b0{}, b1{};
@@ -604,7 +640,20 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         ce_w23[k] = e.w23;
       }
     }
-    auto read_ce = [&](int k, PSet& f) __attribute__((always_inline)) {
+    // the entries of the nine taps from table tbl into registers (offset groups: at
+    // step 7 of a group's last chunk, when every entry of the current group is used)
+    auto load_ce_regs = [&](const CEnt* tbl) __attribute__((always_inline)) {
+      if constexpr (kCeRegs) {
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+          const CEnt e = tbl[k * NT + (ptid >> 2)];
+          ce_off[k] = e.off;
+          ce_w01[k] = e.w01;
+          ce_w23[k] = e.w23;
+        }
+      }
+    };
+    auto read_ce = [&](int k, PSet& f, const CEnt* tbl) __attribute__((always_inline)) {
       if constexpr (kCeRegs) {
         f.ce[0].off = ce_off[k];
         f.ce[0].yx = 0;
@@ -614,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 #pragma unroll
         for (int g = 0; g < GU; ++g)
           if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS)
-            f.ce[g] = __builtin_bit_cast(CEnt, reinterpret_cast<const uint4*>(ctab)[k * NT + ((ptid + g * 256) >> 2)]);
+            f.ce[g] = __builtin_bit_cast(CEnt, reinterpret_cast<const uint4*>(tbl)[k * NT + ((ptid + g * 256) >> 2)]);
       }
     };
     auto read_q = [&](const unsigned char* src, PSet& f) __attribute__((always_inline)) {
@@ -633,7 +682,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       }
     };
     // the global-path corner vectors of the step (chunk cc, tap k) whose table entries are in f
-    auto load_g = [&](int cc, int k, const PSet& f) __attribute__((always_inline)) {
+    auto load_g = [&](int cc, int k, const PSet& f, const CEnt* tbl) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
         if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
@@ -641,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
           gfl[g] = __ballot(ce.off == -1) != 0;
           if (gfl[g]) {
             const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(cc);
-            const int yx = kCeRegs ? ctab[k * NT + ((ptid + g * 256) >> 2)].yx : ce.yx;
+            const int yx = kCeRegs ? tbl[k * NT + ((ptid + g * 256) >> 2)].yx : ce.yx;
             const int y0 = (yx >> 16) - 1, x0 = (yx & 0xffff) - 1;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
@@ -706,11 +755,16 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         constexpr bool odd = decltype(parity)::value;
         const unsigned char* src = odd ? box1 : box0;
         unsigned char* dst = odd ? box0 : box1;
+        const CEnt* t_cur = table_of_chunk(cc);
+        const CEnt* t_nxt = table_of_chunk(cc + 1);
         static_for<0, 9>([&](auto kc) __attribute__((always_inline)) {
           constexpr int k = decltype(kc)::value;
           PSet& s0 = ((k + (odd ? 1 : 0)) & 1) == 0 ? X : Y;   // set of steps s and s+2
           PSet& s1 = ((k + (odd ? 1 : 0)) & 1) == 0 ? Y : X;   // set of step s+1
-          read_ce((k + 2) % 9, s0);
+          if constexpr (GRP && k == 7) {
+            if (cc + 1 < nCC && t_nxt != t_cur) load_ce_regs(t_nxt);
+          }
+          read_ce((k + 2) % 9, s0, t_cur);
           if constexpr (k + 2 < 9) {
             read_q(src, s0);
           } else {
@@ -721,7 +775,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
           if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
           const bool last = k == 8 && cc + 1 == nCC;   // no step s+1
           if (!last) finish(cc * 9 + k + 1, s1);
-          load_g(k < 7 ? cc : cc + 1, (k + 2) % 9, s0);
+          load_g(k < 7 ? cc : cc + 1, (k + 2) % 9, s0, k < 7 ? t_cur : t_nxt);
           if constexpr (k == 6) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           // keep the corner reads and the column store in flight; the previous step's
           // store (older) is complete
@@ -735,22 +789,24 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         constexpr bool odd = decltype(parity)::value;
         const unsigned char* src = odd ? box1 : box0;
         unsigned char* dst = odd ? box0 : box1;
+        const CEnt* t_cur = table_of_chunk(cc);
+        const CEnt* t_nxt = table_of_chunk(cc + 1);
         static_for<0, 9>([&](auto kc) __attribute__((always_inline)) {
           constexpr int k = decltype(kc)::value;
           PSet& cur = ((k + (odd ? 1 : 0)) & 1) == 0 ? X : Y;
           PSet& oth = ((k + (odd ? 1 : 0)) & 1) == 0 ? Y : X;
           if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
           finish(cc * 9 + k, cur);
-          if constexpr (k < 8) load_g(cc, k + 1, oth);
+          if constexpr (k < 8) load_g(cc, k + 1, oth, t_cur);
           asm volatile("" ::: "memory");
           if constexpr (k + 1 < 9) read_q(src, oth);
-          read_ce((k + 2) % 9, cur);
+          read_ce((k + 2) % 9, cur, k + 2 < 9 ? t_cur : t_nxt);
           if constexpr (k == 8) {
             __builtin_amdgcn_s_waitcnt(0);
             lds_barrier_dma();
             if (cc + 1 < nCC) {
               read_q(dst, oth);
-              load_g(cc + 1, 0, oth);
+              load_g(cc + 1, 0, oth, t_nxt);
             }
           } else {
             lds_barrier_keep<kKeep>();
@@ -758,22 +814,22 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         });
       };
       if constexpr (GU == 1) {
-        read_ce(0, X);
+        read_ce(0, X, ctab);
         read_q(box0, X);
-        read_ce(1, Y);
+        read_ce(1, Y, ctab);
         read_q(box0, Y);
-        load_g(0, 0, X);
+        load_g(0, 0, X, ctab);
         finish(0, X);          // column 0, before the loop
-        load_g(0, 1, Y);
+        load_g(0, 1, Y, ctab);
         for (int cc = 0; cc < nCC; cc += 2) {
           chunk9w(cc, std::false_type());
           if (cc + 1 < nCC) chunk9w(cc + 1, std::true_type());
         }
       } else {
-        read_ce(0, X);
-        read_ce(1, Y);
+        read_ce(0, X, ctab);
+        read_ce(1, Y, ctab);
         read_q(box0, X);
-        load_g(0, 0, X);
+        load_g(0, 0, X, ctab);
         for (int cc = 0; cc < nCC; cc += 2) {
           chunk9_two(cc, std::false_type());
           if (cc + 1 < nCC) chunk9_two(cc + 1, std::true_type());
@@ -788,9 +844,9 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         unsigned char* dst = odd ? box0 : box1;
         if (cc + 1 < nCC) copy_box(cc + 1, dst);
         for (int k = 0; k < KK; ++k) {
-          read_ce(k, X);
+          read_ce(k, X, ctab);
           read_q(src, X);
-          load_g(cc, k, X);
+          load_g(cc, k, X, ctab);
           finish(cc * KK + k, X);
           if (k == KK - 1 && cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
           lds_barrier_dma();
@@ -856,12 +912,23 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   }
 }
 
+constexpr bool box_groups_built(int fm, int fn) { return fn <= 8 && !(fm == 4 && fn == 6); }
+
 template <int FM, int FN>
 static hipError_t launch_box_t(const BoxArgs& ba, hipStream_t stream) {
   void* args[] = {const_cast<BoxArgs*>(&ba)};
   const dim3 grid(ba.f.m_tiles * ba.tiles_per_img * ba.f.B);
-  const void* fn = ba.f.KK == 9 ? reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN, 9>)
-                                : reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN, 0>);
+  const void* fn = nullptr;
+  if (ba.f.KK != 9) {
+    fn = reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN, 0, false>);
+  } else if (ba.f.G > 1) {
+    // two corner tables leave too little LDS for the output staging of 160 slots, and
+    // 256 x 96 tiles too few registers for the consumers' table work
+    if constexpr (box_groups_built(FM, FN)) fn = reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN, 9, true>);
+    else return hipErrorInvalidValue;
+  } else {
+    fn = reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN, 9, false>);
+  }
   return hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, stream);
 }
 
@@ -874,12 +941,14 @@ hipError_t launch_box(int fm, int fn, const BoxArgs& ba, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-int box_capacity_px(int fn) {
+bool box_groups_supported(int fm, int fn) { return box_groups_built(fm, fn); }
+
+int box_capacity_px(int fn, bool groups) {
   switch (fn) {
-    case 4: return BoxCfg<4>::BOX_PX;
-    case 6: return BoxCfg<6>::BOX_PX;
-    case 8: return BoxCfg<8>::BOX_PX;
-    case 10: return BoxCfg<10>::BOX_PX;
+    case 4: return groups ? BoxCfg<4, true>::BOX_PX : BoxCfg<4>::BOX_PX;
+    case 6: return groups ? BoxCfg<6, true>::BOX_PX : BoxCfg<6>::BOX_PX;
+    case 8: return groups ? BoxCfg<8, true>::BOX_PX : BoxCfg<8>::BOX_PX;
+    case 10: return groups ? 0 : BoxCfg<10>::BOX_PX;   // no offset-group kernel for 160 slots
     default: return 0;
   }
 }

@@ -72,10 +72,13 @@ const VariantInfo& variant_info(int v);
 hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream);
 hipError_t launch_fused(int variant, const FusedArgs& a, hipStream_t stream);
 
-// box kernel: fm = MT/64 (2: fn 4, 6, 8, 10; 4: fn 4, 6), fn = NT/16.
-// box_capacity_px: pixels one LDS box buffer holds for a given fn (0 if not built).
+// box kernel: fm = MT/64 (2: fn 4, 6, 8, 10; 4: fn 4, 6), fn = NT/16; offset groups
+// (f.G > 1) with K = 3 and 32-channel multiples per group.
+// box_capacity_px: pixels one LDS box buffer holds for a given fn, with one corner
+// table or (groups) two (0 if not built).
 hipError_t launch_box(int fm, int fn, const BoxArgs& a, hipStream_t stream);
-int box_capacity_px(int fn);
+int box_capacity_px(int fn, bool groups);
+bool box_groups_supported(int fm, int fn);   // an offset-group kernel is built for (fm, fn)
 
 // direct kernel (no staging): Cin <= 4 and K*K in {1, 4, 9}
 bool direct_supported(int cin, int kk);

@@ -183,8 +183,9 @@ def test_forced_variant(lib, monkeypatch):
 
 
 def test_offset_groups_planning(lib, monkeypatch):
-    """G > 1: tile kernels only, Cin % G == 0 (else an argument error) and Cin/G a
-    multiple of the 16-byte channel vector (8 bf16, 4 fp32; else unsupported)."""
+    """G > 1: Cin % G == 0 (else an argument error); the box kernel for bf16 3x3 with
+    Cin/G a multiple of 32, else the tile kernels with Cin/G a multiple of the 16-byte
+    channel vector (8 bf16, 4 fp32; else unsupported); never the direct kernel."""
     n = ctypes.c_size_t()
     for dt, vec in ((dcn.BF16, 8), (dcn.F32, 4)):
         for Cin, G in ((256, 4), (64, 2), (48, 3), (64, 16), (16, 4), (12, 3), (3, 3)):
@@ -192,16 +193,20 @@ def test_offset_groups_planning(lib, monkeypatch):
             rc = lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
             if (Cin // G) % vec == 0:
                 assert rc == dcn.OK, (dt, Cin, G)
-                assert dcn.dcn_variant_name(desc).startswith("tile_"), (dt, Cin, G)
+                name = dcn.dcn_variant_name(desc)
+                box = dt == dcn.BF16 and (Cin // G) % 32 == 0
+                assert name.startswith("box_" if box else "tile_"), (dt, Cin, G, name)
                 assert f"offset groups={G}" in dcn.dcn_plan_describe(desc)
             else:
                 assert rc == dcn.E_UNSUPPORTED, (dt, Cin, G)
+    desc = dcn.make_desc(2, 256, 20, 24, 70, 5, 1, 2, 1, dcn.BF16, 4)        # 5x5: the tile kernels
+    assert dcn.dcn_variant_name(desc).startswith("tile_")
     desc = dcn.make_desc(2, 64, 20, 24, 70, 3, 1, 1, 1, dcn.BF16, 3)        # 64 channels in 3 groups
     assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_ARG
     for G in (0, 1):                                                         # one group either way
         desc = dcn.make_desc(2, 256, 40, 40, 256, 3, 1, 1, 1, dcn.BF16, G)
         assert dcn.dcn_variant_name(desc).startswith("box_")
-    desc = dcn.make_desc(2, 256, 40, 40, 256, 3, 1, 1, 1, dcn.BF16, 4)
+    desc = dcn.make_desc(2, 256, 40, 40, 256, 3, 1, 1, 1, dcn.BF16, 16)     # 16 channels per group
     for v in ("box_bf16_m256", "direct_bf16"):
         monkeypatch.setenv("DCN_VARIANT", v)
         assert lib.dcn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_UNSUPPORTED

@@ -212,6 +212,12 @@ GROUPED = [
     ("g2_k1", dict(B=2, Cin=16, H=9, W=7, Cout=24, K=1, s=1, p=0, d=1, G=2)),
     ("g8_k5", dict(B=1, Cin=64, H=12, W=14, Cout=130, K=5, s=1, p=2, d=1, G=8, offset="normal:2")),
     ("g4_cout300", dict(B=3, Cin=96, H=8, W=12, Cout=300, K=3, s=1, p=1, d=1, G=4, offset="normal:1.5")),
+    # 32-channel multiples per group: the box kernel (bf16), group tables swapped per group
+    ("g4_box", dict(B=2, Cin=128, H=19, W=23, Cout=256, K=3, s=2, p=1, d=1, G=4, offset="normal:1.5")),
+    ("g2_box_cpg4", dict(B=1, Cin=256, H=14, W=18, Cout=70, K=3, s=1, p=1, d=1, G=2, offset="normal:2")),
+    ("g3_box_cpg2", dict(B=2, Cin=192, H=11, W=13, Cout=130, K=3, s=1, p=2, d=2, G=3, offset="uniform:6",
+                         mask=None)),
+    ("g8_box_far", dict(B=1, Cin=256, H=24, W=20, Cout=256, K=3, s=1, p=1, d=1, G=8, offset="uniform:12")),
 ]
 
 
@@ -241,3 +247,22 @@ def test_offset_groups_every_tile_variant(variant, monkeypatch):
 def test_offset_groups_sampled_c4_layer():
     print(f"[gpu-test] variant {variant_of(WORKLOADS['c4_g4'])}", flush=True)
     sampled_parity(WORKLOADS["c4_g4"])
+
+
+@pytest.mark.parametrize("roles", ["0", "1"])
+@pytest.mark.parametrize("variant,tile", [("box_bf16_m256", "4,5,10"), ("box_bf16_m128", "4,5,10"),
+                                          ("box_bf16_m128", "6,7,13"), ("box_bf16_m128", "8,8,16")])
+def test_offset_groups_box_tiles(variant, tile, roles, monkeypatch):
+    """Offset groups on the box kernel with one and two samples per producer thread."""
+    monkeypatch.setenv("DCN_VARIANT", variant)
+    monkeypatch.setenv("DCN_BOX_TILE", tile)
+    monkeypatch.setenv("DCN_BOX_ROLES", roles)
+    for seed, (Cin, G) in enumerate([(128, 4), (192, 3)]):
+        w = make(f"gbox_{variant}_{tile}", "bf16", 2, Cin, 13, 17, 150, 3, 1, 1, 1, offset="normal:2",
+                 seed=seed, groups=G)
+        inp = generate(w)
+        desc = dcn.describe(inp["x"], inp["weight"], w.stride, w.pad, w.dilation, inp["offset"])
+        plan = dcn.dcn_plan_describe(desc)
+        print(f"[gpu-test] {plan}", flush=True)
+        assert plan.startswith(variant) and f"offset groups={G}" in plan
+        full_parity(w, inp)
