@@ -41,6 +41,7 @@ struct BoxPlan {
   int TH = 0, TW = 0, tiles_x = 0, tiles_per_img = 0;
   int box_px = 0, lds = 0;
   int split = 0;                // BoxArgs::split_roles
+  int pw = 4;                   // BoxArgs::pw
   double cost = 1e300;
 };
 
@@ -170,6 +171,14 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
   if (const char* r = std::getenv("DCN_BOX_ROLES")) {
     if (r[0] == '0' || r[0] == '1') best.split = r[0] - '0';
   }
+  // Eight producer waves (two per SIMD, 4 channels per thread and sample) where that
+  // kernel is built: 256 x 64 tiles, 3x3, one offset group, paired roles (c4 layer:
+  // 33.4 -> 31.5 us).  DCN_BOX_PW=4|8 pins it where it is built.
+  const bool pw8_ok = best.fm == 4 && best.fn == 4 && d->kernel_size == 3 && offset_groups(d) == 1 && !best.split;
+  best.pw = pw8_ok ? 8 : 4;
+  if (const char* w = std::getenv("DCN_BOX_PW")) {
+    if (w[0] == '4') best.pw = 4;
+  }
   *out = best;
   return true;
 }
@@ -258,7 +267,7 @@ int compute_plan(const dcn_desc* d, Plan* p) {
 // with one shape skip the tile search.  Thread-safe; a small round-robin table.
 struct PlanKey {
   dcn_desc d;
-  char variant[48], tile[48], roles[8];
+  char variant[48], tile[48], roles[8], pw[8];
 };
 struct PlanSlot {
   bool used = false;
@@ -272,6 +281,7 @@ void fill_key(const dcn_desc* d, PlanKey* k) {
   if (const char* v = std::getenv("DCN_VARIANT")) std::strncpy(k->variant, v, sizeof(k->variant) - 1);
   if (const char* t = std::getenv("DCN_BOX_TILE")) std::strncpy(k->tile, t, sizeof(k->tile) - 1);
   if (const char* r = std::getenv("DCN_BOX_ROLES")) std::strncpy(k->roles, r, sizeof(k->roles) - 1);
+  if (const char* w = std::getenv("DCN_BOX_PW")) std::strncpy(k->pw, w, sizeof(k->pw) - 1);
 }
 
 int make_plan(const dcn_desc* d, Plan* p) {
@@ -379,6 +389,7 @@ hipError_t launch_fused_plan(const Plan& p, const FusedArgs& a, hipStream_t stre
   ba.KK_NT = a.KK * 16 * p.box.fn;
   ba.lds_bytes = 0;
   ba.split_roles = p.box.split;
+  ba.pw = p.box.pw;
   return dcn::launch_box(p.box.fm, p.box.fn, ba, stream);
 }
 
@@ -431,12 +442,12 @@ extern "C" int dcn_plan_describe(const dcn_desc* desc, char* buf, size_t len) {
   const dcn::VariantInfo& vi = dcn::variant_info(p.variant);
   if (is_box(p.variant)) {
     std::snprintf(buf, len,
-                  "%s tile=%dx%d px (%d slots) x %d ch, tiles=%lld, box_px=%d, roles=%s, offset groups=%lld, "
-                  "ws=%zu B",
+                  "%s tile=%dx%d px (%d slots) x %d ch, tiles=%lld, box_px=%d, roles=%s, producer waves=%d, "
+                  "offset groups=%lld, ws=%zu B",
                   vi.name, p.box.TH, p.box.TW, 16 * p.box.fn, 64 * p.box.fm,
                   static_cast<long long>(desc->batch) * p.box.tiles_per_img * (p.Mp / (64 * p.box.fm)),
-                  p.box.box_px, p.box.split ? "split" : "paired", static_cast<long long>(offset_groups(desc)),
-                  p.ws_bytes);
+                  p.box.box_px, p.box.split ? "split" : "paired", p.box.pw,
+                  static_cast<long long>(offset_groups(desc)), p.ws_bytes);
   } else {
     std::snprintf(buf, len, "%s tile=%d px x %d ch, offset groups=%lld, ws=%zu B", vi.name, vi.nt, vi.mt,
                   static_cast<long long>(offset_groups(desc)), p.ws_bytes);

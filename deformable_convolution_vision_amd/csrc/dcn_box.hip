@@ -49,7 +49,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kThreads = 512;    // 4 consumer + 4 producer waves
+constexpr int kThreads = 512;    // 4 consumer + 4 producer waves (8 producer waves: 768)
 constexpr int kCK = 32;          // channels per reduction chunk (one MFMA k-step)
 constexpr int kPXB = 64;         // bytes per box pixel (32 bf16 channels)
 constexpr int kCOLB = 80;        // bytes per column-tile row (64 + 16 pad)
@@ -116,11 +116,30 @@ __device__ __forceinline__ uint4 interp8(uint4 q00, uint4 q01, uint4 q10, uint4 
   return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
+// the same for 4 channels (8-byte corner vectors)
+__device__ __forceinline__ uint2 interp8(uint2 q00, uint2 q01, uint2 q10, uint2 q11, uint32_t w01, uint32_t w23) {
+  const uint32_t a0[2] = {q00.x, q00.y}, a1[2] = {q01.x, q01.y};
+  const uint32_t b0[2] = {q10.x, q10.y}, b1[2] = {q11.x, q11.y};
+  uint32_t r[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t p0lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
+    const uint32_t p0hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
+    const uint32_t p1lo = __builtin_amdgcn_perm(b1[e], b0[e], 0x05040100u);
+    const uint32_t p1hi = __builtin_amdgcn_perm(b1[e], b0[e], 0x07060302u);
+    const float lo = dot2(p1lo, w23, dot2_0(p0lo, w01));
+    const float hi = dot2(p1hi, w23, dot2_0(p0hi, w01));
+    r[e] = pk_bf16(lo, hi);
+  }
+  return make_uint2(r[0], r[1]);
+}
+
 // component-wise select (a select of whole structs can become a select of their
 // addresses, which keeps them out of registers)
 __device__ __forceinline__ uint4 sel4(bool c, uint4 a, uint4 b) {
   return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
+__device__ __forceinline__ uint2 sel4(bool c, uint2 a, uint2 b) { return make_uint2(c ? a.x : b.x, c ? a.y : b.y); }
 
 // f(integral_constant<int, I>) for I = B .. E-1, each call inlined with I known at compile time
 template <int I, int E, class F>
@@ -153,6 +172,15 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// the corner vector type's load: 16 or 8 bytes
+__device__ __forceinline__ void buffer_load_q(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint4& out) {
+  out = buffer_load16(r, voff);
+}
+__device__ __forceinline__ void buffer_load_q(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint2& out) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+  out = make_uint2(v[0], v[1]);
 }
 // Direct buffer->LDS load: 16 bytes per lane from byte offset `voff`, lane l's bytes
 // at dst + 16*l.
@@ -188,21 +216,32 @@ __device__ __forceinline__ void lds_barrier_keep() {
 
 }  // namespace
 
-template <int FM, int FN, int KKT, bool GRP>
-__global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
+template <int FM, int FN, int KKT, bool GRP, int PW = 4>
+__global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
   using Cfg = BoxCfg<FN, GRP>;
   const FusedArgs& a = ba.f;
   static_assert(!GRP || KKT == 9, "offset groups: 3x3 only");
+  // PW producer waves: 4 (16-byte column units, 8 channels per thread and sample) or 8
+  // (8-byte units, 4 channels; two producer waves share each SIMD)
+  static_assert(PW == 4 || PW == 8, "four or eight producer waves");
+  constexpr int NTH = 256 + 64 * PW;   // threads per workgroup
+  constexpr int PTH = 64 * PW;         // producer threads
+  constexpr int UB = PW == 8 ? 8 : 16; // bytes per column unit
+  constexpr int UPS = kPXB / UB;       // units per 32-channel sample
+  constexpr int UPS_SH = PW == 8 ? 3 : 2;   // log2(UPS): thread indexes are non-negative, shifts suffice
+  using QV = typename std::conditional<PW == 8, uint2, uint4>::type;
   static_assert(FM % 2 == 0 && FN % 2 == 0, "whole 32x32 MFMA blocks per wave");
   constexpr int TM = FM / 2, TN = FN / 2;   // 32x32 output blocks per consumer wave
   constexpr int WM = 16 * FM;         // rows per consumer wave
   constexpr int MT = 4 * WM;          // rows per workgroup
   constexpr int NT = Cfg::NT;         // pixel slots per workgroup
-  constexpr int GUNITS = NT * 4;      // 16-byte column units per chunk
-  constexpr int GU = (GUNITS + 255) / 256;
+  constexpr int GUNITS = NT * UPS;    // column units per chunk
+  constexpr int GU = (GUNITS + PTH - 1) / PTH;
   constexpr int BOXB = Cfg::BOX_PX * kPXB;
 
-  __shared__ __attribute__((aligned(16))) unsigned char col[Cfg::COL_BYTES];
+  // The column ring is read every step by the consumers: the largest alignment puts it
+  // at the start of LDS, so its reads address it with immediate offsets.
+  __shared__ __attribute__((aligned(1024))) unsigned char col[Cfg::COL_BYTES];
   __shared__ __attribute__((aligned(16))) CEnt ctab[(GRP ? 2 : 1) * kBoxMaxKK * NT];
   __shared__ __attribute__((aligned(16))) unsigned char box0[BOXB + kZeroB];
   __shared__ __attribute__((aligned(16))) unsigned char box1[BOXB + kZeroB];
@@ -214,7 +253,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   // wv is the wave's index within its role, rtid the thread's.
   const int wraw = __builtin_amdgcn_readfirstlane(wave);
   const bool consumer = ba.split_roles ? (wraw & 2) == 0 : wraw < 4;
-  const int wv = ba.split_roles ? (wraw & 1) | ((wraw >> 2) << 1) : (wraw & 3);
+  // (& 7: the index is known non-negative, so index divisions stay unsigned)
+  const int wv = ba.split_roles ? (wraw & 1) | ((wraw >> 2) << 1) : ((consumer ? wraw : wraw - 4) & 7);
   const int rtid = wv * 64 + lane;
   // MFMA 32x32x16 operand lanes: row (A) or column (B) lane & 31, and a 16-byte
   // channel group: lane half lh holds channels 16*lh + 8*h .. +7 of k-half h, so a
@@ -265,21 +305,18 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     }
     return r;
   };
-  // Weight fragments in two sets of G named slots: chunks G*g .. G*g+G-1 live in set
-  // p for even g and in set q for odd g (G = 4 for the smaller tiles; G = 2 where
+  // Weight fragments in two sets of G slots: chunks G*g .. G*g+G-1 live in set pa
+  // for even g and in set qa for odd g (G = 4 for the smaller tiles; G = 2 where
   // 2*G*FM fragments would not fit next to the accumulators and column fragments, and
-  // with offset groups, whose table work adds to the consumers' registers).
-  constexpr int G = (FM * FN <= 16 && !GRP) ? 4 : 2;
-  AFrag p0{}, p1{}, p2{}, p3{}, q0{}, q1{}, q2{}, q3{};
+  // with offset groups, whose table work adds to the consumers' registers; G = 1 with
+  // eight producer waves, three waves per SIMD).
+  constexpr int G = PW == 8 ? 1 : (FM * FN <= 16 && !GRP) ? 4 : 2;
+  AFrag pa[G], qa[G];
   // weights for chunks c0 .. c0+G-1 (past the end a valid chunk is re-read, so every
   // group issues the same loads)
-  auto load_group = [&](int c0, AFrag& x0, AFrag& x1, AFrag& x2, AFrag& x3) __attribute__((always_inline)) {
-    x0 = load_a(min(c0, S - 1));
-    x1 = load_a(min(c0 + 1, S - 1));
-    if constexpr (G == 4) {
-      x2 = load_a(min(c0 + 2, S - 1));
-      x3 = load_a(min(c0 + 3, S - 1));
-    }
+  auto load_group = [&](int c0, AFrag (&x)[G]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) x[i] = load_a(min(c0 + i, S - 1));
   };
 
   // The prologue has one barrier, and it orders LDS traffic only (lds_barrier): it
@@ -345,12 +382,12 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
 
   // ---- the producers' box-copy plan (with the box pixels outside the image zeroed),
   // then chunk 0 of the box
-  const int pw = wv;                        // producer wave 0..3 (unused by consumers)
+  const int pw = wv;                        // producer wave 0..PW-1 (unused by consumers)
   // Box copy, one wave instruction per 16 pixels: lane -> pixel blk*16 + lane/4,
-  // 16-byte quarter lane%4.  Pixels advance by 64 between a wave's blocks; the
+  // 16-byte quarter lane%4.  Pixels advance by 16*PW between a wave's blocks; the
   // row/column step is precomputed so no division is needed per block.
   const int nblk = (npx + 15) >> 4;
-  const int step_r = 64 / BW, step_c = 64 - (64 / BW) * BW;
+  const int step_r = (16 * PW) / BW, step_c = 16 * PW - ((16 * PW) / BW) * BW;
   const int px_first = pw * 16 + (lane >> 2);
   const int ry_first = px_first / BW, rx_first = px_first - (px_first / BW) * BW;
   // per-lane byte offsets (32-bit: the host keeps the staged copy under 4 GiB)
@@ -365,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
   // of the buffer, which moves no data, so every block is issued unconditionally
   // and the number of vector-memory operations of each step is a compile-time
   // constant (exact wait counts for the prefetched global-path corners below).
-  constexpr int MAXB = Cfg::BOX_PX / 64;   // blocks per wave; 4 * MAXB blocks fill the buffer
+  constexpr int MAXB = Cfg::BOX_PX / (16 * PW);   // blocks per wave; PW * MAXB blocks fill the buffer
   const uint32_t xs_bytes = static_cast<uint32_t>(a.B * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u;
   uint32_t boff[MAXB];
   if (!consumer) {
@@ -374,15 +411,15 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       constexpr int j = decltype(jc)::value;
       const int gy = by0 + ry, gx = bx0 + rx;
       const bool inside = gy >= 0 && gy < a.H && gx >= 0 && gx < a.W;
-      const bool ok = pw + 4 * j < nblk && px < npx && inside;
+      const bool ok = pw + PW * j < nblk && px < npx && inside;
       boff[j] = ok ? img_off + static_cast<uint32_t>(gy) * row_bytes + static_cast<uint32_t>(gx) * px_bytes
                    : kOOB;
       // box pixels outside the image stay zero in both buffers
-      if (pw + 4 * j < nblk && px < npx && !inside) {
+      if (pw + PW * j < nblk && px < npx && !inside) {
         *reinterpret_cast<uint4*>(box0 + px * kPXB + (lane & 3) * 16) = make_uint4(0u, 0u, 0u, 0u);
         *reinterpret_cast<uint4*>(box1 + px * kPXB + (lane & 3) * 16) = make_uint4(0u, 0u, 0u, 0u);
       }
-      px += 64;
+      px += 16 * PW;
       ry += step_r;
       rx += step_c;
       if (rx >= BW) { rx -= BW; ++ry; }
@@ -400,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(cc);
     static_for<decltype(j0c)::value, decltype(j1c)::value>([&](auto jc) __attribute__((always_inline)) {
       constexpr int j = decltype(jc)::value;
-      buffer_to_lds16(rsrc, dst + (pw + 4 * j) * 1024, boff[j]);
+      buffer_to_lds16(rsrc, dst + (pw + PW * j) * 1024, boff[j]);
     });
   };
   auto copy_box = [&](int cc, unsigned char* dst) __attribute__((always_inline)) {
@@ -467,8 +504,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     // the two role branches are laid out one after the other in the compiled code, so
     // registers the consumers load before the branch would stay allocated through the
     // producers' code.  Steps 0 and 1 have no multiply, which hides most of the latency.
-    load_group(0, p0, p1, p2, p3);
-    load_group(G, q0, q1, q2, q3);
+    load_group(0, pa);
+    load_group(G, qa);
     floatx16 acc[TM][TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -548,36 +585,35 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     if (S > 1) lds_barrier();      // barrier 1: chunk 1 is produced
     // 2G chunks per iteration (slots p0.. then q0..).  The loop runs while every step
     // of the iteration has all three parts, so its body has no branches.
+    // step c + i of an iteration (c even): column fragments b0 -> b1 for even i
+    auto run = [&](auto tail, int c, auto ic, AFrag& af) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (decltype(tail)::value) {
+        if constexpr ((i & 1) == 0) step_tail(c + i, af, b0, b1);
+        else step_tail(c + i, af, b1, b0);
+      } else {
+        if constexpr ((i & 1) == 0) step(c + i, af, b0, b1);
+        else step(c + i, af, b1, b0);
+      }
+    };
     int c = 0;
     for (; c + 2 * G + 2 <= S; c += 2 * G) {
-      step(c, p0, b0, b1);
-      step(c + 1, p1, b1, b0);
-      if constexpr (G == 4) {
-        step(c + 2, p2, b0, b1);
-        step(c + 3, p3, b1, b0);
-      }
-      step(c + G, q0, b0, b1);
-      step(c + G + 1, q1, b1, b0);
-      if constexpr (G == 4) {
-        step(c + 6, q2, b0, b1);
-        step(c + 7, q3, b1, b0);
-      }
+      static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
+        run(std::false_type(), c, ic, pa[decltype(ic)::value]);
+      });
+      static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
+        run(std::false_type(), c, std::integral_constant<int, G + decltype(ic)::value>(), qa[decltype(ic)::value]);
+      });
     }
     // at most 2G+1 chunks remain; the slots hold chunks c .. c+2G-1 and step c
-    // reloads p0 with chunk c+2G
-    step_tail(c, p0, b0, b1);
-    step_tail(c + 1, p1, b1, b0);
-    if constexpr (G == 4) {
-      step_tail(c + 2, p2, b0, b1);
-      step_tail(c + 3, p3, b1, b0);
-    }
-    step_tail(c + G, q0, b0, b1);
-    step_tail(c + G + 1, q1, b1, b0);
-    if constexpr (G == 4) {
-      step_tail(c + 6, q2, b0, b1);
-      step_tail(c + 7, q3, b1, b0);
-    }
-    step_tail(c + 2 * G, p0, b0, b1);
+    // reloads pa[0] with chunk c+2G
+    static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
+      run(std::true_type(), c, ic, pa[decltype(ic)::value]);
+    });
+    static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
+      run(std::true_type(), c, std::integral_constant<int, G + decltype(ic)::value>(), qa[decltype(ic)::value]);
+    });
+    run(std::true_type(), c, std::integral_constant<int, 2 * G>(), pa[0]);
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0) only; see the end of the producer branch
 
     // ---- epilogue, part 1: bias and bf16 rounding into an LDS copy of the output
@@ -609,19 +645,24 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
         }
   } else {
     // ================= producers: box copies and column tiles =================
-    const int ptid = rtid;                  // producer thread 0..255
+    const int ptid = rtid;                  // producer thread 0..PTH-1
+    // the global-path corners: this thread's unit within a pixel
+    const uint32_t g_img_off =
+        PW == 4 ? img_off   // the copy plan's lane offset is the same 16-byte quarter
+                : static_cast<uint32_t>(b * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u +
+                      static_cast<uint32_t>((ptid & (UPS - 1)) * UB);
 
     // Producer state of one step: the corner-table entries and the four corner vectors
     // of this thread's samples.  A sample with nothing in the box reads the zero bytes
     // after the buffer with a row stride of 0.
-    struct PSet { CEnt ce[GU]; uint4 q[GU][4]; };
+    struct PSet { CEnt ce[GU]; QV q[GU][4]; };
     // Samples whose corners lie outside the box (ce.off == -1) take their corners from
     // the channels-last copy in global memory.  When a wave has any such sample in a
     // step (gfl, wave-uniform), its lanes load the four corner vectors straight into
     // registers (gq) one step ahead, right after the previous step's interpolation,
     // so the loads are in flight across a barrier; lanes without such a sample, and
     // corners outside the image, load zeros.  One step's vectors are live at a time.
-    uint4 gq[GU][4];
+    QV gq[GU][4];
     bool gfl[GU];
     // With one sample per thread and 3x3 taps the offsets and weights of the thread's
     // nine table entries stay in registers for the whole tile (the steps index them
@@ -634,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     if constexpr (kCeRegs) {
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
-        const CEnt e = ctab[k * NT + (ptid >> 2)];
+        const CEnt e = ctab[k * NT + (ptid >> UPS_SH)];
         ce_off[k] = e.off;
         ce_w01[k] = e.w01;
         ce_w23[k] = e.w23;
@@ -646,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       if constexpr (kCeRegs) {
 #pragma unroll
         for (int k = 0; k < 9; ++k) {
-          const CEnt e = tbl[k * NT + (ptid >> 2)];
+          const CEnt e = tbl[k * NT + (ptid >> UPS_SH)];
           ce_off[k] = e.off;
           ce_w01[k] = e.w01;
           ce_w23[k] = e.w23;
@@ -662,22 +703,22 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       } else {
 #pragma unroll
         for (int g = 0; g < GU; ++g)
-          if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS)
-            f.ce[g] = __builtin_bit_cast(CEnt, reinterpret_cast<const uint4*>(tbl)[k * NT + ((ptid + g * 256) >> 2)]);
+          if (GUNITS % PTH == 0 || pw * 64 + g * PTH < GUNITS)
+            f.ce[g] = __builtin_bit_cast(CEnt, reinterpret_cast<const uint4*>(tbl)[k * NT + ((ptid + g * PTH) >> UPS_SH)]);
       }
     };
     auto read_q = [&](const unsigned char* src, PSet& f) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
-        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
+        if (GUNITS % PTH == 0 || pw * 64 + g * PTH < GUNITS) {
           const CEnt& ce = f.ce[g];
           const bool in_box = ce.off >= 0;
-          const unsigned char* q = src + (in_box ? ce.off : BOXB) + (ptid & 3) * 16;
+          const unsigned char* q = src + (in_box ? ce.off : BOXB) + (ptid & (UPS - 1)) * UB;
           const int rs = in_box ? BW * kPXB : 0;
-          f.q[g][0] = *reinterpret_cast<const uint4*>(q);
-          f.q[g][1] = *reinterpret_cast<const uint4*>(q + kPXB);
-          f.q[g][2] = *reinterpret_cast<const uint4*>(q + rs);
-          f.q[g][3] = *reinterpret_cast<const uint4*>(q + rs + kPXB);
+          f.q[g][0] = *reinterpret_cast<const QV*>(q);
+          f.q[g][1] = *reinterpret_cast<const QV*>(q + kPXB);
+          f.q[g][2] = *reinterpret_cast<const QV*>(q + rs);
+          f.q[g][3] = *reinterpret_cast<const QV*>(q + rs + kPXB);
         }
       }
     };
@@ -685,20 +726,20 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     auto load_g = [&](int cc, int k, const PSet& f, const CEnt* tbl) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
-        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
+        if (GUNITS % PTH == 0 || pw * 64 + g * PTH < GUNITS) {
           const CEnt& ce = f.ce[g];
           gfl[g] = __ballot(ce.off == -1) != 0;
           if (gfl[g]) {
             const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(cc);
-            const int yx = kCeRegs ? tbl[k * NT + ((ptid + g * 256) >> 2)].yx : ce.yx;
+            const int yx = kCeRegs ? tbl[k * NT + ((ptid + g * PTH) >> UPS_SH)].yx : ce.yx;
             const int y0 = (yx >> 16) - 1, x0 = (yx & 0xffff) - 1;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
               const int yy = y0 + (qq >> 1), xx = x0 + (qq & 1);
               const bool ok = (ce.off == -1) & (yy >= 0) & (yy < a.H) & (xx >= 0) & (xx < a.W);
               const uint32_t voff =
-                  ok ? img_off + static_cast<uint32_t>(yy) * row_bytes + static_cast<uint32_t>(xx) * px_bytes : kOOB;
-              gq[g][qq] = buffer_load16(rsrc, voff);
+                  ok ? g_img_off + static_cast<uint32_t>(yy) * row_bytes + static_cast<uint32_t>(xx) * px_bytes : kOOB;
+              buffer_load_q(rsrc, voff, gq[g][qq]);
             }
           }
         }
@@ -709,11 +750,11 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
       unsigned char* cdst = col + (s % kColBufs) * NT * kCOLB;
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
-        if (GUNITS % 256 == 0 || pw * 64 + g * 256 < GUNITS) {
-          const int u = ptid + g * 256;
-          const int p = u >> 2, sub = u & 3;
+        if (GUNITS % PTH == 0 || pw * 64 + g * PTH < GUNITS) {
+          const int u = ptid + g * PTH;
+          const int p = u >> UPS_SH, sub = u & (UPS - 1);
           const CEnt& ce = f.ce[g];
-          uint4 c0 = f.q[g][0], c1 = f.q[g][1], c2 = f.q[g][2], c3 = f.q[g][3];
+          QV c0 = f.q[g][0], c1 = f.q[g][1], c2 = f.q[g][2], c3 = f.q[g][3];
           if (gfl[g]) {   // wave-uniform: some lane's sample takes the global-path corners
             const bool o = ce.off == -1;
             c0 = sel4(o, gq[g][0], c0);
@@ -721,8 +762,8 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
             c2 = sel4(o, gq[g][2], c2);
             c3 = sel4(o, gq[g][3], c3);
           }
-          const uint4 r = interp8(c0, c1, c2, c3, ce.w01, ce.w23);
-          *reinterpret_cast<uint4*>(cdst + p * kCOLB + sub * 16) = r;
+          const QV r = interp8(c0, c1, c2, c3, ce.w01, ce.w23);
+          *reinterpret_cast<QV*>(cdst + p * kCOLB + sub * UB) = r;
         }
       }
     };
@@ -878,7 +919,7 @@ __global__ __launch_bounds__(kThreads) void dcn_box_kernel(BoxArgs ba) {
     const int TH = ba.TH, TW = ba.TW;
     const int xs0 = ox0 & ~1;
     const int slots = (ox0 - xs0 + TW + 1) >> 1;
-    const int rows = MT * TH, rstep = kThreads / slots;
+    const int rows = MT * TH, rstep = NTH / slots;
     const int slot = tid % slots, r0 = tid / slots;
     const int c0 = xs0 + slot * 2, xend = min(ox0 + TW, a.Wo);
     const bool in0 = c0 >= ox0 && c0 < xend, in1 = c0 + 1 >= ox0 && c0 + 1 < xend;
@@ -919,6 +960,15 @@ static hipError_t launch_box_t(const BoxArgs& ba, hipStream_t stream) {
   void* args[] = {const_cast<BoxArgs*>(&ba)};
   const dim3 grid(ba.f.m_tiles * ba.tiles_per_img * ba.f.B);
   const void* fn = nullptr;
+  if (ba.pw == 8) {   // eight producer waves: 256 x 64 tiles, 3x3, one offset group
+    if constexpr (FM == 4 && FN == 4) {
+      if (ba.f.KK != 9 || ba.f.G > 1 || ba.split_roles) return hipErrorInvalidValue;
+      return hipLaunchKernel(reinterpret_cast<const void*>(&dcn_box_kernel<4, 4, 9, false, 8>), grid,
+                             dim3(256 + 64 * 8), args, 0, stream);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (ba.f.KK != 9) {
     fn = reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN, 0, false>);
   } else if (ba.f.G > 1) {

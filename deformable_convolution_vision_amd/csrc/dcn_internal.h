@@ -43,6 +43,7 @@ struct BoxArgs {
   int lds_bytes;         // dynamic LDS per workgroup
   int split_roles;       // 0: each SIMD runs one consumer and one producer wave;
                          // 1: the consumers share two SIMDs, the producers the other two
+  int pw;                // producer waves: 4 (512 threads) or 8 (768 threads)
 };
 
 enum Variant : int {

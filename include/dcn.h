@@ -52,7 +52,8 @@
  *    DCN_E_UNSUPPORTED.  DCN_BOX_TILE="fn,TH,TW" restricts the box kernel's tile
  *    to 16*fn pixel slots holding TH x TW output pixels (sweeps only), and
  *    DCN_BOX_ROLES=0|1 pins its placement of consumer and producer waves on the
- *    SIMDs (tests and sweeps).  Plans are cached per descriptor and the three
+ *    SIMDs and DCN_BOX_PW=4 its four-producer-wave schedule where it would take
+ *    eight (tests and sweeps).  Plans are cached per descriptor and the four
  *    variables' values.
  */
 #ifndef DCN_H
