@@ -168,16 +168,25 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
   // the c5 layer: 108 -> 100 us); with 64 slots, halving the SIMDs that run matrix
   // instructions costs more than it saves (c4: 36 -> 38 us).
   best.split = best.fm == 4 && best.fn == 6;
-  if (const char* r = std::getenv("DCN_BOX_ROLES")) {
-    if (r[0] == '0' || r[0] == '1') best.split = r[0] - '0';
-  }
   // Eight producer waves (two per SIMD, 4 channels per thread and sample) where that
-  // kernel is built: 256 x 64 tiles, 3x3, one offset group, paired roles (c4 layer:
-  // 33.4 -> 31.5 us).  DCN_BOX_PW=4|8 pins it where it is built.
-  const bool pw8_ok = best.fm == 4 && best.fn == 4 && d->kernel_size == 3 && offset_groups(d) == 1 && !best.split;
-  best.pw = pw8_ok ? 8 : 4;
+  // kernel is built (256 x 64 and 256 x 96, 128 x 128 and 128 x 160 tiles; 3x3, one
+  // offset group) and the roles are paired (c4 layer: 33.1 -> 31.6 us).
+  // DCN_BOX_PW=4|8 pins it where it is built.
+  const bool pw8_built = dcn::box_pw8_supported(best.fm, best.fn) && d->kernel_size == 3 && offset_groups(d) == 1;
+  // (c3 layer on 128 x 160 tiles: 42.2 -> 41.4 us; the c5 layer's split roles beat
+  // eight paired producer waves: 90.0 against 93.3 us)
+  best.pw = pw8_built && !best.split ? 8 : 4;
   if (const char* w = std::getenv("DCN_BOX_PW")) {
     if (w[0] == '4') best.pw = 4;
+    if (w[0] == '8' && pw8_built) {
+      best.pw = 8;
+      best.split = 0;
+    }
+  }
+  // DCN_BOX_ROLES=0|1 pins the role placement (split roles: four producer waves)
+  if (const char* r = std::getenv("DCN_BOX_ROLES")) {
+    if (r[0] == '0' || r[0] == '1') best.split = r[0] - '0';
+    if (best.split) best.pw = 4;
   }
   *out = best;
   return true;

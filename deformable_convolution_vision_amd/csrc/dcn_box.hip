@@ -224,6 +224,7 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
   // PW producer waves: 4 (16-byte column units, 8 channels per thread and sample) or 8
   // (8-byte units, 4 channels; two producer waves share each SIMD)
   static_assert(PW == 4 || PW == 8, "four or eight producer waves");
+  static_assert(PW == 4 || (KKT == 9 && !GRP), "eight producer waves: 3x3, one offset group");
   constexpr int NTH = 256 + 64 * PW;   // threads per workgroup
   constexpr int PTH = 64 * PW;         // producer threads
   constexpr int UB = PW == 8 ? 8 : 16; // bytes per column unit
@@ -311,6 +312,9 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
   // with offset groups, whose table work adds to the consumers' registers; G = 1 with
   // eight producer waves, three waves per SIMD).
   constexpr int G = PW == 8 ? 1 : (FM * FN <= 16 && !GRP) ? 4 : 2;
+  // consumers keep one column buffer in registers instead of two (eight producer waves
+  // with tiles wider than 256 x 64)
+  constexpr bool kSingleB = PW == 8 && FM * FN > 16;
   AFrag pa[G], qa[G];
   // weights for chunks c0 .. c0+G-1 (past the end a valid chunk is re-read, so every
   // group issues the same loads)
@@ -579,41 +583,66 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
       table_work(c, std::integral_constant<int, 1>());
       if (c + 2 < S) lds_barrier();
     };
-    BFrag b0{}, b1{};
-    lds_barrier();                 // barrier 0: chunk 0 is produced
-    b0 = read_b(0);
-    if (S > 1) lds_barrier();      // barrier 1: chunk 1 is produced
-    // 2G chunks per iteration (slots p0.. then q0..).  The loop runs while every step
-    // of the iteration has all three parts, so its body has no branches.
-    // step c + i of an iteration (c even): column fragments b0 -> b1 for even i
-    auto run = [&](auto tail, int c, auto ic, AFrag& af) __attribute__((always_inline)) {
-      constexpr int i = decltype(ic)::value;
-      if constexpr (decltype(tail)::value) {
-        if constexpr ((i & 1) == 0) step_tail(c + i, af, b0, b1);
-        else step_tail(c + i, af, b1, b0);
-      } else {
-        if constexpr ((i & 1) == 0) step(c + i, af, b0, b1);
-        else step(c + i, af, b1, b0);
+    if constexpr (!kSingleB) {
+      BFrag b0{}, b1{};
+      lds_barrier();                 // barrier 0: chunk 0 is produced
+      b0 = read_b(0);
+      if (S > 1) lds_barrier();      // barrier 1: chunk 1 is produced
+      // 2G chunks per iteration (slots p0.. then q0..).  The loop runs while every step
+      // of the iteration has all three parts, so its body has no branches.
+      // step c + i of an iteration (c even): column fragments b0 -> b1 for even i
+      auto run = [&](auto tail, int c, auto ic, AFrag& af) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (decltype(tail)::value) {
+          if constexpr ((i & 1) == 0) step_tail(c + i, af, b0, b1);
+          else step_tail(c + i, af, b1, b0);
+        } else {
+          if constexpr ((i & 1) == 0) step(c + i, af, b0, b1);
+          else step(c + i, af, b1, b0);
+        }
+      };
+      int c = 0;
+      for (; c + 2 * G + 2 <= S; c += 2 * G) {
+        static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
+          run(std::false_type(), c, ic, pa[decltype(ic)::value]);
+        });
+        static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
+          run(std::false_type(), c, std::integral_constant<int, G + decltype(ic)::value>(), qa[decltype(ic)::value]);
+        });
       }
-    };
-    int c = 0;
-    for (; c + 2 * G + 2 <= S; c += 2 * G) {
+      // at most 2G+1 chunks remain; the slots hold chunks c .. c+2G-1 and step c
+      // reloads pa[0] with chunk c+2G
       static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
-        run(std::false_type(), c, ic, pa[decltype(ic)::value]);
+        run(std::true_type(), c, ic, pa[decltype(ic)::value]);
       });
       static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
-        run(std::false_type(), c, std::integral_constant<int, G + decltype(ic)::value>(), qa[decltype(ic)::value]);
+        run(std::true_type(), c, std::integral_constant<int, G + decltype(ic)::value>(), qa[decltype(ic)::value]);
+      });
+      run(std::true_type(), c, std::integral_constant<int, 2 * G>(), pa[0]);
+    } else {
+      // One column buffer in registers (eight producer waves with the wider tiles,
+      // where two would not fit in 168 registers): chunk c is read after barrier c,
+      // when it is complete, and multiplied at once; the producers meanwhile write
+      // chunk c+2 into another buffer of the ring.
+      auto step1 = [&](int c, AFrag& af) __attribute__((always_inline)) {
+        const BFrag bf = read_b(c);
+        mma(af, bf);
+        af = load_a(min(c + 2 * G, S - 1));
+        if (c + 1 < S) lds_barrier();
+      };
+      lds_barrier();                 // barrier 0: chunk 0 is produced
+      int c = 0;
+      for (; c + 2 * G <= S; c += 2 * G) {
+        static_for<0, G>([&](auto ic) __attribute__((always_inline)) { step1(c + decltype(ic)::value, pa[decltype(ic)::value]); });
+        static_for<0, G>([&](auto ic) __attribute__((always_inline)) { step1(c + G + decltype(ic)::value, qa[decltype(ic)::value]); });
+      }
+      static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
+        if (c + decltype(ic)::value < S) step1(c + decltype(ic)::value, pa[decltype(ic)::value]);
+      });
+      static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
+        if (c + G + decltype(ic)::value < S) step1(c + G + decltype(ic)::value, qa[decltype(ic)::value]);
       });
     }
-    // at most 2G+1 chunks remain; the slots hold chunks c .. c+2G-1 and step c
-    // reloads pa[0] with chunk c+2G
-    static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
-      run(std::true_type(), c, ic, pa[decltype(ic)::value]);
-    });
-    static_for<0, G>([&](auto ic) __attribute__((always_inline)) {
-      run(std::true_type(), c, std::integral_constant<int, G + decltype(ic)::value>(), qa[decltype(ic)::value]);
-    });
-    run(std::true_type(), c, std::integral_constant<int, 2 * G>(), pa[0]);
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0) only; see the end of the producer branch
 
     // ---- epilogue, part 1: bias and bf16 rounding into an LDS copy of the output
@@ -954,16 +983,17 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
 }
 
 constexpr bool box_groups_built(int fm, int fn) { return fn <= 8 && !(fm == 4 && fn == 6); }
+constexpr bool box_pw8_built(int fm, int fn) { return (fm == 4 && fn <= 6) || (fm == 2 && fn >= 8); }
 
 template <int FM, int FN>
 static hipError_t launch_box_t(const BoxArgs& ba, hipStream_t stream) {
   void* args[] = {const_cast<BoxArgs*>(&ba)};
   const dim3 grid(ba.f.m_tiles * ba.tiles_per_img * ba.f.B);
   const void* fn = nullptr;
-  if (ba.pw == 8) {   // eight producer waves: 256 x 64 tiles, 3x3, one offset group
-    if constexpr (FM == 4 && FN == 4) {
+  if (ba.pw == 8) {   // eight producer waves: 3x3, one offset group, paired roles
+    if constexpr (box_pw8_built(FM, FN)) {
       if (ba.f.KK != 9 || ba.f.G > 1 || ba.split_roles) return hipErrorInvalidValue;
-      return hipLaunchKernel(reinterpret_cast<const void*>(&dcn_box_kernel<4, 4, 9, false, 8>), grid,
+      return hipLaunchKernel(reinterpret_cast<const void*>(&dcn_box_kernel<FM, FN, 9, false, 8>), grid,
                              dim3(256 + 64 * 8), args, 0, stream);
     } else {
       return hipErrorInvalidValue;
@@ -992,6 +1022,7 @@ hipError_t launch_box(int fm, int fn, const BoxArgs& ba, hipStream_t stream) {
 }
 
 bool box_groups_supported(int fm, int fn) { return box_groups_built(fm, fn); }
+bool box_pw8_supported(int fm, int fn) { return box_pw8_built(fm, fn); }
 
 int box_capacity_px(int fn, bool groups) {
   switch (fn) {

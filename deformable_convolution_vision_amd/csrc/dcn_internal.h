@@ -80,6 +80,7 @@ hipError_t launch_fused(int variant, const FusedArgs& a, hipStream_t stream);
 hipError_t launch_box(int fm, int fn, const BoxArgs& a, hipStream_t stream);
 int box_capacity_px(int fn, bool groups);
 bool box_groups_supported(int fm, int fn);   // an offset-group kernel is built for (fm, fn)
+bool box_pw8_supported(int fm, int fn);      // an eight-producer-wave kernel is built for (fm, fn)
 
 // direct kernel (no staging): Cin <= 4 and K*K in {1, 4, 9}
 bool direct_supported(int cin, int kk);

@@ -269,16 +269,17 @@ def test_offset_groups_box_tiles(variant, tile, roles, monkeypatch):
 
 
 @pytest.mark.parametrize("pw", ["4", "8"])
-def test_box_producer_waves(pw, monkeypatch):
-    """The 256 x 64-slot box kernel with four and with eight producer waves."""
-    monkeypatch.setenv("DCN_VARIANT", "box_bf16_m256")
-    monkeypatch.setenv("DCN_BOX_TILE", "4,5,10")
+@pytest.mark.parametrize("variant,tile", [("box_bf16_m256", "4,5,10"), ("box_bf16_m256", "6,7,13"),
+                                          ("box_bf16_m128", "8,8,16"), ("box_bf16_m128", "10,9,17")])
+def test_box_producer_waves(variant, tile, pw, monkeypatch):
+    """The box kernel with four and with eight producer waves, paired roles."""
+    monkeypatch.setenv("DCN_VARIANT", variant)
+    monkeypatch.setenv("DCN_BOX_TILE", tile)
     monkeypatch.setenv("DCN_BOX_ROLES", "0")
-    if pw == "4":
-        monkeypatch.setenv("DCN_BOX_PW", "4")
+    monkeypatch.setenv("DCN_BOX_PW", pw)
     shapes = [(2, 64, 9, 10, 260, 3, 2, 1, 1), (2, 40, 12, 14, 300, 3, 1, 2, 2), (1, 256, 30, 34, 256, 3, 2, 1, 1)]
     for seed, shape in enumerate(shapes):
-        w = make(f"pw{pw}", "bf16", *shape, offset="normal:2", seed=seed)
+        w = make(f"pw{pw}_{variant}_{tile}", "bf16", *shape, offset="normal:2", seed=seed)
         desc = dcn.make_desc(w.B, w.Cin, w.H, w.W, w.Cout, w.K, w.stride, w.pad, w.dilation, dcn.BF16)
         plan = dcn.dcn_plan_describe(desc)
         print(f"[gpu-test] {shape} {plan}", flush=True)
