@@ -156,3 +156,29 @@ def points(x, offset, weight, pts, bias=None, stride=1, padding=0, dilation=1, m
 
 def threads_used(threads: int = 0, lib_path: str = LIB) -> int:
     return load(lib_path).oracle_threads(threads)
+
+
+def offset_mask(x, weight_om, bias_om=None, stride=1, padding=0, dilation=1, groups=1, threads=0,
+                lib_path: str = LIB):
+    """The offset/mask branch of DCNv2 (csdn.net tags page "可变形卷积：Deformable ConvNets",
+    DCNv2 section 3.2: a separate regular convolution of the same input, at the layer's
+    resolution, with 3K^2 outputs per offset group; the first 2K^2 are the offsets, the
+    rest go through a sigmoid and are the modulation scalars).
+
+    A regular convolution is the deformable one with zero offsets and no mask, so this
+    is the oracle's forward with a zero offset field, followed by the channel split and
+    a sigmoid written out in float64.  Returns (offset [B, 2GK^2, Ho, Wo], mask
+    [B, GK^2, Ho, Wo], sum of |terms| of the convolution [B, 3GK^2, Ho, Wo])."""
+    w = _f32(weight_om)
+    K = w.shape[2]
+    KK = K * K
+    if w.shape[0] != 3 * groups * KK:
+        raise ValueError(f"weight_om must have 3*G*K*K = {3 * groups * KK} output channels")
+    xs = _f32(x)
+    B, _, H, W = xs.shape
+    Ho, Wo = output_hw(B, xs.shape[1], H, W, w.shape[0], K, stride, padding, dilation, lib_path)
+    zero = np.zeros((B, 2 * KK, Ho, Wo), dtype=np.float32)
+    y, a = forward(xs, zero, w, bias_om, stride, padding, dilation, mask=None, threads=threads,
+                   lib_path=lib_path)
+    n_off = 2 * groups * KK
+    return y[:, :n_off], 1.0 / (1.0 + np.exp(-y[:, n_off:])), a

@@ -20,6 +20,8 @@ What each pin reduces to (no pin restates the oracle's own formula):
   p11 offset groups           -> the sum over groups of one-group problems (each channel slice
                                 with its own offset and mask slice) via the grid_sample
                                 formulation; G copies of one offset field -> one group
+  p12 offset/mask branch      -> torch conv2d (float64) split into 2GK^2 offset channels and
+                                the sigmoid of the other GK^2
   golden                      -> hand-worked examples in tests/golden/
 """
 
@@ -322,6 +324,22 @@ def pin_p11_offset_groups(lib):
             assert np.array_equal(yg, y1), "p11 replicated groups differ from one group"
 
 
+def pin_p12_offset_mask_branch(lib):
+    rng = np.random.default_rng(22)
+    for (B, Cin, H, W, K, s, p, d, G) in [(2, 5, 9, 11, 3, 1, 1, 1, 1), (1, 4, 12, 10, 3, 2, 1, 1, 2),
+                                          (2, 3, 8, 9, 1, 1, 0, 1, 1), (1, 6, 13, 12, 3, 1, 2, 2, 3)]:
+        KK = K * K
+        x = rng.standard_normal((B, Cin, H, W)).astype(np.float32)
+        w = rng.standard_normal((3 * G * KK, Cin, K, K)).astype(np.float32)
+        b = rng.standard_normal(3 * G * KK).astype(np.float32)
+        off, msk, _ = oracle.offset_mask(x, w, b, s, p, d, groups=G, lib_path=lib)
+        ref = F.conv2d(torch.from_numpy(x).double(), torch.from_numpy(w).double(), torch.from_numpy(b).double(),
+                       stride=s, padding=p, dilation=d).numpy()
+        _close(off, ref[:, :2 * G * KK], 1e-12, f"p12 offsets {(B, Cin, H, W, K, s, p, d, G)}")
+        _close(msk, torch.sigmoid(torch.from_numpy(ref[:, 2 * G * KK:])).numpy(), 1e-12,
+               f"p12 mask {(B, Cin, H, W, K, s, p, d, G)}")
+
+
 def pin_golden(lib):
     with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
         g = json.load(f)
@@ -347,4 +365,5 @@ def pin_golden(lib):
 
 ALL_PINS = [pin_p1_zero_offsets, pin_p2_integer_offsets, pin_p3_bilinear_field, pin_p4_all_outside,
             pin_p5_linear_in_mask, pin_p6_mask_absent, pin_p7_half_offsets, pin_p8_constant_input,
-            pin_p9_grid_sample, pin_p10_nonfinite_offsets, pin_p11_offset_groups, pin_golden]
+            pin_p9_grid_sample, pin_p10_nonfinite_offsets, pin_p11_offset_groups, pin_p12_offset_mask_branch,
+            pin_golden]
