@@ -130,6 +130,101 @@ def traffic_for(workload: str):
     return entry.get("bytes_per_launch")
 
 
+def bench_offset_mask(w, steps: int, warmup: int):
+    """The DCNv2 offset/mask convolution (dcn_offset_mask): one step is one call (its
+    staging launch and its convolution launch), timed as a whole with HIP events."""
+    import numpy as np
+    import torch
+
+    import deformable_convolution_vision_amd as dcn
+    import oracle
+    from deformable_convolution_vision_amd.workloads import generate
+
+    host = generate(w)
+    g = {k: (None if v is None else v.cuda()) for k, v in host.items()}
+    dt = dcn.F32 if w.dtype == "f32" else dcn.BF16
+    desc = dcn.make_desc(w.B, w.Cin, w.H, w.W, 1, w.K, w.stride, w.pad, w.dilation, dt, w.groups)
+    Ho, Wo = dcn.dcn_output_hw(desc)
+    nb = dcn.dcn_offset_mask_workspace_bytes(desc)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    KK = w.K * w.K
+    n_off = 2 * w.groups * KK
+    off = torch.empty((w.B, n_off, Ho, Wo), dtype=g["x"].dtype, device="cuda")
+    msk = torch.empty((w.B, w.groups * KK, Ho, Wo), dtype=g["x"].dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        dcn.dcn_offset_mask(desc, g["x"], g["weight"], g["bias"], off, msk, ws, nb, stream)
+
+    step()
+    torch.cuda.synchronize()
+    # parity on sampled outputs: the oracle's convolution (zero offsets) at those points
+    rng = np.random.default_rng(0)
+    npts = 512
+    pts = np.stack([rng.integers(0, w.B, npts), rng.integers(0, w.Cout, npts), rng.integers(0, Ho, npts),
+                    rng.integers(0, Wo, npts)], 1).astype(np.int64)
+    zero = np.zeros((w.B, 2 * KK, Ho, Wo), dtype=np.float32)
+    y, a = oracle.points(host["x"], zero, host["weight"], pts, host["bias"], w.stride, w.pad, w.dilation)
+    got_off = off.float().cpu().numpy()
+    got_msk = msk.float().cpu().numpy()
+    tol = 1e-4 if w.dtype == "f32" else 1e-2
+    max_rel = 0.0
+    for (b, o, oy, ox), yy, aa in zip(pts, y, a):
+        if o < n_off:
+            err = abs(got_off[b, o, oy, ox] - yy) / max(aa, 1e-30)
+        else:   # sigmoid is 1/4-Lipschitz; the mask is rounded to the element type
+            ref = 1.0 / (1.0 + np.exp(-yy))
+            err = max(abs(got_msk[b, o - n_off, oy, ox] - ref) - (2.0 ** -9 if w.dtype == "bf16" else 1e-6), 0.0) \
+                / max(aa / 4, 1e-30)
+        max_rel = max(max_rel, float(err))
+    if not max_rel <= tol:
+        raise SystemExit(f"bench parity failure on {w.name}: max relative error {max_rel:.3e} > {tol}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents(steps + 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(0, sp)
+    for i in range(steps):
+        step()
+        ev.record(i + 1, sp)
+    ev.sync(steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(ev.ms(i, i + 1) for i in range(steps))
+    total_ms = ev.ms(0, steps)
+    ev.close()
+    ms_per_step = total_ms / steps
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK["bf16_mfma"] if w.dtype == "bf16" else PEAK["f32_mfma"]
+    variant = dcn.dcn_variant_name(dcn.make_desc(w.B, w.Cin, w.H, w.W, w.Cout, w.K, w.stride, w.pad, w.dilation, dt))
+    return {
+        "metric": "deform_conv2d fwd effective TFLOP/s + GB/s (c4 stride-2 bf16), % of roofline",
+        "value": round(tflops, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; shapes and value distributions of the workload)",
+        "config": {"workload": f"{w.name}: offset/mask convolution B={w.B} Cin={w.Cin} {w.H}x{w.W} -> "
+                               f"{w.Cout} channels {Ho}x{Wo} (offsets {n_off}, mask {w.groups * KK}), K={w.K} "
+                               f"stride={w.stride} pad={w.pad} dilation={w.dilation}",
+                   "variant": variant, "plan": "dcn_offset_mask: staging launch + tile convolution launch"},
+        "effective_gbps": round(w.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "frac_mfma_peak": round(tflops / peak, 5),
+        "frac_hbm_peak": round(w.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK["hbm"], 5),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 4), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 5), "traffic": None,
+                     "kernel": "dcn_offset_mask (both launches)", "kernel_sha": kernel_hash(),
+                     "per_launch": {"flops": w.flops, "algorithmic_bytes": w.algorithmic_bytes}},
+        "kernels_us": {"call_mean": round(total_ms / steps * 1e3, 3), "call_median": round(per[steps // 2] * 1e3, 3),
+                       "call_min": round(per[0] * 1e3, 3)},
+        "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
+        "parity_max_rel_err_sampled": max_rel,
+        "cold": None,
+        "cpu_baseline": None,
+    }
+
+
 def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: float, cold_steps: int = 0):
     import numpy as np
     import torch
@@ -138,6 +233,8 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
     from deformable_convolution_vision_amd.workloads import WORKLOADS, generate
 
     w = WORKLOADS[name]
+    if w.op == "offset_mask":
+        return bench_offset_mask(w, steps, warmup)
     host = generate(w)
     g = {k: (None if v is None else v.cuda()) for k, v in host.items()}
     desc = dcn.describe(g["x"], g["weight"], w.stride, w.pad, w.dilation, g["offset"])

@@ -20,6 +20,7 @@ import torch
 
 __all__ = ["Desc", "dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_stage",
            "dcn_forward_staged", "dcn_variant_name", "dcn_plan_describe", "dcn_status_str", "deform_conv2d",
+           "dcn_offset_mask_workspace_bytes", "dcn_offset_mask", "offset_mask",
            "DcnError", "library_path", "load_library", "F32", "BF16"]
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +30,8 @@ F32, BF16 = 0, 1
 OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 _EXPORTS = ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_stage", "dcn_forward_staged",
-            "dcn_variant_name", "dcn_plan_describe", "dcn_status_str")
+            "dcn_variant_name", "dcn_plan_describe", "dcn_status_str", "dcn_offset_mask_workspace_bytes",
+            "dcn_offset_mask")
 
 
 class DcnError(RuntimeError):
@@ -78,6 +80,10 @@ def load_library() -> ctypes.CDLL:
     lib.dcn_plan_describe.restype = ctypes.c_int
     lib.dcn_status_str.argtypes = [ctypes.c_int]
     lib.dcn_status_str.restype = ctypes.c_char_p
+    lib.dcn_offset_mask_workspace_bytes.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.dcn_offset_mask_workspace_bytes.restype = ctypes.c_int
+    lib.dcn_offset_mask.argtypes = [D, P, P, P, P, P, P, S, P]
+    lib.dcn_offset_mask.restype = ctypes.c_int
     for name in ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_forward_staged", "dcn_stage"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -221,3 +227,55 @@ def deform_conv2d(input, offset, weight, bias=None, stride=1, padding=0, dilatio
     with torch.cuda.device(input.device):
         dcn_forward(desc, input, offset, mask, weight, bias, out, workspace if nbytes else None, nbytes)
     return out
+
+
+def dcn_offset_mask_workspace_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    rc = load_library().dcn_offset_mask_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    if rc != OK:
+        raise DcnError(rc, "dcn_offset_mask_workspace_bytes")
+    return n.value
+
+
+def dcn_offset_mask(desc: Desc, x, weight_om, bias_om, offset, mask, workspace, workspace_bytes: int,
+                    stream=None) -> None:
+    rc = load_library().dcn_offset_mask(ctypes.byref(desc), _ptr(x), _ptr(weight_om), _ptr(bias_om),
+                                        _ptr(offset), _ptr(mask), _ptr(workspace), workspace_bytes,
+                                        _stream(stream))
+    if rc != OK:
+        raise DcnError(rc, "dcn_offset_mask")
+
+
+def offset_mask(input, weight_om, bias_om=None, stride=1, padding=0, dilation=1, offset_groups=1,
+                workspace=None):
+    """The DCNv2 offset/mask branch on the GPU: returns (offset [B,2GK^2,Ho,Wo], mask
+    [B,GK^2,Ho,Wo]) from the regular convolution of input with weight_om
+    [3GK^2,Cin,K,K] (bias_om [3GK^2] or None), ready for deform_conv2d."""
+    K = weight_om.shape[2]
+    G = int(offset_groups)
+    if weight_om.dim() != 4 or weight_om.shape[0] != 3 * G * K * K or weight_om.shape[3] != K:
+        raise ValueError(f"weight_om must be [3*G*K*K, Cin, K, K], got {tuple(weight_om.shape)}")
+    if input.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {input.dtype}; use float32 or bfloat16")
+    B, Cin, H, W = input.shape
+    if weight_om.shape[1] != Cin:
+        raise ValueError("weight_om does not match the input channels")
+    for name, t in (("weight_om", weight_om), ("bias_om", bias_om)):
+        if t is None:
+            continue
+        if t.dtype != input.dtype or t.device != input.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {input.dtype} tensor on the input's device")
+    if bias_om is not None and tuple(bias_om.shape) != (3 * G * K * K,):
+        raise ValueError("bias_om must be [3*G*K*K]")
+    if not input.is_cuda or not input.is_contiguous():
+        raise ValueError("input must be a contiguous GPU tensor")
+    desc = make_desc(B, Cin, H, W, 1, K, int(stride), int(padding), int(dilation), _DTYPES[input.dtype], G)
+    Ho, Wo = dcn_output_hw(desc)
+    offset = torch.empty((B, 2 * G * K * K, Ho, Wo), dtype=input.dtype, device=input.device)
+    mask = torch.empty((B, G * K * K, Ho, Wo), dtype=input.dtype, device=input.device)
+    nbytes = dcn_offset_mask_workspace_bytes(desc)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=input.device)
+    with torch.cuda.device(input.device):
+        dcn_offset_mask(desc, input, weight_om, bias_om, offset, mask, workspace if nbytes else None, nbytes)
+    return offset, mask

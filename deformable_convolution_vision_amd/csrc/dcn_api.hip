@@ -223,7 +223,7 @@ int choose_variant(const dcn_desc* d, int64_t N, int64_t Ho, int64_t Wo, BoxPlan
   return dcn::V_TILE_BF16_M128_N32;
 }
 
-int compute_plan(const dcn_desc* d, Plan* p) {
+int compute_plan(const dcn_desc* d, Plan* p, int force_variant = -1) {
   if (!geometry_ok(d)) return DCN_E_ARG;
   if (d->dtype != DCN_F32 && d->dtype != DCN_BF16) return DCN_E_UNSUPPORTED;
   p->Ho = out_extent(d->height, d->kernel_size, d->stride, d->pad, d->dilation);
@@ -234,10 +234,11 @@ int compute_plan(const dcn_desc* d, Plan* p) {
   const int64_t HoWo = p->Ho * p->Wo;
   const int64_t N = B * HoWo;
   const int64_t G = offset_groups(d);
-  p->variant = choose_variant(d, N, p->Ho, p->Wo, &p->box);
+  p->variant = force_variant >= 0 ? force_variant : choose_variant(d, N, p->Ho, p->Wo, &p->box);
   // DCN_VARIANT=<name> pins the kernel variant (tile sweeps and tests); an
   // unknown name or one built for the other dtype is rejected.
-  if (const char* force = std::getenv("DCN_VARIANT")) {
+  const char* force = force_variant >= 0 ? nullptr : std::getenv("DCN_VARIANT");
+  if (force) {
     if (force[0] != '\0') {
       int found = -1;
       for (int v = 0; v < dcn::V_COUNT; ++v)
@@ -462,6 +463,55 @@ extern "C" int dcn_plan_describe(const dcn_desc* desc, char* buf, size_t len) {
                   static_cast<long long>(offset_groups(desc)), p.ws_bytes);
   }
   return DCN_OK;
+}
+
+// ---- the offset/mask branch: a regular convolution with 3*G*K*K outputs on the
+// tile kernels (zero offsets, no mask), its epilogue splitting offsets and mask
+namespace {
+
+int om_plan(const dcn_desc* d, dcn_desc* od, Plan* p) {
+  if (!geometry_ok(d)) return DCN_E_ARG;
+  if (d->dtype != DCN_F32 && d->dtype != DCN_BF16) return DCN_E_UNSUPPORTED;
+  *od = *d;
+  od->out_channels = 3 * offset_groups(d) * d->kernel_size * d->kernel_size;
+  od->offset_groups = 1;
+  const bool small = od->out_channels <= 64;
+  const int variant = d->dtype == DCN_F32 ? (small ? dcn::V_TILE_F32_M64_N64 : dcn::V_TILE_F32_M128_N64)
+                                          : (small ? dcn::V_TILE_BF16_M64_N64 : dcn::V_TILE_BF16_M128_N64);
+  return compute_plan(od, p, variant);
+}
+
+}  // namespace
+
+extern "C" int dcn_offset_mask_workspace_bytes(const dcn_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return DCN_E_ARG;
+  dcn_desc od;
+  Plan p;
+  const int rc = om_plan(desc, &od, &p);
+  if (rc != DCN_OK) return rc;
+  *bytes = p.ws_bytes;
+  return DCN_OK;
+}
+
+extern "C" int dcn_offset_mask(const dcn_desc* desc, const void* x, const void* weight_om, const void* bias_om,
+                               void* offset, void* mask, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  dcn_desc od;
+  Plan p;
+  int rc = om_plan(desc, &od, &p);
+  if (rc != DCN_OK) return rc;
+  if (p.empty) return DCN_OK;
+  if (x == nullptr || weight_om == nullptr || offset == nullptr || mask == nullptr) return DCN_E_ARG;
+  rc = check_positions(&od, od.kernel_size, od.stride, od.pad, od.dilation, p.Ho, p.Wo);
+  if (rc != DCN_OK) return rc;
+  rc = check_workspace(p, workspace, workspace_bytes);
+  if (rc != DCN_OK) return rc;
+  const StageArgs s = stage_args(&od, p, x, weight_om, workspace);
+  if (dcn::launch_stage(p.variant, s, stream) != hipSuccess) return DCN_E_HIP;
+  FusedArgs a = fused_args(&od, p, x, nullptr, nullptr, weight_om, bias_om, offset, workspace);
+  a.out2 = mask;
+  a.om_split = static_cast<int>(2 * offset_groups(desc) * desc->kernel_size * desc->kernel_size);
+  return launch_fused_plan(p, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
 }
 
 extern "C" const char* dcn_status_str(int status) {

@@ -21,6 +21,12 @@ struct FusedArgs {
   int B, Cin, H, W, Cp, Cout, K, KK, stride, pad, dil, Ho, Wo, HoWo, N;
   int m_tiles, n_tiles;
   int G, Cg;           // offset groups and channels per group (1 and Cin for one group)
+  // The offset/mask branch (tile kernels): offset == null samples at zero offsets (a
+  // regular convolution); with om_split > 0 the output channels o < om_split go to out
+  // as [B][om_split][Ho][Wo] and the others, through a sigmoid, to out2 as
+  // [B][Cout - om_split][Ho][Wo].
+  void* out2;
+  int om_split;
 };
 
 struct StageArgs {

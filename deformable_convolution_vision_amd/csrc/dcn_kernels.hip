@@ -369,8 +369,8 @@ __global__ __launch_bounds__(kThreads) void dcn_fused_kernel(FusedArgs a) {
       const int grp = a.G == 1 ? 0 : min((cc * C::CK + g_sub[u] * C::VEC) / a.Cg, a.G - 1);
       const int gk = grp * KK + k;
       const int ob = (g_b[u] * 2 * KK * a.G + 2 * gk) * a.HoWo + g_rem[u];
-      const float dy = load_scalar<BF16>(a.offset, ob);
-      const float dx = load_scalar<BF16>(a.offset, ob + a.HoWo);
+      const float dy = a.offset ? load_scalar<BF16>(a.offset, ob) : 0.f;
+      const float dx = a.offset ? load_scalar<BF16>(a.offset, ob + a.HoWo) : 0.f;
       const float m = a.mask ? load_scalar<BF16>(a.mask, (g_b[u] * KK * a.G + gk) * a.HoWo + g_rem[u]) : 1.f;
       // integer and fractional parts of the offset are exact in fp32, so the
       // neighbour rows/columns and the interpolation fractions are exact too.
@@ -557,7 +557,14 @@ __global__ __launch_bounds__(kThreads) void dcn_fused_kernel(FusedArgs a) {
         if (o >= a.Cout) continue;
         float v = acc[fm][fn][i];
         if (a.bias) v += load_scalar<BF16>(a.bias, o);
-        store_scalar<BF16>(a.out, (b * a.Cout + o) * a.HoWo + rem, v);
+        if (a.om_split == 0) {
+          store_scalar<BF16>(a.out, (b * a.Cout + o) * a.HoWo + rem, v);
+        } else if (o < a.om_split) {   // offset channels
+          store_scalar<BF16>(a.out, (b * a.om_split + o) * a.HoWo + rem, v);
+        } else {                       // mask channels: sigmoid
+          store_scalar<BF16>(a.out2, (b * (a.Cout - a.om_split) + o - a.om_split) * a.HoWo + rem,
+                             1.f / (1.f + expf(-v)));
+        }
       }
     }
   }

@@ -47,6 +47,7 @@ class Workload:
     seed: int = 0
     x: str = "normal"     # "normal" = N(0,1)
     groups: int = 1       # offset groups: offset has 2*groups*K^2 channels, mask groups*K^2
+    op: str = "forward"   # "forward" | "offset_mask" (the DCNv2 offset/mask convolution; Cout = 3*groups*K^2)
 
     @property
     def torch_dtype(self):
@@ -62,6 +63,9 @@ class Workload:
         """Each tensor crossing the boundary counted once, at its element size."""
         es = 4 if self.dtype == "f32" else 2
         KK = self.K * self.K
+        if self.op == "offset_mask":   # x, weight, bias in; offsets and mask (Cout channels) out
+            return es * (self.B * self.Cin * self.H * self.W + self.Cout * self.Cin * KK
+                         + (self.Cout if self.bias is not None else 0) + self.B * self.Cout * self.Ho * self.Wo)
         n = (self.B * self.Cin * self.H * self.W
              + self.B * 2 * KK * self.groups * self.Ho * self.Wo
              + (self.B * KK * self.groups * self.Ho * self.Wo if self.mask is not None else 0)
@@ -87,6 +91,9 @@ WORKLOADS = {
     # the c4 layer with four offset groups of 64 channels (deformable groups)
     "c4_g4": Workload("c4_g4", "bf16", 2, 256, 100, 168, 256, 3, 2, 1, 1, 50, 84,
                       offset="normal:1", mask="sigmoid", bias=None, seed=1005, groups=4),
+    # the c4 layer's offset/mask convolution: 3*K^2 = 27 outputs (offset field and mask)
+    "c4_om": Workload("c4_om", "bf16", 2, 256, 100, 168, 27, 3, 2, 1, 1, 50, 84,
+                      offset="normal:1", mask=None, bias="normal:0.1", seed=1006, op="offset_mask"),
 }
 ORDER = ["tiny", "single224", "c3", "c4", "c5"]
 
@@ -119,6 +126,11 @@ def generate(w: Workload, seed: int | None = None) -> dict[str, torch.Tensor | N
     KK = w.K * w.K
     x = _draw(w.x, (w.B, w.Cin, w.H, w.W), g)
     weight = torch.randn((w.Cout, w.Cin, w.K, w.K), generator=g) * math.sqrt(2.0 / (w.Cin * KK))
+    if w.op == "offset_mask":   # x, the 3GK^2-output weight, its bias
+        bias = _draw(w.bias, (w.Cout,), g) if w.bias is not None else None
+        dt = w.torch_dtype
+        cast = (lambda t: None if t is None else t.to(dt).contiguous())
+        return {"x": cast(x), "offset": None, "mask": None, "weight": cast(weight), "bias": cast(bias)}
     offset = _draw(w.offset, (w.B, 2 * KK * w.groups, w.Ho, w.Wo), g)
     mask = _draw(w.mask, (w.B, KK * w.groups, w.Ho, w.Wo), g) if w.mask is not None else None
     bias = _draw(w.bias, (w.Cout,), g) if w.bias is not None else None
@@ -131,7 +143,7 @@ def generate(w: Workload, seed: int | None = None) -> dict[str, torch.Tensor | N
 def custom(name: str, dtype: str, B: int, Cin: int, H: int, W: int, Cout: int, K: int,
            stride: int, pad: int, dilation: int, Ho: int, Wo: int, offset: str = "normal:1",
            mask: str | None = "sigmoid", bias: str | None = "normal:0.1", seed: int = 0,
-           x: str = "normal", groups: int = 1) -> Workload:
+           x: str = "normal", groups: int = 1, op: str = "forward") -> Workload:
     """A workload of any shape (used for edge cases); the caller supplies Ho, Wo."""
     return Workload(name, dtype, B, Cin, H, W, Cout, K, stride, pad, dilation, Ho, Wo,
-                    offset=offset, mask=mask, bias=bias, seed=seed, x=x, groups=groups)
+                    offset=offset, mask=mask, bias=bias, seed=seed, x=x, groups=groups, op=op)

@@ -141,6 +141,22 @@ const char* dcn_variant_name(const dcn_desc* desc);
  * DCN_E_ARG if buf is NULL or len is 0. */
 int dcn_plan_describe(const dcn_desc* desc, char* buf, size_t len);
 
+/* The offset/mask branch of a modulated deformable convolution (csdn.net tags
+ * page "可变形卷积：Deformable ConvNets", DCNv2 section 3.2: a separate regular
+ * convolution of the same input at the layer's resolution, with 3K^2 outputs per
+ * offset group: the first 2K^2 are the offsets, the rest go through a sigmoid and
+ * are the modulation scalars).  For the deformable layer `desc` (its out_channels
+ * is not used): weight_om [3*G*K*K][Cin][K][K], bias_om [3*G*K*K] or NULL, with the
+ * layer's stride, pad and dilation; writes offset [B][2*G*K*K][Ho][Wo] (output
+ * channels 0 .. 2GK^2-1, exactly the layout dcn_forward reads) and mask
+ * [B][G*K*K][Ho][Wo] (sigmoid of channels 2GK^2 .. 3GK^2-1), in desc's dtype.
+ * Device pointers; asynchronous on `stream`; the caller owns every buffer.  The
+ * workspace (256-byte aligned) holds its own staged x and repacked weight_om.
+ * Errors as for dcn_forward, checked before any launch (outputs untouched). */
+int dcn_offset_mask_workspace_bytes(const dcn_desc* desc, size_t* bytes);
+int dcn_offset_mask(const dcn_desc* desc, const void* x, const void* weight_om, const void* bias_om,
+                    void* offset, void* mask, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* dcn_status_str(int status);
 

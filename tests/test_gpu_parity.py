@@ -12,7 +12,7 @@ import torch
 import deformable_convolution_vision_amd as dcn
 import oracle
 from deformable_convolution_vision_amd.workloads import WORKLOADS, custom, generate
-from gpu_common import TOL, check, full_parity, run_hip, sampled_parity, to_gpu
+from gpu_common import TOL, check, full_parity, run_hip, sample_points, sampled_parity, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -285,3 +285,70 @@ def test_box_producer_waves(variant, tile, pw, monkeypatch):
         print(f"[gpu-test] {shape} {plan}", flush=True)
         assert f"producer waves={pw}" in plan
         full_parity(w)
+
+
+OM_SHAPES = [(2, 32, 13, 17, 3, 1, 1, 1, 1), (1, 64, 20, 24, 3, 2, 1, 1, 1), (2, 48, 11, 9, 3, 1, 2, 2, 3),
+             (2, 16, 9, 10, 1, 1, 0, 1, 1), (1, 3, 12, 14, 3, 1, 1, 1, 1), (1, 256, 15, 21, 3, 2, 1, 1, 4)]
+
+
+def _offset_mask_case(dtype, shape, seed):
+    B, Cin, H, W, K, s, p, d, G = shape
+    Ho, Wo = oracle.output_hw(B, Cin, H, W, 1, K, s, p, d)
+    w = custom("om", dtype, B, Cin, H, W, 3 * G * K * K, K, s, p, d, Ho, Wo, mask=None, bias="normal:0.1",
+               seed=seed, groups=G, op="offset_mask")
+    return w, generate(w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", OM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_offset_mask_branch(shape, dtype):
+    """dcn_offset_mask against the oracle's branch: offsets per element to the parity
+    tolerance; the mask to the same tolerance through the sigmoid (1/4-Lipschitz) plus
+    the rounding of a value in [0, 1] to the element type."""
+    w, inp = _offset_mask_case(dtype, shape, zlib.crc32(repr(shape).encode()) % 1000)
+    g = to_gpu(inp)
+    off, msk = dcn.offset_mask(g["x"], g["weight"], g["bias"], w.stride, w.pad, w.dilation, offset_groups=w.groups)
+    torch.cuda.synchronize()
+    o_ref, m_ref, a = oracle.offset_mask(inp["x"], inp["weight"], inp["bias"], w.stride, w.pad, w.dilation,
+                                         groups=w.groups)
+    n_off = o_ref.shape[1]
+    check(off.float().cpu().numpy(), o_ref, a[:, :n_off], TOL[dtype], "offset_mask offsets")
+    round_err = 2.0 ** -9 if dtype == "bf16" else 1e-6
+    err = np.abs(msk.float().cpu().numpy() - m_ref)
+    bound = TOL[dtype] * a[:, n_off:] / 4 + round_err
+    assert np.all(err <= bound), f"offset_mask mask: worst excess {float(np.max(err - bound)):.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_offset_mask_then_forward(dtype):
+    """The branch's outputs fed to the deformable convolution: the forward matches the
+    oracle run on those same (GPU-computed) offsets and mask."""
+    w, inp = _offset_mask_case(dtype, (2, 64, 17, 19, 3, 1, 1, 1, 1), 5)
+    g = to_gpu(inp)
+    off, msk = dcn.offset_mask(g["x"], g["weight"], g["bias"], 1, 1, 1)
+    wd = make("om_fwd", dtype, 2, 64, 17, 19, 70, 3, 1, 1, 1, seed=6)
+    dcn_in = generate(wd)
+    dcn_in["x"] = inp["x"]
+    dcn_in["offset"] = off.cpu()
+    dcn_in["mask"] = msk.cpu()
+    out = run_hip(wd, to_gpu(dcn_in)).cpu()
+    y, a = oracle.forward(dcn_in["x"], dcn_in["offset"], dcn_in["weight"], dcn_in["bias"], 1, 1, 1,
+                          mask=dcn_in["mask"])
+    check(out.float().numpy(), y, a, TOL[dtype], "offset_mask -> forward")
+
+
+def test_offset_mask_sampled_c4_layer():
+    w = WORKLOADS["c4_om"]
+    inp = generate(w)
+    g = to_gpu(inp)
+    off, msk = dcn.offset_mask(g["x"], g["weight"], g["bias"], w.stride, w.pad, w.dilation)
+    torch.cuda.synchronize()
+    o_full, m_full = off.float().cpu().numpy(), msk.float().cpu().numpy()
+    pts = sample_points(w, 2000)
+    zero = np.zeros((w.B, 18, w.Ho, w.Wo), dtype=np.float32)
+    y, a = oracle.points(inp["x"], zero, inp["weight"], pts, inp["bias"], w.stride, w.pad, w.dilation)
+    sel = pts[:, 1] < 18
+    check(o_full[pts[sel, 0], pts[sel, 1], pts[sel, 2], pts[sel, 3]], y[sel], a[sel], TOL["bf16"], "c4_om offsets")
+    mp = pts[~sel]
+    err = np.abs(m_full[mp[:, 0], mp[:, 1] - 18, mp[:, 2], mp[:, 3]] - 1.0 / (1.0 + np.exp(-y[~sel])))
+    assert np.all(err <= TOL["bf16"] * a[~sel] / 4 + 2.0 ** -9)
