@@ -199,7 +199,10 @@ def bench_offset_mask(w, steps: int, warmup: int):
     ms_per_step = total_ms / steps
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK["bf16_mfma"] if w.dtype == "bf16" else PEAK["f32_mfma"]
-    variant = dcn.dcn_variant_name(dcn.make_desc(w.B, w.Cin, w.H, w.W, w.Cout, w.K, w.stride, w.pad, w.dilation, dt))
+    # the kernel dcn_offset_mask runs (its planning rule): bf16 3x3 with >= 24 input
+    # channels and at most 128 outputs on the box kernel's 128-row tiles, else the tile kernels
+    variant = "box_bf16_m128" if (w.dtype == "bf16" and w.K == 3 and w.Cin >= 24 and w.Cout <= 128) else \
+        f"tile_{w.dtype}_m{64 if w.Cout <= 64 else 128}_n64"
     return {
         "metric": "deform_conv2d fwd effective TFLOP/s + GB/s (c4 stride-2 bf16), % of roofline",
         "value": round(tflops, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
@@ -208,7 +211,7 @@ def bench_offset_mask(w, steps: int, warmup: int):
         "config": {"workload": f"{w.name}: offset/mask convolution B={w.B} Cin={w.Cin} {w.H}x{w.W} -> "
                                f"{w.Cout} channels {Ho}x{Wo} (offsets {n_off}, mask {w.groups * KK}), K={w.K} "
                                f"stride={w.stride} pad={w.pad} dilation={w.dilation}",
-                   "variant": variant, "plan": "dcn_offset_mask: staging launch + tile convolution launch"},
+                   "variant": variant, "plan": "dcn_offset_mask: staging launch + convolution launch"},
         "effective_gbps": round(w.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "frac_mfma_peak": round(tflops / peak, 5),
         "frac_hbm_peak": round(w.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK["hbm"], 5),

@@ -475,6 +475,19 @@ int om_plan(const dcn_desc* d, dcn_desc* od, Plan* p) {
   *od = *d;
   od->out_channels = 3 * offset_groups(d) * d->kernel_size * d->kernel_size;
   od->offset_groups = 1;
+  const int64_t Ho = out_extent(od->height, od->kernel_size, od->stride, od->pad, od->dilation);
+  const int64_t Wo = out_extent(od->width, od->kernel_size, od->stride, od->pad, od->dilation);
+  // bf16: the box kernel with 128-row tiles where it plans (zero offsets keep every
+  // sample in the box); else the tile kernels
+  BoxPlan box;
+  if (d->dtype == DCN_BF16 && d->kernel_size == 3 && Ho >= 1 && Wo >= 1 && od->in_channels >= 24 &&
+      od->out_channels <= 128 && plan_box(od, Ho, Wo, 2, &box)) {
+    const int rc = compute_plan(od, p, dcn::V_BOX_BF16_M128);
+    box.pw = 4;        // the branch's kernel: four producer waves, paired roles
+    box.split = 0;
+    p->box = box;
+    return rc;
+  }
   const bool small = od->out_channels <= 64;
   const int variant = d->dtype == DCN_F32 ? (small ? dcn::V_TILE_F32_M64_N64 : dcn::V_TILE_F32_M128_N64)
                                           : (small ? dcn::V_TILE_BF16_M64_N64 : dcn::V_TILE_BF16_M128_N64);

@@ -216,7 +216,7 @@ __device__ __forceinline__ void lds_barrier_keep() {
 
 }  // namespace
 
-template <int FM, int FN, int KKT, bool GRP, int PW = 4>
+template <int FM, int FN, int KKT, bool GRP, int PW = 4, bool OM = false>
 __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
   using Cfg = BoxCfg<FN, GRP>;
   const FusedArgs& a = ba.f;
@@ -225,6 +225,9 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
   // (8-byte units, 4 channels; two producer waves share each SIMD)
   static_assert(PW == 4 || PW == 8, "four or eight producer waves");
   static_assert(PW == 4 || (KKT == 9 && !GRP), "eight producer waves: 3x3, one offset group");
+  // OM: the offset/mask branch (a regular convolution: no offset field; the epilogue
+  // writes the offsets to out and the sigmoid of the mask channels to out2)
+  static_assert(!OM || (!GRP && PW == 4), "offset/mask branch: one group, four producer waves");
   constexpr int NTH = 256 + 64 * PW;   // threads per workgroup
   constexpr int PTH = 64 * PW;         // producer threads
   constexpr int UB = PW == 8 ? 8 : 16; // bytes per column unit
@@ -373,13 +376,18 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
       // branch joins on a value still in flight
       mb[j] = a.mask ? (b * KK * NG + gk) * a.HoWo + rem : ob[j];
     }
-    const uint16_t* offs = reinterpret_cast<const uint16_t*>(a.offset);
-    const uint16_t* msk = reinterpret_cast<const uint16_t*>(a.mask ? a.mask : a.offset);
+    if constexpr (OM) {   // zero offsets, no mask
 #pragma unroll
-    for (int j = 0; j < kPE; ++j) {
-      ldy[j] = offs[ob[j]];
-      ldx[j] = offs[ob[j] + a.HoWo];
-      lm[j] = msk[mb[j]];
+      for (int j = 0; j < kPE; ++j) ldy[j] = ldx[j] = lm[j] = 0u;
+    } else {
+      const uint16_t* offs = reinterpret_cast<const uint16_t*>(a.offset);
+      const uint16_t* msk = reinterpret_cast<const uint16_t*>(a.mask ? a.mask : a.offset);
+#pragma unroll
+      for (int j = 0; j < kPE; ++j) {
+        ldy[j] = offs[ob[j]];
+        ldx[j] = offs[ob[j] + a.HoWo];
+        lm[j] = msk[mb[j]];
+      }
     }
   };
   if (consumer) load_offsets(0);
@@ -661,17 +669,30 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
           bv[tm][r] = ld_bf16(a.bias, min(m0 + wv * WM + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3), a.Cout - 1));
     }
     uint32_t* stage = reinterpret_cast<uint32_t*>(box0);
+    // the offset/mask branch passes the mask channels through a sigmoid; the two
+    // staging loops are separate so the common one carries none of it
+    auto stage_tile = [&](auto sig) __attribute__((always_inline)) {
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
+      for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+        for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int row = wv * WM + tm * 32 + 8 * g + 4 * lh;   // even
-          uint32_t* d = stage + ((tn * 32 + l32) * (MT + 2) + row) / 2;
-          d[0] = pk_bf16(acc[tm][tn][4 * g] + bv[tm][4 * g], acc[tm][tn][4 * g + 1] + bv[tm][4 * g + 1]);
-          d[1] = pk_bf16(acc[tm][tn][4 * g + 2] + bv[tm][4 * g + 2], acc[tm][tn][4 * g + 3] + bv[tm][4 * g + 3]);
-        }
+          for (int g = 0; g < 4; ++g) {
+            const int row = wv * WM + tm * 32 + 8 * g + 4 * lh;   // even
+            uint32_t* d = stage + ((tn * 32 + l32) * (MT + 2) + row) / 2;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[i] = acc[tm][tn][4 * g + i] + bv[tm][4 * g + i];
+              if constexpr (decltype(sig)::value) {
+                if (m0 + row + i >= a.om_split) v[i] = 1.f / (1.f + expf(-v[i]));
+              }
+            }
+            d[0] = pk_bf16(v[0], v[1]);
+            d[1] = pk_bf16(v[2], v[3]);
+          }
+    };
+    stage_tile(std::integral_constant<bool, OM>());
   } else {
     // ================= producers: box copies and column tiles =================
     const int ptid = rtid;                  // producer thread 0..PTH-1
@@ -963,12 +984,21 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
         const uint16_t* src = stage + (py * TW) * (MT + 2) + ol;
         const uint32_t v0 = src[q0 * (MT + 2)], v1 = src[q1 * (MT + 2)];
         if (o < a.Cout && oy < a.Ho) {
-          const int e = (b * a.Cout + o) * a.HoWo + oy * a.Wo + c0;
-          if (pair) {
-            *reinterpret_cast<uint32_t*>(out + e) = v0 | (v1 << 16);
+          uint16_t* dst = out;
+          int e;
+          if constexpr (OM) {   // channels past om_split (the mask) go to out2
+            const bool second = o >= a.om_split;
+            dst = second ? reinterpret_cast<uint16_t*>(a.out2) : out;
+            e = (b * (second ? a.Cout - a.om_split : a.om_split) + (second ? o - a.om_split : o)) * a.HoWo +
+                oy * a.Wo + c0;
           } else {
-            if (in0) out[e] = static_cast<uint16_t>(v0);
-            if (in1) out[e + 1] = static_cast<uint16_t>(v1);
+            e = (b * a.Cout + o) * a.HoWo + oy * a.Wo + c0;
+          }
+          if (pair) {
+            *reinterpret_cast<uint32_t*>(dst + e) = v0 | (v1 << 16);
+          } else {
+            if (in0) dst[e] = static_cast<uint16_t>(v0);
+            if (in1) dst[e + 1] = static_cast<uint16_t>(v1);
           }
         }
         ol += dol;
@@ -990,6 +1020,15 @@ static hipError_t launch_box_t(const BoxArgs& ba, hipStream_t stream) {
   void* args[] = {const_cast<BoxArgs*>(&ba)};
   const dim3 grid(ba.f.m_tiles * ba.tiles_per_img * ba.f.B);
   const void* fn = nullptr;
+  if (ba.f.om_split > 0) {   // the offset/mask branch: 128-row tiles, 3x3, paired roles
+    if constexpr (FM == 2) {
+      if (ba.f.KK != 9 || ba.f.G > 1 || ba.split_roles || ba.pw != 4) return hipErrorInvalidValue;
+      return hipLaunchKernel(reinterpret_cast<const void*>(&dcn_box_kernel<2, FN, 9, false, 4, true>), grid,
+                             dim3(kThreads), args, 0, stream);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (ba.pw == 8) {   // eight producer waves: 3x3, one offset group, paired roles
     if constexpr (box_pw8_built(FM, FN)) {
       if (ba.f.KK != 9 || ba.f.G > 1 || ba.split_roles) return hipErrorInvalidValue;
