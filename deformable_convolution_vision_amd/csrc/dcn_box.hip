@@ -766,9 +766,13 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
           const unsigned char* q = src + (in_box ? ce.off : BOXB) + (ptid & (UPS - 1)) * UB;
           const int rs = in_box ? BW * kPXB : 0;
           f.q[g][0] = *reinterpret_cast<const QV*>(q);
-          f.q[g][1] = *reinterpret_cast<const QV*>(q + kPXB);
-          f.q[g][2] = *reinterpret_cast<const QV*>(q + rs);
-          f.q[g][3] = *reinterpret_cast<const QV*>(q + rs + kPXB);
+          if constexpr (OM) {   // zero offsets: the sample is corner (y0, x0) itself
+            f.q[g][1] = f.q[g][2] = f.q[g][3] = f.q[g][0];
+          } else {
+            f.q[g][1] = *reinterpret_cast<const QV*>(q + kPXB);
+            f.q[g][2] = *reinterpret_cast<const QV*>(q + rs);
+            f.q[g][3] = *reinterpret_cast<const QV*>(q + rs + kPXB);
+          }
         }
       }
     };
@@ -812,7 +816,9 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
             c2 = sel4(o, gq[g][2], c2);
             c3 = sel4(o, gq[g][3], c3);
           }
-          const QV r = interp8(c0, c1, c2, c3, ce.w01, ce.w23);
+          QV r;
+          if constexpr (OM) r = c0;   // weights (1, 0, 0, 0): the copy is exact
+          else r = interp8(c0, c1, c2, c3, ce.w01, ce.w23);
           *reinterpret_cast<QV*>(cdst + p * kCOLB + sub * UB) = r;
         }
       }
@@ -829,7 +835,8 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
       // pipelined over register sets.  The next chunk's box is copied during steps 0-3;
       // each wave waits for its part before barrier 6, after which the whole box is in
       // LDS and steps 7 and 8 read the corners of the next chunk's steps 0 and 1 from it.
-      constexpr int kKeep = GU * 5 < 15 ? GU * 5 : 15;   // LDS reads issued after the column stores
+      constexpr int kRd = OM ? 1 : 4;                    // corner reads per sample
+      constexpr int kKeep = GU * (kRd + 1) < 15 ? GU * (kRd + 1) : 15;   // LDS reads issued after the column stores
       // One sample per thread: each step interpolates the NEXT step's column, so its
       // column store stays in flight across the barrier (the consumers read it only
       // after the next one) and no store latency is on a step's critical path.  Two
@@ -870,8 +877,8 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
           if constexpr (k == 6) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           // keep the corner reads and the column store in flight; the previous step's
           // store (older) is complete
-          if (!last) lds_barrier_keep<5>();
-          else lds_barrier_keep<4>();
+          if (!last) lds_barrier_keep<kRd + 1>();
+          else lds_barrier_keep<kRd>();
         });
       };
       // With more than one sample per thread three sets would not fit in registers:
