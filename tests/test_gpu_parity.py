@@ -65,6 +65,12 @@ EDGE = [
     # H*W a multiple of 8: the register-transpose staging; 70 channels pad to 96, so
     # the second 64-channel block is half padding
     ("stage_cp96", dict(B=3, Cin=70, H=8, W=12, Cout=40, K=3, s=1, p=1, d=1, offset="normal:1.5")),
+    # staging tiles: 280 pixels (a multiple of 8, not of the 256-pixel tile) with an odd
+    # channel count, with two full 64-channel blocks, and 130 pixels (2-pixel vectors,
+    # full 64 x 64 tiles and a 2-pixel tail)
+    ("stage_tail_odd_cin", dict(B=2, Cin=67, H=10, W=28, Cout=48, K=3, s=1, p=1, d=1)),
+    ("stage_full_blocks", dict(B=2, Cin=128, H=10, W=28, Cout=64, K=3, s=1, p=1, d=1)),
+    ("stage_vec2", dict(B=2, Cin=64, H=10, W=13, Cout=32, K=3, s=1, p=1, d=1)),
 ]
 
 
