@@ -1,5 +1,5 @@
 """CPU oracle for the modulated deformable convolution forward (DCNv2; DCNv1 when
-the mask is absent).
+the mask is absent) and its gradients.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
@@ -61,6 +61,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.oracle_points.argtypes = [ctypes.POINTER(_Desc), P, P, P, P, P, P, ctypes.c_int64, P, P,
                                   ctypes.c_int]
     lib.oracle_points.restype = ctypes.c_int
+    lib.oracle_backward.argtypes = [ctypes.POINTER(_Desc), P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+    lib.oracle_backward.restype = ctypes.c_int
     lib.oracle_threads.argtypes = [ctypes.c_int]
     lib.oracle_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
@@ -152,6 +154,34 @@ def points(x, offset, weight, pts, bias=None, stride=1, padding=0, dilation=1, m
     if rc != 0:
         raise ValueError("oracle_points rejected its arguments")
     return out, ab
+
+
+def backward(x, offset, weight, grad_out, stride=1, padding=0, dilation=1, mask=None, threads=0,
+             lib_path: str = LIB):
+    """Gradients of the forward with respect to x, offset, mask, weight and bias for the
+    upstream gradient ``grad_out`` [B, Cout, Ho, Wo] (the gradient equation of the
+    csdn.net tags page "可变形卷积：Deformable ConvNets", part "Deformable Convolutional
+    Networks", section 可变形卷积; the full definition is in dcn_oracle.h).
+
+    Returns a dict of float64 arrays: grad_x, grad_offset, grad_mask (None without a
+    mask), grad_weight, grad_bias."""
+    lib = load(lib_path)
+    x, offset, weight, grad_out, mask = map(_f32, (x, offset, weight, grad_out, mask))
+    d = _desc(x, weight, stride, padding, dilation, offset)
+    Ho, Wo = output_hw(d.B, d.Cin, d.H, d.W, d.Cout, d.K, stride, padding, dilation, lib_path)
+    _check(x, offset, mask, weight, None, d, Ho, Wo)
+    if grad_out.shape != (d.B, d.Cout, Ho, Wo):
+        raise ValueError(f"grad_out must be {(d.B, d.Cout, Ho, Wo)}, got {grad_out.shape}")
+    gx = np.empty(x.shape, dtype=np.float64)
+    goff = np.empty(offset.shape, dtype=np.float64)
+    gm = np.empty(mask.shape, dtype=np.float64) if mask is not None else None
+    gw = np.empty(weight.shape, dtype=np.float64)
+    gb = np.empty(d.Cout, dtype=np.float64)
+    rc = lib.oracle_backward(ctypes.byref(d), _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(grad_out),
+                             _ptr(gx), _ptr(goff), _ptr(gm), _ptr(gw), _ptr(gb), threads)
+    if rc != 0:
+        raise ValueError("oracle_backward rejected its arguments")
+    return {"grad_x": gx, "grad_offset": goff, "grad_mask": gm, "grad_weight": gw, "grad_bias": gb}
 
 
 def threads_used(threads: int = 0, lib_path: str = LIB) -> int:

@@ -95,7 +95,146 @@ void one_output(const oracle_desc* d, int64_t Ho, int64_t Wo, const float* x,
   if (abs_out != nullptr) *abs_out = a;
 }
 
+// The sample S at a float position, its derivatives along py and px, and the
+// four neighbours with their weights (1-|py-yy|)*(1-|px-xx|); neighbours outside
+// the plane have inside = false and contribute nothing.
+struct SampleGrad {
+  double s, dsy, dsx;
+  int64_t iy[4], ix[4];
+  double g[4];
+  bool inside[4];
+};
+
+SampleGrad sample_grad(const float* plane, int64_t H, int64_t W, double py, double px) {
+  SampleGrad r{};
+  const double y0 = std::floor(py), x0 = std::floor(px);
+  for (int n = 0; n < 4; ++n) {
+    const int dy = n >> 1, dx = n & 1;
+    const double yy = y0 + dy, xx = x0 + dx;
+    r.inside[n] = yy >= 0.0 && yy <= static_cast<double>(H - 1) && xx >= 0.0 && xx <= static_cast<double>(W - 1);
+    if (!r.inside[n]) continue;
+    r.iy[n] = static_cast<int64_t>(yy);
+    r.ix[n] = static_cast<int64_t>(xx);
+    const double ty = 1.0 - std::fabs(py - yy), tx = 1.0 - std::fabs(px - xx);
+    const double v = static_cast<double>(plane[r.iy[n] * W + r.ix[n]]);
+    r.g[n] = ty * tx;
+    r.s += ty * tx * v;
+    r.dsy += (dy == 0 ? -1.0 : 1.0) * tx * v;
+    r.dsx += (dx == 0 ? -1.0 : 1.0) * ty * v;
+  }
+  return r;
+}
+
+// Sampling position of kernel point (i, j) at output (oy, ox), rounded to float.
+void position_f(const oracle_desc* d, const float* offset, int64_t Ho, int64_t Wo, int64_t b, int64_t gk,
+                int64_t i, int64_t j, int64_t oy, int64_t ox, double* py, double* px) {
+  const int64_t KKG = d->K * d->K * (d->groups > 1 ? d->groups : 1);
+  const float dy = offset[((b * 2 * KKG + 2 * gk) * Ho + oy) * Wo + ox];
+  const float dx = offset[((b * 2 * KKG + 2 * gk + 1) * Ho + oy) * Wo + ox];
+  const float fy = static_cast<float>(oy * d->stride - d->pad + i * d->dilation) + dy;
+  const float fx = static_cast<float>(ox * d->stride - d->pad + j * d->dilation) + dx;
+  *py = static_cast<double>(fy);
+  *px = static_cast<double>(fx);
+}
+
 }  // namespace
+
+extern "C" int oracle_backward(const oracle_desc* d, const float* x, const float* offset, const float* mask,
+                               const float* weight, const float* grad_out, double* grad_x, double* grad_offset,
+                               double* grad_mask, double* grad_weight, double* grad_bias, int threads) {
+  if (!valid_desc(d) || x == nullptr || offset == nullptr || weight == nullptr || grad_out == nullptr) return -1;
+  int64_t Ho = 0, Wo = 0;
+  if (oracle_output_hw(d, &Ho, &Wo) != 0) return -1;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+  const int64_t B = d->B, Cin = d->Cin, H = d->H, W = d->W, Cout = d->Cout, K = d->K, KK = K * K;
+  const int64_t G = d->groups > 1 ? d->groups : 1, Cg = Cin / G, HoWo = Ho * Wo;
+  // gradient of the column entry (b, c, k) at output pixel pix
+  auto col_grad = [&](int64_t b, int64_t c, int64_t k, int64_t pix) {
+    double acc = 0.0;
+    for (int64_t o = 0; o < Cout; ++o)
+      acc += static_cast<double>(grad_out[(b * Cout + o) * HoWo + pix]) * static_cast<double>(weight[(o * Cin + c) * KK + k]);
+    return acc;
+  };
+  auto mask_of = [&](int64_t b, int64_t gk, int64_t pix) {
+    return mask != nullptr ? static_cast<double>(mask[(b * KK * G + gk) * HoWo + pix]) : 1.0;
+  };
+  if (grad_x != nullptr) {
+    // one (b, c) plane per iteration: every write goes to that plane
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t bc = 0; bc < B * Cin; ++bc) {
+      const int64_t b = bc / Cin, c = bc % Cin, g = c / Cg;
+      double* gx = grad_x + bc * H * W;
+      const float* plane = x + bc * H * W;
+      for (int64_t e = 0; e < H * W; ++e) gx[e] = 0.0;
+      for (int64_t k = 0; k < KK; ++k)
+        for (int64_t oy = 0; oy < Ho; ++oy)
+          for (int64_t ox = 0; ox < Wo; ++ox) {
+            const int64_t pix = oy * Wo + ox;
+            double py, px;
+            position_f(d, offset, Ho, Wo, b, g * KK + k, k / K, k % K, oy, ox, &py, &px);
+            const SampleGrad sg = sample_grad(plane, H, W, py, px);
+            const double t = col_grad(b, c, k, pix) * mask_of(b, g * KK + k, pix);
+            for (int n = 0; n < 4; ++n)
+              if (sg.inside[n]) gx[sg.iy[n] * W + sg.ix[n]] += t * sg.g[n];
+          }
+    }
+  }
+  if (grad_offset != nullptr || (grad_mask != nullptr && mask != nullptr)) {
+    // one (b, group, kernel point, pixel) per iteration: its offset pair and mask entry
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t e = 0; e < B * G * KK * HoWo; ++e) {
+      const int64_t pix = e % HoWo, gk = (e / HoWo) % (G * KK), b = e / (HoWo * G * KK);
+      const int64_t g = gk / KK, k = gk % KK;
+      double py, px;
+      position_f(d, offset, Ho, Wo, b, gk, k / K, k % K, pix / Wo, pix % Wo, &py, &px);
+      const double m = mask_of(b, gk, pix);
+      double gm = 0.0, goy = 0.0, gox = 0.0;
+      for (int64_t c = g * Cg; c < (g + 1) * Cg; ++c) {
+        const SampleGrad sg = sample_grad(x + (b * Cin + c) * H * W, H, W, py, px);
+        const double gc = col_grad(b, c, k, pix);
+        gm += gc * sg.s;
+        goy += gc * m * sg.dsy;
+        gox += gc * m * sg.dsx;
+      }
+      if (grad_offset != nullptr) {
+        grad_offset[(b * 2 * G * KK + 2 * gk) * HoWo + pix] = goy;
+        grad_offset[(b * 2 * G * KK + 2 * gk + 1) * HoWo + pix] = gox;
+      }
+      if (grad_mask != nullptr && mask != nullptr) grad_mask[(b * G * KK + gk) * HoWo + pix] = gm;
+    }
+  }
+  if (grad_weight != nullptr) {
+    // one (o, c) pair per iteration: its K*K weights
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t oc = 0; oc < Cout * Cin; ++oc) {
+      const int64_t o = oc / Cin, c = oc % Cin, g = c / Cg;
+      for (int64_t k = 0; k < KK; ++k) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+          for (int64_t pix = 0; pix < HoWo; ++pix) {
+            double py, px;
+            position_f(d, offset, Ho, Wo, b, g * KK + k, k / K, k % K, pix / Wo, pix % Wo, &py, &px);
+            const SampleGrad sg = sample_grad(x + (b * Cin + c) * H * W, H, W, py, px);
+            acc += static_cast<double>(grad_out[(b * Cout + o) * HoWo + pix]) * mask_of(b, g * KK + k, pix) * sg.s;
+          }
+        grad_weight[oc * KK + k] = acc;
+      }
+    }
+  }
+  if (grad_bias != nullptr) {
+    for (int64_t o = 0; o < Cout; ++o) {
+      double acc = 0.0;
+      for (int64_t b = 0; b < B; ++b)
+        for (int64_t pix = 0; pix < HoWo; ++pix) acc += static_cast<double>(grad_out[(b * Cout + o) * HoWo + pix]);
+      grad_bias[o] = acc;
+    }
+  }
+  return 0;
+}
 
 extern "C" int oracle_output_hw(const oracle_desc* d, int64_t* Ho, int64_t* Wo) {
   if (!valid_desc(d) || Ho == nullptr || Wo == nullptr) return -1;

@@ -83,6 +83,41 @@ int oracle_points(const oracle_desc* d, const float* x, const float* offset,
                   const int64_t* points, int64_t npts,
                   double* out, double* abs_terms, int threads);
 
+/* Gradients of y with respect to every input, for an upstream gradient gy =
+ * grad_out[B,Cout,Ho,Wo] (the gradient equation of the deformable convolution on
+ * the csdn.net tags page "可变形卷积：Deformable ConvNets", part "Deformable
+ * Convolutional Networks", section 可变形卷积 (计算梯度): the offset gradient runs
+ * through the derivative of the bilinear kernel G; the rest is the chain rule
+ * applied to the forward sum above):
+ *
+ *   Gc[b,c,k,oy,ox]   = sum_o gy[b,o,oy,ox] * W[o,c,i,j]        (gradient of one column entry)
+ *   grad_bias[o]      = sum_{b,oy,ox} gy[b,o,oy,ox]
+ *   grad_weight[o,c,i,j] = sum_{b,oy,ox} gy[b,o,oy,ox] * m_k * S(X[b,c], py_k, px_k)
+ *   grad_mask[b,gk,oy,ox]   = sum_{c in group g} Gc * S(X[b,c], py_k, px_k)
+ *   grad_offset[b,2gk,oy,ox]   = sum_{c in group g} Gc * m_k * dS/dpy
+ *   grad_offset[b,2gk+1,oy,ox] = sum_{c in group g} Gc * m_k * dS/dpx
+ *   grad_x[b,c,yy,xx] = sum_{k,oy,ox} Gc * m_k * (1-|py_k-yy|)*(1-|px_k-xx|)
+ *                       over the samples whose neighbours include (yy, xx)
+ *
+ * dS/dpy = sum over the four neighbours of s_y * (1-|px-xx|) * X[yy,xx], with
+ * s_y = -1 for yy = floor(py) and +1 for yy = floor(py)+1 (the derivative of the
+ * tent (1-|py-yy|) on the side of yy that py lies on); likewise dS/dpx.  At an
+ * integer position this is the derivative from the right, the side floor picks.
+ * Neighbours outside the image contribute zero to every term.  The positions are
+ * rounded to float (py_k = float(oy*stride - pad + i*dilation) + offset in one
+ * float addition) because floor(py) decides which side's derivative is taken:
+ * both this oracle and a float implementation then take that integer decision
+ * from the same number; everything after the rounding is in double.
+ *
+ * Outputs are doubles in the layouts of their inputs: grad_x[B,Cin,H,W],
+ * grad_offset[B,2GK^2,Ho,Wo], grad_mask[B,GK^2,Ho,Wo] (NULL if mask is NULL),
+ * grad_weight[Cout,Cin,K,K], grad_bias[Cout].  Any output may be NULL (not
+ * computed).  Each output element is written by one thread, so results do not
+ * depend on the thread count. */
+int oracle_backward(const oracle_desc* d, const float* x, const float* offset,
+                    const float* mask, const float* weight, const float* grad_out,
+                    double* grad_x, double* grad_offset, double* grad_mask,
+                    double* grad_weight, double* grad_bias, int threads);
 /* Number of threads an oracle_forward call with this request would use. */
 int oracle_threads(int threads);
 

@@ -22,6 +22,12 @@ What each pin reduces to (no pin restates the oracle's own formula):
                                 formulation; G copies of one offset field -> one group
   p12 offset/mask branch      -> torch conv2d (float64) split into 2GK^2 offset channels and
                                 the sigmoid of the other GK^2
+  p13 gradients               -> differences of sum(gy * y) from the FORWARD oracle: exact
+                                along x, weight, mask, bias (linear); central differences
+                                along the offsets inside a cell (bilinear), G = 1 and 2
+  p14 gradients, zero offsets  -> torch autograd of conv2d (float64); unfold for the mask
+                                gradient; one-sided input differences for the offsets
+  p15 gradients, all outside   -> zero, except the bias gradient sum(gy)
   golden                      -> hand-worked examples in tests/golden/
 """
 
@@ -363,7 +369,139 @@ def pin_golden(lib):
         assert np.array_equal(a[0, 0], np.array(ex["expected_abs"])), f"golden {ex['name']} abs"
 
 
+def _off_cells(rng, B, KKG, Ho, Wo):
+    """Offsets whose sampling positions sit inside a cell, at least 0.1 from its edges:
+    an integer part plus a fraction in [0.1, 0.9] (the base positions are integers)."""
+    whole = np.round(rng.standard_normal((B, 2 * KKG, Ho, Wo)) * 1.5)
+    return (whole + rng.uniform(0.1, 0.9, whole.shape)).astype(np.float32)
+
+
+def _loss(lib, x, off, m, w, b, gy, s, p, d):
+    """L = sum(gy * y) with the oracle's forward (float64)."""
+    y = oracle.forward(x, off, w, b, s, p, d, mask=m, with_abs=False, lib_path=lib)
+    return float(np.sum(gy.astype(np.float64) * y))
+
+
+def pin_p13_backward_directional(lib):
+    """Gradients against differences of L = sum(gy * y) computed by the FORWARD oracle.
+    L is linear in x, weight, mask and bias, so L(v + D) - L(v) = <grad, D> exactly for
+    any perturbation D (taken as the float32 difference actually applied).  Along the
+    offsets L is bilinear inside a cell, so the central difference (L(+D) - L(-D)) / 2
+    equals <grad, D> up to the float32 rounding of the two perturbed fields."""
+    for G, (B, Cin, H, W, Cout, K, s, p, d) in ((1, (2, 3, 6, 7, 4, 3, 1, 1, 1)),
+                                                  (2, (1, 4, 7, 6, 3, 3, 2, 1, 1)),
+                                                  (1, (1, 2, 8, 7, 3, 2, 1, 0, 2))):
+        rng = np.random.default_rng(1300 + G * 10 + K)
+        Ho, Wo = out_hw(H, W, K, s, p, d)
+        x = rng.standard_normal((B, Cin, H, W)).astype(np.float32)
+        w = rng.standard_normal((Cout, Cin, K, K)).astype(np.float32)
+        b = rng.standard_normal(Cout).astype(np.float32)
+        off = _off_cells(rng, B, G * K * K, Ho, Wo)
+        m = rng.uniform(0.1, 1.0, (B, G * K * K, Ho, Wo)).astype(np.float32)
+        gy = rng.standard_normal((B, Cout, Ho, Wo)).astype(np.float32)
+        r = oracle.backward(x, off, w, gy, s, p, d, mask=m, lib_path=lib)
+        L0 = _loss(lib, x, off, m, w, b, gy, s, p, d)
+        scale = 1.0 + abs(L0)
+
+        def lin(name, arr, grad, make):
+            v = rng.standard_normal(arr.shape)
+            moved = (arr + 0.5 * v).astype(np.float32)
+            D = moved.astype(np.float64) - arr.astype(np.float64)
+            got = _loss(lib, *make(moved)) - L0
+            want = float(np.sum(grad * D))
+            # the backward rounds positions to float32 (the forward keeps them in double):
+            # sample values then differ by about 1e-7 of their size
+            tol = 1e-5 * float(np.sum(np.abs(grad * D))) + 1e-9 * scale
+            assert abs(got - want) <= tol, f"G={G} {name}: {got} vs {want}"
+
+        lin("x", x, r["grad_x"], lambda a: (a, off, m, w, b, gy, s, p, d))
+        lin("weight", w, r["grad_weight"], lambda a: (x, off, m, a, b, gy, s, p, d))
+        lin("mask", m, r["grad_mask"], lambda a: (x, off, a, w, b, gy, s, p, d))
+        lin("bias", b, r["grad_bias"], lambda a: (x, off, m, w, a, gy, s, p, d))
+        v = rng.uniform(-1.0, 1.0, off.shape) * 0.02
+        op = (off + v).astype(np.float32)
+        om = (off - v).astype(np.float32)
+        Dp = op.astype(np.float64) - off.astype(np.float64)
+        Dm = off.astype(np.float64) - om.astype(np.float64)
+        got = (_loss(lib, x, op, m, w, b, gy, s, p, d) - _loss(lib, x, om, m, w, b, gy, s, p, d))
+        want = float(np.sum(r["grad_offset"] * (Dp + Dm)))
+        tol = 1e-5 * float(np.sum(np.abs(r["grad_offset"] * (Dp + Dm)))) + 1e-9 * scale
+        assert abs(got - want) <= tol, f"G={G} offset: {got} vs {want}"
+        # every offset channel on its own (a sign or an axis swap in one channel shows here)
+        for ch in (0, 1, 2 * G * K * K - 1):
+            v1 = np.zeros_like(off)
+            v1[:, ch] = 0.01
+            op = (off + v1).astype(np.float32)
+            om = (off - v1).astype(np.float32)
+            D = (op.astype(np.float64) - om.astype(np.float64))
+            got = _loss(lib, x, op, m, w, b, gy, s, p, d) - _loss(lib, x, om, m, w, b, gy, s, p, d)
+            want = float(np.sum(r["grad_offset"] * D))
+            tol = 1e-5 * float(np.sum(np.abs(r["grad_offset"] * D))) + 1e-9 * scale
+            assert abs(got - want) <= tol, f"G={G} offset channel {ch}: {got} vs {want}"
+
+
+def pin_p14_backward_zero_offsets(lib):
+    """Zero offsets: the gradients of a regular convolution from torch autograd of
+    F.conv2d in float64 (x, weight, bias); the mask gradient from torch's unfold (the
+    column of each kernel point times the column gradient W^T gy); the offset gradient
+    at these integer positions from the one-sided difference X[y+1] - X[y] (and
+    X[x+1] - X[x]) of the zero-padded input, since S(y + t) = (1-t) X[y] + t X[y+1]."""
+    rng = np.random.default_rng(1401)
+    B, Cin, H, W, Cout, K, s, p, d = 2, 3, 7, 6, 4, 3, 2, 1, 1
+    Ho, Wo = out_hw(H, W, K, s, p, d)
+    x = rng.standard_normal((B, Cin, H, W)).astype(np.float32)
+    w = rng.standard_normal((Cout, Cin, K, K)).astype(np.float32)
+    gy = rng.standard_normal((B, Cout, Ho, Wo)).astype(np.float32)
+    off = np.zeros((B, 2 * K * K, Ho, Wo), dtype=np.float32)
+    m = rng.uniform(0.1, 1.0, (B, K * K, Ho, Wo)).astype(np.float32)
+    r = oracle.backward(x, off, w, gy, s, p, d, mask=None, lib_path=lib)
+    xt = torch.from_numpy(x).double().requires_grad_()
+    wt = torch.from_numpy(w).double().requires_grad_()
+    bt = torch.zeros(Cout, dtype=torch.float64, requires_grad=True)
+    y = F.conv2d(xt, wt, bt, stride=s, padding=p, dilation=d)
+    y.backward(torch.from_numpy(gy).double())
+    _close(r["grad_x"], xt.grad.numpy(), 1e-10, "grad_x vs conv2d")
+    _close(r["grad_weight"], wt.grad.numpy(), 1e-10, "grad_weight vs conv2d")
+    _close(r["grad_bias"], bt.grad.numpy(), 1e-10, "grad_bias vs conv2d")
+    # column gradient per (c, k) and the columns themselves (unfold zero-pads)
+    gcol = np.einsum("ocij,bopq->bcijpq", w.astype(np.float64), gy.astype(np.float64)).reshape(B, Cin, K * K, Ho, Wo)
+    cols = F.unfold(torch.from_numpy(x).double(), K, dilation=d, padding=p, stride=s).numpy()
+    cols = cols.reshape(B, Cin, K * K, Ho, Wo)
+    rm = oracle.backward(x, off, w, gy, s, p, d, mask=m, lib_path=lib)
+    _close(rm["grad_mask"], np.sum(gcol * cols, axis=1), 1e-10, "grad_mask vs unfold")
+    # offsets: one-sided differences of the zero-padded input, one row/column past the pad
+    xp = np.zeros((B, Cin, H + 2 * p + 2, W + 2 * p + 2))
+    xp[:, :, p:p + H, p:p + W] = x
+    want = np.zeros((B, 2 * K * K, Ho, Wo))
+    for i in range(K):
+        for j in range(K):
+            k = i * K + j
+            ys = np.arange(Ho) * s + i * d          # row of the sample in padded coordinates
+            xs = np.arange(Wo) * s + j * d
+            X0 = xp[:, :, ys][:, :, :, xs]
+            Xdy = xp[:, :, ys + 1][:, :, :, xs]
+            Xdx = xp[:, :, ys][:, :, :, xs + 1]
+            mk = m[:, k][:, None].astype(np.float64)
+            want[:, 2 * k] = np.sum(gcol[:, :, k] * mk * (Xdy - X0), axis=1)
+            want[:, 2 * k + 1] = np.sum(gcol[:, :, k] * mk * (Xdx - X0), axis=1)
+    _close(rm["grad_offset"], want, 1e-10, "grad_offset at integer positions")
+
+
+def pin_p15_backward_all_outside(lib):
+    """Every sample far outside the image: the output is the bias alone, so every
+    gradient is zero except the bias's, which is the sum of gy."""
+    rng = np.random.default_rng(1501)
+    x, off, m, w, b, Ho, Wo = rand_case(rng, 2, 3, 5, 6, 4, 3, 1, 1, 1)
+    off = np.full_like(off, 1.0e3)
+    gy = rng.standard_normal((2, 4, Ho, Wo)).astype(np.float32)
+    r = oracle.backward(x, off, w, gy, 1, 1, 1, mask=m, lib_path=lib)
+    for k in ("grad_x", "grad_offset", "grad_mask", "grad_weight"):
+        assert np.all(r[k] == 0.0), f"{k} not zero with every sample outside"
+    _close(r["grad_bias"], gy.astype(np.float64).sum(axis=(0, 2, 3)), 1e-12, "grad_bias")
+
+
 ALL_PINS = [pin_p1_zero_offsets, pin_p2_integer_offsets, pin_p3_bilinear_field, pin_p4_all_outside,
             pin_p5_linear_in_mask, pin_p6_mask_absent, pin_p7_half_offsets, pin_p8_constant_input,
             pin_p9_grid_sample, pin_p10_nonfinite_offsets, pin_p11_offset_groups, pin_p12_offset_mask_branch,
-            pin_golden]
+            pin_golden, pin_p13_backward_directional, pin_p14_backward_zero_offsets,
+            pin_p15_backward_all_outside]

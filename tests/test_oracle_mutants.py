@@ -53,6 +53,23 @@ MUTANTS = [
                                     ("offset[((b * 2 * KK * G + 2 * gk + 1) *", "offset[((b * 2 * KK + 2 * gk + 1) *")]),
     ("mask_ignores_group", [("mask[((b * KK * G + gk) * Ho + oy) * Wo + ox]", "mask[((b * KK * G + k) * Ho + oy) * Wo + ox]")]),
     ("x_channel_stride", [("x + ((b * d->Cin + c) * d->H) * d->W", "x + ((b * d->Cin + c) * d->W) * d->W")]),
+    # gradients
+    ("bwd_dsy_sign", [("r.dsy += (dy == 0 ? -1.0 : 1.0) * tx * v;", "r.dsy += (dy == 0 ? 1.0 : -1.0) * tx * v;")]),
+    ("bwd_dsx_uses_tx", [("r.dsx += (dx == 0 ? -1.0 : 1.0) * ty * v;", "r.dsx += (dx == 0 ? -1.0 : 1.0) * tx * v;")]),
+    ("bwd_offset_without_mask", [("goy += gc * m * sg.dsy;", "goy += gc * sg.dsy;")]),
+    ("bwd_grad_x_without_mask", [("const double t = col_grad(b, c, k, pix) * mask_of(b, g * KK + k, pix);",
+                                  "const double t = col_grad(b, c, k, pix);")]),
+    ("bwd_grad_mask_times_mask", [("gm += gc * sg.s;", "gm += gc * m * sg.s;")]),
+    ("bwd_weight_ignores_group", [("const int64_t o = oc / Cin, c = oc % Cin, g = c / Cg;",
+                                   "const int64_t o = oc / Cin, c = oc % Cin, g = 0;")]),
+    ("bwd_offset_pair_swapped", [("grad_offset[(b * 2 * G * KK + 2 * gk) * HoWo + pix] = goy;",
+                                  "grad_offset[(b * 2 * G * KK + 2 * gk) * HoWo + pix] = gox;"),
+                                 ("grad_offset[(b * 2 * G * KK + 2 * gk + 1) * HoWo + pix] = gox;",
+                                  "grad_offset[(b * 2 * G * KK + 2 * gk + 1) * HoWo + pix] = goy;")]),
+    ("bwd_grad_x_corner_weight", [("if (sg.inside[n]) gx[sg.iy[n] * W + sg.ix[n]] += t * sg.g[n];",
+                                   "if (sg.inside[n]) gx[sg.iy[n] * W + sg.ix[n]] += t * sg.g[3 - n];")]),
+    ("bwd_position_ignores_pad", [("static_cast<float>(oy * d->stride - d->pad + i * d->dilation) + dy;",
+                                   "static_cast<float>(oy * d->stride + i * d->dilation) + dy;")]),
 ]
 
 RUNNER = """
