@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16_mfma": 2516.6, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, TFLOP/s, GB/s
 CSRC = os.path.join(ROOT, "deformable_convolution_vision_amd", "csrc")
-KERNEL_SRCS = ("dcn_internal.h", "dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip", "dcn_direct.hip")
+KERNEL_SRCS = ("dcn_internal.h", "dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip", "dcn_direct.hip", "dcn_backward.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -229,6 +229,108 @@ def bench_offset_mask(w, steps: int, warmup: int):
     }
 
 
+def bench_backward(w, steps: int, warmup: int):
+    """The gradients (dcn_backward: every gradient of the layer, one call per step) on the
+    layer's shapes with a seeded upstream gradient.  value counts the two gradient
+    products (2 x 2*B*Cout*Ho*Wo*Cin*K^2 flops); the timed region has events at its ends
+    only, and a second pass with an event after each call gives the call durations."""
+    import numpy as np
+    import torch
+
+    import deformable_convolution_vision_amd as dcn
+    import oracle
+    from deformable_convolution_vision_amd.workloads import generate, grad_output
+
+    host = generate(w)
+    gy_h = grad_output(w)
+    g = {k: (None if v is None else v.cuda()) for k, v in host.items()}
+    gy = gy_h.cuda()
+    desc = dcn.describe(g["x"], g["weight"], w.stride, w.pad, w.dilation, g["offset"])
+    nb = dcn.dcn_backward_workspace_bytes(desc)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(g["x"]), torch.empty_like(g["offset"]),
+            torch.empty_like(g["mask"]) if g["mask"] is not None else None, torch.empty_like(g["weight"]),
+            torch.empty(w.Cout, dtype=g["x"].dtype, device="cuda")]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        dcn.dcn_backward(desc, g["x"], g["offset"], g["mask"], g["weight"], gy, *outs, ws, nb, stream)
+
+    step()
+    torch.cuda.synchronize()
+    # parity on slices the oracle computes in seconds: the weight and bias gradients of
+    # the first and last output channels (they depend on those channels of grad_out
+    # only) and the input gradient of the first and last input channels (one offset
+    # group: they depend on those channels of x and weight only)
+    rtol, atol = (1e-2, 2e-3) if w.dtype == "bf16" else (1e-4, 1e-5)
+    max_rel = 0.0
+    osel = [0, w.Cout - 1]
+    ref = oracle.backward(host["x"], host["offset"], host["weight"][osel].contiguous(), gy_h[:, osel].contiguous(),
+                          w.stride, w.pad, w.dilation, mask=host["mask"], want=("grad_weight", "grad_bias"))
+    csel = [0, w.Cin - 1]
+    refx = oracle.backward(host["x"][:, csel].contiguous(), host["offset"], host["weight"][:, csel].contiguous(),
+                           gy_h, w.stride, w.pad, w.dilation, mask=host["mask"], want=("grad_x",))
+    for got, want in ((outs[3][osel], ref["grad_weight"]), (outs[4][osel], ref["grad_bias"]),
+                      (outs[0][:, csel], refx["grad_x"])):
+        got = got.float().cpu().numpy().astype(np.float64)
+        bound = rtol * np.abs(want) + atol * float(np.max(np.abs(want)))
+        max_rel = max(max_rel, float(np.max(np.abs(got - want) / np.maximum(bound, 1e-300))) * rtol)
+        if not np.all(np.abs(got - want) <= bound):
+            raise SystemExit(f"bench parity failure on {w.name}: gradient outside |d| <= {rtol}|ref| + {atol}max|ref|")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(0, sp)
+    for _ in range(steps):
+        step()
+    ev.record(1, sp)
+    ev.sync(1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev.ms(0, 1)
+    ev.close()
+    ev = HipEvents(steps + 1)
+    ev.record(0, sp)
+    for i in range(steps):
+        step()
+        ev.record(i + 1, sp)
+    ev.sync(steps)
+    per = sorted(ev.ms(i, i + 1) for i in range(steps))
+    call_mean = ev.ms(0, steps) / steps
+    ev.close()
+    ms_per_step = total_ms / steps
+    flops = 2 * w.flops
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK["bf16_mfma"] if w.dtype == "bf16" else PEAK["f32_mfma"]
+    achieved = flops / (call_mean * 1e-3) / 1e12
+    return {
+        "metric": "deform_conv2d fwd effective TFLOP/s + GB/s (c4 stride-2 bf16), % of roofline",
+        "value": round(tflops, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; shapes and value distributions of the workload)",
+        "config": {"workload": f"{w.name}: gradients of B={w.B} Cin={w.Cin} {w.H}x{w.W} -> Cout={w.Cout} "
+                               f"{w.Ho}x{w.Wo}, K={w.K} stride={w.stride} pad={w.pad} dilation={w.dilation}, "
+                               f"mask={'yes' if w.mask else 'no'} (grad x, offset, mask, weight, bias)",
+                   "variant": "backward", "plan": "dcn_backward: transposes, column-gradient MFMA product, "
+                                                   "sampling and scatter, weight-gradient MFMA product"},
+        "frac_mfma_peak": round(tflops / peak, 5),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 4), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 5), "traffic": None,
+                     "kernel": "dcn_backward (all launches of one call)", "kernel_sha": kernel_hash(),
+                     "per_launch": {"flops": flops}},
+        "kernels_us": {"call_mean": round(call_mean * 1e3, 3), "call_median": round(per[steps // 2] * 1e3, 3),
+                       "call_min": round(per[0] * 1e3, 3)},
+        "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
+        "parity_max_rel_err_sampled": max_rel,
+        "cold": None,
+        "cpu_baseline": None,
+    }
+
+
 def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: float, cold_steps: int = 0):
     import numpy as np
     import torch
@@ -239,6 +341,8 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
     w = WORKLOADS[name]
     if w.op == "offset_mask":
         return bench_offset_mask(w, steps, warmup)
+    if w.op == "backward":
+        return bench_backward(w, steps, warmup)
     host = generate(w)
     g = {k: (None if v is None else v.cuda()) for k, v in host.items()}
     desc = dcn.describe(g["x"], g["weight"], w.stride, w.pad, w.dilation, g["offset"])

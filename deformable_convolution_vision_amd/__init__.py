@@ -84,6 +84,10 @@ def load_library() -> ctypes.CDLL:
     lib.dcn_offset_mask_workspace_bytes.restype = ctypes.c_int
     lib.dcn_offset_mask.argtypes = [D, P, P, P, P, P, P, S, P]
     lib.dcn_offset_mask.restype = ctypes.c_int
+    lib.dcn_backward_workspace_bytes.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.dcn_backward_workspace_bytes.restype = ctypes.c_int
+    lib.dcn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.dcn_backward.restype = ctypes.c_int
     for name in ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_forward_staged", "dcn_stage"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -279,3 +283,48 @@ def offset_mask(input, weight_om, bias_om=None, stride=1, padding=0, dilation=1,
     with torch.cuda.device(input.device):
         dcn_offset_mask(desc, input, weight_om, bias_om, offset, mask, workspace if nbytes else None, nbytes)
     return offset, mask
+
+
+def dcn_backward_workspace_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    rc = load_library().dcn_backward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    if rc != OK:
+        raise DcnError(rc, "dcn_backward_workspace_bytes")
+    return n.value
+
+
+def dcn_backward(desc: Desc, x, offset, mask, weight, grad_out, grad_x, grad_offset, grad_mask, grad_weight,
+                 grad_bias, workspace, workspace_bytes: int, stream=None) -> None:
+    """Raw call: tensors (or integer device addresses) laid out as dcn.h states; any
+    gradient may be None (not computed)."""
+    rc = load_library().dcn_backward(ctypes.byref(desc), _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight),
+                                     _ptr(grad_out), _ptr(grad_x), _ptr(grad_offset), _ptr(grad_mask),
+                                     _ptr(grad_weight), _ptr(grad_bias), _ptr(workspace), workspace_bytes,
+                                     _stream(stream))
+    if rc != OK:
+        raise DcnError(rc, "dcn_backward")
+
+
+def deform_conv2d_backward(grad_out, input, offset, weight, stride=1, padding=0, dilation=1, mask=None,
+                           with_bias=True, workspace=None):
+    """Gradients of deform_conv2d on the GPU: returns (grad_input, grad_offset, grad_weight,
+    grad_bias or None, grad_mask or None) for the upstream gradient grad_out
+    [B, Cout, Ho, Wo]."""
+    desc = describe(input, weight, stride, padding, dilation, offset)
+    Ho, Wo = check_tensors(desc, input, offset, weight, None, mask)
+    if tuple(grad_out.shape) != (desc.batch, desc.out_channels, Ho, Wo):
+        raise ValueError(f"grad_out must be {(desc.batch, desc.out_channels, Ho, Wo)}")
+    if grad_out.dtype != input.dtype or grad_out.device != input.device or not grad_out.is_contiguous():
+        raise ValueError("grad_out must be a contiguous tensor of the input's dtype and device")
+    gx = torch.empty_like(input)
+    goff = torch.empty_like(offset)
+    gw = torch.empty_like(weight)
+    gb = torch.empty(desc.out_channels, dtype=input.dtype, device=input.device) if with_bias else None
+    gm = torch.empty_like(mask) if mask is not None else None
+    nbytes = dcn_backward_workspace_bytes(desc)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=input.device)
+    with torch.cuda.device(input.device):
+        dcn_backward(desc, input, offset, mask, weight, grad_out, gx, goff, gm, gw, gb,
+                     workspace if nbytes else None, nbytes)
+    return gx, goff, gw, gb, gm

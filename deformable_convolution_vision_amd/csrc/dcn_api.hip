@@ -416,6 +416,19 @@ int check_positions(const dcn_desc* d, int64_t K, int64_t stride, int64_t pad, i
 
 }  // namespace
 
+namespace dcn {
+
+int check_desc(const dcn_desc* d, int64_t* Ho, int64_t* Wo) {
+  if (!geometry_ok(d)) return DCN_E_ARG;
+  if (d->dtype != DCN_F32 && d->dtype != DCN_BF16) return DCN_E_UNSUPPORTED;
+  *Ho = out_extent(d->height, d->kernel_size, d->stride, d->pad, d->dilation);
+  *Wo = out_extent(d->width, d->kernel_size, d->stride, d->pad, d->dilation);
+  if (*Ho < 1 || *Wo < 1) return DCN_E_ARG;
+  return check_positions(d, d->kernel_size, d->stride, d->pad, d->dilation, *Ho, *Wo);
+}
+
+}  // namespace dcn
+
 extern "C" int dcn_output_hw(const dcn_desc* desc, int64_t* out_h, int64_t* out_w) {
   if (out_h == nullptr || out_w == nullptr || !geometry_ok(desc)) return DCN_E_ARG;
   const int64_t ho = out_extent(desc->height, desc->kernel_size, desc->stride, desc->pad, desc->dilation);

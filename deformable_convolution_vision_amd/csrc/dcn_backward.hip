@@ -1,0 +1,603 @@
+// dcn_backward.hip -- gfx950 gradients of the modulated deformable convolution.
+//
+// For an upstream gradient gy[B][Cout][Ho][Wo], with the column entry
+// col[b][c*K^2+k][p] = m_k * S(x[b,c], py_k, px_k) of the forward's deformable
+// im2col (p an output pixel, S the bilinear sample with zero outside the image):
+//
+//   gcol[b][r][p]   = sum_o W[o][r] * gy[b][o][p]              (r = c*K^2 + k)
+//   grad_weight[o][r] = sum_{b,p} gy[b][o][p] * col[b][r][p]
+//   grad_bias[o]    = sum_{b,p} gy[b][o][p]
+//   grad_mask       = sum_c gcol * S
+//   grad_offset     = sum_c gcol * m * (dS/dpy, dS/dpx)
+//   grad_x          = the column gradient times m, scattered to the four neighbours
+//                     of each sample with their bilinear weights
+//
+// The offset gradient runs through the derivative of the bilinear kernel (the
+// gradient equation of the csdn.net tags page "可变形卷积：Deformable ConvNets",
+// part "Deformable Convolutional Networks", section 可变形卷积); the rest is the
+// chain rule through the forward sum (same page, deformable-convolution equation,
+// with the DCNv2 modulation scalar of section 3.2).  At an integer position the
+// derivative is the one from the right (the side floor picks); positions are formed
+// in fp32 as in the forward.
+//
+// Kernels, in launch order:
+//   prep_w   W [Cout][R] -> Wt [R][Coutp] (the column-gradient product's first operand)
+//   prep_gy  gy -> gyT [B][P][Coutp] and gyP [B][Cout][Pp] (both zero-padded)
+//   fill     zero the fp32 accumulators
+//   gemm     gcol[b] = Wt x gyT[b]^T (MFMA, both operands contiguous along the reduction)
+//   sample   per (b, group, channel block, kernel point, pixel): the sample's corners
+//            and weights once, then for each channel the column entry (for the
+//            weight gradient), the mask and offset partial sums and the four
+//            scattered input-gradient contributions (fp32 atomics)
+//   gemm     grad_weight = sum_b gyP[b] x col[b]^T, the reduction split over workgroups
+//            (fp32 atomics into a zeroed accumulator)
+//   bias     one workgroup per output channel
+//   convert  fp32 accumulators -> the element type
+// The gradient products run on MFMA 32x32x16 bf16 (bf16 data) or 32x32x2 fp32.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "dcn.h"
+#include "dcn_internal.h"
+
+namespace dcn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBT = 256;   // threads per workgroup of the elementwise kernels
+constexpr int kCB = 32;    // channels per thread in the sample kernel
+
+template <typename T>
+__device__ __forceinline__ float to_f(T v);
+template <>
+__device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f<uint16_t>(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+
+template <typename T>
+__device__ __forceinline__ T from_f(float v);
+template <>
+__device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t from_f<uint16_t>(float v) {   // round to nearest even
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+struct BwdArgs {
+  const void* x;        // [B][Cin][H][W]
+  const void* offset;   // [B][2GK^2][Ho][Wo]
+  const void* mask;     // [B][GK^2][Ho][Wo] or null
+  const void* w;        // [Cout][Cin][K][K] = [Cout][R]
+  const void* gy;       // [B][Cout][Ho][Wo]
+  void* wt;             // [R][Coutp]
+  void* gyt;            // [B][P][Coutp]
+  void* gyp;            // [B][Cout][Pp]
+  void* col;            // [B][R][Pp] or null (no weight gradient)
+  float* gcol;          // [B][R][P] or null (no input, offset or mask gradient)
+  float* gx32;          // [B][Cin][H][W] or null
+  float* goff32;        // [B][2GK^2][P] or null
+  float* gm32;          // [B][GK^2][P] or null
+  int B, Cin, H, W, Cout, K, KK, stride, pad, dil, Ho, Wo, P, Pp, Coutp, R, G, Cg, NCB;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_prep_w(BwdArgs a) {
+  const int e = blockIdx.x * kBT + threadIdx.x;
+  if (e >= a.R * a.Coutp) return;
+  const int o = e % a.Coutp, r = e / a.Coutp;
+  const T* w = static_cast<const T*>(a.w);
+  static_cast<T*>(a.wt)[e] = o < a.Cout ? w[static_cast<size_t>(o) * a.R + r] : T(0);
+}
+
+// 32 x 32 tiles of (output channel, pixel) through LDS: gyP keeps gy's layout with
+// the pixel stride padded to Pp; gyT is its transpose with the channel stride
+// padded to Coutp.  Padding is written as zeros.
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_prep_gy(BwdArgs a) {
+  __shared__ T tile[32][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int p0 = blockIdx.x * 32, o0 = blockIdx.y * 32, b = blockIdx.z;
+  const T* gy = static_cast<const T*>(a.gy) + static_cast<size_t>(b) * a.Cout * a.P;
+  T* gyp = static_cast<T*>(a.gyp) + static_cast<size_t>(b) * a.Cout * a.Pp;
+  T* gyt = static_cast<T*>(a.gyt) + static_cast<size_t>(b) * a.P * a.Coutp;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = o0 + ty + 8 * i, p = p0 + tx;
+    const T v = (o < a.Cout && p < a.P) ? gy[static_cast<size_t>(o) * a.P + p] : T(0);
+    tile[ty + 8 * i][tx] = v;
+    if (o < a.Cout && p < a.Pp) gyp[static_cast<size_t>(o) * a.Pp + p] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = p0 + ty + 8 * i, o = o0 + tx;
+    if (p < a.P && o < a.Coutp) gyt[static_cast<size_t>(p) * a.Coutp + o] = tile[tx][ty + 8 * i];
+  }
+}
+
+__global__ __launch_bounds__(kBT) void bwd_fill_zero(float* p, int n) {
+  const int e = blockIdx.x * kBT + threadIdx.x;
+  if (e < n) p[e] = 0.f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_fill_zero_t(T* p, int n) {
+  const int e = blockIdx.x * kBT + threadIdx.x;
+  if (e < n) p[e] = T(0);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_bias(const T* gy, T* gb, int B, int Cout, int P) {
+  __shared__ float part[kBT / 64];
+  const int o = blockIdx.x;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const T* row = gy + (static_cast<size_t>(b) * Cout + o) * P;
+    for (int p = threadIdx.x; p < P; p += kBT) s += to_f(row[p]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) gb[o] = from_f<T>(part[0] + part[1] + part[2] + part[3]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_convert(const float* src, T* dst, int n) {
+  const int e = blockIdx.x * kBT + threadIdx.x;
+  if (e < n) dst[e] = from_f<T>(src[e]);
+}
+
+// One thread per (b, group, channel block, kernel point, pixel), pixels fastest.
+// Threads with a pixel in the padding [P, Pp) write the zero padding of col.
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_sample(BwdArgs a) {
+  const long long e = static_cast<long long>(blockIdx.x) * kBT + threadIdx.x;
+  const long long total = static_cast<long long>(a.B) * a.G * a.NCB * a.KK * a.Pp;
+  if (e >= total) return;
+  const int p = static_cast<int>(e % a.Pp);
+  long long t = e / a.Pp;
+  const int k = static_cast<int>(t % a.KK);
+  t /= a.KK;
+  const int cb = static_cast<int>(t % a.NCB);
+  t /= a.NCB;
+  const int g = static_cast<int>(t % a.G), b = static_cast<int>(t / a.G);
+  const int c0 = g * a.Cg + cb * kCB, c1 = min(c0 + kCB, (g + 1) * a.Cg);
+  T* col = static_cast<T*>(a.col);
+  if (p >= a.P) {
+    if (col != nullptr)
+      for (int c = c0; c < c1; ++c) col[(static_cast<size_t>(b) * a.R + c * a.KK + k) * a.Pp + p] = T(0);
+    return;
+  }
+  const int gk = g * a.KK + k, GKK = a.G * a.KK;
+  const int oy = p / a.Wo, ox = p - (p / a.Wo) * a.Wo, i = k / a.K, j = k - (k / a.K) * a.K;
+  const T* off = static_cast<const T*>(a.offset);
+  const float dy = to_f(off[(static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p]);
+  const float dx = to_f(off[(static_cast<size_t>(b) * 2 * GKK + 2 * gk + 1) * a.P + p]);
+  const float py = static_cast<float>(oy * a.stride - a.pad + i * a.dil) + dy;
+  const float px = static_cast<float>(ox * a.stride - a.pad + j * a.dil) + dx;
+  const float m = a.mask != nullptr ? to_f(static_cast<const T*>(a.mask)[(static_cast<size_t>(b) * GKK + gk) * a.P + p])
+                                    : 1.f;
+  // corners and weights; a position with no neighbour in the image (or NaN) has none.
+  // At py == -1 the cell is [-1, 0): row 0 has weight 0 but its derivative counts.
+  const bool any = py >= -1.f && py < static_cast<float>(a.H) && px >= -1.f && px < static_cast<float>(a.W);
+  const float y0f = any ? floorf(py) : 0.f, x0f = any ? floorf(px) : 0.f;
+  const float ly = py - y0f, lx = px - x0f;
+  const int y0 = static_cast<int>(y0f), x0 = static_cast<int>(x0f);
+  const bool iy0 = any && y0 >= 0, iy1 = any && y0 + 1 < a.H, ix0 = any && x0 >= 0, ix1 = any && x0 + 1 < a.W;
+  const bool in00 = iy0 && ix0, in01 = iy0 && ix1, in10 = iy1 && ix0, in11 = iy1 && ix1;
+  const float w00 = (1.f - ly) * (1.f - lx), w01 = (1.f - ly) * lx, w10 = ly * (1.f - lx), w11 = ly * lx;
+  const int q00 = y0 * a.W + x0;
+  const int HW = a.H * a.W;
+  const T* x = static_cast<const T*>(a.x);
+  const bool grads = a.gcol != nullptr;
+  float gm = 0.f, goy = 0.f, gox = 0.f;
+  for (int c = c0; c < c1; ++c) {
+    const size_t pl = (static_cast<size_t>(b) * a.Cin + c) * HW;
+    const float v00 = in00 ? to_f(x[pl + q00]) : 0.f;
+    const float v01 = in01 ? to_f(x[pl + q00 + 1]) : 0.f;
+    const float v10 = in10 ? to_f(x[pl + q00 + a.W]) : 0.f;
+    const float v11 = in11 ? to_f(x[pl + q00 + a.W + 1]) : 0.f;
+    const float s = w00 * v00 + w01 * v01 + w10 * v10 + w11 * v11;
+    const size_t r = static_cast<size_t>(b) * a.R + c * a.KK + k;
+    if (col != nullptr) col[r * a.Pp + p] = from_f<T>(m * s);
+    if (grads) {
+      const float gc = a.gcol[r * a.P + p];
+      gm += gc * s;
+      goy += gc * ((1.f - lx) * (v10 - v00) + lx * (v11 - v01));
+      gox += gc * ((1.f - ly) * (v01 - v00) + ly * (v11 - v10));
+      if (a.gx32 != nullptr) {
+        const float tg = gc * m;
+        float* gx = a.gx32 + pl + q00;
+        if (in00) unsafeAtomicAdd(gx, tg * w00);
+        if (in01) unsafeAtomicAdd(gx + 1, tg * w01);
+        if (in10) unsafeAtomicAdd(gx + a.W, tg * w10);
+        if (in11) unsafeAtomicAdd(gx + a.W + 1, tg * w11);
+      }
+    }
+  }
+  if (grads) {
+    if (a.goff32 != nullptr) {
+      float* go = a.goff32 + (static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p;
+      unsafeAtomicAdd(go, goy * m);
+      unsafeAtomicAdd(go + a.P, gox * m);
+    }
+    if (a.gm32 != nullptr) unsafeAtomicAdd(a.gm32 + (static_cast<size_t>(b) * GKK + gk) * a.P + p, gm);
+  }
+}
+
+// C[z] (+)= sum over the reduction of A[m][k] * Bm[n][k]: both operands row-major with
+// the reduction contiguous (rows padded with zeros to Kd, a multiple of 8).  The
+// reduction runs over nseg segments of Kd (operand strides sAs, sBs), split evenly
+// over ksplit workgroups per output tile (atomics into a zeroed C when ksplit > 1).
+// blockIdx.z = zb * ksplit + ks, zb selecting independent problems (strides sAz, sBz,
+// sCz).  A 128 x 128 output tile per workgroup, four waves of 64 x 64, 32-deep chunks
+// staged through LDS with the next chunk's loads in flight during the multiply.
+template <typename T>
+struct GemmArgs {
+  const T* A;
+  const T* Bm;
+  float* C;
+  int M, N, Kd, lda, ldb, ldc, nseg, ksplit;
+  long long sAs, sBs, sAz, sBz, sCz;
+};
+
+constexpr int kGM = 128, kGN = 128, kGK = 32;
+
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_gemm_nt(GemmArgs<T> g) {
+  constexpr bool kBF = sizeof(T) == 2;
+  constexpr int VE = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte vector
+  constexpr int VPR = kGK / VE;                           // vectors per tile row
+  constexpr int NV = kGM * VPR / 256;                     // vectors per thread and operand
+  constexpr int LDT = kGK + VE;                           // LDS row stride in elements
+  __shared__ __attribute__((aligned(16))) T As[kGM * LDT];
+  __shared__ __attribute__((aligned(16))) T Bs[kGN * LDT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kGN;
+  const int zb = blockIdx.z / g.ksplit, ks = blockIdx.z - zb * g.ksplit;
+  const T* A = g.A + zb * g.sAz;
+  const T* Bm = g.Bm + zb * g.sBz;
+  float* C = g.C + zb * g.sCz;
+  const int kchunks = (g.Kd + kGK - 1) / kGK;
+  const int total = kchunks * g.nseg;
+  const int per = (total + g.ksplit - 1) / g.ksplit;
+  const int t0 = ks * per, t1 = min(total, t0 + per);
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
+  uint4 ra[NV], rb[NV];
+  auto gload = [&](int t) {
+    const int seg = t / kchunks, kc = t - seg * kchunks;
+    const T* Ap = A + seg * g.sAs;
+    const T* Bp = Bm + seg * g.sBs;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int idx = tid + v * 256, row = idx / VPR, k = kc * kGK + (idx % VPR) * VE;
+      const int ma = m0 + row, nb = n0 + row;
+      ra[v] = (ma < g.M && k < g.Kd) ? *reinterpret_cast<const uint4*>(Ap + static_cast<size_t>(ma) * g.lda + k)
+                                     : make_uint4(0, 0, 0, 0);
+      rb[v] = (nb < g.N && k < g.Kd) ? *reinterpret_cast<const uint4*>(Bp + static_cast<size_t>(nb) * g.ldb + k)
+                                     : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (t0 < t1) gload(t0);
+  for (int t = t0; t < t1; ++t) {
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int idx = tid + v * 256, row = idx / VPR, kv = idx % VPR;
+      *reinterpret_cast<uint4*>(As + row * LDT + kv * VE) = ra[v];
+      *reinterpret_cast<uint4*>(Bs + row * LDT + kv * VE) = rb[v];
+    }
+    __syncthreads();
+    if (t + 1 < t1) gload(t + 1);
+    if constexpr (kBF) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 av[2], bv[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          av[q] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + q * 32 + l32) * LDT + h * 16 + lh * 8);
+          bv[q] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + q * 32 + l32) * LDT + h * 16 + lh * 8);
+        }
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < 2; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < kGK / 2; ++kk) {
+        float av[2], bv[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          av[q] = As[(wm * 64 + q * 32 + l32) * LDT + 2 * kk + lh];
+          bv[q] = Bs[(wn * 64 + q * 32 + l32) * LDT + 2 * kk + lh];
+        }
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < 2; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+      }
+    }
+  }
+  if (t0 >= t1) return;
+  // accumulator element r of a 32x32 block: row 8*(r/4) + 4*lh + r%4, column l32
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int cc = n0 + wn * 64 + tn * 32 + l32;
+        if (row < g.M && cc < g.N) {
+          float* dst = C + static_cast<size_t>(row) * g.ldc + cc;
+          if (g.ksplit > 1) unsafeAtomicAdd(dst, acc[tm][tn][r]);
+          else *dst = acc[tm][tn][r];
+        }
+      }
+}
+
+int64_t rup(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Workspace layout of one backward call.
+struct BwdPlan {
+  int64_t Ho = 0, Wo = 0, P = 0, Pp = 0, Coutp = 0, R = 0, G = 1;
+  size_t o_wt = 0, o_gyt = 0, o_gyp = 0, o_col = 0, o_gcol = 0, o_gx = 0, o_gw = 0, o_goff = 0, o_gm = 0;
+  size_t bytes = 0;
+};
+
+int bwd_plan(const dcn_desc* d, BwdPlan* p) {
+  int rc = check_desc(d, &p->Ho, &p->Wo);
+  if (rc != DCN_OK) return rc;
+  const int64_t B = d->batch, Cin = d->in_channels, Cout = d->out_channels, KK = d->kernel_size * d->kernel_size;
+  p->G = d->offset_groups > 1 ? d->offset_groups : 1;
+  p->P = p->Ho * p->Wo;
+  p->Pp = rup(p->P, 8);
+  p->Coutp = rup(Cout > 0 ? Cout : 1, 8);
+  p->R = Cin * KK;
+  const double lim = 2147483647.0;
+  const double Bd = static_cast<double>(B);
+  if (Bd * p->R * p->Pp > lim || Bd * Cin * d->height * d->width > lim || Bd * p->Coutp * p->Pp > lim ||
+      static_cast<double>(p->R) * p->Coutp > lim || Bd * 2 * p->G * KK * p->P > lim ||
+      static_cast<double>(Cout) * p->R > lim)
+    return DCN_E_UNSUPPORTED;
+  const size_t es = d->dtype == DCN_BF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    const size_t at = o;
+    o += align256(n);
+    return at;
+  };
+  p->o_wt = take(static_cast<size_t>(p->R * p->Coutp) * es);
+  p->o_gyt = take(static_cast<size_t>(B * p->P * p->Coutp) * es);
+  p->o_gyp = take(static_cast<size_t>(B * Cout * p->Pp) * es);
+  p->o_col = take(static_cast<size_t>(B * p->R * p->Pp) * es);
+  p->o_gcol = take(static_cast<size_t>(B * p->R * p->P) * 4);
+  p->o_gx = take(static_cast<size_t>(B * Cin * d->height * d->width) * 4);
+  p->o_gw = take(static_cast<size_t>(Cout * p->R) * 4);
+  p->o_goff = take(static_cast<size_t>(B * 2 * p->G * KK * p->P) * 4);
+  p->o_gm = take(static_cast<size_t>(B * p->G * KK * p->P) * 4);
+  p->bytes = o;
+  return DCN_OK;
+}
+
+hipError_t launch1(const void* fn, int64_t n, void** args, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>((n + kBT - 1) / kBT)), dim3(kBT), args, 0, s);
+}
+
+hipError_t zero_f32(float* p, int64_t n, hipStream_t s) {
+  int nn = static_cast<int>(n);
+  void* args[] = {&p, &nn};
+  return launch1(reinterpret_cast<const void*>(&bwd_fill_zero), n, args, s);
+}
+
+template <typename T>
+hipError_t convert(const float* src, void* dst, int64_t n, hipStream_t s) {
+  T* d = static_cast<T*>(dst);
+  int nn = static_cast<int>(n);
+  void* args[] = {&src, &d, &nn};
+  return launch1(reinterpret_cast<const void*>(&bwd_convert<T>), n, args, s);
+}
+
+template <typename T>
+hipError_t gemm(const GemmArgs<T>& g, int zb, hipStream_t s) {
+  GemmArgs<T> gg = g;
+  void* args[] = {&gg};
+  const dim3 grid(static_cast<unsigned>((g.N + kGN - 1) / kGN), static_cast<unsigned>((g.M + kGM - 1) / kGM),
+                  static_cast<unsigned>(zb * g.ksplit));
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_gemm_nt<T>), grid, dim3(256), args, 0, s);
+}
+
+#define BWD_TRY(e)                          \
+  do {                                      \
+    if ((e) != hipSuccess) return DCN_E_HIP; \
+  } while (0)
+
+template <typename T>
+int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void* offset, const void* mask,
+                 const void* weight, const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
+                 void* grad_weight, void* grad_bias, unsigned char* ws, hipStream_t s) {
+  BwdArgs a{};
+  a.x = x;
+  a.offset = offset;
+  a.mask = mask;
+  a.w = weight;
+  a.gy = grad_out;
+  a.B = static_cast<int>(d->batch);
+  a.Cin = static_cast<int>(d->in_channels);
+  a.H = static_cast<int>(d->height);
+  a.W = static_cast<int>(d->width);
+  a.Cout = static_cast<int>(d->out_channels);
+  a.K = static_cast<int>(d->kernel_size);
+  a.KK = a.K * a.K;
+  a.stride = static_cast<int>(d->stride);
+  a.pad = static_cast<int>(d->pad);
+  a.dil = static_cast<int>(d->dilation);
+  a.Ho = static_cast<int>(p.Ho);
+  a.Wo = static_cast<int>(p.Wo);
+  a.P = static_cast<int>(p.P);
+  a.Pp = static_cast<int>(p.Pp);
+  a.Coutp = static_cast<int>(p.Coutp);
+  a.R = static_cast<int>(p.R);
+  a.G = static_cast<int>(p.G);
+  a.Cg = a.Cin / a.G;
+  a.NCB = (a.Cg + kCB - 1) / kCB;
+  a.wt = ws + p.o_wt;
+  a.gyt = ws + p.o_gyt;
+  a.gyp = ws + p.o_gyp;
+  const bool need_gcol = grad_x != nullptr || grad_offset != nullptr || (grad_mask != nullptr && mask != nullptr);
+  a.col = grad_weight != nullptr ? static_cast<void*>(ws + p.o_col) : nullptr;
+  a.gcol = need_gcol ? reinterpret_cast<float*>(ws + p.o_gcol) : nullptr;
+  a.gx32 = grad_x != nullptr ? reinterpret_cast<float*>(ws + p.o_gx) : nullptr;
+  a.goff32 = grad_offset != nullptr ? reinterpret_cast<float*>(ws + p.o_goff) : nullptr;
+  a.gm32 = (grad_mask != nullptr && mask != nullptr) ? reinterpret_cast<float*>(ws + p.o_gm) : nullptr;
+  float* gw32 = reinterpret_cast<float*>(ws + p.o_gw);
+  const int64_t nx = static_cast<int64_t>(a.B) * a.Cin * a.H * a.W;
+  const int64_t noff = static_cast<int64_t>(a.B) * 2 * a.G * a.KK * a.P;
+  const int64_t nm = noff / 2;
+  const int64_t nw = static_cast<int64_t>(a.Cout) * a.R;
+  void* args[] = {&a};
+
+  if (need_gcol) {
+    BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_prep_w<T>), static_cast<int64_t>(a.R) * a.Coutp, args, s));
+  }
+  if (need_gcol || grad_weight != nullptr) {
+    const dim3 grid(static_cast<unsigned>((a.Pp + 31) / 32), static_cast<unsigned>((a.Coutp + 31) / 32),
+                    static_cast<unsigned>(a.B));
+    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_gy<T>), grid, dim3(kBT), args, 0, s));
+  }
+  if (a.gx32 != nullptr) BWD_TRY(zero_f32(a.gx32, nx, s));
+  if (a.goff32 != nullptr) BWD_TRY(zero_f32(a.goff32, noff, s));
+  if (a.gm32 != nullptr) BWD_TRY(zero_f32(a.gm32, nm, s));
+  if (grad_weight != nullptr) BWD_TRY(zero_f32(gw32, nw, s));
+  if (need_gcol) {
+    GemmArgs<T> g{};
+    g.A = static_cast<const T*>(a.wt);
+    g.Bm = static_cast<const T*>(a.gyt);
+    g.C = a.gcol;
+    g.M = a.R;
+    g.N = a.P;
+    g.Kd = a.Coutp;
+    g.lda = g.ldb = a.Coutp;
+    g.ldc = a.P;
+    g.nseg = 1;
+    g.ksplit = 1;
+    g.sAz = 0;
+    g.sBz = static_cast<long long>(a.P) * a.Coutp;
+    g.sCz = static_cast<long long>(a.R) * a.P;
+    BWD_TRY(gemm<T>(g, a.B, s));
+  }
+  if (need_gcol || grad_weight != nullptr) {
+    const int64_t n = static_cast<int64_t>(a.B) * a.G * a.NCB * a.KK * a.Pp;
+    BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_sample<T>), n, args, s));
+  }
+  if (grad_weight != nullptr) {
+    GemmArgs<T> g{};
+    g.A = static_cast<const T*>(a.gyp);
+    g.Bm = static_cast<const T*>(a.col);
+    g.C = gw32;
+    g.M = a.Cout;
+    g.N = a.R;
+    g.Kd = a.Pp;
+    g.lda = g.ldb = a.Pp;
+    g.ldc = a.R;
+    g.nseg = a.B;
+    g.sAs = static_cast<long long>(a.Cout) * a.Pp;
+    g.sBs = static_cast<long long>(a.R) * a.Pp;
+    // split the reduction until the output tiles and splits give about two workgroups per CU
+    const int tiles = ((a.Cout + kGM - 1) / kGM) * ((a.R + kGN - 1) / kGN);
+    const int chunks = ((a.Pp + kGK - 1) / kGK) * a.B;
+    int ks = 1;
+    while (tiles * ks < 512 && ks * 2 <= chunks / 4) ks *= 2;
+    g.ksplit = ks;
+    BWD_TRY(gemm<T>(g, 1, s));
+    BWD_TRY(convert<T>(gw32, grad_weight, nw, s));
+  }
+  if (grad_bias != nullptr && a.Cout > 0) {
+    const T* gy = static_cast<const T*>(grad_out);
+    T* gb = static_cast<T*>(grad_bias);
+    int B = a.B, Cout = a.Cout, P = a.P;
+    void* bargs[] = {&gy, &gb, &B, &Cout, &P};
+    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_bias<T>), dim3(a.Cout), dim3(kBT), bargs, 0, s));
+  }
+  if (a.gx32 != nullptr) BWD_TRY(convert<T>(a.gx32, grad_x, nx, s));
+  if (a.goff32 != nullptr) BWD_TRY(convert<T>(a.goff32, grad_offset, noff, s));
+  if (a.gm32 != nullptr) BWD_TRY(convert<T>(a.gm32, grad_mask, nm, s));
+  return DCN_OK;
+}
+
+// Outputs of an empty problem (B == 0 or Cout == 0) that still have elements: the
+// sums over nothing are zero.
+template <typename T>
+int zero_outputs(const dcn_desc* d, const BwdPlan& p, void* grad_x, void* grad_offset, void* grad_mask,
+                 const void* mask, void* grad_weight, void* grad_bias, hipStream_t s) {
+  const int64_t B = d->batch, KK = d->kernel_size * d->kernel_size;
+  struct Out {
+    void* ptr;
+    int64_t n;
+  } outs[] = {{grad_x, B * d->in_channels * d->height * d->width},
+              {grad_offset, B * 2 * p.G * KK * p.P},
+              {mask != nullptr ? grad_mask : nullptr, B * p.G * KK * p.P},
+              {grad_weight, d->out_channels * p.R},
+              {grad_bias, d->out_channels}};
+  for (const Out& o : outs) {
+    if (o.ptr == nullptr || o.n == 0) continue;
+    T* ptr = static_cast<T*>(o.ptr);
+    int n = static_cast<int>(o.n);
+    void* args[] = {&ptr, &n};
+    BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_fill_zero_t<T>), o.n, args, s));
+  }
+  return DCN_OK;
+}
+
+}  // namespace
+}  // namespace dcn
+
+extern "C" int dcn_backward_workspace_bytes(const dcn_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return DCN_E_ARG;
+  dcn::BwdPlan p;
+  const int rc = dcn::bwd_plan(desc, &p);
+  if (rc != DCN_OK) return rc;
+  *bytes = (desc->batch == 0 || desc->out_channels == 0) ? 0 : p.bytes;
+  return DCN_OK;
+}
+
+extern "C" int dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                            const void* weight, const void* grad_out, void* grad_x, void* grad_offset,
+                            void* grad_mask, void* grad_weight, void* grad_bias, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  dcn::BwdPlan p;
+  const int rc = dcn::bwd_plan(desc, &p);
+  if (rc != DCN_OK) return rc;
+  const bool bf16 = desc->dtype == DCN_BF16;
+  if (desc->batch == 0 || desc->out_channels == 0)
+    return bf16 ? dcn::zero_outputs<uint16_t>(desc, p, grad_x, grad_offset, grad_mask, mask, grad_weight, grad_bias,
+                                              stream)
+                : dcn::zero_outputs<float>(desc, p, grad_x, grad_offset, grad_mask, mask, grad_weight, grad_bias,
+                                           stream);
+  if (x == nullptr || offset == nullptr || weight == nullptr || grad_out == nullptr) return DCN_E_ARG;
+  if (workspace == nullptr || workspace_bytes < p.bytes || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return DCN_E_WORKSPACE;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  return bf16 ? dcn::run_backward<uint16_t>(desc, p, x, offset, mask, weight, grad_out, grad_x, grad_offset, grad_mask,
+                                            grad_weight, grad_bias, ws, stream)
+              : dcn::run_backward<float>(desc, p, x, offset, mask, weight, grad_out, grad_x, grad_offset, grad_mask,
+                                         grad_weight, grad_bias, ws, stream);
+}

@@ -6,7 +6,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct dcn_desc;
+
 namespace dcn {
+
+// Descriptor checks shared by every entry point: geometry, dtype, the output size
+// (Ho, Wo >= 1) and float-exact base positions.  DCN_OK or a negative dcn_status.
+int check_desc(const dcn_desc* d, int64_t* Ho, int64_t* Wo);
 
 // Everything the fused kernel needs; all sizes fit int32 (checked on the host).
 struct FusedArgs {

@@ -92,6 +92,8 @@ WORKLOADS = {
     "c4_g4": Workload("c4_g4", "bf16", 2, 256, 100, 168, 256, 3, 2, 1, 1, 50, 84,
                       offset="normal:1", mask="sigmoid", bias=None, seed=1005, groups=4),
     # the c4 layer's offset/mask convolution: 3*K^2 = 27 outputs (offset field and mask)
+    "c4_bwd": Workload("c4_bwd", "bf16", 2, 256, 100, 168, 256, 3, 2, 1, 1, 50, 84,
+                       offset="normal:1", mask="sigmoid", bias=None, seed=1007, op="backward"),
     "c4_om": Workload("c4_om", "bf16", 2, 256, 100, 168, 27, 3, 2, 1, 1, 50, 84,
                       offset="normal:1", mask=None, bias="normal:0.1", seed=1006, op="offset_mask"),
 }
@@ -138,6 +140,14 @@ def generate(w: Workload, seed: int | None = None) -> dict[str, torch.Tensor | N
     cast = (lambda t: None if t is None else t.to(dt).contiguous())
     return {"x": cast(x), "offset": cast(offset), "mask": cast(mask), "weight": cast(weight),
             "bias": cast(bias)}
+
+
+def grad_output(w: Workload, seed: int | None = None) -> torch.Tensor:
+    """Seeded upstream gradient [B, Cout, Ho, Wo] for a backward call: N(0, 1) in the
+    workload's element type (CPU)."""
+    g = torch.Generator().manual_seed((w.seed if seed is None else seed) + 7919)
+    gy = torch.randn((w.B, w.Cout, w.Ho, w.Wo), generator=g, dtype=torch.float32)
+    return gy.to(torch.bfloat16 if w.dtype == "bf16" else torch.float32)
 
 
 def custom(name: str, dtype: str, B: int, Cin: int, H: int, W: int, Cout: int, K: int,

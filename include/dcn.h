@@ -157,6 +157,33 @@ int dcn_offset_mask_workspace_bytes(const dcn_desc* desc, size_t* bytes);
 int dcn_offset_mask(const dcn_desc* desc, const void* x, const void* weight_om, const void* bias_om,
                     void* offset, void* mask, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Gradients of dcn_forward (the gradient equation of the csdn.net tags page
+ * "可变形卷积：Deformable ConvNets", part "Deformable Convolutional Networks",
+ * section on deformable convolution: the offset gradient runs through the
+ * derivative of the bilinear kernel; the other gradients follow from the chain rule
+ * through the forward sum).  For the layer `desc` and its inputs x, offset, mask
+ * (NULL: DCNv1), weight as dcn_forward takes them, and grad_out [B,Cout,Ho,Wo] (the
+ * gradient of a loss with respect to out), writes
+ *   grad_x [B,Cin,H,W], grad_offset [B,2GK^2,Ho,Wo], grad_mask [B,GK^2,Ho,Wo],
+ *   grad_weight [Cout,Cin,K,K], grad_bias [Cout]
+ * in desc's dtype.  Any gradient pointer may be NULL (not computed); grad_mask is
+ * ignored when mask is NULL.  Where a sampling position is an integer the offset
+ * gradient is the derivative from the right.  Arithmetic: positions and bilinear
+ * weights in fp32 as in the forward; the two gradient products on MFMA (bf16 data
+ * with fp32 accumulation; fp32 data in fp32), the weight gradient's columns rounded
+ * to dtype; every sum accumulates in fp32 (the input, offset, mask and weight
+ * gradients with atomic adds, so their rounding order varies between calls) and is
+ * rounded to dtype once.  The workspace (256-byte aligned, dcn_backward_workspace_bytes)
+ * holds the transposed weight and grad_out, the columns, the column gradients and the
+ * fp32 accumulators.  Device pointers; asynchronous on `stream`; the caller owns every
+ * buffer.  Errors as for dcn_forward, checked before any launch (outputs untouched).
+ * B == 0 or Cout == 0: the gradients that have elements are written as zeros. */
+int dcn_backward_workspace_bytes(const dcn_desc* desc, size_t* bytes);
+int dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                 const void* weight, const void* grad_out, void* grad_x, void* grad_offset,
+                 void* grad_mask, void* grad_weight, void* grad_bias, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* dcn_status_str(int status);
 

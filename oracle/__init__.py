@@ -157,14 +157,14 @@ def points(x, offset, weight, pts, bias=None, stride=1, padding=0, dilation=1, m
 
 
 def backward(x, offset, weight, grad_out, stride=1, padding=0, dilation=1, mask=None, threads=0,
-             lib_path: str = LIB):
+             want=("grad_x", "grad_offset", "grad_mask", "grad_weight", "grad_bias"), lib_path: str = LIB):
     """Gradients of the forward with respect to x, offset, mask, weight and bias for the
     upstream gradient ``grad_out`` [B, Cout, Ho, Wo] (the gradient equation of the
     csdn.net tags page "可变形卷积：Deformable ConvNets", part "Deformable Convolutional
     Networks", section 可变形卷积; the full definition is in dcn_oracle.h).
 
     Returns a dict of float64 arrays: grad_x, grad_offset, grad_mask (None without a
-    mask), grad_weight, grad_bias."""
+    mask), grad_weight, grad_bias; those not named in ``want`` are None (not computed)."""
     lib = load(lib_path)
     x, offset, weight, grad_out, mask = map(_f32, (x, offset, weight, grad_out, mask))
     d = _desc(x, weight, stride, padding, dilation, offset)
@@ -172,11 +172,11 @@ def backward(x, offset, weight, grad_out, stride=1, padding=0, dilation=1, mask=
     _check(x, offset, mask, weight, None, d, Ho, Wo)
     if grad_out.shape != (d.B, d.Cout, Ho, Wo):
         raise ValueError(f"grad_out must be {(d.B, d.Cout, Ho, Wo)}, got {grad_out.shape}")
-    gx = np.empty(x.shape, dtype=np.float64)
-    goff = np.empty(offset.shape, dtype=np.float64)
-    gm = np.empty(mask.shape, dtype=np.float64) if mask is not None else None
-    gw = np.empty(weight.shape, dtype=np.float64)
-    gb = np.empty(d.Cout, dtype=np.float64)
+    gx = np.empty(x.shape, dtype=np.float64) if "grad_x" in want else None
+    goff = np.empty(offset.shape, dtype=np.float64) if "grad_offset" in want else None
+    gm = np.empty(mask.shape, dtype=np.float64) if mask is not None and "grad_mask" in want else None
+    gw = np.empty(weight.shape, dtype=np.float64) if "grad_weight" in want else None
+    gb = np.empty(d.Cout, dtype=np.float64) if "grad_bias" in want else None
     rc = lib.oracle_backward(ctypes.byref(d), _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight), _ptr(grad_out),
                              _ptr(gx), _ptr(goff), _ptr(gm), _ptr(gw), _ptr(gb), threads)
     if rc != 0:

@@ -241,3 +241,40 @@ def test_python_binding_rejects_bad_tensors(lib):
         dcn.deform_conv2d(x.double(), off.double(), w.double(), padding=1)
     with pytest.raises(ValueError):
         dcn.deform_conv2d(x, off, torch.zeros(4, 2, 3, 3), padding=1)
+
+
+@pytest.mark.parametrize("bad", BAD, ids=lambda b: ",".join(f"{k}={v}" for k, v in b.items()))
+def test_backward_rejects_invalid_descriptor(lib, bad):
+    desc = dcn.make_desc(2, 8, 10, 12, 4, 3, 1, 1, 1, dcn.BF16)
+    for k, v in bad.items():
+        setattr(desc, k, v)
+    n = ctypes.c_size_t(12345)
+    assert lib.dcn_backward_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)) == dcn.E_ARG
+    assert n.value == 12345
+    fake = 0x10000
+    assert lib.dcn_backward(ctypes.byref(desc), fake, fake, None, fake, fake, fake, fake, None, fake, fake,
+                            0x20000, 1 << 30, None) == dcn.E_ARG
+
+
+def test_backward_argument_and_workspace_errors(lib):
+    desc = dcn.make_desc(2, 16, 12, 10, 8, 3, 1, 1, 1, dcn.F32)
+    nb = dcn.dcn_backward_workspace_bytes(desc)
+    # transposed weight, grad_out twice, columns, column gradients and fp32 accumulators
+    assert nb >= 4 * (16 * 9 * 120 * 2 + 2 * 16 * 12 * 10 + 8 * 16 * 9)
+    assert dcn.dcn_backward_workspace_bytes(desc) == nb
+    fake, ws = 0x10000, 0x20000
+    f = lib.dcn_backward
+    outs = (fake, fake, None, fake, fake)
+    for x, off, w, gy in [(None, fake, fake, fake), (fake, None, fake, fake), (fake, fake, None, fake),
+                          (fake, fake, fake, None)]:
+        assert f(ctypes.byref(desc), x, off, None, w, gy, *outs, ws, nb, None) == dcn.E_ARG
+    assert f(ctypes.byref(desc), fake, fake, None, fake, fake, *outs, None, nb, None) == dcn.E_WORKSPACE
+    assert f(ctypes.byref(desc), fake, fake, None, fake, fake, *outs, ws, nb - 1, None) == dcn.E_WORKSPACE
+    assert f(ctypes.byref(desc), fake, fake, None, fake, fake, *outs, ws + 16, nb, None) == dcn.E_WORKSPACE
+    bad = dcn.make_desc(2, 16, 12, 10, 8, 3, 1, 1, 1, 7)
+    n = ctypes.c_size_t()
+    assert lib.dcn_backward_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+    big = dcn.make_desc(64, 1024, 256, 256, 64, 3, 1, 1, 1, dcn.BF16)   # columns beyond 2^31 elements
+    assert lib.dcn_backward_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == dcn.E_UNSUPPORTED
+    for empty in (dcn.make_desc(0, 8, 9, 9, 4, 3, 1, 1, 1, dcn.BF16), dcn.make_desc(2, 8, 9, 9, 0, 3, 1, 1, 1, dcn.F32)):
+        assert dcn.dcn_backward_workspace_bytes(empty) == 0

@@ -1,0 +1,126 @@
+"""The HIP gradients (dcn_backward through the C ABI) against the oracle's gradients,
+element by element, on seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import deformable_convolution_vision_amd as dcn
+import oracle
+from deformable_convolution_vision_amd.workloads import custom, generate, grad_output
+
+pytestmark = pytest.mark.gpu
+
+# |got - ref| <= rtol * |ref| + atol * max|ref|, per gradient tensor
+TOL = {"f32": (1e-4, 1e-5), "bf16": (1e-2, 2e-3)}
+
+
+def out_hw(H, W, K, s, p, d):
+    return (H + 2 * p - d * (K - 1) - 1) // s + 1, (W + 2 * p - d * (K - 1) - 1) // s + 1
+
+
+CASES = [
+    ("basic", dict(B=2, Cin=5, H=9, W=11, Cout=7, K=3, s=1, p=1, d=1, offset="normal:1.5")),
+    ("no_mask_stride2", dict(B=1, Cin=8, H=12, W=10, Cout=6, K=3, s=2, p=1, d=1, mask=None)),
+    ("groups2_dil2", dict(B=2, Cin=8, H=10, W=9, Cout=5, K=3, s=1, p=2, d=2, groups=2, offset="normal:2")),
+    ("k1_two_channel_blocks", dict(B=1, Cin=40, H=6, W=7, Cout=9, K=1, s=1, p=0, d=1)),
+    ("wide_ragged", dict(B=1, Cin=70, H=13, W=17, Cout=130, K=3, s=1, p=1, d=1)),
+    ("far_offsets", dict(B=1, Cin=6, H=8, W=8, Cout=4, K=3, s=1, p=1, d=1, offset="uniform:8")),
+    ("k5", dict(B=1, Cin=4, H=11, W=10, Cout=3, K=5, s=1, p=2, d=1, offset="normal:2")),
+    ("many_pixels", dict(B=1, Cin=16, H=40, W=44, Cout=32, K=3, s=1, p=1, d=1)),
+    ("groups4_stride2", dict(B=2, Cin=64, H=14, W=16, Cout=40, K=3, s=2, p=1, d=1, groups=4)),
+    # every position an integer, the first and last rows and columns at -1 and H (W):
+    # the derivative from the right, also where the cell is [-1, 0)
+    ("zero_offsets", dict(B=2, Cin=6, H=7, W=8, Cout=5, K=3, s=1, p=1, d=1, offset="zeros")),
+]
+
+
+def make(name, kw, dtype, seed=0):
+    kw = dict(kw)
+    g = {k: kw.pop(k) for k in ("B", "Cin", "H", "W", "Cout", "K", "s", "p", "d")}
+    Ho, Wo = out_hw(g["H"], g["W"], g["K"], g["s"], g["p"], g["d"])
+    w = custom(name, dtype, g["B"], g["Cin"], g["H"], g["W"], g["Cout"], g["K"], g["s"], g["p"], g["d"], Ho, Wo,
+               seed=4000 + seed, **kw)
+    return w, generate(w), grad_output(w)
+
+
+def compare(got, ref, dtype, what):
+    rtol, atol = TOL[dtype]
+    got = got.float().cpu().numpy().astype(np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = np.abs(got - ref)
+    bound = rtol * np.abs(ref) + atol * scale
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {ref.size} elements off; worst "
+                           f"{float(np.max(err - bound)):.3e} over the bound at flat index {int(np.argmax(err - bound))}")
+
+
+def run_case(w, inp, gy):
+    gi = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    gx, goff, gw, gb, gm = dcn.deform_conv2d_backward(gy.cuda(), gi["x"], gi["offset"], gi["weight"], w.stride,
+                                                      w.pad, w.dilation, mask=gi["mask"])
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp["x"], inp["offset"], inp["weight"], gy, w.stride, w.pad, w.dilation,
+                          mask=inp["mask"])
+    return (gx, goff, gw, gb, gm), ref
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_backward_parity(name, kw, dtype):
+    w, inp, gy = make(name, kw, dtype)
+    (gx, goff, gw, gb, gm), ref = run_case(w, inp, gy)
+    compare(gx, ref["grad_x"], dtype, f"{name}/{dtype} grad_x")
+    compare(goff, ref["grad_offset"], dtype, f"{name}/{dtype} grad_offset")
+    compare(gw, ref["grad_weight"], dtype, f"{name}/{dtype} grad_weight")
+    compare(gb, ref["grad_bias"], dtype, f"{name}/{dtype} grad_bias")
+    if inp["mask"] is not None:
+        compare(gm, ref["grad_mask"], dtype, f"{name}/{dtype} grad_mask")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_subsets_of_outputs(dtype):
+    """Each gradient requested alone gives the same values as all of them together."""
+    w, inp, gy = make("basic", CASES[0][1], dtype, seed=1)
+    gi = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    desc = dcn.describe(gi["x"], gi["weight"], w.stride, w.pad, w.dilation, gi["offset"])
+    nb = dcn.dcn_backward_workspace_bytes(desc)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    gyc = gy.cuda()
+    full = [torch.empty_like(gi["x"]), torch.empty_like(gi["offset"]), torch.empty_like(gi["mask"]),
+            torch.empty_like(gi["weight"]), torch.empty(w.Cout, dtype=gi["x"].dtype, device="cuda")]
+    dcn.dcn_backward(desc, gi["x"], gi["offset"], gi["mask"], gi["weight"], gyc, *full, ws, nb)
+    rtol, atol = TOL[dtype]
+    for i in range(5):
+        one = [None] * 5
+        one[i] = torch.full_like(full[i], float("nan"))
+        dcn.dcn_backward(desc, gi["x"], gi["offset"], gi["mask"], gi["weight"], gyc, *one, ws, nb)
+        torch.cuda.synchronize()
+        a, b = one[i].float().cpu(), full[i].float().cpu()
+        assert torch.all(torch.isfinite(a)), f"output {i} not written when requested alone"
+        tol = rtol * b.abs() + atol * b.abs().max()
+        assert torch.all((a - b).abs() <= tol), f"output {i} alone differs from the full call"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_empty_problems(dtype):
+    """B == 0: weight and bias gradients are zero; Cout == 0: input, offset and mask
+    gradients are zero."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.zeros((0, 4, 6, 6), dtype=tdt, device="cuda")
+    w = torch.randn((3, 4, 3, 3), device="cuda").to(tdt)
+    off = torch.zeros((0, 18, 6, 6), dtype=tdt, device="cuda")
+    gy = torch.zeros((0, 3, 6, 6), dtype=tdt, device="cuda")
+    gx, goff, gw, gb, gm = dcn.deform_conv2d_backward(gy, x, off, w, 1, 1, 1)
+    torch.cuda.synchronize()
+    assert gw.shape == w.shape and torch.all(gw == 0) and torch.all(gb == 0)
+    x = torch.randn((2, 4, 6, 6), device="cuda").to(tdt)
+    w0 = torch.zeros((0, 4, 3, 3), dtype=tdt, device="cuda")
+    off = torch.randn((2, 18, 6, 6), device="cuda").to(tdt)
+    m = torch.rand((2, 9, 6, 6), device="cuda").to(tdt)
+    gy = torch.zeros((2, 0, 6, 6), dtype=tdt, device="cuda")
+    gx, goff, gw, gb, gm = dcn.deform_conv2d_backward(gy, x, off, w0, 1, 1, 1, mask=m)
+    torch.cuda.synchronize()
+    assert torch.all(gx == 0) and torch.all(goff == 0) and torch.all(gm == 0)
