@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "dcn.h"
@@ -83,7 +84,16 @@ struct BwdArgs {
   float* goff32;        // [B][2GK^2][P] or null
   float* gm32;          // [B][GK^2][P] or null
   int B, Cin, H, W, Cout, K, KK, stride, pad, dil, Ho, Wo, P, Pp, Coutp, R, G, Cg, NCB;
+  // tiled sampling (bwd_sample_tile): output tiles of kTH x kTW pixels, an LDS box of
+  // BH x BW input pixels per channel (the tile's footprint plus a margin of kMargin),
+  // CBL channels of boxes at a time, each group's channels split over nsplit workgroups
+  // of cps channels; gbox [B][Cin][TY][TX][BH*BW] keeps every box for the gather pass
+  float* gbox;
+  int TY, TX, BH, BW, CBL, nsplit, cps;
 };
+
+constexpr int kTH = 8, kTW = 8;   // output tile of the tiled sampling kernel
+constexpr int kMargin = 4;        // box margin (input pixels) around the tile's footprint
 
 template <typename T>
 __global__ __launch_bounds__(kBT) void bwd_prep_w(BwdArgs a) {
@@ -131,6 +141,14 @@ __global__ __launch_bounds__(kBT) void bwd_fill_zero_t(T* p, int n) {
   if (e < n) p[e] = T(0);
 }
 
+// zero columns [P, Pp) of each of the rows of col
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_col_pad(T* col, int rows, int P, int Pp) {
+  const int r = blockIdx.x * kBT + threadIdx.x;
+  if (r >= rows) return;
+  for (int p = P; p < Pp; ++p) col[static_cast<size_t>(r) * Pp + p] = T(0);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kBT) void bwd_bias(const T* gy, T* gb, int B, int Cout, int P) {
   __shared__ float part[kBT / 64];
@@ -151,6 +169,236 @@ template <typename T>
 __global__ __launch_bounds__(kBT) void bwd_convert(const float* src, T* dst, int n) {
   const int e = blockIdx.x * kBT + threadIdx.x;
   if (e < n) dst[e] = from_f<T>(src[e]);
+}
+
+// One workgroup per (b, group, channel split, output tile of kTH x kTW pixels); the
+// tile's K^2 x 64 samples are spread over the threads (NS per thread), and each
+// sample's corners, weights and mask are computed once.  The input gradient is
+// gathered, not scattered: once per workgroup the (sample, corner) pairs that land
+// in the LDS box around the tile are sorted by box pixel (a count, a prefix sum and
+// a placement), and then for each channel
+//   1. each thread forms its samples' column entries (stored for the weight
+//      gradient), reads their column gradients, accumulates the mask and offset sums,
+//      and leaves gcol * m of each sample in LDS;
+//   2. each thread sums, for its box pixels, gcol * m * (corner weight) over the pairs
+//      sorted to that pixel and stores the sum to gbox.
+// A corner outside the box (but inside the image) is added to the fp32 accumulator
+// with a global atomic add.  The gather pass then sums the boxes covering each input
+// pixel.  (LDS float atomics measured far slower than this on gfx950.)
+template <typename T, int NS>
+__global__ __launch_bounds__(kBT) void bwd_sample_tile(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  constexpr int NE = NS * kBT * 4;                        // (sample, corner) pairs
+  float* ent_w = reinterpret_cast<float*>(lds);           // [NE] corner weight
+  uint16_t* ent_s = reinterpret_cast<uint16_t*>(lds + NE * 4);   // [NE] sample
+  int* start = reinterpret_cast<int*>(lds + NE * 6);      // [BP + 1]
+  const int tid = threadIdx.x;
+  int t = blockIdx.x;
+  const int tx = t % a.TX;
+  t /= a.TX;
+  const int ty = t % a.TY;
+  t /= a.TY;
+  const int sp = t % a.nsplit;
+  t /= a.nsplit;
+  const int g = t % a.G, b = t / a.G;
+  const int oy0 = ty * kTH, ox0 = tx * kTW;
+  const int by0 = oy0 * a.stride - a.pad - kMargin, bx0 = ox0 * a.stride - a.pad - kMargin;
+  const int BP = a.BH * a.BW, GKK = a.G * a.KK, HW = a.H * a.W;
+  float* tgs = reinterpret_cast<float*>(lds + NE * 6 + ((BP + 1) * 4 + 15) / 16 * 16);   // [2][NS * kBT]
+  const T* x = static_cast<const T*>(a.x);
+  const T* off = static_cast<const T*>(a.offset);
+  T* col = static_cast<T*>(a.col);
+  const bool grads = a.gcol != nullptr;
+  const bool scat = a.gx32 != nullptr;
+
+  // per-sample state
+  int p_[NS], pq_[NS], k_[NS], q00_[NS], bl_[NS], fl_[NS], o_[NS][4];
+  float m_[NS], w_[NS][4], lx_[NS], ly_[NS], gm_[NS], goy_[NS], gox_[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int s = tid + i * kBT;
+    const int k = s / (kTH * kTW), pl = s - k * (kTH * kTW);
+    const int oy = oy0 + pl / kTW, ox = ox0 + pl % kTW;
+    const bool valid = k < a.KK && oy < a.Ho && ox < a.Wo;
+    p_[i] = valid ? oy * a.Wo + ox : -1;
+    pq_[i] = valid ? p_[i] : 0;
+    k_[i] = valid ? k : 0;
+    o_[i][0] = o_[i][1] = o_[i][2] = o_[i][3] = 0;
+    gm_[i] = goy_[i] = gox_[i] = 0.f;
+    fl_[i] = 0;
+    q00_[i] = 0;
+    bl_[i] = -1;
+    m_[i] = 0.f;
+    lx_[i] = ly_[i] = 0.f;
+    w_[i][0] = w_[i][1] = w_[i][2] = w_[i][3] = 0.f;
+    if (!valid) continue;
+    const int p = p_[i], gk = g * a.KK + k, ki = k / a.K, kj = k - (k / a.K) * a.K;
+    const float dy = to_f(off[(static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p]);
+    const float dx = to_f(off[(static_cast<size_t>(b) * 2 * GKK + 2 * gk + 1) * a.P + p]);
+    const float py = static_cast<float>(oy * a.stride - a.pad + ki * a.dil) + dy;
+    const float px = static_cast<float>(ox * a.stride - a.pad + kj * a.dil) + dx;
+    m_[i] = a.mask != nullptr ? to_f(static_cast<const T*>(a.mask)[(static_cast<size_t>(b) * GKK + gk) * a.P + p]) : 1.f;
+    // a position with no neighbour in the image (or NaN) has none; at py == -1 the cell
+    // is [-1, 0): row 0 has weight 0 but its derivative counts
+    const bool any = py >= -1.f && py < static_cast<float>(a.H) && px >= -1.f && px < static_cast<float>(a.W);
+    if (!any) continue;
+    const float y0f = floorf(py), x0f = floorf(px);
+    const float ly = py - y0f, lx = px - x0f;
+    const int y0 = static_cast<int>(y0f), x0 = static_cast<int>(x0f);
+    const bool iy0 = y0 >= 0, iy1 = y0 + 1 < a.H, ix0 = x0 >= 0, ix1 = x0 + 1 < a.W;
+    fl_[i] = (iy0 && ix0 ? 1 : 0) | (iy0 && ix1 ? 2 : 0) | (iy1 && ix0 ? 4 : 0) | (iy1 && ix1 ? 8 : 0);
+    q00_[i] = y0 * a.W + x0;
+    o_[i][0] = (fl_[i] & 1) ? q00_[i] : 0;
+    o_[i][1] = (fl_[i] & 2) ? q00_[i] + 1 : 0;
+    o_[i][2] = (fl_[i] & 4) ? q00_[i] + a.W : 0;
+    o_[i][3] = (fl_[i] & 8) ? q00_[i] + a.W + 1 : 0;
+    const int yb = y0 - by0, xb = x0 - bx0;
+    bl_[i] = (yb >= 0 && yb + 1 < a.BH && xb >= 0 && xb + 1 < a.BW) ? yb * a.BW + xb : -1;
+    ly_[i] = ly;
+    lx_[i] = lx;
+    w_[i][0] = (1.f - ly) * (1.f - lx);
+    w_[i][1] = (1.f - ly) * lx;
+    w_[i][2] = ly * (1.f - lx);
+    w_[i][3] = ly * lx;
+  }
+
+  // sort the in-box (sample, corner) pairs by box pixel: count, prefix sum, place
+  if (scat) {
+    for (int j = tid; j <= BP; j += kBT) start[j] = 0;
+    __syncthreads();
+    int rank[NS][4];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        rank[i][n] = -1;
+        if (bl_[i] >= 0 && (fl_[i] & (1 << n))) {
+          const int j = bl_[i] + (n & 1) + (n >> 1) * a.BW;
+          rank[i][n] = atomicAdd(&start[j + 1], 1);
+        }
+      }
+    __syncthreads();
+    if (tid < 64) {   // inclusive scan of start[1..BP] by one wave, 64 bins per pass
+      int carry = 0;
+      for (int j0 = 1; j0 <= BP; j0 += 64) {
+        const int j = j0 + tid;
+        int v = j <= BP ? start[j] : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int u = __shfl_up(v, d);
+          if (tid >= d) v += u;
+        }
+        if (j <= BP) start[j] = v + carry;
+        carry += __shfl(v, 63);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        if (rank[i][n] >= 0) {
+          const int j = bl_[i] + (n & 1) + (n >> 1) * a.BW;
+          const int e = start[j] + rank[i][n];
+          ent_s[e] = static_cast<uint16_t>(tid + i * kBT);
+          ent_w[e] = w_[i][n];
+        }
+    __syncthreads();
+  }
+
+  const int cg0 = g * a.Cg + sp * a.cps, cg1 = min(cg0 + a.cps, (g + 1) * a.Cg);
+  const size_t cstride = static_cast<size_t>(a.TY) * a.TX * BP;   // gbox: next channel, same tile
+  float* gdst = scat ? a.gbox + (((static_cast<size_t>(b) * a.Cin + cg0) * a.TY + ty) * a.TX + tx) * BP : nullptr;
+  for (int c = cg0; c < cg1; ++c) {
+    const size_t pl = (static_cast<size_t>(b) * a.Cin + c) * HW;
+    float* tg_s = tgs + ((c - cg0) & 1) * (NS * kBT);
+    // every load of the step first, from valid addresses (a corner outside the image
+    // reads the plane's first element and is replaced by 0 afterwards)
+    float v[NS][4], gcv[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) v[i][n] = to_f(x[pl + o_[i][n]]);
+      gcv[i] = grads ? a.gcol[(static_cast<size_t>(b) * a.R + c * a.KK + k_[i]) * a.P + pq_[i]] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int f = fl_[i];
+      const float v00 = (f & 1) ? v[i][0] : 0.f, v01 = (f & 2) ? v[i][1] : 0.f;
+      const float v10 = (f & 4) ? v[i][2] : 0.f, v11 = (f & 8) ? v[i][3] : 0.f;
+      const float sv = w_[i][0] * v00 + w_[i][1] * v01 + w_[i][2] * v10 + w_[i][3] * v11;
+      const size_t r = static_cast<size_t>(b) * a.R + c * a.KK + k_[i];
+      if (col != nullptr && p_[i] >= 0) col[r * a.Pp + p_[i]] = from_f<T>(m_[i] * sv);
+      if (!grads) continue;
+      const float gc = gcv[i];
+      gm_[i] += gc * sv;
+      goy_[i] += gc * ((1.f - lx_[i]) * (v10 - v00) + lx_[i] * (v11 - v01));
+      gox_[i] += gc * ((1.f - ly_[i]) * (v01 - v00) + ly_[i] * (v11 - v10));
+      if (!scat) continue;
+      const float tg = gc * m_[i];
+      tg_s[tid + i * kBT] = tg;
+      if (bl_[i] < 0 && f != 0) {   // corners outside the box
+        float* gx = a.gx32 + pl + q00_[i];
+        if (f & 1) unsafeAtomicAdd(gx, tg * w_[i][0]);
+        if (f & 2) unsafeAtomicAdd(gx + 1, tg * w_[i][1]);
+        if (f & 4) unsafeAtomicAdd(gx + a.W, tg * w_[i][2]);
+        if (f & 8) unsafeAtomicAdd(gx + a.W + 1, tg * w_[i][3]);
+      }
+    }
+    if (scat) {
+      // one barrier per channel: the two halves of tgs alternate, so a thread still
+      // gathering channel c reads a half that channel c+1 does not write
+      __syncthreads();
+      for (int j = tid; j < BP; j += kBT) {
+        float acc = 0.f;
+        for (int e = start[j]; e < start[j + 1]; ++e) acc += tg_s[ent_s[e]] * ent_w[e];
+        gdst[j] = acc;
+      }
+      gdst += cstride;
+    }
+  }
+  if (grads) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (p_[i] < 0) continue;
+      const int gk = g * a.KK + k_[i];
+      if (a.goff32 != nullptr) {
+        float* go = a.goff32 + (static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p_[i];
+        unsafeAtomicAdd(go, goy_[i] * m_[i]);
+        unsafeAtomicAdd(go + a.P, gox_[i] * m_[i]);
+      }
+      if (a.gm32 != nullptr) unsafeAtomicAdd(a.gm32 + (static_cast<size_t>(b) * GKK + gk) * a.P + p_[i], gm_[i]);
+    }
+  }
+}
+
+// grad_x[b][c][y][x] = the fp32 accumulator (corners outside their box) plus the
+// entries of every box that covers (y, x): tile ty's box starts at row
+// ty*kTH*stride - pad - kMargin and has BH rows (likewise columns).
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_gather_x(BwdArgs a, T* grad_x) {
+  const long long e = static_cast<long long>(blockIdx.x) * kBT + threadIdx.x;
+  const long long n = static_cast<long long>(a.B) * a.Cin * a.H * a.W;
+  if (e >= n) return;
+  const int xx = static_cast<int>(e % a.W);
+  const int yy = static_cast<int>((e / a.W) % a.H);
+  const long long bc = e / (static_cast<long long>(a.H) * a.W);
+  const int sy = kTH * a.stride, sx = kTW * a.stride;
+  const int ry = yy + a.pad + kMargin, rx = xx + a.pad + kMargin;   // >= 0
+  const int ty1 = min(ry / sy, a.TY - 1), tx1 = min(rx / sx, a.TX - 1);
+  const int BP = a.BH * a.BW;
+  float acc = a.gx32[e];
+  const float* base = a.gbox + static_cast<size_t>(bc) * a.TY * a.TX * BP;
+  for (int ty = ty1; ty >= 0; --ty) {
+    const int yb = ry - ty * sy;   // row inside tile ty's box
+    if (yb >= a.BH) break;
+    for (int tx = tx1; tx >= 0; --tx) {
+      const int xb = rx - tx * sx;
+      if (xb >= a.BW) break;
+      acc += base[(static_cast<size_t>(ty) * a.TX + tx) * BP + yb * a.BW + xb];
+    }
+  }
+  grad_x[e] = from_f<T>(acc);
 }
 
 // One thread per (b, group, channel block, kernel point, pixel), pixels fastest.
@@ -359,6 +607,10 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 struct BwdPlan {
   int64_t Ho = 0, Wo = 0, P = 0, Pp = 0, Coutp = 0, R = 0, G = 1;
   size_t o_wt = 0, o_gyt = 0, o_gyp = 0, o_col = 0, o_gcol = 0, o_gx = 0, o_gw = 0, o_goff = 0, o_gm = 0;
+  int64_t TY = 0, TX = 0, BH = 0, BW = 0;
+  int CBL = 0;
+  bool tiled = false;
+  size_t o_gbox = 0;
   size_t bytes = 0;
 };
 
@@ -393,6 +645,16 @@ int bwd_plan(const dcn_desc* d, BwdPlan* p) {
   p->o_gw = take(static_cast<size_t>(Cout * p->R) * 4);
   p->o_goff = take(static_cast<size_t>(B * 2 * p->G * KK * p->P) * 4);
   p->o_gm = take(static_cast<size_t>(B * p->G * KK * p->P) * 4);
+  // tiled sampling: K^2 <= 28 (seven samples per thread at most) and a box of at
+  // least four channels in 64 KB of LDS
+  p->TY = (p->Ho + kTH - 1) / kTH;
+  p->TX = (p->Wo + kTW - 1) / kTW;
+  p->BH = (kTH - 1) * d->stride + (d->kernel_size - 1) * d->dilation + 2 + 2 * kMargin;
+  p->BW = (kTW - 1) * d->stride + (d->kernel_size - 1) * d->dilation + 2 + 2 * kMargin;
+  const double box_elems = static_cast<double>(B) * Cin * p->TY * p->TX * p->BH * p->BW;
+  p->CBL = 1;
+  p->tiled = KK <= 28 && p->BH * p->BW <= 1536 && box_elems <= lim;
+  if (p->tiled) p->o_gbox = take(static_cast<size_t>(box_elems) * 4);
   p->bytes = o;
   return DCN_OK;
 }
@@ -504,7 +766,35 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     g.sCz = static_cast<long long>(a.R) * a.P;
     BWD_TRY(gemm<T>(g, a.B, s));
   }
-  if (need_gcol || grad_weight != nullptr) {
+  if ((need_gcol || grad_weight != nullptr) && p.tiled) {
+    a.gbox = reinterpret_cast<float*>(ws + p.o_gbox);
+    a.TY = static_cast<int>(p.TY);
+    a.TX = static_cast<int>(p.TX);
+    a.BH = static_cast<int>(p.BH);
+    a.BW = static_cast<int>(p.BW);
+    a.CBL = p.CBL;
+    // split each group's channels until there are about two workgroups per CU
+    const int64_t wgs = static_cast<int64_t>(a.B) * a.G * a.TY * a.TX;
+    int ns = 1;
+    while (wgs * ns < 512 && (a.Cg + ns * 2 - 1) / (ns * 2) >= 16) ns *= 2;
+    a.cps = (a.Cg + ns - 1) / ns;
+    a.nsplit = (a.Cg + a.cps - 1) / a.cps;
+    if (grad_weight != nullptr && a.Pp > a.P) {   // zero padding of the columns
+      const int64_t n = static_cast<int64_t>(a.B) * a.R;
+      T* colp = static_cast<T*>(a.col);
+      int rows = static_cast<int>(n), P = a.P, Pp = a.Pp;
+      void* pargs[] = {&colp, &rows, &P, &Pp};
+      BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_col_pad<T>), n, pargs, s));
+    }
+    // LDS: the sorted pairs (weight, sample), the bin starts, two halves of gcol * m
+    const int nsmp = a.KK <= 12 ? 3 : 7;
+    const size_t lds = static_cast<size_t>(nsmp) * kBT * 4 * 6 + ((a.BH * a.BW + 1) * 4 + 15) / 16 * 16 +
+                       static_cast<size_t>(2) * nsmp * kBT * 4;
+    const unsigned grid = static_cast<unsigned>(wgs * a.nsplit);
+    const void* fn = a.KK <= 12 ? reinterpret_cast<const void*>(&bwd_sample_tile<T, 3>)
+                                : reinterpret_cast<const void*>(&bwd_sample_tile<T, 7>);
+    BWD_TRY(hipLaunchKernel(fn, dim3(grid), dim3(kBT), args, lds, s));
+  } else if (need_gcol || grad_weight != nullptr) {
     const int64_t n = static_cast<int64_t>(a.B) * a.G * a.NCB * a.KK * a.Pp;
     BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_sample<T>), n, args, s));
   }
@@ -537,7 +827,15 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     void* bargs[] = {&gy, &gb, &B, &Cout, &P};
     BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_bias<T>), dim3(a.Cout), dim3(kBT), bargs, 0, s));
   }
-  if (a.gx32 != nullptr) BWD_TRY(convert<T>(a.gx32, grad_x, nx, s));
+  if (a.gx32 != nullptr) {
+    if (p.tiled) {
+      T* gxo = static_cast<T*>(grad_x);
+      void* gargs[] = {&a, &gxo};
+      BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_gather_x<T>), nx, gargs, s));
+    } else {
+      BWD_TRY(convert<T>(a.gx32, grad_x, nx, s));
+    }
+  }
   if (a.goff32 != nullptr) BWD_TRY(convert<T>(a.goff32, grad_offset, noff, s));
   if (a.gm32 != nullptr) BWD_TRY(convert<T>(a.gm32, grad_mask, nm, s));
   return DCN_OK;

@@ -32,6 +32,12 @@ CASES = [
     # every position an integer, the first and last rows and columns at -1 and H (W):
     # the derivative from the right, also where the cell is [-1, 0)
     ("zero_offsets", dict(B=2, Cin=6, H=7, W=8, Cout=5, K=3, s=1, p=1, d=1, offset="zeros")),
+    # the largest box (stride 2, dilation 2, K = 5) and offsets beyond the box margin
+    ("k5_s2_d2_far", dict(B=1, Cin=20, H=30, W=27, Cout=12, K=5, s=2, p=4, d=2, offset="uniform:6")),
+    # K*K = 49: the per-sample kernel without tiles
+    ("k7_untiled", dict(B=1, Cin=3, H=12, W=12, Cout=2, K=7, s=1, p=3, d=1)),
+    # several channel splits and tiles of a c4-like layer at reduced size
+    ("c4_like", dict(B=2, Cin=64, H=40, W=56, Cout=64, K=3, s=2, p=1, d=1)),
 ]
 
 
