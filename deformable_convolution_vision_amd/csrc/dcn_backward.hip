@@ -309,18 +309,31 @@ __global__ __launch_bounds__(kBT) void bwd_sample_tile(BwdArgs a) {
   const int cg0 = g * a.Cg + sp * a.cps, cg1 = min(cg0 + a.cps, (g + 1) * a.Cg);
   const size_t cstride = static_cast<size_t>(a.TY) * a.TX * BP;   // gbox: next channel, same tile
   float* gdst = scat ? a.gbox + (((static_cast<size_t>(b) * a.Cin + cg0) * a.TY + ty) * a.TX + tx) * BP : nullptr;
+  // The loads of channel c+1 (from valid addresses: a corner outside the image reads
+  // the plane's first element and is replaced by 0 afterwards) are issued before the
+  // barrier and the gather of channel c, so they are in flight during both.
+  float vn[NS][4], gcn[NS];
+  auto load_channel = [&](int c) __attribute__((always_inline)) {
+    const size_t pl = (static_cast<size_t>(b) * a.Cin + c) * HW;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) vn[i][n] = to_f(x[pl + o_[i][n]]);
+      gcn[i] = grads ? a.gcol[(static_cast<size_t>(b) * a.R + c * a.KK + k_[i]) * a.P + pq_[i]] : 0.f;
+    }
+  };
+  if (cg0 < cg1) load_channel(cg0);
   for (int c = cg0; c < cg1; ++c) {
     const size_t pl = (static_cast<size_t>(b) * a.Cin + c) * HW;
     float* tg_s = tgs + ((c - cg0) & 1) * (NS * kBT);
-    // every load of the step first, from valid addresses (a corner outside the image
-    // reads the plane's first element and is replaced by 0 afterwards)
     float v[NS][4], gcv[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) v[i][n] = to_f(x[pl + o_[i][n]]);
-      gcv[i] = grads ? a.gcol[(static_cast<size_t>(b) * a.R + c * a.KK + k_[i]) * a.P + pq_[i]] : 0.f;
+      for (int n = 0; n < 4; ++n) v[i][n] = vn[i][n];
+      gcv[i] = gcn[i];
     }
+    if (c + 1 < cg1) load_channel(c + 1);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int f = fl_[i];
@@ -773,10 +786,10 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     a.BH = static_cast<int>(p.BH);
     a.BW = static_cast<int>(p.BW);
     a.CBL = p.CBL;
-    // split each group's channels until there are about two workgroups per CU
+    // split each group's channels until there are about four workgroups per CU
     const int64_t wgs = static_cast<int64_t>(a.B) * a.G * a.TY * a.TX;
     int ns = 1;
-    while (wgs * ns < 512 && (a.Cg + ns * 2 - 1) / (ns * 2) >= 16) ns *= 2;
+    while (wgs * ns < 1024 && (a.Cg + ns * 2 - 1) / (ns * 2) >= 16) ns *= 2;
     a.cps = (a.Cg + ns - 1) / ns;
     a.nsplit = (a.Cg + a.cps - 1) / a.cps;
     if (grad_weight != nullptr && a.Pp > a.P) {   // zero padding of the columns
