@@ -61,7 +61,7 @@ def kernel_symbol(variant: str, plan: str, w) -> str:
         grp = re.search(r"offset groups=(\d+)", plan)
         grouped = "true" if grp and int(grp.group(1)) > 1 else "false"
         return (f"dcn_box_kernel<{int(m.group(2)) // 64}, {int(m.group(1)) // 16}, {9 if kk == 9 else 0}, "
-                f"{grouped}, {pw.group(1) if pw else 4}>")
+                f"{grouped}, {pw.group(1) if pw else 4}, false>")
     if variant.startswith("direct"):
         bf16 = "true" if variant.endswith("bf16") else "false"
         return f"dcn_direct_kernel<{bf16}, {kk}, {3 if (w.Cin == 3 and kk == 9) else 0}>"
