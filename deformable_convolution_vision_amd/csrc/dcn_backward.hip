@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kBT) void bwd_convert(const float* src, T* dst, int
 // A corner outside the box (but inside the image) is added to the fp32 accumulator
 // with a global atomic add.  The gather pass then sums the boxes covering each input
 // pixel.  (LDS float atomics measured far slower than this on gfx950.)
-template <typename T, int NS>
+template <typename T, int NS, int CQ>
 __global__ __launch_bounds__(kBT) void bwd_sample_tile(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   constexpr int NE = NS * kBT * 4;                        // (sample, corner) pairs
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kBT) void bwd_sample_tile(BwdArgs a) {
   const int oy0 = ty * kTH, ox0 = tx * kTW;
   const int by0 = oy0 * a.stride - a.pad - kMargin, bx0 = ox0 * a.stride - a.pad - kMargin;
   const int BP = a.BH * a.BW, GKK = a.G * a.KK, HW = a.H * a.W;
-  float* tgs = reinterpret_cast<float*>(lds + NE * 6 + ((BP + 1) * 4 + 15) / 16 * 16);   // [2][NS * kBT]
+  float* tgs = reinterpret_cast<float*>(lds + NE * 6 + ((BP + 1) * 4 + 15) / 16 * 16);   // [2][CQ][NS * kBT]
   const T* x = static_cast<const T*>(a.x);
   const T* off = static_cast<const T*>(a.offset);
   T* col = static_cast<T*>(a.col);
@@ -309,65 +309,73 @@ __global__ __launch_bounds__(kBT) void bwd_sample_tile(BwdArgs a) {
   const int cg0 = g * a.Cg + sp * a.cps, cg1 = min(cg0 + a.cps, (g + 1) * a.Cg);
   const size_t cstride = static_cast<size_t>(a.TY) * a.TX * BP;   // gbox: next channel, same tile
   float* gdst = scat ? a.gbox + (((static_cast<size_t>(b) * a.Cin + cg0) * a.TY + ty) * a.TX + tx) * BP : nullptr;
-  // The loads of channel c+1 (from valid addresses: a corner outside the image reads
-  // the plane's first element and is replaced by 0 afterwards) are issued before the
-  // barrier and the gather of channel c, so they are in flight during both.
-  float vn[NS][4], gcn[NS];
-  auto load_channel = [&](int c) __attribute__((always_inline)) {
-    const size_t pl = (static_cast<size_t>(b) * a.Cin + c) * HW;
+  // CQ channels per step: every load of the step first (from valid addresses: a corner
+  // outside the image reads the plane's first element and is replaced by 0
+  // afterwards), then the samples' work, one barrier, and the gather of the CQ
+  // channels' boxes, which reads each sorted pair once for all of them.  The two
+  // halves of tgs alternate between steps, so a thread still gathering step t reads a
+  // half that step t+1 does not write.
+  for (int c = cg0; c < cg1; c += CQ) {
+    const int nq = min(CQ, cg1 - c);
+    float* tg_s = tgs + (((c - cg0) / CQ) & 1) * (CQ * NS * kBT);
+    float v[CQ][NS][4], gcv[CQ][NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int q = 0; q < CQ; ++q) {
+      const int cq = min(c + q, cg1 - 1);   // past the split's last channel: a repeat, not used
+      const size_t pl = (static_cast<size_t>(b) * a.Cin + cq) * HW;
 #pragma unroll
-      for (int n = 0; n < 4; ++n) vn[i][n] = to_f(x[pl + o_[i][n]]);
-      gcn[i] = grads ? a.gcol[(static_cast<size_t>(b) * a.R + c * a.KK + k_[i]) * a.P + pq_[i]] : 0.f;
+      for (int i = 0; i < NS; ++i) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) v[q][i][n] = to_f(x[pl + o_[i][n]]);
+        gcv[q][i] = grads ? a.gcol[(static_cast<size_t>(b) * a.R + cq * a.KK + k_[i]) * a.P + pq_[i]] : 0.f;
+      }
     }
-  };
-  if (cg0 < cg1) load_channel(cg0);
-  for (int c = cg0; c < cg1; ++c) {
-    const size_t pl = (static_cast<size_t>(b) * a.Cin + c) * HW;
-    float* tg_s = tgs + ((c - cg0) & 1) * (NS * kBT);
-    float v[NS][4], gcv[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int q = 0; q < CQ; ++q) {
+      if (q >= nq) break;
+      const size_t pl = (static_cast<size_t>(b) * a.Cin + c + q) * HW;
 #pragma unroll
-      for (int n = 0; n < 4; ++n) v[i][n] = vn[i][n];
-      gcv[i] = gcn[i];
-    }
-    if (c + 1 < cg1) load_channel(c + 1);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int f = fl_[i];
-      const float v00 = (f & 1) ? v[i][0] : 0.f, v01 = (f & 2) ? v[i][1] : 0.f;
-      const float v10 = (f & 4) ? v[i][2] : 0.f, v11 = (f & 8) ? v[i][3] : 0.f;
-      const float sv = w_[i][0] * v00 + w_[i][1] * v01 + w_[i][2] * v10 + w_[i][3] * v11;
-      const size_t r = static_cast<size_t>(b) * a.R + c * a.KK + k_[i];
-      if (col != nullptr && p_[i] >= 0) col[r * a.Pp + p_[i]] = from_f<T>(m_[i] * sv);
-      if (!grads) continue;
-      const float gc = gcv[i];
-      gm_[i] += gc * sv;
-      goy_[i] += gc * ((1.f - lx_[i]) * (v10 - v00) + lx_[i] * (v11 - v01));
-      gox_[i] += gc * ((1.f - ly_[i]) * (v01 - v00) + ly_[i] * (v11 - v10));
-      if (!scat) continue;
-      const float tg = gc * m_[i];
-      tg_s[tid + i * kBT] = tg;
-      if (bl_[i] < 0 && f != 0) {   // corners outside the box
-        float* gx = a.gx32 + pl + q00_[i];
-        if (f & 1) unsafeAtomicAdd(gx, tg * w_[i][0]);
-        if (f & 2) unsafeAtomicAdd(gx + 1, tg * w_[i][1]);
-        if (f & 4) unsafeAtomicAdd(gx + a.W, tg * w_[i][2]);
-        if (f & 8) unsafeAtomicAdd(gx + a.W + 1, tg * w_[i][3]);
+      for (int i = 0; i < NS; ++i) {
+        const int f = fl_[i];
+        const float v00 = (f & 1) ? v[q][i][0] : 0.f, v01 = (f & 2) ? v[q][i][1] : 0.f;
+        const float v10 = (f & 4) ? v[q][i][2] : 0.f, v11 = (f & 8) ? v[q][i][3] : 0.f;
+        const float sv = w_[i][0] * v00 + w_[i][1] * v01 + w_[i][2] * v10 + w_[i][3] * v11;
+        const size_t r = static_cast<size_t>(b) * a.R + (c + q) * a.KK + k_[i];
+        if (col != nullptr && p_[i] >= 0) col[r * a.Pp + p_[i]] = from_f<T>(m_[i] * sv);
+        if (!grads) continue;
+        const float gc = gcv[q][i];
+        gm_[i] += gc * sv;
+        goy_[i] += gc * ((1.f - lx_[i]) * (v10 - v00) + lx_[i] * (v11 - v01));
+        gox_[i] += gc * ((1.f - ly_[i]) * (v01 - v00) + ly_[i] * (v11 - v10));
+        if (!scat) continue;
+        const float tg = gc * m_[i];
+        tg_s[q * (NS * kBT) + tid + i * kBT] = tg;
+        if (bl_[i] < 0 && f != 0) {   // corners outside the box
+          float* gx = a.gx32 + pl + q00_[i];
+          if (f & 1) unsafeAtomicAdd(gx, tg * w_[i][0]);
+          if (f & 2) unsafeAtomicAdd(gx + 1, tg * w_[i][1]);
+          if (f & 4) unsafeAtomicAdd(gx + a.W, tg * w_[i][2]);
+          if (f & 8) unsafeAtomicAdd(gx + a.W + 1, tg * w_[i][3]);
+        }
       }
     }
     if (scat) {
-      // one barrier per channel: the two halves of tgs alternate, so a thread still
-      // gathering channel c reads a half that channel c+1 does not write
       __syncthreads();
       for (int j = tid; j < BP; j += kBT) {
-        float acc = 0.f;
-        for (int e = start[j]; e < start[j + 1]; ++e) acc += tg_s[ent_s[e]] * ent_w[e];
-        gdst[j] = acc;
+        float acc[CQ];
+#pragma unroll
+        for (int q = 0; q < CQ; ++q) acc[q] = 0.f;
+        for (int e = start[j]; e < start[j + 1]; ++e) {
+          const int sj = ent_s[e];
+          const float w = ent_w[e];
+#pragma unroll
+          for (int q = 0; q < CQ; ++q) acc[q] += tg_s[q * (NS * kBT) + sj] * w;
+        }
+#pragma unroll
+        for (int q = 0; q < CQ; ++q)
+          if (q < nq) gdst[q * cstride + j] = acc[q];
       }
-      gdst += cstride;
+      gdst += CQ * cstride;
     }
   }
   if (grads) {
@@ -800,12 +808,13 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
       BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_col_pad<T>), n, pargs, s));
     }
     // LDS: the sorted pairs (weight, sample), the bin starts, two halves of gcol * m
-    const int nsmp = a.KK <= 12 ? 3 : 7;
+    // (three samples per thread: four channels per step; seven: one)
+    const int nsmp = a.KK <= 12 ? 3 : 7, cq = a.KK <= 12 ? 4 : 1;
     const size_t lds = static_cast<size_t>(nsmp) * kBT * 4 * 6 + ((a.BH * a.BW + 1) * 4 + 15) / 16 * 16 +
-                       static_cast<size_t>(2) * nsmp * kBT * 4;
+                       static_cast<size_t>(2) * cq * nsmp * kBT * 4;
     const unsigned grid = static_cast<unsigned>(wgs * a.nsplit);
-    const void* fn = a.KK <= 12 ? reinterpret_cast<const void*>(&bwd_sample_tile<T, 3>)
-                                : reinterpret_cast<const void*>(&bwd_sample_tile<T, 7>);
+    const void* fn = a.KK <= 12 ? reinterpret_cast<const void*>(&bwd_sample_tile<T, 3, 4>)
+                                : reinterpret_cast<const void*>(&bwd_sample_tile<T, 7, 1>);
     BWD_TRY(hipLaunchKernel(fn, dim3(grid), dim3(kBT), args, lds, s));
   } else if (need_gcol || grad_weight != nullptr) {
     const int64_t n = static_cast<int64_t>(a.B) * a.G * a.NCB * a.KK * a.Pp;
