@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16_mfma": 2516.6, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, TFLOP/s, GB/s
 CSRC = os.path.join(ROOT, "deformable_convolution_vision_amd", "csrc")
-KERNEL_SRCS = ("dcn_internal.h", "dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip", "dcn_direct.hip", "dcn_backward.hip")
+KERNEL_SRCS = ("dcn_internal.h", "dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip", "dcn_direct.hip")   # the forward kernels
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
