@@ -31,6 +31,11 @@ class _Desc(ctypes.Structure):
                 ("B", "Cin", "H", "W", "Cout", "K", "stride", "pad", "dilation", "groups")]
 
 
+class _RoiDesc(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in ("B", "C", "H", "W", "R", "k", "S")] + \
+               [("spatial_scale", ctypes.c_double), ("gamma", ctypes.c_double)]
+
+
 def build(out_path: str = LIB, extra_flags: tuple[str, ...] = (), src: str = SRC) -> str:
     """Compile the oracle with g++ (OpenMP, IEEE arithmetic: no fast-math)."""
     tmp = out_path + ".tmp"
@@ -63,6 +68,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.oracle_points.restype = ctypes.c_int
     lib.oracle_backward.argtypes = [ctypes.POINTER(_Desc), P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_backward.restype = ctypes.c_int
+    lib.oracle_roi_pool.argtypes = [ctypes.POINTER(_RoiDesc), P, P, P, P, P, ctypes.c_int]
+    lib.oracle_roi_pool.restype = ctypes.c_int
     lib.oracle_threads.argtypes = [ctypes.c_int]
     lib.oracle_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
@@ -182,6 +189,30 @@ def backward(x, offset, weight, grad_out, stride=1, padding=0, dilation=1, mask=
     if rc != 0:
         raise ValueError("oracle_backward rejected its arguments")
     return {"grad_x": gx, "grad_offset": goff, "grad_mask": gm, "grad_weight": gw, "grad_bias": gb}
+
+
+def roi_pool(x, rois, k, S, spatial_scale=1.0, gamma=0.1, offset=None, mask=None, threads=0,
+             lib_path: str = LIB):
+    """Deformable RoI pooling (definition and readings in dcn_oracle.h): x [B,C,H,W],
+    rois [R,5] = (batch index, x1, y1, x2, y2), offset [R,2,k,k] (row, column; normalised
+    by the RoI's height and width and scaled by gamma) or None, mask [R,k,k] or None.
+    Returns float64 [R,C,k,k]."""
+    lib = load(lib_path)
+    x, rois, offset, mask = map(_f32, (x, rois, offset, mask))
+    B, C, H, W = x.shape
+    R = rois.shape[0]
+    if rois.shape != (R, 5):
+        raise ValueError("rois must be [R, 5]")
+    if offset is not None and offset.shape != (R, 2, k, k):
+        raise ValueError(f"offset must be {(R, 2, k, k)}")
+    if mask is not None and mask.shape != (R, k, k):
+        raise ValueError(f"mask must be {(R, k, k)}")
+    d = _RoiDesc(B, C, H, W, R, k, S, float(spatial_scale), float(gamma))
+    out = np.empty((R, C, k, k), dtype=np.float64)
+    rc = lib.oracle_roi_pool(ctypes.byref(d), _ptr(x), _ptr(rois), _ptr(offset), _ptr(mask), _ptr(out), threads)
+    if rc != 0:
+        raise ValueError("oracle_roi_pool rejected its arguments")
+    return out
 
 
 def threads_used(threads: int = 0, lib_path: str = LIB) -> int:

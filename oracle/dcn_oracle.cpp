@@ -236,6 +236,51 @@ extern "C" int oracle_backward(const oracle_desc* d, const float* x, const float
   return 0;
 }
 
+extern "C" int oracle_roi_pool(const oracle_roi_desc* d, const float* x, const float* rois, const float* offset,
+                               const float* mask, double* out, int threads) {
+  if (d == nullptr || x == nullptr || rois == nullptr || out == nullptr) return -1;
+  if (d->B < 1 || d->C < 1 || d->H < 1 || d->W < 1 || d->R < 0 || d->k < 1 || d->S < 1) return -1;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+  const int64_t k = d->k, S = d->S, C = d->C;
+  // one (RoI, channel) pair per iteration: its k x k outputs
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t rc = 0; rc < d->R * C; ++rc) {
+    const int64_t r = rc / C, c = rc % C;
+    const float* roi = rois + r * 5;
+    const double bi = static_cast<double>(roi[0]);
+    const double x1 = static_cast<double>(roi[1]) * d->spatial_scale, y1 = static_cast<double>(roi[2]) * d->spatial_scale;
+    const double w = (static_cast<double>(roi[3]) - static_cast<double>(roi[1])) * d->spatial_scale;
+    const double h = (static_cast<double>(roi[4]) - static_cast<double>(roi[2])) * d->spatial_scale;
+    const bool batch_ok = bi >= 0.0 && bi < static_cast<double>(d->B);
+    const int64_t b = batch_ok ? static_cast<int64_t>(bi) : 0;
+    const float* plane = x + (b * C + c) * d->H * d->W;
+    for (int64_t i = 0; i < k; ++i)
+      for (int64_t j = 0; j < k; ++j) {
+        double* y = out + (rc * k + i) * k + j;
+        if (!batch_ok) {
+          *y = 0.0;
+          continue;
+        }
+        const double dy = offset != nullptr ? d->gamma * h * static_cast<double>(offset[((r * 2 + 0) * k + i) * k + j]) : 0.0;
+        const double dx = offset != nullptr ? d->gamma * w * static_cast<double>(offset[((r * 2 + 1) * k + i) * k + j]) : 0.0;
+        const double m = mask != nullptr ? static_cast<double>(mask[(r * k + i) * k + j]) : 1.0;
+        double acc = 0.0;
+        for (int64_t u = 0; u < S; ++u)
+          for (int64_t v = 0; v < S; ++v) {
+            const double py = y1 + (static_cast<double>(i) + (static_cast<double>(u) + 0.5) / static_cast<double>(S)) * h / static_cast<double>(k) + dy;
+            const double px = x1 + (static_cast<double>(j) + (static_cast<double>(v) + 0.5) / static_cast<double>(S)) * w / static_cast<double>(k) + dx;
+            acc += bilinear_zero_outside(plane, d->H, d->W, py, px);
+          }
+        *y = m * acc / static_cast<double>(S * S);
+      }
+  }
+  return 0;
+}
+
 extern "C" int oracle_output_hw(const oracle_desc* d, int64_t* Ho, int64_t* Wo) {
   if (!valid_desc(d) || Ho == nullptr || Wo == nullptr) return -1;
   const int64_t ho = out_size(d->H, d->K, d->stride, d->pad, d->dilation);

@@ -118,6 +118,32 @@ int oracle_backward(const oracle_desc* d, const float* x, const float* offset,
                     const float* mask, const float* weight, const float* grad_out,
                     double* grad_x, double* grad_offset, double* grad_mask,
                     double* grad_weight, double* grad_bias, int threads);
+/* Deformable RoI pooling (the csdn.net tags page "可变形卷积：Deformable ConvNets",
+ * part (i) section 4 "可变形ROI pooling" and part "Deformable Convolutional Networks",
+ * section Deformable RoI Pooling; 51itzy.com/kjqy/64159.html section 二; the DCNv2
+ * modulated form on the tags page, section 3.2).  The RoI is split into k x k bins;
+ * each bin is shifted by its own offset, normalised by the RoI's size, and pooled
+ * by averaging bilinear samples (zero outside the image):
+ *
+ *   y[r,c,i,j] = m[r,i,j] / S^2 * sum_{u,v < S} S(X[b_r, c], py, px)
+ *     x1 = rois[r,1]*scale, y1 = rois[r,2]*scale, w = (rois[r,3]-rois[r,1])*scale,
+ *     h = (rois[r,4]-rois[r,2])*scale, b_r = rois[r,0]
+ *     py = y1 + (i + (u + 0.5)/S) * h/k + gamma * h * offset[r,0,i,j]
+ *     px = x1 + (j + (v + 0.5)/S) * w/k + gamma * w * offset[r,1,i,j]
+ *     m  = mask[r,i,j], or 1 when mask is NULL
+ * Readings where the formulas are missing from the pages: the bin's pixels are an
+ * S x S grid of sample points at the centres of equal sub-cells (n_ij = S^2); RoI
+ * coordinates are continuous, pixel (y, x) sits at the integer position (y, x) as in
+ * the convolution, and no +1 is added to the RoI size; offset channel 0 is the row
+ * displacement; the mask scales the bin's average.
+ * x[B,C,H,W], rois[R,5] (float), offset[R,2,k,k] or NULL, mask[R,k,k] or NULL,
+ * out[R,C,k,k] doubles.  A RoI whose batch index is outside [0, B) gives zeros. */
+typedef struct oracle_roi_desc {
+  int64_t B, C, H, W, R, k, S;
+  double spatial_scale, gamma;
+} oracle_roi_desc;
+int oracle_roi_pool(const oracle_roi_desc* d, const float* x, const float* rois, const float* offset,
+                    const float* mask, double* out, int threads);
 /* Number of threads an oracle_forward call with this request would use. */
 int oracle_threads(int threads);
 

@@ -28,6 +28,9 @@ What each pin reduces to (no pin restates the oracle's own formula):
   p14 gradients, zero offsets  -> torch autograd of conv2d (float64); unfold for the mask
                                 gradient; one-sided input differences for the offsets
   p15 gradients, all outside   -> zero, except the bias gradient sum(gy)
+  p16 RoI pooling, pixel bins   -> the input pixels (moved RoI, whole-pixel offsets, batch image)
+  p17 RoI pooling, linear field -> the field at the shifted bin centre times the mask, any S
+  p18 RoI pooling, outside      -> zeros; a constant image gives the constant times the mask
   golden                      -> hand-worked examples in tests/golden/
 """
 
@@ -500,8 +503,82 @@ def pin_p15_backward_all_outside(lib):
     _close(r["grad_bias"], gy.astype(np.float64).sum(axis=(0, 2, 3)), 1e-12, "grad_bias")
 
 
+def pin_p16_roi_pixel_bins(lib):
+    """RoI pooling with one sample per bin on a RoI whose bins are single pixels: the
+    output is the input pixels themselves, also for a RoI moved by whole pixels, for
+    bin offsets worth whole pixels (gamma * size * offset an integer), and for the
+    RoI's own batch image; spatial_scale maps image coordinates to the feature grid."""
+    rng = np.random.default_rng(1601)
+    B, C, H, W, k = 2, 3, 11, 13, 4
+    x = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    # image coordinates at scale 0.5: bins [2j-1, 2j+1) map to pixel j
+    rois = np.array([[0, -1, -1, 2 * k - 1, 2 * k - 1],
+                     [1, -1 + 2 * 3, -1 + 2 * 2, 2 * k - 1 + 2 * 3, 2 * k - 1 + 2 * 2]], dtype=np.float32)
+    y = oracle.roi_pool(x, rois, k, 1, spatial_scale=0.5, lib_path=lib)
+    _close(y[0], x[0, :, 0:k, 0:k], 1e-12, "pixel bins")
+    _close(y[1], x[1, :, 2:2 + k, 3:3 + k], 1e-12, "pixel bins moved by (2, 3)")
+    # offsets of n whole pixels: gamma * k * off = n with gamma 0.1, k 4 -> off = 2.5 n
+    off = np.zeros((2, 2, k, k), dtype=np.float32)
+    off[:, 0] = 2.5 * 1    # one row down
+    off[:, 1] = 2.5 * -1   # one column left
+    y = oracle.roi_pool(x, rois, k, 1, spatial_scale=0.5, gamma=0.1, offset=off, lib_path=lib)
+    want0 = np.zeros((C, k, k))
+    want0[:, :, 1:] = x[0, :, 1:k + 1, 0:k - 1]   # column -1 is outside: zero
+    _close(y[0], want0, 1e-12, "whole-pixel bin offsets")
+    _close(y[1], x[1, :, 3:3 + k, 2:2 + k], 1e-12, "whole-pixel bin offsets, moved RoI")
+
+
+def pin_p17_roi_linear_field(lib):
+    """On a linear field X = a + b*y + c*x every bilinear sample is exact and the mean of
+    the S x S sub-cell centres is the bin centre, so each output is m times the field at
+    the shifted bin centre: y1 + (i + 1/2) h/k + gamma h dy_hat (rows), likewise columns,
+    for any S, non-square RoIs and both batch images."""
+    rng = np.random.default_rng(1701)
+    B, C, H, W, k, g = 2, 3, 40, 50, 3, 0.1
+    a = rng.standard_normal((B, C))
+    bb = rng.standard_normal((B, C))
+    cc = rng.standard_normal((B, C))
+    yy, xx = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+    x = (a[:, :, None, None] + bb[:, :, None, None] * yy + cc[:, :, None, None] * xx).astype(np.float32)
+    # the field is stored in float32: the tolerance covers that rounding (about 1e-7 of 50)
+    for S in (1, 2, 3):
+        R = 6
+        x1 = rng.uniform(8, 20, R)
+        y1 = rng.uniform(8, 14, R)
+        w = rng.uniform(4, 20, R)
+        h = rng.uniform(4, 16, R)
+        rois = np.stack([rng.integers(0, B, R), x1, y1, x1 + w, y1 + h], 1).astype(np.float32)
+        off = rng.uniform(-0.5, 0.5, (R, 2, k, k)).astype(np.float32)
+        m = rng.uniform(0.2, 1.0, (R, k, k)).astype(np.float32)
+        out = oracle.roi_pool(x, rois, k, S, 1.0, g, off, m, lib_path=lib)
+        r64 = rois.astype(np.float64)
+        for r in range(R):
+            bi = int(r64[r, 0])
+            rw, rh = r64[r, 3] - r64[r, 1], r64[r, 4] - r64[r, 2]
+            i = np.arange(k)[:, None]
+            j = np.arange(k)[None, :]
+            cy = r64[r, 2] + (i + 0.5) * rh / k + g * rh * off[r, 0].astype(np.float64)
+            cx = r64[r, 1] + (j + 0.5) * rw / k + g * rw * off[r, 1].astype(np.float64)
+            want = m[r][None].astype(np.float64) * (a[bi][:, None, None] + bb[bi][:, None, None] * cy[None]
+                                                     + cc[bi][:, None, None] * cx[None])
+            _close(out[r], want, 2e-5, f"linear field, S={S}, RoI {r}")
+
+
+def pin_p18_roi_outside(lib):
+    """A RoI far outside the image, or with a batch index outside [0, B), pools zeros;
+    a constant image pools the constant times the mask inside."""
+    rng = np.random.default_rng(1801)
+    x = np.full((2, 2, 9, 9), 3.0, dtype=np.float32)
+    rois = np.array([[0, 100, 100, 120, 130], [5, 1, 1, 6, 6], [-1, 1, 1, 6, 6], [1, 1, 1, 6, 7]], np.float32)
+    m = rng.uniform(0.1, 1.0, (4, 2, 2)).astype(np.float32)
+    y = oracle.roi_pool(x, rois, 2, 2, mask=m, lib_path=lib)
+    assert np.all(y[:3] == 0.0), "RoIs outside the image or the batch must pool zeros"
+    _close(y[3], 3.0 * np.broadcast_to(m[3].astype(np.float64), (2, 2, 2)), 1e-12, "constant image")
+
+
 ALL_PINS = [pin_p1_zero_offsets, pin_p2_integer_offsets, pin_p3_bilinear_field, pin_p4_all_outside,
             pin_p5_linear_in_mask, pin_p6_mask_absent, pin_p7_half_offsets, pin_p8_constant_input,
             pin_p9_grid_sample, pin_p10_nonfinite_offsets, pin_p11_offset_groups, pin_p12_offset_mask_branch,
             pin_golden, pin_p13_backward_directional, pin_p14_backward_zero_offsets,
-            pin_p15_backward_all_outside]
+            pin_p15_backward_all_outside, pin_p16_roi_pixel_bins, pin_p17_roi_linear_field,
+            pin_p18_roi_outside]

@@ -68,6 +68,16 @@ MUTANTS = [
                                   "grad_offset[(b * 2 * G * KK + 2 * gk + 1) * HoWo + pix] = goy;")]),
     ("bwd_grad_x_corner_weight", [("if (sg.inside[n]) gx[sg.iy[n] * W + sg.ix[n]] += t * sg.g[n];",
                                    "if (sg.inside[n]) gx[sg.iy[n] * W + sg.ix[n]] += t * sg.g[3 - n];")]),
+    # RoI pooling
+    ("roi_offset_scaled_by_width", [("d->gamma * h * static_cast<double>(offset[((r * 2 + 0)",
+                                     "d->gamma * w * static_cast<double>(offset[((r * 2 + 0)")]),
+    ("roi_subcell_corner", [("(static_cast<double>(u) + 0.5)", "static_cast<double>(u)")]),
+    ("roi_bins_transposed", [("double* y = out + (rc * k + i) * k + j;", "double* y = out + (rc * k + j) * k + i;")]),
+    ("roi_batch_ignored", [("const int64_t b = batch_ok ? static_cast<int64_t>(bi) : 0;", "const int64_t b = 0;")]),
+    ("roi_mask_ignored", [("mask != nullptr ? static_cast<double>(mask[(r * k + i) * k + j]) : 1.0", "1.0")]),
+    ("roi_scale_not_on_x1", [("const double x1 = static_cast<double>(roi[1]) * d->spatial_scale,",
+                              "const double x1 = static_cast<double>(roi[1]),")]),
+    ("roi_mean_over_s", [("*y = m * acc / static_cast<double>(S * S);", "*y = m * acc / static_cast<double>(S);")]),
     ("bwd_position_ignores_pad", [("static_cast<float>(oy * d->stride - d->pad + i * d->dilation) + dy;",
                                    "static_cast<float>(oy * d->stride + i * d->dilation) + dy;")]),
 ]
