@@ -331,6 +331,77 @@ def bench_backward(w, steps: int, warmup: int):
     }
 
 
+def bench_roi(w, steps: int, warmup: int):
+    """Deformable RoI pooling (dcn_roi_pool) on the workload's feature map: 256 RoIs per
+    image of an 800 x 1344 image at spatial scale 1/16, k x k bins (k = the workload's K),
+    2 x 2 samples per bin, per-bin offsets and mask.  One step is one call.  value is the
+    effective bandwidth of its algorithmic bytes (x, rois, offsets and mask read once, the
+    output written once); the timed region has events at its ends only."""
+    import numpy as np
+    import torch
+
+    import deformable_convolution_vision_amd as dcn
+    import oracle
+    from deformable_convolution_vision_amd.workloads import roi_inputs
+
+    k, S, scale, gamma, per_img = w.K, 2, 1.0 / 16, 0.1, 256
+    host = roi_inputs(w, per_img, k, (800, 1344))
+    g = {key: v.cuda() for key, v in host.items()}
+    R = g["rois"].shape[0]
+    desc = dcn.RoiDesc(w.B, w.Cin, w.H, w.W, R, k, S, scale, gamma, dcn.BF16 if w.dtype == "bf16" else dcn.F32, 0)
+    out = torch.empty((R, w.Cin, k, k), dtype=g["x"].dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        dcn.dcn_roi_pool(desc, g["x"], g["rois"], g["offset"], g["mask"], out, stream)
+
+    step()
+    torch.cuda.synchronize()
+    ref = oracle.roi_pool(host["x"], host["rois"], k, S, scale, gamma, host["offset"], host["mask"])
+    xmax = float(host["x"].float().abs().max())
+    tol = 1e-2 if w.dtype == "bf16" else 1e-5
+    max_rel = float(np.max(np.abs(out.float().cpu().numpy() - ref))) / xmax
+    if not max_rel <= tol:
+        raise SystemExit(f"bench parity failure on {w.name}: max error {max_rel:.3e} of max|x| > {tol}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    t0 = time.perf_counter()
+    ev.record(0, sp)
+    for _ in range(steps):
+        step()
+    ev.record(1, sp)
+    ev.sync(1)
+    wall = time.perf_counter() - t0
+    total_ms = ev.ms(0, 1)
+    ev.close()
+    ms_per_step = total_ms / steps
+    es = 2 if w.dtype == "bf16" else 4
+    abytes = es * (w.B * w.Cin * w.H * w.W + R * 2 * k * k + R * k * k + R * w.Cin * k * k) + 4 * 5 * R
+    gbps = abytes / (ms_per_step * 1e-3) / 1e9
+    return {
+        "metric": "deform_conv2d fwd effective TFLOP/s + GB/s (c4 stride-2 bf16), % of roofline",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; shapes and value distributions of the workload)",
+        "config": {"workload": f"{w.name}: deformable RoI pooling of x [{w.B},{w.Cin},{w.H},{w.W}], {R} RoIs "
+                               f"({per_img} per image, sides 32-512 px of 800x1344, scale 1/16), {k}x{k} bins, "
+                               f"{S}x{S} samples, offsets and mask",
+                   "variant": "roi_pool", "plan": "dcn_roi_pool: one launch, one thread per output"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK["hbm"], "unit": "GB/s",
+                     "frac": round(gbps / PEAK["hbm"], 5), "traffic": None,
+                     "kernel": "roi_pool_kernel", "kernel_sha": kernel_hash(),
+                     "per_launch": {"algorithmic_bytes": abytes, "outputs": R * w.Cin * k * k}},
+        "kernels_us": {"call_mean": round(ms_per_step * 1e3, 3)},
+        "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
+        "parity_max_rel_err_sampled": max_rel,
+        "cold": None,
+        "cpu_baseline": None,
+    }
+
+
 def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: float, cold_steps: int = 0):
     import numpy as np
     import torch
@@ -343,6 +414,8 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
         return bench_offset_mask(w, steps, warmup)
     if w.op == "backward":
         return bench_backward(w, steps, warmup)
+    if w.op == "roi_pool":
+        return bench_roi(w, steps, warmup)
     host = generate(w)
     g = {k: (None if v is None else v.cuda()) for k, v in host.items()}
     desc = dcn.describe(g["x"], g["weight"], w.stride, w.pad, w.dilation, g["offset"])

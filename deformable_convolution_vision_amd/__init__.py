@@ -51,6 +51,14 @@ class Desc(ctypes.Structure):
         return "Desc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
+class RoiDesc(ctypes.Structure):
+    """Mirror of ``dcn_roi_desc``."""
+    _fields_ = [("batch", ctypes.c_int64), ("channels", ctypes.c_int64), ("height", ctypes.c_int64),
+                ("width", ctypes.c_int64), ("num_rois", ctypes.c_int64), ("pooled_size", ctypes.c_int64),
+                ("samples", ctypes.c_int64), ("spatial_scale", ctypes.c_float), ("gamma", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -88,6 +96,8 @@ def load_library() -> ctypes.CDLL:
     lib.dcn_backward_workspace_bytes.restype = ctypes.c_int
     lib.dcn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.dcn_backward.restype = ctypes.c_int
+    lib.dcn_roi_pool.argtypes = [ctypes.POINTER(RoiDesc), P, P, P, P, P, P]
+    lib.dcn_roi_pool.restype = ctypes.c_int
     for name in ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_forward_staged", "dcn_stage"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -328,3 +338,38 @@ def deform_conv2d_backward(grad_out, input, offset, weight, stride=1, padding=0,
         dcn_backward(desc, input, offset, mask, weight, grad_out, gx, goff, gm, gw, gb,
                      workspace if nbytes else None, nbytes)
     return gx, goff, gw, gb, gm
+
+
+def dcn_roi_pool(desc: RoiDesc, x, rois, offset, mask, out, stream=None) -> None:
+    """Raw call: tensors (or integer device addresses) laid out as dcn.h states."""
+    rc = load_library().dcn_roi_pool(ctypes.byref(desc), _ptr(x), _ptr(rois), _ptr(offset), _ptr(mask), _ptr(out),
+                                     _stream(stream))
+    if rc != OK:
+        raise DcnError(rc, "dcn_roi_pool")
+
+
+def deform_roi_pool(input, rois, offset=None, mask=None, output_size=7, sampling_ratio=2, spatial_scale=1.0,
+                    gamma=0.1):
+    """Deformable RoI pooling on the GPU: input [B,C,H,W]; rois [R,5] float32 (batch index,
+    x1, y1, x2, y2 in image coordinates); offset [R,2,k,k] (row, column, normalised by the
+    RoI's size) or None; mask [R,k,k] or None.  Returns [R,C,k,k] in the input's dtype."""
+    if input.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {input.dtype}; use float32 or bfloat16")
+    k = int(output_size)
+    B, C, H, W = input.shape
+    R = rois.shape[0]
+    if rois.dtype != torch.float32 or tuple(rois.shape) != (R, 5):
+        raise ValueError("rois must be a float32 [R, 5] tensor")
+    for name, t, shape in (("offset", offset, (R, 2, k, k)), ("mask", mask, (R, k, k))):
+        if t is None:
+            continue
+        if tuple(t.shape) != shape or t.dtype != input.dtype:
+            raise ValueError(f"{name} must be {shape} of the input's dtype")
+    for t in (input, rois, offset, mask):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.device != input.device):
+            raise ValueError("tensors must be contiguous and on the input's GPU")
+    desc = RoiDesc(B, C, H, W, R, k, int(sampling_ratio), float(spatial_scale), float(gamma), _DTYPES[input.dtype], 0)
+    out = torch.empty((R, C, k, k), dtype=input.dtype, device=input.device)
+    with torch.cuda.device(input.device):
+        dcn_roi_pool(desc, input, rois, offset, mask, out)
+    return out

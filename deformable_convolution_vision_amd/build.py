@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdcn_hip.so")
-SOURCES = ["dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip", "dcn_direct.hip", "dcn_backward.hip"]
+SOURCES = ["dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip", "dcn_direct.hip", "dcn_backward.hip", "dcn_roi.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -94,6 +94,10 @@ WORKLOADS = {
     # the c4 layer's offset/mask convolution: 3*K^2 = 27 outputs (offset field and mask)
     "c4_bwd": Workload("c4_bwd", "bf16", 2, 256, 100, 168, 256, 3, 2, 1, 1, 50, 84,
                        offset="normal:1", mask="sigmoid", bias=None, seed=1007, op="backward"),
+    # deformable RoI pooling on the c4 feature map (stride 16 of an 800 x 1344 image):
+    # 256 RoIs per image, 7 x 7 bins, 2 x 2 samples per bin
+    "roi_c4": Workload("roi_c4", "bf16", 2, 256, 50, 84, 256, 7, 1, 0, 1, 7, 7,
+                       offset="normal:0.1", mask="sigmoid", bias=None, seed=1008, op="roi_pool"),
     "c4_om": Workload("c4_om", "bf16", 2, 256, 100, 168, 27, 3, 2, 1, 1, 50, 84,
                       offset="normal:1", mask=None, bias="normal:0.1", seed=1006, op="offset_mask"),
 }
@@ -148,6 +152,30 @@ def grad_output(w: Workload, seed: int | None = None) -> torch.Tensor:
     g = torch.Generator().manual_seed((w.seed if seed is None else seed) + 7919)
     gy = torch.randn((w.B, w.Cout, w.Ho, w.Wo), generator=g, dtype=torch.float32)
     return gy.to(torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+
+
+def roi_inputs(w: Workload, num_rois: int, k: int, image_hw: tuple[int, int], seed: int | None = None) -> dict:
+    """Seeded inputs of deformable RoI pooling on the workload's feature map x [B,Cin,H,W]:
+    num_rois boxes per batch image with sides drawn log-uniformly in [32, 512] image pixels,
+    placed uniformly inside the image of size image_hw; offsets N(0, 0.1^2) per bin (row,
+    column); the mask the sigmoid of N(0, 1).  rois are float32 [R,5] (batch index, x1, y1,
+    x2, y2); the others in the workload's element type (CPU)."""
+    g = torch.Generator().manual_seed((w.seed if seed is None else seed) + 104729)
+    x = _draw(w.x, (w.B, w.Cin, w.H, w.W), g)
+    R = num_rois * w.B
+    ih, iw = image_hw
+    side = torch.exp(torch.rand((R, 2), generator=g) * (math.log(512.0) - math.log(32.0)) + math.log(32.0))
+    bw = torch.minimum(side[:, 0], torch.tensor(float(iw)))
+    bh = torch.minimum(side[:, 1], torch.tensor(float(ih)))
+    x1 = torch.rand(R, generator=g) * (iw - bw)
+    y1 = torch.rand(R, generator=g) * (ih - bh)
+    bidx = torch.arange(R) // num_rois
+    rois = torch.stack([bidx.float(), x1, y1, x1 + bw, y1 + bh], 1).float().contiguous()
+    offset = torch.randn((R, 2, k, k), generator=g) * 0.1
+    mask = torch.sigmoid(torch.randn((R, k, k), generator=g))
+    dt = w.torch_dtype
+    return {"x": x.to(dt).contiguous(), "rois": rois, "offset": offset.to(dt).contiguous(),
+            "mask": mask.to(dt).contiguous()}
 
 
 def custom(name: str, dtype: str, B: int, Cin: int, H: int, W: int, Cout: int, K: int,

@@ -184,6 +184,39 @@ int dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const 
                  void* grad_mask, void* grad_weight, void* grad_bias, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
 
+/* Deformable RoI pooling (the csdn.net tags page "可变形卷积：Deformable ConvNets", part
+ * (i) section 4 "可变形ROI pooling" and the DCNv2 section 3.2, and part "Deformable
+ * Convolutional Networks", section Deformable RoI Pooling; 51itzy.com/kjqy/64159.html,
+ * section 二).  Each RoI is split into k x k bins; bin (i, j) is shifted by its own offset,
+ * normalised by the RoI's size, and pooled by averaging S x S bilinear samples at the
+ * centres of equal sub-cells (a neighbour outside the image contributes zero):
+ *   out[r,c,i,j] = m[r,i,j] / S^2 * sum_{u,v<S} S(x[b,c], py, px),  b = rois[r,0],
+ *   py = y1 + (i + (u+0.5)/S) * h/k + gamma * h * offset[r,0,i,j],
+ *   px = x1 + (j + (v+0.5)/S) * w/k + gamma * w * offset[r,1,i,j],
+ *   (x1, y1) = spatial_scale * (rois[r,1], rois[r,2]),
+ *   w = spatial_scale * (rois[r,3] - rois[r,1]), h = spatial_scale * (rois[r,4] - rois[r,2]),
+ *   m = mask[r,i,j] (1 when mask is NULL).
+ * Pixel (y, x) sits at the integer position (y, x), as in the convolution.
+ * x [B,C,H,W], offset [R,2,k,k] or NULL (no shift), mask [R,k,k] or NULL, out [R,C,k,k]
+ * in desc->dtype; rois [R,5] is always float32 (batch index, x1, y1, x2, y2 in image
+ * coordinates).  A RoI whose batch index is not in [0, B) pools zeros.  Positions,
+ * weights and sums in fp32; out rounded to dtype.  Device pointers; asynchronous on
+ * `stream`; no workspace.  DCN_E_ARG for an invalid descriptor or a NULL x, rois or
+ * out (R = 0 launches nothing), DCN_E_UNSUPPORTED for another dtype or a tensor at or
+ * beyond 2^31 elements, DCN_E_HIP for a failed launch; checked before the launch. */
+typedef struct dcn_roi_desc {
+  int64_t batch, channels, height, width;
+  int64_t num_rois;      /* R >= 0 */
+  int64_t pooled_size;   /* k, 1..1024 */
+  int64_t samples;       /* S, samples per bin side, 1..64 */
+  float spatial_scale;   /* image -> feature coordinates */
+  float gamma;           /* offset scale */
+  int32_t dtype;         /* enum dcn_dtype */
+  int32_t reserved;      /* 0 */
+} dcn_roi_desc;
+int dcn_roi_pool(const dcn_roi_desc* desc, const void* x, const float* rois, const void* offset,
+                 const void* mask, void* out, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* dcn_status_str(int status);
 

@@ -74,6 +74,8 @@ def test_output_hw_matches_oracle(lib, g):
 def test_named_workload_sizes(lib):
     from deformable_convolution_vision_amd.workloads import WORKLOADS
     for w in WORKLOADS.values():
+        if w.op == "roi_pool":   # not a convolution: no output geometry of that kind
+            continue
         desc = dcn.make_desc(w.B, w.Cin, w.H, w.W, w.Cout, w.K, w.stride, w.pad, w.dilation,
                              dcn.F32 if w.dtype == "f32" else dcn.BF16)
         assert dcn.dcn_output_hw(desc) == (w.Ho, w.Wo), w.name
@@ -278,3 +280,24 @@ def test_backward_argument_and_workspace_errors(lib):
     assert lib.dcn_backward_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == dcn.E_UNSUPPORTED
     for empty in (dcn.make_desc(0, 8, 9, 9, 4, 3, 1, 1, 1, dcn.BF16), dcn.make_desc(2, 8, 9, 9, 0, 3, 1, 1, 1, dcn.F32)):
         assert dcn.dcn_backward_workspace_bytes(empty) == 0
+
+
+def test_roi_pool_argument_checks(lib):
+    fake = 0x10000
+    f = lib.dcn_roi_pool
+    good = dict(batch=2, channels=8, height=10, width=12, num_rois=3, pooled_size=7, samples=2,
+                spatial_scale=0.0625, gamma=0.1, dtype=dcn.BF16, reserved=0)
+    for k, v in [("batch", 0), ("channels", 0), ("height", 0), ("width", 0), ("num_rois", -1), ("pooled_size", 0),
+                 ("samples", 0), ("samples", 65), ("pooled_size", 1025), ("spatial_scale", float("nan")),
+                 ("gamma", float("inf"))]:
+        d = dcn.RoiDesc(**{**good, k: v})
+        assert f(ctypes.byref(d), fake, fake, None, None, fake, None) == dcn.E_ARG, k
+    d = dcn.RoiDesc(**{**good, "dtype": 7})
+    assert f(ctypes.byref(d), fake, fake, None, None, fake, None) == dcn.E_UNSUPPORTED
+    d = dcn.RoiDesc(**good)
+    for x, r, o in [(None, fake, fake), (fake, None, fake), (fake, fake, None)]:
+        assert f(ctypes.byref(d), x, r, None, None, o, None) == dcn.E_ARG
+    d = dcn.RoiDesc(**{**good, "num_rois": 0})   # nothing to launch
+    assert f(ctypes.byref(d), None, None, None, None, None, None) == dcn.OK
+    d = dcn.RoiDesc(**{**good, "num_rois": 1 << 20, "channels": 1 << 12, "pooled_size": 32})
+    assert f(ctypes.byref(d), fake, fake, None, None, fake, None) == dcn.E_UNSUPPORTED
