@@ -334,7 +334,8 @@ def bench_backward(w, steps: int, warmup: int):
 def bench_roi(w, steps: int, warmup: int):
     """Deformable RoI pooling (dcn_roi_pool) on the workload's feature map: 256 RoIs per
     image of an 800 x 1344 image at spatial scale 1/16, k x k bins (k = the workload's K),
-    2 x 2 samples per bin, per-bin offsets and mask.  One step is one call.  value is the
+    2 x 2 samples per bin, per-bin offsets and mask.  One step is one call (for bf16: the
+    channels-last staging launch and the pooling launch).  value is the
     effective bandwidth of its algorithmic bytes (x, rois, offsets and mask read once, the
     output written once); the timed region has events at its ends only."""
     import numpy as np
@@ -350,11 +351,13 @@ def bench_roi(w, steps: int, warmup: int):
     R = g["rois"].shape[0]
     desc = dcn.RoiDesc(w.B, w.Cin, w.H, w.W, R, k, S, scale, gamma, dcn.BF16 if w.dtype == "bf16" else dcn.F32, 0)
     out = torch.empty((R, w.Cin, k, k), dtype=g["x"].dtype, device="cuda")
+    nb = dcn.dcn_roi_pool_workspace_bytes(desc)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
     def step():
-        dcn.dcn_roi_pool(desc, g["x"], g["rois"], g["offset"], g["mask"], out, stream)
+        dcn.dcn_roi_pool(desc, g["x"], g["rois"], g["offset"], g["mask"], out, ws if nb else None, nb, stream)
 
     step()
     torch.cuda.synchronize()
@@ -389,7 +392,7 @@ def bench_roi(w, steps: int, warmup: int):
         "config": {"workload": f"{w.name}: deformable RoI pooling of x [{w.B},{w.Cin},{w.H},{w.W}], {R} RoIs "
                                f"({per_img} per image, sides 32-512 px of 800x1344, scale 1/16), {k}x{k} bins, "
                                f"{S}x{S} samples, offsets and mask",
-                   "variant": "roi_pool", "plan": "dcn_roi_pool: one launch, one thread per output"},
+                   "variant": "roi_pool", "plan": "dcn_roi_pool: channels-last staging launch + pooling launch"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK["hbm"], "unit": "GB/s",
                      "frac": round(gbps / PEAK["hbm"], 5), "traffic": None,
                      "kernel": "roi_pool_kernel", "kernel_sha": kernel_hash(),

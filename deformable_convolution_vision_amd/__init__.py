@@ -96,8 +96,10 @@ def load_library() -> ctypes.CDLL:
     lib.dcn_backward_workspace_bytes.restype = ctypes.c_int
     lib.dcn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.dcn_backward.restype = ctypes.c_int
-    lib.dcn_roi_pool.argtypes = [ctypes.POINTER(RoiDesc), P, P, P, P, P, P]
+    lib.dcn_roi_pool.argtypes = [ctypes.POINTER(RoiDesc), P, P, P, P, P, P, S, P]
     lib.dcn_roi_pool.restype = ctypes.c_int
+    lib.dcn_roi_pool_workspace_bytes.argtypes = [ctypes.POINTER(RoiDesc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.dcn_roi_pool_workspace_bytes.restype = ctypes.c_int
     for name in ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_forward_staged", "dcn_stage"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -340,10 +342,18 @@ def deform_conv2d_backward(grad_out, input, offset, weight, stride=1, padding=0,
     return gx, goff, gw, gb, gm
 
 
-def dcn_roi_pool(desc: RoiDesc, x, rois, offset, mask, out, stream=None) -> None:
+def dcn_roi_pool_workspace_bytes(desc: RoiDesc) -> int:
+    n = ctypes.c_size_t()
+    rc = load_library().dcn_roi_pool_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    if rc != OK:
+        raise DcnError(rc, "dcn_roi_pool_workspace_bytes")
+    return n.value
+
+
+def dcn_roi_pool(desc: RoiDesc, x, rois, offset, mask, out, workspace, workspace_bytes: int, stream=None) -> None:
     """Raw call: tensors (or integer device addresses) laid out as dcn.h states."""
     rc = load_library().dcn_roi_pool(ctypes.byref(desc), _ptr(x), _ptr(rois), _ptr(offset), _ptr(mask), _ptr(out),
-                                     _stream(stream))
+                                     _ptr(workspace), workspace_bytes, _stream(stream))
     if rc != OK:
         raise DcnError(rc, "dcn_roi_pool")
 
@@ -370,6 +380,8 @@ def deform_roi_pool(input, rois, offset=None, mask=None, output_size=7, sampling
             raise ValueError("tensors must be contiguous and on the input's GPU")
     desc = RoiDesc(B, C, H, W, R, k, int(sampling_ratio), float(spatial_scale), float(gamma), _DTYPES[input.dtype], 0)
     out = torch.empty((R, C, k, k), dtype=input.dtype, device=input.device)
+    nbytes = dcn_roi_pool_workspace_bytes(desc)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=input.device) if nbytes else None
     with torch.cuda.device(input.device):
-        dcn_roi_pool(desc, input, rois, offset, mask, out)
+        dcn_roi_pool(desc, input, rois, offset, mask, out, ws, nbytes)
     return out

@@ -201,9 +201,12 @@ int dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const 
  * in desc->dtype; rois [R,5] is always float32 (batch index, x1, y1, x2, y2 in image
  * coordinates).  A RoI whose batch index is not in [0, B) pools zeros.  Positions,
  * weights and sums in fp32; out rounded to dtype.  Device pointers; asynchronous on
- * `stream`; no workspace.  DCN_E_ARG for an invalid descriptor or a NULL x, rois or
- * out (R = 0 launches nothing), DCN_E_UNSUPPORTED for another dtype or a tensor at or
- * beyond 2^31 elements, DCN_E_HIP for a failed launch; checked before the launch. */
+ * `stream`.  bf16 with k <= 16 first writes a channels-last copy of x into the
+ * workspace (256-byte aligned, dcn_roi_pool_workspace_bytes; 0 bytes otherwise).
+ * DCN_E_ARG for an invalid descriptor or a NULL x, rois or out (R = 0 launches
+ * nothing), DCN_E_UNSUPPORTED for another dtype or a tensor at or beyond 2^31
+ * elements, DCN_E_WORKSPACE for a missing, short or misaligned workspace, DCN_E_HIP
+ * for a failed launch; all checked before any launch. */
 typedef struct dcn_roi_desc {
   int64_t batch, channels, height, width;
   int64_t num_rois;      /* R >= 0 */
@@ -214,8 +217,9 @@ typedef struct dcn_roi_desc {
   int32_t dtype;         /* enum dcn_dtype */
   int32_t reserved;      /* 0 */
 } dcn_roi_desc;
+int dcn_roi_pool_workspace_bytes(const dcn_roi_desc* desc, size_t* bytes);
 int dcn_roi_pool(const dcn_roi_desc* desc, const void* x, const float* rois, const void* offset,
-                 const void* mask, void* out, hipStream_t stream);
+                 const void* mask, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* dcn_status_str(int status);

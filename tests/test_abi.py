@@ -291,13 +291,21 @@ def test_roi_pool_argument_checks(lib):
                  ("samples", 0), ("samples", 65), ("pooled_size", 1025), ("spatial_scale", float("nan")),
                  ("gamma", float("inf"))]:
         d = dcn.RoiDesc(**{**good, k: v})
-        assert f(ctypes.byref(d), fake, fake, None, None, fake, None) == dcn.E_ARG, k
+        assert f(ctypes.byref(d), fake, fake, None, None, fake, fake, 1 << 30, None) == dcn.E_ARG, k
     d = dcn.RoiDesc(**{**good, "dtype": 7})
-    assert f(ctypes.byref(d), fake, fake, None, None, fake, None) == dcn.E_UNSUPPORTED
+    assert f(ctypes.byref(d), fake, fake, None, None, fake, fake, 1 << 30, None) == dcn.E_UNSUPPORTED
     d = dcn.RoiDesc(**good)
     for x, r, o in [(None, fake, fake), (fake, None, fake), (fake, fake, None)]:
-        assert f(ctypes.byref(d), x, r, None, None, o, None) == dcn.E_ARG
+        assert f(ctypes.byref(d), x, r, None, None, o, 0x20000, 1 << 30, None) == dcn.E_ARG
     d = dcn.RoiDesc(**{**good, "num_rois": 0})   # nothing to launch
-    assert f(ctypes.byref(d), None, None, None, None, None, None) == dcn.OK
+    assert f(ctypes.byref(d), None, None, None, None, None, None, 0, None) == dcn.OK
     d = dcn.RoiDesc(**{**good, "num_rois": 1 << 20, "channels": 1 << 12, "pooled_size": 32})
-    assert f(ctypes.byref(d), fake, fake, None, None, fake, None) == dcn.E_UNSUPPORTED
+    assert f(ctypes.byref(d), fake, fake, None, None, fake, fake, 1 << 30, None) == dcn.E_UNSUPPORTED
+    # bf16 with k <= 16 stages a channels-last copy: B*H*W*round_up(C, 8) bf16
+    d = dcn.RoiDesc(**good)
+    nb = dcn.dcn_roi_pool_workspace_bytes(d)
+    assert nb == 2 * 10 * 12 * 8 * 2
+    for ws, n in [(None, nb), (0x20000, nb - 1), (0x20010, nb)]:
+        assert f(ctypes.byref(d), fake, fake, None, None, fake, ws, n, None) == dcn.E_WORKSPACE
+    assert dcn.dcn_roi_pool_workspace_bytes(dcn.RoiDesc(**{**good, "dtype": dcn.F32})) == 0
+    assert dcn.dcn_roi_pool_workspace_bytes(dcn.RoiDesc(**{**good, "pooled_size": 17})) == 0

@@ -22,6 +22,8 @@ CASES = [
     ("one_sample", 1, 4, 9, 9, 6, 4, 1, 1.0, 0.2, True, True),
     ("large_gamma", 1, 3, 12, 14, 10, 5, 2, 1.0, 1.0, True, True),   # bins pushed past the image
     ("k1", 2, 6, 10, 10, 5, 1, 4, 1.0, 0.1, True, True),
+    ("channels_70", 2, 70, 12, 16, 7, 5, 2, 0.5, 0.1, True, True),   # a partial 64-channel block
+    ("k20_unstaged", 1, 4, 30, 30, 3, 20, 1, 1.0, 0.1, True, True),  # bf16 with k > 16: no staging
 ]
 
 
