@@ -22,8 +22,9 @@
 //
 // Kernels, in launch order:
 //   prep_w   W [Cout][R] -> Wt [R][Coutp] (the column-gradient product's first operand)
-//   prep_gy  gy -> gyT [B][P][Coutp] and gyP [B][Cout][Pp] (both zero-padded)
-//   fill     zero the fp32 accumulators
+//   prep_gy  gy -> gyT [B][P][Coutp] and gyP [B][Cout][Pp] (both zero-padded), and
+//            the bias gradient's per-tile sums (fp32 atomics)
+//   fill     zero the fp32 accumulators (one launch)
 //   gemm     gcol[b] = Wt x gyT[b]^T (MFMA, both operands contiguous along the reduction)
 //   sample   per (b, group, channel block, kernel point, pixel): the sample's corners
 //            and weights once, then for each channel the column entry (for the
@@ -31,8 +32,8 @@
 //            scattered input-gradient contributions (fp32 atomics)
 //   gemm     grad_weight = sum_b gyP[b] x col[b]^T, the reduction split over workgroups
 //            (fp32 atomics into a zeroed accumulator)
-//   bias     one workgroup per output channel
-//   convert  fp32 accumulators -> the element type
+//   gather   grad_x from the boxes (tiled path)
+//   convert  fp32 accumulators -> the element type (one launch)
 // The gradient products run on MFMA 32x32x16 bf16 (bf16 data) or 32x32x2 fp32.
 
 #include <hip/hip_runtime.h>
@@ -40,6 +41,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <initializer_list>
+#include <tuple>
 
 #include "dcn.h"
 #include "dcn_internal.h"
@@ -83,6 +86,7 @@ struct BwdArgs {
   float* gx32;          // [B][Cin][H][W] or null
   float* goff32;        // [B][2GK^2][P] or null
   float* gm32;          // [B][GK^2][P] or null
+  float* gb32;          // [Cout] or null (bias gradient accumulator)
   int B, Cin, H, W, Cout, K, KK, stride, pad, dil, Ho, Wo, P, Pp, Coutp, R, G, Cg, NCB;
   // tiled sampling (bwd_sample_tile): output tiles of kTH x kTW pixels, an LDS box of
   // BH x BW input pixels per channel (the tile's footprint plus a margin of kMargin),
@@ -113,26 +117,57 @@ __global__ __launch_bounds__(kBT) void bwd_prep_gy(BwdArgs a) {
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int p0 = blockIdx.x * 32, o0 = blockIdx.y * 32, b = blockIdx.z;
   const T* gy = static_cast<const T*>(a.gy) + static_cast<size_t>(b) * a.Cout * a.P;
-  T* gyp = static_cast<T*>(a.gyp) + static_cast<size_t>(b) * a.Cout * a.Pp;
-  T* gyt = static_cast<T*>(a.gyt) + static_cast<size_t>(b) * a.P * a.Coutp;
+  T* gyp = a.gyp != nullptr ? static_cast<T*>(a.gyp) + static_cast<size_t>(b) * a.Cout * a.Pp : nullptr;
+  T* gyt = a.gyt != nullptr ? static_cast<T*>(a.gyt) + static_cast<size_t>(b) * a.P * a.Coutp : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int o = o0 + ty + 8 * i, p = p0 + tx;
     const T v = (o < a.Cout && p < a.P) ? gy[static_cast<size_t>(o) * a.P + p] : T(0);
     tile[ty + 8 * i][tx] = v;
-    if (o < a.Cout && p < a.Pp) gyp[static_cast<size_t>(o) * a.Pp + p] = v;
+    if (gyp != nullptr && o < a.Cout && p < a.Pp) gyp[static_cast<size_t>(o) * a.Pp + p] = v;
   }
   __syncthreads();
+  if (a.gyt != nullptr) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = p0 + ty + 8 * i, o = o0 + tx;
-    if (p < a.P && o < a.Coutp) gyt[static_cast<size_t>(p) * a.Coutp + o] = tile[tx][ty + 8 * i];
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + ty + 8 * i, o = o0 + tx;
+      if (p < a.P && o < a.Coutp) gyt[static_cast<size_t>(p) * a.Coutp + o] = tile[tx][ty + 8 * i];
+    }
+  }
+  // the bias gradient: this tile's sum over its 32 pixels of each output channel
+  if (a.gb32 != nullptr && threadIdx.x < 32 && o0 + static_cast<int>(threadIdx.x) < a.Cout) {
+    float sum = 0.f;
+#pragma unroll 8
+    for (int t = 0; t < 32; ++t) sum += to_f(tile[threadIdx.x][t]);
+    unsafeAtomicAdd(a.gb32 + o0 + threadIdx.x, sum);
   }
 }
 
-__global__ __launch_bounds__(kBT) void bwd_fill_zero(float* p, int n) {
-  const int e = blockIdx.x * kBT + threadIdx.x;
-  if (e < n) p[e] = 0.f;
+// Up to six fp32 ranges zeroed (or converted) by one launch; the workgroups are
+// split over the ranges in proportion to their sizes (blocks[i] workgroups for range i).
+struct Ranges {
+  float* p[6];
+  void* dst[6];
+  int n[6];
+  int blocks[6];
+  int count;
+};
+
+__global__ __launch_bounds__(kBT) void bwd_fill_zero_ranges(Ranges r) {
+  int blk = blockIdx.x, i = 0;
+  while (i + 1 < r.count && blk >= r.blocks[i]) blk -= r.blocks[i++];
+  const int e = (blk * kBT + static_cast<int>(threadIdx.x)) * 4;   // four floats per thread
+  if (e + 4 <= r.n[i]) *reinterpret_cast<float4*>(r.p[i] + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+  else
+    for (int t = e; t < r.n[i]; ++t) r.p[i][t] = 0.f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_convert_ranges(Ranges r) {
+  int blk = blockIdx.x, i = 0;
+  while (i + 1 < r.count && blk >= r.blocks[i]) blk -= r.blocks[i++];
+  const int e = blk * kBT + static_cast<int>(threadIdx.x);
+  if (e < r.n[i]) static_cast<T*>(r.dst[i])[e] = from_f<T>(r.p[i][e]);
 }
 
 template <typename T>
@@ -147,22 +182,6 @@ __global__ __launch_bounds__(kBT) void bwd_col_pad(T* col, int rows, int P, int 
   const int r = blockIdx.x * kBT + threadIdx.x;
   if (r >= rows) return;
   for (int p = P; p < Pp; ++p) col[static_cast<size_t>(r) * Pp + p] = T(0);
-}
-
-template <typename T>
-__global__ __launch_bounds__(kBT) void bwd_bias(const T* gy, T* gb, int B, int Cout, int P) {
-  __shared__ float part[kBT / 64];
-  const int o = blockIdx.x;
-  float s = 0.f;
-  for (int b = 0; b < B; ++b) {
-    const T* row = gy + (static_cast<size_t>(b) * Cout + o) * P;
-    for (int p = threadIdx.x; p < P; p += kBT) s += to_f(row[p]);
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) gb[o] = from_f<T>(part[0] + part[1] + part[2] + part[3]);
 }
 
 template <typename T>
@@ -627,7 +646,7 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 // Workspace layout of one backward call.
 struct BwdPlan {
   int64_t Ho = 0, Wo = 0, P = 0, Pp = 0, Coutp = 0, R = 0, G = 1;
-  size_t o_wt = 0, o_gyt = 0, o_gyp = 0, o_col = 0, o_gcol = 0, o_gx = 0, o_gw = 0, o_goff = 0, o_gm = 0;
+  size_t o_wt = 0, o_gyt = 0, o_gyp = 0, o_col = 0, o_gcol = 0, o_gx = 0, o_gw = 0, o_goff = 0, o_gm = 0, o_gb = 0;
   int64_t TY = 0, TX = 0, BH = 0, BW = 0;
   int CBL = 0;
   bool tiled = false;
@@ -666,6 +685,7 @@ int bwd_plan(const dcn_desc* d, BwdPlan* p) {
   p->o_gw = take(static_cast<size_t>(Cout * p->R) * 4);
   p->o_goff = take(static_cast<size_t>(B * 2 * p->G * KK * p->P) * 4);
   p->o_gm = take(static_cast<size_t>(B * p->G * KK * p->P) * 4);
+  p->o_gb = take(static_cast<size_t>(Cout) * 4);
   // tiled sampling: K^2 <= 28 (seven samples per thread at most) and a box of at
   // least four channels in 64 KB of LDS
   p->TY = (p->Ho + kTH - 1) / kTH;
@@ -685,10 +705,23 @@ hipError_t launch1(const void* fn, int64_t n, void** args, hipStream_t s) {
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>((n + kBT - 1) / kBT)), dim3(kBT), args, 0, s);
 }
 
-hipError_t zero_f32(float* p, int64_t n, hipStream_t s) {
-  int nn = static_cast<int>(n);
-  void* args[] = {&p, &nn};
-  return launch1(reinterpret_cast<const void*>(&bwd_fill_zero), n, args, s);
+// ranges[i] = (fp32 buffer, destination or null, elements); null buffers are skipped
+hipError_t launch_ranges(const void* fn, int per_thread, std::initializer_list<std::tuple<float*, void*, int64_t>> list,
+                         hipStream_t s) {
+  Ranges r{};
+  int total = 0;
+  for (const auto& t : list) {
+    if (std::get<0>(t) == nullptr || std::get<2>(t) <= 0) continue;
+    r.p[r.count] = std::get<0>(t);
+    r.dst[r.count] = std::get<1>(t);
+    r.n[r.count] = static_cast<int>(std::get<2>(t));
+    r.blocks[r.count] = static_cast<int>((std::get<2>(t) + kBT * per_thread - 1) / (kBT * per_thread));
+    total += r.blocks[r.count];
+    ++r.count;
+  }
+  if (r.count == 0) return hipSuccess;
+  void* args[] = {&r};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(total)), dim3(kBT), args, 0, s);
 }
 
 template <typename T>
@@ -742,10 +775,11 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
   a.G = static_cast<int>(p.G);
   a.Cg = a.Cin / a.G;
   a.NCB = (a.Cg + kCB - 1) / kCB;
-  a.wt = ws + p.o_wt;
-  a.gyt = ws + p.o_gyt;
-  a.gyp = ws + p.o_gyp;
   const bool need_gcol = grad_x != nullptr || grad_offset != nullptr || (grad_mask != nullptr && mask != nullptr);
+  a.wt = ws + p.o_wt;
+  a.gyt = need_gcol ? static_cast<void*>(ws + p.o_gyt) : nullptr;
+  a.gyp = grad_weight != nullptr ? static_cast<void*>(ws + p.o_gyp) : nullptr;
+  a.gb32 = grad_bias != nullptr ? reinterpret_cast<float*>(ws + p.o_gb) : nullptr;
   a.col = grad_weight != nullptr ? static_cast<void*>(ws + p.o_col) : nullptr;
   a.gcol = need_gcol ? reinterpret_cast<float*>(ws + p.o_gcol) : nullptr;
   a.gx32 = grad_x != nullptr ? reinterpret_cast<float*>(ws + p.o_gx) : nullptr;
@@ -761,15 +795,16 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
   if (need_gcol) {
     BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_prep_w<T>), static_cast<int64_t>(a.R) * a.Coutp, args, s));
   }
-  if (need_gcol || grad_weight != nullptr) {
+  // every fp32 accumulator zeroed by one launch (before prep_gy adds the bias sums)
+  BWD_TRY(launch_ranges(reinterpret_cast<const void*>(&bwd_fill_zero_ranges), 4,
+                        {{a.gx32, nullptr, nx}, {a.goff32, nullptr, noff}, {a.gm32, nullptr, nm},
+                         {grad_weight != nullptr ? gw32 : nullptr, nullptr, nw}, {a.gb32, nullptr, a.Cout}},
+                        s));
+  if (need_gcol || grad_weight != nullptr || grad_bias != nullptr) {
     const dim3 grid(static_cast<unsigned>((a.Pp + 31) / 32), static_cast<unsigned>((a.Coutp + 31) / 32),
                     static_cast<unsigned>(a.B));
     BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_gy<T>), grid, dim3(kBT), args, 0, s));
   }
-  if (a.gx32 != nullptr) BWD_TRY(zero_f32(a.gx32, nx, s));
-  if (a.goff32 != nullptr) BWD_TRY(zero_f32(a.goff32, noff, s));
-  if (a.gm32 != nullptr) BWD_TRY(zero_f32(a.gm32, nm, s));
-  if (grad_weight != nullptr) BWD_TRY(zero_f32(gw32, nw, s));
   if (need_gcol) {
     GemmArgs<T> g{};
     g.A = static_cast<const T*>(a.wt);
@@ -840,14 +875,6 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     while (tiles * ks < 512 && ks * 2 <= chunks / 4) ks *= 2;
     g.ksplit = ks;
     BWD_TRY(gemm<T>(g, 1, s));
-    BWD_TRY(convert<T>(gw32, grad_weight, nw, s));
-  }
-  if (grad_bias != nullptr && a.Cout > 0) {
-    const T* gy = static_cast<const T*>(grad_out);
-    T* gb = static_cast<T*>(grad_bias);
-    int B = a.B, Cout = a.Cout, P = a.P;
-    void* bargs[] = {&gy, &gb, &B, &Cout, &P};
-    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_bias<T>), dim3(a.Cout), dim3(kBT), bargs, 0, s));
   }
   if (a.gx32 != nullptr) {
     if (p.tiled) {
@@ -858,8 +885,11 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
       BWD_TRY(convert<T>(a.gx32, grad_x, nx, s));
     }
   }
-  if (a.goff32 != nullptr) BWD_TRY(convert<T>(a.goff32, grad_offset, noff, s));
-  if (a.gm32 != nullptr) BWD_TRY(convert<T>(a.gm32, grad_mask, nm, s));
+  // the other fp32 accumulators to the element type, one launch
+  BWD_TRY(launch_ranges(reinterpret_cast<const void*>(&bwd_convert_ranges<T>), 1,
+                        {{grad_weight != nullptr ? gw32 : nullptr, grad_weight, nw}, {a.goff32, grad_offset, noff},
+                         {a.gm32, grad_mask, nm}, {a.gb32, grad_bias, a.Cout}},
+                        s));
   return DCN_OK;
 }
 
