@@ -94,6 +94,7 @@ struct BwdArgs {
   // of cps channels; gbox [B][Cin][TY][TX][BH*BW] keeps every box for the gather pass
   float* gbox;
   int TY, TX, BH, BW, CBL, nsplit, cps;
+  int tiles_total;      // workgroups of the tiled sampling kernel: B * G * nsplit * TY * TX
 };
 
 constexpr int kTH = 8, kTW = 8;   // output tile of the tiled sampling kernel
@@ -212,7 +213,13 @@ __global__ __launch_bounds__(kBT) void bwd_sample_tile(BwdArgs a) {
   uint16_t* ent_s = reinterpret_cast<uint16_t*>(lds + NE * 4);   // [NE] sample
   int* start = reinterpret_cast<int*>(lds + NE * 6);      // [BP + 1]
   const int tid = threadIdx.x;
-  int t = blockIdx.x;
+  // Workgroups go to the eight XCDs in turn (workgroup w to XCD w % 8), and each XCD has
+  // its own L2.  Neighbouring tiles share cache lines of gcol, x and col (a line holds
+  // 32 fp32 pixels of a gcol row, four tiles' worth), so consecutive logical tiles are
+  // given to workgroups of one XCD: logical index = XCD * per + (workgroup / 8).
+  const int per = (a.tiles_total + 7) / 8;
+  int t = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
+  if (t >= a.tiles_total) return;   // the last XCD's spare workgroups (uniform)
   const int tx = t % a.TX;
   t /= a.TX;
   const int ty = t % a.TY;
@@ -847,7 +854,8 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     const int nsmp = a.KK <= 12 ? 3 : 7, cq = a.KK <= 12 ? 4 : 1;
     const size_t lds = static_cast<size_t>(nsmp) * kBT * 4 * 6 + ((a.BH * a.BW + 1) * 4 + 15) / 16 * 16 +
                        static_cast<size_t>(2) * cq * nsmp * kBT * 4;
-    const unsigned grid = static_cast<unsigned>(wgs * a.nsplit);
+    a.tiles_total = static_cast<int>(wgs * a.nsplit);
+    const unsigned grid = static_cast<unsigned>((a.tiles_total + 7) / 8 * 8);
     const void* fn = a.KK <= 12 ? reinterpret_cast<const void*>(&bwd_sample_tile<T, 3, 4>)
                                 : reinterpret_cast<const void*>(&bwd_sample_tile<T, 7, 1>);
     BWD_TRY(hipLaunchKernel(fn, dim3(grid), dim3(kBT), args, lds, s));
