@@ -555,7 +555,14 @@ __global__ __launch_bounds__(256) void bwd_gemm_nt(GemmArgs<T> g) {
   __shared__ __attribute__((aligned(16))) T Bs[kGN * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kGN;
+  // Output tiles in row-major order (N fastest), handed out so that each XCD (workgroup
+  // w runs on XCD w % 8, each with its own L2) takes a contiguous run of tiles, which
+  // share their A rows (and neighbouring runs their B rows) in that L2.
+  const int ntn = (g.N + kGN - 1) / kGN, ntiles = ntn * ((g.M + kGM - 1) / kGM);
+  const int xper = (ntiles + 7) / 8;
+  const int lt = static_cast<int>(blockIdx.x % 8) * xper + static_cast<int>(blockIdx.x / 8);
+  if (lt >= ntiles) return;   // spare workgroups of the last XCD (uniform)
+  const int m0 = (lt / ntn) * kGM, n0 = (lt % ntn) * kGN;
   const int zb = blockIdx.z / g.ksplit, ks = blockIdx.z - zb * g.ksplit;
   const T* A = g.A + zb * g.sAz;
   const T* Bm = g.Bm + zb * g.sBz;
@@ -743,8 +750,8 @@ template <typename T>
 hipError_t gemm(const GemmArgs<T>& g, int zb, hipStream_t s) {
   GemmArgs<T> gg = g;
   void* args[] = {&gg};
-  const dim3 grid(static_cast<unsigned>((g.N + kGN - 1) / kGN), static_cast<unsigned>((g.M + kGM - 1) / kGM),
-                  static_cast<unsigned>(zb * g.ksplit));
+  const int ntiles = ((g.N + kGN - 1) / kGN) * ((g.M + kGM - 1) / kGM);
+  const dim3 grid(static_cast<unsigned>((ntiles + 7) / 8 * 8), 1, static_cast<unsigned>(zb * g.ksplit));
   return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_gemm_nt<T>), grid, dim3(256), args, 0, s);
 }
 

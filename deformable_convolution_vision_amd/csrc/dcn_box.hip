@@ -53,7 +53,6 @@ constexpr int kThreads = 512;    // 4 consumer + 4 producer waves (8 producer wa
 constexpr int kCK = 32;          // channels per reduction chunk (one MFMA k-step)
 constexpr int kPXB = 64;         // bytes per box pixel (32 bf16 channels)
 constexpr int kCOLB = 80;        // bytes per column-tile row (64 + 16 pad)
-constexpr int kRing = 4;         // weight-fragment prefetch ring depth
 
 // corner-table entry of one (kernel point, pixel)
 struct CEnt {
