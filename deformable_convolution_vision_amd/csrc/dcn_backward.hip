@@ -87,6 +87,7 @@ struct BwdArgs {
   float* goff32;        // [B][2GK^2][P] or null
   float* gm32;          // [B][GK^2][P] or null
   float* gb32;          // [Cout] or null (bias gradient accumulator)
+  float* outliers;      // [1]: set to 1 when a corner outside its box went to gx32
   int B, Cin, H, W, Cout, K, KK, stride, pad, dil, Ho, Wo, P, Pp, Coutp, R, G, Cg, NCB;
   // tiled sampling (bwd_sample_tile): output tiles of kTH x kTW pixels, an LDS box of
   // BH x BW input pixels per channel (the tile's footprint plus a margin of kMargin),
@@ -377,6 +378,7 @@ __global__ __launch_bounds__(kBT) void bwd_sample_tile(BwdArgs a) {
         const float tg = gc * m_[i];
         tg_s[q * (NS * kBT) + tid + i * kBT] = tg;
         if (bl_[i] < 0 && f != 0) {   // corners outside the box
+          *a.outliers = 1.f;
           float* gx = a.gx32 + pl + q00_[i];
           if (f & 1) unsafeAtomicAdd(gx, tg * w_[i][0]);
           if (f & 2) unsafeAtomicAdd(gx + 1, tg * w_[i][1]);
@@ -434,7 +436,8 @@ __global__ __launch_bounds__(kBT) void bwd_gather_x(BwdArgs a, T* grad_x) {
   const int ry = yy + a.pad + kMargin, rx = xx + a.pad + kMargin;   // >= 0
   const int ty1 = min(ry / sy, a.TY - 1), tx1 = min(rx / sx, a.TX - 1);
   const int BP = a.BH * a.BW;
-  float acc = a.gx32[e];
+  // the fp32 accumulator holds anything only if some corner fell outside its box
+  float acc = *a.outliers != 0.f ? a.gx32[e] : 0.f;
   const float* base = a.gbox + static_cast<size_t>(bc) * a.TY * a.TX * BP;
   for (int ty = ty1; ty >= 0; --ty) {
     const int yb = ry - ty * sy;   // row inside tile ty's box
@@ -661,6 +664,7 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 struct BwdPlan {
   int64_t Ho = 0, Wo = 0, P = 0, Pp = 0, Coutp = 0, R = 0, G = 1;
   size_t o_wt = 0, o_gyt = 0, o_gyp = 0, o_col = 0, o_gcol = 0, o_gx = 0, o_gw = 0, o_goff = 0, o_gm = 0, o_gb = 0;
+  size_t o_flag = 0;
   int64_t TY = 0, TX = 0, BH = 0, BW = 0;
   int CBL = 0;
   bool tiled = false;
@@ -700,6 +704,7 @@ int bwd_plan(const dcn_desc* d, BwdPlan* p) {
   p->o_goff = take(static_cast<size_t>(B * 2 * p->G * KK * p->P) * 4);
   p->o_gm = take(static_cast<size_t>(B * p->G * KK * p->P) * 4);
   p->o_gb = take(static_cast<size_t>(Cout) * 4);
+  p->o_flag = take(4);
   // tiled sampling: K^2 <= 28 (seven samples per thread at most) and a box of at
   // least four channels in 64 KB of LDS
   p->TY = (p->Ho + kTH - 1) / kTH;
@@ -794,6 +799,7 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
   a.gyt = need_gcol ? static_cast<void*>(ws + p.o_gyt) : nullptr;
   a.gyp = grad_weight != nullptr ? static_cast<void*>(ws + p.o_gyp) : nullptr;
   a.gb32 = grad_bias != nullptr ? reinterpret_cast<float*>(ws + p.o_gb) : nullptr;
+  a.outliers = reinterpret_cast<float*>(ws + p.o_flag);
   a.col = grad_weight != nullptr ? static_cast<void*>(ws + p.o_col) : nullptr;
   a.gcol = need_gcol ? reinterpret_cast<float*>(ws + p.o_gcol) : nullptr;
   a.gx32 = grad_x != nullptr ? reinterpret_cast<float*>(ws + p.o_gx) : nullptr;
@@ -812,7 +818,8 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
   // every fp32 accumulator zeroed by one launch (before prep_gy adds the bias sums)
   BWD_TRY(launch_ranges(reinterpret_cast<const void*>(&bwd_fill_zero_ranges), 4,
                         {{a.gx32, nullptr, nx}, {a.goff32, nullptr, noff}, {a.gm32, nullptr, nm},
-                         {grad_weight != nullptr ? gw32 : nullptr, nullptr, nw}, {a.gb32, nullptr, a.Cout}},
+                         {grad_weight != nullptr ? gw32 : nullptr, nullptr, nw}, {a.gb32, nullptr, a.Cout},
+                         {a.outliers, nullptr, 1}},
                         s));
   if (need_gcol || grad_weight != nullptr || grad_bias != nullptr) {
     const dim3 grid(static_cast<unsigned>((a.Pp + 31) / 32), static_cast<unsigned>((a.Coutp + 31) / 32),
