@@ -890,11 +890,12 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     g.nseg = a.B;
     g.sAs = static_cast<long long>(a.Cout) * a.Pp;
     g.sBs = static_cast<long long>(a.R) * a.Pp;
-    // split the reduction until the output tiles and splits give about two workgroups per CU
+    // split the reduction until the output tiles and splits give about one workgroup per CU
+    // (more splits measured slower: more fp32 atomics into the accumulator)
     const int tiles = ((a.Cout + kGM - 1) / kGM) * ((a.R + kGN - 1) / kGN);
     const int chunks = ((a.Pp + kGK - 1) / kGK) * a.B;
     int ks = 1;
-    while (tiles * ks < 512 && ks * 2 <= chunks / 4) ks *= 2;
+    while (tiles * ks < 256 && ks * 2 <= chunks / 4) ks *= 2;
     g.ksplit = ks;
     BWD_TRY(gemm<T>(g, 1, s));
   }
