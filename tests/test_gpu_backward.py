@@ -130,3 +130,32 @@ def test_backward_empty_problems(dtype):
     gx, goff, gw, gb, gm = dcn.deform_conv2d_backward(gy, x, off, w0, 1, 1, 1, mask=m)
     torch.cuda.synchronize()
     assert torch.all(gx == 0) and torch.all(goff == 0) and torch.all(gm == 0)
+
+
+def test_backward_c4_layer_slices():
+    """The c4 layer's backward at full size, in the bench's launch configuration, on the
+    slices the oracle computes in seconds: the weight and bias gradients of the first and
+    last output channels (they depend on those channels of grad_out only) and the input
+    gradient of the first and last input channels (one offset group: they depend on those
+    channels of x and weight only)."""
+    from deformable_convolution_vision_amd.workloads import WORKLOADS
+    w = WORKLOADS["c4_bwd"]
+    inp = generate(w)
+    gy = grad_output(w)
+    print("[gpu-test] backward c4 slices", flush=True)
+    g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    gx, goff, gw, gb, gm = dcn.deform_conv2d_backward(gy.cuda(), g["x"], g["offset"], g["weight"], w.stride, w.pad,
+                                                      w.dilation, mask=g["mask"])
+    torch.cuda.synchronize()
+    osel = [0, w.Cout - 1]
+    ref = oracle.backward(inp["x"], inp["offset"], inp["weight"][osel].contiguous(), gy[:, osel].contiguous(),
+                          w.stride, w.pad, w.dilation, mask=inp["mask"], want=("grad_weight", "grad_bias"))
+    compare(gw[osel], ref["grad_weight"], "bf16", "c4 grad_weight rows")
+    compare(gb[osel], ref["grad_bias"], "bf16", "c4 grad_bias")
+    csel = [0, w.Cin - 1]
+    refx = oracle.backward(inp["x"][:, csel].contiguous(), inp["offset"], inp["weight"][:, csel].contiguous(), gy,
+                           w.stride, w.pad, w.dilation, mask=inp["mask"], want=("grad_x",))
+    compare(gx[:, csel], refx["grad_x"], "bf16", "c4 grad_x planes")
+    # the offset and mask gradients sum over every channel: finite and not all zero
+    assert torch.isfinite(goff.float()).all() and torch.isfinite(gm.float()).all()
+    assert goff.float().abs().sum() > 0 and gm.float().abs().sum() > 0
