@@ -413,7 +413,9 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
   // of the buffer, which moves no data, so every block is issued unconditionally
   // and the number of vector-memory operations of each step is a compile-time
   // constant (exact wait counts for the prefetched global-path corners below).
-  constexpr int MAXB = Cfg::BOX_PX / (16 * PW);   // blocks per wave; PW * MAXB blocks fill the buffer
+  // blocks per wave, rounded up: PW * MAXB blocks cover the whole buffer (with eight
+  // producer waves a buffer of 960 or 832 pixels is not a whole number of 128-pixel rounds)
+  constexpr int MAXB = (Cfg::BOX_PX + 16 * PW - 1) / (16 * PW);
   const uint32_t xs_bytes = static_cast<uint32_t>(a.B * a.H) * static_cast<uint32_t>(a.W * Cp) * 2u;
   uint32_t boff[MAXB];
   if (!consumer) {
@@ -448,7 +450,13 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
     const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(cc);
     static_for<decltype(j0c)::value, decltype(j1c)::value>([&](auto jc) __attribute__((always_inline)) {
       constexpr int j = decltype(jc)::value;
-      buffer_to_lds16(rsrc, dst + (pw + PW * j) * 1024, boff[j]);
+      if constexpr (PW * MAXB * 16 > Cfg::BOX_PX) {
+        // the rounded-up last round: only blocks inside the buffer are issued (an
+        // out-of-range load still has an LDS destination)
+        if (pw + PW * j < Cfg::BOX_PX / 16) buffer_to_lds16(rsrc, dst + (pw + PW * j) * 1024, boff[j]);
+      } else {
+        buffer_to_lds16(rsrc, dst + (pw + PW * j) * 1024, boff[j]);
+      }
     });
   };
   auto copy_box = [&](int cc, unsigned char* dst) __attribute__((always_inline)) {

@@ -283,9 +283,13 @@ def test_box_producer_waves(variant, tile, pw, monkeypatch):
     monkeypatch.setenv("DCN_BOX_TILE", tile)
     monkeypatch.setenv("DCN_BOX_ROLES", "0")
     monkeypatch.setenv("DCN_BOX_PW", pw)
-    shapes = [(2, 64, 9, 10, 260, 3, 2, 1, 1), (2, 40, 12, 14, 300, 3, 1, 2, 2), (1, 256, 30, 34, 256, 3, 2, 1, 1)]
+    # the last shape: an image large enough for boxes at full capacity, and offsets that
+    # reach the boxes' last rows (every box pixel must be copied)
+    shapes = [(2, 64, 9, 10, 260, 3, 2, 1, 1), (2, 40, 12, 14, 300, 3, 1, 2, 2), (1, 256, 30, 34, 256, 3, 2, 1, 1),
+              (1, 64, 44, 52, 128, 3, 1, 1, 1)]
     for seed, shape in enumerate(shapes):
-        w = make(f"pw{pw}_{variant}_{tile}", "bf16", *shape, offset="normal:2", seed=seed)
+        w = make(f"pw{pw}_{variant}_{tile}", "bf16", *shape, offset="uniform:9" if seed == 3 else "normal:2",
+                 seed=seed)
         desc = dcn.make_desc(w.B, w.Cin, w.H, w.W, w.Cout, w.K, w.stride, w.pad, w.dilation, dcn.BF16)
         plan = dcn.dcn_plan_describe(desc)
         print(f"[gpu-test] {shape} {plan}", flush=True)
