@@ -101,7 +101,7 @@ WORKLOADS = {
     "c4_om": Workload("c4_om", "bf16", 2, 256, 100, 168, 27, 3, 2, 1, 1, 50, 84,
                       offset="normal:1", mask=None, bias="normal:0.1", seed=1006, op="offset_mask"),
 }
-ORDER = ["tiny", "single224", "c3", "c4", "c5"]
+ORDER = ["tiny", "single224", "c3", "c4", "c5", "c4_g4", "c4_om", "c4_bwd", "roi_c4"]
 
 
 def _draw(kind: str, shape, g: torch.Generator) -> torch.Tensor:
