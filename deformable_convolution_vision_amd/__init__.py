@@ -224,6 +224,37 @@ def check_tensors(desc: Desc, input, offset, weight, bias, mask) -> tuple[int, i
     return Ho, Wo
 
 
+def _check_out(out, shape, dtype, device, name="out"):
+    """A caller-supplied output: the exact shape, dtype and device, contiguous."""
+    if not isinstance(out, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    if out.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {out.dtype}")
+    if not out.is_cuda or out.device != device:
+        raise ValueError(f"{name} must be on {device}, got {out.device}")
+    if not out.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(workspace, nbytes: int, device):
+    """The caller's workspace after checks (contiguous, on the device, at least nbytes),
+    or a fresh one when none is given."""
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a tensor")
+    if not workspace.is_cuda or workspace.device != device:
+        raise ValueError(f"workspace must be on {device}, got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    have = workspace.numel() * workspace.element_size()
+    if have < nbytes:
+        raise ValueError(f"workspace holds {have} bytes, the call needs {nbytes}")
+    return workspace
+
+
 def deform_conv2d(input, offset, weight, bias=None, stride=1, padding=0, dilation=1, mask=None,
                   out=None, workspace=None):
     """Deformable convolution forward on the GPU (torchvision's argument order).
@@ -235,11 +266,13 @@ def deform_conv2d(input, offset, weight, bias=None, stride=1, padding=0, dilatio
     """
     desc = describe(input, weight, stride, padding, dilation, offset)
     Ho, Wo = check_tensors(desc, input, offset, weight, bias, mask)
+    shape = (desc.batch, desc.out_channels, Ho, Wo)
     if out is None:
-        out = torch.empty((desc.batch, desc.out_channels, Ho, Wo), dtype=input.dtype, device=input.device)
+        out = torch.empty(shape, dtype=input.dtype, device=input.device)
+    else:
+        _check_out(out, shape, input.dtype, input.device)
     nbytes = dcn_workspace_bytes(desc)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=input.device)
+    workspace = _workspace(workspace, nbytes, input.device)
     with torch.cuda.device(input.device):
         dcn_forward(desc, input, offset, mask, weight, bias, out, workspace if nbytes else None, nbytes)
     return out
@@ -290,8 +323,7 @@ def offset_mask(input, weight_om, bias_om=None, stride=1, padding=0, dilation=1,
     offset = torch.empty((B, 2 * G * K * K, Ho, Wo), dtype=input.dtype, device=input.device)
     mask = torch.empty((B, G * K * K, Ho, Wo), dtype=input.dtype, device=input.device)
     nbytes = dcn_offset_mask_workspace_bytes(desc)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=input.device)
+    workspace = _workspace(workspace, nbytes, input.device)
     with torch.cuda.device(input.device):
         dcn_offset_mask(desc, input, weight_om, bias_om, offset, mask, workspace if nbytes else None, nbytes)
     return offset, mask
@@ -334,8 +366,7 @@ def deform_conv2d_backward(grad_out, input, offset, weight, stride=1, padding=0,
     gb = torch.empty(desc.out_channels, dtype=input.dtype, device=input.device) if with_bias else None
     gm = torch.empty_like(mask) if mask is not None else None
     nbytes = dcn_backward_workspace_bytes(desc)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=input.device)
+    workspace = _workspace(workspace, nbytes, input.device)
     with torch.cuda.device(input.device):
         dcn_backward(desc, input, offset, mask, weight, grad_out, gx, goff, gm, gw, gb,
                      workspace if nbytes else None, nbytes)

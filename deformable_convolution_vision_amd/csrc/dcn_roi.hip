@@ -21,6 +21,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "dcn.h"
 #include "dcn_internal.h"
@@ -44,6 +45,42 @@ template <>
 __device__ __forceinline__ float st<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ uint16_t st<uint16_t>(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+
+// One bilinear sample of bin (i, j), sub-cell (u, v): its position in P, its top-left
+// neighbour and the four neighbour weights in fp32.  The position follows the
+// definition: y1 + (i + (u + 1/2) / S) * h / k + dy, likewise for columns (with 1/S and
+// h/k formed once per RoI).  The fp32 kernel takes P = double, so the RoI arithmetic rounds nothing that
+// a 1e-4 relative bound would see near the image border; for bf16 results fp32
+// positions (relative error about 1e-6 of the coordinates) are far inside the bound.
+template <typename P>
+struct RoiGeom {
+  P y1, x1, h, w, dy, dx;
+  P bh, bw, inv_s;   // h / k, w / k, 1 / S
+};
+struct RoiSample {
+  bool any;        // at least one neighbour inside the image
+  int y0, x0;
+  float w00, w01, w10, w11;
+};
+template <typename P>
+__device__ __forceinline__ RoiSample roi_sample(const RoiGeom<P>& g, int i, int j, int u, int v, int H, int W) {
+  const P half = static_cast<P>(0.5);
+  const P py = g.y1 + (static_cast<P>(i) + (static_cast<P>(u) + half) * g.inv_s) * g.bh + g.dy;
+  const P px = g.x1 + (static_cast<P>(j) + (static_cast<P>(v) + half) * g.inv_s) * g.bw + g.dx;
+  RoiSample r;
+  // no neighbour inside (or NaN): nothing to add
+  r.any = py > static_cast<P>(-1) && py < static_cast<P>(H) && px > static_cast<P>(-1) && px < static_cast<P>(W);
+  if (!r.any) return r;
+  const P y0f = floor(py), x0f = floor(px);
+  const float ly = static_cast<float>(py - y0f), lx = static_cast<float>(px - x0f);
+  r.y0 = static_cast<int>(y0f);
+  r.x0 = static_cast<int>(x0f);
+  r.w00 = (1.f - ly) * (1.f - lx);
+  r.w01 = (1.f - ly) * lx;
+  r.w10 = ly * (1.f - lx);
+  r.w11 = ly * lx;
+  return r;
+}
 
 struct RoiArgs {
   const void* x;        // [B][C][H][W]
@@ -72,35 +109,38 @@ __global__ __launch_bounds__(kRT) void roi_pool_kernel(RoiArgs a) {
     return;
   }
   const int b = static_cast<int>(bi);
-  const float x1 = roi[1] * a.scale, y1 = roi[2] * a.scale;
-  const float w = (roi[3] - roi[1]) * a.scale, h = (roi[4] - roi[2]) * a.scale;
-  const float bw = w / static_cast<float>(a.k), bh = h / static_cast<float>(a.k);
-  float dy = 0.f, dx = 0.f, m = 1.f;
+  using P = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+  RoiGeom<P> geo;
+  geo.x1 = static_cast<P>(roi[1]) * a.scale;
+  geo.y1 = static_cast<P>(roi[2]) * a.scale;
+  geo.w = (static_cast<P>(roi[3]) - roi[1]) * a.scale;
+  geo.h = (static_cast<P>(roi[4]) - roi[2]) * a.scale;
+  geo.bh = geo.h / static_cast<P>(a.k);
+  geo.bw = geo.w / static_cast<P>(a.k);
+  geo.inv_s = static_cast<P>(1) / static_cast<P>(a.S);
+  geo.dy = geo.dx = 0;
+  float m = 1.f;
   if (a.offset != nullptr) {
     const T* off = static_cast<const T*>(a.offset);
-    dy = a.gamma * h * ld(off, ((static_cast<size_t>(r) * 2 + 0) * a.k + i) * a.k + j);
-    dx = a.gamma * w * ld(off, ((static_cast<size_t>(r) * 2 + 1) * a.k + i) * a.k + j);
+    geo.dy = a.gamma * geo.h * ld(off, ((static_cast<size_t>(r) * 2 + 0) * a.k + i) * a.k + j);
+    geo.dx = a.gamma * geo.w * ld(off, ((static_cast<size_t>(r) * 2 + 1) * a.k + i) * a.k + j);
   }
   if (a.mask != nullptr) m = ld(static_cast<const T*>(a.mask), (static_cast<size_t>(r) * a.k + i) * a.k + j);
   const T* plane = static_cast<const T*>(a.x) + (static_cast<size_t>(b) * a.C + c) * a.H * a.W;
   const float inv = 1.f / static_cast<float>(a.S);
   float acc = 0.f;
   for (int u = 0; u < a.S; ++u) {
-    const float py = y1 + (static_cast<float>(i) + (static_cast<float>(u) + 0.5f) * inv) * bh + dy;
     for (int v = 0; v < a.S; ++v) {
-      const float px = x1 + (static_cast<float>(j) + (static_cast<float>(v) + 0.5f) * inv) * bw + dx;
-      // no neighbour inside (or NaN): nothing to add
-      if (!(py > -1.f && py < static_cast<float>(a.H) && px > -1.f && px < static_cast<float>(a.W))) continue;
-      const float y0f = floorf(py), x0f = floorf(px);
-      const float ly = py - y0f, lx = px - x0f;
-      const int y0 = static_cast<int>(y0f), x0 = static_cast<int>(x0f);
+      const RoiSample sp = roi_sample(geo, i, j, u, v, a.H, a.W);
+      if (!sp.any) continue;
+      const int y0 = sp.y0, x0 = sp.x0;
       const bool iy0 = y0 >= 0, iy1 = y0 + 1 < a.H, ix0 = x0 >= 0, ix1 = x0 + 1 < a.W;
       const int q = y0 * a.W + x0;
       const float v00 = (iy0 && ix0) ? ld(plane, q) : 0.f;
       const float v01 = (iy0 && ix1) ? ld(plane, q + 1) : 0.f;
       const float v10 = (iy1 && ix0) ? ld(plane, q + a.W) : 0.f;
       const float v11 = (iy1 && ix1) ? ld(plane, q + a.W + 1) : 0.f;
-      acc += (1.f - ly) * ((1.f - lx) * v00 + lx * v01) + ly * ((1.f - lx) * v10 + lx * v11);
+      acc += sp.w00 * v00 + sp.w01 * v01 + sp.w10 * v10 + sp.w11 * v11;
     }
   }
   out[e] = st<T>(m * acc * inv * inv);
@@ -120,9 +160,14 @@ __global__ __launch_bounds__(kRT) void roi_pool_cl_kernel(RoiArgs a, const uint1
   const float bi = roi[0];
   const bool batch_ok = bi >= 0.f && bi < static_cast<float>(a.B);
   const int b = batch_ok ? static_cast<int>(bi) : 0;
-  const float x1 = roi[1] * a.scale, y1 = roi[2] * a.scale;
-  const float w = (roi[3] - roi[1]) * a.scale, h = (roi[4] - roi[2]) * a.scale;
-  const float bw = w / static_cast<float>(a.k), bh = h / static_cast<float>(a.k);
+  RoiGeom<float> geo;
+  geo.x1 = roi[1] * a.scale;
+  geo.y1 = roi[2] * a.scale;
+  geo.w = (roi[3] - roi[1]) * a.scale;
+  geo.h = (roi[4] - roi[2]) * a.scale;
+  geo.bh = geo.h / static_cast<float>(a.k);
+  geo.bw = geo.w / static_cast<float>(a.k);
+  geo.inv_s = 1.f / static_cast<float>(a.S);
   const float inv = 1.f / static_cast<float>(a.S);
   const uint16_t* img = xs + static_cast<size_t>(b) * a.H * a.W * Cp;
   for (int u = threadIdx.x; u < kk * 8; u += blockDim.x) {
@@ -133,24 +178,22 @@ __global__ __launch_bounds__(kRT) void roi_pool_cl_kernel(RoiArgs a, const uint1
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     float m = 0.f;
     if (batch_ok && c < a.C) {
-      float dy = 0.f, dx = 0.f;
+      RoiGeom<float> g = geo;
+      g.dy = g.dx = 0.f;
       m = 1.f;
       if (a.offset != nullptr) {
         const uint16_t* off = static_cast<const uint16_t*>(a.offset);
-        dy = a.gamma * h * ld(off, ((static_cast<size_t>(r) * 2 + 0) * a.k + i) * a.k + j);
-        dx = a.gamma * w * ld(off, ((static_cast<size_t>(r) * 2 + 1) * a.k + i) * a.k + j);
+        g.dy = a.gamma * g.h * ld(off, ((static_cast<size_t>(r) * 2 + 0) * a.k + i) * a.k + j);
+        g.dx = a.gamma * g.w * ld(off, ((static_cast<size_t>(r) * 2 + 1) * a.k + i) * a.k + j);
       }
       if (a.mask != nullptr) m = ld(static_cast<const uint16_t*>(a.mask), (static_cast<size_t>(r) * a.k + i) * a.k + j);
       for (int su = 0; su < a.S; ++su) {
-        const float py = y1 + (static_cast<float>(i) + (static_cast<float>(su) + 0.5f) * inv) * bh + dy;
         for (int sv = 0; sv < a.S; ++sv) {
-          const float px = x1 + (static_cast<float>(j) + (static_cast<float>(sv) + 0.5f) * inv) * bw + dx;
-          if (!(py > -1.f && py < static_cast<float>(a.H) && px > -1.f && px < static_cast<float>(a.W))) continue;
-          const float y0f = floorf(py), x0f = floorf(px);
-          const float ly = py - y0f, lx = px - x0f;
-          const int y0 = static_cast<int>(y0f), x0 = static_cast<int>(x0f);
+          const RoiSample sp = roi_sample(g, i, j, su, sv, a.H, a.W);
+          if (!sp.any) continue;
+          const int y0 = sp.y0, x0 = sp.x0;
           const bool iy0 = y0 >= 0, iy1 = y0 + 1 < a.H, ix0 = x0 >= 0, ix1 = x0 + 1 < a.W;
-          const float wt[4] = {(1.f - ly) * (1.f - lx), (1.f - ly) * lx, ly * (1.f - lx), ly * lx};
+          const float wt[4] = {sp.w00, sp.w01, sp.w10, sp.w11};
           const bool in[4] = {iy0 && ix0, iy0 && ix1, iy1 && ix0, iy1 && ix1};
           // the four corner loads together, from valid addresses (a corner outside the
           // image reads pixel 0 and is replaced by zeros)

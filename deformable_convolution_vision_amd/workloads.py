@@ -42,12 +42,14 @@ class Workload:
     Ho: int               # stated output size (data, not computed here)
     Wo: int
     offset: str           # "uniform:a" U(-a,a) | "normal:s" s*N(0,1) | "tanh:s" s*tanh(N(0,1))
+                          # | "frac:n:lo:hi" an integer uniform in [-n, n] plus U(lo, hi)
     mask: str | None      # "sigmoid" = sigmoid(N(0,1)) | "ones" | None (DCNv1)
     bias: str | None      # "zeros" | "normal:s" s*N(0,1) | None
     seed: int = 0
-    x: str = "normal"     # "normal" = N(0,1)
+    x: str = "normal"     # "normal" = N(0,1) | "checker:e" = (-1)^(row+col) * (1 + e*N(0,1))
     groups: int = 1       # offset groups: offset has 2*groups*K^2 channels, mask groups*K^2
     op: str = "forward"   # "forward" | "offset_mask" (the DCNv2 offset/mask convolution; Cout = 3*groups*K^2)
+    weight: str = "kaiming"   # "kaiming" = Kaiming-normal | "kaiming_abs" = its absolute value
 
     @property
     def torch_dtype(self):
@@ -100,6 +102,12 @@ WORKLOADS = {
                        offset="normal:0.1", mask="sigmoid", bias=None, seed=1008, op="roi_pool"),
     "c4_om": Workload("c4_om", "bf16", 2, 256, 100, 168, 27, 3, 2, 1, 1, 50, 84,
                       offset="normal:1", mask=None, bias="normal:0.1", seed=1006, op="offset_mask"),
+    # the c4 layer on inputs whose four corners nearly cancel: x of alternating sign
+    # and almost equal magnitude, sample fractions in [0.45, 0.55], weights of one sign
+    # (a parity case for the interpolation's precision, not a bench workload)
+    "c4_cancel": Workload("c4_cancel", "bf16", 2, 256, 100, 168, 256, 3, 2, 1, 1, 50, 84,
+                          offset="frac:2:0.45:0.55", mask="sigmoid", bias=None, seed=1009,
+                          x="checker:0.01", weight="kaiming_abs"),
 }
 ORDER = ["tiny", "single224", "c3", "c4", "c5", "c4_g4", "c4_om", "c4_bwd", "roi_c4"]
 
@@ -116,6 +124,14 @@ def _draw(kind: str, shape, g: torch.Generator) -> torch.Tensor:
         return torch.tanh(torch.randn(shape, generator=g)) * float(arg)
     if name == "sigmoid":
         return torch.sigmoid(torch.randn(shape, generator=g))
+    if name == "frac":   # integer part uniform in [-n, n], fractional part U(lo, hi)
+        n, lo, hi = arg.split(":")
+        ip = torch.randint(-int(n), int(n) + 1, shape, generator=g).float()
+        return ip + float(lo) + torch.rand(shape, generator=g) * (float(hi) - float(lo))
+    if name == "checker":   # signs alternating like a checkerboard over the last two axes
+        e = float(arg)
+        sign = 1.0 - 2.0 * ((torch.arange(shape[-2])[:, None] + torch.arange(shape[-1])[None, :]) % 2).float()
+        return sign * (1.0 + e * torch.randn(shape, generator=g))
     if name == "ones":
         return torch.ones(shape)
     if name == "zeros":
@@ -132,6 +148,8 @@ def generate(w: Workload, seed: int | None = None) -> dict[str, torch.Tensor | N
     KK = w.K * w.K
     x = _draw(w.x, (w.B, w.Cin, w.H, w.W), g)
     weight = torch.randn((w.Cout, w.Cin, w.K, w.K), generator=g) * math.sqrt(2.0 / (w.Cin * KK))
+    if w.weight == "kaiming_abs":
+        weight = weight.abs()
     if w.op == "offset_mask":   # x, the 3GK^2-output weight, its bias
         bias = _draw(w.bias, (w.Cout,), g) if w.bias is not None else None
         dt = w.torch_dtype
@@ -181,7 +199,7 @@ def roi_inputs(w: Workload, num_rois: int, k: int, image_hw: tuple[int, int], se
 def custom(name: str, dtype: str, B: int, Cin: int, H: int, W: int, Cout: int, K: int,
            stride: int, pad: int, dilation: int, Ho: int, Wo: int, offset: str = "normal:1",
            mask: str | None = "sigmoid", bias: str | None = "normal:0.1", seed: int = 0,
-           x: str = "normal", groups: int = 1, op: str = "forward") -> Workload:
+           x: str = "normal", groups: int = 1, op: str = "forward", weight: str = "kaiming") -> Workload:
     """A workload of any shape (used for edge cases); the caller supplies Ho, Wo."""
     return Workload(name, dtype, B, Cin, H, W, Cout, K, stride, pad, dilation, Ho, Wo,
-                    offset=offset, mask=mask, bias=bias, seed=seed, x=x, groups=groups, op=op)
+                    offset=offset, mask=mask, bias=bias, seed=seed, x=x, groups=groups, op=op, weight=weight)

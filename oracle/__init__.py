@@ -68,7 +68,7 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.oracle_points.restype = ctypes.c_int
     lib.oracle_backward.argtypes = [ctypes.POINTER(_Desc), P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_backward.restype = ctypes.c_int
-    lib.oracle_roi_pool.argtypes = [ctypes.POINTER(_RoiDesc), P, P, P, P, P, ctypes.c_int]
+    lib.oracle_roi_pool.argtypes = [ctypes.POINTER(_RoiDesc), P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_roi_pool.restype = ctypes.c_int
     lib.oracle_threads.argtypes = [ctypes.c_int]
     lib.oracle_threads.restype = ctypes.c_int
@@ -192,11 +192,12 @@ def backward(x, offset, weight, grad_out, stride=1, padding=0, dilation=1, mask=
 
 
 def roi_pool(x, rois, k, S, spatial_scale=1.0, gamma=0.1, offset=None, mask=None, threads=0,
-             lib_path: str = LIB):
+             with_abs=False, lib_path: str = LIB):
     """Deformable RoI pooling (definition and readings in dcn_oracle.h): x [B,C,H,W],
     rois [R,5] = (batch index, x1, y1, x2, y2), offset [R,2,k,k] (row, column; normalised
     by the RoI's height and width and scaled by gamma) or None, mask [R,k,k] or None.
-    Returns float64 [R,C,k,k]."""
+    Returns float64 [R,C,k,k], and with ``with_abs`` also the sum of |terms| of each
+    output (|m| / S^2 times the sum of |corner weight * value| over its samples)."""
     lib = load(lib_path)
     x, rois, offset, mask = map(_f32, (x, rois, offset, mask))
     B, C, H, W = x.shape
@@ -209,10 +210,12 @@ def roi_pool(x, rois, k, S, spatial_scale=1.0, gamma=0.1, offset=None, mask=None
         raise ValueError(f"mask must be {(R, k, k)}")
     d = _RoiDesc(B, C, H, W, R, k, S, float(spatial_scale), float(gamma))
     out = np.empty((R, C, k, k), dtype=np.float64)
-    rc = lib.oracle_roi_pool(ctypes.byref(d), _ptr(x), _ptr(rois), _ptr(offset), _ptr(mask), _ptr(out), threads)
+    ab = np.empty_like(out) if with_abs else None
+    rc = lib.oracle_roi_pool(ctypes.byref(d), _ptr(x), _ptr(rois), _ptr(offset), _ptr(mask), _ptr(out),
+                             _ptr(ab), threads)
     if rc != 0:
         raise ValueError("oracle_roi_pool rejected its arguments")
-    return out
+    return (out, ab) if with_abs else out
 
 
 def threads_used(threads: int = 0, lib_path: str = LIB) -> int:

@@ -42,8 +42,10 @@ int64_t out_size(int64_t in, int64_t K, int64_t stride, int64_t pad, int64_t dil
 // integer neighbours, each weighted by (1-|py-yy|)*(1-|px-xx|) (the areas of
 // the bilinear-interpolation equation), a neighbour outside the plane
 // counting as zero.  Returns the sample; inside tests use floating compares
-// before any integer conversion, so NaN and infinite positions give zero.
-double bilinear_zero_outside(const float* plane, int64_t H, int64_t W, double py, double px) {
+// before any integer conversion, so NaN and infinite positions give zero.  When
+// abs_sum is not null, the sum of the |weight * value| of the corners is added to it.
+double bilinear_zero_outside(const float* plane, int64_t H, int64_t W, double py, double px,
+                             double* abs_sum = nullptr) {
   const double y0 = std::floor(py);
   const double x0 = std::floor(px);
   double acc = 0.0;
@@ -56,7 +58,9 @@ double bilinear_zero_outside(const float* plane, int64_t H, int64_t W, double py
       const double g = (1.0 - std::fabs(py - yy)) * (1.0 - std::fabs(px - xx));
       const int64_t iy = static_cast<int64_t>(yy);
       const int64_t ix = static_cast<int64_t>(xx);
-      acc += g * static_cast<double>(plane[iy * W + ix]);
+      const double t = g * static_cast<double>(plane[iy * W + ix]);
+      acc += t;
+      if (abs_sum != nullptr) *abs_sum += std::fabs(t);
     }
   }
   return acc;
@@ -237,7 +241,7 @@ extern "C" int oracle_backward(const oracle_desc* d, const float* x, const float
 }
 
 extern "C" int oracle_roi_pool(const oracle_roi_desc* d, const float* x, const float* rois, const float* offset,
-                               const float* mask, double* out, int threads) {
+                               const float* mask, double* out, double* abs_out, int threads) {
   if (d == nullptr || x == nullptr || rois == nullptr || out == nullptr) return -1;
   if (d->B < 1 || d->C < 1 || d->H < 1 || d->W < 1 || d->R < 0 || d->k < 1 || d->S < 1) return -1;
 #ifdef _OPENMP
@@ -261,6 +265,8 @@ extern "C" int oracle_roi_pool(const oracle_roi_desc* d, const float* x, const f
     for (int64_t i = 0; i < k; ++i)
       for (int64_t j = 0; j < k; ++j) {
         double* y = out + (rc * k + i) * k + j;
+        double* ya = abs_out != nullptr ? abs_out + (rc * k + i) * k + j : nullptr;
+        if (ya != nullptr) *ya = 0.0;
         if (!batch_ok) {
           *y = 0.0;
           continue;
@@ -268,14 +274,15 @@ extern "C" int oracle_roi_pool(const oracle_roi_desc* d, const float* x, const f
         const double dy = offset != nullptr ? d->gamma * h * static_cast<double>(offset[((r * 2 + 0) * k + i) * k + j]) : 0.0;
         const double dx = offset != nullptr ? d->gamma * w * static_cast<double>(offset[((r * 2 + 1) * k + i) * k + j]) : 0.0;
         const double m = mask != nullptr ? static_cast<double>(mask[(r * k + i) * k + j]) : 1.0;
-        double acc = 0.0;
+        double acc = 0.0, acc_abs = 0.0;
         for (int64_t u = 0; u < S; ++u)
           for (int64_t v = 0; v < S; ++v) {
             const double py = y1 + (static_cast<double>(i) + (static_cast<double>(u) + 0.5) / static_cast<double>(S)) * h / static_cast<double>(k) + dy;
             const double px = x1 + (static_cast<double>(j) + (static_cast<double>(v) + 0.5) / static_cast<double>(S)) * w / static_cast<double>(k) + dx;
-            acc += bilinear_zero_outside(plane, d->H, d->W, py, px);
+            acc += bilinear_zero_outside(plane, d->H, d->W, py, px, &acc_abs);
           }
         *y = m * acc / static_cast<double>(S * S);
+        if (ya != nullptr) *ya = std::fabs(m) * acc_abs / static_cast<double>(S * S);
       }
   }
   return 0;

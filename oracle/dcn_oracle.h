@@ -137,13 +137,16 @@ int oracle_backward(const oracle_desc* d, const float* x, const float* offset,
  * the convolution, and no +1 is added to the RoI size; offset channel 0 is the row
  * displacement; the mask scales the bin's average.
  * x[B,C,H,W], rois[R,5] (float), offset[R,2,k,k] or NULL, mask[R,k,k] or NULL,
- * out[R,C,k,k] doubles.  A RoI whose batch index is outside [0, B) gives zeros. */
+ * out[R,C,k,k] doubles.  A RoI whose batch index is outside [0, B) gives zeros.
+ * abs_out[R,C,k,k] (may be NULL): the sum of the |terms| of each output,
+ * |m| / S^2 * sum over the samples and their corners of |corner weight * value|,
+ * the denominator of the per-element parity rule. */
 typedef struct oracle_roi_desc {
   int64_t B, C, H, W, R, k, S;
   double spatial_scale, gamma;
 } oracle_roi_desc;
 int oracle_roi_pool(const oracle_roi_desc* d, const float* x, const float* rois, const float* offset,
-                    const float* mask, double* out, int threads);
+                    const float* mask, double* out, double* abs_out, int threads);
 /* Number of threads an oracle_forward call with this request would use. */
 int oracle_threads(int threads);
 

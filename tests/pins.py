@@ -514,17 +514,20 @@ def pin_p16_roi_pixel_bins(lib):
     # image coordinates at scale 0.5: bins [2j-1, 2j+1) map to pixel j
     rois = np.array([[0, -1, -1, 2 * k - 1, 2 * k - 1],
                      [1, -1 + 2 * 3, -1 + 2 * 2, 2 * k - 1 + 2 * 3, 2 * k - 1 + 2 * 2]], dtype=np.float32)
-    y = oracle.roi_pool(x, rois, k, 1, spatial_scale=0.5, lib_path=lib)
+    y, ya = oracle.roi_pool(x, rois, k, 1, spatial_scale=0.5, with_abs=True, lib_path=lib)
     _close(y[0], x[0, :, 0:k, 0:k], 1e-12, "pixel bins")
     _close(y[1], x[1, :, 2:2 + k, 3:3 + k], 1e-12, "pixel bins moved by (2, 3)")
+    # one term per output (the pixel itself): the sum of |terms| is |pixel|
+    _close(ya[0], np.abs(x[0, :, 0:k, 0:k]), 1e-12, "sum of |terms| of pixel bins")
     # offsets of n whole pixels: gamma * k * off = n with gamma 0.1, k 4 -> off = 2.5 n
     off = np.zeros((2, 2, k, k), dtype=np.float32)
     off[:, 0] = 2.5 * 1    # one row down
     off[:, 1] = 2.5 * -1   # one column left
-    y = oracle.roi_pool(x, rois, k, 1, spatial_scale=0.5, gamma=0.1, offset=off, lib_path=lib)
+    y, ya = oracle.roi_pool(x, rois, k, 1, spatial_scale=0.5, gamma=0.1, offset=off, with_abs=True, lib_path=lib)
     want0 = np.zeros((C, k, k))
     want0[:, :, 1:] = x[0, :, 1:k + 1, 0:k - 1]   # column -1 is outside: zero
     _close(y[0], want0, 1e-12, "whole-pixel bin offsets")
+    _close(ya[0], np.abs(want0), 1e-12, "sum of |terms| with whole-pixel bin offsets")
     _close(y[1], x[1, :, 3:3 + k, 2:2 + k], 1e-12, "whole-pixel bin offsets, moved RoI")
 
 
@@ -571,9 +574,16 @@ def pin_p18_roi_outside(lib):
     x = np.full((2, 2, 9, 9), 3.0, dtype=np.float32)
     rois = np.array([[0, 100, 100, 120, 130], [5, 1, 1, 6, 6], [-1, 1, 1, 6, 6], [1, 1, 1, 6, 7]], np.float32)
     m = rng.uniform(0.1, 1.0, (4, 2, 2)).astype(np.float32)
-    y = oracle.roi_pool(x, rois, 2, 2, mask=m, lib_path=lib)
+    y, ya = oracle.roi_pool(x, rois, 2, 2, mask=m, with_abs=True, lib_path=lib)
     assert np.all(y[:3] == 0.0), "RoIs outside the image or the batch must pool zeros"
+    assert np.all(ya[:3] == 0.0), "RoIs outside the image or the batch have no terms"
     _close(y[3], 3.0 * np.broadcast_to(m[3].astype(np.float64), (2, 2, 2)), 1e-12, "constant image")
+    # every term positive: the sum of |terms| is the output itself; with the image
+    # negated the output changes sign and the sum does not
+    _close(ya[3], y[3], 1e-12, "sum of |terms| of a positive image")
+    yn, yan = oracle.roi_pool(-x, rois, 2, 2, mask=m, with_abs=True, lib_path=lib)
+    _close(yn[3], -y[3], 1e-12, "negated image")
+    _close(yan[3], ya[3], 1e-12, "sum of |terms| of a negated image")
 
 
 ALL_PINS = [pin_p1_zero_offsets, pin_p2_integer_offsets, pin_p3_bilinear_field, pin_p4_all_outside,

@@ -309,3 +309,23 @@ def test_roi_pool_argument_checks(lib):
         assert f(ctypes.byref(d), fake, fake, None, None, fake, ws, n, None) == dcn.E_WORKSPACE
     assert dcn.dcn_roi_pool_workspace_bytes(dcn.RoiDesc(**{**good, "dtype": dcn.F32})) == 0
     assert dcn.dcn_roi_pool_workspace_bytes(dcn.RoiDesc(**{**good, "pooled_size": 17})) == 0
+
+
+def test_python_binding_checks_out_and_workspace(lib):
+    """A caller-supplied output or workspace is checked before any launch: shape, dtype,
+    device, contiguity and (workspace) byte size."""
+    import torch
+    dev = torch.device("cuda", 0)
+    shape = (2, 4, 5, 6)
+    with pytest.raises(ValueError, match="shape"):
+        dcn._check_out(torch.zeros(2, 4, 5, 7), shape, torch.float32, dev)
+    with pytest.raises(ValueError, match="bfloat16"):
+        dcn._check_out(torch.zeros(shape), shape, torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="cuda"):
+        dcn._check_out(torch.zeros(shape), shape, torch.float32, dev)
+    with pytest.raises(TypeError):
+        dcn._check_out(None, shape, torch.float32, dev)
+    with pytest.raises(ValueError, match="cuda"):
+        dcn._workspace(torch.zeros(64, dtype=torch.uint8), 16, dev)
+    with pytest.raises(TypeError):
+        dcn._workspace(12345, 16, dev)

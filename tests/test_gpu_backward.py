@@ -133,11 +133,11 @@ def test_backward_empty_problems(dtype):
 
 
 def test_backward_c4_layer_slices():
-    """The c4 layer's backward at full size, in the bench's launch configuration, on the
-    slices the oracle computes in seconds: the weight and bias gradients of the first and
-    last output channels (they depend on those channels of grad_out only) and the input
-    gradient of the first and last input channels (one offset group: they depend on those
-    channels of x and weight only)."""
+    """The c4 layer's backward at full size, in the bench's launch configuration: the
+    offset and mask gradients in full, and on the slices the oracle computes in seconds
+    the weight and bias gradients of the first and last output channels (they depend on
+    those channels of grad_out only) and the input gradient of the first and last input
+    channels (one offset group: they depend on those channels of x and weight only)."""
     from deformable_convolution_vision_amd.workloads import WORKLOADS
     w = WORKLOADS["c4_bwd"]
     inp = generate(w)
@@ -156,6 +156,9 @@ def test_backward_c4_layer_slices():
     refx = oracle.backward(inp["x"][:, csel].contiguous(), inp["offset"], inp["weight"][:, csel].contiguous(), gy,
                            w.stride, w.pad, w.dilation, mask=inp["mask"], want=("grad_x",))
     compare(gx[:, csel], refx["grad_x"], "bf16", "c4 grad_x planes")
-    # the offset and mask gradients sum over every channel: finite and not all zero
-    assert torch.isfinite(goff.float()).all() and torch.isfinite(gm.float()).all()
-    assert goff.float().abs().sum() > 0 and gm.float().abs().sum() > 0
+    # the offset and mask gradients in full (every pixel and kernel point; each sums
+    # over all input and output channels: about 5e9 multiply-adds in the oracle)
+    refo = oracle.backward(inp["x"], inp["offset"], inp["weight"], gy, w.stride, w.pad, w.dilation,
+                           mask=inp["mask"], want=("grad_offset", "grad_mask"))
+    compare(goff, refo["grad_offset"], "bf16", "c4 grad_offset")
+    compare(gm, refo["grad_mask"], "bf16", "c4 grad_mask")

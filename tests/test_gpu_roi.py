@@ -1,5 +1,11 @@
 """The HIP deformable RoI pooling (dcn_roi_pool through the C ABI) against the oracle,
-element by element, on seeded inputs."""
+element by element, on seeded inputs.
+
+Tolerance, per output: |got - ref| <= tol * sum|terms|, with tol 1e-4 (fp32) or 1e-2
+(bf16) and the sum of |terms| = |m| / S^2 times the sum of |corner weight * value| over
+the bin's samples; where that sum is 0 the output must be exactly 0."""
+
+import zlib
 
 import numpy as np
 import pytest
@@ -10,8 +16,19 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-# |got - ref| <= tol * max|x| (the output is a weighted mean of input values)
-TOL = {"f32": 1e-5, "bf16": 1e-2}
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def check(got, ref, ab, tol, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    zero = ab == 0
+    assert np.all(err[zero] == 0.0), f"{what}: {int(np.sum(err[zero] != 0))} outputs with no terms are not exact"
+    rel = err[~zero] / ab[~zero]
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= tol, f"{what}: max relative error {worst:.3e} > {tol:.0e}"
+    return worst
 
 CASES = [
     # name, B, C, H, W, R, k, S, scale, gamma, offset, mask
@@ -48,17 +65,15 @@ def make(B, C, H, W, R, k, S, scale, gamma, with_off, with_mask, dtype, seed):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_roi_pool_parity(case, dtype):
     name, B, C, H, W, R, k, S, scale, gamma, wo, wm = case
-    x, rois, off, m = make(B, C, H, W, R, k, S, scale, gamma, wo, wm, dtype, seed=hash(name) % 1000)
+    x, rois, off, m = make(B, C, H, W, R, k, S, scale, gamma, wo, wm, dtype, seed=zlib.crc32(name.encode()) % 1000)
     print(f"[gpu-test] roi {name} {dtype}", flush=True)
     got = dcn.deform_roi_pool(x.cuda(), rois.cuda(), None if off is None else off.cuda(),
                               None if m is None else m.cuda(), k, S, scale, gamma)
     torch.cuda.synchronize()
-    ref = oracle.roi_pool(x, rois, k, S, scale, gamma, off, m)
+    ref, ab = oracle.roi_pool(x, rois, k, S, scale, gamma, off, m, with_abs=True)
     got = got.float().cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(got))
-    err = np.abs(got - ref)
-    tol = TOL[dtype] * float(x.float().abs().max())
-    assert np.all(err <= tol), f"{name}/{dtype}: max error {err.max():.3e} > {tol:.3e}"
+    worst = check(got, ref, ab, TOL[dtype], f"{name}/{dtype}")
+    print(f"[gpu-test] max relative error {worst:.2e}", flush=True)
     assert np.all(got[0] == 0.0), "a RoI past the last image must pool zeros"
 
 
@@ -73,6 +88,6 @@ def test_roi_pool_empty_and_full_size():
     g = {k: v.cuda() for k, v in inp.items()}
     got = dcn.deform_roi_pool(g["x"], g["rois"], g["offset"], g["mask"], w.K, 2, 1.0 / 16, 0.1)
     torch.cuda.synchronize()
-    ref = oracle.roi_pool(inp["x"], inp["rois"], w.K, 2, 1.0 / 16, 0.1, inp["offset"], inp["mask"])
-    err = np.abs(got.float().cpu().numpy() - ref)
-    assert err.max() <= 1e-2 * float(inp["x"].float().abs().max())
+    ref, ab = oracle.roi_pool(inp["x"], inp["rois"], w.K, 2, 1.0 / 16, 0.1, inp["offset"], inp["mask"],
+                              with_abs=True)
+    check(got.float().cpu().numpy(), ref, ab, TOL["bf16"], "roi_c4")

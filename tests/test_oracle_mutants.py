@@ -78,6 +78,8 @@ MUTANTS = [
     ("roi_scale_not_on_x1", [("const double x1 = static_cast<double>(roi[1]) * d->spatial_scale,",
                               "const double x1 = static_cast<double>(roi[1]),")]),
     ("roi_mean_over_s", [("*y = m * acc / static_cast<double>(S * S);", "*y = m * acc / static_cast<double>(S);")]),
+    ("roi_abs_signed", [("if (abs_sum != nullptr) *abs_sum += std::fabs(t);", "if (abs_sum != nullptr) *abs_sum += t;")]),
+    ("roi_abs_without_mask", [("*ya = std::fabs(m) * acc_abs", "*ya = acc_abs")]),
     ("bwd_position_ignores_pad", [("static_cast<float>(oy * d->stride - d->pad + i * d->dilation) + dy;",
                                    "static_cast<float>(oy * d->stride + i * d->dilation) + dy;")]),
 ]
