@@ -20,14 +20,15 @@ import torch
 
 __all__ = ["Desc", "dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_stage",
            "dcn_forward_staged", "dcn_variant_name", "dcn_plan_describe", "dcn_status_str", "deform_conv2d",
-           "dcn_offset_mask_workspace_bytes", "dcn_offset_mask", "offset_mask",
+           "dcn_offset_mask_workspace_bytes", "dcn_offset_mask", "offset_mask", "dcn_forward_noalloc",
            "DcnError", "library_path", "load_library", "F32", "BF16"]
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdcn_hip.so")
 
 F32, BF16 = 0, 1
-OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
+OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_SCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 32 << 20   # DCN_NOALLOC_SCRATCH_BYTES of dcn.h
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 _EXPORTS = ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_stage", "dcn_forward_staged",
             "dcn_variant_name", "dcn_plan_describe", "dcn_status_str", "dcn_offset_mask_workspace_bytes",
@@ -81,6 +82,8 @@ def load_library() -> ctypes.CDLL:
     lib.dcn_workspace_bytes.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
     lib.dcn_forward.argtypes = [D, P, P, P, P, P, P, P, S, P]
     lib.dcn_forward_staged.argtypes = [D, P, P, P, P, P, P, P, S, P]
+    lib.dcn_forward_noalloc.argtypes = [D, P, P, P, P, P, P, P]
+    lib.dcn_forward_noalloc.restype = ctypes.c_int
     lib.dcn_stage.argtypes = [D, P, P, P, S, P]
     lib.dcn_variant_name.argtypes = [D]
     lib.dcn_variant_name.restype = ctypes.c_char_p
@@ -180,6 +183,16 @@ def dcn_forward_staged(desc: Desc, x, offset, mask, weight, bias, out, workspace
                                            workspace_bytes, _stream(stream))
     if rc != OK:
         raise DcnError(rc, "dcn_forward_staged")
+
+
+def dcn_forward_noalloc(desc: Desc, x, offset, mask, weight, bias, out, stream=None) -> None:
+    """Raw call of the entry point that allocates nothing (its workspace is a device
+    array of NOALLOC_SCRATCH_BYTES held by the library per GPU); tensors or device
+    addresses as dcn.h states."""
+    rc = load_library().dcn_forward_noalloc(ctypes.byref(desc), _ptr(x), _ptr(offset), _ptr(mask), _ptr(weight),
+                                            _ptr(bias), _ptr(out), _stream(stream))
+    if rc != OK:
+        raise DcnError(rc, "dcn_forward_noalloc")
 
 
 def describe(input, weight, stride=1, padding=0, dilation=1, offset=None) -> Desc:

@@ -547,6 +547,7 @@ extern "C" const char* dcn_status_str(int status) {
     case DCN_E_UNSUPPORTED: return "unsupported (dtype or size limit)";
     case DCN_E_WORKSPACE: return "workspace missing, too small or misaligned";
     case DCN_E_HIP: return "HIP kernel launch failed";
+    case DCN_E_SCRATCH: return "the problem needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -604,5 +605,54 @@ extern "C" int dcn_forward(const dcn_desc* desc, const void* x, const void* offs
     if (dcn::launch_stage(p.variant, s, stream) != hipSuccess) return DCN_E_HIP;
   }
   const FusedArgs a = fused_args(desc, p, x, offset, mask, weight, bias, out, workspace);
+  return launch_fused_plan(p, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
+}
+
+// ---- dcn_forward without a caller workspace: a file-scope device array serves as the
+// workspace.  In host code `scratch` names a host-side stand-in, never the device
+// array: its device address is looked up once per device with hipGetSymbolAddress
+// (that device current) and only that address is passed to kernels.
+namespace {
+
+__device__ __align__(256) unsigned char scratch[DCN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// the current device's address of `scratch`, looked up on the first call on that device
+int current_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return DCN_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DCN_E_HIP;
+    if (reinterpret_cast<uintptr_t>(p) % kAlign != 0) return DCN_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return DCN_OK;
+}
+
+}  // namespace
+
+extern "C" int dcn_forward_noalloc(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                                   const void* weight, const void* bias, void* out, hipStream_t stream) {
+  Plan p;
+  int rc = validate_call(desc, &p, offset, weight, out, x);
+  if (rc != DCN_OK) return rc;
+  if (p.empty) return DCN_OK;
+  if (p.ws_bytes > DCN_NOALLOC_SCRATCH_BYTES) return DCN_E_SCRATCH;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    rc = current_scratch(&ws);
+    if (rc != DCN_OK) return rc;
+  }
+  if (dcn::variant_info(p.variant).staged) {
+    const StageArgs s = stage_args(desc, p, x, weight, ws);
+    if (dcn::launch_stage(p.variant, s, stream) != hipSuccess) return DCN_E_HIP;
+  }
+  const FusedArgs a = fused_args(desc, p, x, offset, mask, weight, bias, out, ws);
   return launch_fused_plan(p, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
 }

@@ -37,10 +37,10 @@
  *    on the host before any HIP call; on an error nothing is launched and out
  *    is not written.  DCN_E_HIP reports a failed kernel launch (the launch's own
  *    return code).  No C++ exception crosses this interface.
- *  - Arithmetic: positions and bilinear weights in fp32; bf16 samples are
- *    interpolated in fp32 (the box kernel rounds the bilinear weights times the
- *    mask to bf16 first) and rounded to bf16 (nearest even) before the matrix
- *    product; products accumulate in fp32; out is rounded to dtype.  With at
+ *  - Arithmetic: positions and bilinear weights (times the mask) in fp32; bf16
+ *    samples are interpolated in fp32 from their exactly widened corners and
+ *    rounded to bf16 (nearest even) before the matrix product; products
+ *    accumulate in fp32; out is rounded to dtype.  With at
  *    most 4 input channels and K*K in {1, 4, 9} the column stays in fp32 and no
  *    workspace is needed (dcn_workspace_bytes returns 0).
  *  - Limits: every tensor (and the staged copy of x) has fewer than 2^31
@@ -75,7 +75,10 @@ enum dcn_status {
   DCN_E_ARG = -1,          /* NULL required pointer, a dimension out of range, Ho or Wo < 1 */
   DCN_E_UNSUPPORTED = -2,  /* dtype not built, or a tensor at or beyond 2^31 elements */
   DCN_E_WORKSPACE = -3,    /* workspace NULL or smaller than dcn_workspace_bytes() */
-  DCN_E_HIP = -4           /* a kernel launch failed */
+  DCN_E_HIP = -4,          /* a kernel launch failed (or, for dcn_forward_noalloc, the
+                              device's scratch array could not be located) */
+  DCN_E_SCRATCH = -5       /* dcn_forward_noalloc: the problem needs more scratch than
+                              DCN_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Problem descriptor.  B >= 0 and Cout >= 0 (0 means an empty output: the
@@ -130,6 +133,23 @@ int dcn_stage(const dcn_desc* desc, const void* x, const void* weight,
 int dcn_forward_staged(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
                        const void* weight, const void* bias, void* out,
                        const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the device array that dcn_forward_noalloc uses as its workspace. */
+#define DCN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* dcn_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments and
+ * result as dcn_forward without the workspace: the staged copy of x and the repacked
+ * weight go to a file-scope device array of DCN_NOALLOC_SCRATCH_BYTES (32 MiB) that
+ * each GPU holds from the first call on it until the process ends (located once per
+ * device with hipGetSymbolAddress; DCN_E_HIP if that fails).  A descriptor whose
+ * dcn_workspace_bytes exceeds that size returns DCN_E_SCRATCH before any launch.
+ * Calls no allocating routine.  Every call on one GPU shares that GPU's array and the
+ * staging launch of each call writes every byte its fused launch reads, so nothing is
+ * carried between calls; calls that overlap in time on one GPU (different streams, or
+ * host threads with no ordering) race on the array and must not be issued. */
+int dcn_forward_noalloc(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                        const void* weight, const void* bias, void* out, hipStream_t stream);
 
 /* Name of the kernel variant dcn_forward runs for this descriptor (static
  * string; "invalid" if the descriptor is rejected). */

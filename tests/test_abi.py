@@ -227,7 +227,7 @@ def test_small_reductions_take_the_direct_kernel_without_workspace(lib):
 
 
 def test_status_strings(lib):
-    for s in (dcn.OK, dcn.E_ARG, dcn.E_UNSUPPORTED, dcn.E_WORKSPACE, dcn.E_HIP):
+    for s in (dcn.OK, dcn.E_ARG, dcn.E_UNSUPPORTED, dcn.E_WORKSPACE, dcn.E_HIP, dcn.E_SCRATCH):
         assert dcn.dcn_status_str(s) != "unknown status"
     assert dcn.dcn_status_str(-99) == "unknown status"
 
@@ -329,3 +329,18 @@ def test_python_binding_checks_out_and_workspace(lib):
         dcn._workspace(torch.zeros(64, dtype=torch.uint8), 16, dev)
     with pytest.raises(TypeError):
         dcn._workspace(12345, 16, dev)
+
+
+def test_noalloc_checks_before_any_launch(lib):
+    """dcn_forward_noalloc validates like dcn_forward and rejects a problem whose
+    workspace exceeds its scratch array, all on the host (no device is touched)."""
+    desc = dcn.make_desc(2, 8, 10, 12, 4, 3, 1, 1, 1, dcn.BF16)
+    with pytest.raises(dcn.DcnError) as e:
+        dcn.dcn_forward_noalloc(desc, None, None, None, None, None, None, stream=0)
+    assert e.value.status == dcn.E_ARG
+    big = dcn.make_desc(2, 512, 100, 168, 64, 3, 1, 1, 1, dcn.BF16)
+    assert dcn.dcn_workspace_bytes(big) > dcn.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(dcn.DcnError) as e:
+        dcn.dcn_forward_noalloc(big, 16, 16, None, 16, None, 16, stream=0)   # never dereferenced
+    assert e.value.status == dcn.E_SCRATCH
+    assert "scratch" in dcn.dcn_status_str(dcn.E_SCRATCH)
