@@ -36,6 +36,11 @@ class _RoiDesc(ctypes.Structure):
                [("spatial_scale", ctypes.c_double), ("gamma", ctypes.c_double)]
 
 
+class _PsRoiDesc(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in ("B", "C", "H", "W", "R", "k", "S", "G")] + \
+               [("spatial_scale", ctypes.c_double), ("gamma", ctypes.c_double)]
+
+
 def build(out_path: str = LIB, extra_flags: tuple[str, ...] = (), src: str = SRC) -> str:
     """Compile the oracle with g++ (OpenMP, IEEE arithmetic: no fast-math)."""
     tmp = out_path + ".tmp"
@@ -70,6 +75,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.oracle_backward.restype = ctypes.c_int
     lib.oracle_roi_pool.argtypes = [ctypes.POINTER(_RoiDesc), P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_roi_pool.restype = ctypes.c_int
+    lib.oracle_ps_roi_pool.argtypes = [ctypes.POINTER(_PsRoiDesc), P, P, P, P, P, P, ctypes.c_int]
+    lib.oracle_ps_roi_pool.restype = ctypes.c_int
     lib.oracle_threads.argtypes = [ctypes.c_int]
     lib.oracle_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
@@ -215,6 +222,41 @@ def roi_pool(x, rois, k, S, spatial_scale=1.0, gamma=0.1, offset=None, mask=None
                              _ptr(ab), threads)
     if rc != 0:
         raise ValueError("oracle_roi_pool rejected its arguments")
+    return (out, ab) if with_abs else out
+
+
+def ps_roi_pool(x, rois, k, S, spatial_scale=1.0, gamma=0.1, offset=None, mask=None, threads=0,
+                with_abs=False, lib_path: str = LIB):
+    """Deformable position-sensitive RoI pooling (definition and readings in
+    dcn_oracle.h): x [B, C*k*k, H, W] (k*k score maps per output channel; bin (i, j) of
+    output channel c pools input channel (c*k + i)*k + j), rois [R,5], offset [R,2G,k,k]
+    (G groups of output channels, each with its own row/column offsets) or None, mask
+    [R,k,k] or None.  Returns float64 [R,C,k,k], and with ``with_abs`` the sum of |terms|."""
+    lib = load(lib_path)
+    x, rois, offset, mask = map(_f32, (x, rois, offset, mask))
+    B, Cin, H, W = x.shape
+    if Cin % (k * k) != 0:
+        raise ValueError("x must have C*k*k channels")
+    C = Cin // (k * k)
+    R = rois.shape[0]
+    if rois.shape != (R, 5):
+        raise ValueError("rois must be [R, 5]")
+    G = 1
+    if offset is not None:
+        if offset.ndim != 4 or offset.shape[0] != R or offset.shape[1] % 2 or offset.shape[2:] != (k, k):
+            raise ValueError(f"offset must be [R, 2G, {k}, {k}]")
+        G = offset.shape[1] // 2
+        if C % G:
+            raise ValueError("the output channels must split into the offset groups")
+    if mask is not None and mask.shape != (R, k, k):
+        raise ValueError(f"mask must be {(R, k, k)}")
+    d = _PsRoiDesc(B, C, H, W, R, k, S, G, float(spatial_scale), float(gamma))
+    out = np.empty((R, C, k, k), dtype=np.float64)
+    ab = np.empty_like(out) if with_abs else None
+    rc = lib.oracle_ps_roi_pool(ctypes.byref(d), _ptr(x), _ptr(rois), _ptr(offset), _ptr(mask), _ptr(out),
+                                _ptr(ab), threads)
+    if rc != 0:
+        raise ValueError("oracle_ps_roi_pool rejected its arguments")
     return (out, ab) if with_abs else out
 
 

@@ -147,6 +147,29 @@ typedef struct oracle_roi_desc {
 } oracle_roi_desc;
 int oracle_roi_pool(const oracle_roi_desc* d, const float* x, const float* rois, const float* offset,
                     const float* mask, double* out, double* abs_out, int threads);
+/* Deformable position-sensitive RoI pooling (the csdn.net tags page "可变形卷积：
+ * Deformable ConvNets", part "Deformable Convolutional Networks", section Deformable
+ * RoI Pooling: a learnable offset per bin combined with ordinary position-sensitive RoI
+ * pooling).  The pages do not spell out position-sensitive pooling; the reading taken
+ * is the usual one: the input holds k*k score maps per output channel, and bin (i, j)
+ * of output channel c pools only its own map, input channel (c*k + i)*k + j.  Bins,
+ * sub-cell samples, offsets (normalised by the RoI size and scaled by gamma) and the
+ * modulation scalar are exactly those of oracle_roi_pool.  Offsets may be given per
+ * group of output channels ("per class"): the C output channels split into G
+ * consecutive groups of C/G, group g using offset channels 2g (rows) and 2g+1
+ * (columns); G = 1 shares one offset per bin.
+ *
+ *   y[r,c,i,j] = m[r,i,j] / S^2 * sum_{u,v < S} S(X[b_r, (c*k + i)*k + j], py, px)
+ *     py, px as for oracle_roi_pool with offset[r, 2g + {0, 1}, i, j], g = c / (C/G)
+ *
+ * x[B, C*k*k, H, W], rois[R,5], offset[R, 2G, k, k] or NULL, mask[R,k,k] or NULL,
+ * out[R,C,k,k] and abs_out[R,C,k,k] (may be NULL; as for oracle_roi_pool) doubles. */
+typedef struct oracle_ps_roi_desc {
+  int64_t B, C, H, W, R, k, S, G;   /* C output channels; x has C*k*k; G offset groups (0 means 1) */
+  double spatial_scale, gamma;
+} oracle_ps_roi_desc;
+int oracle_ps_roi_pool(const oracle_ps_roi_desc* d, const float* x, const float* rois, const float* offset,
+                       const float* mask, double* out, double* abs_out, int threads);
 /* Number of threads an oracle_forward call with this request would use. */
 int oracle_threads(int threads);
 

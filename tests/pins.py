@@ -31,6 +31,9 @@ What each pin reduces to (no pin restates the oracle's own formula):
   p16 RoI pooling, pixel bins   -> the input pixels (moved RoI, whole-pixel offsets, batch image)
   p17 RoI pooling, linear field -> the field at the shifted bin centre times the mask, any S
   p18 RoI pooling, outside      -> zeros; a constant image gives the constant times the mask
+  p19 PS RoI pooling, constant score maps -> bin (i, j) of channel c reads map (c*k+i)*k+j only
+  p20 PS RoI pooling, replicated maps     -> plain deformable RoI pooling (p16-p18), per offset group
+  p21 PS RoI pooling, pixel bins          -> the score maps' pixels; past the batch -> zeros
   golden                      -> hand-worked examples in tests/golden/
 """
 
@@ -586,9 +589,80 @@ def pin_p18_roi_outside(lib):
     _close(yan[3], ya[3], 1e-12, "sum of |terms| of a negated image")
 
 
+def pin_p19_ps_roi_score_map_per_bin(lib):
+    """Position-sensitive pooling: bin (i, j) of output channel c reads only score map
+    (c*k + i)*k + j.  Every score map a distinct constant (per batch image) and every
+    sample inside the image: each output is m times that constant (the bilinear weights
+    of an inside sample sum to 1), for one and for two offset groups."""
+    rng = np.random.default_rng(1901)
+    B, C, H, W, k = 2, 3, 20, 24, 3
+    vals = rng.permutation(B * C * k * k).astype(np.float32).reshape(B, C * k * k) / 8.0 + 0.125
+    x = np.broadcast_to(vals[:, :, None, None], (B, C * k * k, H, W)).copy()
+    R = 5
+    x1 = rng.uniform(3, 8, R)
+    y1 = rng.uniform(3, 7, R)
+    rois = np.stack([rng.integers(0, B, R), x1, y1, x1 + rng.uniform(4, 10, R), y1 + rng.uniform(4, 9, R)],
+                    1).astype(np.float32)
+    m = rng.uniform(0.2, 1.0, (R, k, k)).astype(np.float32)
+    for G in (1, 3):
+        off = rng.uniform(-0.2, 0.2, (R, 2 * G, k, k)).astype(np.float32)
+        y = oracle.ps_roi_pool(x, rois, k, 2, 1.0, 0.1, off, m, lib_path=lib)
+        for r in range(R):
+            b = int(rois[r, 0])
+            want = vals[b].reshape(C, k, k).astype(np.float64) * m[r][None].astype(np.float64)
+            _close(y[r], want, 1e-12, f"score map per bin, G={G}, RoI {r}")
+
+
+def pin_p20_ps_roi_replicated_maps(lib):
+    """With the k*k score maps of each output channel all equal to one plane z[c], the
+    position-sensitive pooling is the plain deformable RoI pooling of z (pinned by
+    p16-p18); with G offset groups, group g equals the plain pooling of its channel
+    slice of z with offset channels 2g, 2g+1."""
+    rng = np.random.default_rng(2001)
+    B, C, H, W, k, S = 2, 4, 17, 21, 3, 2
+    z = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    x = np.repeat(z, k * k, axis=1)   # channel (c*k + i)*k + j = z[c]
+    R = 6
+    x1 = rng.uniform(-4, 14, R)
+    y1 = rng.uniform(-4, 10, R)
+    rois = np.stack([rng.integers(0, B, R), x1, y1, x1 + rng.uniform(2, 12, R), y1 + rng.uniform(2, 10, R)],
+                    1).astype(np.float32)
+    m = rng.uniform(0.1, 1.0, (R, k, k)).astype(np.float32)
+    for G in (1, 2):
+        off = rng.uniform(-1.0, 1.0, (R, 2 * G, k, k)).astype(np.float32)
+        y = oracle.ps_roi_pool(x, rois, k, S, 0.9, 0.2, off, m, lib_path=lib)
+        Cg = C // G
+        for g in range(G):
+            want = oracle.roi_pool(z[:, g * Cg:(g + 1) * Cg], rois, k, S, 0.9, 0.2,
+                                   np.ascontiguousarray(off[:, 2 * g:2 * g + 2]), m, lib_path=lib)
+            _close(y[:, g * Cg:(g + 1) * Cg], want, 1e-12, f"replicated score maps, group {g} of {G}")
+
+
+def pin_p21_ps_roi_pixel_bins_and_outside(lib):
+    """One sample per bin on a RoI whose bins are single pixels: output (r, c, i, j) is
+    pixel (y0 + i, x0 + j) of score map (c*k + i)*k + j; a RoI past the last batch image
+    pools zeros (sum of |terms| zero too)."""
+    rng = np.random.default_rng(2101)
+    B, C, H, W, k = 2, 2, 9, 10, 3
+    x = rng.standard_normal((B, C * k * k, H, W)).astype(np.float32)
+    # scale 0.5: image coordinates [2j-1, 2j+1) map to pixel j
+    rois = np.array([[1, -1 + 2 * 4, -1 + 2 * 2, 2 * k - 1 + 2 * 4, 2 * k - 1 + 2 * 2],
+                     [2, 0, 0, 4, 4]], dtype=np.float32)
+    y, ya = oracle.ps_roi_pool(x, rois, k, 1, 0.5, 0.1, None, None, with_abs=True, lib_path=lib)
+    want = np.empty((C, k, k))
+    for c in range(C):
+        for i in range(k):
+            for j in range(k):
+                want[c, i, j] = x[1, (c * k + i) * k + j, 2 + i, 4 + j]
+    _close(y[0], want, 1e-12, "pixel bins of the score maps")
+    _close(ya[0], np.abs(want), 1e-12, "sum of |terms| of pixel bins")
+    assert np.all(y[1] == 0.0) and np.all(ya[1] == 0.0), "a RoI past the last image pools zeros"
+
+
 ALL_PINS = [pin_p1_zero_offsets, pin_p2_integer_offsets, pin_p3_bilinear_field, pin_p4_all_outside,
             pin_p5_linear_in_mask, pin_p6_mask_absent, pin_p7_half_offsets, pin_p8_constant_input,
             pin_p9_grid_sample, pin_p10_nonfinite_offsets, pin_p11_offset_groups, pin_p12_offset_mask_branch,
             pin_golden, pin_p13_backward_directional, pin_p14_backward_zero_offsets,
             pin_p15_backward_all_outside, pin_p16_roi_pixel_bins, pin_p17_roi_linear_field,
-            pin_p18_roi_outside]
+            pin_p18_roi_outside, pin_p19_ps_roi_score_map_per_bin, pin_p20_ps_roi_replicated_maps,
+            pin_p21_ps_roi_pixel_bins_and_outside]

@@ -80,6 +80,13 @@ MUTANTS = [
     ("roi_mean_over_s", [("*y = m * acc / static_cast<double>(S * S);", "*y = m * acc / static_cast<double>(S);")]),
     ("roi_abs_signed", [("if (abs_sum != nullptr) *abs_sum += std::fabs(t);", "if (abs_sum != nullptr) *abs_sum += t;")]),
     ("roi_abs_without_mask", [("*ya = std::fabs(m) * acc_abs", "*ya = acc_abs")]),
+    # position-sensitive RoI pooling
+    ("ps_bins_transposed_in_map", [("const int64_t ch = (c * k + i) * k + j;", "const int64_t ch = (c * k + j) * k + i;")]),
+    ("ps_bin_major_maps", [("const int64_t ch = (c * k + i) * k + j;", "const int64_t ch = (i * k + j) * C + c;")]),
+    ("ps_offset_group_ignored", [("const int64_t r = rc / C, c = rc % C, g = c / Cg;",
+                                  "const int64_t r = rc / C, c = rc % C, g = 0 * Cg;")]),
+    ("ps_offset_group_by_modulo", [("const int64_t r = rc / C, c = rc % C, g = c / Cg;",
+                                    "const int64_t r = rc / C, c = rc % C, g = c % G;")]),
     ("bwd_position_ignores_pad", [("static_cast<float>(oy * d->stride - d->pad + i * d->dilation) + dy;",
                                    "static_cast<float>(oy * d->stride + i * d->dilation) + dy;")]),
 ]
