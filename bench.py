@@ -332,10 +332,11 @@ def bench_backward(w, steps: int, warmup: int):
 
 
 def bench_roi(w, steps: int, warmup: int):
-    """Deformable RoI pooling (dcn_roi_pool) on the workload's feature map: 256 RoIs per
-    image of an 800 x 1344 image at spatial scale 1/16, k x k bins (k = the workload's K),
-    2 x 2 samples per bin, per-bin offsets and mask.  One step is one call (for bf16: the
-    channels-last staging launch and the pooling launch).  value is the
+    """Deformable RoI pooling (dcn_roi_pool), or its position-sensitive form
+    (dcn_ps_roi_pool), on the workload's feature map: 256 RoIs per image of an 800 x 1344
+    image at spatial scale 1/16, k x k bins (k = the workload's K), 2 x 2 samples per bin,
+    per-bin offsets and mask.  One step is one call (plain bf16 pooling: the channels-last
+    staging launch and the pooling launch; position-sensitive: one launch).  value is the
     effective bandwidth of its algorithmic bytes (x, rois, offsets and mask read once, the
     output written once); the timed region has events at its ends only."""
     import numpy as np
@@ -345,24 +346,33 @@ def bench_roi(w, steps: int, warmup: int):
     import oracle
     from deformable_convolution_vision_amd.workloads import roi_inputs
 
+    ps = w.op == "ps_roi_pool"
     k, S, scale, gamma, per_img = w.K, 2, 1.0 / 16, 0.1, 256
     host = roi_inputs(w, per_img, k, (800, 1344))
     g = {key: v.cuda() for key, v in host.items()}
     R = g["rois"].shape[0]
-    desc = dcn.RoiDesc(w.B, w.Cin, w.H, w.W, R, k, S, scale, gamma, dcn.BF16 if w.dtype == "bf16" else dcn.F32, 0)
-    out = torch.empty((R, w.Cin, k, k), dtype=g["x"].dtype, device="cuda")
-    nb = dcn.dcn_roi_pool_workspace_bytes(desc)
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    C_out = w.Cout if ps else w.Cin
+    dt = dcn.BF16 if w.dtype == "bf16" else dcn.F32
+    out = torch.empty((R, C_out, k, k), dtype=g["x"].dtype, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    if ps:
+        desc = dcn.PsRoiDesc(w.B, C_out, w.H, w.W, R, k, S, 1, scale, gamma, dt, 0)
 
-    def step():
-        dcn.dcn_roi_pool(desc, g["x"], g["rois"], g["offset"], g["mask"], out, ws if nb else None, nb, stream)
+        def step():
+            dcn.dcn_ps_roi_pool(desc, g["x"], g["rois"], g["offset"], g["mask"], out, stream)
+    else:
+        desc = dcn.RoiDesc(w.B, w.Cin, w.H, w.W, R, k, S, scale, gamma, dt, 0)
+        nb = dcn.dcn_roi_pool_workspace_bytes(desc)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+
+        def step():
+            dcn.dcn_roi_pool(desc, g["x"], g["rois"], g["offset"], g["mask"], out, ws if nb else None, nb, stream)
 
     step()
     torch.cuda.synchronize()
-    ref, ab = oracle.roi_pool(host["x"], host["rois"], k, S, scale, gamma, host["offset"], host["mask"],
-                              with_abs=True)
+    pool = oracle.ps_roi_pool if ps else oracle.roi_pool
+    ref, ab = pool(host["x"], host["rois"], k, S, scale, gamma, host["offset"], host["mask"], with_abs=True)
     tol = 1e-2 if w.dtype == "bf16" else 1e-4
     err = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
     if np.any(err[ab == 0] != 0):
@@ -385,21 +395,27 @@ def bench_roi(w, steps: int, warmup: int):
     ev.close()
     ms_per_step = total_ms / steps
     es = 2 if w.dtype == "bf16" else 4
-    abytes = es * (w.B * w.Cin * w.H * w.W + R * 2 * k * k + R * k * k + R * w.Cin * k * k) + 4 * 5 * R
+    abytes = es * (w.B * w.Cin * w.H * w.W + R * 2 * k * k + R * k * k + R * C_out * k * k) + 4 * 5 * R
     gbps = abytes / (ms_per_step * 1e-3) / 1e9
+    if ps:
+        what = (f"{w.name}: deformable position-sensitive RoI pooling of {w.Cin} score maps ({C_out} classes x "
+                f"{k}x{k} bins) [{w.B},{w.Cin},{w.H},{w.W}], {R} RoIs ({per_img} per image, sides 32-512 px of "
+                f"800x1344, scale 1/16), {S}x{S} samples, one offset per bin, mask")
+        plan, kname = "dcn_ps_roi_pool: one pooling launch", "roi_pool_kernel (position-sensitive)"
+    else:
+        what = (f"{w.name}: deformable RoI pooling of x [{w.B},{w.Cin},{w.H},{w.W}], {R} RoIs ({per_img} per image, "
+                f"sides 32-512 px of 800x1344, scale 1/16), {k}x{k} bins, {S}x{S} samples, offsets and mask")
+        plan, kname = "dcn_roi_pool: channels-last staging launch + pooling launch", "roi_pool_cl_kernel"
     return {
         "metric": "deform_conv2d fwd effective TFLOP/s + GB/s (c4 stride-2 bf16), % of roofline",
         "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded; shapes and value distributions of the workload)",
-        "config": {"workload": f"{w.name}: deformable RoI pooling of x [{w.B},{w.Cin},{w.H},{w.W}], {R} RoIs "
-                               f"({per_img} per image, sides 32-512 px of 800x1344, scale 1/16), {k}x{k} bins, "
-                               f"{S}x{S} samples, offsets and mask",
-                   "variant": "roi_pool", "plan": "dcn_roi_pool: channels-last staging launch + pooling launch"},
+        "config": {"workload": what, "variant": w.op, "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK["hbm"], "unit": "GB/s",
                      "frac": round(gbps / PEAK["hbm"], 5), "traffic": None,
-                     "kernel": "roi_pool_kernel", "kernel_sha": kernel_hash(),
-                     "per_launch": {"algorithmic_bytes": abytes, "outputs": R * w.Cin * k * k}},
+                     "kernel": kname, "kernel_sha": kernel_hash(),
+                     "per_launch": {"algorithmic_bytes": abytes, "outputs": R * C_out * k * k}},
         "kernels_us": {"call_mean": round(ms_per_step * 1e3, 3)},
         "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
         "parity_max_rel_err_sampled": max_rel,
@@ -420,7 +436,7 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
         return bench_offset_mask(w, steps, warmup)
     if w.op == "backward":
         return bench_backward(w, steps, warmup)
-    if w.op == "roi_pool":
+    if w.op in ("roi_pool", "ps_roi_pool"):
         return bench_roi(w, steps, warmup)
     host = generate(w)
     g = {k: (None if v is None else v.cuda()) for k, v in host.items()}

@@ -60,6 +60,14 @@ class RoiDesc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class PsRoiDesc(ctypes.Structure):
+    """Mirror of ``dcn_ps_roi_desc``."""
+    _fields_ = [("batch", ctypes.c_int64), ("out_channels", ctypes.c_int64), ("height", ctypes.c_int64),
+                ("width", ctypes.c_int64), ("num_rois", ctypes.c_int64), ("pooled_size", ctypes.c_int64),
+                ("samples", ctypes.c_int64), ("offset_groups", ctypes.c_int64), ("spatial_scale", ctypes.c_float),
+                ("gamma", ctypes.c_float), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -103,6 +111,8 @@ def load_library() -> ctypes.CDLL:
     lib.dcn_roi_pool.restype = ctypes.c_int
     lib.dcn_roi_pool_workspace_bytes.argtypes = [ctypes.POINTER(RoiDesc), ctypes.POINTER(ctypes.c_size_t)]
     lib.dcn_roi_pool_workspace_bytes.restype = ctypes.c_int
+    lib.dcn_ps_roi_pool.argtypes = [ctypes.POINTER(PsRoiDesc), P, P, P, P, P, P]
+    lib.dcn_ps_roi_pool.restype = ctypes.c_int
     for name in ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_forward_staged", "dcn_stage"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -428,4 +438,50 @@ def deform_roi_pool(input, rois, offset=None, mask=None, output_size=7, sampling
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=input.device) if nbytes else None
     with torch.cuda.device(input.device):
         dcn_roi_pool(desc, input, rois, offset, mask, out, ws, nbytes)
+    return out
+
+
+def dcn_ps_roi_pool(desc: PsRoiDesc, x, rois, offset, mask, out, stream=None) -> None:
+    """Raw call: tensors (or integer device addresses) laid out as dcn.h states."""
+    rc = load_library().dcn_ps_roi_pool(ctypes.byref(desc), _ptr(x), _ptr(rois), _ptr(offset), _ptr(mask), _ptr(out),
+                                        _stream(stream))
+    if rc != OK:
+        raise DcnError(rc, "dcn_ps_roi_pool")
+
+
+def deform_ps_roi_pool(input, rois, offset=None, mask=None, output_size=7, sampling_ratio=2, spatial_scale=1.0,
+                       gamma=0.1):
+    """Deformable position-sensitive RoI pooling on the GPU: input [B, C*k*k, H, W] (k*k
+    score maps per output channel); rois [R,5] float32; offset [R,2G,k,k] (G groups of
+    output channels) or None; mask [R,k,k] or None.  Returns [R,C,k,k]."""
+    if input.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {input.dtype}; use float32 or bfloat16")
+    k = int(output_size)
+    B, Cin, H, W = input.shape
+    if Cin % (k * k) != 0:
+        raise ValueError(f"input must have C*k*k channels (k = {k}), got {Cin}")
+    C = Cin // (k * k)
+    R = rois.shape[0]
+    if rois.dtype != torch.float32 or tuple(rois.shape) != (R, 5):
+        raise ValueError("rois must be a float32 [R, 5] tensor")
+    G = 1
+    if offset is not None:
+        if offset.dim() != 4 or offset.shape[0] != R or offset.shape[1] % 2 or tuple(offset.shape[2:]) != (k, k):
+            raise ValueError(f"offset must be [R, 2G, {k}, {k}]")
+        G = offset.shape[1] // 2
+        if C % G != 0:
+            raise ValueError(f"{C} output channels do not split into {G} offset groups")
+    for name, t in (("offset", offset), ("mask", mask)):
+        if t is not None and t.dtype != input.dtype:
+            raise ValueError(f"{name} must have the input's dtype")
+    if mask is not None and tuple(mask.shape) != (R, k, k):
+        raise ValueError(f"mask must be {(R, k, k)}")
+    for t in (input, rois, offset, mask):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.device != input.device):
+            raise ValueError("tensors must be contiguous and on the input's GPU")
+    desc = PsRoiDesc(B, C, H, W, R, k, int(sampling_ratio), G, float(spatial_scale), float(gamma),
+                     _DTYPES[input.dtype], 0)
+    out = torch.empty((R, C, k, k), dtype=input.dtype, device=input.device)
+    with torch.cuda.device(input.device):
+        dcn_ps_roi_pool(desc, input, rois, offset, mask, out)
     return out

@@ -83,13 +83,15 @@ __device__ __forceinline__ RoiSample roi_sample(const RoiGeom<P>& g, int i, int 
 }
 
 struct RoiArgs {
-  const void* x;        // [B][C][H][W]
+  const void* x;        // [B][C][H][W]; position-sensitive: [B][C*k*k][H][W]
   const float* rois;    // [R][5]: batch index, x1, y1, x2, y2
-  const void* offset;   // [R][2][k][k] or null
+  const void* offset;   // [R][2G][k][k] or null
   const void* mask;     // [R][k][k] or null
   void* out;            // [R][C][k][k]
   int B, C, H, W, R, k, S;
   float scale, gamma;
+  int ps;               // 1: bin (i, j) of output channel c pools score map (c*k + i)*k + j
+  int G;                // offset groups of output channels (1 for plain pooling)
 };
 
 template <typename T>
@@ -101,6 +103,10 @@ __global__ __launch_bounds__(kRT) void roi_pool_kernel(RoiArgs a) {
   const int j = static_cast<int>(e % a.k), i = static_cast<int>((e / a.k) % a.k);
   const long long rc = e / kk;
   const int c = static_cast<int>(rc % a.C), r = static_cast<int>(rc / a.C);
+  // the plane this output pools: channel c, or (position-sensitive) the bin's own score map
+  const int cin = a.ps ? (c * a.k + i) * a.k + j : c;
+  const int nin = a.ps ? a.C * a.k * a.k : a.C;
+  const int g = c / (a.C / a.G);   // offset group
   const float* roi = a.rois + static_cast<size_t>(r) * 5;
   const float bi = roi[0];
   T* out = static_cast<T*>(a.out);
@@ -122,11 +128,11 @@ __global__ __launch_bounds__(kRT) void roi_pool_kernel(RoiArgs a) {
   float m = 1.f;
   if (a.offset != nullptr) {
     const T* off = static_cast<const T*>(a.offset);
-    geo.dy = a.gamma * geo.h * ld(off, ((static_cast<size_t>(r) * 2 + 0) * a.k + i) * a.k + j);
-    geo.dx = a.gamma * geo.w * ld(off, ((static_cast<size_t>(r) * 2 + 1) * a.k + i) * a.k + j);
+    geo.dy = a.gamma * geo.h * ld(off, ((static_cast<size_t>(r) * 2 * a.G + 2 * g) * a.k + i) * a.k + j);
+    geo.dx = a.gamma * geo.w * ld(off, ((static_cast<size_t>(r) * 2 * a.G + 2 * g + 1) * a.k + i) * a.k + j);
   }
   if (a.mask != nullptr) m = ld(static_cast<const T*>(a.mask), (static_cast<size_t>(r) * a.k + i) * a.k + j);
-  const T* plane = static_cast<const T*>(a.x) + (static_cast<size_t>(b) * a.C + c) * a.H * a.W;
+  const T* plane = static_cast<const T*>(a.x) + (static_cast<size_t>(b) * nin + cin) * a.H * a.W;
   const float inv = 1.f / static_cast<float>(a.S);
   float acc = 0.f;
   for (int u = 0; u < a.S; ++u) {
@@ -287,6 +293,8 @@ extern "C" int dcn_roi_pool(const dcn_roi_desc* d, const void* x, const float* r
   a.S = static_cast<int>(d->samples);
   a.scale = d->spatial_scale;
   a.gamma = d->gamma;
+  a.ps = 0;
+  a.G = 1;
   void* args[] = {&a};
   if (roi_staged(d)) {
     // the channels-last copy, with the forward's staging kernel (no weight to repack)
@@ -314,6 +322,61 @@ extern "C" int dcn_roi_pool(const dcn_roi_desc* d, const void* x, const float* r
                ? DCN_OK
                : DCN_E_HIP;
   }
+  const long long n = static_cast<long long>(a.R) * a.C * a.k * a.k;
+  const void* fn = d->dtype == DCN_BF16 ? reinterpret_cast<const void*>(&dcn::roi_pool_kernel<uint16_t>)
+                                        : reinterpret_cast<const void*>(&dcn::roi_pool_kernel<float>);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>((n + dcn::kRT - 1) / dcn::kRT)), dim3(dcn::kRT), args, 0,
+                         stream) == hipSuccess
+             ? DCN_OK
+             : DCN_E_HIP;
+}
+
+// ---- deformable position-sensitive RoI pooling: the one-thread-per-output kernel with
+// the bin's own score map as its plane (no workspace)
+namespace {
+
+int ps_roi_check(const dcn_ps_roi_desc* d) {
+  if (d == nullptr) return DCN_E_ARG;
+  const int64_t G = d->offset_groups > 1 ? d->offset_groups : 1;
+  if (d->batch < 1 || d->out_channels < 1 || d->height < 1 || d->width < 1 || d->num_rois < 0 ||
+      d->pooled_size < 1 || d->samples < 1 || d->pooled_size > 1024 || d->samples > 64 || d->offset_groups < 0 ||
+      d->out_channels % G != 0 || !std::isfinite(d->spatial_scale) || !std::isfinite(d->gamma))
+    return DCN_E_ARG;
+  if (d->dtype != DCN_F32 && d->dtype != DCN_BF16) return DCN_E_UNSUPPORTED;
+  const double lim = 2147483647.0, kk = static_cast<double>(d->pooled_size) * d->pooled_size;
+  if (static_cast<double>(d->batch) * d->out_channels * kk * d->height * d->width > lim ||
+      static_cast<double>(d->num_rois) * d->out_channels * kk > lim ||
+      static_cast<double>(d->num_rois) * 2 * G * kk > lim || static_cast<double>(d->out_channels) * kk > lim)
+    return DCN_E_UNSUPPORTED;
+  return DCN_OK;
+}
+
+}  // namespace
+
+extern "C" int dcn_ps_roi_pool(const dcn_ps_roi_desc* d, const void* x, const float* rois, const void* offset,
+                               const void* mask, void* out, hipStream_t stream) {
+  const int rc = ps_roi_check(d);
+  if (rc != DCN_OK) return rc;
+  if (d->num_rois == 0) return DCN_OK;
+  if (x == nullptr || rois == nullptr || out == nullptr) return DCN_E_ARG;
+  dcn::RoiArgs a{};
+  a.x = x;
+  a.rois = rois;
+  a.offset = offset;
+  a.mask = mask;
+  a.out = out;
+  a.B = static_cast<int>(d->batch);
+  a.C = static_cast<int>(d->out_channels);
+  a.H = static_cast<int>(d->height);
+  a.W = static_cast<int>(d->width);
+  a.R = static_cast<int>(d->num_rois);
+  a.k = static_cast<int>(d->pooled_size);
+  a.S = static_cast<int>(d->samples);
+  a.scale = d->spatial_scale;
+  a.gamma = d->gamma;
+  a.ps = 1;
+  a.G = d->offset_groups > 1 ? d->offset_groups : 1;
+  void* args[] = {&a};
   const long long n = static_cast<long long>(a.R) * a.C * a.k * a.k;
   const void* fn = d->dtype == DCN_BF16 ? reinterpret_cast<const void*>(&dcn::roi_pool_kernel<uint16_t>)
                                         : reinterpret_cast<const void*>(&dcn::roi_pool_kernel<float>);

@@ -100,6 +100,11 @@ WORKLOADS = {
     # 256 RoIs per image, 7 x 7 bins, 2 x 2 samples per bin
     "roi_c4": Workload("roi_c4", "bf16", 2, 256, 50, 84, 256, 7, 1, 0, 1, 7, 7,
                        offset="normal:0.1", mask="sigmoid", bias=None, seed=1008, op="roi_pool"),
+    # deformable position-sensitive RoI pooling on R-FCN-style score maps of the c4 grid:
+    # 81 classes (80 + background) x 7 x 7 bins = 3969 maps at 50 x 84, 256 RoIs per image,
+    # 2 x 2 samples per bin, one offset per bin shared by all classes, and a mask
+    "psroi_c4": Workload("psroi_c4", "bf16", 2, 3969, 50, 84, 81, 7, 1, 0, 1, 7, 7,
+                         offset="normal:0.1", mask="sigmoid", bias=None, seed=1010, op="ps_roi_pool"),
     "c4_om": Workload("c4_om", "bf16", 2, 256, 100, 168, 27, 3, 2, 1, 1, 50, 84,
                       offset="normal:1", mask=None, bias="normal:0.1", seed=1006, op="offset_mask"),
     # the c4 layer on inputs whose four corners nearly cancel: x of alternating sign
@@ -109,7 +114,7 @@ WORKLOADS = {
                           offset="frac:2:0.45:0.55", mask="sigmoid", bias=None, seed=1009,
                           x="checker:0.01", weight="kaiming_abs"),
 }
-ORDER = ["tiny", "single224", "c3", "c4", "c5", "c4_g4", "c4_om", "c4_bwd", "roi_c4"]
+ORDER = ["tiny", "single224", "c3", "c4", "c5", "c4_g4", "c4_om", "c4_bwd", "roi_c4", "psroi_c4"]
 
 
 def _draw(kind: str, shape, g: torch.Generator) -> torch.Tensor:

@@ -219,8 +219,9 @@ int dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const 
  * Pixel (y, x) sits at the integer position (y, x), as in the convolution.
  * x [B,C,H,W], offset [R,2,k,k] or NULL (no shift), mask [R,k,k] or NULL, out [R,C,k,k]
  * in desc->dtype; rois [R,5] is always float32 (batch index, x1, y1, x2, y2 in image
- * coordinates).  A RoI whose batch index is not in [0, B) pools zeros.  Positions,
- * weights and sums in fp32; out rounded to dtype.  Device pointers; asynchronous on
+ * coordinates).  A RoI whose batch index is not in [0, B) pools zeros.  Bilinear
+ * weights and sums in fp32 (sample positions in double for fp32 data, in fp32 for
+ * bf16); out rounded to dtype.  Device pointers; asynchronous on
  * `stream`.  bf16 with k <= 16 first writes a channels-last copy of x into the
  * workspace (256-byte aligned, dcn_roi_pool_workspace_bytes; 0 bytes otherwise).
  * DCN_E_ARG for an invalid descriptor or a NULL x, rois or out (R = 0 launches
@@ -242,6 +243,31 @@ int dcn_roi_pool(const dcn_roi_desc* desc, const void* x, const float* rois, con
                  const void* mask, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
+/* Deformable position-sensitive RoI pooling (the tags page above, part "Deformable
+ * Convolutional Networks", section Deformable RoI Pooling: a learnable offset per bin
+ * combined with ordinary position-sensitive RoI pooling).  x holds k*k score maps per
+ * output channel, and bin (i, j) of output channel c pools only its own map:
+ *   out[r,c,i,j] = m[r,i,j] / S^2 * sum_{u,v<S} S(x[b, (c*k + i)*k + j], py, px)
+ * with b, py, px, m exactly as for dcn_roi_pool, the offset of bin (i, j) taken from
+ * offset[r, 2g + {0: rows, 1: columns}, i, j] for output channel group g = c / (C/G)
+ * (G = offset_groups, 0 or 1 meaning one offset per bin shared by every channel).
+ * x [B, C*k*k, H, W], offset [R, 2G, k, k] or NULL, mask [R, k, k] or NULL,
+ * out [R, C, k, k] in desc->dtype; rois [R, 5] float32.  No workspace.  Errors as for
+ * dcn_roi_pool (DCN_E_ARG also when C % G != 0), all checked before any launch. */
+typedef struct dcn_ps_roi_desc {
+  int64_t batch, out_channels, height, width;   /* x has out_channels * k * k channels */
+  int64_t num_rois;      /* R >= 0 */
+  int64_t pooled_size;   /* k, 1..1024 */
+  int64_t samples;       /* S, 1..64 */
+  int64_t offset_groups; /* G >= 0; out_channels % G == 0 */
+  float spatial_scale;
+  float gamma;
+  int32_t dtype;
+  int32_t reserved;      /* 0 */
+} dcn_ps_roi_desc;
+int dcn_ps_roi_pool(const dcn_ps_roi_desc* desc, const void* x, const float* rois, const void* offset,
+                    const void* mask, void* out, hipStream_t stream);
+
 const char* dcn_status_str(int status);
 
 #ifdef __cplusplus

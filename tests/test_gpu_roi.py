@@ -91,3 +91,49 @@ def test_roi_pool_empty_and_full_size():
     ref, ab = oracle.roi_pool(inp["x"], inp["rois"], w.K, 2, 1.0 / 16, 0.1, inp["offset"], inp["mask"],
                               with_abs=True)
     check(got.float().cpu().numpy(), ref, ab, TOL["bf16"], "roi_c4")
+
+
+PS_CASES = [
+    # name, B, C (output channels), H, W, R, k, S, scale, gamma, G (offset groups; 0: no offsets), mask
+    ("ps_k3_plain", 2, 4, 17, 23, 9, 3, 2, 1.0, 0.1, 0, False),
+    ("ps_k3_offsets", 2, 5, 17, 23, 9, 3, 2, 1.0, 0.1, 1, False),
+    ("ps_k7_modulated", 1, 6, 20, 15, 12, 7, 2, 0.5, 0.1, 1, True),
+    ("ps_class_offsets", 2, 6, 25, 42, 20, 7, 2, 1.0 / 16, 0.1, 3, True),
+    ("ps_one_sample", 1, 3, 9, 9, 6, 4, 1, 1.0, 0.2, 1, True),
+    ("ps_four_samples_large_gamma", 1, 2, 12, 14, 10, 5, 4, 1.0, 1.0, 2, True),
+    ("ps_k1", 2, 7, 10, 10, 5, 1, 3, 1.0, 0.1, 7, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", PS_CASES, ids=[c[0] for c in PS_CASES])
+def test_ps_roi_pool_parity(case, dtype):
+    name, B, C, H, W, R, k, S, scale, gamma, G, wm = case
+    seed = zlib.crc32(name.encode()) % 1000
+    x, rois, off, m = make(B, C * k * k, H, W, R, k, S, scale, gamma, G > 0, wm, dtype, seed=seed)
+    if G > 1:   # offsets per group of output channels
+        gen = torch.Generator().manual_seed(seed + 1)
+        off = (torch.randn((R, 2 * G, k, k), generator=gen) * 0.3).to(x.dtype)
+    print(f"[gpu-test] ps roi {name} {dtype}", flush=True)
+    got = dcn.deform_ps_roi_pool(x.cuda(), rois.cuda(), None if off is None else off.cuda(),
+                                 None if m is None else m.cuda(), k, S, scale, gamma)
+    torch.cuda.synchronize()
+    ref, ab = oracle.ps_roi_pool(x, rois, k, S, scale, gamma, off, m, with_abs=True)
+    worst = check(got.float().cpu().numpy(), ref, ab, TOL[dtype], f"{name}/{dtype}")
+    print(f"[gpu-test] max relative error {worst:.2e}", flush=True)
+    assert np.all(got[0].float().cpu().numpy() == 0.0), "a RoI past the last image must pool zeros"
+
+
+def test_ps_roi_pool_full_size():
+    """The bench's layer in full: 81 classes x 7 x 7 score maps on the c4 grid, 512 RoIs."""
+    from deformable_convolution_vision_amd.workloads import WORKLOADS, roi_inputs
+    w = WORKLOADS["psroi_c4"]
+    inp = roi_inputs(w, 256, w.K, (800, 1344))
+    g = {k: v.cuda() for k, v in inp.items()}
+    got = dcn.deform_ps_roi_pool(g["x"], g["rois"], g["offset"], g["mask"], w.K, 2, 1.0 / 16, 0.1)
+    torch.cuda.synchronize()
+    ref, ab = oracle.ps_roi_pool(inp["x"], inp["rois"], w.K, 2, 1.0 / 16, 0.1, inp["offset"], inp["mask"],
+                                 with_abs=True)
+    check(got.float().cpu().numpy(), ref, ab, TOL["bf16"], "psroi_c4")
+    out = dcn.deform_ps_roi_pool(g["x"], torch.zeros((0, 5), device="cuda"), output_size=7)
+    assert out.shape == (0, 81, 7, 7)
