@@ -200,10 +200,10 @@ def bench_offset_mask(w, steps: int, warmup: int):
     ms_per_step = total_ms / steps
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK["bf16_mfma"] if w.dtype == "bf16" else PEAK["f32_mfma"]
-    # the kernel dcn_offset_mask runs (its planning rule): bf16 3x3 with >= 24 input
-    # channels and at most 128 outputs on the box kernel's 128-row tiles, else the tile kernels
-    variant = "box_bf16_m128" if (w.dtype == "bf16" and w.K == 3 and w.Cin >= 24 and w.Cout <= 128) else \
-        f"tile_{w.dtype}_m{64 if w.Cout <= 64 else 128}_n64"
+    gbps = w.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9
+    # the kernel dcn_offset_mask runs (its planning rule): bf16 on the convolution kernel
+    # of dcn_om.hip, fp32 on the tile kernels
+    variant = "om_bf16" if w.dtype == "bf16" else f"tile_f32_m{64 if w.Cout <= 64 else 128}_n64"
     return {
         "metric": "deform_conv2d fwd effective TFLOP/s + GB/s (c4 stride-2 bf16), % of roofline",
         "value": round(tflops, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
@@ -216,12 +216,122 @@ def bench_offset_mask(w, steps: int, warmup: int):
         "effective_gbps": round(w.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "frac_mfma_peak": round(tflops / peak, 5),
         "frac_hbm_peak": round(w.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK["hbm"], 5),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 4), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 5), "traffic": None,
+        # about 58 flop per algorithmic byte, far below the bf16 ridge: bound by HBM
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK["hbm"], "unit": "GB/s",
+                     "frac": round(gbps / PEAK["hbm"], 5), "traffic": None,
                      "kernel": "dcn_offset_mask (both launches)", "kernel_sha": kernel_hash(),
                      "per_launch": {"flops": w.flops, "algorithmic_bytes": w.algorithmic_bytes}},
         "kernels_us": {"call_mean": round(total_ms / steps * 1e3, 3), "call_median": round(per[steps // 2] * 1e3, 3),
                        "call_min": round(per[0] * 1e3, 3)},
+        "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
+        "parity_max_rel_err_sampled": max_rel,
+        "cold": None,
+        "cpu_baseline": None,
+    }
+
+
+def bench_layer(w, steps: int, warmup: int):
+    """The whole DCNv2 layer (dcn_layer_forward): the offset/mask branch of the c4 layer
+    (256 -> 27 channels) and its deformable convolution (256 -> 256) off one staged copy
+    of x, one call per step (staging launch, branch launch, deformable launch).  The same
+    work as two separate calls (dcn_offset_mask, then dcn_forward) is timed beside it.
+    value is TFLOP/s of both convolutions."""
+    import numpy as np
+    import torch
+
+    import deformable_convolution_vision_amd as dcn
+    import oracle
+    from deformable_convolution_vision_amd.workloads import WORKLOADS, generate
+
+    wf, wo = WORKLOADS["c4"], WORKLOADS["c4_om"]
+    inp, inp_om = generate(wf), generate(wo)
+    inp["x"] = inp_om["x"]
+    g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    go = {k: (None if v is None else v.cuda()) for k, v in inp_om.items()}
+    desc = dcn.make_desc(wf.B, wf.Cin, wf.H, wf.W, wf.Cout, wf.K, wf.stride, wf.pad, wf.dilation, dcn.BF16, 1)
+    Ho, Wo = dcn.dcn_output_hw(desc)
+    nb = dcn.dcn_layer_workspace_bytes(desc)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wf.B, wf.Cout, Ho, Wo), dtype=torch.bfloat16, device="cuda")
+    off = torch.empty((wf.B, 18, Ho, Wo), dtype=torch.bfloat16, device="cuda")
+    msk = torch.empty((wf.B, 9, Ho, Wo), dtype=torch.bfloat16, device="cuda")
+    nb_om = dcn.dcn_offset_mask_workspace_bytes(desc)
+    nb_f = dcn.dcn_workspace_bytes(desc)
+    ws_om = torch.empty(max(nb_om, 1), dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(max(nb_f, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        dcn.dcn_layer_forward(desc, g["x"], go["weight"], go["bias"], g["weight"], None, off, msk, out, ws, nb,
+                              stream)
+
+    def step_separate():
+        dcn.dcn_offset_mask(desc, g["x"], go["weight"], go["bias"], off, msk, ws_om, nb_om, stream)
+        dcn.dcn_forward(desc, g["x"], off, msk, g["weight"], None, out, ws_f, nb_f, stream)
+
+    step()
+    torch.cuda.synchronize()
+    # parity on sampled outputs: the branch against the oracle's convolution, the layer's
+    # output against the oracle's forward on the offsets and mask the call produced
+    rng = np.random.default_rng(0)
+    npts = 512
+    pts = np.stack([rng.integers(0, wf.B, npts), rng.integers(0, wf.Cout, npts), rng.integers(0, Ho, npts),
+                    rng.integers(0, Wo, npts)], 1).astype(np.int64)
+    offh, mskh = off.cpu(), msk.cpu()
+    y, a = oracle.points(inp["x"], offh, inp["weight"], pts, None, wf.stride, wf.pad, wf.dilation, mask=mskh)
+    got = out.float().cpu().numpy()[pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
+    max_rel = float(np.max(np.abs(got - y) / a))
+    pts_o = pts.copy()
+    pts_o[:, 1] = rng.integers(0, 27, npts)
+    zero = np.zeros((wf.B, 18, Ho, Wo), dtype=np.float32)
+    yo, ao = oracle.points(inp["x"], zero, inp_om["weight"], pts_o, inp_om["bias"], wf.stride, wf.pad, wf.dilation)
+    for (b, o, oy, ox), yy, aa in zip(pts_o, yo, ao):
+        if o < 18:
+            e = abs(float(offh[b, o, oy, ox]) - yy) / aa
+        else:
+            e = max(abs(float(mskh[b, o - 18, oy, ox]) - 1.0 / (1.0 + np.exp(-yy))) - 2.0 ** -9, 0.0) / (aa / 4)
+        max_rel = max(max_rel, float(e))
+    if not max_rel <= 1e-2:
+        raise SystemExit(f"bench parity failure on {w.name}: max relative error {max_rel:.3e} > 1e-2")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = HipEvents(2)
+        t0 = time.perf_counter()
+        ev.record(0, sp)
+        for _ in range(steps):
+            fn()
+        ev.record(1, sp)
+        ev.sync(1)
+        wall = time.perf_counter() - t0
+        ms = ev.ms(0, 1) / steps
+        ev.close()
+        return ms, wall
+
+    ms_sep, _ = timed(step_separate)
+    ms_per_step, wall = timed(step)
+    flops = wf.flops + wo.flops
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK["bf16_mfma"]
+    return {
+        "metric": "deform_conv2d fwd effective TFLOP/s + GB/s (c4 stride-2 bf16), % of roofline",
+        "value": round(tflops, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; shapes and value distributions of the workload)",
+        "config": {"workload": f"{w.name}: the c4 DCNv2 layer in one call: offset/mask convolution 256 -> 27 "
+                               f"channels and the deformable convolution 256 -> 256, B=2 100x168 -> 50x84, K=3 "
+                               f"stride=2 pad=1, off one staged copy of x",
+                   "variant": "layer", "plan": "dcn_layer_forward: staging (x once, both weights) + branch + "
+                                               "deformable launch"},
+        "separate_calls_ms_per_step": round(ms_sep, 6),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 4), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 5), "traffic": None,
+                     "kernel": "dcn_layer_forward (all launches)", "kernel_sha": kernel_hash(),
+                     "per_launch": {"flops": flops}},
+        "kernels_us": {"call_mean": round(ms_per_step * 1e3, 3), "separate_calls_mean": round(ms_sep * 1e3, 3)},
         "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
         "parity_max_rel_err_sampled": max_rel,
         "cold": None,
@@ -436,6 +546,8 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
         return bench_offset_mask(w, steps, warmup)
     if w.op == "backward":
         return bench_backward(w, steps, warmup)
+    if w.op == "layer":
+        return bench_layer(w, steps, warmup)
     if w.op in ("roi_pool", "ps_roi_pool"):
         return bench_roi(w, steps, warmup)
     host = generate(w)

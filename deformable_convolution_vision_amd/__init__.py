@@ -91,6 +91,10 @@ def load_library() -> ctypes.CDLL:
     lib.dcn_forward.argtypes = [D, P, P, P, P, P, P, P, S, P]
     lib.dcn_forward_staged.argtypes = [D, P, P, P, P, P, P, P, S, P]
     lib.dcn_forward_noalloc.argtypes = [D, P, P, P, P, P, P, P]
+    lib.dcn_layer_workspace_bytes.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.dcn_layer_workspace_bytes.restype = ctypes.c_int
+    lib.dcn_layer_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
+    lib.dcn_layer_forward.restype = ctypes.c_int
     lib.dcn_forward_noalloc.restype = ctypes.c_int
     lib.dcn_stage.argtypes = [D, P, P, P, S, P]
     lib.dcn_variant_name.argtypes = [D]
@@ -485,3 +489,58 @@ def deform_ps_roi_pool(input, rois, offset=None, mask=None, output_size=7, sampl
     with torch.cuda.device(input.device):
         dcn_ps_roi_pool(desc, input, rois, offset, mask, out)
     return out
+
+
+def dcn_layer_workspace_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    rc = load_library().dcn_layer_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    if rc != OK:
+        raise DcnError(rc, "dcn_layer_workspace_bytes")
+    return n.value
+
+
+def dcn_layer_forward(desc: Desc, x, weight_om, bias_om, weight, bias, offset, mask, out, workspace,
+                      workspace_bytes: int, stream=None) -> None:
+    """Raw call: tensors (or integer device addresses) laid out as dcn.h states."""
+    rc = load_library().dcn_layer_forward(ctypes.byref(desc), _ptr(x), _ptr(weight_om), _ptr(bias_om), _ptr(weight),
+                                          _ptr(bias), _ptr(offset), _ptr(mask), _ptr(out), _ptr(workspace),
+                                          workspace_bytes, _stream(stream))
+    if rc != OK:
+        raise DcnError(rc, "dcn_layer_forward")
+
+
+def deform_conv2d_layer(input, weight_om, bias_om, weight, bias=None, stride=1, padding=0, dilation=1,
+                        offset_groups=1, workspace=None):
+    """The whole DCNv2 layer on the GPU in one call: the offset/mask branch (weight_om
+    [3GK^2,Cin,K,K], bias_om [3GK^2] or None) and the deformable convolution (weight
+    [Cout,Cin,K,K], bias [Cout] or None) off one staged copy of input.  Returns (out
+    [B,Cout,Ho,Wo], offset [B,2GK^2,Ho,Wo], mask [B,GK^2,Ho,Wo])."""
+    if input.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {input.dtype}; use float32 or bfloat16")
+    if input.dim() != 4 or weight.dim() != 4 or weight_om.dim() != 4:
+        raise ValueError("input, weight and weight_om must be 4-D")
+    B, Cin, H, W = input.shape
+    Cout, K = weight.shape[0], weight.shape[2]
+    G = int(offset_groups)
+    if tuple(weight.shape) != (Cout, Cin, K, K) or tuple(weight_om.shape) != (3 * G * K * K, Cin, K, K):
+        raise ValueError("weight must be [Cout, Cin, K, K] and weight_om [3*G*K*K, Cin, K, K]")
+    for name, t, shape in (("bias", bias, (Cout,)), ("bias_om", bias_om, (3 * G * K * K,))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    for name, t in (("input", input), ("weight", weight), ("weight_om", weight_om), ("bias", bias),
+                    ("bias_om", bias_om)):
+        if t is None:
+            continue
+        if t.dtype != input.dtype or not t.is_cuda or t.device != input.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {input.dtype} tensor on the input's GPU")
+    desc = make_desc(B, Cin, H, W, Cout, K, int(stride), int(padding), int(dilation), _DTYPES[input.dtype], G)
+    Ho, Wo = dcn_output_hw(desc)
+    out = torch.empty((B, Cout, Ho, Wo), dtype=input.dtype, device=input.device)
+    offset = torch.empty((B, 2 * G * K * K, Ho, Wo), dtype=input.dtype, device=input.device)
+    mask = torch.empty((B, G * K * K, Ho, Wo), dtype=input.dtype, device=input.device)
+    nbytes = dcn_layer_workspace_bytes(desc)
+    workspace = _workspace(workspace, nbytes, input.device)
+    with torch.cuda.device(input.device):
+        dcn_layer_forward(desc, input, weight_om, bias_om, weight, bias, offset, mask, out,
+                          workspace if nbytes else None, nbytes)
+    return out, offset, mask

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdcn_hip.so")
 SOURCES = ["dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip", "dcn_box_inst_a.hip", "dcn_box_inst_b.hip",
-           "dcn_box_inst_c.hip", "dcn_box_inst_d.hip", "dcn_direct.hip", "dcn_backward.hip", "dcn_roi.hip"]
+           "dcn_box_inst_c.hip", "dcn_box_inst_d.hip", "dcn_direct.hip", "dcn_backward.hip", "dcn_roi.hip",
+           "dcn_om.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -243,7 +243,8 @@ int compute_plan(const dcn_desc* d, Plan* p, int force_variant = -1) {
       int found = -1;
       for (int v = 0; v < dcn::V_COUNT; ++v)
         if (std::strcmp(force, dcn::variant_info(v).name) == 0) found = v;
-      if (found < 0 || dcn::variant_info(found).is_bf16 != (d->dtype == DCN_BF16)) return DCN_E_UNSUPPORTED;
+      if (found < 0 || found == dcn::V_OM_BF16 || dcn::variant_info(found).is_bf16 != (d->dtype == DCN_BF16))
+        return DCN_E_UNSUPPORTED;
       if ((found == dcn::V_DIRECT_F32 || found == dcn::V_DIRECT_BF16) && !direct_fits(d, HoWo))
         return DCN_E_UNSUPPORTED;
       if (found == dcn::V_BOX_BF16_M128 || found == dcn::V_BOX_BF16_M256) {
@@ -262,6 +263,9 @@ int compute_plan(const dcn_desc* d, Plan* p, int force_variant = -1) {
       static_cast<double>(Cout) * Cin * KK > lim || static_cast<double>(B) * Cout * HoWo > lim ||
       static_cast<double>(B) * H * W * p->Cp > lim || static_cast<double>(p->Mp) * KK * p->Cp > lim ||
       static_cast<double>(N) + vi.nt > lim)
+    return DCN_E_UNSUPPORTED;
+  // the offset/mask convolution addresses the staged copy with 32-bit byte offsets
+  if (p->variant == dcn::V_OM_BF16 && static_cast<double>(B) * H * W * p->Cp * 2 >= 4294967296.0 - 64)
     return DCN_E_UNSUPPORTED;
   const size_t es = d->dtype == DCN_BF16 ? 2 : 4;
   p->empty = (B == 0 || Cout == 0);
@@ -347,7 +351,7 @@ StageArgs stage_args(const dcn_desc* d, const Plan& p, const void* x, const void
   a.Cout = static_cast<int>(d->out_channels);
   a.Mp = static_cast<int>(p.Mp);
   a.KK = static_cast<int>(d->kernel_size * d->kernel_size);
-  a.wlayout = is_box(p.variant) ? 1 : 0;
+  a.wlayout = p.variant == dcn::V_OM_BF16 ? 2 : is_box(p.variant) ? 1 : 0;
   return a;
 }
 
@@ -478,9 +482,39 @@ extern "C" int dcn_plan_describe(const dcn_desc* desc, char* buf, size_t len) {
   return DCN_OK;
 }
 
-// ---- the offset/mask branch: a regular convolution with 3*G*K*K outputs on the
-// tile kernels (zero offsets, no mask), its epilogue splitting offsets and mask
+// ---- the offset/mask branch: a regular convolution with 3*G*K*K outputs (bf16: the
+// kernel of dcn_om.hip; fp32: the tile kernels at zero offsets with no mask), its
+// epilogue splitting offsets and mask
 namespace {
+
+// arguments of the offset/mask convolution reading the staged copy at ws + p.ws_x and the
+// repacked branch weight at wp_om
+dcn::OmArgs om_args(const dcn_desc* od, const Plan& p, const void* ws, const void* bias_om, void* offset,
+                    void* mask, int split, const void* wp_om = nullptr) {
+  dcn::OmArgs a{};
+  a.xs = static_cast<const unsigned char*>(ws) + p.ws_x;
+  a.wp = wp_om != nullptr ? wp_om : static_cast<const unsigned char*>(ws) + p.ws_w;
+  a.bias = bias_om;
+  a.offset = offset;
+  a.mask = mask;
+  a.B = static_cast<int>(od->batch);
+  a.H = static_cast<int>(od->height);
+  a.W = static_cast<int>(od->width);
+  a.Cp = static_cast<int>(p.Cp);
+  a.M = static_cast<int>(od->out_channels);
+  a.Mp = static_cast<int>(p.Mp);
+  a.K = static_cast<int>(od->kernel_size);
+  a.KK = a.K * a.K;
+  a.stride = static_cast<int>(od->stride);
+  a.pad = static_cast<int>(od->pad);
+  a.dil = static_cast<int>(od->dilation);
+  a.Ho = static_cast<int>(p.Ho);
+  a.Wo = static_cast<int>(p.Wo);
+  a.HoWo = a.Ho * a.Wo;
+  a.N = a.B * a.HoWo;
+  a.split = split;
+  return a;
+}
 
 int om_plan(const dcn_desc* d, dcn_desc* od, Plan* p) {
   if (!geometry_ok(d)) return DCN_E_ARG;
@@ -490,17 +524,11 @@ int om_plan(const dcn_desc* d, dcn_desc* od, Plan* p) {
   od->offset_groups = 1;
   const int64_t Ho = out_extent(od->height, od->kernel_size, od->stride, od->pad, od->dilation);
   const int64_t Wo = out_extent(od->width, od->kernel_size, od->stride, od->pad, od->dilation);
-  // bf16: the box kernel with 128-row tiles where it plans (zero offsets keep every
-  // sample in the box); else the tile kernels
-  BoxPlan box;
-  if (d->dtype == DCN_BF16 && d->kernel_size == 3 && Ho >= 1 && Wo >= 1 && od->in_channels >= 24 &&
-      od->out_channels <= 128 && plan_box(od, Ho, Wo, 2, &box)) {
-    const int rc = compute_plan(od, p, dcn::V_BOX_BF16_M128);
-    box.pw = 4;        // the branch's kernel: four producer waves, paired roles
-    box.split = 0;
-    p->box = box;
-    return rc;
-  }
+  // bf16: the convolution kernel of dcn_om.hip (rows in 32-row tiles, the column
+  // matrix read straight from the staged copy); fp32: the tile kernels
+  (void)Ho;
+  (void)Wo;
+  if (d->dtype == DCN_BF16) return compute_plan(od, p, dcn::V_OM_BF16);
   const bool small = od->out_channels <= 64;
   const int variant = d->dtype == DCN_F32 ? (small ? dcn::V_TILE_F32_M64_N64 : dcn::V_TILE_F32_M128_N64)
                                           : (small ? dcn::V_TILE_BF16_M64_N64 : dcn::V_TILE_BF16_M128_N64);
@@ -534,9 +562,14 @@ extern "C" int dcn_offset_mask(const dcn_desc* desc, const void* x, const void* 
   if (rc != DCN_OK) return rc;
   const StageArgs s = stage_args(&od, p, x, weight_om, workspace);
   if (dcn::launch_stage(p.variant, s, stream) != hipSuccess) return DCN_E_HIP;
+  const int split = static_cast<int>(2 * offset_groups(desc) * desc->kernel_size * desc->kernel_size);
+  if (p.variant == dcn::V_OM_BF16) {
+    const dcn::OmArgs oa = om_args(&od, p, workspace, bias_om, offset, mask, split);
+    return dcn::launch_om(oa, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
+  }
   FusedArgs a = fused_args(&od, p, x, nullptr, nullptr, weight_om, bias_om, offset, workspace);
   a.out2 = mask;
-  a.om_split = static_cast<int>(2 * offset_groups(desc) * desc->kernel_size * desc->kernel_size);
+  a.om_split = split;
   return launch_fused_plan(p, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
 }
 
@@ -655,4 +688,97 @@ extern "C" int dcn_forward_noalloc(const dcn_desc* desc, const void* x, const vo
   }
   const FusedArgs a = fused_args(desc, p, x, offset, mask, weight, bias, out, ws);
   return launch_fused_plan(p, a, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
+}
+
+// ---- the DCNv2 layer in one call: the offset/mask branch and the deformable convolution
+// off one staged copy of x (csdn.net tags page "可变形卷积：Deformable ConvNets", DCNv2
+// section 3.2: the branch is a convolution of the same input feature map)
+namespace {
+
+struct LayerPlan {
+  Plan fwd, om;
+  dcn_desc od;          // the branch's convolution
+  bool shared = false;  // one staging launch writes x once and both repacked weights
+  size_t wp_om = 0;     // shared: byte offset of the branch's weight; else of its workspace part
+  size_t fwd_base = 0;  // byte offset of the deformable layer's workspace part (not shared)
+  size_t ws_bytes = 0;
+  int split = 0;
+};
+
+int layer_plan(const dcn_desc* d, LayerPlan* lp) {
+  int rc = make_plan(d, &lp->fwd);
+  if (rc != DCN_OK) return rc;
+  rc = om_plan(d, &lp->od, &lp->om);
+  if (rc != DCN_OK) return rc;
+  lp->split = static_cast<int>(2 * offset_groups(d) * d->kernel_size * d->kernel_size);
+  const bool fs = dcn::variant_info(lp->fwd.variant).staged && !lp->fwd.empty;
+  const bool os = dcn::variant_info(lp->om.variant).staged && !lp->om.empty;
+  // the staged copies coincide when both paths stage x with the same channel padding
+  lp->shared = fs && os && lp->fwd.Cp == lp->om.Cp && lp->fwd.ws_x == 0 && lp->om.ws_x == 0 &&
+               lp->fwd.ws_w == lp->om.ws_w;
+  if (lp->shared) {
+    lp->wp_om = lp->fwd.ws_bytes;
+    lp->ws_bytes = lp->fwd.ws_bytes + (lp->om.ws_bytes - lp->om.ws_w);
+  } else {
+    lp->wp_om = 0;
+    lp->fwd_base = align_up(lp->om.ws_bytes, kAlign);
+    lp->ws_bytes = lp->fwd_base + lp->fwd.ws_bytes;
+  }
+  return DCN_OK;
+}
+
+}  // namespace
+
+extern "C" int dcn_layer_workspace_bytes(const dcn_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return DCN_E_ARG;
+  LayerPlan lp;
+  const int rc = layer_plan(desc, &lp);
+  if (rc != DCN_OK) return rc;
+  *bytes = lp.ws_bytes;
+  return DCN_OK;
+}
+
+extern "C" int dcn_layer_forward(const dcn_desc* desc, const void* x, const void* weight_om, const void* bias_om,
+                                 const void* weight, const void* bias, void* offset, void* mask, void* out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  LayerPlan lp;
+  int rc = layer_plan(desc, &lp);
+  if (rc != DCN_OK) return rc;
+  if (lp.om.empty) return DCN_OK;   // B == 0
+  if (x == nullptr || weight_om == nullptr || offset == nullptr || mask == nullptr) return DCN_E_ARG;
+  if (!lp.fwd.empty && (weight == nullptr || out == nullptr)) return DCN_E_ARG;
+  rc = check_positions(&lp.od, lp.od.kernel_size, lp.od.stride, lp.od.pad, lp.od.dilation, lp.om.Ho, lp.om.Wo);
+  if (rc != DCN_OK) return rc;
+  if (lp.ws_bytes > 0 &&
+      (workspace == nullptr || workspace_bytes < lp.ws_bytes || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0))
+    return DCN_E_WORKSPACE;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if (lp.shared) {
+    // one launch: x staged once, the layer's weight and the branch's weight repacked
+    StageArgs s = stage_args(desc, lp.fwd, x, weight, ws);
+    s.w2 = weight_om;
+    s.wp2 = ws + lp.wp_om;
+    s.Cout2 = static_cast<int>(lp.od.out_channels);
+    s.Mp2 = static_cast<int>(lp.om.Mp);
+    s.wlayout2 = stage_args(&lp.od, lp.om, x, weight_om, ws).wlayout;
+    if (dcn::launch_stage(lp.fwd.variant, s, stream) != hipSuccess) return DCN_E_HIP;
+    if (lp.om.variant == dcn::V_OM_BF16) {
+      const dcn::OmArgs oa = om_args(&lp.od, lp.om, ws, bias_om, offset, mask, lp.split, ws + lp.wp_om);
+      if (dcn::launch_om(oa, stream) != hipSuccess) return DCN_E_HIP;
+    } else {
+      FusedArgs a = fused_args(&lp.od, lp.om, x, nullptr, nullptr, weight_om, bias_om, offset, ws);
+      a.wp = ws + lp.wp_om;
+      a.out2 = mask;
+      a.om_split = lp.split;
+      if (launch_fused_plan(lp.om, a, stream) != hipSuccess) return DCN_E_HIP;
+    }
+    const FusedArgs f = fused_args(desc, lp.fwd, x, offset, mask, weight, bias, out, ws);
+    return launch_fused_plan(lp.fwd, f, stream) == hipSuccess ? DCN_OK : DCN_E_HIP;
+  }
+  // the two calls one after the other, each on its own part of the workspace
+  rc = dcn_offset_mask(desc, x, weight_om, bias_om, offset, mask, lp.om.ws_bytes ? ws : nullptr, lp.om.ws_bytes,
+                       stream);
+  if (rc != DCN_OK || lp.fwd.empty) return rc;
+  return dcn_forward(desc, x, offset, mask, weight, bias, out, lp.fwd.ws_bytes ? ws + lp.fwd_base : nullptr,
+                     lp.fwd.ws_bytes, stream);
 }

@@ -18,15 +18,7 @@ static hipError_t launch_box_t(const BoxArgs& ba, hipStream_t stream) {
   void* args[] = {const_cast<BoxArgs*>(&ba)};
   const dim3 grid(ba.f.m_tiles * ba.tiles_per_img * ba.f.B);
   const void* fn = nullptr;
-  if (ba.f.om_split > 0) {   // the offset/mask branch: 128-row tiles, 3x3, paired roles
-    if constexpr (FM == 2) {
-      if (ba.f.KK != 9 || ba.f.G > 1 || ba.split_roles || ba.pw != 4) return hipErrorInvalidValue;
-      return hipLaunchKernel(reinterpret_cast<const void*>(&dcn_box_kernel<2, FN, 9, false, 4, true>), grid,
-                             dim3(kThreads), args, 0, stream);
-    } else {
-      return hipErrorInvalidValue;
-    }
-  }
+  if (ba.f.om_split > 0) return hipErrorInvalidValue;   // the offset/mask branch has its own kernel
   if (ba.pw == 8) {   // eight producer waves: 3x3, one offset group, paired roles
     if constexpr (box_pw8_built(FM, FN)) {
       if (ba.f.KK != 9 || ba.f.G > 1 || ba.split_roles) return hipErrorInvalidValue;

@@ -211,7 +211,7 @@ __device__ __forceinline__ void lds_barrier_keep() {
 
 }  // namespace
 
-template <int FM, int FN, int KKT, bool GRP, int PW = 4, bool OM = false>
+template <int FM, int FN, int KKT, bool GRP, int PW = 4>
 __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
   using Cfg = BoxCfg<FN, GRP>;
   const FusedArgs& a = ba.f;
@@ -220,9 +220,6 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
   // (8-byte units, 4 channels; two producer waves share each SIMD)
   static_assert(PW == 4 || PW == 8, "four or eight producer waves");
   static_assert(PW == 4 || (KKT == 9 && !GRP), "eight producer waves: 3x3, one offset group");
-  // OM: the offset/mask branch (a regular convolution: no offset field; the epilogue
-  // writes the offsets to out and the sigmoid of the mask channels to out2)
-  static_assert(!OM || (!GRP && PW == 4), "offset/mask branch: one group, four producer waves");
   constexpr int NTH = 256 + 64 * PW;   // threads per workgroup
   constexpr int PTH = 64 * PW;         // producer threads
   constexpr int UB = PW == 8 ? 8 : 16; // bytes per column unit
@@ -376,18 +373,13 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
       // branch joins on a value still in flight
       mb[j] = a.mask ? (b * KK * NG + gk) * a.HoWo + rem : ob[j];
     }
-    if constexpr (OM) {   // zero offsets, no mask
+    const uint16_t* offs = reinterpret_cast<const uint16_t*>(a.offset);
+    const uint16_t* msk = reinterpret_cast<const uint16_t*>(a.mask ? a.mask : a.offset);
 #pragma unroll
-      for (int j = 0; j < kPE; ++j) ldy[j] = ldx[j] = lm[j] = 0u;
-    } else {
-      const uint16_t* offs = reinterpret_cast<const uint16_t*>(a.offset);
-      const uint16_t* msk = reinterpret_cast<const uint16_t*>(a.mask ? a.mask : a.offset);
-#pragma unroll
-      for (int j = 0; j < kPE; ++j) {
-        ldy[j] = offs[ob[j]];
-        ldx[j] = offs[ob[j] + a.HoWo];
-        lm[j] = msk[mb[j]];
-      }
+    for (int j = 0; j < kPE; ++j) {
+      ldy[j] = offs[ob[j]];
+      ldx[j] = offs[ob[j] + a.HoWo];
+      lm[j] = msk[mb[j]];
     }
   };
   if (consumer) load_offsets(0);
@@ -677,9 +669,7 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
           bv[tm][r] = ld_bf16(a.bias, min(m0 + wv * WM + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3), a.Cout - 1));
     }
     uint32_t* stage = reinterpret_cast<uint32_t*>(box0);
-    // the offset/mask branch passes the mask channels through a sigmoid; the two
-    // staging loops are separate so the common one carries none of it
-    auto stage_tile = [&](auto sig) __attribute__((always_inline)) {
+    {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
@@ -690,17 +680,11 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
             uint32_t* d = stage + ((tn * 32 + l32) * (MT + 2) + row) / 2;
             float v[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              v[i] = acc[tm][tn][4 * g + i] + bv[tm][4 * g + i];
-              if constexpr (decltype(sig)::value) {
-                if (m0 + row + i >= a.om_split) v[i] = 1.f / (1.f + expf(-v[i]));
-              }
-            }
+            for (int i = 0; i < 4; ++i) v[i] = acc[tm][tn][4 * g + i] + bv[tm][4 * g + i];
             d[0] = pk_bf16(v[0], v[1]);
             d[1] = pk_bf16(v[2], v[3]);
           }
-    };
-    stage_tile(std::integral_constant<bool, OM>());
+    }
   } else {
     // ================= producers: box copies and column tiles =================
     const int ptid = rtid;                  // producer thread 0..PTH-1
@@ -763,13 +747,9 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
           const unsigned char* q = src + (in_box ? ce.off : BOXB) + (ptid & (UPS - 1)) * UB;
           const int rs = in_box ? BW * kPXB : 0;
           f.q[g][0] = *reinterpret_cast<const QV*>(q);
-          if constexpr (OM) {   // zero offsets: the sample is corner (y0, x0) itself
-            f.q[g][1] = f.q[g][2] = f.q[g][3] = f.q[g][0];
-          } else {
-            f.q[g][1] = *reinterpret_cast<const QV*>(q + kPXB);
-            f.q[g][2] = *reinterpret_cast<const QV*>(q + rs);
-            f.q[g][3] = *reinterpret_cast<const QV*>(q + rs + kPXB);
-          }
+          f.q[g][1] = *reinterpret_cast<const QV*>(q + kPXB);
+          f.q[g][2] = *reinterpret_cast<const QV*>(q + rs);
+          f.q[g][3] = *reinterpret_cast<const QV*>(q + rs + kPXB);
         }
       }
     };
@@ -813,9 +793,7 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
             c2 = sel4(o, gq[g][2], c2);
             c3 = sel4(o, gq[g][3], c3);
           }
-          QV r;
-          if constexpr (OM) r = c0;   // weights (1, 0, 0, 0): the copy is exact
-          else r = interp8(c0, c1, c2, c3, ce.w);
+          const QV r = interp8(c0, c1, c2, c3, ce.w);
           *reinterpret_cast<QV*>(cdst + p * kCOLB + sub * UB) = r;
         }
       }
@@ -832,7 +810,7 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
       // pipelined over register sets.  The next chunk's box is copied during steps 0-3;
       // each wave waits for its part before barrier 6, after which the whole box is in
       // LDS and steps 7 and 8 read the corners of the next chunk's steps 0 and 1 from it.
-      constexpr int kRd = OM ? 1 : 4;                    // corner reads per sample
+      constexpr int kRd = 4;                             // corner reads per sample
       constexpr int kKeep = GU * (kRd + 1) < 15 ? GU * (kRd + 1) : 15;   // LDS reads issued after the column stores
       // One sample per thread: each step interpolates the NEXT step's column, so its
       // column store stays in flight across the barrier (the consumers read it only
@@ -989,15 +967,7 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
         const uint32_t v0 = src[q0 * (MT + 2)], v1 = src[q1 * (MT + 2)];
         if (o < a.Cout && oy < a.Ho) {
           uint16_t* dst = out;
-          int e;
-          if constexpr (OM) {   // channels past om_split (the mask) go to out2
-            const bool second = o >= a.om_split;
-            dst = second ? reinterpret_cast<uint16_t*>(a.out2) : out;
-            e = (b * (second ? a.Cout - a.om_split : a.om_split) + (second ? o - a.om_split : o)) * a.HoWo +
-                oy * a.Wo + c0;
-          } else {
-            e = (b * a.Cout + o) * a.HoWo + oy * a.Wo + c0;
-          }
+          const int e = (b * a.Cout + o) * a.HoWo + oy * a.Wo + c0;
           if (pair) {
             *reinterpret_cast<uint32_t*>(dst + e) = v0 | (v1 << 16);
           } else {
@@ -1021,20 +991,19 @@ constexpr bool box_pw8_built(int fm, int fn) { return (fm == 4 && fn <= 6) || (f
 
 
 // optional instances per tile shape (must agree with box_pw8_built / box_groups_built)
-#define DCN_BOX_IF_2_4(KW) KW __global__ void dcn_box_kernel<2, 4, 9, false, 4, true>(BoxArgs); KW __global__ void dcn_box_kernel<2, 4, 9, true, 4, false>(BoxArgs);
-#define DCN_BOX_IF_2_6(KW) KW __global__ void dcn_box_kernel<2, 6, 9, false, 4, true>(BoxArgs); KW __global__ void dcn_box_kernel<2, 6, 9, true, 4, false>(BoxArgs);
-#define DCN_BOX_IF_2_8(KW) KW __global__ void dcn_box_kernel<2, 8, 9, false, 4, true>(BoxArgs); KW __global__ void dcn_box_kernel<2, 8, 9, false, 8, false>(BoxArgs); KW __global__ void dcn_box_kernel<2, 8, 9, true, 4, false>(BoxArgs);
-#define DCN_BOX_IF_2_10(KW) KW __global__ void dcn_box_kernel<2, 10, 9, false, 4, true>(BoxArgs); KW __global__ void dcn_box_kernel<2, 10, 9, false, 8, false>(BoxArgs);
-#define DCN_BOX_IF_4_4(KW) KW __global__ void dcn_box_kernel<4, 4, 9, false, 8, false>(BoxArgs); KW __global__ void dcn_box_kernel<4, 4, 9, true, 4, false>(BoxArgs);
-#define DCN_BOX_IF_4_6(KW) KW __global__ void dcn_box_kernel<4, 6, 9, false, 8, false>(BoxArgs);
+#define DCN_BOX_IF_2_4(KW) KW __global__ void dcn_box_kernel<2, 4, 9, true, 4>(BoxArgs);
+#define DCN_BOX_IF_2_6(KW) KW __global__ void dcn_box_kernel<2, 6, 9, true, 4>(BoxArgs);
+#define DCN_BOX_IF_2_8(KW) KW __global__ void dcn_box_kernel<2, 8, 9, false, 8>(BoxArgs); KW __global__ void dcn_box_kernel<2, 8, 9, true, 4>(BoxArgs);
+#define DCN_BOX_IF_2_10(KW) KW __global__ void dcn_box_kernel<2, 10, 9, false, 8>(BoxArgs);
+#define DCN_BOX_IF_4_4(KW) KW __global__ void dcn_box_kernel<4, 4, 9, false, 8>(BoxArgs); KW __global__ void dcn_box_kernel<4, 4, 9, true, 4>(BoxArgs);
+#define DCN_BOX_IF_4_6(KW) KW __global__ void dcn_box_kernel<4, 6, 9, false, 8>(BoxArgs);
 
-// The instances built for one (FM, FN): the offset/mask branch (FM = 2), eight producer
-// waves where built, any K*K <= 9, offset groups where built, and the 3x3 schedule.
+// The instances built for one (FM, FN): eight producer waves where built, any K*K <= 9, offset groups where built, and the 3x3 schedule.
 // DCN_BOX_INSTANCES(template, ...) instantiates them; with "extern template" it declares
 // them for the launcher.
 #define DCN_BOX_INSTANCES(KW, FM, FN)                                                          \
-  KW __global__ void dcn_box_kernel<FM, FN, 0, false, 4, false>(BoxArgs);                     \
-  KW __global__ void dcn_box_kernel<FM, FN, 9, false, 4, false>(BoxArgs);                     \
+  KW __global__ void dcn_box_kernel<FM, FN, 0, false, 4>(BoxArgs);                     \
+  KW __global__ void dcn_box_kernel<FM, FN, 9, false, 4>(BoxArgs);                     \
   DCN_BOX_IF_##FM##_##FN(KW)
 
 }  // namespace dcn

@@ -39,9 +39,28 @@ struct StageArgs {
   const void* x;   // [B][Cin][H][W]
   const void* w;   // [Cout][Cin][K][K]
   void* xs;        // [B][H*W][Cp]
-  void* wp;        // wlayout 0: [Mp][KK][Cp]; wlayout 1: [Cp/32 * KK][Mp][32] (step-major)
+  void* wp;        // wlayout 0: [Mp][KK][Cp]; wlayout 1: [Cp/32 * KK][Mp][32] (step-major);
+                   // wlayout 2: [KK * Cp/16][Mp][16] (tap-major 16-channel steps)
   int B, Cin, HW, Cp, Cout, Mp, KK;
   int wlayout;
+  // an optional second weight of the same input (w2 null: none), repacked by the same
+  // launch: [Cout2][Cin][K][K] -> wp2 in wlayout2 with Mp2 rows
+  const void* w2;
+  void* wp2;
+  int Cout2, Mp2, wlayout2;
+  int nw2;         // workgroups repacking the second weight (set by launch_stage)
+};
+
+// The offset/mask branch as a regular convolution on the staged channels-last input:
+// M = 3*G*K*K outputs, the first `split` (2*G*K*K) written to offset, the sigmoid of the
+// rest to mask, both [B][channels][Ho][Wo], bf16.
+struct OmArgs {
+  const void* xs;      // [B][H][W][Cp] bf16
+  const void* wp;      // [KK * Cp/16][Mp][16] bf16 (wlayout 2)
+  const void* bias;    // [M] bf16 or null
+  void* offset;        // [B][split][Ho][Wo]
+  void* mask;          // [B][M - split][Ho][Wo]
+  int B, H, W, Cp, M, Mp, K, KK, stride, pad, dil, Ho, Wo, HoWo, N, split;
 };
 
 // Box kernel (bf16): FusedArgs plus the output-tile geometry and the LDS budget.
@@ -69,6 +88,7 @@ enum Variant : int {
   V_BOX_BF16_M256,
   V_DIRECT_F32,
   V_DIRECT_BF16,
+  V_OM_BF16,       // the offset/mask branch's regular convolution (dcn_om.hip)
   V_COUNT
 };
 
@@ -93,6 +113,9 @@ hipError_t launch_box(int fm, int fn, const BoxArgs& a, hipStream_t stream);
 int box_capacity_px(int fn, bool groups);
 bool box_groups_supported(int fm, int fn);   // an offset-group kernel is built for (fm, fn)
 bool box_pw8_supported(int fm, int fn);      // an eight-producer-wave kernel is built for (fm, fn)
+
+// the offset/mask branch's convolution (bf16, staged input, weight in wlayout 2)
+hipError_t launch_om(const OmArgs& a, hipStream_t stream);
 
 // direct kernel (no staging): Cin <= 4 and K*K in {1, 4, 9}
 bool direct_supported(int cin, int kk);

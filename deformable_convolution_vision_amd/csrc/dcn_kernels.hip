@@ -91,7 +91,8 @@ __device__ __forceinline__ int xcd_tile(int g, int T) {
 
 // Weight repack, one thread per (row o, channel c): the K*K values of (o, c) are
 // contiguous in w, and for each kernel point neighbouring threads write neighbouring
-// channels.  Layout 0: wp[o][k][c]; layout 1 (box kernel): wp[c/32 * KK + k][o][c%32].
+// channels.  Layout 0: wp[o][k][c]; layout 1 (box kernel): wp[c/32 * KK + k][o][c%32];
+// layout 2 (offset/mask convolution): wp[(k * Cp + c) / 16][o][c%16].
 // Rows >= Cout and channels >= Cin are written as 0.
 template <typename T>
 __device__ __forceinline__ void pack_weight(const StageArgs& a, int wg, int nwg) {
@@ -113,9 +114,10 @@ __device__ __forceinline__ void pack_weight(const StageArgs& a, int wg, int nwg)
       for (int j = 0; j < 9; ++j) {
         const int k = k0 + j;
         if (k >= a.KK) break;
-        const size_t dst = a.wlayout == 0
-                               ? (static_cast<size_t>(o) * a.KK + k) * a.Cp + c
-                               : ((static_cast<size_t>(c >> 5) * a.KK + k) * a.Mp + o) * 32 + (c & 31);
+        const size_t dst = a.wlayout == 0 ? (static_cast<size_t>(o) * a.KK + k) * a.Cp + c
+                           : a.wlayout == 1
+                               ? ((static_cast<size_t>(c >> 5) * a.KK + k) * a.Mp + o) * 32 + (c & 31)
+                               : ((static_cast<size_t>(k) * (a.Cp >> 4) + (c >> 4)) * a.Mp + o) * 16 + (c & 15);
         wp[dst] = v[j];
       }
     }
@@ -226,7 +228,25 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a, int nx, in
   const int tid = threadIdx.x;
   // the weight workgroups come first, so that they run beside the first x tiles
   // rather than after the last
-  const int nw = static_cast<int>(gridDim.x) - nx;
+  const int nw2 = a.w2 != nullptr ? a.nw2 : 0;
+  const int nw = static_cast<int>(gridDim.x) - nx - nw2;
+  if (nw2 > 0 && static_cast<int>(blockIdx.x) >= nw && static_cast<int>(blockIdx.x) < nw + nw2) {
+    // the second weight
+    StageArgs a2 = a;
+    a2.w = a.w2;
+    a2.wp = a.wp2;
+    a2.Cout = a.Cout2;
+    a2.Mp = a.Mp2;
+    a2.wlayout = a.wlayout2;
+    if constexpr (BF16) {
+      if (pack_weight_v8_ok(a2)) {
+        pack_weight_v8(a2, static_cast<int>(blockIdx.x) - nw, nw2);
+        return;
+      }
+    }
+    pack_weight<T>(a2, static_cast<int>(blockIdx.x) - nw, nw2);
+    return;
+  }
   if (static_cast<int>(blockIdx.x) < nw) {
     if constexpr (BF16) {
       if (pack_weight_v8_ok(a)) {
@@ -237,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a, int nx, in
     pack_weight<T>(a, static_cast<int>(blockIdx.x), nw);
     return;
   }
-  const int bx = static_cast<int>(blockIdx.x) - nw;
+  const int bx = static_cast<int>(blockIdx.x) - nw - nw2;
   const int per_img = s_tiles * c_tiles;
   const int b = bx / per_img;
   const int r = bx - b * per_img;
@@ -585,6 +605,7 @@ static const VariantInfo kVariants[V_COUNT] = {
     {"box_bf16_m256", 1, 256, 0, 32, 1},
     {"direct_f32", 0, 64, 64, 1, 0},
     {"direct_bf16", 1, 64, 64, 1, 0},
+    {"om_bf16", 1, 32, 32, 32, 1},
 };
 
 const VariantInfo& variant_info(int v) { return kVariants[v]; }
@@ -602,9 +623,16 @@ hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream) {
   const bool wv8 = vi.is_bf16 && a.wlayout == 1 && a.KK == 9 && a.Cin % 8 == 0 &&
                    reinterpret_cast<uintptr_t>(a.w) % 16 == 0;   // pack_weight_v8_ok
   const int wunits = wv8 ? a.Mp * (a.Cp / 8) : a.Mp * a.Cp;
-  const int nw = min((wunits + kThreads - 1) / kThreads, 1024);
-  const dim3 grid(nx + nw);
+  const int nw = a.w != nullptr ? min((wunits + kThreads - 1) / kThreads, 1024) : 0;
   StageArgs sa = a;
+  sa.nw2 = 0;
+  if (a.w2 != nullptr) {
+    const bool wv8b = vi.is_bf16 && a.wlayout2 == 1 && a.KK == 9 && a.Cin % 8 == 0 &&
+                      reinterpret_cast<uintptr_t>(a.w2) % 16 == 0;
+    const int wunits2 = wv8b ? a.Mp2 * (a.Cp / 8) : a.Mp2 * a.Cp;
+    sa.nw2 = min((wunits2 + kThreads - 1) / kThreads, 1024);
+  }
+  const dim3 grid(nx + nw + sa.nw2);
   void* args[] = {&sa, const_cast<int*>(&nx), const_cast<int*>(&s_tiles), const_cast<int*>(&c_tiles)};
   const void* fn;
   if (vi.is_bf16)

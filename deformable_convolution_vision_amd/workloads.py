@@ -105,6 +105,10 @@ WORKLOADS = {
     # 2 x 2 samples per bin, one offset per bin shared by all classes, and a mask
     "psroi_c4": Workload("psroi_c4", "bf16", 2, 3969, 50, 84, 81, 7, 1, 0, 1, 7, 7,
                          offset="normal:0.1", mask="sigmoid", bias=None, seed=1010, op="ps_roi_pool"),
+    # the c4 layer with its offset/mask branch in one call (the branch's weight and bias
+    # are c4_om's, the layer's weight c4's; x is c4_om's)
+    "c4_layer": Workload("c4_layer", "bf16", 2, 256, 100, 168, 256, 3, 2, 1, 1, 50, 84,
+                         offset="normal:1", mask="sigmoid", bias=None, seed=1003, op="layer"),
     "c4_om": Workload("c4_om", "bf16", 2, 256, 100, 168, 27, 3, 2, 1, 1, 50, 84,
                       offset="normal:1", mask=None, bias="normal:0.1", seed=1006, op="offset_mask"),
     # the c4 layer on inputs whose four corners nearly cancel: x of alternating sign
@@ -114,7 +118,7 @@ WORKLOADS = {
                           offset="frac:2:0.45:0.55", mask="sigmoid", bias=None, seed=1009,
                           x="checker:0.01", weight="kaiming_abs"),
 }
-ORDER = ["tiny", "single224", "c3", "c4", "c5", "c4_g4", "c4_om", "c4_bwd", "roi_c4", "psroi_c4"]
+ORDER = ["tiny", "single224", "c3", "c4", "c5", "c4_g4", "c4_om", "c4_layer", "c4_bwd", "roi_c4", "psroi_c4"]
 
 
 def _draw(kind: str, shape, g: torch.Generator) -> torch.Tensor:

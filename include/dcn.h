@@ -177,6 +177,23 @@ int dcn_offset_mask_workspace_bytes(const dcn_desc* desc, size_t* bytes);
 int dcn_offset_mask(const dcn_desc* desc, const void* x, const void* weight_om, const void* bias_om,
                     void* offset, void* mask, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The whole DCNv2 layer in one call: the offset/mask branch (as dcn_offset_mask) and
+ * then the deformable convolution (as dcn_forward) on the offsets and mask it produced,
+ * off one staged channels-last copy of x: x is staged once and both weights are
+ * repacked by the same launch (the branch is a convolution of the same input feature
+ * map: csdn.net tags page "可变形卷积：Deformable ConvNets", DCNv2 section 3.2).
+ * Arguments as for dcn_offset_mask and dcn_forward; offset [B][2*G*K*K][Ho][Wo] and
+ * mask [B][G*K*K][Ho][Wo] are written as outputs (the backward needs them) and read by
+ * the convolution.  desc->out_channels is the layer's.  Workspace (256-byte aligned):
+ * dcn_layer_workspace_bytes.  Where the two paths would stage x differently (for
+ * example the direct kernel, which stages nothing), the two calls run one after the
+ * other, each on its own part of the workspace.  Errors as for dcn_forward, all
+ * checked before any launch. */
+int dcn_layer_workspace_bytes(const dcn_desc* desc, size_t* bytes);
+int dcn_layer_forward(const dcn_desc* desc, const void* x, const void* weight_om, const void* bias_om,
+                      const void* weight, const void* bias, void* offset, void* mask, void* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Gradients of dcn_forward (the gradient equation of the csdn.net tags page
  * "可变形卷积：Deformable ConvNets", part "Deformable Convolutional Networks",
  * section on deformable convolution: the offset gradient runs through the

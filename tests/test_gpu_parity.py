@@ -439,3 +439,62 @@ def test_binding_rejects_bad_out_and_workspace():
     ws32 = torch.empty((nb + 3) // 4, dtype=torch.float32, device="cuda")
     out = dcn.deform_conv2d(*args, mask=g["mask"], out=good, workspace=ws32)
     assert torch.equal(out, run_hip(w, g))
+
+
+LAYER_SHAPES = [  # B, Cin, H, W, Cout, K, s, p, d, G
+    (2, 64, 17, 19, 70, 3, 1, 1, 1, 1),
+    (1, 256, 30, 34, 256, 3, 2, 1, 1, 1),
+    (2, 48, 11, 9, 33, 3, 1, 2, 2, 3),
+    (2, 16, 9, 10, 24, 1, 1, 0, 1, 1),
+    (1, 3, 12, 14, 8, 3, 1, 1, 1, 1),
+    (1, 128, 15, 21, 130, 3, 2, 1, 1, 4),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", LAYER_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_layer_forward(shape, dtype):
+    """dcn_layer_forward (branch and deformable convolution off one staged x): offsets
+    and mask against the oracle's branch, the output against the oracle's forward on the
+    offsets and mask the call produced, and bit for bit against dcn_forward on them."""
+    B, Cin, H, W, Cout, K, s, p, d, G = shape
+    seed = zlib.crc32(repr(shape).encode()) % 1000
+    w_om, inp_om = _offset_mask_case(dtype, (B, Cin, H, W, K, s, p, d, G), seed)
+    wd = make("layer", dtype, B, Cin, H, W, Cout, K, s, p, d, seed=seed + 1, groups=G)
+    inp = generate(wd)
+    inp["x"] = inp_om["x"]
+    g = to_gpu(inp)
+    go = to_gpu(inp_om)
+    desc = dcn.make_desc(B, Cin, H, W, Cout, K, s, p, d, dcn.BF16 if dtype == "bf16" else dcn.F32, G)
+    print(f"[gpu-test] layer {shape} {dtype}: {dcn.dcn_plan_describe(desc)}", flush=True)
+    out, off, msk = dcn.deform_conv2d_layer(g["x"], go["weight"], go["bias"], g["weight"], g["bias"], s, p, d,
+                                            offset_groups=G)
+    torch.cuda.synchronize()
+    o_ref, m_ref, a = oracle.offset_mask(inp["x"], inp_om["weight"], inp_om["bias"], s, p, d, groups=G)
+    n_off = o_ref.shape[1]
+    check(off.float().cpu().numpy(), o_ref, a[:, :n_off], TOL[dtype], "layer offsets")
+    round_err = 2.0 ** -9 if dtype == "bf16" else 1e-6
+    err = np.abs(msk.float().cpu().numpy() - m_ref)
+    assert np.all(err <= TOL[dtype] * a[:, n_off:] / 4 + round_err), "layer mask"
+    y, ay = oracle.forward(inp["x"], off.cpu(), inp["weight"], inp["bias"], s, p, d, mask=msk.cpu())
+    check(out.float().cpu().numpy(), y, ay, TOL[dtype], "layer output")
+    ref = dcn.deform_conv2d(g["x"], off, g["weight"], g["bias"], s, p, d, mask=msk)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), "dcn_layer_forward differs from dcn_forward on its own offsets and mask"
+
+
+def test_layer_forward_c4():
+    """The c4 layer with its branch (256 -> 27 channels, then 256 -> 256) in one call,
+    every output against the oracle."""
+    w_om, w = WORKLOADS["c4_om"], WORKLOADS["c4"]
+    inp_om, inp = generate(w_om), generate(w)
+    inp["x"] = inp_om["x"]
+    g, go = to_gpu(inp), to_gpu(inp_om)
+    out, off, msk = dcn.deform_conv2d_layer(g["x"], go["weight"], go["bias"], g["weight"], None, 2, 1, 1)
+    torch.cuda.synchronize()
+    o_ref, m_ref, a = oracle.offset_mask(inp["x"], inp_om["weight"], inp_om["bias"], 2, 1, 1, threads=0)
+    check(off.float().cpu().numpy(), o_ref, a[:, :18], TOL["bf16"], "c4 layer offsets")
+    assert np.all(np.abs(msk.float().cpu().numpy() - m_ref) <= TOL["bf16"] * a[:, 18:] / 4 + 2.0 ** -9)
+    y, ay = oracle.forward(inp["x"], off.cpu(), inp["weight"], None, 2, 1, 1, mask=msk.cpu(), threads=0)
+    worst = check(out.float().cpu().numpy(), y, ay, TOL["bf16"], "c4 layer output")
+    print(f"[gpu-test] max relative error {worst:.2e}", flush=True)
