@@ -126,7 +126,8 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
           if (TW < 1 || (TH * TW + 15) / 16 != fn) continue;
           if (want_fn && (fn != want_fn || TH != want_th || TW != want_tw)) continue;
           const int64_t bh0 = (TH - 1) * s + (K - 1) * dil + 2, bw0 = (TW - 1) * s + (K - 1) * dil + 2;
-          if (bh0 * bw0 > box_px) continue;
+          // the kernel clips the box to one pixel around the image
+          if (std::min<int64_t>(bh0, d->height + 2) * std::min<int64_t>(bw0, d->width + 2) > box_px) continue;
           const int64_t ty = (Ho + TH - 1) / TH, tx = (Wo + TW - 1) / TW;
           const int64_t tiles = d->batch * ty * tx * m_tiles;
           if (tiles > (int64_t(1) << 30)) continue;

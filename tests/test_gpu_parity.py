@@ -325,7 +325,7 @@ def test_offset_groups_box_tiles(variant, tile, roles, monkeypatch):
 
 @pytest.mark.parametrize("pw", ["4", "8"])
 @pytest.mark.parametrize("variant,tile", [("box_bf16_m256", "4,5,10"), ("box_bf16_m256", "6,7,13"),
-                                          ("box_bf16_m128", "8,8,16"), ("box_bf16_m128", "10,9,17")])
+                                          ("box_bf16_m128", "8,8,16"), ("box_bf16_m128", "10,10,15")])
 def test_box_producer_waves(variant, tile, pw, monkeypatch):
     """The box kernel with four and with eight producer waves, paired roles."""
     monkeypatch.setenv("DCN_VARIANT", variant)
