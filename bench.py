@@ -468,9 +468,11 @@ def bench_roi(w, steps: int, warmup: int):
     sp = stream.cuda_stream
     if ps:
         desc = dcn.PsRoiDesc(w.B, C_out, w.H, w.W, R, k, S, 1, scale, gamma, dt, 0)
+        nb = dcn.dcn_ps_roi_pool_workspace_bytes(desc)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
 
         def step():
-            dcn.dcn_ps_roi_pool(desc, g["x"], g["rois"], g["offset"], g["mask"], out, stream)
+            dcn.dcn_ps_roi_pool(desc, g["x"], g["rois"], g["offset"], g["mask"], out, ws if nb else None, nb, stream)
     else:
         desc = dcn.RoiDesc(w.B, w.Cin, w.H, w.W, R, k, S, scale, gamma, dt, 0)
         nb = dcn.dcn_roi_pool_workspace_bytes(desc)
@@ -511,7 +513,8 @@ def bench_roi(w, steps: int, warmup: int):
         what = (f"{w.name}: deformable position-sensitive RoI pooling of {w.Cin} score maps ({C_out} classes x "
                 f"{k}x{k} bins) [{w.B},{w.Cin},{w.H},{w.W}], {R} RoIs ({per_img} per image, sides 32-512 px of "
                 f"800x1344, scale 1/16), {S}x{S} samples, one offset per bin, mask")
-        plan, kname = "dcn_ps_roi_pool: one pooling launch", "roi_pool_kernel (position-sensitive)"
+        plan, kname = ("dcn_ps_roi_pool: staging launch (score maps channels-last, bin-major) + pooling launch",
+                       "roi_pool_cl_kernel (position-sensitive)")
     else:
         what = (f"{w.name}: deformable RoI pooling of x [{w.B},{w.Cin},{w.H},{w.W}], {R} RoIs ({per_img} per image, "
                 f"sides 32-512 px of 800x1344, scale 1/16), {k}x{k} bins, {S}x{S} samples, offsets and mask")

@@ -115,8 +115,10 @@ def load_library() -> ctypes.CDLL:
     lib.dcn_roi_pool.restype = ctypes.c_int
     lib.dcn_roi_pool_workspace_bytes.argtypes = [ctypes.POINTER(RoiDesc), ctypes.POINTER(ctypes.c_size_t)]
     lib.dcn_roi_pool_workspace_bytes.restype = ctypes.c_int
-    lib.dcn_ps_roi_pool.argtypes = [ctypes.POINTER(PsRoiDesc), P, P, P, P, P, P]
+    lib.dcn_ps_roi_pool.argtypes = [ctypes.POINTER(PsRoiDesc), P, P, P, P, P, P, S, P]
     lib.dcn_ps_roi_pool.restype = ctypes.c_int
+    lib.dcn_ps_roi_pool_workspace_bytes.argtypes = [ctypes.POINTER(PsRoiDesc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.dcn_ps_roi_pool_workspace_bytes.restype = ctypes.c_int
     for name in ("dcn_output_hw", "dcn_workspace_bytes", "dcn_forward", "dcn_forward_staged", "dcn_stage"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -445,10 +447,19 @@ def deform_roi_pool(input, rois, offset=None, mask=None, output_size=7, sampling
     return out
 
 
-def dcn_ps_roi_pool(desc: PsRoiDesc, x, rois, offset, mask, out, stream=None) -> None:
+def dcn_ps_roi_pool_workspace_bytes(desc: PsRoiDesc) -> int:
+    n = ctypes.c_size_t()
+    rc = load_library().dcn_ps_roi_pool_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    if rc != OK:
+        raise DcnError(rc, "dcn_ps_roi_pool_workspace_bytes")
+    return n.value
+
+
+def dcn_ps_roi_pool(desc: PsRoiDesc, x, rois, offset, mask, out, workspace, workspace_bytes: int,
+                    stream=None) -> None:
     """Raw call: tensors (or integer device addresses) laid out as dcn.h states."""
     rc = load_library().dcn_ps_roi_pool(ctypes.byref(desc), _ptr(x), _ptr(rois), _ptr(offset), _ptr(mask), _ptr(out),
-                                        _stream(stream))
+                                        _ptr(workspace), workspace_bytes, _stream(stream))
     if rc != OK:
         raise DcnError(rc, "dcn_ps_roi_pool")
 
@@ -486,8 +497,10 @@ def deform_ps_roi_pool(input, rois, offset=None, mask=None, output_size=7, sampl
     desc = PsRoiDesc(B, C, H, W, R, k, int(sampling_ratio), G, float(spatial_scale), float(gamma),
                      _DTYPES[input.dtype], 0)
     out = torch.empty((R, C, k, k), dtype=input.dtype, device=input.device)
+    nbytes = dcn_ps_roi_pool_workspace_bytes(desc)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=input.device) if nbytes else None
     with torch.cuda.device(input.device):
-        dcn_ps_roi_pool(desc, input, rois, offset, mask, out)
+        dcn_ps_roi_pool(desc, input, rois, offset, mask, out, ws, nbytes)
     return out
 
 

@@ -152,12 +152,17 @@ __global__ __launch_bounds__(kRT) void roi_pool_kernel(RoiArgs a) {
   out[e] = st<T>(m * acc * inv * inv);
 }
 
-// bf16 with a channels-last copy xs [B][H][W][Cp] of the input: one workgroup per (RoI,
-// block of 64 channels).  A unit of work is (bin, 8 channels): eight neighbouring lanes
-// take the eight 8-channel groups of one bin, so each corner is one 128-byte read of
-// 64 channels of one pixel.  The k*k x 64 results go through LDS, channel-major, and are
-// stored as one contiguous run of out[r][c0 .. c0+63][k][k].
-__global__ __launch_bounds__(kRT) void roi_pool_cl_kernel(RoiArgs a, const uint16_t* xs, int Cp) {
+// bf16 with a channels-last copy of the input: one workgroup per (RoI, block of 64
+// channels).  A unit of work is (bin, 8 channels): eight neighbouring lanes take the
+// eight 8-channel groups of one bin, so each corner is one 128-byte read of 64 channels
+// of one pixel.  The k*k x 64 results go through LDS, channel-major, and are stored as
+// one contiguous run of out[r][c0 .. c0+63][k][k].
+// Plain pooling: xs [B][H][W][Cp] (px_stride = Cp, bin_stride = 0).  Position-sensitive
+// pooling: xs [B][H][W][k*k][Cp] (px_stride = k*k*Cp, bin_stride = Cp), bin (i, j)'s
+// score maps of every output channel contiguous, with one offset group or (C/G) % 8 == 0
+// so that each 8-channel group lies in one offset group.
+__global__ __launch_bounds__(kRT) void roi_pool_cl_kernel(RoiArgs a, const uint16_t* xs, int px_stride,
+                                                          int bin_stride) {
   extern __shared__ uint16_t tile[];   // [64 channels][bin], stride k*k + 1
   const int ncb = (a.C + 63) / 64;
   const int r = blockIdx.x / ncb, c0 = (blockIdx.x - r * ncb) * 64;
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(kRT) void roi_pool_cl_kernel(RoiArgs a, const uint1
   geo.bw = geo.w / static_cast<float>(a.k);
   geo.inv_s = 1.f / static_cast<float>(a.S);
   const float inv = 1.f / static_cast<float>(a.S);
-  const uint16_t* img = xs + static_cast<size_t>(b) * a.H * a.W * Cp;
+  const uint16_t* img = xs + static_cast<size_t>(b) * a.H * a.W * px_stride;
   for (int u = threadIdx.x; u < kk * 8; u += blockDim.x) {
     const int bin = u >> 3, gq = u & 7, c = c0 + 8 * gq;
     const int i = bin / a.k, j = bin - (bin / a.k) * a.k;
@@ -189,8 +194,9 @@ __global__ __launch_bounds__(kRT) void roi_pool_cl_kernel(RoiArgs a, const uint1
       m = 1.f;
       if (a.offset != nullptr) {
         const uint16_t* off = static_cast<const uint16_t*>(a.offset);
-        g.dy = a.gamma * g.h * ld(off, ((static_cast<size_t>(r) * 2 + 0) * a.k + i) * a.k + j);
-        g.dx = a.gamma * g.w * ld(off, ((static_cast<size_t>(r) * 2 + 1) * a.k + i) * a.k + j);
+        const int og = c / (a.C / a.G);   // offset group of the 8 channels
+        g.dy = a.gamma * g.h * ld(off, ((static_cast<size_t>(r) * 2 * a.G + 2 * og) * a.k + i) * a.k + j);
+        g.dx = a.gamma * g.w * ld(off, ((static_cast<size_t>(r) * 2 * a.G + 2 * og + 1) * a.k + i) * a.k + j);
       }
       if (a.mask != nullptr) m = ld(static_cast<const uint16_t*>(a.mask), (static_cast<size_t>(r) * a.k + i) * a.k + j);
       for (int su = 0; su < a.S; ++su) {
@@ -207,7 +213,8 @@ __global__ __launch_bounds__(kRT) void roi_pool_cl_kernel(RoiArgs a, const uint1
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int yy = in[q] ? y0 + (q >> 1) : 0, xc = in[q] ? x0 + (q & 1) : 0;
-            cv[q] = *reinterpret_cast<const uint4*>(img + (static_cast<size_t>(yy) * a.W + xc) * Cp + c);
+            cv[q] = *reinterpret_cast<const uint4*>(img + (static_cast<size_t>(yy) * a.W + xc) * px_stride +
+                                                    bin * bin_stride + c);
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -229,6 +236,53 @@ __global__ __launch_bounds__(kRT) void roi_pool_cl_kernel(RoiArgs a, const uint1
   const int nch = min(64, a.C - c0);
   uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(r) * a.C + c0) * kk;
   for (int e = threadIdx.x; e < nch * kk; e += blockDim.x) out[e] = tile[(e / kk) * ts + e % kk];
+}
+
+// Staging of the score maps for position-sensitive pooling: x [B][C*k*k][H*W] (bf16)
+// -> xs [B][H*W][k*k][Cp] with Cp = C rounded up to 8 (zeros past C), so that the
+// C maps of one bin at one pixel are contiguous.  One workgroup per (image, bin, block
+// of 64 pixels, block of 64 output channels), transposed through LDS: reads are two
+// pixels (4 bytes) of one map, writes 16-byte vectors of 8 channels of one pixel.
+constexpr int kPsPx = 64;
+__global__ __launch_bounds__(kRT) void ps_stage_kernel(const uint16_t* x, uint16_t* xs, int B, int C, int KK, int HW,
+                                                       int Cp, int ptiles, int ctiles) {
+  __shared__ uint32_t t[64][kPsPx / 2 + 1];   // [channel][pixel pair]
+  int e = blockIdx.x;
+  const int ct = e % ctiles;
+  e /= ctiles;
+  const int pt = e % ptiles;
+  e /= ptiles;
+  const int bin = e % KK, b = e / KK;
+  const int c0 = ct * 64, p0 = pt * kPsPx;
+  const int tid = threadIdx.x;
+  // 64 channels x 32 pixel pairs
+  for (int q = tid; q < 64 * (kPsPx / 2); q += kRT) {
+    const int cl = q / (kPsPx / 2), pp = q - (q / (kPsPx / 2)) * (kPsPx / 2);
+    const int c = c0 + cl, p = p0 + 2 * pp;
+    uint32_t v = 0u;
+    if (c < C && p < HW) {
+      const uint16_t* src = x + (static_cast<size_t>(b) * C * KK + static_cast<size_t>(c) * KK + bin) * HW + p;
+      // H*W even (checked on the host): a pair never straddles the end of a map
+      v = *reinterpret_cast<const uint32_t*>(src);
+    }
+    t[cl][pp] = v;
+  }
+  __syncthreads();
+  // 64 pixels x 8 groups of 8 channels
+  for (int q = tid; q < kPsPx * 8; q += kRT) {
+    const int pl = q >> 3, g = q & 7;
+    const int p = p0 + pl, c = c0 + 8 * g;
+    if (p >= HW || c >= Cp) continue;
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = t[8 * g + i][pl >> 1];
+    const uint32_t sh = (pl & 1) ? 16u : 0u;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = ((h[2 * i] >> sh) & 0xffffu) | (((h[2 * i + 1] >> sh) & 0xffffu) << 16);
+    *reinterpret_cast<uint4*>(xs + ((static_cast<size_t>(b) * HW + p) * KK + bin) * Cp + c) =
+        make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 }  // namespace
@@ -313,8 +367,8 @@ extern "C" int dcn_roi_pool(const dcn_roi_desc* d, const void* x, const float* r
     sa.wlayout = 0;
     if (dcn::launch_stage(dcn::V_TILE_BF16_M64_N64, sa, stream) != hipSuccess) return DCN_E_HIP;
     const uint16_t* xs = static_cast<const uint16_t*>(workspace);
-    int Cp = sa.Cp;
-    void* cargs[] = {&a, &xs, &Cp};
+    int px_stride = sa.Cp, bin_stride = 0;
+    void* cargs[] = {&a, &xs, &px_stride, &bin_stride};
     const unsigned grid = static_cast<unsigned>(a.R * ((a.C + 63) / 64));
     const size_t lds = static_cast<size_t>(64) * (a.k * a.k + 1) * 2;
     return hipLaunchKernel(reinterpret_cast<const void*>(&dcn::roi_pool_cl_kernel), dim3(grid), dim3(dcn::kRT),
@@ -353,12 +407,41 @@ int ps_roi_check(const dcn_ps_roi_desc* d) {
 
 }  // namespace
 
+namespace {
+
+// the staged path of position-sensitive pooling: bf16, k <= 16, H*W even, and every
+// 8-channel group in one offset group (one group, or C/G a multiple of 8)
+bool ps_staged(const dcn_ps_roi_desc* d) {
+  const int64_t G = d->offset_groups > 1 ? d->offset_groups : 1;
+  return d->dtype == DCN_BF16 && d->pooled_size <= 16 && (d->height * d->width) % 2 == 0 &&
+         (G == 1 || (d->out_channels / G) % 8 == 0);
+}
+int64_t ps_cp(const dcn_ps_roi_desc* d) { return (d->out_channels + 7) / 8 * 8; }
+
+}  // namespace
+
+extern "C" int dcn_ps_roi_pool_workspace_bytes(const dcn_ps_roi_desc* d, size_t* bytes) {
+  if (bytes == nullptr) return DCN_E_ARG;
+  const int rc = ps_roi_check(d);
+  if (rc != DCN_OK) return rc;
+  const int64_t kk = d->pooled_size * d->pooled_size;
+  *bytes = (ps_staged(d) && d->num_rois > 0)
+               ? static_cast<size_t>(d->batch * d->height * d->width) * static_cast<size_t>(kk * ps_cp(d)) * 2
+               : 0;
+  return DCN_OK;
+}
+
 extern "C" int dcn_ps_roi_pool(const dcn_ps_roi_desc* d, const void* x, const float* rois, const void* offset,
-                               const void* mask, void* out, hipStream_t stream) {
+                               const void* mask, void* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   const int rc = ps_roi_check(d);
   if (rc != DCN_OK) return rc;
   if (d->num_rois == 0) return DCN_OK;
   if (x == nullptr || rois == nullptr || out == nullptr) return DCN_E_ARG;
+  size_t need = 0;
+  dcn_ps_roi_pool_workspace_bytes(d, &need);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+    return DCN_E_WORKSPACE;
   dcn::RoiArgs a{};
   a.x = x;
   a.rois = rois;
@@ -375,7 +458,30 @@ extern "C" int dcn_ps_roi_pool(const dcn_ps_roi_desc* d, const void* x, const fl
   a.scale = d->spatial_scale;
   a.gamma = d->gamma;
   a.ps = 1;
-  a.G = d->offset_groups > 1 ? d->offset_groups : 1;
+  a.G = d->offset_groups > 1 ? static_cast<int>(d->offset_groups) : 1;
+  if (need > 0) {
+    // the score maps channels-last, bin-major, then the pooling from that copy
+    const int KK = a.k * a.k, HW = a.H * a.W, Cp = static_cast<int>(ps_cp(d));
+    const int ptiles = (HW + dcn::kPsPx - 1) / dcn::kPsPx, ctiles = (Cp + 63) / 64;
+    const uint16_t* xin = static_cast<const uint16_t*>(x);
+    uint16_t* xs = static_cast<uint16_t*>(workspace);
+    int B = a.B, C = a.C;
+    void* sargs[] = {&xin, &xs, &B, &C, const_cast<int*>(&KK), const_cast<int*>(&HW), const_cast<int*>(&Cp),
+                     const_cast<int*>(&ptiles), const_cast<int*>(&ctiles)};
+    const unsigned sgrid = static_cast<unsigned>(a.B * KK * ptiles * ctiles);
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&dcn::ps_stage_kernel), dim3(sgrid), dim3(dcn::kRT), sargs, 0,
+                        stream) != hipSuccess)
+      return DCN_E_HIP;
+    const uint16_t* xsc = xs;
+    int px_stride = KK * Cp, bin_stride = Cp;
+    void* cargs[] = {&a, &xsc, &px_stride, &bin_stride};
+    const unsigned grid = static_cast<unsigned>(a.R * ((a.C + 63) / 64));
+    const size_t lds = static_cast<size_t>(64) * (KK + 1) * 2;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&dcn::roi_pool_cl_kernel), dim3(grid), dim3(dcn::kRT),
+                           cargs, lds, stream) == hipSuccess
+               ? DCN_OK
+               : DCN_E_HIP;
+  }
   void* args[] = {&a};
   const long long n = static_cast<long long>(a.R) * a.C * a.k * a.k;
   const void* fn = d->dtype == DCN_BF16 ? reinterpret_cast<const void*>(&dcn::roi_pool_kernel<uint16_t>)

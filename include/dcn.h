@@ -269,7 +269,11 @@ int dcn_roi_pool(const dcn_roi_desc* desc, const void* x, const float* rois, con
  * offset[r, 2g + {0: rows, 1: columns}, i, j] for output channel group g = c / (C/G)
  * (G = offset_groups, 0 or 1 meaning one offset per bin shared by every channel).
  * x [B, C*k*k, H, W], offset [R, 2G, k, k] or NULL, mask [R, k, k] or NULL,
- * out [R, C, k, k] in desc->dtype; rois [R, 5] float32.  No workspace.  Errors as for
+ * out [R, C, k, k] in desc->dtype; rois [R, 5] float32.  bf16 with k <= 16, H*W even
+ * and G = 1 or (C/G) % 8 == 0 first writes the score maps channels-last and bin-major,
+ * [B][H][W][k*k][round_up(C, 8)], into the workspace (256-byte aligned,
+ * dcn_ps_roi_pool_workspace_bytes; 0 bytes otherwise), so that a bin's maps of 8
+ * channels are one 16-byte read; the others read x directly.  Errors as for
  * dcn_roi_pool (DCN_E_ARG also when C % G != 0), all checked before any launch. */
 typedef struct dcn_ps_roi_desc {
   int64_t batch, out_channels, height, width;   /* x has out_channels * k * k channels */
@@ -282,8 +286,9 @@ typedef struct dcn_ps_roi_desc {
   int32_t dtype;
   int32_t reserved;      /* 0 */
 } dcn_ps_roi_desc;
+int dcn_ps_roi_pool_workspace_bytes(const dcn_ps_roi_desc* desc, size_t* bytes);
 int dcn_ps_roi_pool(const dcn_ps_roi_desc* desc, const void* x, const float* rois, const void* offset,
-                    const void* mask, void* out, hipStream_t stream);
+                    const void* mask, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 const char* dcn_status_str(int status);
 

@@ -357,13 +357,24 @@ def test_ps_roi_pool_argument_checks(lib):
                  ("offset_groups", -1), ("offset_groups", 4), ("spatial_scale", float("nan")),
                  ("gamma", float("inf"))]:
         d = dcn.PsRoiDesc(**{**good, k: v})
-        assert f(ctypes.byref(d), fake, fake, None, None, fake, None) == dcn.E_ARG, k
+        assert f(ctypes.byref(d), fake, fake, None, None, fake, fake, 1 << 30, None) == dcn.E_ARG, k
     d = dcn.PsRoiDesc(**{**good, "dtype": 7})
-    assert f(ctypes.byref(d), fake, fake, None, None, fake, None) == dcn.E_UNSUPPORTED
+    assert f(ctypes.byref(d), fake, fake, None, None, fake, fake, 1 << 30, None) == dcn.E_UNSUPPORTED
     d = dcn.PsRoiDesc(**good)
     for x, r, o in [(None, fake, fake), (fake, None, fake), (fake, fake, None)]:
-        assert f(ctypes.byref(d), x, r, None, None, o, None) == dcn.E_ARG
+        assert f(ctypes.byref(d), x, r, None, None, o, fake, 1 << 30, None) == dcn.E_ARG
     d = dcn.PsRoiDesc(**{**good, "num_rois": 0})   # nothing to launch
-    assert f(ctypes.byref(d), None, None, None, None, None, None) == dcn.OK
+    assert f(ctypes.byref(d), None, None, None, None, None, None, 0, None) == dcn.OK
     d = dcn.PsRoiDesc(**{**good, "out_channels": 3 << 16, "height": 1 << 10, "width": 1 << 10})
-    assert f(ctypes.byref(d), fake, fake, None, None, fake, None) == dcn.E_UNSUPPORTED
+    assert f(ctypes.byref(d), fake, fake, None, None, fake, fake, 1 << 30, None) == dcn.E_UNSUPPORTED
+    # bf16, k <= 16, H*W even, C/G a multiple of 8: the bin-major copy of the maps
+    d = dcn.PsRoiDesc(**{**good, "out_channels": 16, "offset_groups": 2})
+    nb = dcn.dcn_ps_roi_pool_workspace_bytes(d)
+    assert nb == 2 * 10 * 12 * 49 * 16 * 2
+    for ws, n in [(None, nb), (0x20000, nb - 1), (0x20010, nb)]:
+        assert f(ctypes.byref(d), fake, fake, None, None, fake, ws, n, None) == dcn.E_WORKSPACE
+    assert dcn.dcn_ps_roi_pool_workspace_bytes(dcn.PsRoiDesc(**{**good, "out_channels": 6})) == 0   # C/G = 2
+    assert dcn.dcn_ps_roi_pool_workspace_bytes(dcn.PsRoiDesc(**{**good, "out_channels": 81, "offset_groups": 1})) == \
+        2 * 10 * 12 * 49 * 88 * 2
+    assert dcn.dcn_ps_roi_pool_workspace_bytes(dcn.PsRoiDesc(**{**good, "out_channels": 16, "offset_groups": 2,
+                                                                "dtype": dcn.F32})) == 0

@@ -102,6 +102,11 @@ PS_CASES = [
     ("ps_one_sample", 1, 3, 9, 9, 6, 4, 1, 1.0, 0.2, 1, True),
     ("ps_four_samples_large_gamma", 1, 2, 12, 14, 10, 5, 4, 1.0, 1.0, 2, True),
     ("ps_k1", 2, 7, 10, 10, 5, 1, 3, 1.0, 0.1, 7, True),
+    # the bf16 staged path (bin-major channels-last maps): one offset group with a
+    # partial 8-channel group and a partial 64-channel block, C/G a multiple of 8
+    ("ps_staged_c81", 2, 81, 12, 14, 7, 7, 2, 0.5, 0.1, 1, True),
+    ("ps_staged_groups", 1, 24, 20, 15, 9, 3, 2, 1.0, 0.2, 3, True),
+    ("ps_staged_no_offsets", 2, 16, 17, 24, 9, 4, 1, 1.0, 0.1, 0, False),
 ]
 
 
