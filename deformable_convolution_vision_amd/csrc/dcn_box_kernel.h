@@ -577,6 +577,9 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
     auto step = [&](int c, AFrag& af, const BFrag& bc, BFrag& bn) __attribute__((always_inline)) {
       table_work(c, std::integral_constant<int, 0>());
       bn = read_b(c + 1);
+      // the column reads go out before the multiplies, so their latency hides behind them
+      // (scheduled after, the barrier below would wait for the whole LDS round trip)
+      __builtin_amdgcn_sched_barrier(0);
       mma(af, bc);
       af = load_a(min(c + 2 * G, S - 1));
       table_work(c, std::integral_constant<int, 1>());
@@ -586,6 +589,7 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
       if (c >= S) return;
       table_work(c, std::integral_constant<int, 0>());
       if (c + 1 < S) bn = read_b(c + 1);
+      __builtin_amdgcn_sched_barrier(0);
       mma(af, bc);
       if (c + 2 * G < S) af = load_a(c + 2 * G);
       table_work(c, std::integral_constant<int, 1>());
@@ -754,7 +758,9 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
       }
     };
     // the global-path corner vectors of the step (chunk cc, tap k) whose table entries are in f
-    auto load_g = [&](int cc, int k, const PSet& f, int tb) __attribute__((always_inline)) {
+    // (glob false: the wave has no global-path sample in any tap, and nothing is loaded)
+    auto load_g = [&](int cc, int k, const PSet& f, int tb, auto glob) __attribute__((always_inline)) {
+      if constexpr (!decltype(glob)::value) return;
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
         if (GUNITS % PTH == 0 || pw * 64 + g * PTH < GUNITS) {
@@ -777,7 +783,7 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
       }
     };
     // interpolate and store into column buffer s % 3
-    auto finish = [&](int s, const PSet& f) __attribute__((always_inline)) {
+    auto finish = [&](int s, const PSet& f, auto glob) __attribute__((always_inline)) {
       unsigned char* cdst = col + (s % kColBufs) * NT * kCOLB;
 #pragma unroll
       for (int g = 0; g < GU; ++g) {
@@ -786,12 +792,14 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
           const int p = u >> UPS_SH, sub = u & (UPS - 1);
           const CEw& ce = f.ce[g];
           QV c0 = f.q[g][0], c1 = f.q[g][1], c2 = f.q[g][2], c3 = f.q[g][3];
-          if (gfl[g]) {   // wave-uniform: some lane's sample takes the global-path corners
-            const bool o = ce_global(ce);
-            c0 = sel4(o, gq[g][0], c0);
-            c1 = sel4(o, gq[g][1], c1);
-            c2 = sel4(o, gq[g][2], c2);
-            c3 = sel4(o, gq[g][3], c3);
+          if constexpr (decltype(glob)::value) {
+            if (gfl[g]) {   // wave-uniform: some lane's sample takes the global-path corners
+              const bool o = ce_global(ce);
+              c0 = sel4(o, gq[g][0], c0);
+              c1 = sel4(o, gq[g][1], c1);
+              c2 = sel4(o, gq[g][2], c2);
+              c3 = sel4(o, gq[g][3], c3);
+            }
           }
           const QV r = interp8(c0, c1, c2, c3, ce.w);
           *reinterpret_cast<QV*>(cdst + p * kCOLB + sub * UB) = r;
@@ -824,7 +832,7 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
       //   3. interpolates step s+1 from corners read a step earlier and stores it;
       //   4. loads the global-path corners of step s+2.
       // The corner-table entries of all nine taps are in registers.
-      auto chunk9w = [&](int cc, auto parity) __attribute__((always_inline)) {
+      auto chunk9w = [&](int cc, auto parity, auto glob) __attribute__((always_inline)) {
         constexpr bool odd = decltype(parity)::value;
         const unsigned char* src = odd ? box1 : box0;
         unsigned char* dst = odd ? box0 : box1;
@@ -847,8 +855,8 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
           }
           if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
           const bool last = k == 8 && cc + 1 == nCC;   // no step s+1
-          if (!last) finish(cc * 9 + k + 1, s1);
-          load_g(k < 7 ? cc : cc + 1, (k + 2) % 9, s0, k < 7 ? t_cur : t_nxt);
+          if (!last) finish(cc * 9 + k + 1, s1, glob);
+          load_g(k < 7 ? cc : cc + 1, (k + 2) % 9, s0, k < 7 ? t_cur : t_nxt, glob);
           if constexpr (k == 6) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           // keep the corner reads and the column store in flight; the previous step's
           // store (older) is complete
@@ -869,8 +877,8 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
           PSet& cur = ((k + (odd ? 1 : 0)) & 1) == 0 ? X : Y;
           PSet& oth = ((k + (odd ? 1 : 0)) & 1) == 0 ? Y : X;
           if constexpr (k < 4) copy_part4(cc + 1, dst, kc);
-          finish(cc * 9 + k, cur);
-          if constexpr (k < 8) load_g(cc, k + 1, oth, t_cur);
+          finish(cc * 9 + k, cur, std::true_type());
+          if constexpr (k < 8) load_g(cc, k + 1, oth, t_cur, std::true_type());
           asm volatile("" ::: "memory");
           if constexpr (k + 1 < 9) read_q(src, oth);
           read_ce((k + 2) % 9, cur, k + 2 < 9 ? t_cur : t_nxt);
@@ -879,7 +887,7 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
             lds_barrier_dma();
             if (cc + 1 < nCC) {
               read_q(dst, oth);
-              load_g(cc + 1, 0, oth, t_nxt);
+              load_g(cc + 1, 0, oth, t_nxt, std::true_type());
             }
           } else {
             lds_barrier_keep<kKeep>();
@@ -887,22 +895,32 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
         });
       };
       if constexpr (GU == 1) {
-        read_ce(0, X, 0);
-        read_q(box0, X);
-        read_ce(1, Y, 0);
-        read_q(box0, Y);
-        load_g(0, 0, X, 0);
-        finish(0, X);          // column 0, before the loop
-        load_g(0, 1, Y, 0);
-        for (int cc = 0; cc < nCC; cc += 2) {
-          chunk9w(cc, std::false_type());
-          if (cc + 1 < nCC) chunk9w(cc + 1, std::true_type());
-        }
+        auto run = [&](auto glob) __attribute__((always_inline)) {
+          read_ce(0, X, 0);
+          read_q(box0, X);
+          read_ce(1, Y, 0);
+          read_q(box0, Y);
+          load_g(0, 0, X, 0, glob);
+          finish(0, X, glob);          // column 0, before the loop
+          load_g(0, 1, Y, 0, glob);
+          for (int cc = 0; cc < nCC; cc += 2) {
+            chunk9w(cc, std::false_type(), glob);
+            if (cc + 1 < nCC) chunk9w(cc + 1, std::true_type(), glob);
+          }
+        };
+        // A wave none of whose samples (all nine taps, one offset group) leaves the box
+        // runs the loop without the global path: no ballot, branch or select per step.
+        // Both versions pass the same barriers.
+        bool anyg = false;
+#pragma unroll
+        for (int k = 0; k < 9; ++k) anyg |= ce_r[k].off <= -3;
+        if (!GRP && __ballot(anyg) == 0) run(std::false_type());
+        else run(std::true_type());
       } else {
         read_ce(0, X, 0);
         read_ce(1, Y, 0);
         read_q(box0, X);
-        load_g(0, 0, X, 0);
+        load_g(0, 0, X, 0, std::true_type());
         for (int cc = 0; cc < nCC; cc += 2) {
           chunk9_two(cc, std::false_type());
           if (cc + 1 < nCC) chunk9_two(cc + 1, std::true_type());
@@ -919,8 +937,8 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
         for (int k = 0; k < KK; ++k) {
           read_ce(k, X, 0);
           read_q(src, X);
-          load_g(cc, k, X, 0);
-          finish(cc * KK + k, X);
+          load_g(cc, k, X, 0, std::true_type());
+          finish(cc * KK + k, X, std::true_type());
           if (k == KK - 1 && cc + 1 < nCC) __builtin_amdgcn_s_waitcnt(0);
           lds_barrier_dma();
         }
