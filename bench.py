@@ -38,14 +38,17 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16_mfma": 2516.6, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, TFLOP/s, GB/s
 CSRC = os.path.join(ROOT, "deformable_convolution_vision_amd", "csrc")
-KERNEL_SRCS = ("dcn_internal.h", "dcn_api.hip", "dcn_kernels.hip", "dcn_box.hip", "dcn_direct.hip")   # the forward kernels
+def _kernel_srcs():
+    """Every kernel and host source of the library (a change to any of them invalidates
+    the committed counter figures)."""
+    return tuple(sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".h"))))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_hash() -> str:
     """Hash of the kernel sources (the counter figures are valid only for these)."""
     h = hashlib.sha256()
-    for name in KERNEL_SRCS:
+    for name in _kernel_srcs():
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -61,7 +64,7 @@ def kernel_symbol(variant: str, plan: str, w) -> str:
         grp = re.search(r"offset groups=(\d+)", plan)
         grouped = "true" if grp and int(grp.group(1)) > 1 else "false"
         return (f"dcn_box_kernel<{int(m.group(2)) // 64}, {int(m.group(1)) // 16}, {9 if kk == 9 else 0}, "
-                f"{grouped}, {pw.group(1) if pw else 4}, false>")
+                f"{grouped}, {pw.group(1) if pw else 4}>")
     if variant.startswith("direct"):
         bf16 = "true" if variant.endswith("bf16") else "false"
         return f"dcn_direct_kernel<{bf16}, {kk}, {3 if (w.Cin == 3 and kk == 9) else 0}>"

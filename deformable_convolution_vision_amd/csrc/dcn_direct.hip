@@ -1,22 +1,20 @@
 // dcn_direct.hip -- gfx950 kernel for deformable convolutions with a tiny reduction
 // (at most 4 input channels, K*K in {1, 4, 9}), such as a first layer on RGB input.
 //
-// With Cin*K*K <= 36 the column of one output pixel fits in registers and the
-// contraction is a handful of fused multiply-adds per output channel, so there is no
-// staging copy, no LDS tile and no matrix-core work: the output write dominates the
-// traffic.  A workgroup owns 64 output pixels (one per lane) and up to 64 output
-// channels:
+// With Cin*K*K <= 36 the column of a workgroup's pixels is a few KB, so there is no
+// staging copy and the output write dominates the traffic.  A workgroup owns 64
+// output pixels and up to 64 output channels:
 //   * each of its four waves samples a share of the kernel points: it reads the
 //     offsets and the mask of its pixels (consecutive lanes, consecutive pixels),
 //     forms the sampling position and the four bilinear weights times the mask (zero
 //     for a neighbour outside the image), interpolates the Cin input channels from x
-//     in its given [B][Cin][H][W] layout (x is small; its reads are cache hits; two
-//     horizontal neighbours are one 8-byte load in fp32) and puts the column entries
-//     in LDS;
-//   * after a barrier every lane holds its pixel's whole column in registers and
-//     each wave contracts it with a quarter of the output channels' weight rows (the
-//     rows are staged in LDS at the start; every lane of a wave reads the same
-//     address), adds the bias and stores; consecutive lanes store consecutive pixels.
+//     in its given [B][Cin][H][W] layout (x is small; its reads are cache hits) and
+//     puts the column entries, in fp32, in LDS.  The weight rows are loaded at the
+//     same time as the offsets;
+//   * after a barrier each wave multiplies one 32 x 32 block (output channels x
+//     pixels) on the matrix cores, MFMA 32x32x2 in fp32 (a bf16 input is exact in
+//     fp32, so one contraction serves both element types), adds the bias and stores;
+//     a store instruction writes 32 consecutive pixels of two output channels.
 //
 // The computation is the deformable-convolution equation (csdn.net tags page
 // "可变形卷积：Deformable ConvNets", part "Deformable Convolutional Networks",
@@ -34,6 +32,7 @@ namespace dcn {
 namespace {
 
 constexpr int kCinMax = 4;
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // Raw buffer loads with 32-bit byte offsets (the host keeps every tensor the kernel
 // reads under 2 GiB).  An offset past the end reads 0 without touching memory, which
@@ -76,8 +75,11 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
   constexpr uint32_t ES = BF16 ? 2u : 4u;
   constexpr int CMAX = CINT > 0 ? CINT : kCinMax;
   constexpr int RMAX = CMAX * KKT;
-  __shared__ float colbuf[RMAX][64];
-  __shared__ __attribute__((aligned(16))) float wsm[64][RMAX];   // weight rows o0 .. o0+63 (zero past Cin*K*K)
+  constexpr int RP = (RMAX + 1) & ~1;   // reduction length padded to the MFMA's k = 2
+  // column [r][pixel] and weight rows [r][output channel - o0], zero past Cin*K*K
+  // (one padding column keeps the 32 lanes of a weight read on distinct banks)
+  __shared__ float colbuf[RP][64];
+  __shared__ float wsm[RP][65];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int RK = a.Cin * KKT;
   const int o0 = blockIdx.y * 64, o1 = min(o0 + 64, a.Cout);
@@ -85,21 +87,17 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
   const auto rx = rsrc(a.x, static_cast<uint32_t>(a.B) * a.Cin * HW * ES);
   const auto ro = rsrc(a.offset, static_cast<uint32_t>(a.B) * 2 * KKT * a.HoWo * ES);
   const auto rm = rsrc(a.mask ? a.mask : a.offset, static_cast<uint32_t>(a.B) * KKT * a.HoWo * ES);
+  // weight rows: the loads are issued here and stored to LDS after the offsets' loads
+  // have gone out too, so the two latencies overlap
+  constexpr int NW = (64 * RP + 255) / 256;
+  float wv[NW];
   {
-    // weight rows into LDS: all loads first, then the stores
     const auto rw = rsrc(a.w, static_cast<uint32_t>(a.Cout) * RK * ES);
-    constexpr int NW = (64 * RMAX + 255) / 256;
-    float wv[NW];
 #pragma unroll
     for (int t = 0; t < NW; ++t) {
       const int e = tid + t * 256;
-      const int ol = e / RMAX, r = e - (e / RMAX) * RMAX;
-      wv[t] = ldb_if<BF16>(rw, e < 64 * RMAX && o0 + ol < a.Cout && r < RK, static_cast<uint32_t>(o0 + ol) * RK + r);
-    }
-#pragma unroll
-    for (int t = 0; t < NW; ++t) {
-      const int e = tid + t * 256;
-      if (e < 64 * RMAX) wsm[e / RMAX][e - (e / RMAX) * RMAX] = wv[t];
+      const int ol = e / RP, r = e - (e / RP) * RP;
+      wv[t] = ldb_if<BF16>(rw, e < 64 * RP && o0 + ol < a.Cout && r < RK, static_cast<uint32_t>(o0 + ol) * RK + r);
     }
   }
   const int n = blockIdx.x * 64 + lane;
@@ -120,6 +118,11 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
     dy[t] = ldb<BF16>(ro, ob);
     dx[t] = ldb<BF16>(ro, ob + a.HoWo);
     mk[t] = a.mask ? ldb<BF16>(rm, (static_cast<uint32_t>(b) * KKT + k) * a.HoWo + rem) : 1.f;
+  }
+#pragma unroll
+  for (int t = 0; t < NW; ++t) {
+    const int e = tid + t * 256;
+    if (e < 64 * RP) wsm[e - (e / RP) * RP][e / RP] = wv[t];
   }
   float xv[KPW][CMAX][4], wq[KPW][4];
 #pragma unroll
@@ -162,36 +165,43 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
     if (k >= KKT) continue;
 #pragma unroll
     for (int c = 0; c < CMAX; ++c) {
-      if (c >= a.Cin) continue;
-      colbuf[c * KKT + k][lane] =
-          wq[t][0] * xv[t][c][0] + wq[t][1] * xv[t][c][1] + wq[t][2] * xv[t][c][2] + wq[t][3] * xv[t][c][3];
+      // channels past Cin (and a padding row) are zero
+      colbuf[c * KKT + k][lane] = c < a.Cin ? wq[t][0] * xv[t][c][0] + wq[t][1] * xv[t][c][1] +
+                                                  wq[t][2] * xv[t][c][2] + wq[t][3] * xv[t][c][3]
+                                            : 0.f;
     }
+  }
+  if constexpr (RP > RMAX) {
+    if (tid < 64) colbuf[RMAX][tid] = 0.f;
   }
   __syncthreads();
 
-  // ---- contraction: every lane holds its pixel's column; wave w does output channels
-  // o0 + 16w .. o0 + 16w + 15, four at a time (independent accumulators); the weight
-  // rows come from LDS (every lane of the wave reads the same address)
-  float col[RMAX];
+  // ---- contraction on the matrix cores: wave w multiplies the 32 x 32 block of output
+  // channels o0 + 32*(w/2) .. +31 and pixels 32*(w%2) .. +31.  MFMA 32x32x2 f32 operands:
+  // lane l holds row (A) / column (B) l % 32 at reduction index 2*step + l / 32.
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int om = 32 * (wave >> 1), pn = 32 * (wave & 1);
+  floatx16 acc;
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) col[r] = (r < RK) ? colbuf[r][lane] : 0.f;
-  const int ob0 = o0 + 16 * wave, ob1 = min(ob0 + 16, o1);
-  for (int o = ob0; o < ob1; o += 4) {
-    float acc[4];
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = (a.bias && o + u < ob1) ? ldb<BF16>(rsrc(a.bias, a.Cout * ES), o + u) : 0.f;
+  for (int st = 0; st < RP / 2; ++st) {
+    const float av = wsm[2 * st + lh][om + l32];
+    const float bv = colbuf[2 * st + lh][pn + l32];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+  }
+  // accumulator element r: output channel o0 + om + 8*(r/4) + 4*lh + r%4, pixel pn + l32
+  const int np = blockIdx.x * 64 + pn + l32;
+  if (np < a.N) {
+    const int bp = np / a.HoWo, remp = np - (np / a.HoWo) * a.HoWo;
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = __builtin_fmaf(wsm[min(o + u - o0, 63)][r], col[r], acc[u]);
-    if (live) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (o + u >= ob1) break;
-        const int64_t e = (static_cast<int64_t>(b) * a.Cout + o + u) * a.HoWo + rem;
-        if constexpr (BF16) reinterpret_cast<uint16_t*>(a.out)[e] = to_bf16(acc[u]);
-        else reinterpret_cast<float*>(a.out)[e] = acc[u];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int o = o0 + om + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (o >= o1) continue;
+      const float v = acc[r] + (a.bias ? ldb<BF16>(rsrc(a.bias, a.Cout * ES), o) : 0.f);
+      const int64_t e = (static_cast<int64_t>(bp) * a.Cout + o) * a.HoWo + remp;
+      if constexpr (BF16) reinterpret_cast<uint16_t*>(a.out)[e] = to_bf16(v);
+      else reinterpret_cast<float*>(a.out)[e] = v;
     }
   }
 }
