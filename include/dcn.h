@@ -41,8 +41,9 @@
  *    samples are interpolated in fp32 from their exactly widened corners and
  *    rounded to bf16 (nearest even) before the matrix product; products
  *    accumulate in fp32; out is rounded to dtype.  With at
- *    most 4 input channels and K*K in {1, 4, 9} the column stays in fp32 and no
- *    workspace is needed (dcn_workspace_bytes returns 0).
+ *    most 4 input channels and K*K in {1, 4, 9} the column stays in fp32 and is
+ *    contracted on fp32 MFMA, and no workspace is needed (dcn_workspace_bytes
+ *    returns 0).
  *  - Limits: every tensor (and the staged copy of x) has fewer than 2^31
  *    elements; otherwise DCN_E_UNSUPPORTED.
  *  - Variant choice: a kernel variant is picked from the descriptor.  The
