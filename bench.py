@@ -122,7 +122,8 @@ class HipEvents:
 
 
 def traffic_for(workload: str):
-    """HBM bytes per fused launch from the committed counter runs, if the kernel is unchanged."""
+    """HBM bytes per fused launch (per call, all launches, for the offset/mask branch and
+    the layer) from the committed counter runs, if the sources are unchanged."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -221,7 +222,7 @@ def bench_offset_mask(w, steps: int, warmup: int):
         "frac_hbm_peak": round(w.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK["hbm"], 5),
         # about 58 flop per algorithmic byte, far below the bf16 ridge: bound by HBM
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK["hbm"], "unit": "GB/s",
-                     "frac": round(gbps / PEAK["hbm"], 5), "traffic": None,
+                     "frac": round(gbps / PEAK["hbm"], 5), "traffic": traffic_for(w.name),
                      "kernel": "dcn_offset_mask (both launches)", "kernel_sha": kernel_hash(),
                      "per_launch": {"flops": w.flops, "algorithmic_bytes": w.algorithmic_bytes}},
         "kernels_us": {"call_mean": round(total_ms / steps * 1e3, 3), "call_median": round(per[steps // 2] * 1e3, 3),
@@ -331,7 +332,7 @@ def bench_layer(w, steps: int, warmup: int):
                                                "deformable launch"},
         "separate_calls_ms_per_step": round(ms_sep, 6),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 4), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 5), "traffic": None,
+                     "frac": round(tflops / peak, 5), "traffic": traffic_for(w.name),
                      "kernel": "dcn_layer_forward (all launches)", "kernel_sha": kernel_hash(),
                      "per_launch": {"flops": flops}},
         "kernels_us": {"call_mean": round(ms_per_step * 1e3, 3), "separate_calls_mean": round(ms_sep * 1e3, 3)},
