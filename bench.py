@@ -38,17 +38,34 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16_mfma": 2516.6, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, TFLOP/s, GB/s
 CSRC = os.path.join(ROOT, "deformable_convolution_vision_amd", "csrc")
-def _kernel_srcs():
-    """Every kernel and host source of the library (a change to any of them invalidates
-    the committed counter figures)."""
+# The library sources each bench workload's launches come from: the host code and the
+# staging kernel for every workload, plus the kernels the workload runs.  A change to any
+# of them invalidates that workload's committed counter figures.
+_COMMON_SRCS = ("dcn_internal.h", "dcn_api.hip", "dcn_kernels.hip")
+_BOX_SRCS = ("dcn_box_kernel.h", "dcn_box.hip", "dcn_box_inst_a.hip", "dcn_box_inst_b.hip", "dcn_box_inst_c.hip",
+             "dcn_box_inst_d.hip")
+_WORKLOAD_SRCS = {
+    "c3": _BOX_SRCS, "c4": _BOX_SRCS, "c5": _BOX_SRCS, "c4_g4": _BOX_SRCS,
+    "single224": ("dcn_direct.hip",), "tiny": ("dcn_direct.hip",),
+    "c4_om": ("dcn_om.hip",), "c4_layer": ("dcn_om.hip",) + _BOX_SRCS,
+    "c4_bwd": ("dcn_backward.hip",), "roi_c4": ("dcn_roi.hip",), "psroi_c4": ("dcn_roi.hip",),
+}
+
+
+def _kernel_srcs(workload: str | None = None):
+    """The sources behind a workload's launches (every source of the library when the
+    workload is not one of the named ones)."""
+    if workload in _WORKLOAD_SRCS:
+        return tuple(sorted(set(_COMMON_SRCS + _WORKLOAD_SRCS[workload])))
     return tuple(sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".h"))))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_hash() -> str:
-    """Hash of the kernel sources (the counter figures are valid only for these)."""
+def kernel_hash(workload: str | None = None) -> str:
+    """Hash of the sources behind a workload's launches (its counter figures are valid
+    only for these)."""
     h = hashlib.sha256()
-    for name in _kernel_srcs():
+    for name in _kernel_srcs(workload):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -130,7 +147,7 @@ def traffic_for(workload: str):
     except (OSError, ValueError):
         return None
     entry = t.get(workload)
-    if not entry or entry.get("kernel_sha") != kernel_hash():
+    if not entry or entry.get("kernel_sha") != kernel_hash(workload):
         return None
     return entry.get("bytes_per_launch")
 
@@ -223,7 +240,7 @@ def bench_offset_mask(w, steps: int, warmup: int):
         # about 58 flop per algorithmic byte, far below the bf16 ridge: bound by HBM
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK["hbm"], "unit": "GB/s",
                      "frac": round(gbps / PEAK["hbm"], 5), "traffic": traffic_for(w.name),
-                     "kernel": "dcn_offset_mask (both launches)", "kernel_sha": kernel_hash(),
+                     "kernel": "dcn_offset_mask (both launches)", "kernel_sha": kernel_hash(w.name),
                      "per_launch": {"flops": w.flops, "algorithmic_bytes": w.algorithmic_bytes}},
         "kernels_us": {"call_mean": round(total_ms / steps * 1e3, 3), "call_median": round(per[steps // 2] * 1e3, 3),
                        "call_min": round(per[0] * 1e3, 3)},
@@ -333,7 +350,7 @@ def bench_layer(w, steps: int, warmup: int):
         "separate_calls_ms_per_step": round(ms_sep, 6),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 4), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 5), "traffic": traffic_for(w.name),
-                     "kernel": "dcn_layer_forward (all launches)", "kernel_sha": kernel_hash(),
+                     "kernel": "dcn_layer_forward (all launches)", "kernel_sha": kernel_hash(w.name),
                      "per_launch": {"flops": flops}},
         "kernels_us": {"call_mean": round(ms_per_step * 1e3, 3), "separate_calls_mean": round(ms_sep * 1e3, 3)},
         "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
@@ -434,7 +451,7 @@ def bench_backward(w, steps: int, warmup: int):
         "frac_mfma_peak": round(tflops / peak, 5),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 4), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 5), "traffic": None,
-                     "kernel": "dcn_backward (all launches of one call)", "kernel_sha": kernel_hash(),
+                     "kernel": "dcn_backward (all launches of one call)", "kernel_sha": kernel_hash(w.name),
                      "per_launch": {"flops": flops}},
         "kernels_us": {"call_mean": round(call_mean * 1e3, 3), "call_median": round(per[steps // 2] * 1e3, 3),
                        "call_min": round(per[0] * 1e3, 3)},
@@ -531,7 +548,7 @@ def bench_roi(w, steps: int, warmup: int):
         "config": {"workload": what, "variant": w.op, "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK["hbm"], "unit": "GB/s",
                      "frac": round(gbps / PEAK["hbm"], 5), "traffic": None,
-                     "kernel": kname, "kernel_sha": kernel_hash(),
+                     "kernel": kname, "kernel_sha": kernel_hash(w.name),
                      "per_launch": {"algorithmic_bytes": abytes, "outputs": R * C_out * k * k}},
         "kernels_us": {"call_mean": round(ms_per_step * 1e3, 3)},
         "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
@@ -696,7 +713,7 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
         "frac_hbm_peak": round(gbps / PEAK["hbm"], 5),
         "roofline": {"bound": bound, "achieved": round(achieved, 4), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 5), "traffic": traffic,
-                     "kernel": kernel_symbol(variant, plan, w), "kernel_sha": kernel_hash(),
+                     "kernel": kernel_symbol(variant, plan, w), "kernel_sha": kernel_hash(name),
                      "per_launch": {"flops": flops, "algorithmic_bytes": abytes}},
         "kernels_us": {"stage_mean": round(stage_mean * 1e3, 3), "fused_mean": round(fused_mean * 1e3, 3),
                        "fused_median": round(fused_ms[steps // 2] * 1e3, 3),

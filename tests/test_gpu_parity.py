@@ -107,6 +107,12 @@ EDGE = [
     ("no_mask_no_bias", dict(B=2, Cin=33, H=10, W=12, Cout=17, K=3, s=1, p=1, d=1, mask=None, bias=None)),
     ("odd_stride2", dict(B=1, Cin=40, H=15, W=17, Cout=66, K=3, s=2, p=1, d=1)),
     ("cin3", dict(B=2, Cin=3, H=20, W=21, Cout=9, K=3, s=1, p=1, d=1, offset="uniform:2")),
+    # small-reduction kernel: rows of two 64-pixel segments with offsets that leave the
+    # input window (its corners then come from x); stride 2 and dilation 2, whose window
+    # does not fit (every corner from x); K = 2
+    ("direct_far_offsets", dict(B=2, Cin=4, H=21, W=70, Cout=20, K=3, s=1, p=1, d=1, offset="uniform:6")),
+    ("direct_s2_d2", dict(B=1, Cin=2, H=30, W=150, Cout=70, K=3, s=2, p=2, d=2)),
+    ("direct_k2", dict(B=2, Cin=1, H=9, W=11, Cout=5, K=2, s=1, p=0, d=1, offset="normal:1.5")),
     ("cout300", dict(B=1, Cin=64, H=12, W=14, Cout=300, K=3, s=1, p=1, d=1)),
     ("far_offsets_d2", dict(B=2, Cin=24, H=13, W=11, Cout=20, K=3, s=1, p=2, d=2, offset="uniform:8",
                             mask=None)),
