@@ -257,11 +257,16 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a, int nx, in
     pack_weight<T>(a, static_cast<int>(blockIdx.x), nw);
     return;
   }
-  const int bx = static_cast<int>(blockIdx.x) - nw - nw2;
+  // The x tiles run in (image, pixel block, channel block) order, channel blocks fastest,
+  // and each XCD (workgroup g runs on XCD g % 8; the weight workgroups before them are
+  // a multiple of 8) takes a contiguous run of them: a band of input rows of one image,
+  // the band the fused kernel's workgroups on that XCD read (they take contiguous runs
+  // of output tiles in the same raster order).
+  const int bx = xcd_tile(static_cast<int>(blockIdx.x) - nw - nw2, nx);
   const int per_img = s_tiles * c_tiles;
   const int b = bx / per_img;
   const int r = bx - b * per_img;
-  const int ct = r / s_tiles, st = r - (r / s_tiles) * s_tiles;
+  const int st = r / c_tiles, ct = r - (r / c_tiles) * c_tiles;
   const int s0 = st * (kPairs ? kPairPx : 64), c0 = ct * 64;
   if constexpr (kPairs) {
     stage_x_bf16_v8(a, reinterpret_cast<uint32_t*>(&tile[0][0]), b, s0, c0);
@@ -623,14 +628,16 @@ hipError_t launch_stage(int variant, const StageArgs& a, hipStream_t stream) {
   const bool wv8 = vi.is_bf16 && a.wlayout == 1 && a.KK == 9 && a.Cin % 8 == 0 &&
                    reinterpret_cast<uintptr_t>(a.w) % 16 == 0;   // pack_weight_v8_ok
   const int wunits = wv8 ? a.Mp * (a.Cp / 8) : a.Mp * a.Cp;
-  const int nw = a.w != nullptr ? min((wunits + kThreads - 1) / kThreads, 1024) : 0;
+  // (rounded up to a multiple of 8, so the x tiles' workgroups start on XCD 0; a
+  // weight workgroup past the last unit has nothing to do)
+  const int nw = a.w != nullptr ? (min((wunits + kThreads - 1) / kThreads, 1024) + 7) / 8 * 8 : 0;
   StageArgs sa = a;
   sa.nw2 = 0;
   if (a.w2 != nullptr) {
     const bool wv8b = vi.is_bf16 && a.wlayout2 == 1 && a.KK == 9 && a.Cin % 8 == 0 &&
                       reinterpret_cast<uintptr_t>(a.w2) % 16 == 0;
     const int wunits2 = wv8b ? a.Mp2 * (a.Cp / 8) : a.Mp2 * a.Cp;
-    sa.nw2 = min((wunits2 + kThreads - 1) / kThreads, 1024);
+    sa.nw2 = (min((wunits2 + kThreads - 1) / kThreads, 1024) + 7) / 8 * 8;
   }
   const dim3 grid(nx + nw + sa.nw2);
   void* args[] = {&sa, const_cast<int*>(&nx), const_cast<int*>(&s_tiles), const_cast<int*>(&c_tiles)};
