@@ -240,19 +240,26 @@ __global__ __launch_bounds__(kRT) void roi_pool_cl_kernel(RoiArgs a, const uint1
 
 // Staging of the score maps for position-sensitive pooling: x [B][C*k*k][H*W] (bf16)
 // -> xs [B][H*W][k*k][Cp] with Cp = C rounded up to 8 (zeros past C), so that the
-// C maps of one bin at one pixel are contiguous.  One workgroup per (image, bin, block
-// of 64 pixels, block of 64 output channels), transposed through LDS: reads are two
-// pixels (4 bytes) of one map, writes 16-byte vectors of 8 channels of one pixel.
+// C maps of one bin at one pixel are contiguous.  One workgroup per (image, block of 64
+// pixels, bin, block of 64 output channels), transposed through LDS: reads are two
+// pixels (4 bytes) of one map, writes 16-byte vectors of 8 channels of one pixel.  The
+// workgroups run in that order (channel blocks fastest, then bins), so consecutive ones
+// fill the k*k*Cp run of the same 64 pixels, and each XCD (workgroup g runs on XCD
+// g % 8) takes a contiguous run of them.
 constexpr int kPsPx = 64;
 __global__ __launch_bounds__(kRT) void ps_stage_kernel(const uint16_t* x, uint16_t* xs, int B, int C, int KK, int HW,
                                                        int Cp, int ptiles, int ctiles) {
   __shared__ uint32_t t[64][kPsPx / 2 + 1];   // [channel][pixel pair]
   int e = blockIdx.x;
+  {   // contiguous runs of workgroups per XCD (a bijection on [0, gridDim.x))
+    const int T = static_cast<int>(gridDim.x), xcd = e & 7, q = T >> 3, rr = T & 7;
+    e = xcd * q + min(xcd, rr) + (e >> 3);
+  }
   const int ct = e % ctiles;
   e /= ctiles;
-  const int pt = e % ptiles;
-  e /= ptiles;
-  const int bin = e % KK, b = e / KK;
+  const int bin = e % KK;
+  e /= KK;
+  const int pt = e % ptiles, b = e / ptiles;
   const int c0 = ct * 64, p0 = pt * kPsPx;
   const int tid = threadIdx.x;
   // 64 channels x 32 pixel pairs
