@@ -4,13 +4,13 @@
 // col[b][c*K^2+k][p] = m_k * S(x[b,c], py_k, px_k) of the forward's deformable
 // im2col (p an output pixel, S the bilinear sample with zero outside the image):
 //
-//   gcol[b][r][p]   = sum_o W[o][r] * gy[b][o][p]              (r = c*K^2 + k)
+//   gcol[b][p][k][c]  = sum_o W[o][c][k] * gy[b][o][p]
 //   grad_weight[o][r] = sum_{b,p} gy[b][o][p] * col[b][r][p]
-//   grad_bias[o]    = sum_{b,p} gy[b][o][p]
-//   grad_mask       = sum_c gcol * S
-//   grad_offset     = sum_c gcol * m * (dS/dpy, dS/dpx)
-//   grad_x          = the column gradient times m, scattered to the four neighbours
-//                     of each sample with their bilinear weights
+//   grad_bias[o]      = sum_{b,p} gy[b][o][p]
+//   grad_mask         = sum_c gcol * S
+//   grad_offset       = sum_c gcol * m * (dS/dpy, dS/dpx)
+//   grad_x            = the column gradient times m, carried to the four neighbours
+//                       of each sample with their bilinear weights
 //
 // The offset gradient runs through the derivative of the bilinear kernel (the
 // gradient equation of the csdn.net tags page "可变形卷积：Deformable ConvNets",
@@ -21,20 +21,31 @@
 // in fp32 as in the forward.
 //
 // Kernels, in launch order:
-//   prep_w   W [Cout][R] -> Wt [R][Coutp] (the column-gradient product's first operand)
-//   prep_gy  gy -> gyT [B][P][Coutp] and gyP [B][Cout][Pp] (both zero-padded), and
-//            the bias gradient's per-tile sums (fp32 atomics)
-//   fill     zero the fp32 accumulators (one launch)
-//   gemm     gcol[b] = Wt x gyT[b]^T (MFMA, both operands contiguous along the reduction)
-//   sample   per (b, group, channel block, kernel point, pixel): the sample's corners
-//            and weights once, then for each channel the column entry (for the
-//            weight gradient), the mask and offset partial sums and the four
-//            scattered input-gradient contributions (fp32 atomics)
+//   stage    x -> xs [B][H][W][Cp], channels last (the forward's staging kernel)
+//   prep_w   W [Cout][Cin][K^2] -> Wt [K^2][Cin][Coutp] (the column-gradient product's
+//            second operand, rows in the column gradient's channel-fastest order)
+//   fill     zero the fp32 weight and bias accumulators and the pair counters (one launch)
+//   prep_gy  gy -> gyT [B][P][Coutp] and gyP [B][Cout][Pp] (both zero-padded), and the
+//            bias gradient's per-tile sums (fp32 atomics)
+//   count    per sample (b, group, kernel point, pixel): each corner inside the image
+//            counted at its input pixel; the atomic increment's old value is the pair's
+//            rank in that pixel's list
+//   scan     exclusive prefix sums of the counts: per block of 2048, then the block sums
+//   gemm     gcol[b] = gyT[b] x Wt^T, channels fastest: [B][P][K^2][Cin] (MFMA)
+//   sample   per (b, group, kernel point, 64 output pixels): the corners from xs as
+//            16-byte channel vectors; the column entries, transposed through LDS to
+//            col [B][R][Pp] for the weight gradient; the offset and mask gradients summed
+//            over the group's channels across the lanes of the sample and written once;
+//            and each in-image corner's pair (column-gradient row, m * corner weight)
+//            placed in its input pixel's list
+//   gather   grad_x per input pixel: the sum over its pairs of weight * column-gradient
+//            row, transposed through LDS to [B][Cin][H][W]
 //   gemm     grad_weight = sum_b gyP[b] x col[b]^T, the reduction split over workgroups
 //            (fp32 atomics into a zeroed accumulator)
-//   gather   grad_x from the boxes (tiled path)
-//   convert  fp32 accumulators -> the element type (one launch)
-// The gradient products run on MFMA 32x32x16 bf16 (bf16 data) or 32x32x2 fp32.
+//   convert  the weight and bias accumulators -> the element type (one launch)
+// The gradient products run on MFMA 32x32x16 bf16 (bf16 data) or 32x32x2 fp32.  The
+// input, offset and mask gradients take no atomics: each is summed by one thread or one
+// group of lanes and rounded to the element type once.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -53,8 +64,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBT = 256;   // threads per workgroup of the elementwise kernels
-constexpr int kCB = 32;    // channels per thread in the sample kernel
+constexpr int kBT = 256;     // threads per workgroup
+constexpr int kSP = 64;      // output pixels per workgroup of the sampling kernel (one kernel point)
+constexpr int kGP = 64;      // input pixels per workgroup of the gather kernel
+constexpr int kCC = 256;     // channels per chunk of the sampling and gather kernels
+constexpr int kScanB = 2048; // counts per block of the first scan pass (256 threads x 8)
 
 template <typename T>
 __device__ __forceinline__ float to_f(T v);
@@ -72,42 +86,67 @@ __device__ __forceinline__ uint16_t from_f<uint16_t>(float v) {   // round to ne
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
+// Workgroup id -> work item, so that consecutive items run on the same XCD (workgroups
+// are dealt to the 8 XCDs round-robin; XCD x takes the contiguous item range
+// [x*q + min(x,r), ... + q + (x<r)) of T = 8q + r items; a bijection on [0, T)).
+__device__ __forceinline__ int xcd_item(int g, int T) {
+  const int xcd = g & 7, idx = g >> 3;
+  const int q = T >> 3, r = T & 7;
+  return xcd * q + min(xcd, r) + idx;
+}
+
 struct BwdArgs {
-  const void* x;        // [B][Cin][H][W]
+  const void* xs;       // staged x, [B][H][W][Cp] (channels >= Cin zero)
   const void* offset;   // [B][2GK^2][Ho][Wo]
   const void* mask;     // [B][GK^2][Ho][Wo] or null
   const void* w;        // [Cout][Cin][K][K] = [Cout][R]
   const void* gy;       // [B][Cout][Ho][Wo]
-  void* wt;             // [R][Coutp]
+  void* wt;             // [K^2][Cin][Coutp]
   void* gyt;            // [B][P][Coutp]
   void* gyp;            // [B][Cout][Pp]
   void* col;            // [B][R][Pp] or null (no weight gradient)
-  float* gcol;          // [B][R][P] or null (no input, offset or mask gradient)
-  float* gx32;          // [B][Cin][H][W] or null
-  float* goff32;        // [B][2GK^2][P] or null
-  float* gm32;          // [B][GK^2][P] or null
+  float* gcol;          // [B][P][K^2][Cin] or null (no input, offset or mask gradient)
   float* gb32;          // [Cout] or null (bias gradient accumulator)
-  float* outliers;      // [1]: set to 1 when a corner outside its box went to gx32
-  int B, Cin, H, W, Cout, K, KK, stride, pad, dil, Ho, Wo, P, Pp, Coutp, R, G, Cg, NCB;
-  // tiled sampling (bwd_sample_tile): output tiles of kTH x kTW pixels, an LDS box of
-  // BH x BW input pixels per channel (the tile's footprint plus a margin of kMargin),
-  // CBL channels of boxes at a time, each group's channels split over nsplit workgroups
-  // of cps channels; gbox [B][Cin][TY][TX][BH*BW] keeps every box for the gather pass
-  float* gbox;
-  int TY, TX, BH, BW, CBL, nsplit, cps;
-  int tiles_total;      // workgroups of the tiled sampling kernel: B * G * nsplit * TY * TX
+  void* grad_offset;    // [B][2GK^2][Ho][Wo] or null
+  void* grad_mask;      // [B][GK^2][Ho][Wo] or null
+  void* grad_x;         // [B][Cin][H][W] or null
+  int* cnt;             // [B*G*H*W + 1]: pairs per input pixel, then their block-local
+                        // exclusive prefix sums
+  int* bsum;            // [ceil((B*G*H*W + 1) / kScanB)]: block sums, then their exclusive sums
+  int4* rank;           // [B][G][K^2][P]: each corner's rank in its pixel's list, -1 for none
+  int2* pairs;          // [B*G*K^2*P*4]: (column-gradient row, bits of m * corner weight)
+  int B, Cin, H, W, Cout, K, KK, stride, pad, dil, Ho, Wo, P, Pp, Coutp, R, G, Cg, Cp;
+  int lg;               // lanes per sample (sampling) or pixel (gather): a power of two
+                        // <= 32, eight channels per lane
+  int npb;              // 64-pixel blocks of the output plane
+  int nqb;              // 64-pixel blocks of the input plane
+  int ncc;              // 256-channel chunks of a group
+  int nsamp;            // B * G * K^2 * P
 };
 
-constexpr int kTH = 8, kTW = 8;   // output tile of the tiled sampling kernel
-constexpr int kMargin = 4;        // box margin (input pixels) around the tile's footprint
-
+// Wt[k*Cin + c][o] = W[o][c*K^2 + k] (zero for o >= Cout): 32 x 32 tiles of (o, r)
+// through LDS, read along r and written along o.
 template <typename T>
 __global__ __launch_bounds__(kBT) void bwd_prep_w(BwdArgs a) {
-  const int e = blockIdx.x * kBT + threadIdx.x;
-  if (e >= a.R * a.Coutp) return;
-  const int o = e % a.Coutp, r = e / a.Coutp;
+  __shared__ T tile[32][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int r0 = blockIdx.x * 32, o0 = blockIdx.y * 32;
   const T* w = static_cast<const T*>(a.w);
-  static_cast<T*>(a.wt)[e] = o < a.Cout ? w[static_cast<size_t>(o) * a.R + r] : T(0);
+  T* wt = static_cast<T*>(a.wt);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = o0 + ty + 8 * i, r = r0 + tx;
+    tile[ty + 8 * i][tx] = (o < a.Cout && r < a.R) ? w[static_cast<size_t>(o) * a.R + r] : T(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + ty + 8 * i, o = o0 + tx;
+    if (r < a.R && o < a.Coutp) {
+      const int c = r / a.KK, k = r - (r / a.KK) * a.KK;
+      wt[(static_cast<size_t>(k) * a.Cin + c) * a.Coutp + o] = tile[tx][ty + 8 * i];
+    }
+  }
 }
 
 // 32 x 32 tiles of (output channel, pixel) through LDS: gyP keeps gy's layout with
@@ -178,354 +217,381 @@ __global__ __launch_bounds__(kBT) void bwd_fill_zero_t(T* p, int n) {
   if (e < n) p[e] = T(0);
 }
 
-// zero columns [P, Pp) of each of the rows of col
-template <typename T>
-__global__ __launch_bounds__(kBT) void bwd_col_pad(T* col, int rows, int P, int Pp) {
-  const int r = blockIdx.x * kBT + threadIdx.x;
-  if (r >= rows) return;
-  for (int p = P; p < Pp; ++p) col[static_cast<size_t>(r) * Pp + p] = T(0);
-}
+// One sample's geometry: its corners inside the image (bit n of fl: corner n of 00, 01,
+// 10, 11), the flat index of corner 00, the four bilinear weights, the cell
+// fractions and the mask.  A position with no neighbour in the image (or NaN) has no
+// corner; at py == -1 the cell is [-1, 0): row 0 has weight 0 but its derivative counts.
+struct Geo {
+  int fl, q00;
+  float w00, w01, w10, w11, ly, lx, m;
+};
 
 template <typename T>
-__global__ __launch_bounds__(kBT) void bwd_convert(const float* src, T* dst, int n) {
-  const int e = blockIdx.x * kBT + threadIdx.x;
-  if (e < n) dst[e] = from_f<T>(src[e]);
-}
-
-// One workgroup per (b, group, channel split, output tile of kTH x kTW pixels); the
-// tile's K^2 x 64 samples are spread over the threads (NS per thread), and each
-// sample's corners, weights and mask are computed once.  The input gradient is
-// gathered, not scattered: once per workgroup the (sample, corner) pairs that land
-// in the LDS box around the tile are sorted by box pixel (a count, a prefix sum and
-// a placement), and then for each channel
-//   1. each thread forms its samples' column entries (stored for the weight
-//      gradient), reads their column gradients, accumulates the mask and offset sums,
-//      and leaves gcol * m of each sample in LDS;
-//   2. each thread sums, for its box pixels, gcol * m * (corner weight) over the pairs
-//      sorted to that pixel and stores the sum to gbox.
-// A corner outside the box (but inside the image) is added to the fp32 accumulator
-// with a global atomic add.  The gather pass then sums the boxes covering each input
-// pixel.  (LDS float atomics measured far slower than this on gfx950.)
-template <typename T, int NS, int CQ>
-__global__ __launch_bounds__(kBT) void bwd_sample_tile(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  constexpr int NE = NS * kBT * 4;                        // (sample, corner) pairs
-  float* ent_w = reinterpret_cast<float*>(lds);           // [NE] corner weight
-  uint16_t* ent_s = reinterpret_cast<uint16_t*>(lds + NE * 4);   // [NE] sample
-  int* start = reinterpret_cast<int*>(lds + NE * 6);      // [BP + 1]
-  const int tid = threadIdx.x;
-  // Workgroups go to the eight XCDs in turn (workgroup w to XCD w % 8), and each XCD has
-  // its own L2.  Neighbouring tiles share cache lines of gcol, x and col (a line holds
-  // 32 fp32 pixels of a gcol row, four tiles' worth), so consecutive logical tiles are
-  // given to workgroups of one XCD: logical index = XCD * per + (workgroup / 8).
-  const int per = (a.tiles_total + 7) / 8;
-  int t = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
-  if (t >= a.tiles_total) return;   // the last XCD's spare workgroups (uniform)
-  const int tx = t % a.TX;
-  t /= a.TX;
-  const int ty = t % a.TY;
-  t /= a.TY;
-  const int sp = t % a.nsplit;
-  t /= a.nsplit;
-  const int g = t % a.G, b = t / a.G;
-  const int oy0 = ty * kTH, ox0 = tx * kTW;
-  const int by0 = oy0 * a.stride - a.pad - kMargin, bx0 = ox0 * a.stride - a.pad - kMargin;
-  const int BP = a.BH * a.BW, GKK = a.G * a.KK, HW = a.H * a.W;
-  float* tgs = reinterpret_cast<float*>(lds + NE * 6 + ((BP + 1) * 4 + 15) / 16 * 16);   // [2][CQ][NS * kBT]
-  const T* x = static_cast<const T*>(a.x);
-  const T* off = static_cast<const T*>(a.offset);
-  T* col = static_cast<T*>(a.col);
-  const bool grads = a.gcol != nullptr;
-  const bool scat = a.gx32 != nullptr;
-
-  // per-sample state
-  int p_[NS], pq_[NS], k_[NS], q00_[NS], bl_[NS], fl_[NS], o_[NS][4];
-  float m_[NS], w_[NS][4], lx_[NS], ly_[NS], gm_[NS], goy_[NS], gox_[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int s = tid + i * kBT;
-    const int k = s / (kTH * kTW), pl = s - k * (kTH * kTW);
-    const int oy = oy0 + pl / kTW, ox = ox0 + pl % kTW;
-    const bool valid = k < a.KK && oy < a.Ho && ox < a.Wo;
-    p_[i] = valid ? oy * a.Wo + ox : -1;
-    pq_[i] = valid ? p_[i] : 0;
-    k_[i] = valid ? k : 0;
-    o_[i][0] = o_[i][1] = o_[i][2] = o_[i][3] = 0;
-    gm_[i] = goy_[i] = gox_[i] = 0.f;
-    fl_[i] = 0;
-    q00_[i] = 0;
-    bl_[i] = -1;
-    m_[i] = 0.f;
-    lx_[i] = ly_[i] = 0.f;
-    w_[i][0] = w_[i][1] = w_[i][2] = w_[i][3] = 0.f;
-    if (!valid) continue;
-    const int p = p_[i], gk = g * a.KK + k, ki = k / a.K, kj = k - (k / a.K) * a.K;
-    const float dy = to_f(off[(static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p]);
-    const float dx = to_f(off[(static_cast<size_t>(b) * 2 * GKK + 2 * gk + 1) * a.P + p]);
-    const float py = static_cast<float>(oy * a.stride - a.pad + ki * a.dil) + dy;
-    const float px = static_cast<float>(ox * a.stride - a.pad + kj * a.dil) + dx;
-    m_[i] = a.mask != nullptr ? to_f(static_cast<const T*>(a.mask)[(static_cast<size_t>(b) * GKK + gk) * a.P + p]) : 1.f;
-    // a position with no neighbour in the image (or NaN) has none; at py == -1 the cell
-    // is [-1, 0): row 0 has weight 0 but its derivative counts
-    const bool any = py >= -1.f && py < static_cast<float>(a.H) && px >= -1.f && px < static_cast<float>(a.W);
-    if (!any) continue;
-    const float y0f = floorf(py), x0f = floorf(px);
-    const float ly = py - y0f, lx = px - x0f;
-    const int y0 = static_cast<int>(y0f), x0 = static_cast<int>(x0f);
-    const bool iy0 = y0 >= 0, iy1 = y0 + 1 < a.H, ix0 = x0 >= 0, ix1 = x0 + 1 < a.W;
-    fl_[i] = (iy0 && ix0 ? 1 : 0) | (iy0 && ix1 ? 2 : 0) | (iy1 && ix0 ? 4 : 0) | (iy1 && ix1 ? 8 : 0);
-    q00_[i] = y0 * a.W + x0;
-    o_[i][0] = (fl_[i] & 1) ? q00_[i] : 0;
-    o_[i][1] = (fl_[i] & 2) ? q00_[i] + 1 : 0;
-    o_[i][2] = (fl_[i] & 4) ? q00_[i] + a.W : 0;
-    o_[i][3] = (fl_[i] & 8) ? q00_[i] + a.W + 1 : 0;
-    const int yb = y0 - by0, xb = x0 - bx0;
-    bl_[i] = (yb >= 0 && yb + 1 < a.BH && xb >= 0 && xb + 1 < a.BW) ? yb * a.BW + xb : -1;
-    ly_[i] = ly;
-    lx_[i] = lx;
-    w_[i][0] = (1.f - ly) * (1.f - lx);
-    w_[i][1] = (1.f - ly) * lx;
-    w_[i][2] = ly * (1.f - lx);
-    w_[i][3] = ly * lx;
-  }
-
-  // sort the in-box (sample, corner) pairs by box pixel: count, prefix sum, place
-  if (scat) {
-    for (int j = tid; j <= BP; j += kBT) start[j] = 0;
-    __syncthreads();
-    int rank[NS][4];
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        rank[i][n] = -1;
-        if (bl_[i] >= 0 && (fl_[i] & (1 << n))) {
-          const int j = bl_[i] + (n & 1) + (n >> 1) * a.BW;
-          rank[i][n] = atomicAdd(&start[j + 1], 1);
-        }
-      }
-    __syncthreads();
-    if (tid < 64) {   // inclusive scan of start[1..BP] by one wave, 64 bins per pass
-      int carry = 0;
-      for (int j0 = 1; j0 <= BP; j0 += 64) {
-        const int j = j0 + tid;
-        int v = j <= BP ? start[j] : 0;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int u = __shfl_up(v, d);
-          if (tid >= d) v += u;
-        }
-        if (j <= BP) start[j] = v + carry;
-        carry += __shfl(v, 63);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-        if (rank[i][n] >= 0) {
-          const int j = bl_[i] + (n & 1) + (n >> 1) * a.BW;
-          const int e = start[j] + rank[i][n];
-          ent_s[e] = static_cast<uint16_t>(tid + i * kBT);
-          ent_w[e] = w_[i][n];
-        }
-    __syncthreads();
-  }
-
-  const int cg0 = g * a.Cg + sp * a.cps, cg1 = min(cg0 + a.cps, (g + 1) * a.Cg);
-  const size_t cstride = static_cast<size_t>(a.TY) * a.TX * BP;   // gbox: next channel, same tile
-  float* gdst = scat ? a.gbox + (((static_cast<size_t>(b) * a.Cin + cg0) * a.TY + ty) * a.TX + tx) * BP : nullptr;
-  // CQ channels per step: every load of the step first (from valid addresses: a corner
-  // outside the image reads the plane's first element and is replaced by 0
-  // afterwards), then the samples' work, one barrier, and the gather of the CQ
-  // channels' boxes, which reads each sorted pair once for all of them.  The two
-  // halves of tgs alternate between steps, so a thread still gathering step t reads a
-  // half that step t+1 does not write.
-  for (int c = cg0; c < cg1; c += CQ) {
-    const int nq = min(CQ, cg1 - c);
-    float* tg_s = tgs + (((c - cg0) / CQ) & 1) * (CQ * NS * kBT);
-    float v[CQ][NS][4], gcv[CQ][NS];
-#pragma unroll
-    for (int q = 0; q < CQ; ++q) {
-      const int cq = min(c + q, cg1 - 1);   // past the split's last channel: a repeat, not used
-      const size_t pl = (static_cast<size_t>(b) * a.Cin + cq) * HW;
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) v[q][i][n] = to_f(x[pl + o_[i][n]]);
-        gcv[q][i] = grads ? a.gcol[(static_cast<size_t>(b) * a.R + cq * a.KK + k_[i]) * a.P + pq_[i]] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < CQ; ++q) {
-      if (q >= nq) break;
-      const size_t pl = (static_cast<size_t>(b) * a.Cin + c + q) * HW;
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const int f = fl_[i];
-        const float v00 = (f & 1) ? v[q][i][0] : 0.f, v01 = (f & 2) ? v[q][i][1] : 0.f;
-        const float v10 = (f & 4) ? v[q][i][2] : 0.f, v11 = (f & 8) ? v[q][i][3] : 0.f;
-        const float sv = w_[i][0] * v00 + w_[i][1] * v01 + w_[i][2] * v10 + w_[i][3] * v11;
-        const size_t r = static_cast<size_t>(b) * a.R + (c + q) * a.KK + k_[i];
-        if (col != nullptr && p_[i] >= 0) col[r * a.Pp + p_[i]] = from_f<T>(m_[i] * sv);
-        if (!grads) continue;
-        const float gc = gcv[q][i];
-        gm_[i] += gc * sv;
-        goy_[i] += gc * ((1.f - lx_[i]) * (v10 - v00) + lx_[i] * (v11 - v01));
-        gox_[i] += gc * ((1.f - ly_[i]) * (v01 - v00) + ly_[i] * (v11 - v10));
-        if (!scat) continue;
-        const float tg = gc * m_[i];
-        tg_s[q * (NS * kBT) + tid + i * kBT] = tg;
-        if (bl_[i] < 0 && f != 0) {   // corners outside the box
-          *a.outliers = 1.f;
-          float* gx = a.gx32 + pl + q00_[i];
-          if (f & 1) unsafeAtomicAdd(gx, tg * w_[i][0]);
-          if (f & 2) unsafeAtomicAdd(gx + 1, tg * w_[i][1]);
-          if (f & 4) unsafeAtomicAdd(gx + a.W, tg * w_[i][2]);
-          if (f & 8) unsafeAtomicAdd(gx + a.W + 1, tg * w_[i][3]);
-        }
-      }
-    }
-    if (scat) {
-      __syncthreads();
-      for (int j = tid; j < BP; j += kBT) {
-        float acc[CQ];
-#pragma unroll
-        for (int q = 0; q < CQ; ++q) acc[q] = 0.f;
-        for (int e = start[j]; e < start[j + 1]; ++e) {
-          const int sj = ent_s[e];
-          const float w = ent_w[e];
-#pragma unroll
-          for (int q = 0; q < CQ; ++q) acc[q] += tg_s[q * (NS * kBT) + sj] * w;
-        }
-#pragma unroll
-        for (int q = 0; q < CQ; ++q)
-          if (q < nq) gdst[q * cstride + j] = acc[q];
-      }
-      gdst += CQ * cstride;
-    }
-  }
-  if (grads) {
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (p_[i] < 0) continue;
-      const int gk = g * a.KK + k_[i];
-      if (a.goff32 != nullptr) {
-        float* go = a.goff32 + (static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p_[i];
-        unsafeAtomicAdd(go, goy_[i] * m_[i]);
-        unsafeAtomicAdd(go + a.P, gox_[i] * m_[i]);
-      }
-      if (a.gm32 != nullptr) unsafeAtomicAdd(a.gm32 + (static_cast<size_t>(b) * GKK + gk) * a.P + p_[i], gm_[i]);
-    }
-  }
-}
-
-// grad_x[b][c][y][x] = the fp32 accumulator (corners outside their box) plus the
-// entries of every box that covers (y, x): tile ty's box starts at row
-// ty*kTH*stride - pad - kMargin and has BH rows (likewise columns).
-template <typename T>
-__global__ __launch_bounds__(kBT) void bwd_gather_x(BwdArgs a, T* grad_x) {
-  const long long e = static_cast<long long>(blockIdx.x) * kBT + threadIdx.x;
-  const long long n = static_cast<long long>(a.B) * a.Cin * a.H * a.W;
-  if (e >= n) return;
-  const int xx = static_cast<int>(e % a.W);
-  const int yy = static_cast<int>((e / a.W) % a.H);
-  const long long bc = e / (static_cast<long long>(a.H) * a.W);
-  const int sy = kTH * a.stride, sx = kTW * a.stride;
-  const int ry = yy + a.pad + kMargin, rx = xx + a.pad + kMargin;   // >= 0
-  const int ty1 = min(ry / sy, a.TY - 1), tx1 = min(rx / sx, a.TX - 1);
-  const int BP = a.BH * a.BW;
-  // the fp32 accumulator holds anything only if some corner fell outside its box
-  float acc = *a.outliers != 0.f ? a.gx32[e] : 0.f;
-  const float* base = a.gbox + static_cast<size_t>(bc) * a.TY * a.TX * BP;
-  for (int ty = ty1; ty >= 0; --ty) {
-    const int yb = ry - ty * sy;   // row inside tile ty's box
-    if (yb >= a.BH) break;
-    for (int tx = tx1; tx >= 0; --tx) {
-      const int xb = rx - tx * sx;
-      if (xb >= a.BW) break;
-      acc += base[(static_cast<size_t>(ty) * a.TX + tx) * BP + yb * a.BW + xb];
-    }
-  }
-  grad_x[e] = from_f<T>(acc);
-}
-
-// One thread per (b, group, channel block, kernel point, pixel), pixels fastest.
-// Threads with a pixel in the padding [P, Pp) write the zero padding of col.
-template <typename T>
-__global__ __launch_bounds__(kBT) void bwd_sample(BwdArgs a) {
-  const long long e = static_cast<long long>(blockIdx.x) * kBT + threadIdx.x;
-  const long long total = static_cast<long long>(a.B) * a.G * a.NCB * a.KK * a.Pp;
-  if (e >= total) return;
-  const int p = static_cast<int>(e % a.Pp);
-  long long t = e / a.Pp;
-  const int k = static_cast<int>(t % a.KK);
-  t /= a.KK;
-  const int cb = static_cast<int>(t % a.NCB);
-  t /= a.NCB;
-  const int g = static_cast<int>(t % a.G), b = static_cast<int>(t / a.G);
-  const int c0 = g * a.Cg + cb * kCB, c1 = min(c0 + kCB, (g + 1) * a.Cg);
-  T* col = static_cast<T*>(a.col);
-  if (p >= a.P) {
-    if (col != nullptr)
-      for (int c = c0; c < c1; ++c) col[(static_cast<size_t>(b) * a.R + c * a.KK + k) * a.Pp + p] = T(0);
-    return;
-  }
-  const int gk = g * a.KK + k, GKK = a.G * a.KK;
-  const int oy = p / a.Wo, ox = p - (p / a.Wo) * a.Wo, i = k / a.K, j = k - (k / a.K) * a.K;
+__device__ __forceinline__ Geo sample_geo(const BwdArgs& a, int b, int g, int k, int p) {
+  Geo e;
+  const int GKK = a.G * a.KK, gk = g * a.KK + k;
+  const int oy = p / a.Wo, ox = p - (p / a.Wo) * a.Wo, ki = k / a.K, kj = k - (k / a.K) * a.K;
   const T* off = static_cast<const T*>(a.offset);
   const float dy = to_f(off[(static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p]);
   const float dx = to_f(off[(static_cast<size_t>(b) * 2 * GKK + 2 * gk + 1) * a.P + p]);
-  const float py = static_cast<float>(oy * a.stride - a.pad + i * a.dil) + dy;
-  const float px = static_cast<float>(ox * a.stride - a.pad + j * a.dil) + dx;
-  const float m = a.mask != nullptr ? to_f(static_cast<const T*>(a.mask)[(static_cast<size_t>(b) * GKK + gk) * a.P + p])
-                                    : 1.f;
-  // corners and weights; a position with no neighbour in the image (or NaN) has none.
-  // At py == -1 the cell is [-1, 0): row 0 has weight 0 but its derivative counts.
+  const float py = static_cast<float>(oy * a.stride - a.pad + ki * a.dil) + dy;
+  const float px = static_cast<float>(ox * a.stride - a.pad + kj * a.dil) + dx;
+  e.m = a.mask != nullptr ? to_f(static_cast<const T*>(a.mask)[(static_cast<size_t>(b) * GKK + gk) * a.P + p]) : 1.f;
   const bool any = py >= -1.f && py < static_cast<float>(a.H) && px >= -1.f && px < static_cast<float>(a.W);
   const float y0f = any ? floorf(py) : 0.f, x0f = any ? floorf(px) : 0.f;
-  const float ly = py - y0f, lx = px - x0f;
+  const float ly = any ? py - y0f : 0.f, lx = any ? px - x0f : 0.f;
   const int y0 = static_cast<int>(y0f), x0 = static_cast<int>(x0f);
   const bool iy0 = any && y0 >= 0, iy1 = any && y0 + 1 < a.H, ix0 = any && x0 >= 0, ix1 = any && x0 + 1 < a.W;
-  const bool in00 = iy0 && ix0, in01 = iy0 && ix1, in10 = iy1 && ix0, in11 = iy1 && ix1;
-  const float w00 = (1.f - ly) * (1.f - lx), w01 = (1.f - ly) * lx, w10 = ly * (1.f - lx), w11 = ly * lx;
-  const int q00 = y0 * a.W + x0;
-  const int HW = a.H * a.W;
-  const T* x = static_cast<const T*>(a.x);
+  e.fl = (iy0 && ix0 ? 1 : 0) | (iy0 && ix1 ? 2 : 0) | (iy1 && ix0 ? 4 : 0) | (iy1 && ix1 ? 8 : 0);
+  e.q00 = y0 * a.W + x0;
+  e.ly = ly;
+  e.lx = lx;
+  e.w00 = (1.f - ly) * (1.f - lx);
+  e.w01 = (1.f - ly) * lx;
+  e.w10 = ly * (1.f - lx);
+  e.w11 = ly * lx;
+  return e;
+}
+
+__device__ __forceinline__ int corner_dq(int n, int W) { return (n & 1) + (n >> 1) * W; }
+__device__ __forceinline__ float corner_w(const Geo& e, int n) {
+  return n == 0 ? e.w00 : n == 1 ? e.w01 : n == 2 ? e.w10 : e.w11;
+}
+__device__ __forceinline__ int int4_at(const int4& v, int n) { return n == 0 ? v.x : n == 1 ? v.y : n == 2 ? v.z : v.w; }
+
+// One thread per sample s = ((b*G + g)*K^2 + k)*P + p: each corner inside the image is
+// counted at its input pixel; the count before the increment is the pair's rank.
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_count(BwdArgs a) {
+  const int s = blockIdx.x * kBT + threadIdx.x;
+  if (s >= a.nsamp) return;
+  const int p = s % a.P;
+  int t = s / a.P;
+  const int k = t % a.KK;
+  t /= a.KK;
+  const int g = t % a.G, b = t / a.G;
+  const Geo e = sample_geo<T>(a, b, g, k, p);
+  int* c = a.cnt + (b * a.G + g) * a.H * a.W;
+  int r[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) r[n] = (e.fl >> n) & 1 ? atomicAdd(c + e.q00 + corner_dq(n, a.W), 1) : -1;
+  a.rank[s] = make_int4(r[0], r[1], r[2], r[3]);
+}
+
+// Exclusive prefix sums of cnt[0, n) within blocks of kScanB (in place); each block's
+// total to bsum[block].
+__global__ __launch_bounds__(kBT) void bwd_scan_blocks(int* cnt, int n, int* bsum) {
+  __shared__ int wsum[kBT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int base = blockIdx.x * kScanB + tid * 8;
+  int v[8], run = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = base + i;
+    const int c = j < n ? cnt[j] : 0;
+    v[i] = run;
+    run += c;
+  }
+  int inc = run;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(inc, d);
+    if (lane >= d) inc += u;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int woff = 0;
+  for (int w = 0; w < wv; ++w) woff += wsum[w];
+  const int off = woff + inc - run;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = base + i;
+    if (j < n) cnt[j] = v[i] + off;
+  }
+  if (tid == kBT - 1) bsum[blockIdx.x] = woff + inc;
+}
+
+// Exclusive prefix sums of bsum[0, nb) in place, one workgroup.
+__global__ __launch_bounds__(kBT) void bwd_scan_top(int* bsum, int nb) {
+  __shared__ int wsum[kBT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = 0;
+  for (int j0 = 0; j0 < nb; j0 += kBT) {
+    const int j = j0 + tid;
+    const int v = j < nb ? bsum[j] : 0;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(inc, d);
+      if (lane >= d) inc += u;
+    }
+    if (lane == 63) wsum[wv] = inc;
+    __syncthreads();
+    int woff = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kBT / 64; ++w) {
+      if (w < wv) woff += wsum[w];
+      total += wsum[w];
+    }
+    if (j < nb) bsum[j] = carry + woff + inc - v;
+    carry += total;
+    __syncthreads();
+  }
+}
+
+// first pair of input pixel i (flat over (b, group, pixel)); i + 1 gives the end
+__device__ __forceinline__ int pair_start(const BwdArgs& a, int i) { return a.cnt[i] + a.bsum[i / kScanB]; }
+
+// eight values from 8 consecutive elements (16- or 32-byte aligned) as fp32
+__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  const float4 q0 = *reinterpret_cast<const float4*>(p), q1 = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
+  v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float v[8]) {
+  uint32_t u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    u[i] = static_cast<uint32_t>(from_f<uint16_t>(v[2 * i])) | (static_cast<uint32_t>(from_f<uint16_t>(v[2 * i + 1])) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(u[0], u[1], u[2], u[3]);
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// One workgroup per (b, group, 64 output pixels, kernel point), kernel points fastest
+// and consecutive items on one XCD (the nine kernel points of a pixel block read
+// neighbouring corners).  A sample is taken by lg lanes, eight channels each (16-byte
+// channel vectors of xs and 32 bytes of its column-gradient row); with 256 channels,
+// 32 lanes and eight samples at a time.  The group's channels go in chunks of 256:
+// the chunk's column entries of the 64 pixels wait in LDS ([pixel][channel]) and leave
+// as rows of col (64 pixels of one (channel, kernel point) row per 128 bytes).  The
+// offset and mask sums of a chunk are summed over the sample's lanes, and carried from
+// chunk to chunk in LDS by the sample's first lane.
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_sample_cl(BwdArgs a) {
+  constexpr int ES = sizeof(T), VE = 16 / ES;   // elements per 16-byte vector
+  constexpr int TP = kCC + VE;                   // LDS pitch of one pixel's entries
+  __shared__ __attribute__((aligned(16))) T tile[kSP * TP];
+  __shared__ float sacc[3][kSP];   // offset (y, x) and mask sums of the chunks so far
+  const int tid = threadIdx.x;
+  int t = xcd_item(blockIdx.x, a.B * a.G * a.npb * a.KK);
+  const int k = t % a.KK;
+  t /= a.KK;
+  const int pb = t % a.npb;
+  t /= a.npb;
+  const int g = t % a.G, b = t / a.G;
+  const int LG = a.lg, li = tid & (LG - 1), si = tid / LG, SPI = kBT / LG;
+  const int nit = (kSP + SPI - 1) / SPI;
   const bool grads = a.gcol != nullptr;
-  float gm = 0.f, goy = 0.f, gox = 0.f;
-  for (int c = c0; c < c1; ++c) {
-    const size_t pl = (static_cast<size_t>(b) * a.Cin + c) * HW;
-    const float v00 = in00 ? to_f(x[pl + q00]) : 0.f;
-    const float v01 = in01 ? to_f(x[pl + q00 + 1]) : 0.f;
-    const float v10 = in10 ? to_f(x[pl + q00 + a.W]) : 0.f;
-    const float v11 = in11 ? to_f(x[pl + q00 + a.W + 1]) : 0.f;
-    const float s = w00 * v00 + w01 * v01 + w10 * v10 + w11 * v11;
-    const size_t r = static_cast<size_t>(b) * a.R + c * a.KK + k;
-    if (col != nullptr) col[r * a.Pp + p] = from_f<T>(m * s);
-    if (grads) {
-      const float gc = a.gcol[r * a.P + p];
-      gm += gc * s;
-      goy += gc * ((1.f - lx) * (v10 - v00) + lx * (v11 - v01));
-      gox += gc * ((1.f - ly) * (v01 - v00) + ly * (v11 - v10));
-      if (a.gx32 != nullptr) {
-        const float tg = gc * m;
-        float* gx = a.gx32 + pl + q00;
-        if (in00) unsafeAtomicAdd(gx, tg * w00);
-        if (in01) unsafeAtomicAdd(gx + 1, tg * w01);
-        if (in10) unsafeAtomicAdd(gx + a.W, tg * w10);
-        if (in11) unsafeAtomicAdd(gx + a.W + 1, tg * w11);
+  const bool vec = a.Cg % 8 == 0;
+  T* col = static_cast<T*>(a.col);
+  const T* xs = static_cast<const T*>(a.xs) + static_cast<size_t>(b) * a.H * a.W * a.Cp + g * a.Cg;
+  const int GKK = a.G * a.KK, gk = g * a.KK + k;
+  for (int cc0 = 0; cc0 < a.Cg; cc0 += kCC) {
+    const int ccn = min(kCC, a.Cg - cc0);
+    for (int it = 0; it < nit; ++it) {
+      const int pl = it * SPI + si, p = pb * kSP + pl;
+      if (pl >= kSP || p >= a.P) continue;
+      const Geo e = sample_geo<T>(a, b, g, k, p);
+      const int row = (b * a.P + p) * a.KK + k;   // the sample's column-gradient row
+      const float* gcr = grads ? a.gcol + static_cast<size_t>(row) * a.Cin + g * a.Cg + cc0 : nullptr;
+      const T* xq = xs + cc0;
+      float gm = 0.f, goy = 0.f, gox = 0.f;
+      for (int c8 = li * 8; c8 < ccn; c8 += LG * 8) {
+        float v[4][8], gc[8];
+        if (vec) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            if ((e.fl >> n) & 1) {
+              load8(xq + static_cast<size_t>(e.q00 + corner_dq(n, a.W)) * a.Cp + c8, v[n]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v[n][j] = 0.f;
+            }
+          }
+          if (grads) {
+            load8(gcr + c8, gc);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) gc[j] = 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const bool in = c8 + j < ccn;
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+              v[n][j] = in && ((e.fl >> n) & 1) ? to_f(xq[static_cast<size_t>(e.q00 + corner_dq(n, a.W)) * a.Cp + c8 + j]) : 0.f;
+            gc[j] = in && grads ? gcr[c8 + j] : 0.f;
+          }
+        }
+        float cv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float v00 = v[0][j], v01 = v[1][j], v10 = v[2][j], v11 = v[3][j];
+          const float sv = e.w00 * v00 + e.w01 * v01 + e.w10 * v10 + e.w11 * v11;
+          cv[j] = e.m * sv;
+          gm += gc[j] * sv;
+          goy += gc[j] * ((1.f - e.lx) * (v10 - v00) + e.lx * (v11 - v01));
+          gox += gc[j] * ((1.f - e.ly) * (v01 - v00) + e.ly * (v11 - v10));
+        }
+        if (col != nullptr) {
+          T* dst = tile + pl * TP + c8;
+          if (vec) {
+            store8(dst, cv);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (c8 + j < ccn) dst[j] = from_f<T>(cv[j]);
+          }
+        }
+      }
+      if (grads) {   // the sums over the sample's lanes (all lanes of a sample share pl)
+        for (int d = LG >> 1; d >= 1; d >>= 1) {
+          gm += __shfl_xor(gm, d);
+          goy += __shfl_xor(goy, d);
+          gox += __shfl_xor(gox, d);
+        }
+        if (li == 0) {
+          if (cc0 > 0) {
+            goy += sacc[0][pl];
+            gox += sacc[1][pl];
+            gm += sacc[2][pl];
+          }
+          if (cc0 + kCC < a.Cg) {
+            sacc[0][pl] = goy;
+            sacc[1][pl] = gox;
+            sacc[2][pl] = gm;
+          } else {
+            if (a.grad_offset != nullptr) {
+              T* go = static_cast<T*>(a.grad_offset) + (static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p;
+              go[0] = from_f<T>(goy * e.m);
+              go[a.P] = from_f<T>(gox * e.m);
+            }
+            if (a.grad_mask != nullptr)
+              static_cast<T*>(a.grad_mask)[(static_cast<size_t>(b) * GKK + gk) * a.P + p] = from_f<T>(gm);
+          }
+        }
+      }
+      // the sample's pairs, once: lanes li, li + lg, ... < 4 take corners li, ...
+      if (cc0 == 0 && a.pairs != nullptr) {
+        const int4 rk = a.rank[((b * a.G + g) * a.KK + k) * a.P + p];
+        const int i0 = (b * a.G + g) * a.H * a.W + e.q00;
+        for (int n = li; n < 4; n += LG) {
+          const int rn = int4_at(rk, n);
+          if (rn >= 0) {
+            const int i = i0 + corner_dq(n, a.W);
+            a.pairs[pair_start(a, i) + rn] = make_int2(row, __float_as_int(e.m * corner_w(e, n)));
+          }
+        }
       }
     }
-  }
-  if (grads) {
-    if (a.goff32 != nullptr) {
-      float* go = a.goff32 + (static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p;
-      unsafeAtomicAdd(go, goy * m);
-      unsafeAtomicAdd(go + a.P, gox * m);
+    if (col != nullptr) {
+      __syncthreads();
+      // rows (channel, kernel point) of col: 16 bytes (VE pixels) per thread, channels
+      // fastest over the threads (an LDS read of 64 neighbouring channels of one pixel)
+      const int ng = kSP / VE;
+      for (int idx = tid; idx < ccn * ng; idx += kBT) {
+        const int c = idx % ccn, pg = idx / ccn;
+        const int p0 = pb * kSP + pg * VE;
+        if (p0 >= a.Pp) continue;
+        T vals[VE];
+#pragma unroll
+        for (int j = 0; j < VE; ++j) vals[j] = p0 + j < a.P ? tile[(pg * VE + j) * TP + c] : T(0);
+        const size_t r = static_cast<size_t>(b) * a.R + static_cast<size_t>(g * a.Cg + cc0 + c) * a.KK + k;
+        uint4 q;
+        __builtin_memcpy(&q, vals, 16);
+        *reinterpret_cast<uint4*>(col + r * a.Pp + p0) = q;
+      }
+      __syncthreads();
     }
-    if (a.gm32 != nullptr) unsafeAtomicAdd(a.gm32 + (static_cast<size_t>(b) * GKK + gk) * a.P + p, gm);
+  }
+}
+
+// One workgroup per (b, group, 256-channel chunk, 64 input pixels), consecutive pixel
+// blocks on one XCD.  lg lanes per pixel, eight channels each: the sum over the pixel's
+// pairs of weight * its column-gradient row (four pairs' loads issued together), then
+// the chunk's sums leave through LDS ([channel][pixel]) as runs of 64 pixels per channel.
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_gather_cl(BwdArgs a) {
+  constexpr int GP = kGP + 1;   // LDS pitch of one channel's pixels
+  __shared__ T tile[kCC * GP];
+  const int tid = threadIdx.x, HW = a.H * a.W;
+  int t = xcd_item(blockIdx.x, a.B * a.G * a.ncc * a.nqb);
+  const int qb = t % a.nqb;
+  t /= a.nqb;
+  const int ci = t % a.ncc;
+  t /= a.ncc;
+  const int g = t % a.G, b = t / a.G;
+  const int cc0 = ci * kCC, ccn = min(kCC, a.Cg - cc0);
+  const int LG = a.lg, li = tid & (LG - 1), si = tid / LG, SPI = kBT / LG;
+  const int nit = (kGP + SPI - 1) / SPI;
+  const bool vec = a.Cg % 8 == 0;
+  const int ib = (b * a.G + g) * HW;
+  const float* gsrc = a.gcol + g * a.Cg + cc0;
+  for (int it = 0; it < nit; ++it) {
+    const int pl = it * SPI + si, q = qb * kGP + pl;
+    if (pl >= kGP || q >= HW) continue;
+    const int e0 = pair_start(a, ib + q), e1 = pair_start(a, ib + q + 1);
+    for (int c8 = li * 8; c8 < ccn; c8 += LG * 8) {
+      float acc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+      int e = e0;
+      if (vec) {
+        for (; e + 4 <= e1; e += 4) {
+          int2 pr[4];
+          float v[4][8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) pr[u] = a.pairs[e + u];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) load8(gsrc + static_cast<size_t>(pr[u].x) * a.Cin + c8, v[u]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float wm = __int_as_float(pr[u].y);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] += wm * v[u][j];
+          }
+        }
+        for (; e < e1; ++e) {
+          const int2 pr = a.pairs[e];
+          float v[8];
+          load8(gsrc + static_cast<size_t>(pr.x) * a.Cin + c8, v);
+          const float wm = __int_as_float(pr.y);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] += wm * v[j];
+        }
+      } else {
+        for (; e < e1; ++e) {
+          const int2 pr = a.pairs[e];
+          const float wm = __int_as_float(pr.y);
+          const float* src = gsrc + static_cast<size_t>(pr.x) * a.Cin + c8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c8 + j < ccn) acc[j] += wm * src[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c8 + j < ccn) tile[(c8 + j) * GP + pl] = from_f<T>(acc[j]);
+    }
+  }
+  __syncthreads();
+  T* gx = static_cast<T*>(a.grad_x) + (static_cast<size_t>(b) * a.Cin + g * a.Cg + cc0) * HW;
+  for (int idx = tid; idx < ccn * kGP; idx += kBT) {
+    const int c = idx / kGP, px = idx - (idx / kGP) * kGP, q = qb * kGP + px;
+    if (q < HW) gx[static_cast<size_t>(c) * HW + q] = tile[c * GP + px];
   }
 }
 
@@ -662,13 +728,9 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Workspace layout of one backward call.
 struct BwdPlan {
-  int64_t Ho = 0, Wo = 0, P = 0, Pp = 0, Coutp = 0, R = 0, G = 1;
-  size_t o_wt = 0, o_gyt = 0, o_gyp = 0, o_col = 0, o_gcol = 0, o_gx = 0, o_gw = 0, o_goff = 0, o_gm = 0, o_gb = 0;
-  size_t o_flag = 0;
-  int64_t TY = 0, TX = 0, BH = 0, BW = 0;
-  int CBL = 0;
-  bool tiled = false;
-  size_t o_gbox = 0;
+  int64_t Ho = 0, Wo = 0, P = 0, Pp = 0, Coutp = 0, R = 0, G = 1, Cp = 0, ncnt = 0, nblk = 0, nsamp = 0;
+  size_t o_wt = 0, o_gyt = 0, o_gyp = 0, o_col = 0, o_gcol = 0, o_xs = 0, o_gw = 0, o_gb = 0;
+  size_t o_cnt = 0, o_bsum = 0, o_rank = 0, o_pairs = 0;
   size_t bytes = 0;
 };
 
@@ -676,16 +738,22 @@ int bwd_plan(const dcn_desc* d, BwdPlan* p) {
   int rc = check_desc(d, &p->Ho, &p->Wo);
   if (rc != DCN_OK) return rc;
   const int64_t B = d->batch, Cin = d->in_channels, Cout = d->out_channels, KK = d->kernel_size * d->kernel_size;
+  const int64_t HW = d->height * d->width;
   p->G = d->offset_groups > 1 ? d->offset_groups : 1;
   p->P = p->Ho * p->Wo;
   p->Pp = rup(p->P, 8);
   p->Coutp = rup(Cout > 0 ? Cout : 1, 8);
   p->R = Cin * KK;
+  p->Cp = rup(Cin, 8);
+  p->nsamp = B * p->G * KK * p->P;
+  p->ncnt = B * p->G * HW + 1;
+  p->nblk = (p->ncnt + kScanB - 1) / kScanB;
   const double lim = 2147483647.0;
   const double Bd = static_cast<double>(B);
-  if (Bd * p->R * p->Pp > lim || Bd * Cin * d->height * d->width > lim || Bd * p->Coutp * p->Pp > lim ||
+  if (Bd * p->R * p->Pp > lim || Bd * Cin * HW > lim || Bd * p->Coutp * p->Pp > lim ||
       static_cast<double>(p->R) * p->Coutp > lim || Bd * 2 * p->G * KK * p->P > lim ||
-      static_cast<double>(Cout) * p->R > lim)
+      static_cast<double>(Cout) * p->R > lim || Bd * HW * p->Cp > lim || 4.0 * p->nsamp > lim ||
+      static_cast<double>(p->ncnt) > lim)
     return DCN_E_UNSUPPORTED;
   const size_t es = d->dtype == DCN_BF16 ? 2 : 4;
   size_t o = 0;
@@ -698,23 +766,14 @@ int bwd_plan(const dcn_desc* d, BwdPlan* p) {
   p->o_gyt = take(static_cast<size_t>(B * p->P * p->Coutp) * es);
   p->o_gyp = take(static_cast<size_t>(B * Cout * p->Pp) * es);
   p->o_col = take(static_cast<size_t>(B * p->R * p->Pp) * es);
-  p->o_gcol = take(static_cast<size_t>(B * p->R * p->P) * 4);
-  p->o_gx = take(static_cast<size_t>(B * Cin * d->height * d->width) * 4);
+  p->o_gcol = take(static_cast<size_t>(B * p->P * p->R) * 4);
+  p->o_xs = take(static_cast<size_t>(B * HW * p->Cp) * es);
   p->o_gw = take(static_cast<size_t>(Cout * p->R) * 4);
-  p->o_goff = take(static_cast<size_t>(B * 2 * p->G * KK * p->P) * 4);
-  p->o_gm = take(static_cast<size_t>(B * p->G * KK * p->P) * 4);
   p->o_gb = take(static_cast<size_t>(Cout) * 4);
-  p->o_flag = take(4);
-  // tiled sampling: K^2 <= 28 (seven samples per thread at most) and a box of at
-  // least four channels in 64 KB of LDS
-  p->TY = (p->Ho + kTH - 1) / kTH;
-  p->TX = (p->Wo + kTW - 1) / kTW;
-  p->BH = (kTH - 1) * d->stride + (d->kernel_size - 1) * d->dilation + 2 + 2 * kMargin;
-  p->BW = (kTW - 1) * d->stride + (d->kernel_size - 1) * d->dilation + 2 + 2 * kMargin;
-  const double box_elems = static_cast<double>(B) * Cin * p->TY * p->TX * p->BH * p->BW;
-  p->CBL = 1;
-  p->tiled = KK <= 28 && p->BH * p->BW <= 1536 && box_elems <= lim;
-  if (p->tiled) p->o_gbox = take(static_cast<size_t>(box_elems) * 4);
+  p->o_cnt = take(static_cast<size_t>(p->ncnt) * 4);
+  p->o_bsum = take(static_cast<size_t>(p->nblk) * 4);
+  p->o_rank = take(static_cast<size_t>(p->nsamp) * 16);
+  p->o_pairs = take(static_cast<size_t>(p->nsamp) * 4 * 8);
   p->bytes = o;
   return DCN_OK;
 }
@@ -744,14 +803,6 @@ hipError_t launch_ranges(const void* fn, int per_thread, std::initializer_list<s
 }
 
 template <typename T>
-hipError_t convert(const float* src, void* dst, int64_t n, hipStream_t s) {
-  T* d = static_cast<T*>(dst);
-  int nn = static_cast<int>(n);
-  void* args[] = {&src, &d, &nn};
-  return launch1(reinterpret_cast<const void*>(&bwd_convert<T>), n, args, s);
-}
-
-template <typename T>
 hipError_t gemm(const GemmArgs<T>& g, int zb, hipStream_t s) {
   GemmArgs<T> gg = g;
   void* args[] = {&gg};
@@ -769,8 +820,8 @@ template <typename T>
 int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void* offset, const void* mask,
                  const void* weight, const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
                  void* grad_weight, void* grad_bias, unsigned char* ws, hipStream_t s) {
+  constexpr bool kBF16 = sizeof(T) == 2;
   BwdArgs a{};
-  a.x = x;
   a.offset = offset;
   a.mask = mask;
   a.w = weight;
@@ -793,89 +844,94 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
   a.R = static_cast<int>(p.R);
   a.G = static_cast<int>(p.G);
   a.Cg = a.Cin / a.G;
-  a.NCB = (a.Cg + kCB - 1) / kCB;
+  a.Cp = static_cast<int>(p.Cp);
+  a.nsamp = static_cast<int>(p.nsamp);
+  const int cch = std::min(a.Cg, kCC);
+  a.lg = 1;
+  while (a.lg < 32 && a.lg * 8 < cch) a.lg *= 2;
+  a.npb = (a.P + kSP - 1) / kSP;
+  a.nqb = (a.H * a.W + kGP - 1) / kGP;
+  a.ncc = (a.Cg + kCC - 1) / kCC;
   const bool need_gcol = grad_x != nullptr || grad_offset != nullptr || (grad_mask != nullptr && mask != nullptr);
+  const bool sample = need_gcol || grad_weight != nullptr;
+  a.xs = ws + p.o_xs;
   a.wt = ws + p.o_wt;
   a.gyt = need_gcol ? static_cast<void*>(ws + p.o_gyt) : nullptr;
   a.gyp = grad_weight != nullptr ? static_cast<void*>(ws + p.o_gyp) : nullptr;
-  a.gb32 = grad_bias != nullptr ? reinterpret_cast<float*>(ws + p.o_gb) : nullptr;
-  a.outliers = reinterpret_cast<float*>(ws + p.o_flag);
   a.col = grad_weight != nullptr ? static_cast<void*>(ws + p.o_col) : nullptr;
   a.gcol = need_gcol ? reinterpret_cast<float*>(ws + p.o_gcol) : nullptr;
-  a.gx32 = grad_x != nullptr ? reinterpret_cast<float*>(ws + p.o_gx) : nullptr;
-  a.goff32 = grad_offset != nullptr ? reinterpret_cast<float*>(ws + p.o_goff) : nullptr;
-  a.gm32 = (grad_mask != nullptr && mask != nullptr) ? reinterpret_cast<float*>(ws + p.o_gm) : nullptr;
+  a.gb32 = grad_bias != nullptr ? reinterpret_cast<float*>(ws + p.o_gb) : nullptr;
+  a.grad_offset = grad_offset;
+  a.grad_mask = mask != nullptr ? grad_mask : nullptr;
+  a.grad_x = grad_x;
+  if (grad_x != nullptr) {
+    a.cnt = reinterpret_cast<int*>(ws + p.o_cnt);
+    a.bsum = reinterpret_cast<int*>(ws + p.o_bsum);
+    a.rank = reinterpret_cast<int4*>(ws + p.o_rank);
+    a.pairs = reinterpret_cast<int2*>(ws + p.o_pairs);
+  }
   float* gw32 = reinterpret_cast<float*>(ws + p.o_gw);
-  const int64_t nx = static_cast<int64_t>(a.B) * a.Cin * a.H * a.W;
-  const int64_t noff = static_cast<int64_t>(a.B) * 2 * a.G * a.KK * a.P;
-  const int64_t nm = noff / 2;
   const int64_t nw = static_cast<int64_t>(a.Cout) * a.R;
   void* args[] = {&a};
 
-  if (need_gcol) {
-    BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_prep_w<T>), static_cast<int64_t>(a.R) * a.Coutp, args, s));
+  if (sample) {   // x channels last, with the forward's staging kernel (no weight to repack)
+    StageArgs sa{};
+    sa.x = x;
+    sa.xs = ws + p.o_xs;
+    sa.B = a.B;
+    sa.Cin = a.Cin;
+    sa.HW = a.H * a.W;
+    sa.Cp = a.Cp;
+    sa.KK = 1;
+    BWD_TRY(launch_stage(kBF16 ? V_TILE_BF16_M64_N64 : V_TILE_F32_M64_N64, sa, s));
   }
-  // every fp32 accumulator zeroed by one launch (before prep_gy adds the bias sums)
+  if (need_gcol) {
+    const dim3 grid(static_cast<unsigned>((a.R + 31) / 32), static_cast<unsigned>((a.Coutp + 31) / 32));
+    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_w<T>), grid, dim3(kBT), args, 0, s));
+  }
+  // the fp32 accumulators and the pair counters zeroed by one launch (before prep_gy
+  // adds the bias sums)
   BWD_TRY(launch_ranges(reinterpret_cast<const void*>(&bwd_fill_zero_ranges), 4,
-                        {{a.gx32, nullptr, nx}, {a.goff32, nullptr, noff}, {a.gm32, nullptr, nm},
-                         {grad_weight != nullptr ? gw32 : nullptr, nullptr, nw}, {a.gb32, nullptr, a.Cout},
-                         {a.outliers, nullptr, 1}},
+                        {{grad_weight != nullptr ? gw32 : nullptr, nullptr, nw}, {a.gb32, nullptr, a.Cout},
+                         {reinterpret_cast<float*>(a.cnt), nullptr, p.ncnt}},
                         s));
-  if (need_gcol || grad_weight != nullptr || grad_bias != nullptr) {
+  if (sample || grad_bias != nullptr) {
     const dim3 grid(static_cast<unsigned>((a.Pp + 31) / 32), static_cast<unsigned>((a.Coutp + 31) / 32),
                     static_cast<unsigned>(a.B));
     BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_gy<T>), grid, dim3(kBT), args, 0, s));
   }
-  if (need_gcol) {
+  if (grad_x != nullptr) {
+    BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_count<T>), a.nsamp, args, s));
+    int n = static_cast<int>(p.ncnt), nb = static_cast<int>(p.nblk);
+    void* s1[] = {&a.cnt, &n, &a.bsum};
+    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_scan_blocks), dim3(nb), dim3(kBT), s1, 0, s));
+    void* s2[] = {&a.bsum, &nb};
+    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_scan_top), dim3(1), dim3(kBT), s2, 0, s));
+  }
+  if (need_gcol) {   // gcol[b][p][r'] = sum_o gyT[b][p][o] * Wt[r'][o], r' = k*Cin + c
     GemmArgs<T> g{};
-    g.A = static_cast<const T*>(a.wt);
-    g.Bm = static_cast<const T*>(a.gyt);
+    g.A = static_cast<const T*>(a.gyt);
+    g.Bm = static_cast<const T*>(a.wt);
     g.C = a.gcol;
-    g.M = a.R;
-    g.N = a.P;
+    g.M = a.P;
+    g.N = a.R;
     g.Kd = a.Coutp;
     g.lda = g.ldb = a.Coutp;
-    g.ldc = a.P;
+    g.ldc = a.R;
     g.nseg = 1;
     g.ksplit = 1;
-    g.sAz = 0;
-    g.sBz = static_cast<long long>(a.P) * a.Coutp;
-    g.sCz = static_cast<long long>(a.R) * a.P;
+    g.sAz = static_cast<long long>(a.P) * a.Coutp;
+    g.sBz = 0;
+    g.sCz = static_cast<long long>(a.P) * a.R;
     BWD_TRY(gemm<T>(g, a.B, s));
   }
-  if ((need_gcol || grad_weight != nullptr) && p.tiled) {
-    a.gbox = reinterpret_cast<float*>(ws + p.o_gbox);
-    a.TY = static_cast<int>(p.TY);
-    a.TX = static_cast<int>(p.TX);
-    a.BH = static_cast<int>(p.BH);
-    a.BW = static_cast<int>(p.BW);
-    a.CBL = p.CBL;
-    // split each group's channels until there are about four workgroups per CU
-    const int64_t wgs = static_cast<int64_t>(a.B) * a.G * a.TY * a.TX;
-    int ns = 1;
-    while (wgs * ns < 1024 && (a.Cg + ns * 2 - 1) / (ns * 2) >= 16) ns *= 2;
-    a.cps = (a.Cg + ns - 1) / ns;
-    a.nsplit = (a.Cg + a.cps - 1) / a.cps;
-    if (grad_weight != nullptr && a.Pp > a.P) {   // zero padding of the columns
-      const int64_t n = static_cast<int64_t>(a.B) * a.R;
-      T* colp = static_cast<T*>(a.col);
-      int rows = static_cast<int>(n), P = a.P, Pp = a.Pp;
-      void* pargs[] = {&colp, &rows, &P, &Pp};
-      BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_col_pad<T>), n, pargs, s));
-    }
-    // LDS: the sorted pairs (weight, sample), the bin starts, two halves of gcol * m
-    // (three samples per thread: four channels per step; seven: one)
-    const int nsmp = a.KK <= 12 ? 3 : 7, cq = a.KK <= 12 ? 4 : 1;
-    const size_t lds = static_cast<size_t>(nsmp) * kBT * 4 * 6 + ((a.BH * a.BW + 1) * 4 + 15) / 16 * 16 +
-                       static_cast<size_t>(2) * cq * nsmp * kBT * 4;
-    a.tiles_total = static_cast<int>(wgs * a.nsplit);
-    const unsigned grid = static_cast<unsigned>((a.tiles_total + 7) / 8 * 8);
-    const void* fn = a.KK <= 12 ? reinterpret_cast<const void*>(&bwd_sample_tile<T, 3, 4>)
-                                : reinterpret_cast<const void*>(&bwd_sample_tile<T, 7, 1>);
-    BWD_TRY(hipLaunchKernel(fn, dim3(grid), dim3(kBT), args, lds, s));
-  } else if (need_gcol || grad_weight != nullptr) {
-    const int64_t n = static_cast<int64_t>(a.B) * a.G * a.NCB * a.KK * a.Pp;
-    BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_sample<T>), n, args, s));
+  if (sample) {
+    const unsigned grid = static_cast<unsigned>(a.B * a.G * a.npb * a.KK);
+    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_sample_cl<T>), dim3(grid), dim3(kBT), args, 0, s));
+  }
+  if (grad_x != nullptr) {
+    const unsigned grid = static_cast<unsigned>(a.B * a.G * a.ncc * a.nqb);
+    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_gather_cl<T>), dim3(grid), dim3(kBT), args, 0, s));
   }
   if (grad_weight != nullptr) {
     GemmArgs<T> g{};
@@ -899,20 +955,9 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     g.ksplit = ks;
     BWD_TRY(gemm<T>(g, 1, s));
   }
-  if (a.gx32 != nullptr) {
-    if (p.tiled) {
-      T* gxo = static_cast<T*>(grad_x);
-      void* gargs[] = {&a, &gxo};
-      BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_gather_x<T>), nx, gargs, s));
-    } else {
-      BWD_TRY(convert<T>(a.gx32, grad_x, nx, s));
-    }
-  }
-  // the other fp32 accumulators to the element type, one launch
+  // the weight and bias accumulators to the element type, one launch
   BWD_TRY(launch_ranges(reinterpret_cast<const void*>(&bwd_convert_ranges<T>), 1,
-                        {{grad_weight != nullptr ? gw32 : nullptr, grad_weight, nw}, {a.goff32, grad_offset, noff},
-                         {a.gm32, grad_mask, nm}, {a.gb32, grad_bias, a.Cout}},
-                        s));
+                        {{grad_weight != nullptr ? gw32 : nullptr, grad_weight, nw}, {a.gb32, grad_bias, a.Cout}}, s));
   return DCN_OK;
 }
 
