@@ -32,7 +32,7 @@
 //            rank in that pixel's list
 //   scan     exclusive prefix sums of the counts: per block of 2048, then the block sums
 //   gemm     gcol[b] = gyT[b] x Wt^T, channels fastest: [B][P][K^2][Cin] (MFMA)
-//   sample   per (b, group, kernel point, 64 output pixels): the corners from xs as
+//   sample   per (b, group, kernel point, 16 output pixels): the corners from xs as
 //            16-byte channel vectors; the column entries, transposed through LDS to
 //            col [B][R][Pp] for the weight gradient; the offset and mask gradients summed
 //            over the group's channels across the lanes of the sample and written once;
@@ -65,10 +65,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBT = 256;     // threads per workgroup
-constexpr int kSP = 64;      // output pixels per workgroup of the sampling kernel (one kernel point)
-constexpr int kGP = 64;      // input pixels per workgroup of the gather kernel
-constexpr int kCC = 256;     // channels per chunk of the sampling and gather kernels
+constexpr int kSP = 16;      // output pixels per workgroup of the sampling kernel (one kernel point)
+constexpr int kGH = 1, kGW = 8;   // input tile (rows x columns) of a workgroup of the gather kernel
+constexpr int kGP = kGH * kGW;
+constexpr int kCC = 256;     // channels per chunk of the sampling and gather kernels (32 lanes x 8)
 constexpr int kScanB = 2048; // counts per block of the first scan pass (256 threads x 8)
+static_assert(kSP * 4 <= kBT, "the sampling kernel places four corners per sample with one thread each");
 
 template <typename T>
 __device__ __forceinline__ float to_f(T v);
@@ -84,6 +86,16 @@ __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ uint16_t from_f<uint16_t>(float v) {   // round to nearest even
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+// A workgroup barrier that orders LDS traffic only: global loads and stores issued
+// before it stay in flight across it (a plain __syncthreads also waits for those).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Workgroup id -> work item, so that consecutive items run on the same XCD (workgroups
@@ -105,7 +117,8 @@ struct BwdArgs {
   void* gyt;            // [B][P][Coutp]
   void* gyp;            // [B][Cout][Pp]
   void* col;            // [B][R][Pp] or null (no weight gradient)
-  float* gcol;          // [B][P][K^2][Cin] or null (no input, offset or mask gradient)
+  void* gcol;           // [B][P][K^2][Cin] in the element type, or null (no input, offset or
+                        // mask gradient)
   float* gb32;          // [Cout] or null (bias gradient accumulator)
   void* grad_offset;    // [B][2GK^2][Ho][Wo] or null
   void* grad_mask;      // [B][GK^2][Ho][Wo] or null
@@ -118,8 +131,8 @@ struct BwdArgs {
   int B, Cin, H, W, Cout, K, KK, stride, pad, dil, Ho, Wo, P, Pp, Coutp, R, G, Cg, Cp;
   int lg;               // lanes per sample (sampling) or pixel (gather): a power of two
                         // <= 32, eight channels per lane
-  int npb;              // 64-pixel blocks of the output plane
-  int nqb;              // 64-pixel blocks of the input plane
+  int npb;              // kSP-pixel blocks of the output plane
+  int nqy, nqx;         // kGH x kGW tiles of the input plane (rows, columns)
   int ncc;              // 256-channel chunks of a group
   int nsamp;            // B * G * K^2 * P
 };
@@ -184,7 +197,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_gy(BwdArgs a) {
   }
 }
 
-// Up to six fp32 ranges zeroed (or converted) by one launch; the workgroups are
+// Up to six fp32 ranges zeroed by one launch; the workgroups are
 // split over the ranges in proportion to their sizes (blocks[i] workgroups for range i).
 struct Ranges {
   float* p[6];
@@ -204,17 +217,28 @@ __global__ __launch_bounds__(kBT) void bwd_fill_zero_ranges(Ranges r) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(kBT) void bwd_convert_ranges(Ranges r) {
-  int blk = blockIdx.x, i = 0;
-  while (i + 1 < r.count && blk >= r.blocks[i]) blk -= r.blocks[i++];
-  const int e = blk * kBT + static_cast<int>(threadIdx.x);
-  if (e < r.n[i]) static_cast<T*>(r.dst[i])[e] = from_f<T>(r.p[i][e]);
-}
-
-template <typename T>
 __global__ __launch_bounds__(kBT) void bwd_fill_zero_t(T* p, int n) {
   const int e = blockIdx.x * kBT + threadIdx.x;
   if (e < n) p[e] = T(0);
+}
+
+// Data-parallel-primitive lane moves: v from lane (lane permuted by CTRL) of the same row
+// of 16 lanes.  0xB1: quad_perm [1,0,3,2] (lane ^ 1); 0x4E: quad_perm [2,3,0,1] (lane ^ 2);
+// 0x141: row_half_mirror (lane 7 - i within each 8 lanes); 0x140: row_mirror (lane 15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+// The sum of v over an aligned group of lg lanes (a power of two <= 32), in every lane of
+// the group: each step adds the value of a lane in the other half of a group twice the
+// size, whose lanes already agree.
+__device__ __forceinline__ float group_sum(float v, int lg) {
+  if (lg >= 2) v += dpp_move<0xB1>(v);
+  if (lg >= 4) v += dpp_move<0x4E>(v);
+  if (lg >= 8) v += dpp_move<0x141>(v);
+  if (lg >= 16) v += dpp_move<0x140>(v);
+  if (lg >= 32) v += __shfl_xor(v, 16);
+  return v;
 }
 
 // One sample's geometry: its corners inside the image (bit n of fl: corner n of 00, 01,
@@ -369,21 +393,27 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// One workgroup per (b, group, 64 output pixels, kernel point), kernel points fastest
-// and consecutive items on one XCD (the nine kernel points of a pixel block read
-// neighbouring corners).  A sample is taken by lg lanes, eight channels each (16-byte
-// channel vectors of xs and 32 bytes of its column-gradient row); with 256 channels,
-// 32 lanes and eight samples at a time.  The group's channels go in chunks of 256:
-// the chunk's column entries of the 64 pixels wait in LDS ([pixel][channel]) and leave
-// as rows of col (64 pixels of one (channel, kernel point) row per 128 bytes).  The
-// offset and mask sums of a chunk are summed over the sample's lanes, and carried from
-// chunk to chunk in LDS by the sample's first lane.
+// One workgroup per (b, group, kSP output pixels, kernel point), kernel points fastest
+// and consecutive items on one XCD (the kernel points of a pixel block read neighbouring
+// corners).  Small items keep the dispatcher's tail short and, with few registers (no
+// sample's loads kept across another's), five waves per SIMD in flight.  First, four
+// threads per sample: the sample's geometry (to LDS) and, one corner each, the position
+// of its pair in its input pixel's list (the pair is stored after the channel work,
+// whose first loads overlap these).  Then a sample is taken by lg lanes, eight channels
+// each (16-byte channel vectors of xs and of its column-gradient row), all its loads
+// issued together; with 256 channels, 32 lanes and eight samples at a time.  The group's
+// channels go in chunks of 256: the chunk's column entries of the block wait in LDS
+// ([pixel][channel]) and leave as row segments of col (kSP pixels of one (channel,
+// kernel point) row).  The corner sums of a chunk are summed over the sample's lanes,
+// and carried from chunk to chunk in LDS by the sample's first lane.
 template <typename T>
 __global__ __launch_bounds__(kBT) void bwd_sample_cl(BwdArgs a) {
   constexpr int ES = sizeof(T), VE = 16 / ES;   // elements per 16-byte vector
   constexpr int TP = kCC + VE;                   // LDS pitch of one pixel's entries
   __shared__ __attribute__((aligned(16))) T tile[kSP * TP];
-  __shared__ float sacc[3][kSP];   // offset (y, x) and mask sums of the chunks so far
+  __shared__ float sacc[4][kSP];   // corner sums of the chunks so far
+  __shared__ float sgeo[7][kSP];   // w00, w01, w10, w11, ly, lx, m of each sample
+  __shared__ int sfl[kSP], sq[kSP];
   const int tid = threadIdx.x;
   int t = xcd_item(blockIdx.x, a.B * a.G * a.npb * a.KK);
   const int k = t % a.KK;
@@ -391,114 +421,158 @@ __global__ __launch_bounds__(kBT) void bwd_sample_cl(BwdArgs a) {
   const int pb = t % a.npb;
   t /= a.npb;
   const int g = t % a.G, b = t / a.G;
+  const int GKK = a.G * a.KK, gk = g * a.KK + k;
+  // this thread's pair: sample tid / 4, corner tid % 4 (pos < 0: none)
+  int pos = -1, prow = 0;
+  float pw = 0.f;
+  if (tid < 4 * kSP) {
+    const int pl = tid >> 2, n = tid & 3, p = pb * kSP + pl;
+    if (p < a.P) {
+      const Geo e = sample_geo<T>(a, b, g, k, p);
+      if (n == 0) {
+        sgeo[0][pl] = e.w00;
+        sgeo[1][pl] = e.w01;
+        sgeo[2][pl] = e.w10;
+        sgeo[3][pl] = e.w11;
+        sgeo[4][pl] = e.ly;
+        sgeo[5][pl] = e.lx;
+        sgeo[6][pl] = e.m;
+        sfl[pl] = e.fl;
+        sq[pl] = e.q00;
+      }
+      if (a.pairs != nullptr && ((e.fl >> n) & 1)) {
+        const int s = ((b * a.G + g) * a.KK + k) * a.P + p;
+        const int rn = reinterpret_cast<const int*>(a.rank)[4 * s + n];
+        const int i = (b * a.G + g) * a.H * a.W + e.q00 + corner_dq(n, a.W);
+        pos = pair_start(a, i) + rn;
+        prow = (b * a.P + p) * a.KK + k;
+        pw = e.m * corner_w(e, n);
+      }
+    }
+  }
+  lds_barrier();
   const int LG = a.lg, li = tid & (LG - 1), si = tid / LG, SPI = kBT / LG;
   const int nit = (kSP + SPI - 1) / SPI;
   const bool grads = a.gcol != nullptr;
   const bool vec = a.Cg % 8 == 0;
+  const int c8 = li * 8;   // lg * 8 >= the chunk's channels: one octet per lane at most
   T* col = static_cast<T*>(a.col);
   const T* xs = static_cast<const T*>(a.xs) + static_cast<size_t>(b) * a.H * a.W * a.Cp + g * a.Cg;
-  const int GKK = a.G * a.KK, gk = g * a.KK + k;
+  struct Ld {
+    float v[4][8], gc[8];
+  };
   for (int cc0 = 0; cc0 < a.Cg; cc0 += kCC) {
     const int ccn = min(kCC, a.Cg - cc0);
-    for (int it = 0; it < nit; ++it) {
+    const bool act = c8 < ccn;
+    // the corners and column gradients of the sample of iteration it (zeros where none)
+    // The loads are unconditional (a corner outside the image, a lane past the chunk's
+    // channels or a missing sample reads pixel 0 / channel 0 and is zeroed afterwards):
+    // a load under a lane-dependent branch would be waited for before the branch ends.
+    auto load = [&](int it, Ld& L) {
       const int pl = it * SPI + si, p = pb * kSP + pl;
-      if (pl >= kSP || p >= a.P) continue;
-      const Geo e = sample_geo<T>(a, b, g, k, p);
-      const int row = (b * a.P + p) * a.KK + k;   // the sample's column-gradient row
-      const float* gcr = grads ? a.gcol + static_cast<size_t>(row) * a.Cin + g * a.Cg + cc0 : nullptr;
-      const T* xq = xs + cc0;
-      float gm = 0.f, goy = 0.f, gox = 0.f;
-      for (int c8 = li * 8; c8 < ccn; c8 += LG * 8) {
-        float v[4][8], gc[8];
-        if (vec) {
+      const bool ok = act && pl < kSP && p < a.P;
+      const int fl = ok ? sfl[pl] : 0, q00 = ok ? sq[pl] : 0;
+      const int ce = act ? c8 : 0;
+      const T* xq = xs + cc0 + ce;
+      // element indices within the image's xs and within gcol fit 32 bits (checked by the plan)
+      const uint32_t grow = ok ? static_cast<uint32_t>((b * a.P + p) * a.KK + k) : 0u;
+      const T* gcr = static_cast<const T*>(a.gcol) + (grow * static_cast<uint32_t>(a.Cin) + g * a.Cg + cc0 + ce);
+      if (vec) {
 #pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            if ((e.fl >> n) & 1) {
-              load8(xq + static_cast<size_t>(e.q00 + corner_dq(n, a.W)) * a.Cp + c8, v[n]);
-            } else {
+        for (int n = 0; n < 4; ++n) {
+          const bool on = (fl >> n) & 1;
+          const uint32_t q = on ? static_cast<uint32_t>(q00 + corner_dq(n, a.W)) : 0u;
+          load8(xq + q * static_cast<uint32_t>(a.Cp), L.v[n]);
 #pragma unroll
-              for (int j = 0; j < 8; ++j) v[n][j] = 0.f;
-            }
-          }
-          if (grads) {
-            load8(gcr + c8, gc);
-          } else {
+          for (int j = 0; j < 8; ++j) L.v[n][j] = on ? L.v[n][j] : 0.f;
+        }
+        if (grads) {   // uniform
+          load8(gcr, L.gc);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) gc[j] = 0.f;
-          }
+          for (int j = 0; j < 8; ++j) L.gc[j] = ok ? L.gc[j] : 0.f;
         } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const bool in = c8 + j < ccn;
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-              v[n][j] = in && ((e.fl >> n) & 1) ? to_f(xq[static_cast<size_t>(e.q00 + corner_dq(n, a.W)) * a.Cp + c8 + j]) : 0.f;
-            gc[j] = in && grads ? gcr[c8 + j] : 0.f;
-          }
+          for (int j = 0; j < 8; ++j) L.gc[j] = 0.f;
         }
-        float cv[8];
+      } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float v00 = v[0][j], v01 = v[1][j], v10 = v[2][j], v11 = v[3][j];
-          const float sv = e.w00 * v00 + e.w01 * v01 + e.w10 * v10 + e.w11 * v11;
-          cv[j] = e.m * sv;
-          gm += gc[j] * sv;
-          goy += gc[j] * ((1.f - e.lx) * (v10 - v00) + e.lx * (v11 - v01));
-          gox += gc[j] * ((1.f - e.ly) * (v01 - v00) + e.ly * (v11 - v10));
-        }
-        if (col != nullptr) {
-          T* dst = tile + pl * TP + c8;
-          if (vec) {
-            store8(dst, cv);
-          } else {
+          const bool in = ok && c8 + j < ccn;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (c8 + j < ccn) dst[j] = from_f<T>(cv[j]);
+          for (int n = 0; n < 4; ++n) {
+            const bool on = in && ((fl >> n) & 1);
+            const uint32_t e = on ? static_cast<uint32_t>(q00 + corner_dq(n, a.W)) * static_cast<uint32_t>(a.Cp) + j : 0u;
+            const float v = to_f(xq[e]);
+            L.v[n][j] = on ? v : 0.f;
           }
+          const float gv = grads ? to_f(gcr[in ? j : 0]) : 0.f;
+          L.gc[j] = in ? gv : 0.f;
         }
       }
-      if (grads) {   // the sums over the sample's lanes (all lanes of a sample share pl)
-        for (int d = LG >> 1; d >= 1; d >>= 1) {
-          gm += __shfl_xor(gm, d);
-          goy += __shfl_xor(goy, d);
-          gox += __shfl_xor(gox, d);
-        }
-        if (li == 0) {
-          if (cc0 > 0) {
-            goy += sacc[0][pl];
-            gox += sacc[1][pl];
-            gm += sacc[2][pl];
-          }
-          if (cc0 + kCC < a.Cg) {
-            sacc[0][pl] = goy;
-            sacc[1][pl] = gox;
-            sacc[2][pl] = gm;
-          } else {
-            if (a.grad_offset != nullptr) {
-              T* go = static_cast<T*>(a.grad_offset) + (static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p;
-              go[0] = from_f<T>(goy * e.m);
-              go[a.P] = from_f<T>(gox * e.m);
-            }
-            if (a.grad_mask != nullptr)
-              static_cast<T*>(a.grad_mask)[(static_cast<size_t>(b) * GKK + gk) * a.P + p] = from_f<T>(gm);
-          }
+    };
+    // Column entries to LDS; the four corner sums sum_c gc * v_corner over the sample's
+    // lanes, kept (more chunks to come) or turned into the gradients.  The mask and
+    // offset gradients are linear in the corner values, so each is the same combination
+    // of the corner sums: grad_mask = sum_n w_n * S_n, and the position derivatives
+    // (1 - lx)(S10 - S00) + lx (S11 - S01) and (1 - ly)(S01 - S00) + ly (S11 - S10).
+    auto work = [&](int it, const Ld& L) {
+      const int pl = it * SPI + si, p = pb * kSP + pl;
+      if (pl >= kSP || p >= a.P) return;   // uniform over the sample's lanes
+      const float w00 = sgeo[0][pl], w01 = sgeo[1][pl], w10 = sgeo[2][pl], w11 = sgeo[3][pl];
+      const float m = sgeo[6][pl];
+      if (col != nullptr && act) {
+        const float m00 = m * w00, m01 = m * w01, m10 = m * w10, m11 = m * w11;
+        float cv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cv[j] = m00 * L.v[0][j] + m01 * L.v[1][j] + m10 * L.v[2][j] + m11 * L.v[3][j];
+        T* dst = tile + pl * TP + c8;
+        if (vec) {
+          store8(dst, cv);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c8 + j < ccn) dst[j] = from_f<T>(cv[j]);
         }
       }
-      // the sample's pairs, once: lanes li, li + lg, ... < 4 take corners li, ...
-      if (cc0 == 0 && a.pairs != nullptr) {
-        const int4 rk = a.rank[((b * a.G + g) * a.KK + k) * a.P + p];
-        const int i0 = (b * a.G + g) * a.H * a.W + e.q00;
-        for (int n = li; n < 4; n += LG) {
-          const int rn = int4_at(rk, n);
-          if (rn >= 0) {
-            const int i = i0 + corner_dq(n, a.W);
-            a.pairs[pair_start(a, i) + rn] = make_int2(row, __float_as_int(e.m * corner_w(e, n)));
-          }
-        }
+      if (!grads) return;
+      float sc[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += L.gc[j] * L.v[n][j];
+        sc[n] = acc;
       }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) sc[n] = group_sum(sc[n], LG);
+      if (li != 0) return;
+      if (cc0 > 0)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) sc[n] += sacc[n][pl];
+      if (cc0 + kCC < a.Cg) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) sacc[n][pl] = sc[n];
+        return;
+      }
+      const float ly = sgeo[4][pl], lx = sgeo[5][pl];
+      if (a.grad_offset != nullptr) {
+        const float goy = (1.f - lx) * (sc[2] - sc[0]) + lx * (sc[3] - sc[1]);
+        const float gox = (1.f - ly) * (sc[1] - sc[0]) + ly * (sc[3] - sc[2]);
+        T* go = static_cast<T*>(a.grad_offset) + (static_cast<size_t>(b) * 2 * GKK + 2 * gk) * a.P + p;
+        go[0] = from_f<T>(goy * m);
+        go[a.P] = from_f<T>(gox * m);
+      }
+      if (a.grad_mask != nullptr)
+        static_cast<T*>(a.grad_mask)[(static_cast<size_t>(b) * GKK + gk) * a.P + p] =
+            from_f<T>(w00 * sc[0] + w01 * sc[1] + w10 * sc[2] + w11 * sc[3]);
+    };
+    for (int it = 0; it < nit; ++it) {
+      Ld L;
+      load(it, L);
+      work(it, L);
     }
     if (col != nullptr) {
-      __syncthreads();
+      lds_barrier();
       // rows (channel, kernel point) of col: 16 bytes (VE pixels) per thread, channels
       // fastest over the threads (an LDS read of 64 neighbouring channels of one pixel)
       const int ng = kSP / VE;
@@ -509,134 +583,158 @@ __global__ __launch_bounds__(kBT) void bwd_sample_cl(BwdArgs a) {
         T vals[VE];
 #pragma unroll
         for (int j = 0; j < VE; ++j) vals[j] = p0 + j < a.P ? tile[(pg * VE + j) * TP + c] : T(0);
-        const size_t r = static_cast<size_t>(b) * a.R + static_cast<size_t>(g * a.Cg + cc0 + c) * a.KK + k;
+        const uint32_t r = static_cast<uint32_t>(b * a.R + (g * a.Cg + cc0 + c) * a.KK + k);
         uint4 q;
         __builtin_memcpy(&q, vals, 16);
-        *reinterpret_cast<uint4*>(col + r * a.Pp + p0) = q;
+        *reinterpret_cast<uint4*>(col + (r * static_cast<uint32_t>(a.Pp) + p0)) = q;
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
+  if (pos >= 0) a.pairs[pos] = make_int2(prow, __float_as_int(pw));
 }
 
-// One workgroup per (b, group, 256-channel chunk, 64 input pixels), consecutive pixel
-// blocks on one XCD.  lg lanes per pixel, eight channels each: the sum over the pixel's
-// pairs of weight * its column-gradient row (four pairs' loads issued together), then
-// the chunk's sums leave through LDS ([channel][pixel]) as runs of 64 pixels per channel.
+// One workgroup per (b, group, 256-channel chunk, kGH x kGW input pixels), tiles in
+// raster order and consecutive tiles on one XCD, so that the rows of a sample's corners
+// are fetched by neighbouring workgroups of one L2.  First each pixel's pair range (to
+// LDS); then lg lanes per pixel, eight channels each: the pixel's pairs loaded by its
+// lanes at once (one pair per lane, then passed round by lane shuffles), their
+// column-gradient rows eight at a time, and the sum of weight * row; the chunk's sums
+// leave through LDS ([channel][pixel]) as kGW-pixel row segments per channel.
 template <typename T>
 __global__ __launch_bounds__(kBT) void bwd_gather_cl(BwdArgs a) {
   constexpr int GP = kGP + 1;   // LDS pitch of one channel's pixels
   __shared__ T tile[kCC * GP];
+  __shared__ int sst[2 * kGP];  // pair range of each pixel
   const int tid = threadIdx.x, HW = a.H * a.W;
-  int t = xcd_item(blockIdx.x, a.B * a.G * a.ncc * a.nqb);
-  const int qb = t % a.nqb;
-  t /= a.nqb;
+  int t = xcd_item(blockIdx.x, a.B * a.G * a.ncc * a.nqy * a.nqx);
+  const int tx = t % a.nqx;
+  t /= a.nqx;
+  const int ty = t % a.nqy;
+  t /= a.nqy;
   const int ci = t % a.ncc;
   t /= a.ncc;
   const int g = t % a.G, b = t / a.G;
+  const int ib = (b * a.G + g) * HW;
+  const int y0 = ty * kGH, x0 = tx * kGW;
+  if (tid < kGP) {
+    const int y = y0 + tid / kGW, x = x0 + tid % kGW;
+    const bool in = y < a.H && x < a.W;
+    const int i = ib + y * a.W + x;
+    sst[2 * tid] = in ? pair_start(a, i) : 0;
+    sst[2 * tid + 1] = in ? pair_start(a, i + 1) : 0;
+  }
+  lds_barrier();
   const int cc0 = ci * kCC, ccn = min(kCC, a.Cg - cc0);
   const int LG = a.lg, li = tid & (LG - 1), si = tid / LG, SPI = kBT / LG;
   const int nit = (kGP + SPI - 1) / SPI;
   const bool vec = a.Cg % 8 == 0;
-  const int ib = (b * a.G + g) * HW;
-  const float* gsrc = a.gcol + g * a.Cg + cc0;
+  const T* gsrc = static_cast<const T*>(a.gcol) + g * a.Cg + cc0;
+  const int lbase = threadIdx.x & 63 & ~(LG - 1);   // the group's first lane in the wave
   for (int it = 0; it < nit; ++it) {
-    const int pl = it * SPI + si, q = qb * kGP + pl;
-    if (pl >= kGP || q >= HW) continue;
-    const int e0 = pair_start(a, ib + q), e1 = pair_start(a, ib + q + 1);
-    for (int c8 = li * 8; c8 < ccn; c8 += LG * 8) {
-      float acc[8];
+    const int pl = it * SPI + si;
+    if (pl >= kGP) continue;
+    const int e0 = sst[2 * pl], e1 = sst[2 * pl + 1];   // empty outside the image
+    // every lane of the pixel takes part in loading and passing round the pairs, also
+    // the lanes past the chunk's channels (lg * 8 >= the chunk's channels)
+    const int c8 = li * 8;
+    const bool act = c8 < ccn;
+    float acc[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-      int e = e0;
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    for (int eb = e0; eb < e1; eb += LG) {
+      const int nb = min(LG, e1 - eb);
+      const int2 mine = li < nb ? a.pairs[eb + li] : make_int2(0, 0);
       if (vec) {
-        for (; e + 4 <= e1; e += 4) {
-          int2 pr[4];
-          float v[4][8];
+        for (int u0 = 0; u0 < nb; u0 += 8) {
+          float v[8][8], wm[8];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) pr[u] = a.pairs[e + u];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) load8(gsrc + static_cast<size_t>(pr[u].x) * a.Cin + c8, v[u]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float wm = __int_as_float(pr[u].y);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] += wm * v[u][j];
+          for (int u = 0; u < 8; ++u) {
+            const int src = lbase + min(u0 + u, nb - 1);
+            const int row = __shfl(mine.x, src);
+            wm[u] = u0 + u < nb ? __int_as_float(__shfl(mine.y, src)) : 0.f;
+            // unconditional (row is a valid pair's, c8 clamped): its data only feed lanes
+            // whose sums are stored
+            load8(gsrc + (static_cast<uint32_t>(row) * static_cast<uint32_t>(a.Cin) + (act ? c8 : 0)), v[u]);
           }
-        }
-        for (; e < e1; ++e) {
-          const int2 pr = a.pairs[e];
-          float v[8];
-          load8(gsrc + static_cast<size_t>(pr.x) * a.Cin + c8, v);
-          const float wm = __int_as_float(pr.y);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j] += wm * v[j];
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] += wm[u] * v[u][j];
         }
       } else {
-        for (; e < e1; ++e) {
-          const int2 pr = a.pairs[e];
-          const float wm = __int_as_float(pr.y);
-          const float* src = gsrc + static_cast<size_t>(pr.x) * a.Cin + c8;
+        for (int u = 0; u < nb; ++u) {
+          const int row = __shfl(mine.x, lbase + u);
+          const float wm = __int_as_float(__shfl(mine.y, lbase + u));
+          const T* src = gsrc + (static_cast<uint32_t>(row) * static_cast<uint32_t>(a.Cin) + c8);
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            if (c8 + j < ccn) acc[j] += wm * src[j];
+            if (c8 + j < ccn) acc[j] += wm * to_f(src[j]);
         }
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (c8 + j < ccn) tile[(c8 + j) * GP + pl] = from_f<T>(acc[j]);
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c8 + j < ccn) tile[(c8 + j) * GP + pl] = from_f<T>(acc[j]);
   }
-  __syncthreads();
+  lds_barrier();
   T* gx = static_cast<T*>(a.grad_x) + (static_cast<size_t>(b) * a.Cin + g * a.Cg + cc0) * HW;
   for (int idx = tid; idx < ccn * kGP; idx += kBT) {
-    const int c = idx / kGP, px = idx - (idx / kGP) * kGP, q = qb * kGP + px;
-    if (q < HW) gx[static_cast<size_t>(c) * HW + q] = tile[c * GP + px];
+    const int c = idx / kGP, px = idx - (idx / kGP) * kGP;
+    const int y = y0 + px / kGW, x = x0 + px % kGW;
+    if (y < a.H && x < a.W) gx[static_cast<size_t>(c) * HW + y * a.W + x] = tile[c * GP + px];
   }
 }
 
-// C[z] (+)= sum over the reduction of A[m][k] * Bm[n][k]: both operands row-major with
-// the reduction contiguous (rows padded with zeros to Kd, a multiple of 8).  The
-// reduction runs over nseg segments of Kd (operand strides sAs, sBs), split evenly
-// over ksplit workgroups per output tile (atomics into a zeroed C when ksplit > 1).
-// blockIdx.z = zb * ksplit + ks, zb selecting independent problems (strides sAz, sBz,
-// sCz).  A 128 x 128 output tile per workgroup, four waves of 64 x 64, 32-deep chunks
-// staged through LDS with the next chunk's loads in flight during the multiply.
+// C = sum over the reduction of A[m][k] * Bm[n][k]: both operands row-major with the
+// reduction contiguous (rows padded with zeros to Kd, a multiple of 8).  The reduction
+// runs over nseg segments of Kd (operand strides sAs, sBs), split evenly over ksplit
+// workgroups per output tile; split ks writes its partial sum to C + ks * sCk (a later
+// pass adds the partials in a fixed order).  blockIdx.z = zb * ksplit + ks, zb
+// selecting independent problems (strides sAz, sBz, sCz).  A 128 x 128 output tile per
+// workgroup, four waves of 64 x 64; chunks of 128 bytes of the reduction per row (64
+// bf16 or 32 fp32 values) in two LDS buffers: while the waves multiply one, the next
+// chunk goes from registers into the other and the one after is loaded into
+// registers, one barrier per chunk.
 template <typename T>
 struct GemmArgs {
   const T* A;
   const T* Bm;
-  float* C;
+  void* C;       // fp32, or the element type with c_elem
   int M, N, Kd, lda, ldb, ldc, nseg, ksplit;
-  long long sAs, sBs, sAz, sBz, sCz;
+  int mfast;   // 1: output tiles in column-major order (M fastest)
+  int c_elem;  // 1: C in the element type T (rounded once), else fp32
+  long long sAs, sBs, sAz, sBz, sCz, sCk;
 };
 
-constexpr int kGM = 128, kGN = 128, kGK = 32;
+constexpr int kGM = 128, kGN = 128;
+constexpr int kGKB = 128;   // bytes of the reduction per tile row and chunk
 
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_gemm_nt(GemmArgs<T> g) {
   constexpr bool kBF = sizeof(T) == 2;
-  constexpr int VE = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte vector
-  constexpr int VPR = kGK / VE;                           // vectors per tile row
-  constexpr int NV = kGM * VPR / 256;                     // vectors per thread and operand
-  constexpr int LDT = kGK + VE;                           // LDS row stride in elements
-  __shared__ __attribute__((aligned(16))) T As[kGM * LDT];
-  __shared__ __attribute__((aligned(16))) T Bs[kGN * LDT];
+  constexpr int GK = kGKB / static_cast<int>(sizeof(T));  // reduction depth of a chunk
+  constexpr int VE = 16 / static_cast<int>(sizeof(T));    // elements per 16-byte vector
+  constexpr int VPR = GK / VE;                            // vectors per tile row (8)
+  constexpr int NV = kGM * VPR / 256;                     // vectors per thread and operand (4)
+  constexpr int LDT = GK + VE;                            // LDS row stride: 144 bytes
+  __shared__ __attribute__((aligned(16))) T As[2][kGM * LDT];
+  __shared__ __attribute__((aligned(16))) T Bs[2][kGN * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
-  // Output tiles in row-major order (N fastest), handed out so that each XCD (workgroup
-  // w runs on XCD w % 8, each with its own L2) takes a contiguous run of tiles, which
-  // share their A rows (and neighbouring runs their B rows) in that L2.
-  const int ntn = (g.N + kGN - 1) / kGN, ntiles = ntn * ((g.M + kGM - 1) / kGM);
+  // Output tiles in row-major order (N fastest; M fastest with mfast), handed out so that
+  // each XCD (workgroup w runs on XCD w % 8, each with its own L2) takes a contiguous run
+  // of tiles, which share their A rows (B rows with mfast) in that L2.
+  const int ntn = (g.N + kGN - 1) / kGN, ntm = (g.M + kGM - 1) / kGM, ntiles = ntn * ntm;
   const int xper = (ntiles + 7) / 8;
   const int lt = static_cast<int>(blockIdx.x % 8) * xper + static_cast<int>(blockIdx.x / 8);
   if (lt >= ntiles) return;   // spare workgroups of the last XCD (uniform)
-  const int m0 = (lt / ntn) * kGM, n0 = (lt % ntn) * kGN;
+  const int m0 = (g.mfast ? lt % ntm : lt / ntn) * kGM, n0 = (g.mfast ? lt / ntm : lt % ntn) * kGN;
   const int zb = blockIdx.z / g.ksplit, ks = blockIdx.z - zb * g.ksplit;
   const T* A = g.A + zb * g.sAz;
   const T* Bm = g.Bm + zb * g.sBz;
-  float* C = g.C + zb * g.sCz;
-  const int kchunks = (g.Kd + kGK - 1) / kGK;
+  const size_t c0 = zb * g.sCz + ks * g.sCk;
+  const int kchunks = (g.Kd + GK - 1) / GK;
   const int total = kchunks * g.nseg;
   const int per = (total + g.ksplit - 1) / g.ksplit;
   const int t0 = ks * per, t1 = min(total, t0 + per);
@@ -654,7 +752,7 @@ __global__ __launch_bounds__(256) void bwd_gemm_nt(GemmArgs<T> g) {
     const T* Bp = Bm + seg * g.sBs;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int idx = tid + v * 256, row = idx / VPR, k = kc * kGK + (idx % VPR) * VE;
+      const int idx = tid + v * 256, row = idx / VPR, k = kc * GK + (idx % VPR) * VE;
       const int ma = m0 + row, nb = n0 + row;
       ra[v] = (ma < g.M && k < g.Kd) ? *reinterpret_cast<const uint4*>(Ap + static_cast<size_t>(ma) * g.lda + k)
                                      : make_uint4(0, 0, 0, 0);
@@ -662,25 +760,25 @@ __global__ __launch_bounds__(256) void bwd_gemm_nt(GemmArgs<T> g) {
                                      : make_uint4(0, 0, 0, 0);
     }
   };
-  if (t0 < t1) gload(t0);
-  for (int t = t0; t < t1; ++t) {
-    __syncthreads();
+  auto sstore = [&](int buf) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int idx = tid + v * 256, row = idx / VPR, kv = idx % VPR;
-      *reinterpret_cast<uint4*>(As + row * LDT + kv * VE) = ra[v];
-      *reinterpret_cast<uint4*>(Bs + row * LDT + kv * VE) = rb[v];
+      *reinterpret_cast<uint4*>(&As[buf][row * LDT + kv * VE]) = ra[v];
+      *reinterpret_cast<uint4*>(&Bs[buf][row * LDT + kv * VE]) = rb[v];
     }
-    __syncthreads();
-    if (t + 1 < t1) gload(t + 1);
+  };
+  auto mma = [&](int buf) {
+    const T* as = As[buf];
+    const T* bs = Bs[buf];
     if constexpr (kBF) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < GK / 16; ++h) {
         bf16x8 av[2], bv[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          av[q] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + q * 32 + l32) * LDT + h * 16 + lh * 8);
-          bv[q] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + q * 32 + l32) * LDT + h * 16 + lh * 8);
+          av[q] = *reinterpret_cast<const bf16x8*>(as + (wm * 64 + q * 32 + l32) * LDT + h * 16 + lh * 8);
+          bv[q] = *reinterpret_cast<const bf16x8*>(bs + (wn * 64 + q * 32 + l32) * LDT + h * 16 + lh * 8);
         }
 #pragma unroll
         for (int tm = 0; tm < 2; ++tm)
@@ -690,12 +788,12 @@ __global__ __launch_bounds__(256) void bwd_gemm_nt(GemmArgs<T> g) {
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < kGK / 2; ++kk) {
+      for (int kk = 0; kk < GK / 2; ++kk) {
         float av[2], bv[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          av[q] = As[(wm * 64 + q * 32 + l32) * LDT + 2 * kk + lh];
-          bv[q] = Bs[(wn * 64 + q * 32 + l32) * LDT + 2 * kk + lh];
+          av[q] = as[(wm * 64 + q * 32 + l32) * LDT + 2 * kk + lh];
+          bv[q] = bs[(wn * 64 + q * 32 + l32) * LDT + 2 * kk + lh];
         }
 #pragma unroll
         for (int tm = 0; tm < 2; ++tm)
@@ -704,9 +802,24 @@ __global__ __launch_bounds__(256) void bwd_gemm_nt(GemmArgs<T> g) {
             acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
       }
     }
+  };
+  if (t0 < t1) {
+    gload(t0);
+    sstore(0);
+    if (t0 + 1 < t1) gload(t0 + 1);
   }
-  if (t0 >= t1) return;
-  // accumulator element r of a 32x32 block: row 8*(r/4) + 4*lh + r%4, column l32
+  lds_barrier();
+  for (int t = t0; t < t1; ++t) {
+    const int cur = (t - t0) & 1;
+    mma(cur);
+    if (t + 1 < t1) {
+      sstore(cur ^ 1);   // no wave still reads this buffer: all passed the last barrier
+      if (t + 2 < t1) gload(t + 2);
+    }
+    lds_barrier();
+  }
+  // accumulator element r of a 32x32 block: row 8*(r/4) + 4*lh + r%4, column l32 (an
+  // empty split writes zeros)
 #pragma unroll
   for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
@@ -716,11 +829,27 @@ __global__ __launch_bounds__(256) void bwd_gemm_nt(GemmArgs<T> g) {
         const int row = m0 + wm * 64 + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
         const int cc = n0 + wn * 64 + tn * 32 + l32;
         if (row < g.M && cc < g.N) {
-          float* dst = C + static_cast<size_t>(row) * g.ldc + cc;
-          if (g.ksplit > 1) unsafeAtomicAdd(dst, acc[tm][tn][r]);
-          else *dst = acc[tm][tn][r];
+          const size_t e = c0 + static_cast<size_t>(row) * g.ldc + cc;
+          if (g.c_elem) static_cast<T*>(g.C)[e] = from_f<T>(acc[tm][tn][r]);
+          else static_cast<float*>(g.C)[e] = acc[tm][tn][r];
         }
       }
+}
+
+// The weight gradient's partial sums added in split order and rounded to the element
+// type; the bias accumulator converted by the threads past the weight's elements.
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_reduce_w(const float* part, int nsplit, int n, T* out, const float* gb32,
+                                                    T* gbo, int nb) {
+  const int e = blockIdx.x * kBT + threadIdx.x;
+  if (e < n) {
+    if (out == nullptr) return;
+    float s = part[e];
+    for (int k = 1; k < nsplit; ++k) s += part[static_cast<size_t>(k) * n + e];
+    out[e] = from_f<T>(s);
+  } else if (e - n < nb && gbo != nullptr) {
+    gbo[e - n] = from_f<T>(gb32[e - n]);
+  }
 }
 
 int64_t rup(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -729,6 +858,7 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 // Workspace layout of one backward call.
 struct BwdPlan {
   int64_t Ho = 0, Wo = 0, P = 0, Pp = 0, Coutp = 0, R = 0, G = 1, Cp = 0, ncnt = 0, nblk = 0, nsamp = 0;
+  int wks = 1;   // splits of the weight gradient's reduction (partial sums in the workspace)
   size_t o_wt = 0, o_gyt = 0, o_gyp = 0, o_col = 0, o_gcol = 0, o_xs = 0, o_gw = 0, o_gb = 0;
   size_t o_cnt = 0, o_bsum = 0, o_rank = 0, o_pairs = 0;
   size_t bytes = 0;
@@ -766,9 +896,16 @@ int bwd_plan(const dcn_desc* d, BwdPlan* p) {
   p->o_gyt = take(static_cast<size_t>(B * p->P * p->Coutp) * es);
   p->o_gyp = take(static_cast<size_t>(B * Cout * p->Pp) * es);
   p->o_col = take(static_cast<size_t>(B * p->R * p->Pp) * es);
-  p->o_gcol = take(static_cast<size_t>(B * p->P * p->R) * 4);
+  p->o_gcol = take(static_cast<size_t>(B * p->P * p->R) * es);
   p->o_xs = take(static_cast<size_t>(B * HW * p->Cp) * es);
-  p->o_gw = take(static_cast<size_t>(Cout * p->R) * 4);
+  // split the weight gradient's reduction (B segments of Pp) until the output tiles and
+  // splits give about one workgroup per CU, with at least four chunks per split
+  {
+    const int64_t tiles = ((Cout + kGM - 1) / kGM) * ((p->R + kGN - 1) / kGN);
+    const int64_t chunks = (p->Pp + kGKB / static_cast<int64_t>(es) - 1) / (kGKB / static_cast<int64_t>(es)) * B;
+    while (tiles * p->wks < 256 && p->wks * 2 <= chunks / 4) p->wks *= 2;
+  }
+  p->o_gw = take(static_cast<size_t>(Cout * p->R) * 4 * p->wks);
   p->o_gb = take(static_cast<size_t>(Cout) * 4);
   p->o_cnt = take(static_cast<size_t>(p->ncnt) * 4);
   p->o_bsum = take(static_cast<size_t>(p->nblk) * 4);
@@ -846,11 +983,13 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
   a.Cg = a.Cin / a.G;
   a.Cp = static_cast<int>(p.Cp);
   a.nsamp = static_cast<int>(p.nsamp);
+  // lanes per sample or pixel: eight channels each, enough for a chunk (kCC = 32 * 8)
   const int cch = std::min(a.Cg, kCC);
   a.lg = 1;
   while (a.lg < 32 && a.lg * 8 < cch) a.lg *= 2;
   a.npb = (a.P + kSP - 1) / kSP;
-  a.nqb = (a.H * a.W + kGP - 1) / kGP;
+  a.nqy = (a.H + kGH - 1) / kGH;
+  a.nqx = (a.W + kGW - 1) / kGW;
   a.ncc = (a.Cg + kCC - 1) / kCC;
   const bool need_gcol = grad_x != nullptr || grad_offset != nullptr || (grad_mask != nullptr && mask != nullptr);
   const bool sample = need_gcol || grad_weight != nullptr;
@@ -859,7 +998,7 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
   a.gyt = need_gcol ? static_cast<void*>(ws + p.o_gyt) : nullptr;
   a.gyp = grad_weight != nullptr ? static_cast<void*>(ws + p.o_gyp) : nullptr;
   a.col = grad_weight != nullptr ? static_cast<void*>(ws + p.o_col) : nullptr;
-  a.gcol = need_gcol ? reinterpret_cast<float*>(ws + p.o_gcol) : nullptr;
+  a.gcol = need_gcol ? static_cast<void*>(ws + p.o_gcol) : nullptr;
   a.gb32 = grad_bias != nullptr ? reinterpret_cast<float*>(ws + p.o_gb) : nullptr;
   a.grad_offset = grad_offset;
   a.grad_mask = mask != nullptr ? grad_mask : nullptr;
@@ -870,7 +1009,7 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     a.rank = reinterpret_cast<int4*>(ws + p.o_rank);
     a.pairs = reinterpret_cast<int2*>(ws + p.o_pairs);
   }
-  float* gw32 = reinterpret_cast<float*>(ws + p.o_gw);
+  float* gw32 = reinterpret_cast<float*>(ws + p.o_gw);   // [wks][Cout][R] partial sums
   const int64_t nw = static_cast<int64_t>(a.Cout) * a.R;
   void* args[] = {&a};
 
@@ -889,12 +1028,10 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     const dim3 grid(static_cast<unsigned>((a.R + 31) / 32), static_cast<unsigned>((a.Coutp + 31) / 32));
     BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_w<T>), grid, dim3(kBT), args, 0, s));
   }
-  // the fp32 accumulators and the pair counters zeroed by one launch (before prep_gy
-  // adds the bias sums)
+  // the bias accumulator and the pair counters zeroed by one launch (before prep_gy adds
+  // the bias sums)
   BWD_TRY(launch_ranges(reinterpret_cast<const void*>(&bwd_fill_zero_ranges), 4,
-                        {{grad_weight != nullptr ? gw32 : nullptr, nullptr, nw}, {a.gb32, nullptr, a.Cout},
-                         {reinterpret_cast<float*>(a.cnt), nullptr, p.ncnt}},
-                        s));
+                        {{a.gb32, nullptr, a.Cout}, {reinterpret_cast<float*>(a.cnt), nullptr, p.ncnt}}, s));
   if (sample || grad_bias != nullptr) {
     const dim3 grid(static_cast<unsigned>((a.Pp + 31) / 32), static_cast<unsigned>((a.Coutp + 31) / 32),
                     static_cast<unsigned>(a.B));
@@ -913,6 +1050,7 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     g.A = static_cast<const T*>(a.gyt);
     g.Bm = static_cast<const T*>(a.wt);
     g.C = a.gcol;
+    g.c_elem = 1;
     g.M = a.P;
     g.N = a.R;
     g.Kd = a.Coutp;
@@ -930,7 +1068,7 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_sample_cl<T>), dim3(grid), dim3(kBT), args, 0, s));
   }
   if (grad_x != nullptr) {
-    const unsigned grid = static_cast<unsigned>(a.B * a.G * a.ncc * a.nqb);
+    const unsigned grid = static_cast<unsigned>(a.B * a.G * a.ncc * a.nqy * a.nqx);
     BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_gather_cl<T>), dim3(grid), dim3(kBT), args, 0, s));
   }
   if (grad_weight != nullptr) {
@@ -946,18 +1084,21 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     g.nseg = a.B;
     g.sAs = static_cast<long long>(a.Cout) * a.Pp;
     g.sBs = static_cast<long long>(a.R) * a.Pp;
-    // split the reduction until the output tiles and splits give about one workgroup per CU
-    // (more splits measured slower: more fp32 atomics into the accumulator)
-    const int tiles = ((a.Cout + kGM - 1) / kGM) * ((a.R + kGN - 1) / kGN);
-    const int chunks = ((a.Pp + kGK - 1) / kGK) * a.B;
-    int ks = 1;
-    while (tiles * ks < 256 && ks * 2 <= chunks / 4) ks *= 2;
-    g.ksplit = ks;
+    g.ksplit = p.wks;
+    g.sCk = nw;
+    g.mfast = 1;   // the tiles of one column block (all output channels) share its col rows
     BWD_TRY(gemm<T>(g, 1, s));
   }
-  // the weight and bias accumulators to the element type, one launch
-  BWD_TRY(launch_ranges(reinterpret_cast<const void*>(&bwd_convert_ranges<T>), 1,
-                        {{grad_weight != nullptr ? gw32 : nullptr, grad_weight, nw}, {a.gb32, grad_bias, a.Cout}}, s));
+  // the weight gradient's partial sums added and the bias accumulator converted, one launch
+  if (grad_weight != nullptr || grad_bias != nullptr) {
+    const float* part = gw32;
+    int nsplit = p.wks, n = grad_weight != nullptr ? static_cast<int>(nw) : 0, nb = grad_bias != nullptr ? a.Cout : 0;
+    T* out = static_cast<T*>(grad_weight);
+    T* gbo = static_cast<T*>(grad_bias);
+    const float* gb = a.gb32;
+    void* rargs[] = {&part, &nsplit, &n, &out, &gb, &gbo, &nb};
+    BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_reduce_w<T>), static_cast<int64_t>(n) + nb, rargs, s));
+  }
   return DCN_OK;
 }
 
