@@ -208,13 +208,17 @@ int dcn_layer_forward(const dcn_desc* desc, const void* x, const void* weight_om
  * ignored when mask is NULL.  Where a sampling position is an integer the offset
  * gradient is the derivative from the right.  Arithmetic: positions and bilinear
  * weights in fp32 as in the forward; the two gradient products on MFMA (bf16 data
- * with fp32 accumulation; fp32 data in fp32), the weight gradient's columns rounded
- * to dtype; every sum accumulates in fp32 (the input, offset, mask and weight
- * gradients with atomic adds, so their rounding order varies between calls) and is
- * rounded to dtype once.  The workspace (256-byte aligned, dcn_backward_workspace_bytes)
- * holds the transposed weight and grad_out, the columns, the column gradients and the
- * fp32 accumulators.  Device pointers; asynchronous on `stream`; the caller owns every
- * buffer.  Errors as for dcn_forward, checked before any launch (outputs untouched).
+ * with fp32 accumulation; fp32 data in fp32); the column gradients (W^T grad_out) and
+ * the weight gradient's columns rounded to dtype; every other sum accumulates in fp32
+ * and is rounded to dtype once.  The weight gradient's split reduction is added in a
+ * fixed order; only the bias gradient's per-tile sums (atomic adds) and the terms of
+ * each input pixel's gradient (ordered by atomic counters) can be summed in a
+ * different order from call to call.  The
+ * workspace (256-byte aligned, dcn_backward_workspace_bytes) holds a channels-last copy
+ * of x, the transposed weight and grad_out, the columns, the column gradients, the
+ * weight gradient's partial sums and the per-pixel lists of (sample, corner) pairs.
+ * Device pointers; asynchronous on `stream`; the caller owns every buffer.  Errors as
+ * for dcn_forward, checked before any launch (outputs untouched).
  * B == 0 or Cout == 0: the gradients that have elements are written as zeros. */
 int dcn_backward_workspace_bytes(const dcn_desc* desc, size_t* bytes);
 int dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
