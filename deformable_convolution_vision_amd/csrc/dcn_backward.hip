@@ -836,6 +836,158 @@ __global__ __launch_bounds__(256) void bwd_gemm_nt(GemmArgs<T> g) {
       }
 }
 
+// bf16 operands: the same product with the chunks moved by buffer->LDS loads straight
+// into a ring of kDS LDS stages, three chunks ahead of the multiply and no registers
+// held for them.  A chunk is 32 values (64 bytes) of the reduction for the tile's 128
+// rows of each operand; lane s of a 1 KB load fills 16-byte slot s of a 16-row block,
+// and the slots of a row are XOR-swizzled with (row / 4) % 4, so that the multiply's
+// 16-byte reads of 16 rows at one reduction offset fall in distinct banks.  Rows past
+// M or N and reduction indices past Kd read zeros (the load's offset is past the
+// buffer).  With c_elem the tile leaves through LDS as 16-byte row pieces.
+constexpr int kDK = 32;   // reduction values per chunk
+constexpr int kDS = 4;    // LDS stages
+constexpr int kDRB = kDK * 2;   // bytes of a row in a chunk
+constexpr uint32_t kDOOB = 0xfffffff0u;   // a byte offset past every operand (operands < 2 GiB)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// a barrier after this wave's LDS operations completed (the direct loads into LDS are
+// waited for separately with wait_vm)
+__device__ __forceinline__ void barrier_lds_done() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(256) void bwd_gemm_dma(GemmArgs<uint16_t> g, uint32_t a_bytes, uint32_t b_bytes) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kDS][2][kGM * kDRB];   // [stage][A, B][row][128 B]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
+  const int ntn = (g.N + kGN - 1) / kGN, ntm = (g.M + kGM - 1) / kGM, ntiles = ntn * ntm;
+  const int xper = (ntiles + 7) / 8;
+  const int lt = static_cast<int>(blockIdx.x % 8) * xper + static_cast<int>(blockIdx.x / 8);
+  if (lt >= ntiles) return;   // spare workgroups of the last XCD (uniform)
+  const int m0 = (g.mfast ? lt % ntm : lt / ntn) * kGM, n0 = (g.mfast ? lt / ntm : lt % ntn) * kGN;
+  const int zb = blockIdx.z / g.ksplit, ks = blockIdx.z - zb * g.ksplit;
+  const __amdgpu_buffer_rsrc_t ra = gemm_rsrc(g.A + zb * g.sAz, a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = gemm_rsrc(g.Bm + zb * g.sBz, b_bytes);
+  const int kchunks = (g.Kd + kDK - 1) / kDK;
+  const int total = kchunks * g.nseg;
+  const int per = (total + g.ksplit - 1) / g.ksplit;
+  const int t0 = ks * per, t1 = min(total, t0 + per);
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
+  // this lane's slot in a 16-row block: row s / 4, physical piece s % 4
+  const int srow = lane >> 2, sphys = lane & 3;
+  // chunk t into stage st: four 1 KB loads per wave (two 16-row blocks of each operand)
+  auto issue = [&](int t, int st) {
+    const int seg = t / kchunks, kc = t - seg * kchunks;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = wave * 2 + i, row = blk * 16 + srow;
+      const int k = kc * kDK + (sphys ^ ((row >> 2) & 3)) * 8;
+      const int ma = m0 + row, nb = n0 + row;
+      const uint32_t va = ma < g.M && k < g.Kd
+                              ? static_cast<uint32_t>((seg * g.sAs + static_cast<long long>(ma) * g.lda + k) * 2)
+                              : kDOOB;
+      const uint32_t vb = nb < g.N && k < g.Kd
+                              ? static_cast<uint32_t>((seg * g.sBs + static_cast<long long>(nb) * g.ldb + k) * 2)
+                              : kDOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(smem[st][0] + blk * 1024), 16, va, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(smem[st][1] + blk * 1024), 16, vb, 0, 0, 0);
+    }
+  };
+  auto mma = [&](int st) {
+    const unsigned char* as = smem[st][0];
+    const unsigned char* bs = smem[st][1];
+#pragma unroll
+    for (int h = 0; h < kDK / 16; ++h) {
+      const int kv = 2 * h + lh;
+      bf16x8 av[2], bv[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ra_ = wm * 64 + q * 32 + l32, rb_ = wn * 64 + q * 32 + l32;
+        av[q] = *reinterpret_cast<const bf16x8*>(as + ra_ * kDRB + ((kv ^ ((ra_ >> 2) & 3)) << 4));
+        bv[q] = *reinterpret_cast<const bf16x8*>(bs + rb_ * kDRB + ((kv ^ ((rb_ >> 2) & 3)) << 4));
+      }
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kDS - 1; ++j)
+    if (t0 + j < t1) issue(t0 + j, j);
+  for (int t = t0; t < t1; ++t) {
+    // this wave's loads of chunk t are done when at most (chunks issued after t) x 4 remain
+    static_assert(kDS == 4, "the wait below allows two chunks after t");
+    const int after = min(t1 - 1 - t, kDS - 2);
+    if (after >= 2) wait_vm<8>();
+    else if (after == 1) wait_vm<4>();
+    else wait_vm<0>();
+    barrier_lds_done();   // every wave's chunk t is in LDS; stage (t - 1) % kDS is free
+    if (t + kDS - 1 < t1) issue(t + kDS - 1, (t + kDS - 1 - t0) % kDS);
+    mma((t - t0) % kDS);
+  }
+  // accumulator element r of a 32x32 block: row 8*(r/4) + 4*lh + r%4, column l32
+  const size_t c0 = zb * g.sCz + ks * g.sCk;
+  if (!g.c_elem || g.ldc % 8 != 0) {
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 64 + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int cc = n0 + wn * 64 + tn * 32 + l32;
+          if (row < g.M && cc < g.N) {
+            const size_t e = c0 + static_cast<size_t>(row) * g.ldc + cc;
+            if (g.c_elem) static_cast<uint16_t*>(g.C)[e] = from_f<uint16_t>(acc[tm][tn][r]);
+            else static_cast<float*>(g.C)[e] = acc[tm][tn][r];
+          }
+        }
+    return;
+  }
+  // through LDS: the tile as bf16 [128][136], then 16-byte pieces of rows
+  uint16_t* ct = reinterpret_cast<uint16_t*>(&smem[0][0][0]);
+  constexpr int CP = kGN + 8;
+  wait_vm<0>();
+  barrier_lds_done();
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + tm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        ct[row * CP + wn * 64 + tn * 32 + l32] = from_f<uint16_t>(acc[tm][tn][r]);
+      }
+  barrier_lds_done();
+  uint16_t* C = static_cast<uint16_t*>(g.C) + c0;
+#pragma unroll
+  for (int i = 0; i < kGM * kGN / 8 / 256; ++i) {
+    const int idx = tid + i * 256, row = idx >> 4, pc = (idx & 15) * 8;
+    const int gr = m0 + row, gc = n0 + pc;
+    if (gr >= g.M || gc >= g.N) continue;
+    if (gc + 8 <= g.N) {
+      *reinterpret_cast<uint4*>(C + static_cast<size_t>(gr) * g.ldc + gc) = *reinterpret_cast<const uint4*>(ct + row * CP + pc);
+    } else {
+      for (int j = 0; j < g.N - gc; ++j) C[static_cast<size_t>(gr) * g.ldc + gc + j] = ct[row * CP + pc + j];
+    }
+  }
+}
+
 // The weight gradient's partial sums added in split order and rounded to the element
 // type; the bias accumulator converted by the threads past the weight's elements.
 template <typename T>
@@ -939,12 +1091,26 @@ hipError_t launch_ranges(const void* fn, int per_thread, std::initializer_list<s
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>(total)), dim3(kBT), args, 0, s);
 }
 
+// bf16 products with a short reduction per workgroup (at most 256 values: the column
+// gradients' 256 output channels on c4) whose operands are under 2 GiB take the LDS-ring
+// kernel (a_bytes and b_bytes: the extent of A and Bm over the segments); the others,
+// whose long reductions the register-staged kernel's 128-byte chunks run through with
+// half the barriers, take that one (c4: column gradients 31 -> 26 us on the ring, the
+// weight gradient 28 -> 36 us).
 template <typename T>
 hipError_t gemm(const GemmArgs<T>& g, int zb, hipStream_t s) {
   GemmArgs<T> gg = g;
-  void* args[] = {&gg};
   const int ntiles = ((g.N + kGN - 1) / kGN) * ((g.M + kGM - 1) / kGM);
   const dim3 grid(static_cast<unsigned>((ntiles + 7) / 8 * 8), 1, static_cast<unsigned>(zb * g.ksplit));
+  const double ab = 2.0 * ((g.nseg - 1) * static_cast<double>(g.sAs) + static_cast<double>(g.M) * g.lda);
+  const double bb = 2.0 * ((g.nseg - 1) * static_cast<double>(g.sBs) + static_cast<double>(g.N) * g.ldb);
+  const int per_split = (g.nseg * ((g.Kd + 31) / 32) + g.ksplit - 1) / g.ksplit;   // 32-value chunks
+  if (sizeof(T) == 2 && per_split <= 8 && ab < 2147483648.0 && bb < 2147483648.0) {
+    uint32_t a_bytes = static_cast<uint32_t>(ab), b_bytes = static_cast<uint32_t>(bb);
+    void* args[] = {&gg, &a_bytes, &b_bytes};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_gemm_dma), grid, dim3(256), args, 0, s);
+  }
+  void* args[] = {&gg};
   return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_gemm_nt<T>), grid, dim3(256), args, 0, s);
 }
 
