@@ -28,16 +28,16 @@
 //   prep_gy  gy -> gyT [B][P][Coutp] and gyP [B][Cout][Pp] (both zero-padded), and the
 //            bias gradient's per-tile sums (fp32 atomics)
 //   count    per sample (b, group, kernel point, pixel): each corner inside the image
-//            counted at its input pixel; the atomic increment's old value is the pair's
-//            rank in that pixel's list
-//   scan     exclusive prefix sums of the counts: per block of 2048, then the block sums
+//            counted at its input pixel
+//   scan     exclusive prefix sums of the counts: per block of 2048 (also copied to the
+//            per-pixel cursors), then the block sums
 //   gemm     gcol[b] = gyT[b] x Wt^T, channels fastest: [B][P][K^2][Cin] (MFMA)
 //   sample   per (b, group, kernel point, 16 output pixels): the corners from xs as
 //            16-byte channel vectors; the column entries, transposed through LDS to
 //            col [B][R][Pp] for the weight gradient; the offset and mask gradients summed
 //            over the group's channels across the lanes of the sample and written once;
 //            and each in-image corner's pair (column-gradient row, m * corner weight)
-//            placed in its input pixel's list
+//            placed in its input pixel's list at the slot its cursor hands out
 //   gather   grad_x per input pixel: the sum over its pairs of weight * column-gradient
 //            row, transposed through LDS to [B][Cin][H][W]
 //   gemm     grad_weight = sum_b gyP[b] x col[b]^T, the reduction split over workgroups
@@ -126,7 +126,7 @@ struct BwdArgs {
   int* cnt;             // [B*G*H*W + 1]: pairs per input pixel, then their block-local
                         // exclusive prefix sums
   int* bsum;            // [ceil((B*G*H*W + 1) / kScanB)]: block sums, then their exclusive sums
-  int4* rank;           // [B][G][K^2][P]: each corner's rank in its pixel's list, -1 for none
+  int* cur;             // [B*G*H*W + 1]: each pixel's next free slot (block-local, as cnt)
   int2* pairs;          // [B*G*K^2*P*4]: (column-gradient row, bits of m * corner weight)
   int B, Cin, H, W, Cout, K, KK, stride, pad, dil, Ho, Wo, P, Pp, Coutp, R, G, Cg, Cp;
   int lg;               // lanes per sample (sampling) or pixel (gather): a power of two
@@ -135,15 +135,15 @@ struct BwdArgs {
   int nqy, nqx;         // kGH x kGW tiles of the input plane (rows, columns)
   int ncc;              // 256-channel chunks of a group
   int nsamp;            // B * G * K^2 * P
+  int gyp_copy;         // 1: gyp is a padded copy to write (Pp > P); 0: gyp is gy
 };
 
 // Wt[k*Cin + c][o] = W[o][c*K^2 + k] (zero for o >= Cout): 32 x 32 tiles of (o, r)
 // through LDS, read along r and written along o.
 template <typename T>
-__global__ __launch_bounds__(kBT) void bwd_prep_w(BwdArgs a) {
-  __shared__ T tile[32][33];
+__device__ __forceinline__ void prep_w_tile(const BwdArgs& a, T (*tile)[33], int bx, int by) {
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int r0 = blockIdx.x * 32, o0 = blockIdx.y * 32;
+  const int r0 = bx * 32, o0 = by * 32;
   const T* w = static_cast<const T*>(a.w);
   T* wt = static_cast<T*>(a.wt);
 #pragma unroll
@@ -162,38 +162,61 @@ __global__ __launch_bounds__(kBT) void bwd_prep_w(BwdArgs a) {
   }
 }
 
-// 32 x 32 tiles of (output channel, pixel) through LDS: gyP keeps gy's layout with
-// the pixel stride padded to Pp; gyT is its transpose with the channel stride
-// padded to Coutp.  Padding is written as zeros.
+// 64 x 64 tiles of (output channel, pixel) through LDS: gyP keeps gy's layout with the
+// pixel stride padded to Pp (written only when Pp > P; otherwise gy itself serves); gyT
+// is its transpose with the channel stride padded to Coutp.  Padding is written as
+// zeros.  With vec (P a multiple of 16 bytes' worth and gy 16-byte aligned) rows are
+// read as 16-byte vectors; gyT rows are written as 16-byte vectors of channels.  Also
+// the bias gradient: this tile's sum over its pixels of each output channel (fp32
+// atomics).
+constexpr int kGT = 64;   // tile edge of the grad_out transposes
 template <typename T>
-__global__ __launch_bounds__(kBT) void bwd_prep_gy(BwdArgs a) {
-  __shared__ T tile[32][33];
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int p0 = blockIdx.x * 32, o0 = blockIdx.y * 32, b = blockIdx.z;
+__device__ __forceinline__ void prep_gy_tile(const BwdArgs& a, T* tile, int bx, int by, int b, bool vec) {
+  constexpr int VE = 16 / static_cast<int>(sizeof(T)), TPV = kGT + VE;   // LDS pitch
+  const int tid = threadIdx.x;
+  const int p0 = bx * kGT, o0 = by * kGT;
   const T* gy = static_cast<const T*>(a.gy) + static_cast<size_t>(b) * a.Cout * a.P;
-  T* gyp = a.gyp != nullptr ? static_cast<T*>(a.gyp) + static_cast<size_t>(b) * a.Cout * a.Pp : nullptr;
+  T* gyp = a.gyp != nullptr && a.gyp_copy ? static_cast<T*>(a.gyp) + static_cast<size_t>(b) * a.Cout * a.Pp : nullptr;
   T* gyt = a.gyt != nullptr ? static_cast<T*>(a.gyt) + static_cast<size_t>(b) * a.P * a.Coutp : nullptr;
+  // read: rows o of kGT pixels, VE pixels per item
+  for (int idx = tid; idx < kGT * (kGT / VE); idx += kBT) {
+    const int ol = idx / (kGT / VE), pl = (idx % (kGT / VE)) * VE;
+    const int o = o0 + ol, p = p0 + pl;
+    T v[VE];
+    if (vec && o < a.Cout && p < a.P) {
+      const uint4 q = *reinterpret_cast<const uint4*>(gy + static_cast<size_t>(o) * a.P + p);
+      __builtin_memcpy(v, &q, 16);
+    } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int o = o0 + ty + 8 * i, p = p0 + tx;
-    const T v = (o < a.Cout && p < a.P) ? gy[static_cast<size_t>(o) * a.P + p] : T(0);
-    tile[ty + 8 * i][tx] = v;
-    if (gyp != nullptr && o < a.Cout && p < a.Pp) gyp[static_cast<size_t>(o) * a.Pp + p] = v;
+      for (int j = 0; j < VE; ++j) v[j] = (o < a.Cout && p + j < a.P) ? gy[static_cast<size_t>(o) * a.P + p + j] : T(0);
+    }
+    uint4 q;
+    __builtin_memcpy(&q, v, 16);
+    *reinterpret_cast<uint4*>(tile + ol * TPV + pl) = q;
+    if (gyp != nullptr && o < a.Cout)
+#pragma unroll
+      for (int j = 0; j < VE; ++j)
+        if (p + j < a.Pp) gyp[static_cast<size_t>(o) * a.Pp + p + j] = v[j];
   }
   __syncthreads();
-  if (a.gyt != nullptr) {
+  if (gyt != nullptr) {   // rows p of kGT channels, VE channels per item (Coutp: a multiple of 8)
+    for (int idx = tid; idx < kGT * (kGT / VE); idx += kBT) {
+      const int pl = idx / (kGT / VE), ol = (idx % (kGT / VE)) * VE;
+      const int p = p0 + pl, o = o0 + ol;
+      if (p >= a.P || o >= a.Coutp) continue;
+      T v[VE];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = p0 + ty + 8 * i, o = o0 + tx;
-      if (p < a.P && o < a.Coutp) gyt[static_cast<size_t>(p) * a.Coutp + o] = tile[tx][ty + 8 * i];
+      for (int j = 0; j < VE; ++j) v[j] = tile[(ol + j) * TPV + pl];
+      uint4 q;
+      __builtin_memcpy(&q, v, 16);
+      *reinterpret_cast<uint4*>(gyt + static_cast<size_t>(p) * a.Coutp + o) = q;
     }
   }
-  // the bias gradient: this tile's sum over its 32 pixels of each output channel
-  if (a.gb32 != nullptr && threadIdx.x < 32 && o0 + static_cast<int>(threadIdx.x) < a.Cout) {
+  if (a.gb32 != nullptr && tid < kGT && o0 + tid < a.Cout) {
     float sum = 0.f;
 #pragma unroll 8
-    for (int t = 0; t < 32; ++t) sum += to_f(tile[threadIdx.x][t]);
-    unsafeAtomicAdd(a.gb32 + o0 + threadIdx.x, sum);
+    for (int t = 0; t < kGT; ++t) sum += to_f(tile[tid * TPV + t]);   // pixels past P are zero
+    unsafeAtomicAdd(a.gb32 + o0 + tid, sum);
   }
 }
 
@@ -207,8 +230,8 @@ struct Ranges {
   int count;
 };
 
-__global__ __launch_bounds__(kBT) void bwd_fill_zero_ranges(Ranges r) {
-  int blk = blockIdx.x, i = 0;
+__device__ __forceinline__ void fill_zero_block(const Ranges& r, int blk) {
+  int i = 0;
   while (i + 1 < r.count && blk >= r.blocks[i]) blk -= r.blocks[i++];
   const int e = (blk * kBT + static_cast<int>(threadIdx.x)) * 4;   // four floats per thread
   if (e + 4 <= r.n[i]) *reinterpret_cast<float4*>(r.p[i] + e) = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -281,13 +304,12 @@ __device__ __forceinline__ int corner_dq(int n, int W) { return (n & 1) + (n >> 
 __device__ __forceinline__ float corner_w(const Geo& e, int n) {
   return n == 0 ? e.w00 : n == 1 ? e.w01 : n == 2 ? e.w10 : e.w11;
 }
-__device__ __forceinline__ int int4_at(const int4& v, int n) { return n == 0 ? v.x : n == 1 ? v.y : n == 2 ? v.z : v.w; }
 
 // One thread per sample s = ((b*G + g)*K^2 + k)*P + p: each corner inside the image is
-// counted at its input pixel; the count before the increment is the pair's rank.
+// counted at its input pixel (increments whose old value nobody waits for).
 template <typename T>
-__global__ __launch_bounds__(kBT) void bwd_count(BwdArgs a) {
-  const int s = blockIdx.x * kBT + threadIdx.x;
+__device__ __forceinline__ void count_block(const BwdArgs& a, int blk) {
+  const int s = blk * kBT + threadIdx.x;
   if (s >= a.nsamp) return;
   const int p = s % a.P;
   int t = s / a.P;
@@ -296,15 +318,42 @@ __global__ __launch_bounds__(kBT) void bwd_count(BwdArgs a) {
   const int g = t % a.G, b = t / a.G;
   const Geo e = sample_geo<T>(a, b, g, k, p);
   int* c = a.cnt + (b * a.G + g) * a.H * a.W;
-  int r[4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) r[n] = (e.fl >> n) & 1 ? atomicAdd(c + e.q00 + corner_dq(n, a.W), 1) : -1;
-  a.rank[s] = make_int4(r[0], r[1], r[2], r[3]);
+  for (int n = 0; n < 4; ++n)
+    if ((e.fl >> n) & 1) atomicAdd(c + e.q00 + corner_dq(n, a.W), 1);
 }
 
-// Exclusive prefix sums of cnt[0, n) within blocks of kScanB (in place); each block's
-// total to bsum[block].
-__global__ __launch_bounds__(kBT) void bwd_scan_blocks(int* cnt, int n, int* bsum) {
+// Two launches share the small independent steps: the first the weight transpose and
+// the zero fill (bias accumulator, pair counters), the second the grad_out transposes
+// (with the bias sums) and the pair count.  Workgroups [0, n1) take the first step,
+// the rest the second.
+struct PrepLaunch {
+  BwdArgs a;
+  Ranges r;            // ranges to zero
+  int wx, wy;          // weight-transpose tiles (0 x 0: none)
+  int gx, gy, gz;      // grad_out tiles (0: none)
+  int gy_vec;          // grad_out rows readable as 16-byte vectors
+};
+
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_prep_1(PrepLaunch L) {
+  __shared__ T tile[32][33];
+  const int n1 = L.wx * L.wy, blk = blockIdx.x;
+  if (blk < n1) prep_w_tile<T>(L.a, tile, blk % L.wx, blk / L.wx);
+  else fill_zero_block(L.r, blk - n1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_prep_2(PrepLaunch L) {
+  __shared__ __attribute__((aligned(16))) T tile[kGT * (kGT + 16 / sizeof(T))];
+  const int n1 = L.gx * L.gy * L.gz, blk = blockIdx.x;
+  if (blk < n1) prep_gy_tile<T>(L.a, tile, blk % L.gx, (blk / L.gx) % L.gy, blk / (L.gx * L.gy), L.gy_vec);
+  else count_block<T>(L.a, blk - n1);
+}
+
+// Exclusive prefix sums of cnt[0, n) within blocks of kScanB (in place, and copied to
+// cur); each block's total to bsum[block].
+__global__ __launch_bounds__(kBT) void bwd_scan_blocks(int* cnt, int n, int* bsum, int* cur) {
   __shared__ int wsum[kBT / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int base = blockIdx.x * kScanB + tid * 8;
@@ -330,7 +379,7 @@ __global__ __launch_bounds__(kBT) void bwd_scan_blocks(int* cnt, int n, int* bsu
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = base + i;
-    if (j < n) cnt[j] = v[i] + off;
+    if (j < n) cnt[j] = cur[j] = v[i] + off;
   }
   if (tid == kBT - 1) bsum[blockIdx.x] = woff + inc;
 }
@@ -397,9 +446,9 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
 // and consecutive items on one XCD (the kernel points of a pixel block read neighbouring
 // corners).  Small items keep the dispatcher's tail short and, with few registers (no
 // sample's loads kept across another's), five waves per SIMD in flight.  First, four
-// threads per sample: the sample's geometry (to LDS) and, one corner each, the position
-// of its pair in its input pixel's list (the pair is stored after the channel work,
-// whose first loads overlap these).  Then a sample is taken by lg lanes, eight channels
+// threads per sample: the sample's geometry (to LDS) and, one corner each, a slot for
+// its pair in its input pixel's list from the pixel's cursor (the pair is stored after
+// the channel work, whose first loads overlap these).  Then a sample is taken by lg lanes, eight channels
 // each (16-byte channel vectors of xs and of its column-gradient row), all its loads
 // issued together; with 256 channels, 32 lanes and eight samples at a time.  The group's
 // channels go in chunks of 256: the chunk's column entries of the block wait in LDS
@@ -441,10 +490,8 @@ __global__ __launch_bounds__(kBT) void bwd_sample_cl(BwdArgs a) {
         sq[pl] = e.q00;
       }
       if (a.pairs != nullptr && ((e.fl >> n) & 1)) {
-        const int s = ((b * a.G + g) * a.KK + k) * a.P + p;
-        const int rn = reinterpret_cast<const int*>(a.rank)[4 * s + n];
         const int i = (b * a.G + g) * a.H * a.W + e.q00 + corner_dq(n, a.W);
-        pos = pair_start(a, i) + rn;
+        pos = atomicAdd(a.cur + i, 1) + a.bsum[i / kScanB];
         prow = (b * a.P + p) * a.KK + k;
         pw = e.m * corner_w(e, n);
       }
@@ -1012,7 +1059,7 @@ struct BwdPlan {
   int64_t Ho = 0, Wo = 0, P = 0, Pp = 0, Coutp = 0, R = 0, G = 1, Cp = 0, ncnt = 0, nblk = 0, nsamp = 0;
   int wks = 1;   // splits of the weight gradient's reduction (partial sums in the workspace)
   size_t o_wt = 0, o_gyt = 0, o_gyp = 0, o_col = 0, o_gcol = 0, o_xs = 0, o_gw = 0, o_gb = 0;
-  size_t o_cnt = 0, o_bsum = 0, o_rank = 0, o_pairs = 0;
+  size_t o_cnt = 0, o_bsum = 0, o_cur = 0, o_pairs = 0;
   size_t bytes = 0;
 };
 
@@ -1061,7 +1108,7 @@ int bwd_plan(const dcn_desc* d, BwdPlan* p) {
   p->o_gb = take(static_cast<size_t>(Cout) * 4);
   p->o_cnt = take(static_cast<size_t>(p->ncnt) * 4);
   p->o_bsum = take(static_cast<size_t>(p->nblk) * 4);
-  p->o_rank = take(static_cast<size_t>(p->nsamp) * 16);
+  p->o_cur = take(static_cast<size_t>(p->ncnt) * 4);
   p->o_pairs = take(static_cast<size_t>(p->nsamp) * 4 * 8);
   p->bytes = o;
   return DCN_OK;
@@ -1072,23 +1119,20 @@ hipError_t launch1(const void* fn, int64_t n, void** args, hipStream_t s) {
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>((n + kBT - 1) / kBT)), dim3(kBT), args, 0, s);
 }
 
-// ranges[i] = (fp32 buffer, destination or null, elements); null buffers are skipped
-hipError_t launch_ranges(const void* fn, int per_thread, std::initializer_list<std::tuple<float*, void*, int64_t>> list,
-                         hipStream_t s) {
-  Ranges r{};
+// ranges[i] = (fp32 buffer, elements) to zero, four floats per thread; null buffers
+// are skipped.  Returns the workgroups the ranges take.
+int make_ranges(Ranges* r, std::initializer_list<std::tuple<float*, int64_t>> list) {
+  *r = Ranges{};
   int total = 0;
   for (const auto& t : list) {
-    if (std::get<0>(t) == nullptr || std::get<2>(t) <= 0) continue;
-    r.p[r.count] = std::get<0>(t);
-    r.dst[r.count] = std::get<1>(t);
-    r.n[r.count] = static_cast<int>(std::get<2>(t));
-    r.blocks[r.count] = static_cast<int>((std::get<2>(t) + kBT * per_thread - 1) / (kBT * per_thread));
-    total += r.blocks[r.count];
-    ++r.count;
+    if (std::get<0>(t) == nullptr || std::get<1>(t) <= 0) continue;
+    r->p[r->count] = std::get<0>(t);
+    r->n[r->count] = static_cast<int>(std::get<1>(t));
+    r->blocks[r->count] = static_cast<int>((std::get<1>(t) + kBT * 4 - 1) / (kBT * 4));
+    total += r->blocks[r->count];
+    ++r->count;
   }
-  if (r.count == 0) return hipSuccess;
-  void* args[] = {&r};
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(total)), dim3(kBT), args, 0, s);
+  return total;
 }
 
 // bf16 products with a short reduction per workgroup (at most 256 values: the column
@@ -1162,7 +1206,9 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
   a.xs = ws + p.o_xs;
   a.wt = ws + p.o_wt;
   a.gyt = need_gcol ? static_cast<void*>(ws + p.o_gyt) : nullptr;
-  a.gyp = grad_weight != nullptr ? static_cast<void*>(ws + p.o_gyp) : nullptr;
+  // grad_out with its pixel stride padded to Pp: grad_out itself when P is a multiple of 8
+  a.gyp_copy = a.Pp > a.P ? 1 : 0;
+  a.gyp = grad_weight == nullptr ? nullptr : a.gyp_copy ? static_cast<void*>(ws + p.o_gyp) : const_cast<void*>(grad_out);
   a.col = grad_weight != nullptr ? static_cast<void*>(ws + p.o_col) : nullptr;
   a.gcol = need_gcol ? static_cast<void*>(ws + p.o_gcol) : nullptr;
   a.gb32 = grad_bias != nullptr ? reinterpret_cast<float*>(ws + p.o_gb) : nullptr;
@@ -1172,7 +1218,7 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
   if (grad_x != nullptr) {
     a.cnt = reinterpret_cast<int*>(ws + p.o_cnt);
     a.bsum = reinterpret_cast<int*>(ws + p.o_bsum);
-    a.rank = reinterpret_cast<int4*>(ws + p.o_rank);
+    a.cur = reinterpret_cast<int*>(ws + p.o_cur);
     a.pairs = reinterpret_cast<int2*>(ws + p.o_pairs);
   }
   float* gw32 = reinterpret_cast<float*>(ws + p.o_gw);   // [wks][Cout][R] partial sums
@@ -1190,23 +1236,34 @@ int run_backward(const dcn_desc* d, const BwdPlan& p, const void* x, const void*
     sa.KK = 1;
     BWD_TRY(launch_stage(kBF16 ? V_TILE_BF16_M64_N64 : V_TILE_F32_M64_N64, sa, s));
   }
-  if (need_gcol) {
-    const dim3 grid(static_cast<unsigned>((a.R + 31) / 32), static_cast<unsigned>((a.Coutp + 31) / 32));
-    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_w<T>), grid, dim3(kBT), args, 0, s));
-  }
-  // the bias accumulator and the pair counters zeroed by one launch (before prep_gy adds
-  // the bias sums)
-  BWD_TRY(launch_ranges(reinterpret_cast<const void*>(&bwd_fill_zero_ranges), 4,
-                        {{a.gb32, nullptr, a.Cout}, {reinterpret_cast<float*>(a.cnt), nullptr, p.ncnt}}, s));
-  if (sample || grad_bias != nullptr) {
-    const dim3 grid(static_cast<unsigned>((a.Pp + 31) / 32), static_cast<unsigned>((a.Coutp + 31) / 32),
-                    static_cast<unsigned>(a.B));
-    BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_gy<T>), grid, dim3(kBT), args, 0, s));
+  {
+    // the weight transpose and the zero fill (bias accumulator, pair counters: before the
+    // bias sums and the count), then the grad_out transposes and the pair count
+    PrepLaunch L{};
+    L.a = a;
+    if (need_gcol) {
+      L.wx = (a.R + 31) / 32;
+      L.wy = (a.Coutp + 31) / 32;
+    }
+    const int nfill = make_ranges(&L.r, {{a.gb32, a.Cout}, {reinterpret_cast<float*>(a.cnt), p.ncnt}});
+    const int n1 = L.wx * L.wy + nfill;
+    void* largs[] = {&L};
+    if (n1 > 0)
+      BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_1<T>), dim3(n1), dim3(kBT), largs, 0, s));
+    if (sample || grad_bias != nullptr) {
+      L.gx = (a.Pp + kGT - 1) / kGT;
+      L.gy = (a.Coutp + kGT - 1) / kGT;
+      L.gz = a.B;
+      L.gy_vec = a.P % (16 / static_cast<int>(sizeof(T))) == 0 && reinterpret_cast<uintptr_t>(grad_out) % 16 == 0;
+    }
+    const int ncount = grad_x != nullptr ? (a.nsamp + kBT - 1) / kBT : 0;
+    const int n2 = L.gx * L.gy * L.gz + ncount;
+    if (n2 > 0)
+      BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_2<T>), dim3(n2), dim3(kBT), largs, 0, s));
   }
   if (grad_x != nullptr) {
-    BWD_TRY(launch1(reinterpret_cast<const void*>(&bwd_count<T>), a.nsamp, args, s));
     int n = static_cast<int>(p.ncnt), nb = static_cast<int>(p.nblk);
-    void* s1[] = {&a.cnt, &n, &a.bsum};
+    void* s1[] = {&a.cnt, &n, &a.bsum, &a.cur};
     BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_scan_blocks), dim3(nb), dim3(kBT), s1, 0, s));
     void* s2[] = {&a.bsum, &nb};
     BWD_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&bwd_scan_top), dim3(1), dim3(kBT), s2, 0, s));
