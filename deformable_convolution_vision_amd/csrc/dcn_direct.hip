@@ -190,7 +190,18 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
     const float bv = colbuf[2 * st + lh][pn + l32];
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
   }
-  // accumulator element r: output channel o0 + om + 8*(r/4) + 4*lh + r%4, pixel pn + l32
+  // accumulator element r: output channel o0 + om + 8*(r/4) + 4*lh + r%4, pixel pn + l32.
+  // The bias values are loaded first, all of them (past Cout the buffer reads zero): a
+  // load under the per-element branch would make each store wait for the ones before.
+  float bias[16];
+  if (a.bias != nullptr) {   // uniform
+    const auto rbias = rsrc(a.bias, a.Cout * ES);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[r] = ldb<BF16>(rbias, o0 + om + 8 * (r >> 2) + 4 * lh + (r & 3));
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[r] = 0.f;
+  }
   const int np = blockIdx.x * 64 + pn + l32;
   if (np < a.N) {
     const int bp = np / a.HoWo, remp = np - (np / a.HoWo) * a.HoWo;
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int o = o0 + om + 8 * (r >> 2) + 4 * lh + (r & 3);
       if (o >= o1) continue;
-      const float v = acc[r] + (a.bias ? ldb<BF16>(rsrc(a.bias, a.Cout * ES), o) : 0.f);
+      const float v = acc[r] + bias[r];
       const int64_t e = (static_cast<int64_t>(bp) * a.Cout + o) * a.HoWo + remp;
       if constexpr (BF16) reinterpret_cast<uint16_t*>(a.out)[e] = to_bf16(v);
       else reinterpret_cast<float*>(a.out)[e] = v;
