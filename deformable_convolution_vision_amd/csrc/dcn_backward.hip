@@ -65,7 +65,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBT = 256;     // threads per workgroup
-constexpr int kSP = 16;      // output pixels per workgroup of the sampling kernel (one kernel point)
+constexpr int kSP = 32;      // output pixels per workgroup of the sampling kernel (one kernel point)
 constexpr int kGH = 1, kGW = 8;   // input tile (rows x columns) of a workgroup of the gather kernel
 constexpr int kGP = kGH * kGW;
 constexpr int kCC = 256;     // channels per chunk of the sampling and gather kernels (32 lanes x 8)
@@ -620,11 +620,12 @@ __global__ __launch_bounds__(kBT) void bwd_sample_cl(BwdArgs a) {
     }
     if (col != nullptr) {
       lds_barrier();
-      // rows (channel, kernel point) of col: 16 bytes (VE pixels) per thread, channels
-      // fastest over the threads (an LDS read of 64 neighbouring channels of one pixel)
+      // rows (channel, kernel point) of col: 16 bytes (VE pixels) per thread, the pieces
+      // of one row on neighbouring lanes, so that a store instruction writes whole row
+      // segments (few, large write requests) rather than 16 bytes in each of 64 rows
       const int ng = kSP / VE;
       for (int idx = tid; idx < ccn * ng; idx += kBT) {
-        const int c = idx % ccn, pg = idx / ccn;
+        const int pg = idx % ng, c = idx / ng;
         const int p0 = pb * kSP + pg * VE;
         if (p0 >= a.Pp) continue;
         T vals[VE];
