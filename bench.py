@@ -446,8 +446,9 @@ def bench_backward(w, steps: int, warmup: int):
         "config": {"workload": f"{w.name}: gradients of B={w.B} Cin={w.Cin} {w.H}x{w.W} -> Cout={w.Cout} "
                                f"{w.Ho}x{w.Wo}, K={w.K} stride={w.stride} pad={w.pad} dilation={w.dilation}, "
                                f"mask={'yes' if w.mask else 'no'} (grad x, offset, mask, weight, bias)",
-                   "variant": "backward", "plan": "dcn_backward: transposes, column-gradient MFMA product, "
-                                                   "sampling and scatter, weight-gradient MFMA product"},
+                   "variant": "backward", "plan": "dcn_backward: channels-last staging, transposes, pair count "
+                                                   "and scan, column-gradient MFMA product, sampling, input-gradient "
+                                                   "gather, weight-gradient MFMA product and split sum"},
         "frac_mfma_peak": round(tflops / peak, 5),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 4), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 5), "traffic": None,

@@ -61,12 +61,14 @@ CANCEL = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("name,force,kw", CANCEL, ids=[c[0] for c in CANCEL])
+# both element types for the planner's own choice; bf16 alone where a bf16 kernel is forced
+CANCEL_CASES = [(name, force, kw, dtype) for name, force, kw in CANCEL
+                for dtype in (("bf16",) if force is not None else ("f32", "bf16"))]
+
+
+@pytest.mark.parametrize("name,force,kw,dtype", CANCEL_CASES, ids=[f"{c[0]}-{c[3]}" for c in CANCEL_CASES])
 def test_corner_cancellation(name, force, kw, dtype, monkeypatch):
     if force is not None:
-        if dtype == "f32":
-            pytest.skip("the forced variant is a bf16 kernel; the f32 planner's choice runs in the other cases")
         variant, tile, pw = force
         monkeypatch.setenv("DCN_VARIANT", variant)
         if tile:
