@@ -15,10 +15,10 @@
 //    its extent comes from the tile's own offsets, clipped to one pixel around the
 //    image) into LDS with direct global->LDS loads, one chunk ahead, so each input
 //    vector crosses the vector-memory pipe once per chunk instead of once per
-//    (sample, corner).  A sample is interpolated from the box with two bf16 dot
-//    products per channel (corner pairs built with byte permutes); samples whose
-//    corners lie outside the box are read from the channels-last copy in global
-//    memory instead;
+//    (sample, corner).  A sample is interpolated from the box in fp32 (the bf16
+//    corners widened exactly, four fp32 weights, fused multiply-adds), rounded to bf16
+//    once; samples whose corners lie outside the box are read from the channels-last
+//    copy in global memory instead;
 //  * four consumer waves multiply the previous step's column tile with MFMA
 //    32x32x16 bf16 (two per 32-channel step and 32x32 output block) against their
 //    rows of the repacked weight, which they stream from L2 straight into registers
