@@ -20,19 +20,21 @@
 // derivative is the one from the right (the side floor picks); positions are formed
 // in fp32 as in the forward.
 //
-// Kernels, in launch order:
+// Launches, in order:
 //   stage    x -> xs [B][H][W][Cp], channels last (the forward's staging kernel)
-//   prep_w   W [Cout][Cin][K^2] -> Wt [K^2][Cin][Coutp] (the column-gradient product's
-//            second operand, rows in the column gradient's channel-fastest order)
-//   fill     zero the fp32 weight and bias accumulators and the pair counters (one launch)
-//   prep_gy  gy -> gyT [B][P][Coutp] and gyP [B][Cout][Pp] (both zero-padded), and the
-//            bias gradient's per-tile sums (fp32 atomics)
-//   count    per sample (b, group, kernel point, pixel): each corner inside the image
-//            counted at its input pixel
+//   prep_1   W [Cout][Cin][K^2] -> Wt [K^2][Cin][Coutp] (the column-gradient product's
+//            second operand, rows in the column gradient's channel-fastest order), and
+//            the bias accumulator and the pair counters zeroed
+//   prep_2   gy -> gyT [B][P][Coutp] and, when P is not a multiple of 8, gyP
+//            [B][Cout][Pp] (both zero-padded; otherwise gy itself serves as gyP), with
+//            the bias gradient's per-tile sums (fp32 atomics); and the pair count: per
+//            sample (b, group, kernel point, pixel) each corner inside the image counted
+//            at its input pixel
 //   scan     exclusive prefix sums of the counts: per block of 2048 (also copied to the
 //            per-pixel cursors), then the block sums
-//   gemm     gcol[b] = gyT[b] x Wt^T, channels fastest: [B][P][K^2][Cin] (MFMA)
-//   sample   per (b, group, kernel point, 16 output pixels): the corners from xs as
+//   gemm     gcol[b] = gyT[b] x Wt^T, channels fastest: [B][P][K^2][Cin] (MFMA), rounded
+//            to the element type
+//   sample   per (b, group, kernel point, 32 output pixels): the corners from xs as
 //            16-byte channel vectors; the column entries, transposed through LDS to
 //            col [B][R][Pp] for the weight gradient; the offset and mask gradients summed
 //            over the group's channels across the lanes of the sample and written once;
@@ -40,12 +42,13 @@
 //            placed in its input pixel's list at the slot its cursor hands out
 //   gather   grad_x per input pixel: the sum over its pairs of weight * column-gradient
 //            row, transposed through LDS to [B][Cin][H][W]
-//   gemm     grad_weight = sum_b gyP[b] x col[b]^T, the reduction split over workgroups
-//            (fp32 atomics into a zeroed accumulator)
-//   convert  the weight and bias accumulators -> the element type (one launch)
+//   gemm     grad_weight = sum_b gyP[b] x col[b]^T, the reduction split over workgroups,
+//            each split's partial sum to its own fp32 slice
+//   reduce   the partial sums added in split order and rounded to the element type; the
+//            bias accumulator converted
 // The gradient products run on MFMA 32x32x16 bf16 (bf16 data) or 32x32x2 fp32.  The
-// input, offset and mask gradients take no atomics: each is summed by one thread or one
-// group of lanes and rounded to the element type once.
+// input, offset, mask and weight gradients take no atomics: each is summed by one thread,
+// one group of lanes or one pass in a fixed order, and rounded to the element type once.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -224,7 +227,6 @@ __device__ __forceinline__ void prep_gy_tile(const BwdArgs& a, T* tile, int bx, 
 // split over the ranges in proportion to their sizes (blocks[i] workgroups for range i).
 struct Ranges {
   float* p[6];
-  void* dst[6];
   int n[6];
   int blocks[6];
   int count;
