@@ -194,14 +194,15 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
 }
 
 // The direct kernel: at most 4 input channels, K*K in {1, 4, 9}, and every tensor it
-// reads under 2 GiB (it addresses them with 32-bit byte offsets).
+// reads or writes under 2 GiB (it addresses them with 32-bit byte offsets).
 bool direct_fits(const dcn_desc* d, int64_t HoWo) {
   const int64_t KK = d->kernel_size * d->kernel_size;
   if (!dcn::direct_supported(static_cast<int>(d->in_channels), static_cast<int>(KK))) return false;
   const double es = d->dtype == DCN_BF16 ? 2.0 : 4.0, lim = 2147483647.0;
   return static_cast<double>(d->batch) * d->in_channels * d->height * d->width * es < lim &&
          static_cast<double>(d->batch) * 2 * KK * HoWo * es < lim &&
-         static_cast<double>(d->out_channels) * d->in_channels * KK * es < lim;
+         static_cast<double>(d->out_channels) * d->in_channels * KK * es < lim &&
+         static_cast<double>(d->batch) * d->out_channels * HoWo * es < lim;
 }
 
 // Pick the kernel variant for a valid descriptor.

@@ -80,7 +80,8 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
   // (one padding column keeps the 32 lanes of a weight read on distinct banks)
   __shared__ float colbuf[RP][64];
   __shared__ float wsm[RP][65];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int RK = a.Cin * KKT;
   const int o0 = blockIdx.y * 64, o1 = min(o0 + 64, a.Cout);
   const uint32_t HW = static_cast<uint32_t>(a.H) * static_cast<uint32_t>(a.W);
@@ -107,13 +108,18 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
   const int oy = rem / a.Wo, ox = rem - (rem / a.Wo) * a.Wo;
 
   // ---- column of the workgroup's 64 pixels: wave w samples kernel points k = w, w+4, ...
-  // Offsets and mask first, then the positions, then every input load (no branches:
-  // neighbours outside the image read as zero), then the interpolation.
+  // Offsets and mask first, then the positions, then every input load (no lane-dependent
+  // branches: neighbours outside the image read as zero), then the interpolation.  Only
+  // the last round of kernel points can be short of a point for some waves; those skip it.
   constexpr int KPW = (KKT + 3) / 4;   // kernel points per wave (at most)
+  auto has = [&](int t) { return t < KPW - 1 || wave + 4 * t < KKT; };   // uniform
   float dy[KPW], dx[KPW], mk[KPW];
 #pragma unroll
   for (int t = 0; t < KPW; ++t) {
-    const int k = min(wave + 4 * t, KKT - 1);
+    dy[t] = dx[t] = 0.f;
+    mk[t] = 1.f;
+    if (!has(t)) continue;
+    const int k = wave + 4 * t;
     const uint32_t ob = (static_cast<uint32_t>(b) * 2 * KKT + 2 * k) * a.HoWo + rem;
     dy[t] = ldb<BF16>(ro, ob);
     dx[t] = ldb<BF16>(ro, ob + a.HoWo);
@@ -127,7 +133,8 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
   float xv[KPW][CMAX][4], wq[KPW][4];
 #pragma unroll
   for (int t = 0; t < KPW; ++t) {
-    const int k = min(wave + 4 * t, KKT - 1);
+    if (!has(t)) continue;
+    const int k = wave + 4 * t;
     const int i = k / a.K, j = k - (k / a.K) * a.K;
     // integer and fractional parts of the offset are exact in fp32
     const float fy = floorf(dy[t]), fx = floorf(dx[t]);
@@ -161,8 +168,8 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
   }
 #pragma unroll
   for (int t = 0; t < KPW; ++t) {
+    if (!has(t)) continue;
     const int k = wave + 4 * t;
-    if (k >= KKT) continue;
 #pragma unroll
     for (int c = 0; c < CMAX; ++c) {
       // channels past Cin (and a padding row) are zero
@@ -202,18 +209,25 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) bias[r] = 0.f;
   }
+  // Stores go through a buffer resource: the lane's offset of its first element, and per
+  // accumulator element a uniform offset of whole output-channel planes (no per-element
+  // address arithmetic).  A pixel past N or an output channel past Cout gets an offset
+  // past the buffer, and the store is dropped.
   const int np = blockIdx.x * 64 + pn + l32;
-  if (np < a.N) {
-    const int bp = np / a.HoWo, remp = np - (np / a.HoWo) * a.HoWo;
+  const auto rout = rsrc(a.out, static_cast<uint32_t>(a.B) * a.Cout * a.HoWo * ES);
+  const int npc = np < a.N ? np : 0;
+  const int bp = npc / a.HoWo, remp = npc - (npc / a.HoWo) * a.HoWo;
+  const int orow = o0 + om + 4 * lh;   // output channel of accumulator element 0
+  const uint32_t vo = ((static_cast<uint32_t>(bp) * a.Cout + orow) * static_cast<uint32_t>(a.HoWo) + remp) * ES;
+  const uint32_t plane = static_cast<uint32_t>(a.HoWo) * ES;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int o = o0 + om + 8 * (r >> 2) + 4 * lh + (r & 3);
-      if (o >= o1) continue;
-      const float v = acc[r] + bias[r];
-      const int64_t e = (static_cast<int64_t>(bp) * a.Cout + o) * a.HoWo + remp;
-      if constexpr (BF16) reinterpret_cast<uint16_t*>(a.out)[e] = to_bf16(v);
-      else reinterpret_cast<float*>(a.out)[e] = v;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int dr = 8 * (r >> 2) + (r & 3);
+    const bool ok = np < a.N && orow + dr < o1;
+    const float v = acc[r] + bias[r];
+    const uint32_t off = ok ? vo : kOutside;
+    if constexpr (BF16) __builtin_amdgcn_raw_buffer_store_b16(to_bf16(v), rout, off, dr * plane, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rout, off, dr * plane, 0);
   }
 }
 
