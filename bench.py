@@ -19,6 +19,8 @@ roofline    = the fused kernel alone: algorithmic flops per launch / its mean du
               per launch from the committed counter runs, if the kernels are unchanged
 cpu_baseline = the CPU oracle on a bounded slice of the same workload (a range of
               output channels), scaled to TFLOP/s, with the threads it used
+clock ramp  = before the W warm-up steps, untimed steps for --ramp-ms of wall time
+              (default 200) bring the GPU to its steady clocks
 cold        = separate from value: steps each preceded by a 512 MiB device write that
               evicts the inputs from L2 and the 256 MB last-level cache (MALL), timed
               with events around the step alone
@@ -152,6 +154,25 @@ def traffic_for(workload: str):
     return entry.get("bytes_per_launch")
 
 
+RAMP_MS = 200.0   # set by --ramp-ms
+
+
+def clock_ramp(fn) -> float:
+    """Untimed calls of fn for RAMP_MS of wall time before the W warm-up steps: the GPU
+    reaches its steady clocks only after tens of milliseconds of load, so a short
+    warm-up alone (W = 5) would time the clock ramp instead of the kernels.  Returns
+    the milliseconds spent."""
+    import torch
+    if RAMP_MS <= 0:
+        return 0.0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < RAMP_MS:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3
+
+
 def bench_offset_mask(w, steps: int, warmup: int):
     """The DCNv2 offset/mask convolution (dcn_offset_mask): one step is one call (its
     staging launch and its convolution launch), timed as a whole with HIP events."""
@@ -202,6 +223,7 @@ def bench_offset_mask(w, steps: int, warmup: int):
         max_rel = max(max_rel, float(err))
     if not max_rel <= tol:
         raise SystemExit(f"bench parity failure on {w.name}: max relative error {max_rel:.3e} > {tol}")
+    clock_ramp(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -317,6 +339,7 @@ def bench_layer(w, steps: int, warmup: int):
         raise SystemExit(f"bench parity failure on {w.name}: max relative error {max_rel:.3e} > 1e-2")
 
     def timed(fn):
+        clock_ramp(fn)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -409,6 +432,7 @@ def bench_backward(w, steps: int, warmup: int):
         max_rel = max(max_rel, float(np.max(np.abs(got - want) / np.maximum(bound, 1e-300))) * rtol)
         if not np.all(np.abs(got - want) <= bound):
             raise SystemExit(f"bench parity failure on {w.name}: gradient outside |d| <= {rtol}|ref| + {atol}max|ref|")
+    clock_ramp(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -514,6 +538,7 @@ def bench_roi(w, steps: int, warmup: int):
     max_rel = float(np.max(err[ab > 0] / ab[ab > 0]))
     if not max_rel <= tol:
         raise SystemExit(f"bench parity failure on {w.name}: max relative error {max_rel:.3e} > {tol}")
+    clock_ramp(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -608,6 +633,7 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
     if not max_rel <= tol:
         raise SystemExit(f"bench parity failure on {name}: max relative error {max_rel:.3e} > {tol}")
 
+    clock_ramp(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -723,6 +749,7 @@ def bench_workload(name: str, steps: int, warmup: int, cpu: bool, cpu_seconds: f
         "host_wall_ms_per_step": round(wall * 1e3 / steps, 6),
         "parity_max_rel_err_sampled": max_rel,
         "cold": cold,
+        "clock_ramp_ms": RAMP_MS,
         "cpu_baseline": None,
     }
     if cpu:
@@ -778,6 +805,8 @@ def main(argv=None):
     # milliseconds of load (c4 fused launch: 35.1 us after 20 warm-up steps, 33.1 us
     # after 2000)
     ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--ramp-ms", type=float, default=200.0,
+                    help="untimed steps for this many ms before the warm-up steps (steady GPU clocks)")
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--all", action="store_true", help="also print one line per other named workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -787,6 +816,8 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
+    global RAMP_MS
+    RAMP_MS = args.ramp_ms
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
               f"multi-GPU path: the forward shards by batch or output channel with no exchange).",
