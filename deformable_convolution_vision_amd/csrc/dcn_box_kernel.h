@@ -168,6 +168,12 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// the same with a wave-uniform byte offset added (the instruction's scalar offset)
+__device__ __forceinline__ uint4 buffer_load16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 // the corner vector type's load: 16 or 8 bytes
 __device__ __forceinline__ void buffer_load_q(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint4& out) {
   out = buffer_load16(r, voff);
@@ -287,31 +293,32 @@ __global__ __launch_bounds__(256 + 64 * PW) void dcn_box_kernel(BoxArgs ba) {
 
   // ---- consumer state: weight fragments
   // The repacked weight is step-major, [step][Mp][32 channels], so the 32 rows x 64
-  // bytes of one 32-row block are one contiguous 2 KB.  Per-lane byte offsets of this
-  // wave's rows (the host keeps the repacked weight under 4 GiB) plus a wave-uniform
-  // base per step: scalar-base + vector-offset loads, the second half at +16 bytes.
+  // bytes of one 32-row block are one contiguous 2 KB.  Raw buffer loads: one per-lane
+  // byte offset (the lane's row of the wave's first block; the host keeps the repacked
+  // weight under 4 GiB) in a vector register, and the step's base plus the block and
+  // half offsets as the wave-uniform scalar offset, so the loop holds one address
+  // register and forms no 64-bit address per lane.
   struct AFrag { uint4 v[TM][2]; };
   const uint32_t step_bytes = static_cast<uint32_t>(a.m_tiles * MT) * 64u;
-  uint32_t aoff[TM];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-    aoff[tm] = static_cast<uint32_t>(m0 + wv * WM + tm * 32 + l32) * 64u + static_cast<uint32_t>(lh * 32);
+  const uint32_t aoff = static_cast<uint32_t>(m0 + wv * WM + l32) * 64u + static_cast<uint32_t>(lh * 32);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wp, static_cast<uint32_t>(S) * step_bytes);
   auto load_a = [&](int s) __attribute__((always_inline)) -> AFrag {
     AFrag r;
-    const unsigned char* base = wp + static_cast<size_t>(static_cast<uint32_t>(s) * step_bytes);
+    const uint32_t sb = static_cast<uint32_t>(s) * step_bytes;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-      r.v[tm][0] = *reinterpret_cast<const uint4*>(base + aoff[tm]);
-      r.v[tm][1] = *reinterpret_cast<const uint4*>(base + aoff[tm] + 16);
+      r.v[tm][0] = buffer_load16s(wrs, aoff, sb + static_cast<uint32_t>(tm * 32 * 64));
+      r.v[tm][1] = buffer_load16s(wrs, aoff, sb + static_cast<uint32_t>(tm * 32 * 64 + 16));
     }
     return r;
   };
   // Weight fragments in two sets of G slots: chunks G*g .. G*g+G-1 live in set pa
-  // for even g and in set qa for odd g (G = 4 for the smaller tiles; G = 2 where
-  // 2*G*FM fragments would not fit next to the accumulators and column fragments, and
-  // with offset groups, whose table work adds to the consumers' registers; G = 1 with
-  // eight producer waves, three waves per SIMD).
-  constexpr int G = PW == 8 ? 1 : (FM * FN <= 16 && !GRP) ? 4 : 2;
+  // for even g and in set qa for odd g.  With four producer waves G = 4 for the smaller
+  // tiles and G = 2 where 2*G*FM fragments would not fit next to the accumulators and
+  // column fragments, and with offset groups, whose table work adds to the consumers'
+  // registers.  With eight producer waves (three waves per SIMD) G = 2 for tiles up to
+  // 256 x 64 (loads two steps ahead: c4 fused 31.6 -> 30.9 us) and G = 1 for wider ones.
+  constexpr int G = PW == 8 ? (FM * FN <= 16 ? 2 : 1) : (FM * FN <= 16 && !GRP) ? 4 : 2;
   // consumers keep one column buffer in registers instead of two (eight producer waves
   // with tiles wider than 256 x 64)
   constexpr bool kSingleB = PW == 8 && FM * FN > 16;
