@@ -38,6 +38,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // reads under 2 GiB).  An offset past the end reads 0 without touching memory, which
 // is how neighbours outside the image are read: no branch around the load.
 constexpr uint32_t kOutside = 0x80000000u;
+// cache-policy bits of a buffer store: nontemporal
+constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
@@ -212,7 +214,8 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
   // Stores go through a buffer resource: the lane's offset of its first element, and per
   // accumulator element a uniform offset of whole output-channel planes (no per-element
   // address arithmetic).  A pixel past N or an output channel past Cout gets an offset
-  // past the buffer, and the store is dropped.
+  // past the buffer, and the store is dropped.  The stores are nontemporal (nothing here
+  // reads the output again, so it does not displace the inputs from L2).
   const int np = blockIdx.x * 64 + pn + l32;
   const auto rout = rsrc(a.out, static_cast<uint32_t>(a.B) * a.Cout * a.HoWo * ES);
   const int npc = np < a.N ? np : 0;
@@ -226,8 +229,8 @@ __global__ __launch_bounds__(256) void dcn_direct_kernel(FusedArgs a) {
     const bool ok = np < a.N && orow + dr < o1;
     const float v = acc[r] + bias[r];
     const uint32_t off = ok ? vo : kOutside;
-    if constexpr (BF16) __builtin_amdgcn_raw_buffer_store_b16(to_bf16(v), rout, off, dr * plane, 0);
-    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rout, off, dr * plane, 0);
+    if constexpr (BF16) __builtin_amdgcn_raw_buffer_store_b16(to_bf16(v), rout, off, dr * plane, kNonTemporal);
+    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rout, off, dr * plane, kNonTemporal);
   }
 }
 
