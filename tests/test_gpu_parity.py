@@ -468,6 +468,33 @@ def test_layer_forward(shape, dtype):
     """dcn_layer_forward (branch and deformable convolution off one staged x): offsets
     and mask against the oracle's branch, the output against the oracle's forward on the
     offsets and mask the call produced, and bit for bit against dcn_forward on them."""
+    _layer_case(shape, dtype)
+
+
+# The layer with the deformable convolution's box tile and producer-wave schedule pinned:
+# edge tiles, four and eight producer waves, one and three 32-channel chunks, dilation 2,
+# stride 2 without padding, two tiles of output channels.
+LAYER_PINNED_CASES = [  # shape (B, Cin, H, W, Cout, K, s, p, d, G), DCN_BOX_TILE, DCN_BOX_PW
+    ((1, 256, 30, 34, 256, 3, 2, 1, 1, 1), "4,5,10", "8"),
+    ((1, 256, 30, 34, 256, 3, 2, 1, 1, 1), "4,5,10", "4"),
+    ((2, 64, 17, 19, 70, 3, 1, 1, 1, 1), "4,4,16", "4"),
+    ((1, 96, 23, 29, 300, 3, 1, 2, 2, 1), "4,8,8", "8"),
+    ((2, 32, 13, 11, 64, 3, 2, 0, 1, 1), "4,6,10", "4"),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_PINNED_CASES, ids=lambda c: "x".join(map(str, c[0])) + f"_t{c[1]}_pw{c[2]}")
+def test_layer_forward_pinned_tiles(case, monkeypatch):
+    """dcn_layer_forward on the box kernel with its tile and schedule pinned, against the
+    oracle and bit for bit against dcn_forward on the offsets and mask it produced."""
+    shape, tile, pw = case
+    monkeypatch.setenv("DCN_BOX_TILE", tile)
+    monkeypatch.setenv("DCN_BOX_PW", pw)
+    plan = _layer_case(shape, "bf16")
+    assert "(64 slots)" in plan, plan
+
+
+def _layer_case(shape, dtype):
     B, Cin, H, W, Cout, K, s, p, d, G = shape
     seed = zlib.crc32(repr(shape).encode()) % 1000
     w_om, inp_om = _offset_mask_case(dtype, (B, Cin, H, W, K, s, p, d, G), seed)
@@ -477,7 +504,8 @@ def test_layer_forward(shape, dtype):
     g = to_gpu(inp)
     go = to_gpu(inp_om)
     desc = dcn.make_desc(B, Cin, H, W, Cout, K, s, p, d, dcn.BF16 if dtype == "bf16" else dcn.F32, G)
-    print(f"[gpu-test] layer {shape} {dtype}: {dcn.dcn_plan_describe(desc)}", flush=True)
+    plan = dcn.dcn_plan_describe(desc)
+    print(f"[gpu-test] layer {shape} {dtype}: {plan}", flush=True)
     out, off, msk = dcn.deform_conv2d_layer(g["x"], go["weight"], go["bias"], g["weight"], g["bias"], s, p, d,
                                             offset_groups=G)
     torch.cuda.synchronize()
@@ -492,6 +520,7 @@ def test_layer_forward(shape, dtype):
     ref = dcn.deform_conv2d(g["x"], off, g["weight"], g["bias"], s, p, d, mask=msk)
     torch.cuda.synchronize()
     assert torch.equal(out, ref), "dcn_layer_forward differs from dcn_forward on its own offsets and mask"
+    return plan
 
 
 def test_layer_forward_c4():
@@ -509,3 +538,6 @@ def test_layer_forward_c4():
     y, ay = oracle.forward(inp["x"], off.cpu(), inp["weight"], None, 2, 1, 1, mask=msk.cpu(), threads=0)
     worst = check(out.float().cpu().numpy(), y, ay, TOL["bf16"], "c4 layer output")
     print(f"[gpu-test] max relative error {worst:.2e}", flush=True)
+    ref = dcn.deform_conv2d(g["x"], off, g["weight"], None, 2, 1, 1, mask=msk)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), "the c4 layer differs from dcn_forward on its own offsets and mask"
