@@ -146,7 +146,12 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
           // tiles about twice as wide as tall measured fastest (rows of the box and of
           // the NCHW output are longer; the margin still grows in both directions)
           const double aspect = std::fabs(std::log2(double(TW) / (2.0 * TH)));
-          const double cost = rounds * wg * (1.0 + 4.0 / (1.0 + static_cast<double>(mg))) * (1.0 + 0.3 * aspect);
+          // an odd tile width (narrower than the output) leaves half the tiles' output
+          // column pairs misaligned, stored as single elements (c3: 9x17 -> 10x16 tiles
+          // 40.5 -> 39.7 us; c5: 7x13 -> 6x14 98.9 -> 97.1 us); fewer tiles break ties
+          const double odd_w = (TW & 1) && TW < Wo ? 1.15 : 1.0;
+          const double cost = rounds * wg * (1.0 + 4.0 / (1.0 + static_cast<double>(mg))) * (1.0 + 0.3 * aspect) *
+                              odd_w * (1.0 + 1e-6 * static_cast<double>(tiles));
           if (cost < best.cost) {
             best.fm = fm;
             best.fn = fn;
