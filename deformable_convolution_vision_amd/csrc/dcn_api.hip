@@ -168,22 +168,24 @@ bool plan_box(const dcn_desc* d, int64_t Ho, int64_t Wo, int fm_only, BoxPlan* o
     }
   }
   if (best.fm == 0) return false;
-  // Role placement: with 256 output channels and 96 pixel slots (12 matrix
-  // instructions per consumer wave and step, two samples per producer thread) the
-  // step is shorter when the consumers and producers do not share SIMDs (measured on
-  // the c5 layer: 108 -> 100 us); with 64 slots, halving the SIMDs that run matrix
-  // instructions costs more than it saves (c4: 36 -> 38 us).
-  best.split = best.fm == 4 && best.fn == 6;
   // Eight producer waves (two per SIMD, 4 channels per thread and sample) where that
   // kernel is built (256 x 64 and 256 x 96, 128 x 128 and 128 x 160 tiles; 3x3, one
-  // offset group) and the roles are paired (c4 layer: 33.1 -> 31.6 us).
-  // DCN_BOX_PW=4|8 pins it where it is built.
+  // offset group), on paired roles (c4 layer: 33.1 -> 31.6 us; the c5 layer's 6x14 tiles:
+  // 93.1 us, against 96.4 us with four producer waves on split roles).
+  // Otherwise four producer waves, and for 256 output channels and 96 pixel slots (12
+  // matrix instructions per consumer wave and step, two samples per producer thread)
+  // split roles: the consumers and producers do not share SIMDs (c5, 6x14 tiles: 104.9
+  // -> 96.4 us); with 64 slots, halving the SIMDs that run matrix instructions costs more
+  // than it saves (c4: 36 -> 38 us).
+  // DCN_BOX_PW=4|8 pins the producer waves where built.
   const bool pw8_built = dcn::box_pw8_supported(best.fm, best.fn) && d->kernel_size == 3 && offset_groups(d) == 1;
-  // (c3 layer on 128 x 160 tiles: 42.2 -> 41.4 us; the c5 layer's split roles beat
-  // eight paired producer waves: 90.0 against 93.3 us)
-  best.pw = pw8_built && !best.split ? 8 : 4;
+  best.split = best.fm == 4 && best.fn == 6 && !pw8_built;
+  best.pw = pw8_built ? 8 : 4;
   if (const char* w = std::getenv("DCN_BOX_PW")) {
-    if (w[0] == '4') best.pw = 4;
+    if (w[0] == '4') {   // four producer waves, on the roles that suit them
+      best.pw = 4;
+      best.split = best.fm == 4 && best.fn == 6;
+    }
     if (w[0] == '8' && pw8_built) {
       best.pw = 8;
       best.split = 0;
