@@ -141,8 +141,9 @@ class HipEvents:
 
 
 def traffic_for(workload: str):
-    """HBM bytes per fused launch (per call, all launches, for the offset/mask branch and
-    the layer) from the committed counter runs, if the sources are unchanged."""
+    """HBM bytes per fused launch (per call, all launches, for the offset/mask branch, the
+    layer, the backward and RoI pooling) from the committed counter runs, if the sources
+    are unchanged."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -475,7 +476,7 @@ def bench_backward(w, steps: int, warmup: int):
                                                    "gather, weight-gradient MFMA product and split sum"},
         "frac_mfma_peak": round(tflops / peak, 5),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 4), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 5), "traffic": None,
+                     "frac": round(achieved / peak, 5), "traffic": traffic_for(w.name),
                      "kernel": "dcn_backward (all launches of one call)", "kernel_sha": kernel_hash(w.name),
                      "per_launch": {"flops": flops}},
         "kernels_us": {"call_mean": round(call_mean * 1e3, 3), "call_median": round(per[steps // 2] * 1e3, 3),
@@ -573,7 +574,7 @@ def bench_roi(w, steps: int, warmup: int):
         "dtype": w.dtype, "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": what, "variant": w.op, "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK["hbm"], "unit": "GB/s",
-                     "frac": round(gbps / PEAK["hbm"], 5), "traffic": None,
+                     "frac": round(gbps / PEAK["hbm"], 5), "traffic": traffic_for(w.name),
                      "kernel": kname, "kernel_sha": kernel_hash(w.name),
                      "per_launch": {"algorithmic_bytes": abytes, "outputs": R * C_out * k * k}},
         "kernels_us": {"call_mean": round(ms_per_step * 1e3, 3)},
